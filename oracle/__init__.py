@@ -1,0 +1,236 @@
+"""fp64 CPU oracle for the selective scan (S6), its decode step and the Mamba-2 (SSD) layer.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. It shares no code with the GPU library
+(``selective_state_space_37_amd``) and never imports it; the GPU library never imports this.
+
+Functions take numpy arrays holding the *stored* input values (fp32 arrays, or bf16 values
+already widened to fp32/fp64 -- widening is exact) and return fp64 results.
+
+* ``scan``      -- the plain sequential recurrence in fp64 (C, ``oracle.c``): zero-order-hold
+                   discretisation of the continuous SSM and the discrete recurrence/readout of
+                   "Beyond attention: exploring Mamba and state space models", section on
+                   state-space basics; softplus step size from the selective-SSM section.
+* ``step``      -- one decode token with the width-W causal conv register of the
+                   "Mamba and state space models" page, section on the fixed-size state.
+* ``ssd``       -- Mamba-2 with a scalar A per head as the plain recurrence (same page, section
+                   "Mamba-2: two algorithms").
+* ``ssd_quadratic`` -- the same layer written as multiplication by the lower-triangular matrix
+                   M[i, j] = (C_i . B_j) * (all decay from step j to step i) * (ZOH input scale
+                   of step j), for tiny inputs only (numpy; O(L^2)).
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against closed forms, the
+continuous-time ODE, brute force and the pages' printed numbers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile ``oracle.c`` with gcc (-O2, OpenMP) into ``oracle/liboracle.so``."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
+               "-fno-fast-math", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _configure(lib):
+    i64, ci, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    lib.oracle_scan.argtypes = [i64, i64, i64, i64] + [vp, vp, vp, ci] + [vp] * 8
+    lib.oracle_scan.restype = None
+    lib.oracle_step.argtypes = [i64, i64, i64, i64] + [vp, vp, vp, ci] + [vp] * 10
+    lib.oracle_step.restype = None
+    lib.oracle_ssd.argtypes = [i64, i64, i64, i64, i64] + [vp, vp, vp, ci] + [vp] * 8
+    lib.oracle_ssd.restype = None
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ci
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        _lib = _configure(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+class Variant:
+    """The same Python API bound to another build of ``oracle.c`` (used by the mutation tests,
+    which compile copies of the source with a planted mistake)."""
+
+    def __init__(self, so_path: str):
+        self._lib = _configure(ctypes.CDLL(so_path))
+
+    def scan(self, *a, **k):
+        return scan(*a, _lib=self._lib, **k)
+
+    def step(self, *a, **k):
+        return step(*a, _lib=self._lib, **k)
+
+    def ssd(self, *a, **k):
+        return ssd(*a, _lib=self._lib, **k)
+
+
+def compile_source(src_text: str, so_path: str) -> str:
+    """Compile C source text (a variant of ``oracle.c``) to ``so_path`` with the oracle's flags."""
+    c_path = so_path[:-3] + ".c"
+    with open(c_path, "w") as f:
+        f.write(src_text)
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-fno-fast-math",
+                    "-o", so_path, c_path, "-lm"], check=True)
+    return so_path
+
+
+def source_text() -> str:
+    with open(_SRC) as f:
+        return f.read()
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def _f64(a, shape=None):
+    if a is None:
+        return None
+    out = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    if shape is not None and out.shape != tuple(shape):
+        raise ValueError("oracle: expected shape %s, got %s" % (tuple(shape), out.shape))
+    return out
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def scan(x, delta, A, Bm, Cm, *, delta_bias=None, delta_softplus=False, Dskip=None, z=None,
+         h0=None, return_state=True, _lib=None):
+    """Selective scan. x, delta, z: [B, L, D]; A: [D, N]; Bm, Cm: [B, L, N]; delta_bias, Dskip: [D];
+    h0: [B, D, N]. Returns (y [B, L, D], h_last [B, D, N]) in fp64."""
+    x = _f64(x)
+    if x.ndim != 3:
+        raise ValueError("oracle.scan: x must be [B, L, D]")
+    Bsz, L, D = x.shape
+    A = _f64(A)
+    N = A.shape[1]
+    delta = _f64(delta, (Bsz, L, D))
+    A = _f64(A, (D, N))
+    Bm = _f64(Bm, (Bsz, L, N))
+    Cm = _f64(Cm, (Bsz, L, N))
+    delta_bias = _f64(delta_bias, (D,))
+    Dskip = _f64(Dskip, (D,))
+    z = _f64(z, (Bsz, L, D))
+    h0 = _f64(h0, (Bsz, D, N))
+    y = np.empty((Bsz, L, D), dtype=np.float64)
+    h_last = np.empty((Bsz, D, N), dtype=np.float64) if return_state else None
+    (_lib or _load()).oracle_scan(Bsz, L, D, N, _p(x), _p(delta), _p(delta_bias), int(bool(delta_softplus)),
+                        _p(A), _p(Bm), _p(Cm), _p(Dskip), _p(z), _p(h0), _p(y), _p(h_last))
+    return (y, h_last) if return_state else y
+
+
+def step(x, delta, A, Bm, Cm, h, *, delta_bias=None, delta_softplus=False, Dskip=None, z=None,
+         conv_state=None, conv_w=None, conv_b=None, _lib=None):
+    """One decode token. x, delta, z: [B, D]; Bm, Cm: [B, N]; h: [B, D, N]; conv_state: [B, D, W];
+    conv_w: [D, W]; conv_b: [D]. Returns (y [B, D], h_new, conv_state_new) in fp64; inputs untouched."""
+    x = _f64(x)
+    Bsz, D = x.shape
+    A = _f64(A)
+    N = A.shape[1]
+    delta = _f64(delta, (Bsz, D))
+    Bm = _f64(Bm, (Bsz, N))
+    Cm = _f64(Cm, (Bsz, N))
+    h_new = _f64(h, (Bsz, D, N)).copy()
+    delta_bias = _f64(delta_bias, (D,))
+    Dskip = _f64(Dskip, (D,))
+    z = _f64(z, (Bsz, D))
+    W = 0
+    cs = None
+    if conv_state is not None:
+        cs = _f64(conv_state).copy()
+        W = cs.shape[2]
+        if cs.shape != (Bsz, D, W):
+            raise ValueError("oracle.step: conv_state must be [B, D, W]")
+        conv_w = _f64(conv_w, (D, W))
+        conv_b = _f64(conv_b, (D,))
+    y = np.empty((Bsz, D), dtype=np.float64)
+    (_lib or _load()).oracle_step(Bsz, D, N, W, _p(x), _p(delta), _p(delta_bias), int(bool(delta_softplus)),
+                        _p(A), _p(Bm), _p(Cm), _p(Dskip), _p(z), _p(cs), _p(conv_w), _p(conv_b),
+                        _p(h_new), _p(y))
+    return y, h_new, cs
+
+
+def ssd(x, delta, A, Bm, Cm, *, delta_bias=None, delta_softplus=False, Dskip=None, z=None, h0=None,
+        _lib=None):
+    """Mamba-2 scalar-A layer as the plain recurrence. x, z: [B, L, H, P]; delta: [B, L, H];
+    A, delta_bias, Dskip: [H]; Bm, Cm: [B, L, N]; h0: [B, H, P, N]. Returns (y, h_last) in fp64."""
+    x = _f64(x)
+    Bsz, L, H, P = x.shape
+    Bm = _f64(Bm)
+    N = Bm.shape[2]
+    delta = _f64(delta, (Bsz, L, H))
+    A = _f64(A, (H,))
+    Bm = _f64(Bm, (Bsz, L, N))
+    Cm = _f64(Cm, (Bsz, L, N))
+    delta_bias = _f64(delta_bias, (H,))
+    Dskip = _f64(Dskip, (H,))
+    z = _f64(z, (Bsz, L, H, P))
+    h0 = _f64(h0, (Bsz, H, P, N))
+    y = np.empty((Bsz, L, H, P), dtype=np.float64)
+    h_last = np.empty((Bsz, H, P, N), dtype=np.float64)
+    (_lib or _load()).oracle_ssd(Bsz, L, H, P, N, _p(x), _p(delta), _p(delta_bias), int(bool(delta_softplus)),
+                       _p(A), _p(Bm), _p(Cm), _p(Dskip), _p(z), _p(h0), _p(y), _p(h_last))
+    return y, h_last
+
+
+def ssd_quadratic(x, delta, A, Bm, Cm, *, delta_bias=None, delta_softplus=False,
+                  Dskip=None, z=None):
+    """Mamba-2 layer as one lower-triangular matrix per (batch, head), tiny inputs only.
+
+    Per the "Mamba-2: two algorithms" section: entry (i, j), j <= i, is C_i . B_j times all decay
+    between step j and step i, i.e. exp(a * (sum of Delta over steps j+1..i)), times the
+    zero-order-hold input scale expm1(a Delta_j) / a of step j. y = M x, then D term and gate.
+    Zero initial state.
+    """
+    x = _f64(x)
+    Bsz, L, H, P = x.shape
+    if L > 512:
+        raise ValueError("ssd_quadratic is for tiny inputs (L <= 512)")
+    Bm, Cm = _f64(Bm), _f64(Cm)
+    delta = _f64(delta, (Bsz, L, H))
+    A = _f64(A, (H,))
+    u = delta + (0.0 if delta_bias is None else _f64(delta_bias, (H,))[None, None, :])
+    dt = np.logaddexp(0.0, u) if delta_softplus else u
+    y = np.zeros((Bsz, L, H, P), dtype=np.float64)
+    for b in range(Bsz):
+        G = Cm[b] @ Bm[b].T  # [L, L]: C_i . B_j
+        for hd in range(H):
+            a = A[hd]
+            d = dt[b, :, hd]
+            M = np.zeros((L, L))
+            for i in range(L):
+                for j in range(i + 1):
+                    decay = np.exp(a * d[j + 1:i + 1].sum())
+                    scale = d[j] if a == 0.0 else np.expm1(a * d[j]) / a
+                    M[i, j] = G[i, j] * decay * scale
+            y[b, :, hd, :] = M @ x[b, :, hd, :]
+    if Dskip is not None:
+        y += _f64(Dskip, (H,))[None, None, :, None] * x
+    if z is not None:
+        zz = _f64(z, (Bsz, L, H, P))
+        y *= zz / (1.0 + np.exp(-zz))
+    return y

@@ -1,0 +1,202 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU oracle for the selective state-space (S6) forward pass,
+ * its one-token decode step, and the Mamba-2 scalar-A (SSD) layer.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU-baseline leg
+ * may load this library. It shares no code, header, table or constant with the GPU library;
+ * the product path never calls it.
+ *
+ * Every input arrives as fp64 (the callers upcast the stored bf16 / fp32 values, which is
+ * exact). Every loop runs in the order the definitions are written: sequential in time,
+ * one channel (or head) at a time. OpenMP splits only the independent (batch, channel) or
+ * (batch, head) pairs, so the result does not depend on the thread count.
+ *
+ * Sources (web pages on Mamba / selective state-space models):
+ *   "Beyond attention: exploring Mamba and state space models" (ai-lab.club), section on
+ *     state-space basics: the continuous system h' = A h + B x, y = C h + D x and its
+ *     zero-order-hold discretisation  Abar = exp(dA),  Bbar = (dA)^-1 (exp(dA) - I) dB,
+ *     h_t = Abar h_{t-1} + Bbar x_t,  y_t = C h_t + D x_t.
+ *   Same page, section on the selective SSM: Delta_t = softplus(W x_t + b), B_t, C_t per token.
+ *   "Mamba and state space models" (world.lapla.si), section "fixed-size state": the decode
+ *     state is the SSM state plus a short convolution holding the last 4 inputs.
+ *   Same page, section "Mamba-2: two algorithms": with A a scalar times identity, the layer is
+ *     multiplication by a lower-triangular matrix whose (i, j) entry is C at step i times B at
+ *     step j times all decay between the two steps.
+ *
+ * Readings taken where the pages are silent (each is listed in the design notes):
+ *   - A is diagonal, given as A[d, n] (the pages' discretisation specialised to diagonal A:
+ *     Bbar_n = expm1(Delta A_n) / A_n * B_n, with the limit Delta * B_n when A_n == 0).
+ *   - B_t and C_t are N-wide per token and shared by all channels (and by all SSD heads).
+ *   - D multiplies the SSM input of the channel; NULL means no D term.
+ *   - The optional gate is applied after the D term: y <- y * z * sigmoid(z). NULL z: no gate.
+ *   - The initial state is zero unless h0 is given.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* softplus(u) = log(1 + e^u), evaluated without overflow for either sign. */
+static double o_softplus(double u) {
+  return u > 0.0 ? u + log1p(exp(-u)) : log1p(exp(u));
+}
+
+/* logistic sigmoid, evaluated without overflow for either sign. */
+static double o_sigmoid(double v) {
+  if (v >= 0.0) return 1.0 / (1.0 + exp(-v));
+  double e = exp(v);
+  return e / (1.0 + e);
+}
+
+/* Zero-order-hold input scale for one diagonal entry: (Delta a)^-1 (exp(Delta a) - 1) Delta
+ * = expm1(Delta a) / a, whose limit at a == 0 is Delta. */
+static double o_zoh_scale(double dt, double a) {
+  return a == 0.0 ? dt : expm1(dt * a) / a;
+}
+
+static double o_step_size(double delta, const double* delta_bias, int64_t idx, int delta_softplus) {
+  double u = delta + (delta_bias ? delta_bias[idx] : 0.0);
+  return delta_softplus ? o_softplus(u) : u;
+}
+
+/*
+ * oracle_scan: selective scan, one (b, d) channel at a time, sequential in t.
+ *   x, delta, z, y : [Bsz, L, D]      delta_bias, Dskip : [D]      A : [D, N]
+ *   Bm, Cm         : [Bsz, L, N]      h0, h_last        : [Bsz, D, N]
+ * delta_bias, Dskip, z, h0, h_last may be NULL.
+ */
+void oracle_scan(int64_t Bsz, int64_t L, int64_t D, int64_t N,
+                 const double* x, const double* delta, const double* delta_bias, int delta_softplus,
+                 const double* A, const double* Bm, const double* Cm, const double* Dskip,
+                 const double* z, const double* h0, double* y, double* h_last) {
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int64_t b = 0; b < Bsz; ++b) {
+    for (int64_t d = 0; d < D; ++d) {
+      double* h = (double*)malloc((size_t)N * sizeof(double));
+      for (int64_t n = 0; n < N; ++n) h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        const int64_t io = (b * L + t) * D + d;
+        const double* Bt = Bm + (b * L + t) * N;
+        const double* Ct = Cm + (b * L + t) * N;
+        const double dt = o_step_size(delta[io], delta_bias, d, delta_softplus);
+        const double xt = x[io];
+        double out = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          const double a = A[d * N + n];
+          const double abar = exp(dt * a);
+          const double bbar = o_zoh_scale(dt, a) * Bt[n];
+          h[n] = abar * h[n] + bbar * xt;
+          out += Ct[n] * h[n];
+        }
+        if (Dskip) out += Dskip[d] * xt;
+        if (z) out *= z[io] * o_sigmoid(z[io]);
+        y[io] = out;
+      }
+      if (h_last)
+        for (int64_t n = 0; n < N; ++n) h_last[(b * D + d) * N + n] = h[n];
+      free(h);
+    }
+  }
+}
+
+/*
+ * oracle_step: one decode token per (b, d).
+ *   x, delta, z, y : [Bsz, D]   Bm, Cm : [Bsz, N]   A : [D, N]   h : [Bsz, D, N] (in/out)
+ *   conv_state     : [Bsz, D, W] (in/out; oldest input first, newest last) or NULL
+ *   conv_w         : [D, W] (conv_w[d, W-1] multiplies the newest input)   conv_b : [D] or NULL
+ * With conv_state == NULL the SSM input is x itself; otherwise the register is shifted by one,
+ * x enters at the newest slot, and the SSM input is the depthwise causal convolution
+ * u = sum_k conv_w[d, k] * register[k] (+ conv_b[d]). u replaces x in the D term too.
+ */
+void oracle_step(int64_t Bsz, int64_t D, int64_t N, int64_t W,
+                 const double* x, const double* delta, const double* delta_bias, int delta_softplus,
+                 const double* A, const double* Bm, const double* Cm, const double* Dskip,
+                 const double* z, double* conv_state, const double* conv_w, const double* conv_b,
+                 double* h, double* y) {
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t b = 0; b < Bsz; ++b) {
+    for (int64_t d = 0; d < D; ++d) {
+      const int64_t io = b * D + d;
+      double u = x[io];
+      if (conv_state) {
+        double* reg = conv_state + io * W;
+        for (int64_t k = 0; k + 1 < W; ++k) reg[k] = reg[k + 1];
+        reg[W - 1] = x[io];
+        u = conv_b ? conv_b[d] : 0.0;
+        for (int64_t k = 0; k < W; ++k) u += conv_w[d * W + k] * reg[k];
+      }
+      const double dt = o_step_size(delta[io], delta_bias, d, delta_softplus);
+      double* hs = h + io * N;
+      double out = 0.0;
+      for (int64_t n = 0; n < N; ++n) {
+        const double a = A[d * N + n];
+        hs[n] = exp(dt * a) * hs[n] + o_zoh_scale(dt, a) * Bm[b * N + n] * u;
+        out += Cm[b * N + n] * hs[n];
+      }
+      if (Dskip) out += Dskip[d] * u;
+      if (z) out *= z[io] * o_sigmoid(z[io]);
+      y[io] = out;
+    }
+  }
+}
+
+/*
+ * oracle_ssd: Mamba-2 layer with one scalar A per head, run as the plain recurrence
+ * (the chunk size plays no part in the result).
+ *   x, z, y : [Bsz, L, H, P]   delta : [Bsz, L, H]   delta_bias, A, Dskip : [H]
+ *   Bm, Cm  : [Bsz, L, N] (shared by all heads)       h0, h_last : [Bsz, H, P, N]
+ * State per (b, h): S[p, n] <- exp(Delta a) S[p, n] + expm1(Delta a)/a * x[p] * B[n];
+ * y[p] = sum_n C[n] S[p, n] (+ Dskip[h] x[p]), then the optional gate.
+ */
+void oracle_ssd(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t N,
+                const double* x, const double* delta, const double* delta_bias, int delta_softplus,
+                const double* A, const double* Bm, const double* Cm, const double* Dskip,
+                const double* z, const double* h0, double* y, double* h_last) {
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int64_t b = 0; b < Bsz; ++b) {
+    for (int64_t hd = 0; hd < H; ++hd) {
+      double* S = (double*)malloc((size_t)(P * N) * sizeof(double));
+      for (int64_t i = 0; i < P * N; ++i) S[i] = h0 ? h0[(b * H + hd) * P * N + i] : 0.0;
+      const double a = A[hd];
+      for (int64_t t = 0; t < L; ++t) {
+        const double dt = o_step_size(delta[(b * L + t) * H + hd], delta_bias, hd, delta_softplus);
+        const double abar = exp(dt * a);
+        const double phi = o_zoh_scale(dt, a);
+        const double* Bt = Bm + (b * L + t) * N;
+        const double* Ct = Cm + (b * L + t) * N;
+        const double* xt = x + ((b * L + t) * H + hd) * P;
+        const double* zt = z ? z + ((b * L + t) * H + hd) * P : NULL;
+        double* yt = y + ((b * L + t) * H + hd) * P;
+        for (int64_t p = 0; p < P; ++p) {
+          double out = 0.0;
+          for (int64_t n = 0; n < N; ++n) {
+            S[p * N + n] = abar * S[p * N + n] + phi * xt[p] * Bt[n];
+            out += Ct[n] * S[p * N + n];
+          }
+          if (Dskip) out += Dskip[hd] * xt[p];
+          if (zt) out *= zt[p] * o_sigmoid(zt[p]);
+          yt[p] = out;
+        }
+      }
+      if (h_last)
+        for (int64_t i = 0; i < P * N; ++i) h_last[(b * H + hd) * P * N + i] = S[i];
+      free(S);
+    }
+  }
+}
+
+/* Number of threads an OpenMP region would use (reported beside CPU timings). */
+int oracle_num_threads(void) {
+  int n = 1;
+#ifdef _OPENMP
+#pragma omp parallel
+  {
+#pragma omp single
+    n = omp_get_num_threads();
+  }
+#endif
+  return n;
+}

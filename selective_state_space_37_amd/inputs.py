@@ -1,0 +1,245 @@
+"""Seeded synthetic inputs for the selective-scan workloads.
+
+This module only draws random numbers and stores them in the I/O dtype. It holds none of the
+method's arithmetic, so both the GPU library's tests and the CPU oracle can take their inputs
+from it.
+
+Draw recipe: every tensor and every (batch row, block of 8192 tokens) draws from its own
+``numpy.random.Generator(PCG64(SeedSequence([seed, tensor_id, b, block])))`` in float64, is cast
+to fp32, and, for bf16 tensors, rounded to bf16 with round-to-nearest-even. Tensor ids:
+x=0, delta=1, B=2, C=3, z=4, D=5, conv_w=6, A=7, conv register=8; decode step s draws with
+tensor id 100 + s. Large workloads can therefore be produced block by block and reproduced.
+
+bf16 tensors are held as ``numpy.uint16`` arrays of bf16 bit patterns.
+
+Workload shapes and value distributions follow the pages' workloads: a Mamba-2.8B layer
+(d_inner 5120, state size 16, training length 2048), the two-layer induction task run out to
+1,048,576 tokens, generation at batch 128 after a 2,048-token prompt, and the Mamba-2 layer with
+state size 128. A[d, n] = -(n + 1) is the S4D-real style initialisation the Mamba page describes
+(A from -1 to -16 across the 16 states).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, Optional
+
+import numpy as np
+
+TOKEN_BLOCK = 8192
+TID_X, TID_DELTA, TID_B, TID_C, TID_Z, TID_D, TID_CONVW, TID_A, TID_CONVREG = range(9)
+TID_STEP0 = 100
+
+# 0.5 * ln(expm1(0.01)): the per-channel step-size bias of the oracle-sized workload.
+DELTA_BIAS_SMALL = 0.5 * math.log(math.expm1(0.01))
+
+
+# ----------------------------------------------------------------------------- bf16 storage
+def f32_to_bf16_bits(a) -> np.ndarray:
+    """Round fp32 values to bf16 (round to nearest, ties to even); returns uint16 bit patterns."""
+    u = np.ascontiguousarray(np.asarray(a, dtype=np.float32)).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    """Widen bf16 bit patterns to fp32 (exact)."""
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def widen(a, dtype: str) -> Optional[np.ndarray]:
+    """Stored values (fp32 array or bf16 bits) -> float64 array, exactly."""
+    if a is None:
+        return None
+    if dtype == "bf16" and np.asarray(a).dtype == np.uint16:
+        return bf16_bits_to_f32(a).astype(np.float64)
+    return np.asarray(a, dtype=np.float64)
+
+
+def store(a_f32, dtype: str) -> np.ndarray:
+    a32 = np.ascontiguousarray(np.asarray(a_f32, dtype=np.float32))
+    return f32_to_bf16_bits(a32) if dtype == "bf16" else a32
+
+
+# ----------------------------------------------------------------------------- raw draws
+def _rng(seed: int, tid: int, b: int = 0, block: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tid, b, block])))
+
+
+def draw_tokens(seed: int, tid: int, Bsz: int, L: int, width: int, kind: str = "normal",
+                loc: float = 0.0, scale: float = 1.0) -> np.ndarray:
+    """fp32 array [Bsz, L, width]; rows (b, token block) drawn from independent streams."""
+    out = np.empty((Bsz, L, width), dtype=np.float32)
+    for b in range(Bsz):
+        for blk, t0 in enumerate(range(0, L, TOKEN_BLOCK)):
+            t1 = min(L, t0 + TOKEN_BLOCK)
+            g = _rng(seed, tid, b, blk)
+            if kind == "normal":
+                v = g.standard_normal((t1 - t0, width)) * scale + loc
+            elif kind == "uniform":
+                v = g.uniform(loc, scale, (t1 - t0, width))
+            else:
+                raise ValueError(kind)
+            out[b, t0:t1] = v
+    return out
+
+
+def draw_param(seed: int, tid: int, shape, kind: str = "normal", loc: float = 0.0,
+               scale: float = 1.0) -> np.ndarray:
+    g = _rng(seed, tid)
+    if kind == "normal":
+        return (g.standard_normal(shape) * scale + loc).astype(np.float32)
+    if kind == "uniform":
+        return g.uniform(loc, scale, shape).astype(np.float32)
+    raise ValueError(kind)
+
+
+def clipped_softplus_normal(v: np.ndarray, lo: float = 1e-3, hi: float = 0.1) -> np.ndarray:
+    """Distribution transform for already-activated step sizes: log(1 + e^v), clipped.
+
+    Data generation only (numpy's ``logaddexp``): the workload hands the kernel a step size that
+    an upstream projection has already activated, so the kernel's own activation is off.
+    """
+    return np.clip(np.logaddexp(0.0, v.astype(np.float64)), lo, hi).astype(np.float32)
+
+
+def structured_A(D: int, N: int) -> np.ndarray:
+    """A[d, n] = -(n + 1): -1 .. -N across the states of every channel."""
+    return np.tile(-(np.arange(N, dtype=np.float32) + 1.0), (D, 1))
+
+
+# ----------------------------------------------------------------------------- workloads
+@dataclass
+class ScanInputs:
+    """Inputs of one selective-scan call, in their stored dtype."""
+    dtype: str                   # "f32" or "bf16" (x, delta, z, Bm, Cm, y)
+    x: np.ndarray                # [B, L, D]
+    delta: np.ndarray            # [B, L, D]
+    A: np.ndarray                # [D, N] fp32
+    Bm: np.ndarray               # [B, L, N]
+    Cm: np.ndarray               # [B, L, N]
+    delta_bias: Optional[np.ndarray] = None   # [D] fp32
+    delta_softplus: bool = False
+    Dskip: Optional[np.ndarray] = None        # [D] fp32
+    z: Optional[np.ndarray] = None            # [B, L, D]
+    h0: Optional[np.ndarray] = None           # [B, D, N] fp32
+
+    @property
+    def shape(self):
+        Bsz, L, D = self.x.shape
+        return Bsz, L, D, self.A.shape[1]
+
+
+def scan_small(seed: int = 0, Bsz: int = 1, L: int = 256, D: int = 64, N: int = 16,
+               dtype: str = "f32", gate: bool = True, dskip: bool = True,
+               h0: bool = False) -> ScanInputs:
+    """Oracle-sized scan: delta = 0.5 N(0,1) with per-channel bias 0.5 ln(expm1(0.01)), activation on;
+    x, B, C, z, D ~ N(0, 1); A[d, n] = -(n + 1)."""
+    x = draw_tokens(seed, TID_X, Bsz, L, D)
+    delta = draw_tokens(seed, TID_DELTA, Bsz, L, D, scale=0.5)
+    Bm = draw_tokens(seed, TID_B, Bsz, L, N)
+    Cm = draw_tokens(seed, TID_C, Bsz, L, N)
+    z = draw_tokens(seed, TID_Z, Bsz, L, D) if gate else None
+    Dp = draw_param(seed, TID_D, (D,)) if dskip else None
+    hinit = draw_param(seed, TID_CONVREG + 1, (Bsz, D, N)) if h0 else None
+    return ScanInputs(dtype=dtype, x=store(x, dtype), delta=store(delta, dtype),
+                      A=structured_A(D, N), Bm=store(Bm, dtype), Cm=store(Cm, dtype),
+                      delta_bias=np.full((D,), DELTA_BIAS_SMALL, dtype=np.float32),
+                      delta_softplus=True, Dskip=Dp,
+                      z=None if z is None else store(z, dtype), h0=hinit)
+
+
+def scan_layer(seed: int = 1, Bsz: int = 8, L: int = 2048, D: int = 5120, N: int = 16,
+               dtype: str = "bf16", gate: bool = True, dskip: bool = True) -> ScanInputs:
+    """Mamba-2.8B-layer-shaped forward: x, z, B, C ~ N(0, 1); delta = clip(log(1+e^N(-4,1)),
+    1e-3, 0.1) already activated (activation off, no bias); A[d, n] = -(n + 1); D ~ N(0, 1)."""
+    x = draw_tokens(seed, TID_X, Bsz, L, D)
+    delta = clipped_softplus_normal(draw_tokens(seed, TID_DELTA, Bsz, L, D, loc=-4.0))
+    Bm = draw_tokens(seed, TID_B, Bsz, L, N)
+    Cm = draw_tokens(seed, TID_C, Bsz, L, N)
+    z = draw_tokens(seed, TID_Z, Bsz, L, D) if gate else None
+    Dp = draw_param(seed, TID_D, (D,)) if dskip else None
+    return ScanInputs(dtype=dtype, x=store(x, dtype), delta=store(delta, dtype),
+                      A=structured_A(D, N), Bm=store(Bm, dtype), Cm=store(Cm, dtype),
+                      delta_bias=None, delta_softplus=False, Dskip=Dp,
+                      z=None if z is None else store(z, dtype))
+
+
+def scan_long(seed: int = 2, Bsz: int = 1, L: int = 1 << 20, D: int = 256, N: int = 16,
+              dtype: str = "f32") -> ScanInputs:
+    """Long, narrow sequence (the induction-task length 1,048,576): distributions of scan_small."""
+    return scan_small(seed=seed, Bsz=Bsz, L=L, D=D, N=N, dtype=dtype)
+
+
+@dataclass
+class DecodeStep:
+    x: np.ndarray       # [B, D]
+    delta: np.ndarray   # [B, D]
+    Bm: np.ndarray      # [B, N]
+    Cm: np.ndarray      # [B, N]
+    z: np.ndarray       # [B, D]
+
+
+def decode_params(seed: int = 3, D: int = 4096, N: int = 16, W: int = 4):
+    """Per-channel parameters of the decode workload: A = -(n+1), D ~ N(0,1), conv_w ~ 0.5 N(0,1)."""
+    return dict(A=structured_A(D, N), Dskip=draw_param(seed, TID_D, (D,)),
+                conv_w=draw_param(seed, TID_CONVW, (D, W), scale=0.5))
+
+
+def decode_step(seed: int, step: int, Bsz: int = 128, D: int = 4096, N: int = 16,
+                dtype: str = "bf16") -> DecodeStep:
+    """Fresh per-token inputs for decode step ``step``; distributions of ``scan_layer``."""
+    tid = TID_STEP0 + step
+    g = lambda sub: _rng(seed, tid, sub)
+    x = g(0).standard_normal((Bsz, D)).astype(np.float32)
+    delta = clipped_softplus_normal((g(1).standard_normal((Bsz, D)) - 4.0).astype(np.float32))
+    Bm = g(2).standard_normal((Bsz, N)).astype(np.float32)
+    Cm = g(3).standard_normal((Bsz, N)).astype(np.float32)
+    z = g(4).standard_normal((Bsz, D)).astype(np.float32)
+    return DecodeStep(x=store(x, dtype), delta=store(delta, dtype), Bm=store(Bm, dtype),
+                      Cm=store(Cm, dtype), z=store(z, dtype))
+
+
+def conv_register(seed: int, Bsz: int, D: int, W: int = 4, dtype: str = "bf16") -> np.ndarray:
+    """Raw inputs of the last W prompt tokens, oldest first: [B, D, W] ~ N(0, 1)."""
+    v = _rng(seed, TID_CONVREG).standard_normal((Bsz, D, W)).astype(np.float32)
+    return store(v, dtype)
+
+
+@dataclass
+class SSDInputs:
+    dtype: str
+    x: np.ndarray        # [B, L, H, P]
+    delta: np.ndarray    # [B, L, H]
+    A: np.ndarray        # [H] fp32
+    Bm: np.ndarray       # [B, L, N]
+    Cm: np.ndarray       # [B, L, N]
+    delta_bias: Optional[np.ndarray] = None
+    delta_softplus: bool = False
+    Dskip: Optional[np.ndarray] = None   # [H]
+    z: Optional[np.ndarray] = None       # [B, L, H, P]
+    h0: Optional[np.ndarray] = None      # [B, H, P, N]
+
+    @property
+    def shape(self):
+        Bsz, L, H, P = self.x.shape
+        return Bsz, L, H, P, self.Bm.shape[2]
+
+
+def ssd_layer(seed: int = 4, Bsz: int = 2, L: int = 8192, H: int = 80, P: int = 64, N: int = 128,
+              dtype: str = "bf16", gate: bool = False, dskip: bool = False,
+              h0: bool = False) -> SSDInputs:
+    """Mamba-2 chunked-form workload: x, B, C ~ N(0, 1); delta per (b, t, head) as scan_layer;
+    A_h = -U(1, 16)."""
+    x = draw_tokens(seed, TID_X, Bsz, L, H * P).reshape(Bsz, L, H, P)
+    delta = clipped_softplus_normal(draw_tokens(seed, TID_DELTA, Bsz, L, H, loc=-4.0))
+    Bm = draw_tokens(seed, TID_B, Bsz, L, N)
+    Cm = draw_tokens(seed, TID_C, Bsz, L, N)
+    A = -draw_param(seed, TID_A, (H,), kind="uniform", loc=1.0, scale=16.0)
+    z = draw_tokens(seed, TID_Z, Bsz, L, H * P).reshape(Bsz, L, H, P) if gate else None
+    Dp = draw_param(seed, TID_D, (H,)) if dskip else None
+    hinit = draw_param(seed, TID_CONVREG + 1, (Bsz, H, P, N), scale=0.5) if h0 else None
+    return SSDInputs(dtype=dtype, x=store(x, dtype), delta=store(delta, dtype), A=A,
+                     Bm=store(Bm, dtype), Cm=store(Cm, dtype), Dskip=Dp,
+                     z=None if z is None else store(z, dtype), h0=hinit)

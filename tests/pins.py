@@ -1,0 +1,356 @@
+"""Pins for the fp64 oracle: each check compares an oracle function with something fixed by the
+pages or by mathematics -- never with a retyped copy of the oracle's own formula.
+
+Each ``check_*`` takes the oracle callable(s) as arguments and returns the worst relative error,
+so the same checks also run against deliberately broken copies of the oracle (the mutation
+suite in ``test_oracle_pins.py``), which shows that each planted mistake fails at least one pin.
+
+Pages cited (titles as given):
+  [BA] "Beyond attention: exploring Mamba and state space models" -- continuous SSM, ZOH
+       discretisation, recurrence/readout (state-space basics section); softplus step size and
+       per-token B, C (selective SSM section).
+  [MS] "Mamba and state space models" -- LTI convolution view ("every step the same"),
+       Delta large resets / small keeps and Theorem 1 gate ("decided by the token"),
+       fixed-size decode state with the last 4 inputs ("fixed-size state"), Mamba-2 matrix
+       form ("Mamba-2: two algorithms").
+"""
+from __future__ import annotations
+
+import numpy as np
+import scipy.integrate
+import scipy.linalg
+import scipy.special
+
+RNG = np.random.default_rng
+
+
+def rel_err(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    scale = max(float(np.max(np.abs(b))), 1e-300)
+    return float(np.max(np.abs(a - b))) / scale
+
+
+def tiny_scan_case(seed, Bsz=2, L=7, D=3, N=4, a_zero=True, softplus=True, gate=True, dskip=True,
+                   h0=True):
+    g = RNG(seed)
+    A = -g.uniform(0.2, 3.0, (D, N))
+    if a_zero:
+        A[0, 1] = 0.0  # the a -> 0 limit of the ZOH scale
+    case = dict(
+        x=g.standard_normal((Bsz, L, D)),
+        delta=g.standard_normal((Bsz, L, D)) * 0.7 if softplus else g.uniform(0.05, 0.8, (Bsz, L, D)),
+        A=A,
+        Bm=g.standard_normal((Bsz, L, N)),
+        Cm=g.standard_normal((Bsz, L, N)),
+        delta_bias=g.standard_normal(D) * 0.3 if softplus else None,
+        delta_softplus=softplus,
+        Dskip=g.standard_normal(D) if dskip else None,
+        z=g.standard_normal((Bsz, L, D)) if gate else None,
+        h0=g.standard_normal((Bsz, D, N)) if h0 else None,
+    )
+    return case
+
+
+def _step_sizes(case):
+    u = case["delta"] + (0.0 if case["delta_bias"] is None else case["delta_bias"][None, None, :])
+    # softplus via numpy's logaddexp: log(e^0 + e^u)
+    return np.logaddexp(0.0, u) if case["delta_softplus"] else u
+
+
+def check_ode(scan, case):
+    """[BA] continuous system h' = A h + B x held constant over each step of length Delta_t
+    (zero-order hold), integrated numerically; y_t = C_t h(t) + D x_t, then the gate z*sigmoid(z).
+    Pins the ZOH discretisation, the softplus step size, the recurrence, the readout, D and gate."""
+    dt = _step_sizes(case)
+    x, A, Bm, Cm = case["x"], case["A"], case["Bm"], case["Cm"]
+    Bsz, L, D = x.shape
+    N = A.shape[1]
+    h = np.zeros((Bsz, D, N)) if case["h0"] is None else case["h0"].copy()
+    y_ref = np.zeros((Bsz, L, D))
+    for b in range(Bsz):
+        for t in range(L):
+            for d in range(D):
+                drive = Bm[b, t, :] * x[b, t, d]
+                a = A[d, :]
+                sol = scipy.integrate.solve_ivp(lambda s, hh: a * hh + drive, (0.0, dt[b, t, d]),
+                                                h[b, d, :], method="DOP853", rtol=1e-13, atol=1e-15)
+                h[b, d, :] = sol.y[:, -1]
+                out = float(Cm[b, t, :] @ h[b, d, :])
+                if case["Dskip"] is not None:
+                    out += case["Dskip"][d] * x[b, t, d]
+                if case["z"] is not None:
+                    zz = case["z"][b, t, d]
+                    out *= zz * scipy.special.expit(zz)
+                y_ref[b, t, d] = out
+    y, h_last = scan(**case)
+    return max(rel_err(y, y_ref), rel_err(h_last, h))
+
+
+def _zoh_pair_expm(dt, a_vec, b_vec):
+    """Abar, Bbar for diagonal A from the matrix exponential of [[dt A, dt B], [0, 0]]
+    (Van Loan's block form of the zero-order hold), via scipy.linalg.expm."""
+    N = len(a_vec)
+    M = np.zeros((N + 1, N + 1))
+    M[:N, :N] = dt * np.diag(a_vec)
+    M[:N, N] = dt * b_vec
+    E = scipy.linalg.expm(M)
+    return np.diag(E[:N, :N]).copy(), E[:N, N].copy()
+
+
+def check_lti_convolution(scan, seed=1, L=24, D=3, N=5):
+    """[MS] 'every step the same': with Delta, B, C constant the output is the convolution of x
+    with the kernel K_k = sum_n C_n Abar_n^k Bbar_n (plus D x), computed by O(L^2) brute force
+    with Abar, Bbar from the matrix exponential."""
+    g = RNG(seed)
+    A = -g.uniform(0.1, 2.0, (D, N))
+    dts = g.uniform(0.05, 0.6, D)
+    Bc = g.standard_normal(N)
+    Cc = g.standard_normal(N)
+    x = g.standard_normal((1, L, D))
+    Dp = g.standard_normal(D)
+    delta = np.broadcast_to(dts[None, None, :], (1, L, D)).copy()
+    Bm = np.broadcast_to(Bc[None, None, :], (1, L, N)).copy()
+    Cm = np.broadcast_to(Cc[None, None, :], (1, L, N)).copy()
+    y_ref = np.zeros((1, L, D))
+    for d in range(D):
+        Ab, Bb = _zoh_pair_expm(dts[d], A[d], Bc)
+        K = np.array([np.sum(Cc * Ab ** k * Bb) for k in range(L)])
+        for t in range(L):
+            y_ref[0, t, d] = sum(K[k] * x[0, t - k, d] for k in range(t + 1)) + Dp[d] * x[0, t, d]
+    y, _ = scan(x=x, delta=delta, A=A, Bm=Bm, Cm=Cm, Dskip=Dp)
+    return rel_err(y, y_ref)
+
+
+def check_theorem1_gate(scan, seed=2, L=50):
+    """[MS] Theorem 1: one state, A = -1, B = C = 1, softplus step size: the update is the RNN gate
+    h <- (1 - g) h + g x with g = sigmoid(delta)."""
+    g = RNG(seed)
+    x = g.standard_normal((1, L, 1))
+    delta = g.standard_normal((1, L, 1)) * 2.0
+    ones = np.ones((1, L, 1))
+    y, _ = scan(x=x, delta=delta, A=-np.ones((1, 1)), Bm=ones, Cm=ones, delta_softplus=True)
+    h = 0.0
+    ref = np.zeros(L)
+    for t in range(L):
+        gt = scipy.special.expit(delta[0, t, 0])
+        h = (1.0 - gt) * h + gt * x[0, t, 0]
+        ref[t] = h
+    return rel_err(y[0, :, 0], ref)
+
+
+def check_zero_input_decay(scan, seed=3, L=40, D=3, N=6):
+    """With x = 0 the state only decays: h_t = exp(A * sum_{s<=t} Delta_s) h0 and y_t = C_t . h_t."""
+    g = RNG(seed)
+    A = -g.uniform(0.1, 4.0, (D, N))
+    delta = g.uniform(0.01, 0.3, (2, L, D))
+    Cm = g.standard_normal((2, L, N))
+    h0 = g.standard_normal((2, D, N))
+    y, h_last = scan(x=np.zeros((2, L, D)), delta=delta, A=A, Bm=g.standard_normal((2, L, N)),
+                     Cm=Cm, h0=h0)
+    S = np.cumsum(delta, axis=1)                        # [2, L, D]
+    h_t = np.exp(A[None, None] * S[..., None]) * h0[:, None]  # [2, L, D, N]
+    y_ref = np.einsum("bln,bldn->bld", Cm, h_t)
+    return max(rel_err(y, y_ref), rel_err(h_last, h_t[:, -1]))
+
+
+def check_delta_limits(scan, seed=4, L=12, D=2, N=5):
+    """[MS] Delta large resets the state to the current input: h_t = -B_t x_t / A.
+    Delta tiny keeps the state: h_t = h0."""
+    g = RNG(seed)
+    A = -g.uniform(0.5, 3.0, (D, N))
+    x = g.standard_normal((1, L, D))
+    Bm = g.standard_normal((1, L, N))
+    Cm = g.standard_normal((1, L, N))
+    h0 = g.standard_normal((1, D, N))
+    _, hl = scan(x=x, delta=np.full((1, L, D), 1e3), A=A, Bm=Bm, Cm=Cm, h0=h0)
+    reset_ref = -Bm[0, -1][None, :] * x[0, -1][:, None] / A
+    e1 = rel_err(hl[0], reset_ref)
+    y2, hl2 = scan(x=x, delta=np.full((1, L, D), 1e-15), A=A, Bm=Bm, Cm=Cm, h0=h0)
+    e2 = rel_err(hl2, h0)
+    y2_ref = np.einsum("ln,dn->ld", Cm[0], h0[0])[None]
+    return max(e1, e2, rel_err(y2, y2_ref))
+
+
+def check_fixed_point(scan, seed=5, L=30, D=3, N=4):
+    """Zero-order hold is exact for constant input: with x_t = x0, B_t = B0 and random Delta_t,
+    the state h0 = -B0 x0 / A (the equilibrium of h' = A h + B x) never moves."""
+    g = RNG(seed)
+    A = -g.uniform(0.2, 5.0, (D, N))
+    x0 = g.standard_normal(D)
+    B0 = g.standard_normal(N)
+    h0 = -(B0[None, :] * x0[:, None]) / A
+    x = np.broadcast_to(x0[None, None, :], (1, L, D)).copy()
+    Bm = np.broadcast_to(B0[None, None, :], (1, L, N)).copy()
+    _, hl = scan(x=x, delta=g.uniform(0.001, 2.0, (1, L, D)), A=A, Bm=Bm,
+                 Cm=g.standard_normal((1, L, N)), h0=h0[None])
+    return rel_err(hl[0], h0)
+
+
+def check_split_handoff(scan, seed=6, L=33, L1=14):
+    """The state is the whole context: scanning L tokens equals scanning L1 tokens and then the
+    remaining ones from the carried state."""
+    c = tiny_scan_case(seed, L=L)
+    y, hl = scan(**c)
+    first = {k: (v[:, :L1] if k in ("x", "delta", "Bm", "Cm", "z") and v is not None else v)
+             for k, v in c.items()}
+    y1, h1 = scan(**first)
+    second = {k: (v[:, L1:] if k in ("x", "delta", "Bm", "Cm", "z") and v is not None else v)
+              for k, v in c.items()}
+    second["h0"] = h1
+    y2, h2 = scan(**second)
+    return max(rel_err(np.concatenate([y1, y2], axis=1), y), rel_err(h2, hl))
+
+
+def check_linearity_causality(scan, seed=7, L=20):
+    """Before the gate the layer is linear in (x, h0) and causal."""
+    c1 = tiny_scan_case(seed, L=L, gate=False)
+    c2 = tiny_scan_case(seed + 100, L=L, gate=False)
+    c2.update({k: c1[k] for k in ("delta", "A", "Bm", "Cm", "delta_bias", "Dskip")})
+    a, b = 0.7, -1.3
+    c3 = dict(c1)
+    c3["x"] = a * c1["x"] + b * c2["x"]
+    c3["h0"] = a * c1["h0"] + b * c2["h0"]
+    y1, _ = scan(**c1)
+    y2, _ = scan(**c2)
+    y3, _ = scan(**c3)
+    e_lin = rel_err(y3, a * y1 + b * y2)
+    c4 = dict(c1)
+    c4["x"] = c1["x"].copy()
+    t0 = L // 2
+    c4["x"][:, t0:] += 5.0
+    y4, _ = scan(**c4)
+    e_causal = rel_err(y4[:, :t0], y1[:, :t0])
+    return max(e_lin, e_causal)
+
+
+def check_gate_and_skip(scan, seed=8):
+    """D adds D * x to each output; the gate multiplies the output by z * sigmoid(z)."""
+    c = tiny_scan_case(seed, gate=False, dskip=False)
+    y0, _ = scan(**c)
+    cd = dict(c)
+    cd["Dskip"] = RNG(seed + 1).standard_normal(c["x"].shape[2])
+    yd, _ = scan(**cd)
+    e1 = rel_err(yd - y0, cd["Dskip"][None, None, :] * c["x"])
+    cz = dict(cd)
+    cz["z"] = RNG(seed + 2).standard_normal(c["x"].shape) * 2.0
+    yz, _ = scan(**cz)
+    e2 = rel_err(yz, yd * cz["z"] * scipy.special.expit(cz["z"]))
+    return max(e1, e2)
+
+
+SCAN_CHECKS = [
+    ("ode_zoh", lambda s: max(check_ode(s, tiny_scan_case(11)),
+                              check_ode(s, tiny_scan_case(12, softplus=False, h0=False)))),
+    ("lti_convolution", check_lti_convolution),
+    ("theorem1_gate", check_theorem1_gate),
+    ("zero_input_decay", check_zero_input_decay),
+    ("delta_limits", check_delta_limits),
+    ("fixed_point", check_fixed_point),
+    ("split_handoff", check_split_handoff),
+    ("linearity_causality", check_linearity_causality),
+    ("gate_and_skip", check_gate_and_skip),
+]
+SCAN_TOL = {"ode_zoh": 1e-9}
+DEFAULT_TOL = 1e-11
+
+
+# ----------------------------------------------------------------------------- decode step
+def check_step_equals_scan(step, scan, seed=20, L=9):
+    """Without the conv register, L decode steps equal one scan over the L tokens."""
+    c = tiny_scan_case(seed, L=L)
+    y_scan, h_scan = scan(**c)
+    h = c["h0"].copy()
+    ys = []
+    for t in range(L):
+        y, h, _ = step(x=c["x"][:, t], delta=c["delta"][:, t], A=c["A"], Bm=c["Bm"][:, t],
+                       Cm=c["Cm"][:, t], h=h, delta_bias=c["delta_bias"],
+                       delta_softplus=c["delta_softplus"], Dskip=c["Dskip"], z=c["z"][:, t])
+        ys.append(y)
+    return max(rel_err(np.stack(ys, axis=1), y_scan), rel_err(h, h_scan))
+
+
+def check_step_conv(step, scan, seed=21, L=11, W=4):
+    """[MS] the decode state keeps the last 4 inputs: after each step the register holds the last W
+    raw inputs, and the outputs equal a scan over the causal depthwise convolution of the raw
+    inputs (numpy.convolve, zero history), with the convolution output as the SSM input."""
+    c = tiny_scan_case(seed, L=L, h0=False)
+    Bsz, _, D = c["x"].shape
+    g = RNG(seed + 1)
+    w = g.standard_normal((D, W))
+    cb = g.standard_normal(D)
+    u = np.zeros_like(c["x"])
+    for b in range(Bsz):
+        for d in range(D):
+            # causal conv: u_t = sum_k w[d, W-1-k] x_{t-k}; numpy.convolve flips its second operand
+            u[b, :, d] = np.convolve(c["x"][b, :, d], w[d, ::-1])[:L] + cb[d]
+    cu = dict(c)
+    cu["x"] = u
+    y_ref, h_ref = scan(**cu)
+    h = np.zeros((Bsz, D, c["A"].shape[1]))
+    reg = np.zeros((Bsz, D, W))
+    ys = []
+    e_reg = 0.0
+    for t in range(L):
+        y, h, reg = step(x=c["x"][:, t], delta=c["delta"][:, t], A=c["A"], Bm=c["Bm"][:, t],
+                         Cm=c["Cm"][:, t], h=h, delta_bias=c["delta_bias"],
+                         delta_softplus=c["delta_softplus"], Dskip=c["Dskip"], z=c["z"][:, t],
+                         conv_state=reg, conv_w=w, conv_b=cb)
+        ys.append(y)
+        hist = np.zeros((Bsz, D, W))
+        for k in range(W):
+            src = t - (W - 1) + k
+            if src >= 0:
+                hist[:, :, k] = c["x"][:, src]
+        e_reg = max(e_reg, float(np.max(np.abs(reg - hist))))
+    return max(rel_err(np.stack(ys, axis=1), y_ref), rel_err(h, h_ref), e_reg)
+
+
+# ----------------------------------------------------------------------------- SSD
+def tiny_ssd_case(seed, Bsz=2, L=20, H=2, P=3, N=4, gate=True, dskip=True, softplus=True):
+    g = RNG(seed)
+    return dict(
+        x=g.standard_normal((Bsz, L, H, P)),
+        delta=g.standard_normal((Bsz, L, H)) * 0.6,
+        A=-g.uniform(0.3, 4.0, H),
+        Bm=g.standard_normal((Bsz, L, N)),
+        Cm=g.standard_normal((Bsz, L, N)),
+        delta_bias=g.standard_normal(H) * 0.2,
+        delta_softplus=softplus,
+        Dskip=g.standard_normal(H) if dskip else None,
+        z=g.standard_normal((Bsz, L, H, P)) if gate else None,
+    )
+
+
+def check_ssd_quadratic(ssd, ssd_quadratic, seed=30):
+    """[MS] Mamba-2: the recurrence equals multiplication by the lower-triangular matrix."""
+    e = 0.0
+    for s, kw in ((seed, {}), (seed + 1, dict(gate=False, dskip=False, L=33, N=6, P=2))):
+        c = tiny_ssd_case(s, **kw)
+        y, _ = ssd(**c)
+        e = max(e, rel_err(y, ssd_quadratic(**c)))
+    return e
+
+
+def check_ssd_equals_scan(ssd, scan, seed=31):
+    """[MS] Mamba-2 restricts A to a scalar times the identity: the SSD layer equals the selective
+    scan with A[d, n] = A_h and Delta[b, t, d] = Delta[b, t, h] for every channel d = (h, p)."""
+    c = tiny_ssd_case(seed)
+    Bsz, L, H, P = c["x"].shape
+    N = c["Bm"].shape[2]
+    g = RNG(seed + 5)
+    h0 = g.standard_normal((Bsz, H, P, N))
+    y, hl = ssd(h0=h0, **c)
+    sc = dict(
+        x=c["x"].reshape(Bsz, L, H * P),
+        delta=np.repeat(c["delta"], P, axis=2),
+        A=np.repeat(c["A"], P)[:, None] * np.ones((1, N)),
+        Bm=c["Bm"], Cm=c["Cm"],
+        delta_bias=np.repeat(c["delta_bias"], P),
+        delta_softplus=c["delta_softplus"],
+        Dskip=np.repeat(c["Dskip"], P),
+        z=c["z"].reshape(Bsz, L, H * P),
+        h0=h0.reshape(Bsz, H * P, N),
+    )
+    ys, hs = scan(**sc)
+    return max(rel_err(y.reshape(Bsz, L, H * P), ys), rel_err(hl.reshape(Bsz, H * P, N), hs))

@@ -1,0 +1,152 @@
+"""The fp64 oracle against what the pages and mathematics fix (CPU only).
+
+Each pin is described in ``tests/pins.py``. The mutation suite compiles copies of ``oracle.c``
+with one plausible mistake planted in each (a dropped term, a wrong sign, index or operand,
+the Euler shortcut the ai-lab.club page's simplified code uses) and requires that every mutant
+fails at least one pin -- evidence that the pins would catch such a mistake in the oracle.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from selective_state_space_37_amd import inputs
+from tests import pins
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.mark.parametrize("name,check", pins.SCAN_CHECKS, ids=[n for n, _ in pins.SCAN_CHECKS])
+def test_scan_pin(name, check):
+    err = check(oracle.scan)
+    assert err <= pins.SCAN_TOL.get(name, pins.DEFAULT_TOL), (name, err)
+
+
+def test_step_equals_scan():
+    assert pins.check_step_equals_scan(oracle.step, oracle.scan) <= 1e-12
+
+
+def test_step_conv_register():
+    assert pins.check_step_conv(oracle.step, oracle.scan) <= 1e-12
+
+
+def test_ssd_matrix_form():
+    assert pins.check_ssd_quadratic(oracle.ssd, oracle.ssd_quadratic) <= 1e-12
+
+
+def test_ssd_equals_scan():
+    assert pins.check_ssd_equals_scan(oracle.ssd, oracle.scan) <= 1e-12
+
+
+def test_ssd_quadratic_matches_recurrence_long():
+    """The matrix form and the recurrence agree over a chunk-sized length (64 tokens)."""
+    c = pins.tiny_ssd_case(40, Bsz=1, L=64, H=1, P=2, N=3)
+    y, _ = oracle.ssd(**c)
+    assert pins.rel_err(y, oracle.ssd_quadratic(**c)) <= 1e-12
+
+
+def test_state_sizing_golden():
+    """Page numbers for the decode state: N=16 states plus the 4 conv inputs per channel."""
+    g = json.load(open(os.path.join(GOLDEN, "state_sizing.json")))
+    m = g["mamba_2p8b"]
+    numbers = m["layers"] * m["channels_per_layer"] * (m["ssm_state_per_channel"] + m["conv_inputs_kept"])
+    assert numbers == m["state_numbers"] == 6_553_600
+    assert round(numbers * 2 / 1e6, 1) == m["state_megabytes_16bit"]
+    p = g["pythia_2p8b"]
+    per_tok = 2 * p["layers"] * p["key_or_value_numbers_per_layer"] * p["bytes_per_number"]
+    assert per_tok == p["bytes_per_token"]
+    assert round(per_tok * p["tokens"] / 1e6) == p["cache_megabytes"]
+    assert int(per_tok * p["tokens"] / (numbers * 2)) == p["ratio_to_mamba_state_at_2048"]
+    k = p["cache_passes_mamba_state_at_token"]
+    assert per_tok * k >= numbers * 2 > per_tok * (k - 1)
+    a = g["A_initialisation"]
+    A = inputs.structured_A(3, a["states"])
+    assert A[0, 0] == a["first"] and A[0, -1] == a["last"]
+
+
+# ----------------------------------------------------------------------------- mutation suite
+SCAN_MUTANTS = {
+    "euler_input_scale": [("o_zoh_scale(dt, a) * Bt[n]", "dt * Bt[n]")],
+    "dropped_D_term": [("if (Dskip) out += Dskip[d] * xt;", "")],
+    "stale_B_index": [("const double* Bt = Bm + (b * L + t) * N;",
+                       "const double* Bt = Bm + (b * L + (t > 0 ? t - 1 : 0)) * N;")],
+    "readout_before_update": [("h[n] = abar * h[n] + bbar * xt;\n          out += Ct[n] * h[n];",
+                               "out += Ct[n] * h[n];\n          h[n] = abar * h[n] + bbar * xt;")],
+    "decay_sign": [("const double abar = exp(dt * a);", "const double abar = exp(-dt * a);")],
+    "transposed_A": [("const double a = A[d * N + n];\n          const double abar",
+                      "const double a = A[n * D + d];\n          const double abar")],
+    "gate_before_D": [("if (Dskip) out += Dskip[d] * xt;\n        if (z) out *= z[io] * o_sigmoid(z[io]);",
+                       "if (z) out *= z[io] * o_sigmoid(z[io]);\n        if (Dskip) out += Dskip[d] * xt;")],
+    "bias_ignored": [("double u = delta + (delta_bias ? delta_bias[idx] : 0.0);", "double u = delta;")],
+    "B_C_swapped": [("const double* Ct = Cm + (b * L + t) * N;", "const double* Ct = Bm + (b * L + t) * N;")],
+    "sigmoid_sign": [("if (z) out *= z[io] * o_sigmoid(z[io]);", "if (z) out *= z[io] * o_sigmoid(-z[io]);")],
+    "softplus_truncated": [("return u > 0.0 ? u + log1p(exp(-u)) : log1p(exp(u));",
+                            "return u > 0.0 ? u : log1p(exp(u));")],
+    "h0_ignored": [("h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;", "h[n] = 0.0;")],
+    "zoh_limit_zero": [("return a == 0.0 ? dt : expm1(dt * a) / a;", "return a == 0.0 ? 0.0 : expm1(dt * a) / a;")],
+    "h_last_reversed": [("h_last[(b * D + d) * N + n] = h[n];", "h_last[(b * D + d) * N + (N - 1 - n)] = h[n];")],
+    "x_from_next_channel": [("const double xt = x[io];", "const double xt = x[(b * L + t) * D + (d + 1) % D];")],
+}
+
+STEP_MUTANTS = {
+    "conv_shift_wrong_way": [("for (int64_t k = 0; k + 1 < W; ++k) reg[k] = reg[k + 1];\n        reg[W - 1] = x[io];",
+                              "for (int64_t k = W - 1; k > 0; --k) reg[k] = reg[k - 1];\n        reg[0] = x[io];")],
+    "conv_weights_reversed": [("u += conv_w[d * W + k] * reg[k];", "u += conv_w[d * W + (W - 1 - k)] * reg[k];")],
+    "conv_bias_dropped": [("u = conv_b ? conv_b[d] : 0.0;", "u = 0.0;")],
+    "step_D_uses_raw_x": [("if (Dskip) out += Dskip[d] * u;", "if (Dskip) out += Dskip[d] * x[io];")],
+    "step_euler": [("hs[n] = exp(dt * a) * hs[n] + o_zoh_scale(dt, a) * Bm[b * N + n] * u;",
+                    "hs[n] = exp(dt * a) * hs[n] + dt * Bm[b * N + n] * u;")],
+}
+
+SSD_MUTANTS = {
+    "ssd_euler": [("const double phi = o_zoh_scale(dt, a);", "const double phi = dt;")],
+    "ssd_readout_B": [("out += Ct[n] * S[p * N + n];", "out += Bt[n] * S[p * N + n];")],
+    "ssd_x_index": [("phi * xt[p] * Bt[n];", "phi * xt[0] * Bt[n];")],
+    "ssd_D_head": [("if (Dskip) out += Dskip[hd] * xt[p];", "if (Dskip) out += Dskip[0] * xt[p];")],
+    "ssd_delta_head": [("delta[(b * L + t) * H + hd]", "delta[(b * L + t) * H]")],
+}
+
+
+def _mutant(tmp_path, name, edits):
+    src = oracle.source_text()
+    for old, new in edits:
+        assert old in src, "mutation anchor not found: %r" % old
+        src = src.replace(old, new)
+    so = oracle.compile_source(src, str(tmp_path / ("mut_%s.so" % name)))
+    return oracle.Variant(so)
+
+
+def _scan_pins_fail(v):
+    import warnings
+    failed = []
+    for name, check in pins.SCAN_CHECKS:
+        with warnings.catch_warnings():
+            warnings.simplefilter("ignore")
+            with np.errstate(all="ignore"):
+                err = check(v.scan)
+        if not (err <= pins.SCAN_TOL.get(name, pins.DEFAULT_TOL)):
+            failed.append(name)
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(SCAN_MUTANTS))
+def test_scan_mutant_caught(tmp_path, name):
+    v = _mutant(tmp_path, name, SCAN_MUTANTS[name])
+    failed = _scan_pins_fail(v)
+    assert failed, "planted mistake %s passed every scan pin" % name
+
+
+@pytest.mark.parametrize("name", sorted(STEP_MUTANTS))
+def test_step_mutant_caught(tmp_path, name):
+    v = _mutant(tmp_path, name, STEP_MUTANTS[name])
+    errs = [pins.check_step_equals_scan(v.step, oracle.scan), pins.check_step_conv(v.step, oracle.scan)]
+    assert max(errs) > 1e-12, name
+
+
+@pytest.mark.parametrize("name", sorted(SSD_MUTANTS))
+def test_ssd_mutant_caught(tmp_path, name):
+    v = _mutant(tmp_path, name, SSD_MUTANTS[name])
+    errs = [pins.check_ssd_quadratic(v.ssd, oracle.ssd_quadratic), pins.check_ssd_equals_scan(v.ssd, oracle.scan)]
+    assert max(errs) > 1e-12, name

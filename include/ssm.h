@@ -1,0 +1,179 @@
+/*
+ * ssm.h -- C ABI of libssm: the selective state-space (S6) forward pass on MI355X (gfx950).
+ *
+ * Three operations, as the Mamba pages state them:
+ *
+ *   ssm_scan_fwd      The selective scan. Page "Beyond attention: exploring Mamba and state
+ *                     space models" (ai-lab.club), state-space basics section: zero-order-hold
+ *                     discretisation Abar = exp(Delta A), Bbar = (Delta A)^-1 (exp(Delta A) - I)
+ *                     Delta B, recurrence h_t = Abar h_{t-1} + Bbar x_t, readout
+ *                     y_t = C h_t + D x_t; selective-SSM section: Delta_t = softplus(. + b),
+ *                     B_t and C_t per token. Page "Mamba and state space models"
+ *                     (world.lapla.si), section "scan on the chip": the expanded state is never
+ *                     written out; only y (and, here, the final state) leave the chip.
+ *   ssm_state_update  One generated token with constant work: same page, section "fixed-size
+ *                     state" -- per channel the N-number SSM state plus a short convolution
+ *                     that keeps the last few (4) inputs.
+ *   ssd_chunk_fwd     Mamba-2 with A a scalar times the identity per head: same page, section
+ *                     "Mamba-2: two algorithms" -- the layer is a lower-triangular matrix
+ *                     (C_i . B_j times all decay between steps j and i); the sequence is cut
+ *                     into chunks, each chunk is a masked matrix product, and only the state
+ *                     passes between chunks.
+ *
+ * Conventions shared by every entry point
+ *   - Sizes are int64_t. Tensors are dense, row-major, contiguous; no strides.
+ *   - Tensor pointers are DEVICE pointers (memory the caller allocated on the current HIP
+ *     device). The library never allocates, frees or keeps them. Scratch space, when an
+ *     operation needs it, is a caller-provided device workspace whose size the matching
+ *     *_workspace_bytes query returns.
+ *   - io_dtype selects the storage type of the per-token tensors (x, delta, z, B, C, y and the
+ *     decode conv register): SSM_F32 (float) or SSM_BF16 (bfloat16 bits). Parameters (A,
+ *     delta_bias, D, conv weights) and states (h0, h_last, h) are always float32.
+ *     All arithmetic is float32; bf16 results are rounded to nearest-even.
+ *   - stream is a hipStream_t (NULL = the null stream). Calls only enqueue work; a device
+ *     fault surfaces at the caller's next synchronisation.
+ *   - Every argument is validated on the host before anything is enqueued; no call
+ *     synchronises the device. A failed call returns a non-zero ssm_status, enqueues nothing
+ *     and leaves the text in ssm_last_error_detail() (per thread).
+ *   - Per-token pointers (x, delta, z, y, B, C) and the conv register must be 16-byte aligned.
+ *   - A must be strictly negative (the decaying diagonal the pages use; A = 0 is the
+ *     Delta * B limit, which the kernels do not special-case: it gives NaN).
+ */
+#ifndef SSM_H_
+#define SSM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+typedef enum ssm_status {
+  SSM_OK = 0,
+  SSM_ERR_INVALID_ARGUMENT = 1,   /* NULL required pointer, bad size, misalignment, aliasing */
+  SSM_ERR_UNSUPPORTED = 2,        /* valid but not implemented: N, P, chunk, dtype combination */
+  SSM_ERR_WORKSPACE_TOO_SMALL = 3,
+  SSM_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+} ssm_status;
+
+typedef enum ssm_dtype { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
+
+/* SSM_ABI_VERSION of the built library. */
+int ssm_abi_version(void);
+
+/* Static text for a status code ("SSM_OK", ...). Never NULL. */
+const char* ssm_status_string(ssm_status status);
+
+/* Detail of the last failed call on this thread ("" if none). Valid until the next call. */
+const char* ssm_last_error_detail(void);
+
+/*
+ * ssm_scan_fwd -- selective scan over L tokens for B sequences of D channels, N states each.
+ *
+ *   x, delta, z, y : [B, L, D]  io_dtype     (channels innermost)
+ *   Bm, Cm         : [B, L, N]  io_dtype     (one N-vector per token, shared by all channels)
+ *   A              : [D, N]     float32      (< 0)
+ *   delta_bias     : [D]        float32 or NULL (0)
+ *   Dskip          : [D]        float32 or NULL (no D x term)
+ *   h0             : [B, D, N]  float32 or NULL (zero initial state)
+ *   h_last         : [B, D, N]  float32 or NULL (final state not returned); may equal h0
+ *   z              : NULL, or the gate input: y <- y * z * sigmoid(z) after the D term
+ *
+ *   Per (b, t, d): Delta = delta + delta_bias[d], then softplus(Delta) if delta_softplus != 0;
+ *   for each n: Abar = exp(Delta A[d,n]), h[n] = Abar h[n] + expm1(Delta A[d,n]) / A[d,n]
+ *   * Bm[b,t,n] * x[b,t,d]; y = sum_n Cm[b,t,n] h[n] + Dskip[d] x[b,t,d]; gate.
+ *
+ *   Requirements: B, L >= 0 (B == 0 or L == 0 is a no-op, except that with L == 0 h_last
+ *   receives h0 or zeros); D >= 1 and D % 4 == 0; N in {1, 2, 4, 8, 16} (else
+ *   SSM_ERR_UNSUPPORTED); y must not overlap any input. workspace may be NULL when
+ *   ssm_scan_fwd_workspace_bytes() returns 0.
+ *
+ *   Long, narrow inputs are split along L into segments whose carries are combined by a
+ *   separate pass; that plan needs the workspace. The result does not depend on the plan
+ *   beyond float32 rounding.
+ */
+size_t ssm_scan_fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io_dtype);
+
+ssm_status ssm_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io_dtype,
+                        const void* x, const void* delta, const float* delta_bias, int delta_softplus,
+                        const float* A, const void* Bm, const void* Cm, const float* Dskip,
+                        const void* z, const float* h0, void* y, float* h_last,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ssm_scan_fwd_segmented -- ssm_scan_fwd with an explicit segment length along L
+ * (segment_len >= 1; segment_len >= L means one segment). The workspace size for it is
+ * ssm_scan_fwd_segmented_workspace_bytes(). Used to check that results do not depend on the
+ * split (the pages: only state passes between chunks).
+ */
+size_t ssm_scan_fwd_segmented_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
+                                              int64_t segment_len);
+
+ssm_status ssm_scan_fwd_segmented(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io_dtype,
+                                  const void* x, const void* delta, const float* delta_bias,
+                                  int delta_softplus, const float* A, const void* Bm, const void* Cm,
+                                  const float* Dskip, const void* z, const float* h0, void* y,
+                                  float* h_last, int64_t segment_len,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ssm_state_update -- one decode token for B sequences of D channels (N states each).
+ *
+ *   x, delta, z, y : [B, D]      io_dtype
+ *   Bm, Cm         : [B, N]      io_dtype
+ *   A              : [D, N]      float32 (< 0)
+ *   delta_bias     : [D] float32 or NULL;  Dskip : [D] float32 or NULL;  z : [B, D] or NULL
+ *   h              : [B, D, N]   float32, read and overwritten with the new state
+ *   conv_state     : [B, D, W]   io_dtype, oldest input first, read and overwritten; or NULL
+ *   conv_w         : [D, W]      float32 (conv_w[d, W-1] multiplies the newest input)
+ *   conv_b         : [D]         float32 or NULL
+ *
+ *   With conv_state: the register shifts by one, x enters as the newest entry, and the SSM
+ *   input of the channel is u = sum_k conv_w[d,k] * register[k] + conv_b[d] (no activation);
+ *   without it, u = x. Then the scan step on u (u is also the input of the D term), then gate.
+ *
+ *   Requirements: B >= 0 (0 is a no-op), D >= 1, N in {1, 2, 4, 8, 16}, 1 <= W <= 8 when
+ *   conv_state is given (conv_width is ignored otherwise); y must not overlap any input.
+ */
+ssm_status ssm_state_update(int64_t B, int64_t D, int64_t N, int64_t conv_width, ssm_dtype io_dtype,
+                            const void* x, const void* delta, const float* delta_bias,
+                            int delta_softplus, const float* A, const void* Bm, const void* Cm,
+                            const float* Dskip, const void* z, void* conv_state,
+                            const float* conv_w, const float* conv_b, float* h, void* y,
+                            void* stream);
+
+/*
+ * ssd_chunk_fwd -- Mamba-2 layer: H heads of P channels, one scalar A per head, N states.
+ *
+ *   x, z, y        : [B, L, H, P]   io_dtype
+ *   delta          : [B, L, H]      io_dtype (one step size per token and head)
+ *   Bm, Cm         : [B, L, N]      io_dtype (shared by all heads)
+ *   A              : [H] float32 (< 0);  delta_bias, Dskip : [H] float32 or NULL
+ *   h0, h_last     : [B, H, P, N] float32 or NULL; h_last may equal h0
+ *
+ *   Result: per head the plain recurrence S <- exp(Delta a) S + expm1(Delta a)/a x B^T,
+ *   y = S C (+ D x, gate), computed chunk by chunk: within a chunk the masked matrix
+ *   (C_i . B_j) exp(a (cumsum Delta_i - cumsum Delta_j)) expm1(a Delta_j)/a on the matrix
+ *   cores (bf16 operands, float32 accumulation); between chunks the float32 state.
+ *
+ *   Requirements: io_dtype SSM_BF16; P == 64; N in {64, 128}; chunk in {64, 128, 256};
+ *   B, L >= 0 (0 is a no-op; with L == 0 h_last receives h0 or zeros); H >= 1.
+ */
+size_t ssd_chunk_fwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N,
+                                     int64_t chunk, ssm_dtype io_dtype);
+
+ssm_status ssd_chunk_fwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t chunk,
+                         ssm_dtype io_dtype, const void* x, const void* delta,
+                         const float* delta_bias, int delta_softplus, const float* A,
+                         const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                         const float* h0, void* y, float* h_last, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_H_ */

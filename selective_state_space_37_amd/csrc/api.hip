@@ -1,0 +1,260 @@
+// C ABI of libssm: argument validation on the host, plan selection, kernel launches.
+// Every check runs before anything is enqueued and without touching the device, so invalid
+// calls fail the same way on a machine with no GPU.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/ssm.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_detail;
+
+ssm_status fail(ssm_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return s;
+}
+
+ssm_status ok() {
+  g_detail.clear();
+  return SSM_OK;
+}
+
+ssm_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SSM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t io_size(ssm_dtype t) { return t == SSM_BF16 ? 2 : 4; }
+
+bool valid_dtype(ssm_dtype t) { return t == SSM_F32 || t == SSM_BF16; }
+
+// [p, p + bytes) overlaps [q, q + qbytes)?
+bool overlaps(const void* p, size_t bytes, const void* q, size_t qbytes) {
+  if (!p || !q || bytes == 0 || qbytes == 0) return false;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + qbytes && b < a + bytes;
+}
+
+bool supported_scan_n(int64_t N) { return N == 1 || N == 2 || N == 4 || N == 8 || N == 16; }
+
+// The library targets MI355X (256 compute units); the plan depends only on the shapes, so the
+// workspace query needs no device.
+constexpr int64_t kPlanCUs = 256;
+constexpr int64_t kTile = 16;         // tokens per LDS tile of the scan kernels
+constexpr int64_t kMinSegment = 256;  // shortest automatic segment
+
+int64_t auto_segment_len(int64_t B, int64_t L, int64_t D) {
+  const int64_t wgs = ((D + 63) / 64) * B;
+  if (L <= kMinSegment || wgs >= 2 * kPlanCUs) return L;
+  int64_t nseg = (4 * kPlanCUs + wgs - 1) / wgs;
+  int64_t seg = (L + nseg - 1) / nseg;
+  seg = ((seg + kTile - 1) / kTile) * kTile;
+  if (seg < kMinSegment) seg = kMinSegment;
+  return seg >= L ? L : seg;
+}
+
+int64_t num_segments(int64_t L, int64_t seg_len) { return seg_len >= L ? 1 : (L + seg_len - 1) / seg_len; }
+
+ssm_status scan_common(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io, const void* x,
+                       const void* delta, const float* delta_bias, int delta_softplus, const float* A,
+                       const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
+                       void* y, float* h_last, int64_t seg_len, void* ws, size_t ws_bytes, void* stream) {
+  if (B < 0 || L < 0) return fail(SSM_ERR_INVALID_ARGUMENT, "B=%lld and L=%lld must be >= 0", (long long)B, (long long)L);
+  if (D < 1 || (D % 4) != 0) return fail(SSM_ERR_INVALID_ARGUMENT, "D=%lld must be >= 1 and a multiple of 4", (long long)D);
+  if (!valid_dtype(io)) return fail(SSM_ERR_INVALID_ARGUMENT, "unknown io_dtype %d", (int)io);
+  if (!supported_scan_n(N)) return fail(SSM_ERR_UNSUPPORTED, "N=%lld: supported state sizes are 1, 2, 4, 8, 16", (long long)N);
+  if (seg_len < 1) return fail(SSM_ERR_INVALID_ARGUMENT, "segment_len=%lld must be >= 1", (long long)seg_len);
+  if (B == 0) return ok();
+  if (!A) return fail(SSM_ERR_INVALID_ARGUMENT, "A is NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t stb = (size_t)(B * D * N) * sizeof(float);
+  if (h_last && h0 && h_last != h0 && overlaps(h_last, stb, h0, stb))
+    return fail(SSM_ERR_INVALID_ARGUMENT, "h_last partially overlaps h0 (it may only equal it)");
+  if (L == 0) {
+    if (!h_last || h_last == h0) return ok();
+    hipError_t e = h0 ? hipMemcpyAsync(h_last, h0, stb, hipMemcpyDeviceToDevice, st)
+                      : hipMemsetAsync(h_last, 0, stb, st);
+    return from_hip(e, "L == 0 state copy");
+  }
+  if (!x || !delta || !Bm || !Cm || !y)
+    return fail(SSM_ERR_INVALID_ARGUMENT, "x, delta, Bm, Cm and y must not be NULL");
+  if (!aligned16(x) || !aligned16(delta) || !aligned16(y) || (z && !aligned16(z)) || !aligned16(Bm) || !aligned16(Cm))
+    return fail(SSM_ERR_INVALID_ARGUMENT, "per-token tensors must be 16-byte aligned");
+  const size_t es = io_size(io);
+  const size_t tok = (size_t)(B * L * D) * es, bc = (size_t)(B * L * N) * es;
+  const void* ins[] = {x, delta, z, Bm, Cm, A, delta_bias, Dskip, h0};
+  const size_t insz[] = {tok, tok, tok, bc, bc, (size_t)(D * N) * 4, (size_t)D * 4, (size_t)D * 4, stb};
+  for (int k = 0; k < 9; ++k)
+    if (overlaps(y, tok, ins[k], insz[k])) return fail(SSM_ERR_INVALID_ARGUMENT, "y overlaps an input");
+  if (h_last && overlaps(h_last, stb, y, tok)) return fail(SSM_ERR_INVALID_ARGUMENT, "h_last overlaps y");
+
+  const int64_t nseg = num_segments(L, seg_len);
+  const size_t need = ssm::scan_workspace_bytes(B, D, N, nseg);
+  if (need > 0) {
+    if (!ws) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace is NULL; %zu bytes needed", need);
+    if (ws_bytes < need) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    if (!aligned16(ws)) return fail(SSM_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  }
+  ssm::ScanParams p{};
+  p.B = B; p.L = L; p.D = D; p.N = N;
+  p.io_bf16 = io == SSM_BF16;
+  p.x = x; p.delta = delta; p.z = z; p.Bm = Bm; p.Cm = Cm;
+  p.delta_bias = delta_bias; p.A = A; p.Dskip = Dskip; p.h0 = h0;
+  p.y = y; p.h_last = h_last; p.delta_softplus = delta_softplus ? 1 : 0;
+  p.nseg = nseg;
+  p.seg_len = nseg == 1 ? L : seg_len;
+  if (nseg > 1) {
+    p.ws_h = static_cast<float*>(ws);
+    p.ws_sum = p.ws_h + B * nseg * D * N;
+  }
+  return from_hip(ssm::launch_scan(p, st), "ssm_scan_fwd launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char* ssm_status_string(ssm_status s) {
+  switch (s) {
+    case SSM_OK: return "SSM_OK";
+    case SSM_ERR_INVALID_ARGUMENT: return "SSM_ERR_INVALID_ARGUMENT";
+    case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED";
+    case SSM_ERR_WORKSPACE_TOO_SMALL: return "SSM_ERR_WORKSPACE_TOO_SMALL";
+    case SSM_ERR_HIP: return "SSM_ERR_HIP";
+  }
+  return "SSM_ERR_UNKNOWN";
+}
+
+const char* ssm_last_error_detail(void) { return g_detail.c_str(); }
+
+size_t ssm_scan_fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype) {
+  if (B <= 0 || L <= 0 || D <= 0 || N <= 0) return 0;
+  return ssm::scan_workspace_bytes(B, D, N, num_segments(L, auto_segment_len(B, L, D)));
+}
+
+size_t ssm_scan_fwd_segmented_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int64_t segment_len) {
+  if (B <= 0 || L <= 0 || D <= 0 || N <= 0 || segment_len < 1) return 0;
+  return ssm::scan_workspace_bytes(B, D, N, num_segments(L, segment_len));
+}
+
+ssm_status ssm_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io, const void* x,
+                        const void* delta, const float* delta_bias, int delta_softplus, const float* A,
+                        const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
+                        void* y, float* h_last, void* ws, size_t ws_bytes, void* stream) {
+  const int64_t seg = (B > 0 && L > 0 && D > 0) ? auto_segment_len(B, L, D) : 1;
+  return scan_common(B, L, D, N, io, x, delta, delta_bias, delta_softplus, A, Bm, Cm, Dskip, z, h0, y,
+                     h_last, seg, ws, ws_bytes, stream);
+}
+
+ssm_status ssm_scan_fwd_segmented(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io, const void* x,
+                                  const void* delta, const float* delta_bias, int delta_softplus,
+                                  const float* A, const void* Bm, const void* Cm, const float* Dskip,
+                                  const void* z, const float* h0, void* y, float* h_last, int64_t segment_len,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  return scan_common(B, L, D, N, io, x, delta, delta_bias, delta_softplus, A, Bm, Cm, Dskip, z, h0, y,
+                     h_last, segment_len, ws, ws_bytes, stream);
+}
+
+ssm_status ssm_state_update(int64_t B, int64_t D, int64_t N, int64_t W, ssm_dtype io, const void* x,
+                            const void* delta, const float* delta_bias, int delta_softplus, const float* A,
+                            const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                            void* conv_state, const float* conv_w, const float* conv_b, float* h, void* y,
+                            void* stream) {
+  if (B < 0) return fail(SSM_ERR_INVALID_ARGUMENT, "B=%lld must be >= 0", (long long)B);
+  if (D < 1) return fail(SSM_ERR_INVALID_ARGUMENT, "D=%lld must be >= 1", (long long)D);
+  if (!valid_dtype(io)) return fail(SSM_ERR_INVALID_ARGUMENT, "unknown io_dtype %d", (int)io);
+  if (!supported_scan_n(N)) return fail(SSM_ERR_UNSUPPORTED, "N=%lld: supported state sizes are 1, 2, 4, 8, 16", (long long)N);
+  if (conv_state && (W < 1 || W > 8)) return fail(SSM_ERR_UNSUPPORTED, "conv_width=%lld: supported 1..8", (long long)W);
+  if (B == 0) return ok();
+  if (!x || !delta || !A || !Bm || !Cm || !h || !y)
+    return fail(SSM_ERR_INVALID_ARGUMENT, "x, delta, A, Bm, Cm, h and y must not be NULL");
+  if (conv_state && !conv_w) return fail(SSM_ERR_INVALID_ARGUMENT, "conv_w is NULL while conv_state is given");
+  if (!aligned16(h) || !aligned16(x) || !aligned16(y) || (conv_state && !aligned16(conv_state)))
+    return fail(SSM_ERR_INVALID_ARGUMENT, "h, x, y and conv_state must be 16-byte aligned");
+  const size_t es = io_size(io), tok = (size_t)(B * D) * es;
+  const size_t stb = (size_t)(B * D * N) * 4;
+  const void* ins[] = {x, delta, z, Bm, Cm, A, h, conv_state, conv_w};
+  const size_t insz[] = {tok, tok, tok, (size_t)(B * N) * es, (size_t)(B * N) * es, (size_t)(D * N) * 4, stb,
+                         (size_t)(B * D * (W > 0 ? W : 1)) * es, (size_t)(D * (W > 0 ? W : 1)) * 4};
+  for (int k = 0; k < 9; ++k)
+    if (overlaps(y, tok, ins[k], insz[k])) return fail(SSM_ERR_INVALID_ARGUMENT, "y overlaps an input");
+  ssm::StepParams p{};
+  p.B = B; p.D = D; p.N = N; p.W = conv_state ? W : 0;
+  p.io_bf16 = io == SSM_BF16;
+  p.x = x; p.delta = delta; p.z = z; p.Bm = Bm; p.Cm = Cm;
+  p.delta_bias = delta_bias; p.A = A; p.Dskip = Dskip;
+  p.conv_state = conv_state; p.conv_w = conv_w; p.conv_b = conv_b;
+  p.h = h; p.y = y; p.delta_softplus = delta_softplus ? 1 : 0;
+  return from_hip(ssm::launch_state_update(p, static_cast<hipStream_t>(stream)), "ssm_state_update launch");
+}
+
+size_t ssd_chunk_fwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t chunk,
+                                     ssm_dtype) {
+  if (B <= 0 || L <= 0 || H <= 0 || P <= 0 || N <= 0 || chunk <= 0) return 0;
+  return ssm::ssd_workspace_bytes(B, L, H, P, N, chunk);
+}
+
+ssm_status ssd_chunk_fwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t chunk, ssm_dtype io,
+                         const void* x, const void* delta, const float* delta_bias, int delta_softplus,
+                         const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                         const float* h0, void* y, float* h_last, void* ws, size_t ws_bytes, void* stream) {
+  if (B < 0 || L < 0) return fail(SSM_ERR_INVALID_ARGUMENT, "B and L must be >= 0");
+  if (H < 1) return fail(SSM_ERR_INVALID_ARGUMENT, "H=%lld must be >= 1", (long long)H);
+  if (!valid_dtype(io)) return fail(SSM_ERR_INVALID_ARGUMENT, "unknown io_dtype %d", (int)io);
+  if (io != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "ssd_chunk_fwd supports io_dtype SSM_BF16 only");
+  if (P != 64) return fail(SSM_ERR_UNSUPPORTED, "P=%lld: supported head dim is 64", (long long)P);
+  if (N != 64 && N != 128) return fail(SSM_ERR_UNSUPPORTED, "N=%lld: supported 64, 128", (long long)N);
+  if (chunk != 64 && chunk != 128 && chunk != 256)
+    return fail(SSM_ERR_UNSUPPORTED, "chunk=%lld: supported 64, 128, 256", (long long)chunk);
+  if (B == 0) return ok();
+  if (!A) return fail(SSM_ERR_INVALID_ARGUMENT, "A is NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t stb = (size_t)(B * H * P * N) * 4;
+  if (h_last && h0 && h_last != h0 && overlaps(h_last, stb, h0, stb))
+    return fail(SSM_ERR_INVALID_ARGUMENT, "h_last partially overlaps h0 (it may only equal it)");
+  if (L == 0) {
+    if (!h_last || h_last == h0) return ok();
+    hipError_t e = h0 ? hipMemcpyAsync(h_last, h0, stb, hipMemcpyDeviceToDevice, st) : hipMemsetAsync(h_last, 0, stb, st);
+    return from_hip(e, "L == 0 state copy");
+  }
+  if (!x || !delta || !Bm || !Cm || !y) return fail(SSM_ERR_INVALID_ARGUMENT, "x, delta, Bm, Cm and y must not be NULL");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(Bm) || !aligned16(Cm) || (z && !aligned16(z)))
+    return fail(SSM_ERR_INVALID_ARGUMENT, "per-token tensors must be 16-byte aligned");
+  const size_t tok = (size_t)(B * L * H * P) * 2;
+  const void* ins[] = {x, delta, z, Bm, Cm, A, h0};
+  const size_t insz[] = {tok, (size_t)(B * L * H) * 2, tok, (size_t)(B * L * N) * 2, (size_t)(B * L * N) * 2,
+                         (size_t)H * 4, stb};
+  for (int k = 0; k < 7; ++k)
+    if (overlaps(y, tok, ins[k], insz[k])) return fail(SSM_ERR_INVALID_ARGUMENT, "y overlaps an input");
+  const size_t need = ssm::ssd_workspace_bytes(B, L, H, P, N, chunk);
+  if (!ws) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace is NULL; %zu bytes needed", need);
+  if (ws_bytes < need) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (!aligned16(ws)) return fail(SSM_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  if (overlaps(ws, need, y, tok)) return fail(SSM_ERR_INVALID_ARGUMENT, "workspace overlaps y");
+  const int64_t nch = (L + chunk - 1) / chunk;
+  ssm::SsdParams p{};
+  p.B = B; p.L = L; p.H = H; p.P = P; p.N = N; p.Q = chunk;
+  p.x = x; p.delta = delta; p.z = z; p.Bm = Bm; p.Cm = Cm;
+  p.delta_bias = delta_bias; p.A = A; p.Dskip = Dskip; p.h0 = h0;
+  p.y = y; p.h_last = h_last; p.delta_softplus = delta_softplus ? 1 : 0;
+  p.ws_state = static_cast<float*>(ws);
+  p.ws_sum = p.ws_state + B * nch * H * P * N;
+  return from_hip(ssm::launch_ssd(p, st), "ssd_chunk_fwd launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Device helpers shared by the gfx950 kernels of libssm.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// bfloat16 storage: the 16 high bits of an IEEE float.
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bf16, round to nearest even (finite inputs; NaN stays NaN-like).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// Hardware base-2 exponential (v_exp_f32).
+__device__ __forceinline__ float exp2_fast(float v) { return __builtin_amdgcn_exp2f(v); }
+
+// Hardware reciprocal (v_rcp_f32, about 1 ulp).
+__device__ __forceinline__ float rcp_fast(float v) { return __builtin_amdgcn_rcpf(v); }
+
+// z * sigmoid(z) with the hardware exp and reciprocal; exp2 overflows to +inf for very
+// negative z, which gives -0 (the limit).
+__device__ __forceinline__ float silu(float zv) {
+  return zv * rcp_fast(1.0f + exp2_fast(-zv * kLog2e));
+}
+
+// softplus with the accurate library log1p/exp; the identity above 20 (error < 2.1e-9).
+__device__ __forceinline__ float softplus_f32(float u) { return u > 20.0f ? u : log1pf(expf(u)); }
+
+// Element loads/stores of the per-token tensors in either storage type.
+template <typename T> struct IoTraits;
+
+template <> struct IoTraits<float> {
+  __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float* p, int64_t i, float v) { p[i] = v; }
+  // four consecutive elements (16-byte aligned)
+  __device__ __forceinline__ static void load4(const float* p, int64_t i, float out[4]) {
+    float4 v = *reinterpret_cast<const float4*>(p + i);
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+  }
+  using raw4 = uint4;
+  __device__ __forceinline__ static raw4 load4_raw(const float* p, int64_t i) {
+    return *reinterpret_cast<const uint4*>(p + i);
+  }
+  __device__ __forceinline__ static void unpack4(raw4 r, float out[4]) {
+    out[0] = __uint_as_float(r.x); out[1] = __uint_as_float(r.y);
+    out[2] = __uint_as_float(r.z); out[3] = __uint_as_float(r.w);
+  }
+  __device__ __forceinline__ static raw4 zero4() { return make_uint4(0, 0, 0, 0); }
+};
+
+template <> struct IoTraits<bf16_t> {
+  __device__ __forceinline__ static float load(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i].bits); }
+  __device__ __forceinline__ static void store(bf16_t* p, int64_t i, float v) { p[i].bits = f32_to_bf16(v); }
+  using raw4 = uint2;
+  // four consecutive elements (8-byte aligned)
+  __device__ __forceinline__ static raw4 load4_raw(const bf16_t* p, int64_t i) {
+    return *reinterpret_cast<const uint2*>(p + i);
+  }
+  __device__ __forceinline__ static void unpack4(raw4 r, float out[4]) {
+    out[0] = bf16_lo(r.x); out[1] = bf16_hi(r.x); out[2] = bf16_lo(r.y); out[3] = bf16_hi(r.y);
+  }
+  __device__ __forceinline__ static void load4(const bf16_t* p, int64_t i, float out[4]) {
+    unpack4(load4_raw(p, i), out);
+  }
+  __device__ __forceinline__ static raw4 zero4() { return make_uint2(0, 0); }
+};
+
+}  // namespace ssm

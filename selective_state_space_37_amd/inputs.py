@@ -5,8 +5,9 @@ method's arithmetic, so both the GPU library's tests and the CPU oracle can take
 from it.
 
 Draw recipe: every tensor and every (batch row, block of 8192 tokens) draws from its own
-``numpy.random.Generator(PCG64(SeedSequence([seed, tensor_id, b, block])))`` in float64, is cast
-to fp32, and, for bf16 tensors, rounded to bf16 with round-to-nearest-even. Tensor ids:
+``numpy.random.Generator(PCG64(SeedSequence([seed, tensor_id, b, block])))``; per-token tensors
+draw standard normals directly in float32 (numpy's float32 ziggurat), parameters in float64 then
+cast; bf16 tensors are rounded from fp32 with round-to-nearest-even. Tensor ids:
 x=0, delta=1, B=2, C=3, z=4, D=5, conv_w=6, A=7, conv register=8; decode step s draws with
 tensor id 100 + s. Large workloads can therefore be produced block by block and reproduced.
 
@@ -76,7 +77,11 @@ def draw_tokens(seed: int, tid: int, Bsz: int, L: int, width: int, kind: str = "
             t1 = min(L, t0 + TOKEN_BLOCK)
             g = _rng(seed, tid, b, blk)
             if kind == "normal":
-                v = g.standard_normal((t1 - t0, width)) * scale + loc
+                v = g.standard_normal((t1 - t0, width), dtype=np.float32)
+                if scale != 1.0:
+                    v *= np.float32(scale)
+                if loc != 0.0:
+                    v += np.float32(loc)
             elif kind == "uniform":
                 v = g.uniform(loc, scale, (t1 - t0, width))
             else:

@@ -1,0 +1,205 @@
+"""Python binding of libssm (ctypes). Argument marshalling only: every step of the computation
+runs in the HIP kernels behind the C ABI declared in ``include/ssm.h``; PyTorch supplies device
+memory and the current stream. There is no fallback: without the built library every call
+raises."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssm.so")
+
+SSM_F32, SSM_BF16 = 0, 1
+STATUS = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARGUMENT", 2: "SSM_ERR_UNSUPPORTED",
+          3: "SSM_ERR_WORKSPACE_TOO_SMALL", 4: "SSM_ERR_HIP"}
+
+# Every symbol include/ssm.h declares.
+EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_last_error_detail",
+           "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd",
+           "ssm_scan_fwd_segmented_workspace_bytes", "ssm_scan_fwd_segmented",
+           "ssm_state_update", "ssd_chunk_fwd_workspace_bytes", "ssd_chunk_fwd")
+
+_lib = None
+
+
+class SSMError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__("%s: %s" % (STATUS.get(status, status), detail))
+        self.status = status
+        self.detail = detail
+
+
+def load(path: str = LIB_PATH):
+    """Load libssm.so and declare the C signatures. Raises if the library is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libssm.so is not built (%s); run __graft_entry__.build() or "
+                           "python selective_state_space_37_amd/build.py" % path)
+    lib = ctypes.CDLL(path)
+    i64, ci, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    lib.ssm_abi_version.argtypes, lib.ssm_abi_version.restype = [], ci
+    lib.ssm_status_string.argtypes, lib.ssm_status_string.restype = [ci], ctypes.c_char_p
+    lib.ssm_last_error_detail.argtypes, lib.ssm_last_error_detail.restype = [], ctypes.c_char_p
+    lib.ssm_scan_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
+    lib.ssm_scan_fwd_workspace_bytes.restype = sz
+    lib.ssm_scan_fwd_segmented_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    lib.ssm_scan_fwd_segmented_workspace_bytes.restype = sz
+    scan_args = [i64, i64, i64, i64, ci, vp, vp, vp, ci, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ssm_scan_fwd.argtypes = scan_args + [vp, sz, vp]
+    lib.ssm_scan_fwd.restype = ci
+    lib.ssm_scan_fwd_segmented.argtypes = scan_args + [i64, vp, sz, vp]
+    lib.ssm_scan_fwd_segmented.restype = ci
+    lib.ssm_state_update.argtypes = [i64, i64, i64, i64, ci, vp, vp, vp, ci, vp, vp, vp, vp, vp,
+                                     vp, vp, vp, vp, vp, vp]
+    lib.ssm_state_update.restype = ci
+    lib.ssd_chunk_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ci]
+    lib.ssd_chunk_fwd_workspace_bytes.restype = sz
+    lib.ssd_chunk_fwd.argtypes = [i64, i64, i64, i64, i64, i64, ci, vp, vp, vp, ci, vp, vp, vp, vp,
+                                  vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_chunk_fwd.restype = ci
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise SSMError(status, load().ssm_last_error_detail().decode())
+
+
+def _io_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SSM_F32
+    if t.dtype == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError("per-token tensors must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None, shape=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+
+
+def scan_fwd(x, delta, A, Bm, Cm, *, delta_bias=None, delta_softplus=False, Dskip=None, z=None,
+             h0=None, return_state=True, segment_len: Optional[int] = None, y=None,
+             ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Selective scan: x, delta, z [B, L, D]; A [D, N] fp32; Bm, Cm [B, L, N]; -> (y, h_last)."""
+    lib = load()
+    Bsz, L, D = x.shape
+    N = A.shape[1]
+    io = x.dtype
+    _dev(x, "x")
+    _dev(delta, "delta", io, (Bsz, L, D))
+    _dev(z, "z", io, (Bsz, L, D))
+    _dev(Bm, "Bm", io, (Bsz, L, N))
+    _dev(Cm, "Cm", io, (Bsz, L, N))
+    _dev(A, "A", torch.float32, (D, N))
+    _dev(delta_bias, "delta_bias", torch.float32, (D,))
+    _dev(Dskip, "Dskip", torch.float32, (D,))
+    _dev(h0, "h0", torch.float32, (Bsz, D, N))
+    if y is None:
+        y = torch.empty_like(x)
+    h_last = torch.empty((Bsz, D, N), dtype=torch.float32, device=x.device) if return_state else None
+    code = _io_code(x)
+    if segment_len is None:
+        nb = lib.ssm_scan_fwd_workspace_bytes(Bsz, L, D, N, code)
+    else:
+        nb = lib.ssm_scan_fwd_segmented_workspace_bytes(Bsz, L, D, N, int(segment_len))
+    if ws is None or ws.numel() < nb:
+        ws = workspace(nb, x.device)
+    args = [Bsz, L, D, N, code, _p(x), _p(delta), _p(delta_bias), int(bool(delta_softplus)), _p(A),
+            _p(Bm), _p(Cm), _p(Dskip), _p(z), _p(h0), _p(y), _p(h_last)]
+    if segment_len is None:
+        st = lib.ssm_scan_fwd(*args, _p(ws), nb, _stream(x))
+    else:
+        st = lib.ssm_scan_fwd_segmented(*args, int(segment_len), _p(ws), nb, _stream(x))
+    _check(st)
+    return y, h_last
+
+
+def state_update(x, delta, A, Bm, Cm, h, *, delta_bias=None, delta_softplus=False, Dskip=None,
+                 z=None, conv_state=None, conv_w=None, conv_b=None, y=None) -> torch.Tensor:
+    """One decode token: x, delta, z [B, D]; Bm, Cm [B, N]; h [B, D, N] fp32 (updated in place);
+    conv_state [B, D, W] (updated in place). Returns y [B, D]."""
+    lib = load()
+    Bsz, D = x.shape
+    N = A.shape[1]
+    io = x.dtype
+    _dev(x, "x")
+    _dev(delta, "delta", io, (Bsz, D))
+    _dev(z, "z", io, (Bsz, D))
+    _dev(Bm, "Bm", io, (Bsz, N))
+    _dev(Cm, "Cm", io, (Bsz, N))
+    _dev(A, "A", torch.float32, (D, N))
+    _dev(h, "h", torch.float32, (Bsz, D, N))
+    _dev(delta_bias, "delta_bias", torch.float32, (D,))
+    _dev(Dskip, "Dskip", torch.float32, (D,))
+    W = 0
+    if conv_state is not None:
+        W = conv_state.shape[2]
+        _dev(conv_state, "conv_state", io, (Bsz, D, W))
+        _dev(conv_w, "conv_w", torch.float32, (D, W))
+        _dev(conv_b, "conv_b", torch.float32, (D,))
+    if y is None:
+        y = torch.empty_like(x)
+    st = lib.ssm_state_update(Bsz, D, N, W, _io_code(x), _p(x), _p(delta), _p(delta_bias),
+                              int(bool(delta_softplus)), _p(A), _p(Bm), _p(Cm), _p(Dskip), _p(z),
+                              _p(conv_state), _p(conv_w), _p(conv_b), _p(h), _p(y), _stream(x))
+    _check(st)
+    return y
+
+
+def ssd_chunk_fwd(x, delta, A, Bm, Cm, *, chunk: int = 256, delta_bias=None, delta_softplus=False,
+                  Dskip=None, z=None, h0=None, return_state=True, y=None,
+                  ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Mamba-2 layer: x, z [B, L, H, P]; delta [B, L, H]; A [H]; Bm, Cm [B, L, N] -> (y, h_last)."""
+    lib = load()
+    Bsz, L, H, P = x.shape
+    N = Bm.shape[2]
+    io = x.dtype
+    _dev(x, "x")
+    _dev(delta, "delta", io, (Bsz, L, H))
+    _dev(z, "z", io, (Bsz, L, H, P))
+    _dev(Bm, "Bm", io, (Bsz, L, N))
+    _dev(Cm, "Cm", io, (Bsz, L, N))
+    _dev(A, "A", torch.float32, (H,))
+    _dev(delta_bias, "delta_bias", torch.float32, (H,))
+    _dev(Dskip, "Dskip", torch.float32, (H,))
+    _dev(h0, "h0", torch.float32, (Bsz, H, P, N))
+    if y is None:
+        y = torch.empty_like(x)
+    h_last = torch.empty((Bsz, H, P, N), dtype=torch.float32, device=x.device) if return_state else None
+    code = _io_code(x)
+    nb = lib.ssd_chunk_fwd_workspace_bytes(Bsz, L, H, P, N, chunk, code)
+    if ws is None or ws.numel() < nb:
+        ws = workspace(nb, x.device)
+    st = lib.ssd_chunk_fwd(Bsz, L, H, P, N, chunk, code, _p(x), _p(delta), _p(delta_bias),
+                           int(bool(delta_softplus)), _p(A), _p(Bm), _p(Cm), _p(Dskip), _p(z),
+                           _p(h0), _p(y), _p(h_last), _p(ws), nb, _stream(x))
+    _check(st)
+    return y, h_last

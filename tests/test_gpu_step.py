@@ -1,0 +1,95 @@
+"""GPU parity of ssm_state_update (one decode token) against the fp64 oracle, and the decode
+workload: a 2,048-token prompt through ssm_scan_fwd, then 128 single-token steps at batch 128,
+d_inner 4096, N = 16, bf16 with float32 state (sampled channels for the full-size run)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from selective_state_space_37_amd import inputs, ssm
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("conv", [True, False])
+def test_step_matches_oracle(dtype, N, conv):
+    Bsz, D, W, seed = 3, 136, 4, 40 + N
+    prm = inputs.decode_params(seed=seed, D=D, N=N, W=W)
+    h0 = inputs.draw_param(seed, 50, (Bsz, D, N), scale=0.5)
+    bias = inputs.draw_param(seed, 51, (D,), scale=0.3)
+    cb = inputs.draw_param(seed, 52, (D,), scale=0.1)
+    reg = inputs.conv_register(seed, Bsz, D, W, dtype) if conv else None
+    st = inputs.decode_step(seed, 0, Bsz, D, N, dtype)
+    h = gu.dev(h0)
+    creg = gu.dev(reg) if conv else None
+    y = gu.step_on_gpu(st, gu.dev(prm["A"]), h, Dskip=gu.dev(prm["Dskip"]), conv_state=creg,
+                       conv_w=gu.dev(prm["conv_w"]) if conv else None, conv_b=gu.dev(cb) if conv else None,
+                       delta_bias=gu.dev(bias), delta_softplus=True)
+    torch.cuda.synchronize()
+    w = lambda a: inputs.widen(a, dtype)
+    ry, rh, rc = oracle.step(w(st.x), w(st.delta), prm["A"], w(st.Bm), w(st.Cm), h0,
+                             delta_bias=bias, delta_softplus=True, Dskip=prm["Dskip"], z=w(st.z),
+                             conv_state=w(reg) if conv else None, conv_w=prm["conv_w"] if conv else None,
+                             conv_b=cb if conv else None)
+    tol = gu.TOL[dtype]
+    assert gu.rel_err(gu.host(y), ry) <= tol
+    assert gu.rel_err(gu.host(h), rh) <= tol
+    if conv:  # the register holds stored inputs: exact
+        assert np.array_equal(gu.host(creg), rc)
+
+
+def test_repeated_steps_equal_scan():
+    """L decode steps without the conv register equal one scan over the L tokens."""
+    inp = inputs.scan_small(seed=60, Bsz=2, L=37, D=64, h0=True)
+    y_scan, h_scan = gu.scan_on_gpu(inp)
+    h = gu.dev(inp.h0).clone()
+    A = gu.dev(inp.A)
+    ys = []
+    for t in range(inp.x.shape[1]):
+        y = ssm.state_update(gu.dev(inp.x[:, t]), gu.dev(inp.delta[:, t]), A, gu.dev(inp.Bm[:, t]),
+                             gu.dev(inp.Cm[:, t]), h, delta_bias=gu.dev(inp.delta_bias),
+                             delta_softplus=True, Dskip=gu.dev(inp.Dskip), z=gu.dev(inp.z[:, t]))
+        ys.append(gu.host(y))
+    torch.cuda.synchronize()
+    assert gu.rel_err(np.stack(ys, axis=1), y_scan) <= 1e-5
+    assert gu.rel_err(gu.host(h), h_scan) <= 1e-5
+
+
+@pytest.mark.slow
+def test_decode_workload_full_size():
+    """Prompt of 2,048 tokens (scan, h_last) then 128 decode steps at batch 128, d_inner 4096,
+    N = 16, bf16 I/O, float32 state. The prompt's scan inputs are synthetic draws standing for the
+    convolved prompt; the conv register starts as the last 4 raw prompt inputs. Every step's y and
+    the final state are compared with the oracle on sampled channels."""
+    Bsz, L, D, N, W, seed, steps = 128, 2048, 4096, 16, 4, 3, 128
+    prm = inputs.decode_params(seed=seed, D=D, N=N, W=W)
+    pre = inputs.scan_layer(seed=seed, Bsz=Bsz, L=L, D=D, N=N)
+    _, h_pre = ssm.scan_fwd(gu.dev(pre.x), gu.dev(pre.delta), gu.dev(pre.A), gu.dev(pre.Bm), gu.dev(pre.Cm),
+                            Dskip=gu.dev(pre.Dskip), z=gu.dev(pre.z))
+    ch = np.unique(np.concatenate([[0, D - 1], np.random.default_rng(7).choice(D, 6, replace=False)]))
+    w = lambda a: inputs.widen(a, "bf16")
+    _, rh = oracle.scan(w(pre.x[:, :, ch]), w(pre.delta[:, :, ch]), pre.A[ch], w(pre.Bm), w(pre.Cm),
+                        Dskip=pre.Dskip[ch], z=w(pre.z[:, :, ch]))
+    torch.cuda.synchronize()
+    assert gu.rel_err(gu.host(h_pre)[:, ch], rh) <= gu.TOL["bf16"]
+    del pre
+    reg = inputs.conv_register(seed, Bsz, D, W, "bf16")
+    creg = gu.dev(reg)
+    A, Dk, cw = gu.dev(prm["A"]), gu.dev(prm["Dskip"]), gu.dev(prm["conv_w"])
+    r_reg = w(reg[:, ch])
+    worst = 0.0
+    for s in range(steps):
+        st = inputs.decode_step(seed, s, Bsz, D, N, "bf16")
+        y = gu.step_on_gpu(st, A, h_pre, Dskip=Dk, conv_state=creg, conv_w=cw)
+        ry, rh, r_reg = oracle.step(w(st.x[:, ch]), w(st.delta[:, ch]), prm["A"][ch], w(st.Bm), w(st.Cm), rh,
+                                    Dskip=prm["Dskip"][ch], z=w(st.z[:, ch]), conv_state=r_reg,
+                                    conv_w=prm["conv_w"][ch])
+        worst = max(worst, gu.rel_err(gu.host(y)[:, ch], ry))
+    torch.cuda.synchronize()
+    worst = max(worst, gu.rel_err(gu.host(h_pre)[:, ch], rh))
+    print("decode 128 steps sampled err", worst)
+    assert worst <= gu.TOL["bf16"]
+    assert np.array_equal(gu.host(creg)[:, ch], r_reg)

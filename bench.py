@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Throughput of the selective-scan forward pass on one MI355X.
+
+One step = one ssm_scan_fwd over the Mamba-2.8B-layer-shaped workload: batch 8, L = 2048,
+d_inner 5120, N = 16, bf16 x / delta / z / B / C / y, float32 state and arithmetic, SiLU(z) gate and
+D term on, final state returned. Inputs are synthetic (seeded; the same generator the parity tests
+use) and resident in HBM before the timed region; three independent input sets rotate so the
+256 MB last-level cache cannot serve them.
+
+Prints ONE JSON line: value = algorithmic HBM GB/s of the whole step (wall clock, synchronised),
+plus Gelem/s (token-channels per second), the roofline of the dominant kernel (measured with HIP
+events on the stream the kernel runs on), the fp64 CPU oracle timed on the host, and secondary
+figures for the long-sequence, decode and Mamba-2 (SSD) workloads.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0                       # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0                   # dense bf16 MFMA, published
+CUS, SIMDS, LANES, CLOCK = 256, 4, 16, 2.4e9
+PEAK_VALU_TOPS = CUS * SIMDS * LANES * CLOCK / 1e12   # fp32 lane-ops/s without packed FP32: 39.3
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_layer_8x2048x5120_bf16_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_37_amd", "csrc", f)
+                  for f in ("scan.hip", "device_common.h", "kernels.h")]
+
+LAYER = dict(B=8, L=2048, D=5120, N=16)
+
+
+def scan_bytes(B, L, D, N, es, gate=True, dskip=True, bias=False, h0=False, h_last=True):
+    """Algorithmic HBM bytes of one scan: every input once, every output once; the N-wide state
+    never goes to HBM (only the optional initial and final states)."""
+    tok = B * L * D * es
+    n = tok * (3 + (1 if gate else 0))          # x, delta, y (+ z)
+    n += 2 * B * L * N * es                     # B_t, C_t
+    n += D * N * 4 + (D * 4 if dskip else 0) + (D * 4 if bias else 0)
+    n += (B * D * N * 4 if h0 else 0) + (B * D * N * 4 if h_last else 0)
+    return n
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel source; else None."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    kv = {}
+    for line in open(PROFILE_TRAFFIC):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def timed(fn, steps, warmup, torch):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    return wall_ms, e0.elapsed_time(e1) / steps
+
+
+def device_layer_set(torch, seed, B, L, D, N):
+    """An extra independent input set drawn on the device with the same distributions as the
+    layer workload (timing only; parity runs use the host generator)."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    bf = torch.bfloat16
+    r = lambda *s: torch.randn(*s, generator=g, device="cuda", dtype=torch.float32)
+    delta = torch.clamp(torch.nn.functional.softplus(r(B, L, D) - 4.0), 1e-3, 0.1).to(bf)
+    return dict(x=r(B, L, D).to(bf), delta=delta, z=r(B, L, D).to(bf), Bm=r(B, L, N).to(bf),
+                Cm=r(B, L, N).to(bf))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=3, help="rotating independent input sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 512 MiB device copy three times (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        sys.stderr.write("bench.py measures one GPU: this library has no multi-GPU path "
+                         "(--gpus %d requested). Run with --gpus 1.\n" % args.gpus)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from selective_state_space_37_amd import inputs, ssm
+    ssm.load()  # fails loudly without the built HIP library
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(1 << 27, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    B, L, D, N = LAYER["B"], LAYER["L"], LAYER["D"], LAYER["N"]
+    host = inputs.scan_layer()
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16) \
+        if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    A, Dskip = dev(host.A), dev(host.Dskip)
+    sets = [dict(x=dev(host.x), delta=dev(host.delta), z=dev(host.z), Bm=dev(host.Bm), Cm=dev(host.Cm))]
+    for s in range(1, max(1, args.sets)):
+        sets.append(device_layer_set(torch, 1000 + s, B, L, D, N))
+    for s in sets:
+        s["y"] = torch.empty_like(s["x"])
+        s["h"] = torch.empty((B, D, N), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        s = sets[i % len(sets)]
+        ssm.scan_fwd(s["x"], s["delta"], A, s["Bm"], s["Cm"], Dskip=Dskip, z=s["z"], y=s["y"], h_last=s["h"])
+
+    wall_ms, kern_ms = timed(step, args.steps, args.warmup, torch)
+    nbytes = scan_bytes(B, L, D, N, 2)
+    elems = B * L * D
+    value = nbytes / (wall_ms * 1e-3) / 1e9
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    state_steps = elems * N
+    # issue-limited VALU model of the recurrence: 6 VALU ops per state-step
+    valu_tops = state_steps * 6 / (kern_ms * 1e-3) / 1e12
+
+    out = {
+        "metric": "selective-scan HBM GB/s (% of peak) + Gelem/s at B=8,L=2048,D=5120,N=16",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) x/z/B/C, delta = clip(softplus(N(-4,1)), 1e-3, 0.1), A[d,n] = -(n+1))",
+        "config": {"workload": "selective scan, Mamba-2.8B layer shape: batch 8, L 2048, d_inner 5120, N 16",
+                   "B": B, "L": L, "D": D, "N": N, "io_dtype": "bf16", "state_dtype": "f32",
+                   "gate": True, "D_term": True, "final_state": True, "input_sets": len(sets)},
+        "gelem_per_s": round(elems / (wall_ms * 1e-3) / 1e9, 2),
+        "hbm_frac_of_peak": round(value / PEAK_HBM_GBS, 4),
+        "kernel_ms": round(kern_ms, 5),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": read_traffic(),
+                     "bytes_per_launch": nbytes, "kernel": "scan_kernel<bf16, NS=4, KW=4, T=16, N=16, full>"},
+        "valu_model": {"ops_per_state_step": 6, "achieved_tops": round(valu_tops, 2),
+                       "peak_tops": round(PEAK_VALU_TOPS, 2), "frac": round(valu_tops / PEAK_VALU_TOPS, 4)},
+    }
+
+    if not args.no_secondary:
+        out["secondary"] = secondary(torch, np, inputs, ssm, dev)
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(host, np, inputs)
+
+    print(json.dumps(out), flush=True)
+
+
+def secondary(torch, np, inputs, ssm, dev):
+    """Long-sequence scan, decode step and SSD layer: kernel-time throughput (HIP events)."""
+    res = {}
+    g = torch.Generator(device="cuda").manual_seed(7)
+    r = lambda *s: torch.randn(*s, generator=g, device="cuda", dtype=torch.float32)
+
+    # long, narrow scan: 1 x 1,048,576 x 256, N = 16, fp32 (segmented plan)
+    B, L, D, N = 1, 1 << 20, 256, 16
+    x, z = r(B, L, D), r(B, L, D)
+    delta = 0.5 * r(B, L, D)
+    Bm, Cm = r(B, L, N), r(B, L, N)
+    A = dev(inputs.structured_A(D, N))
+    bias = torch.full((D,), inputs.DELTA_BIAS_SMALL, device="cuda")
+    Dk = r(D)
+    y = torch.empty_like(x)
+    hl = torch.empty((B, D, N), device="cuda")
+    nb = ssm.load().ssm_scan_fwd_workspace_bytes(B, L, D, N, ssm.SSM_F32)
+    ws = ssm.workspace(nb, "cuda")
+    fn = lambda i: ssm.scan_fwd(x, delta, A, Bm, Cm, delta_bias=bias, delta_softplus=True, Dskip=Dk, z=z,
+                                y=y, h_last=hl, ws=ws)
+    _, ms = timed(fn, 10, 3, torch)
+    nbytes = scan_bytes(B, L, D, N, 4, bias=True)
+    res["scan_long_1x1048576x256_f32"] = {"ms": round(ms, 4), "GB_s": round(nbytes / ms / 1e6, 1),
+                                           "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
+                                           "gelem_s": round(B * L * D / ms / 1e6, 1)}
+    del x, z, delta, Bm, Cm, y
+
+    # decode: batch 128, d_inner 4096, N 16, bf16 I/O, conv width 4; 16 layers' states rotate
+    B, D, N, W, layers = 128, 4096, 16, 4, 16
+    bf = torch.bfloat16
+    A = dev(inputs.structured_A(D, N))
+    hs = [r(B, D, N) * 0.1 for _ in range(layers)]
+    cs = [r(B, D, W).to(bf) for _ in range(layers)]
+    cw, Dk = r(D, W) * 0.5, r(D)
+    xs = [r(B, D).to(bf) for _ in range(layers)]
+    ds = [torch.clamp(torch.nn.functional.softplus(r(B, D) - 4), 1e-3, 0.1).to(bf) for _ in range(layers)]
+    zs = [r(B, D).to(bf) for _ in range(layers)]
+    Bs = [r(B, N).to(bf) for _ in range(layers)]
+    Cs = [r(B, N).to(bf) for _ in range(layers)]
+    ys = [torch.empty(B, D, dtype=bf, device="cuda") for _ in range(layers)]
+
+    def dec(i):
+        k = i % layers
+        ssm.state_update(xs[k], ds[k], A, Bs[k], Cs[k], hs[k], Dskip=Dk, z=zs[k], conv_state=cs[k], conv_w=cw,
+                         y=ys[k])
+
+    # one graph holds 16 layer steps, so Python launch overhead is not measured
+    for i in range(layers):
+        dec(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(layers):
+            dec(i)
+    _, ms = timed(lambda i: graph.replay(), 20, 3, torch)
+    per_step = ms / layers
+    nbytes = B * D * (2 * N * 4 + 2 * W * 2 + 4 * 2) + D * N * 4 + D * W * 4 + D * 4 + 2 * B * N * 2
+    res["decode_128x4096_n16_bf16_16_layers"] = {
+        "us_per_step": round(per_step * 1e3, 3), "GB_s": round(nbytes / per_step / 1e6, 1),
+        "hbm_frac": round(nbytes / per_step / 1e6 / PEAK_HBM_GBS, 4),
+        "tokens_per_s_per_layer": round(B / (per_step * 1e-3), 1)}
+    del hs, cs, xs, ds, zs, Bs, Cs, ys, graph
+
+    # Mamba-2 SSD: batch 2, L 8192, 80 heads x 64, N 128, chunk 256, bf16
+    B, L, H, P, N, Q = 2, 8192, 80, 64, 128, 256
+    x = r(B, L, H, P).to(bf)
+    delta = torch.clamp(torch.nn.functional.softplus(r(B, L, H) - 4), 1e-3, 0.1).to(bf)
+    Bm, Cm = r(B, L, N).to(bf), r(B, L, N).to(bf)
+    Ah = -(1.0 + 15.0 * torch.rand(H, generator=g, device="cuda"))
+    y = torch.empty_like(x)
+    nb = ssm.load().ssd_chunk_fwd_workspace_bytes(B, L, H, P, N, Q, ssm.SSM_BF16)
+    ws = ssm.workspace(nb, "cuda")
+    fn = lambda i: ssm.ssd_chunk_fwd(x, delta, Ah, Bm, Cm, chunk=Q, y=y, ws=ws)
+    _, ms = timed(fn, 10, 3, torch)
+    nbytes = 2 * B * L * H * P * 2 + B * L * H * 2 + 2 * B * L * N * 2 + H * 4 + B * H * P * N * 4
+    nch = L // Q
+    flops = B * nch * H * (2 * Q * Q * P + 2 * Q * P * N * 2) + B * nch * 2 * Q * Q * N
+    res["ssd_2x8192x80x64_n128_q256_bf16"] = {
+        "ms": round(ms, 4), "GB_s": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
+        "TFLOP_s": round(flops / ms / 1e9, 1), "mfma_frac": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    return res
+
+
+def cpu_baseline(host, np, inputs):
+    """The fp64 oracle (as it stands) on the host cores, over the same layer workload."""
+    import oracle
+    w = lambda a: inputs.widen(a, "bf16")
+    x, d, z, Bm, Cm = w(host.x), w(host.delta), w(host.z), w(host.Bm), w(host.Cm)
+    B, L, D = x.shape
+    N = host.A.shape[1]
+    t0 = time.perf_counter()
+    oracle.scan(x, d, host.A, Bm, Cm, Dskip=host.Dskip, z=z)
+    dt = time.perf_counter() - t0
+    nbytes = scan_bytes(B, L, D, N, 2)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 3), "gelem_per_s": round(B * L * D / dt / 1e9, 5),
+            "sample": "the whole layer workload (8 x 2048 x 5120, N 16): fp64 recurrence, OpenMP over (b, d)",
+            "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -56,8 +56,12 @@ constexpr int64_t kPlanCUs = 256;
 constexpr int64_t kTile = 16;         // tokens per LDS tile of the scan kernels
 constexpr int64_t kMinSegment = 256;  // shortest automatic segment
 
-int64_t auto_segment_len(int64_t B, int64_t L, int64_t D) {
-  const int64_t wgs = ((D + 63) / 64) * B;
+// Channels per scan workgroup (the kernels use 32 for N >= 8, 64 below).
+int64_t scan_channels_per_wg(int64_t N) { return N >= 8 ? 32 : 64; }
+
+int64_t auto_segment_len(int64_t B, int64_t L, int64_t D, int64_t N) {
+  const int64_t ch = scan_channels_per_wg(N);
+  const int64_t wgs = ((D + ch - 1) / ch) * B;
   if (L <= kMinSegment || wgs >= 2 * kPlanCUs) return L;
   int64_t nseg = (4 * kPlanCUs + wgs - 1) / wgs;
   int64_t seg = (L + nseg - 1) / nseg;
@@ -144,7 +148,7 @@ const char* ssm_last_error_detail(void) { return g_detail.c_str(); }
 
 size_t ssm_scan_fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype) {
   if (B <= 0 || L <= 0 || D <= 0 || N <= 0) return 0;
-  return ssm::scan_workspace_bytes(B, D, N, num_segments(L, auto_segment_len(B, L, D)));
+  return ssm::scan_workspace_bytes(B, D, N, num_segments(L, auto_segment_len(B, L, D, N)));
 }
 
 size_t ssm_scan_fwd_segmented_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int64_t segment_len) {
@@ -156,7 +160,7 @@ ssm_status ssm_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io
                         const void* delta, const float* delta_bias, int delta_softplus, const float* A,
                         const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
                         void* y, float* h_last, void* ws, size_t ws_bytes, void* stream) {
-  const int64_t seg = (B > 0 && L > 0 && D > 0) ? auto_segment_len(B, L, D) : 1;
+  const int64_t seg = (B > 0 && L > 0 && D > 0) ? auto_segment_len(B, L, D, N) : 1;
   return scan_common(B, L, D, N, io, x, delta, delta_bias, delta_softplus, A, Bm, Cm, Dskip, z, h0, y,
                      h_last, seg, ws, ws_bytes, stream);
 }

@@ -8,15 +8,19 @@
 // registers for the whole sequence and is never written to HBM; only y (and the final state)
 // leave the chip.
 //
-// Work split (one workgroup = 64 channels of one sequence, one L-segment):
-//   * wave w of the KW waves owns states [w*NS, (w+1)*NS) of all 64 channels; lane = channel.
-//     B_t and C_t are then wave-uniform (broadcast LDS reads).
-//   * T-token tiles of x, Delta (activated once per element by the loader), z, B and C are
-//     staged through LDS with wide coalesced loads, double buffered: the global loads of tile
-//     i+1 are in flight while tile i runs.
-//   * each wave writes its partial readout sum per (token, channel) to LDS; after a barrier the
-//     waves split the tile's tokens, add the KW partials in a fixed order (deterministic), add
-//     D x, gate, round and store y with coalesced row stores.
+// Work split (one workgroup = CH channels of one sequence, one L-segment):
+//   * the N states of a channel are cut into KS slices of NS states; thread tid owns slice
+//     tid / CH of channel tid % CH, so the readout of a channel is split over KS lanes.
+//     At N = 16 the split is CH = 32, NS = 2, KS = 8: 256 threads, and the layer workload
+//     (8 x 5120 channels) becomes 1280 workgroups -- exactly five per CU and five waves per SIMD
+//     on MI355X's 256 CUs, so no SIMD carries an extra wave at the end.
+//   * T-token tiles of (Delta, x) pairs (Delta activated once per element by the loader), z in
+//     its storage type, and (B_n, C_n) pairs are staged through LDS with wide coalesced loads,
+//     double buffered: the global loads of tile i+1 are in flight while tile i runs. Per token a
+//     lane then needs one 8-byte and one 16-byte LDS read.
+//   * each lane writes its partial readout to LDS; after a barrier the threads split the tile's
+//     (token, channel) outputs, add the KS partials in a fixed order (deterministic), add D x,
+//     gate, round and store y with coalesced row stores.
 //   * padded tokens (ragged L tail) get Delta = 0 and x = 0, which makes the step the identity.
 // Long, narrow inputs (few channel tiles) are cut into L-segments: a state-only pass gives each
 // segment's local end state and sum of Delta; a carry pass runs the segment recurrence
@@ -29,36 +33,34 @@ namespace ssm {
 
 namespace {
 
-constexpr int kChan = 64;  // channels per workgroup (one per lane)
-
-template <typename io_t, int NS, int KW, int T, int N>
-struct ScanTile {
-  static constexpr int kThreads = 64 * KW;
-  static constexpr int kGroups = T * (kChan / 4);                     // 4-channel groups per tensor
+template <int CH, int NS, int KS, int T, int N>
+struct ScanCfg {
+  static_assert(NS * KS == N, "slices must cover the state");
+  static_assert(T % KS == 0, "post-processing splits a tile's tokens over the slices");
+  static constexpr int kThreads = CH * KS;
+  static constexpr int kGroups = T * (CH / 4);                      // 4-channel groups per tensor
   static constexpr int kGroupsPerThr = (kGroups + kThreads - 1) / kThreads;
-  static constexpr int kBC = T * N;                                    // B (or C) elements per tile
+  static constexpr int kBC = T * N;                                  // B (and C) elements per tile
   static constexpr int kBCPerThr = (kBC + kThreads - 1) / kThreads;
-  using raw4 = typename IoTraits<io_t>::raw4;
 };
 
-template <typename io_t, int NS, int KW, int T, int N, bool FULL>
-__global__ __launch_bounds__(64 * KW) void scan_kernel(ScanParams p) {
-  using Tile = ScanTile<io_t, NS, KW, T, N>;
+// OCC = waves per SIMD the launch plan needs resident (five at N = 16: <= 102 VGPRs per lane).
+template <typename io_t, int CH, int NS, int KS, int T, int N, bool FULL, int OCC>
+__global__ __launch_bounds__(CH * KS)
+void scan_kernel(ScanParams p) {
+  using Cfg = ScanCfg<CH, NS, KS, T, N>;
   using Io = IoTraits<io_t>;
-  using raw4 = typename Tile::raw4;
+  using raw4 = typename Io::raw4;
+  static_assert(Cfg::kThreads % (CH / 4) == 0, "a thread always loads the same channel group");
 
-  __shared__ float s_x[2][T][kChan];
-  __shared__ float s_dt[2][T][kChan];
-  __shared__ float s_z[FULL ? 2 : 1][FULL ? T : 1][kChan];
-  __shared__ float s_B[2][T][N];
-  __shared__ float s_C[FULL ? 2 : 1][FULL ? T : 1][N];
-  __shared__ float s_y[FULL ? KW : 1][FULL ? T : 1][kChan];
+  __shared__ __attribute__((aligned(16))) float2 s_dx[2][T][CH];          // (Delta, x)
+  __shared__ __attribute__((aligned(16))) raw4 s_z[FULL ? 2 : 1][FULL ? T : 1][CH / 4];
+  __shared__ __attribute__((aligned(16))) float s_bc[2][T][N][2];          // (B_n, C_n)
+  __shared__ float s_y[FULL ? KS : 1][FULL ? T : 1][CH];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
   const int64_t D = p.D, L = p.L;
-  const int64_t c0 = (int64_t)blockIdx.x * kChan;
+  const int64_t c0 = (int64_t)blockIdx.x * CH;
   const int64_t b = blockIdx.y;
   const int64_t seg = blockIdx.z;
   const int64_t t_begin = seg * p.seg_len;
@@ -72,34 +74,35 @@ __global__ __launch_bounds__(64 * KW) void scan_kernel(ScanParams p) {
   const io_t* __restrict__ Cg = static_cast<const io_t*>(p.Cm);
   const bool has_z = FULL && (zg != nullptr);
 
-  // ---- per-thread loader constants: this thread always loads channel group tid % 16
-  const int cg = tid & 15;
-  const int64_t cgl = c0 + 4 * cg;  // first channel of the group
-  const bool cg_ok = cgl < D;       // D % 4 == 0: a group is wholly in or out
+  // ---- loader: this thread always handles channel group tid % (CH / 4)
+  const int cg = tid % (CH / 4);
+  const int64_t cgl = c0 + 4 * cg;
+  const bool cg_ok = cgl < D;  // D % 4 == 0: a group is wholly in or out
   float bias4[4] = {0.f, 0.f, 0.f, 0.f};
   if (p.delta_bias && cg_ok)
+#pragma unroll
     for (int k = 0; k < 4; ++k) bias4[k] = p.delta_bias[cgl + k];
 
-  raw4 rx[Tile::kGroupsPerThr], rd[Tile::kGroupsPerThr], rz[Tile::kGroupsPerThr];
-  float rB[Tile::kBCPerThr], rC[Tile::kBCPerThr];
+  raw4 rx[Cfg::kGroupsPerThr], rd[Cfg::kGroupsPerThr], rz[Cfg::kGroupsPerThr];
+  float rB[Cfg::kBCPerThr], rC[Cfg::kBCPerThr];
 
   auto issue_loads = [&](int tile) {
     const int64_t t0 = t_begin + (int64_t)tile * T;
 #pragma unroll
-    for (int k = 0; k < Tile::kGroupsPerThr; ++k) {
-      const int g = tid + k * Tile::kThreads;
-      const int r = g >> 4;
-      const bool ok = (g < Tile::kGroups) && cg_ok && (t0 + r < t_end);
+    for (int k = 0; k < Cfg::kGroupsPerThr; ++k) {
+      const int g = tid + k * Cfg::kThreads;
+      const int r = g / (CH / 4);
+      const bool ok = (g < Cfg::kGroups) && cg_ok && (t0 + r < t_end);
       const int64_t off = ((b * L) + t0 + r) * D + cgl;
       rx[k] = ok ? Io::load4_raw(xg, off) : Io::zero4();
       rd[k] = ok ? Io::load4_raw(dg, off) : Io::zero4();
       if (has_z) rz[k] = ok ? Io::load4_raw(zg, off) : Io::zero4();
     }
 #pragma unroll
-    for (int k = 0; k < Tile::kBCPerThr; ++k) {
-      const int e = tid + k * Tile::kThreads;
+    for (int k = 0; k < Cfg::kBCPerThr; ++k) {
+      const int e = tid + k * Cfg::kThreads;
       const int r = e / N;
-      const bool ok = (e < Tile::kBC) && (t0 + r < t_end);
+      const bool ok = (e < Cfg::kBC) && (t0 + r < t_end);
       const int64_t off = ((b * L) + t0) * N + e;
       rB[k] = ok ? Io::load(Bg, off) : 0.f;
       if (FULL) rC[k] = ok ? Io::load(Cg, off) : 0.f;
@@ -109,12 +112,12 @@ __global__ __launch_bounds__(64 * KW) void scan_kernel(ScanParams p) {
   auto commit_tile = [&](int tile, int buf) {
     const int64_t t0 = t_begin + (int64_t)tile * T;
 #pragma unroll
-    for (int k = 0; k < Tile::kGroupsPerThr; ++k) {
-      const int g = tid + k * Tile::kThreads;
-      if (g < Tile::kGroups) {
-        const int r = g >> 4;
+    for (int k = 0; k < Cfg::kGroupsPerThr; ++k) {
+      const int g = tid + k * Cfg::kThreads;
+      if (g < Cfg::kGroups) {
+        const int r = g / (CH / 4);
         const bool valid = (t0 + r < t_end);
-        float xv[4], dv[4], zv[4];
+        float xv[4], dv[4];
         Io::unpack4(rx[k], xv);
         Io::unpack4(rd[k], dv);
 #pragma unroll
@@ -123,28 +126,29 @@ __global__ __launch_bounds__(64 * KW) void scan_kernel(ScanParams p) {
           if (p.delta_softplus) u = softplus_f32(u);
           dv[q] = valid ? u : 0.f;  // padded token: Delta = 0 -> identity step
         }
-        *reinterpret_cast<float4*>(&s_x[buf][r][4 * cg]) = make_float4(xv[0], xv[1], xv[2], xv[3]);
-        *reinterpret_cast<float4*>(&s_dt[buf][r][4 * cg]) = make_float4(dv[0], dv[1], dv[2], dv[3]);
-        if (has_z) {
-          Io::unpack4(rz[k], zv);
-          *reinterpret_cast<float4*>(&s_z[buf][r][4 * cg]) = make_float4(zv[0], zv[1], zv[2], zv[3]);
-        }
+        float4* dst = reinterpret_cast<float4*>(&s_dx[buf][r][4 * cg]);
+        dst[0] = make_float4(dv[0], xv[0], dv[1], xv[1]);
+        dst[1] = make_float4(dv[2], xv[2], dv[3], xv[3]);
+        if (has_z) s_z[buf][r][cg] = rz[k];
       }
     }
 #pragma unroll
-    for (int k = 0; k < Tile::kBCPerThr; ++k) {
-      const int e = tid + k * Tile::kThreads;
-      if (e < Tile::kBC) {
-        (&s_B[buf][0][0])[e] = rB[k];
-        if (FULL) (&s_C[buf][0][0])[e] = rC[k];
+    for (int k = 0; k < Cfg::kBCPerThr; ++k) {
+      const int e = tid + k * Cfg::kThreads;
+      if (e < Cfg::kBC) {
+        float* bc = &s_bc[buf][0][0][0] + 2 * e;
+        bc[0] = rB[k];
+        if (FULL) bc[1] = rC[k];
       }
     }
   };
 
   // ---- per-lane recurrence constants: channel c, states n0 .. n0+NS-1
-  const int64_t c = c0 + lane;
+  const int slice = tid / CH;
+  const int chl = tid % CH;
+  const int64_t c = c0 + chl;
   const bool c_ok = c < D;
-  const int n0 = w * NS;
+  const int n0 = slice * NS;
   float a2[NS], ia[NS], h[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
@@ -163,9 +167,11 @@ __global__ __launch_bounds__(64 * KW) void scan_kernel(ScanParams p) {
 #pragma unroll
       for (int j = 0; j < NS; ++j) h[j] = hin[j];
   }
-  const float dsk = (FULL && p.Dskip && c_ok) ? p.Dskip[c] : 0.f;
   float dsum = 0.f;
 
+  // ---- post-processing constants: this thread finishes channel tid % CH of tokens
+  //      slice, slice + KS, ... of each tile (the same channel as its recurrence lane)
+  const float dsk = (FULL && p.Dskip && c_ok) ? p.Dskip[c] : 0.f;
   io_t* __restrict__ yg = static_cast<io_t*>(p.y);
 
   if (ntiles > 0) {
@@ -178,37 +184,52 @@ __global__ __launch_bounds__(64 * KW) void scan_kernel(ScanParams p) {
     const int buf = tile & 1;
     if (tile + 1 < ntiles) issue_loads(tile + 1);
 
-    // ---- recurrence over the tile (identity on padded tokens)
+    // ---- recurrence over the tile (identity on padded tokens), in sub-tiles of PH tokens:
+    //      phase 1 forms Abar and the input term of every token of the sub-tile (independent
+    //      work, so several exps are in flight); phase 2 is the serial part, h = Abar h + u,
+    //      and the readout.
+    constexpr int PH = T < 4 ? T : 4;
+    static_assert(T % PH == 0, "sub-tiles must cover the tile");
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const float dt = s_dt[buf][t][lane];
-      const float xv = s_x[buf][t][lane];
-      float yp = 0.f;
+    for (int t0 = 0; t0 < T; t0 += PH) {
+      float abar_t[PH][NS], u_t[PH][NS];
 #pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        const float abar = exp2_fast(dt * a2[j]);
-        const float coef = fmaf(abar, ia[j], -ia[j]);  // expm1(Delta a) / a
-        h[j] = fmaf(abar, h[j], coef * (s_B[buf][t][n0 + j] * xv));
-        if (FULL) yp = fmaf(s_C[buf][t][n0 + j], h[j], yp);
+      for (int i = 0; i < PH; ++i) {
+        const float2 dx = s_dx[buf][t0 + i][chl];
+        const float* bc = &s_bc[buf][t0 + i][n0][0];
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          const float abar = exp2_fast(dx.x * a2[j]);
+          abar_t[i][j] = abar;
+          u_t[i][j] = fmaf(abar, ia[j], -ia[j]) * (bc[2 * j] * dx.y);  // expm1(Delta a)/a B x
+        }
+        if (!FULL) dsum += dx.x;
       }
-      if (FULL)
-        s_y[w][t][lane] = yp;
-      else
-        dsum += dt;
+#pragma unroll
+      for (int i = 0; i < PH; ++i) {
+        const float* bc = &s_bc[buf][t0 + i][n0][0];
+        float yp = 0.f;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          h[j] = fmaf(abar_t[i][j], h[j], u_t[i][j]);
+          if (FULL) yp = (j == 0) ? bc[1] * h[0] : fmaf(bc[2 * j + 1], h[j], yp);
+        }
+        if (FULL) s_y[slice][t0 + i][chl] = yp;
+      }
     }
 
     if (FULL) {
       __syncthreads();
-      // ---- combine the KW partial readouts, D term, gate, store
+      // ---- combine the KS partial readouts, D term, gate, store
       const int64_t t0 = t_begin + (int64_t)tile * T;
 #pragma unroll
-      for (int k = 0; k < T / KW; ++k) {
-        const int t = k * KW + w;
+      for (int k = 0; k < T / KS; ++k) {
+        const int t = slice + k * KS;
         float yv = 0.f;
 #pragma unroll
-        for (int q = 0; q < KW; ++q) yv += s_y[q][t][lane];
-        yv = fmaf(dsk, s_x[buf][t][lane], yv);
-        if (has_z) yv *= silu(s_z[buf][t][lane]);
+        for (int q = 0; q < KS; ++q) yv += s_y[q][t][chl];
+        yv = fmaf(dsk, s_dx[buf][t][chl].y, yv);
+        if (has_z) yv *= silu(Io::load(reinterpret_cast<const io_t*>(&s_z[buf][t][0]), chl));
         if (c_ok && t0 + t < t_end) Io::store(yg, ((b * L) + t0 + t) * D + c, yv);
       }
     }
@@ -227,7 +248,7 @@ __global__ __launch_bounds__(64 * KW) void scan_kernel(ScanParams p) {
     float* hl = p.ws_h + ((b * p.nseg + seg) * D + c) * N + n0;
 #pragma unroll
     for (int j = 0; j < NS; ++j) hl[j] = h[j];
-    if (w == 0) p.ws_sum[(b * p.nseg + seg) * D + c] = dsum;
+    if (slice == 0) p.ws_sum[(b * p.nseg + seg) * D + c] = dsum;
   }
 }
 
@@ -253,30 +274,30 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(ScanParams p) {
   p.ws_h[((b * p.nseg + p.nseg - 1) * D + c) * N + n] = h;
 }
 
-template <typename io_t, int NS, int KW, int N>
+template <typename io_t, int CH, int NS, int KS, int N, int OCC>
 hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
   constexpr int T = 16;
-  const dim3 block(64 * KW);
-  const unsigned gx = (unsigned)((p.D + kChan - 1) / kChan);
+  const dim3 block(CH * KS);
+  const unsigned gx = (unsigned)((p.D + CH - 1) / CH);
   if (p.nseg > 1) {
     const dim3 grid_a(gx, (unsigned)p.B, (unsigned)(p.nseg - 1));
-    hipLaunchKernelGGL((scan_kernel<io_t, NS, KW, T, N, false>), grid_a, block, 0, stream, p);
+    hipLaunchKernelGGL((scan_kernel<io_t, CH, NS, KS, T, N, false, OCC>), grid_a, block, 0, stream, p);
     const int64_t chains = p.B * p.D * p.N;
     hipLaunchKernelGGL(scan_carry_kernel, dim3((unsigned)((chains + 255) / 256)), dim3(256), 0, stream, p);
   }
   const dim3 grid(gx, (unsigned)p.B, (unsigned)p.nseg);
-  hipLaunchKernelGGL((scan_kernel<io_t, NS, KW, T, N, true>), grid, block, 0, stream, p);
+  hipLaunchKernelGGL((scan_kernel<io_t, CH, NS, KS, T, N, true, OCC>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
 template <typename io_t>
 hipError_t launch_io(const ScanParams& p, hipStream_t stream) {
   switch (p.N) {
-    case 1: return launch_typed<io_t, 1, 1, 1>(p, stream);
-    case 2: return launch_typed<io_t, 2, 1, 2>(p, stream);
-    case 4: return launch_typed<io_t, 4, 1, 4>(p, stream);
-    case 8: return launch_typed<io_t, 4, 2, 8>(p, stream);
-    case 16: return launch_typed<io_t, 4, 4, 16>(p, stream);
+    case 1: return launch_typed<io_t, 64, 1, 1, 1, 1>(p, stream);
+    case 2: return launch_typed<io_t, 64, 2, 1, 2, 1>(p, stream);
+    case 4: return launch_typed<io_t, 64, 2, 2, 4, 1>(p, stream);
+    case 8: return launch_typed<io_t, 32, 2, 4, 8, 1>(p, stream);
+    case 16: return launch_typed<io_t, 32, 2, 8, 16, 5>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

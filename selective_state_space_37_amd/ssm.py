@@ -106,7 +106,7 @@ def workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 
 
 def scan_fwd(x, delta, A, Bm, Cm, *, delta_bias=None, delta_softplus=False, Dskip=None, z=None,
-             h0=None, return_state=True, segment_len: Optional[int] = None, y=None,
+             h0=None, return_state=True, segment_len: Optional[int] = None, y=None, h_last=None,
              ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Selective scan: x, delta, z [B, L, D]; A [D, N] fp32; Bm, Cm [B, L, N]; -> (y, h_last)."""
     lib = load()
@@ -124,7 +124,10 @@ def scan_fwd(x, delta, A, Bm, Cm, *, delta_bias=None, delta_softplus=False, Dski
     _dev(h0, "h0", torch.float32, (Bsz, D, N))
     if y is None:
         y = torch.empty_like(x)
-    h_last = torch.empty((Bsz, D, N), dtype=torch.float32, device=x.device) if return_state else None
+    _dev(y, "y", io, (Bsz, L, D))
+    if h_last is None and return_state:
+        h_last = torch.empty((Bsz, D, N), dtype=torch.float32, device=x.device)
+    _dev(h_last, "h_last", torch.float32, (Bsz, D, N))
     code = _io_code(x)
     if segment_len is None:
         nb = lib.ssm_scan_fwd_workspace_bytes(Bsz, L, D, N, code)

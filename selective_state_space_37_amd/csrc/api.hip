@@ -250,14 +250,12 @@ ssm_status ssd_chunk_fwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, 
   if (ws_bytes < need) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, need);
   if (!aligned16(ws)) return fail(SSM_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
   if (overlaps(ws, need, y, tok)) return fail(SSM_ERR_INVALID_ARGUMENT, "workspace overlaps y");
-  const int64_t nch = (L + chunk - 1) / chunk;
   ssm::SsdParams p{};
   p.B = B; p.L = L; p.H = H; p.P = P; p.N = N; p.Q = chunk;
   p.x = x; p.delta = delta; p.z = z; p.Bm = Bm; p.Cm = Cm;
   p.delta_bias = delta_bias; p.A = A; p.Dskip = Dskip; p.h0 = h0;
   p.y = y; p.h_last = h_last; p.delta_softplus = delta_softplus ? 1 : 0;
-  p.ws_state = static_cast<float*>(ws);
-  p.ws_sum = p.ws_state + B * nch * H * P * N;
+  ssm::ssd_workspace_carve(p, ws);
   return from_hip(ssm::launch_ssd(p, st), "ssd_chunk_fwd launch");
 }
 

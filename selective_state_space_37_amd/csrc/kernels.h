@@ -68,11 +68,15 @@ struct SsdParams {
   void* y;
   float* h_last;           // nullable
   int delta_softplus;
-  float* ws_state;         // [B, nchunks, H, P, N]
-  float* ws_sum;           // [B, nchunks, H]
+  void* ws_hin;            // bf16 [B, nchunks, H, P, N]: state entering each chunk
+  float* ws_G;             // [B, nchunks, Q, Q]: C_i . B_j inside each chunk
+  void* ws_Bt;             // bf16 [B, nchunks, N, Q]: B of each chunk, transposed
+  float2* ws_sphi;         // [B, nchunks, H, Q]: (inclusive cumulative Delta, ZOH input scale)
 };
 
 size_t ssd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t Q);
+// Point the workspace fields of p at their parts of ws (ssd_workspace_bytes() bytes).
+void ssd_workspace_carve(SsdParams& p, void* ws);
 hipError_t launch_ssd(const SsdParams& p, hipStream_t stream);
 
 }  // namespace ssm

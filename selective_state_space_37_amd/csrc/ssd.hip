@@ -6,9 +6,13 @@
 // chunks of Q tokens; inside a chunk that masked product runs on the matrix cores, and only the
 // state passes between chunks. With zero-order hold the input of step j enters with the scale
 // phi_j = expm1(a Delta_j) / a, and with S the inclusive cumulative sum of Delta in the chunk:
-//   state kernel : s_c[p, n] = sum_j exp(a (S_last - S_j)) phi_j x_j[p] B_j[n]     (MFMA, K = Q)
-//   pass kernel  : h_c = exp(a S_last,c) h_{c-1} + s_c, in float32, over the chunks of a head
-//   output kernel: y_i = sum_{j<=i} (C_i . B_j) exp(a (S_i - S_j)) phi_j x_j        (MFMA, K = N, Q)
+//   prep kernel  : per (batch, chunk), G = C B^T (Q x Q, MFMA, shared by all heads) and a
+//                  transposed copy of B for the state kernel's operand layout
+//   state kernel : per (batch, head, quarter of P), sequential over the chunks with the state
+//                  in MFMA accumulators: store h_{c-1} (bf16, the carry the outputs need), then
+//                  h_c = exp(a S_last) h_{c-1} + sum_j exp(a (S_last - S_j)) phi_j x_j B_j^T
+//   output kernel: per (batch, chunk, head),
+//                  y_i = sum_{j<=i} G_ij exp(a (S_i - S_j)) phi_j x_j                 (MFMA, K = Q)
 //                      + exp(a S_i) C_i . h_{c-1}                                    (MFMA, K = N)
 //                      (+ D x_i, gate)
 // Decays are always formed from differences of cumulative sums inside one chunk, so no
@@ -77,201 +81,344 @@ __device__ void chunk_prologue(const SsdParams& p, int64_t b, int64_t c, int64_t
 }
 
 // Stage x[b, chunk, h, :] transposed into LDS as bf16 Xt[p][j] (row stride Q + 8), optionally
-// scaled per token by sScale[j].
+// scaled per token by sScale[j]. Each thread takes two consecutive tokens so that every LDS write
+// is one 32-bit word holding the pair (j, j + 1) of one row p.
 template <int Q>
 __device__ void stage_x_transposed(const SsdParams& p, int64_t b, int64_t c, int64_t h,
                                    __bf16* Xt, const float* sScale) {
   const bf16_t* xg = static_cast<const bf16_t*>(p.x);
-  for (int g = threadIdx.x; g < Q * (kP / 8); g += blockDim.x) {
-    const int j = g / (kP / 8), pg = g % (kP / 8);
+  uint32_t* X32 = reinterpret_cast<uint32_t*>(Xt);
+  for (int g = threadIdx.x; g < (Q / 2) * (kP / 8); g += blockDim.x) {
+    const int jp = g / (kP / 8), pg = g % (kP / 8);
+    const int j = 2 * jp;
+    uint32_t w0[4] = {0, 0, 0, 0}, w1[4] = {0, 0, 0, 0};
     const int64_t t = c * Q + j;
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    if (t < p.L) raw = *reinterpret_cast<const uint4*>(xg + ((b * p.L + t) * p.H + h) * kP + pg * 8);
-    const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
-    const float sc = sScale ? sScale[j] : 1.0f;
+    if (t < p.L) {
+      const uint4 r = *reinterpret_cast<const uint4*>(xg + ((b * p.L + t) * p.H + h) * kP + pg * 8);
+      w0[0] = r.x; w0[1] = r.y; w0[2] = r.z; w0[3] = r.w;
+    }
+    if (t + 1 < p.L) {
+      const uint4 r = *reinterpret_cast<const uint4*>(xg + ((b * p.L + t + 1) * p.H + h) * kP + pg * 8);
+      w1[0] = r.x; w1[1] = r.y; w1[2] = r.z; w1[3] = r.w;
+    }
+    const float s0 = sScale ? sScale[j] : 1.0f, s1 = sScale ? sScale[j + 1] : 1.0f;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const float f = (q & 1) ? bf16_hi(wv[q >> 1]) : bf16_lo(wv[q >> 1]);
-      Xt[(pg * 8 + q) * (Q + 8) + j] = (__bf16)(f * sc);
+      const float f0 = (q & 1) ? bf16_hi(w0[q >> 1]) : bf16_lo(w0[q >> 1]);
+      const float f1 = (q & 1) ? bf16_hi(w1[q >> 1]) : bf16_lo(w1[q >> 1]);
+      X32[(pg * 8 + q) * ((Q + 8) / 2) + jp] =
+          (uint32_t)f32_to_bf16(f0 * s0) | ((uint32_t)f32_to_bf16(f1 * s1) << 16);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------- step sizes
+// grid (H, chunks, B): per chunk and head, the inclusive cumulative sum S_j of the step sizes and
+// the ZOH input scale phi_j = expm1(a Delta_j) / a, for the state and output kernels.
+template <int Q>
+__global__ __launch_bounds__(256) void ssd_cumsum_kernel(SsdParams p) {
+  __shared__ float sS[Q], sPhi[Q], sTot[4];
+  const int64_t h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
+  const int64_t nch = gridDim.y;
+  chunk_prologue<Q>(p, b, c, h, p.A[h], sS, sPhi, sTot);
+  const int tid = threadIdx.x;
+  if (tid < Q) p.ws_sphi[((b * nch + c) * p.H + h) * Q + tid] = make_float2(sS[tid], sPhi[tid]);
+}
+
+// ---------------------------------------------------------------------------- prep
+// grid (4, chunks, B): part `part` transposes states [part N/4, (part+1) N/4) of B and computes
+// every fourth lower-triangular 16 x 16 tile of G (row blocks ib, column tiles jt <= ib).
+template <int Q, int N>
+__global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
+  const int part = blockIdx.x;
+  const int64_t c = blockIdx.y, b = blockIdx.z;
+  const int64_t nch = gridDim.y;
+  const int tid = threadIdx.x;
+  const bf16_t* Bg = static_cast<const bf16_t*>(p.Bm);
+  const bf16_t* Cg = static_cast<const bf16_t*>(p.Cm);
+  // transposed B: Bt[n][j], 8 tokens per 16-byte store
+  bf16_t* Bt = static_cast<bf16_t*>(p.ws_Bt) + (b * nch + c) * (int64_t)(N * Q);
+  constexpr int NQ = N / 4;
+  for (int it = tid; it < NQ * (Q / 8); it += 256) {
+    const int n = part * NQ + it / (Q / 8);
+    const int j0 = (it % (Q / 8)) * 8;
+    uint32_t wv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t lo = 0, hi = 0;
+      const int64_t t0 = c * Q + j0 + 2 * q;
+      if (t0 < p.L) lo = Bg[(b * p.L + t0) * N + n].bits;
+      if (t0 + 1 < p.L) hi = Bg[(b * p.L + t0 + 1) * N + n].bits;
+      wv[q] = lo | (hi << 16);
+    }
+    *reinterpret_cast<uint4*>(Bt + (int64_t)n * Q + j0) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  }
+  // G tiles
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  constexpr int NIB = Q / 16, KS = N / 32, NTILES = NIB * (NIB + 1) / 2;
+  float* G = p.ws_G + (b * nch + c) * (int64_t)(Q * Q);
+  for (int k = part * 4 + w; k < NTILES; k += 16) {
+    int ib = 0, rem = k;
+    while (rem > ib) { rem -= ib + 1; ++ib; }
+    const int jt = rem;
+    const int64_t ti = c * Q + ib * 16 + r16, tj = c * Q + jt * 16 + r16;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 ca = ti < p.L ? load_frag(Cg + (b * p.L + ti) * N + ks * 32 + 8 * g) : zero_frag();
+      const bf16x8 bb = tj < p.L ? load_frag(Bg + (b * p.L + tj) * N + ks * 32 + 8 * g) : zero_frag();
+      acc = mfma16(ca, bb, acc);  // D[i][j] = sum_n C_i[n] B_j[n]
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) G[(int64_t)(ib * 16 + 4 * g + r) * Q + jt * 16 + r16] = acc[r];
   }
 }
 
 // ---------------------------------------------------------------------------- chunk states
+// grid (H, B), 512 threads: one head, sequential over the chunks. Wave w owns the state block
+// p in [16 pq, 16 pq + 16) x n in [NH w2 .. NH (w2 + 1)) with pq = w / 2, w2 = w % 2 and
+// NH = N / 2, as NTW = N / 32 MFMA D tiles: acc[k][r] = h[p = 16 pq + 4 g + r][n = (w2 NTW + k) 16
+// + lane % 16]. Per chunk the transposed B (shared by every head) and the scaled, transposed x of
+// the head are staged in LDS once for all eight waves; the next chunk's inputs are loaded into
+// registers while the current chunk's products run.
 template <int Q, int N>
-__global__ __launch_bounds__(256) void ssd_state_kernel(SsdParams p) {
-  __shared__ __attribute__((aligned(16))) __bf16 Xt[kP * (Q + 8)];
-  __shared__ __attribute__((aligned(16))) __bf16 Bt[N * (Q + 8)];
-  __shared__ float sS[Q], sPhi[Q], sW[Q], sTot[4];
-  const int64_t h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
-  const int64_t nch = gridDim.y;
-  const float a = p.A[h];
-  const float a2 = a * kLog2e;
-  chunk_prologue<Q>(p, b, c, h, a, sS, sPhi, sTot);
+__global__ __launch_bounds__(512) void ssd_state_kernel(SsdParams p) {
+  constexpr int KQ = Q / 32;                 // K steps over a chunk
+  constexpr int NTW = N / 32;                // state tiles per wave
+  constexpr int XPAIRS = Q / 2 * 4;          // (token pair, 16-channel group) items of x
+  constexpr int BT16 = N * Q / 8;            // 16-byte pieces of B^T
+  constexpr int BT_PER = (BT16 + 511) / 512;
+  __shared__ __attribute__((aligned(16))) __bf16 Xs[kP * (Q + 8)];
+  __shared__ __attribute__((aligned(16))) __bf16 Bs[N * (Q + 8)];
+  const int64_t h = blockIdx.x, b = blockIdx.y;
+  const int64_t nch = (p.L + Q - 1) / Q;
   const int tid = threadIdx.x;
-  const float s_last = sS[Q - 1];
-  if (tid < Q) sW[tid] = exp2_fast(a2 * (s_last - sS[tid])) * sPhi[tid];
-  if (tid == 0) p.ws_sum[(b * nch + c) * p.H + h] = s_last;
-  __syncthreads();
-  stage_x_transposed<Q>(p, b, c, h, Xt, sW);
-  const bf16_t* Bg = static_cast<const bf16_t*>(p.Bm);
-  for (int g = tid; g < Q * (N / 8); g += 256) {
-    const int j = g / (N / 8), ng = g % (N / 8);
-    const int64_t t = c * Q + j;
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    if (t < p.L) raw = *reinterpret_cast<const uint4*>(Bg + (b * p.L + t) * N + ng * 8);
-    const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint16_t bits = (q & 1) ? (uint16_t)(wv[q >> 1] >> 16) : (uint16_t)(wv[q >> 1] & 0xffff);
-      Bt[(ng * 8 + q) * (Q + 8) + j] = __builtin_bit_cast(__bf16, bits);
-    }
-  }
-  __syncthreads();
-
   const int lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
-  constexpr int NT = N / 16;           // n tiles
-  constexpr int NTW = NT / 4;          // n tiles per wave
-  f32x4 acc[4][NTW];
-#pragma unroll
-  for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-    for (int k = 0; k < NTW; ++k) acc[pt][k] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int k0 = 0; k0 < Q; k0 += 32) {
-    bf16x8 av[4], bv[NTW];
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
-      av[pt] = *reinterpret_cast<const bf16x8*>(&Xt[(pt * 16 + r16) * (Q + 8) + k0 + 8 * g]);
-#pragma unroll
-    for (int k = 0; k < NTW; ++k)
-      bv[k] = *reinterpret_cast<const bf16x8*>(&Bt[((w * NTW + k) * 16 + r16) * (Q + 8) + k0 + 8 * g]);
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-      for (int k = 0; k < NTW; ++k) acc[pt][k] = mfma16(av[pt], bv[k], acc[pt][k]);
-  }
-  float* out = p.ws_state + ((b * nch + c) * p.H + h) * (int64_t)(kP * N);
-#pragma unroll
-  for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-    for (int k = 0; k < NTW; ++k)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        out[(pt * 16 + 4 * g + r) * N + (w * NTW + k) * 16 + r16] = acc[pt][k][r];
-}
-
-// ---------------------------------------------------------------------------- state pass
-// One thread per (b, h, p, n): h_in[c] = state entering chunk c (written over s_c).
-__global__ __launch_bounds__(256) void ssd_pass_kernel(SsdParams p, int64_t nch) {
-  const int64_t PN = kP * p.N;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= p.B * p.H * PN) return;
-  const int64_t e = i % PN;
-  const int64_t h = (i / PN) % p.H;
-  const int64_t b = i / (PN * p.H);
+  const int pq = w >> 1, w2 = w & 1;
   const float a2 = p.A[h] * kLog2e;
-  float st = p.h0 ? p.h0[(b * p.H + h) * PN + e] : 0.f;
+  const int64_t PN = (int64_t)kP * N;
+  auto st_idx = [&](int k, int r) { return (int64_t)(16 * pq + 4 * g + r) * N + (w2 * NTW + k) * 16 + r16; };
+
+  f32x4 acc[NTW];
+#pragma unroll
+  for (int k = 0; k < NTW; ++k)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[k][r] = p.h0 ? p.h0[(b * p.H + h) * PN + st_idx(k, r)] : 0.f;
+  const bf16_t* xg = static_cast<const bf16_t*>(p.x);
+  bf16_t* hin_all = static_cast<bf16_t*>(p.ws_hin);
+  const bf16_t* Bt_all = static_cast<const bf16_t*>(p.ws_Bt);
+
+  // x item of this thread: tokens (2 jp, 2 jp + 1), channels [16 pg, 16 pg + 16)
+  const int jp = tid >> 2, pg = tid & 3;
+  const bool x_item = tid < XPAIRS;
+  struct ChunkIn {
+    uint4 x[2][2];      // two tokens x 16 channels
+    float2 sphi[2];     // (S_j, phi_j) of the two tokens
+    float s_last;
+    uint4 bt[BT_PER];   // pieces of the chunk's B^T
+  };
+  auto load_chunk = [&](int64_t c, ChunkIn& in) {
+    const float2* sp = p.ws_sphi + ((b * nch + c) * p.H + h) * Q;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = 2 * jp + u;
+      const int64_t t = c * Q + j;
+      const bool ok = x_item && t < p.L;
+      in.x[u][0] = in.x[u][1] = make_uint4(0, 0, 0, 0);
+      if (ok) {
+        const uint4* src = reinterpret_cast<const uint4*>(xg + ((b * p.L + t) * p.H + h) * kP + 16 * pg);
+        in.x[u][0] = src[0];
+        in.x[u][1] = src[1];
+      }
+      in.sphi[u] = x_item ? sp[j] : make_float2(0.f, 0.f);
+    }
+    in.s_last = sp[Q - 1].x;
+    const uint4* bt = reinterpret_cast<const uint4*>(Bt_all + (b * nch + c) * (int64_t)(N * Q));
+#pragma unroll
+    for (int k = 0; k < BT_PER; ++k) {
+      const int e = tid + 512 * k;
+      in.bt[k] = e < BT16 ? bt[e] : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  ChunkIn cur, nxt;
+  load_chunk(0, cur);
   for (int64_t c = 0; c < nch; ++c) {
-    float* slot = p.ws_state + ((b * nch + c) * p.H + h) * PN + e;
-    const float sc = *slot;
-    *slot = st;
-    st = fmaf(exp2_fast(a2 * p.ws_sum[(b * nch + c) * p.H + h]), st, sc);
+    // stage B^T and the decay-scaled x^T of chunk c
+#pragma unroll
+    for (int k = 0; k < BT_PER; ++k) {
+      const int e = tid + 512 * k;
+      if (e < BT16) {
+        const int n = e / (Q / 8), j8 = (e % (Q / 8)) * 8;
+        *reinterpret_cast<uint4*>(&Bs[n * (Q + 8) + j8]) = cur.bt[k];
+      }
+    }
+    if (x_item) {
+      float wj[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) wj[u] = exp2_fast(a2 * (cur.s_last - cur.sphi[u].x)) * cur.sphi[u].y;
+      uint32_t* X32 = reinterpret_cast<uint32_t*>(Xs);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const uint4 v0 = cur.x[0][q >> 3], v1 = cur.x[1][q >> 3];
+        const uint32_t u0 = ((q & 7) >> 1) == 0 ? v0.x : ((q & 7) >> 1) == 1 ? v0.y : ((q & 7) >> 1) == 2 ? v0.z : v0.w;
+        const uint32_t u1 = ((q & 7) >> 1) == 0 ? v1.x : ((q & 7) >> 1) == 1 ? v1.y : ((q & 7) >> 1) == 2 ? v1.z : v1.w;
+        const float f0 = (q & 1) ? bf16_hi(u0) : bf16_lo(u0);
+        const float f1 = (q & 1) ? bf16_hi(u1) : bf16_lo(u1);
+        X32[(16 * pg + q) * ((Q + 8) / 2) + jp] =
+            (uint32_t)f32_to_bf16(f0 * wj[0]) | ((uint32_t)f32_to_bf16(f1 * wj[1]) << 16);
+      }
+    }
+    const float decay = exp2_fast(a2 * cur.s_last);
+    if (c + 1 < nch) load_chunk(c + 1, nxt);
+    // the state entering chunk c, for the output kernel; then decay it over the chunk
+    bf16_t* hin = hin_all + ((b * nch + c) * p.H + h) * PN;
+#pragma unroll
+    for (int k = 0; k < NTW; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        hin[st_idx(k, r)].bits = f32_to_bf16(acc[k][r]);
+        acc[k][r] *= decay;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq) {
+      const bf16x8 xa = *reinterpret_cast<const bf16x8*>(&Xs[(16 * pq + r16) * (Q + 8) + kq * 32 + 8 * g]);
+#pragma unroll
+      for (int k = 0; k < NTW; ++k) {
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&Bs[((w2 * NTW + k) * 16 + r16) * (Q + 8) + kq * 32 + 8 * g]);
+        acc[k] = mfma16(xa, bv, acc[k]);
+      }
+    }
+    __syncthreads();
+    cur = nxt;
   }
-  if (p.h_last) p.h_last[(b * p.H + h) * PN + e] = st;
+  if (p.h_last) {
+#pragma unroll
+    for (int k = 0; k < NTW; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p.h_last[(b * p.H + h) * PN + st_idx(k, r)] = acc[k][r];
+  }
 }
 
 // ---------------------------------------------------------------------------- outputs
+// Decay of a mask entry (i, j), j <= i: exp(a (S_i - S_j)) phi_j. For a tile whose 16 tokens j all
+// precede row i (off the diagonal) it factors through the tile's last token e:
+//   exp(a (S_i - S_e)) * [exp(a (S_e - S_j)) phi_j],
+// both exponents <= 0 (no overflow); the bracket depends on j only and is tabulated once per
+// chunk (sCp), the first factor is one exp per lane per tile. Diagonal tiles use the direct form.
 template <int Q, int N>
 __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 Xt[kP * (Q + 8)];
-  __shared__ float sS[Q], sPhi[Q], sTot[4];
+  __shared__ __attribute__((aligned(16))) float sCp[Q];
+  __shared__ float sS[Q], sPhi[Q];
   const int64_t h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
   const int64_t nch = gridDim.y;
-  const float a = p.A[h];
-  const float a2 = a * kLog2e;
-  chunk_prologue<Q>(p, b, c, h, a, sS, sPhi, sTot);
+  const float a2 = p.A[h] * kLog2e;
+  const int tid = threadIdx.x;
+  {
+    const float2* sp = p.ws_sphi + ((b * nch + c) * p.H + h) * Q;
+    if (tid < Q) {
+      const float2 v = sp[tid];
+      sS[tid] = v.x;
+      sPhi[tid] = v.y;
+      sCp[tid] = exp2_fast(a2 * (sp[tid | 15].x - v.x)) * v.y;
+    }
+  }
   stage_x_transposed<Q>(p, b, c, h, Xt, nullptr);
   __syncthreads();
 
-  const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
   constexpr int NIB = Q / 16;   // 16-row blocks of the chunk
   constexpr int KS = N / 32;    // K steps over the state dimension
-  const bf16_t* Bg = static_cast<const bf16_t*>(p.Bm);
   const bf16_t* Cg = static_cast<const bf16_t*>(p.Cm);
-  const float* hin = p.ws_state + ((b * nch + c) * p.H + h) * (int64_t)(kP * N);
+  const float* G = p.ws_G + (b * nch + c) * (int64_t)(Q * Q);
+  const bf16_t* hin = static_cast<const bf16_t*>(p.ws_hin) + ((b * nch + c) * p.H + h) * (int64_t)(kP * N);
   const float dsk = p.Dskip ? p.Dskip[h] : 0.f;
   const bf16_t* zg = static_cast<const bf16_t*>(p.z);
   bf16_t* yg = static_cast<bf16_t*>(p.y);
 
   // Balanced triangle: block x and block NIB-1-x hold NIB+1 tiles together.
   constexpr int kBlocksPerWave = NIB >= 8 ? NIB / 4 : 1;
-  for (int kb = 0; kb < kBlocksPerWave; ++kb) {
-    int ib;
-    if (NIB >= 8) {
-      const int pair = w + 4 * (kb >> 1);
-      ib = (kb & 1) ? (NIB - 1 - pair) : pair;
-    } else {
-      ib = w;
-      if (ib >= NIB) break;
-    }
-    const int i0 = ib * 16;
-    const int il = i0 + r16;                  // this lane's row (A operand / G^T column)
-    const int64_t ti = c * Q + il;
-    const bool ti_ok = ti < p.L;
-    const float Si = sS[il];
-    bf16x8 cf[KS];
+  auto block_of = [&](int kb) {
+    if (NIB < 8) return w;
+    const int pair = w + 4 * (kb >> 1);
+    return (kb & 1) ? (NIB - 1 - pair) : pair;
+  };
+  // carried-state fragments (the B operand of the carried term), the same for every row block
+  bf16x8 hf[KS][4];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) hf[ks][pt] = load_frag(hin + (pt * 16 + r16) * N + ks * 32 + 8 * g);
+  auto load_c = [&](int ib, bf16x8 out[KS]) {
+    const int64_t ti = c * Q + ib * 16 + r16;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      cf[ks] = ti_ok ? load_frag(Cg + (b * p.L + ti) * N + ks * 32 + 8 * g) : zero_frag();
+      out[ks] = ti < p.L ? load_frag(Cg + (b * p.L + ti) * N + ks * 32 + 8 * g) : zero_frag();
+  };
+  bf16x8 cnext[KS];
+  if (NIB >= 4 || w < NIB) load_c(block_of(0), cnext);
+  for (int kb = 0; kb < kBlocksPerWave; ++kb) {
+    const int ib = block_of(kb);
+    if (ib >= NIB) break;
+    bf16x8 cf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) cf[ks] = cnext[ks];
+    if (kb + 1 < kBlocksPerWave) load_c(block_of(kb + 1), cnext);
+    const int i0 = ib * 16;
+    const int il = i0 + r16;                  // this lane's row of M (A operand)
+    const float Si = sS[il];
+    const float* Grow = G + (int64_t)il * Q;  // G[il][j]: the lane's four j of a tile are contiguous
 
     f32x4 acc[4];
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // carried state: exp(a S_i) C_i . h_in[p, :]
-    const float eSi = exp2_fast(a2 * Si);
+    {
+      const float eSi = exp2_fast(a2 * Si);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 av;
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 av;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) av[q] = (__bf16)((float)cf[ks][q] * eSi);
+        for (int q = 0; q < 8; ++q) av[q] = (__bf16)((float)cf[ks][q] * eSi);
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const float* hp = hin + (pt * 16 + r16) * N + ks * 32 + 8 * g;
-        const float4 h0v = *reinterpret_cast<const float4*>(hp);
-        const float4 h1v = *reinterpret_cast<const float4*>(hp + 4);
-        bf16x8 bv;
-        bv[0] = (__bf16)h0v.x; bv[1] = (__bf16)h0v.y; bv[2] = (__bf16)h0v.z; bv[3] = (__bf16)h0v.w;
-        bv[4] = (__bf16)h1v.x; bv[5] = (__bf16)h1v.y; bv[6] = (__bf16)h1v.z; bv[7] = (__bf16)h1v.w;
-        acc[pt] = mfma16(av, bv, acc[pt]);
+        for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16(av, hf[ks][pt], acc[pt]);
       }
     }
 
-    // within the chunk: masked (C_i . B_j) decay phi_j times x_j, two 16-token j tiles per product
+    // within the chunk: masked G_ij decay phi_j times x_j, two 16-token j tiles per product
+    float4 gcur[2], gnext[2];
+    gcur[0] = *reinterpret_cast<const float4*>(Grow + 4 * g);
+    gcur[1] = ib >= 1 ? *reinterpret_cast<const float4*>(Grow + 16 + 4 * g) : make_float4(0.f, 0.f, 0.f, 0.f);
     for (int jp = 0; 2 * jp <= ib; ++jp) {
+      gnext[0] = (2 * jp + 2 <= ib) ? *reinterpret_cast<const float4*>(Grow + (2 * jp + 2) * 16 + 4 * g)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+      gnext[1] = (2 * jp + 3 <= ib) ? *reinterpret_cast<const float4*>(Grow + (2 * jp + 3) * 16 + 4 * g)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
       float m[8];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int jt = 2 * jp + half;
-        if (jt > ib) {
+        const float gv[4] = {gcur[half].x, gcur[half].y, gcur[half].z, gcur[half].w};
+        const int j0 = jt * 16 + 4 * g;
+        if (jt < ib) {
+          const float r = exp2_fast(a2 * (Si - sS[jt * 16 + 15]));
+          const float4 cp = *reinterpret_cast<const float4*>(&sCp[j0]);
+          m[half * 4 + 0] = gv[0] * r * cp.x;
+          m[half * 4 + 1] = gv[1] * r * cp.y;
+          m[half * 4 + 2] = gv[2] * r * cp.z;
+          m[half * 4 + 3] = gv[3] * r * cp.w;
+        } else if (jt == ib) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = j0 + r;
+            m[half * 4 + r] = (j <= il) ? gv[r] * exp2_fast(a2 * (Si - sS[j])) * sPhi[j] : 0.f;
+          }
+        } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) m[half * 4 + r] = 0.f;
-          continue;
-        }
-        const int64_t tj = c * Q + jt * 16 + r16;
-        const bool tj_ok = tj < p.L;
-        f32x4 gacc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 bfr = tj_ok ? load_frag(Bg + (b * p.L + tj) * N + ks * 32 + 8 * g) : zero_frag();
-          gacc = mfma16(bfr, cf[ks], gacc);   // G^T[j][i]
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = jt * 16 + 4 * g + r;
-          m[half * 4 + r] = (j <= il) ? gacc[r] * exp2_fast(a2 * (Si - sS[j])) * sPhi[j] : 0.f;
         }
       }
       bf16x8 av;
@@ -280,15 +427,13 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
       const int jb = jp * 32;
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
-        const __bf16* xr = &Xt[(pt * 16 + r16) * (Q + 8) + jb + 4 * g];
-        bf16x8 bv;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          bv[q] = xr[q];
-          bv[4 + q] = xr[16 + q];
-        }
-        acc[pt] = mfma16(av, bv, acc[pt]);
+        const uint2 lo = *reinterpret_cast<const uint2*>(&Xt[(pt * 16 + r16) * (Q + 8) + jb + 4 * g]);
+        const uint2 hi = *reinterpret_cast<const uint2*>(&Xt[(pt * 16 + r16) * (Q + 8) + jb + 16 + 4 * g]);
+        const uint4 pk = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        acc[pt] = mfma16(av, __builtin_bit_cast(bf16x8, pk), acc[pt]);
       }
+      gcur[0] = gnext[0];
+      gcur[1] = gnext[1];
     }
 
     // epilogue: D term, gate, store y[b, t, h, p]
@@ -314,19 +459,37 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
 template <int Q, int N>
 hipError_t launch_qn(const SsdParams& p, hipStream_t stream) {
   const int64_t nch = (p.L + Q - 1) / Q;
-  const dim3 grid((unsigned)p.H, (unsigned)nch, (unsigned)p.B);
-  hipLaunchKernelGGL((ssd_state_kernel<Q, N>), grid, dim3(256), 0, stream, p);
-  const int64_t chains = p.B * p.H * kP * p.N;
-  hipLaunchKernelGGL(ssd_pass_kernel, dim3((unsigned)((chains + 255) / 256)), dim3(256), 0, stream, p, nch);
-  hipLaunchKernelGGL((ssd_out_kernel<Q, N>), grid, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((ssd_cumsum_kernel<Q>), dim3((unsigned)p.H, (unsigned)nch, (unsigned)p.B), dim3(256), 0,
+                     stream, p);
+  hipLaunchKernelGGL((ssd_prep_kernel<Q, N>), dim3(4, (unsigned)nch, (unsigned)p.B), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((ssd_state_kernel<Q, N>), dim3((unsigned)p.H, (unsigned)p.B), dim3(512), 0, stream, p);
+  hipLaunchKernelGGL((ssd_out_kernel<Q, N>), dim3((unsigned)p.H, (unsigned)nch, (unsigned)p.B), dim3(256), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Workspace: carried states (bf16), G per chunk (float), transposed B per chunk (bf16),
+// (S, phi) per chunk, head and token (float2), each 256-byte aligned.
+static size_t ssd_align(size_t n) { return (n + 255) & ~(size_t)255; }
+
 size_t ssd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t Q) {
   const int64_t nch = (L + Q - 1) / Q;
-  return (size_t)(B * nch * H * P * N) * sizeof(float) + (size_t)(B * nch * H) * sizeof(float) + 256;
+  return ssd_align((size_t)(B * nch * H * P * N) * 2) + ssd_align((size_t)(B * nch * Q * Q) * 4) +
+         ssd_align((size_t)(B * nch * N * Q) * 2) + ssd_align((size_t)(B * nch * H * Q) * 8);
+}
+
+void ssd_workspace_carve(SsdParams& p, void* ws) {
+  const int64_t nch = (p.L + p.Q - 1) / p.Q;
+  char* base = static_cast<char*>(ws);
+  p.ws_hin = base;
+  base += ssd_align((size_t)(p.B * nch * p.H * p.P * p.N) * 2);
+  p.ws_G = reinterpret_cast<float*>(base);
+  base += ssd_align((size_t)(p.B * nch * p.Q * p.Q) * 4);
+  p.ws_Bt = base;
+  base += ssd_align((size_t)(p.B * nch * p.N * p.Q) * 2);
+  p.ws_sphi = reinterpret_cast<float2*>(base);
 }
 
 hipError_t launch_ssd(const SsdParams& p, hipStream_t stream) {

@@ -136,7 +136,8 @@ ssm_status ssm_scan_fwd_segmented(int64_t B, int64_t L, int64_t D, int64_t N, ss
  *   without it, u = x. Then the scan step on u (u is also the input of the D term), then gate.
  *
  *   Requirements: B >= 0 (0 is a no-op), D >= 1, N in {1, 2, 4, 8, 16}, 1 <= W <= 8 when
- *   conv_state is given (conv_width is ignored otherwise); y must not overlap any input.
+ *   conv_state is given (conv_width is ignored otherwise); y must not overlap any input;
+ *   h, A and conv_w (besides the per-token tensors) are 16-byte aligned.
  */
 ssm_status ssm_state_update(int64_t B, int64_t D, int64_t N, int64_t conv_width, ssm_dtype io_dtype,
                             const void* x, const void* delta, const float* delta_bias,

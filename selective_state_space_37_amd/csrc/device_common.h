@@ -49,6 +49,9 @@ template <> struct IoTraits<float> {
     float4 v = *reinterpret_cast<const float4*>(p + i);
     out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
   }
+  __device__ __forceinline__ static void store4(float* p, int64_t i, const float v[4]) {
+    *reinterpret_cast<float4*>(p + i) = make_float4(v[0], v[1], v[2], v[3]);
+  }
   using raw4 = uint4;
   __device__ __forceinline__ static raw4 load4_raw(const float* p, int64_t i) {
     return *reinterpret_cast<const uint4*>(p + i);
@@ -73,6 +76,11 @@ template <> struct IoTraits<bf16_t> {
   }
   __device__ __forceinline__ static void load4(const bf16_t* p, int64_t i, float out[4]) {
     unpack4(load4_raw(p, i), out);
+  }
+  __device__ __forceinline__ static void store4(bf16_t* p, int64_t i, const float v[4]) {
+    const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    *reinterpret_cast<uint2*>(p + i) = make_uint2(lo, hi);
   }
   __device__ __forceinline__ static raw4 zero4() { return make_uint2(0, 0); }
 };

@@ -105,6 +105,7 @@ def step_call(lib, B=4, D=64, N=16, W=4, io=BF16, x=A_, delta=2 * A_, A=3 * A_, 
     (dict(N=5), UNSUPPORTED), (dict(D=0), INVALID), (dict(B=-1), INVALID), (dict(h=0), INVALID),
     (dict(x=0), INVALID), (dict(A=0), INVALID), (dict(conv=8 * A_, W=9), UNSUPPORTED),
     (dict(conv=8 * A_, conv_w=None), INVALID), (dict(h=6 * A_ + 4), INVALID), (dict(y=A_), INVALID),
+    (dict(A=3 * A_ + 4), INVALID), (dict(conv=8 * A_, conv_w=9 * A_ + 8), INVALID),
     (dict(io=3), INVALID),
 ])
 def test_step_rejects(lib, kw, expect):

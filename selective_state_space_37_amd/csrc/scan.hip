@@ -60,9 +60,24 @@ void scan_kernel(ScanParams p) {
 
   const int tid = threadIdx.x;
   const int64_t D = p.D, L = p.L;
-  const int64_t c0 = (int64_t)blockIdx.x * CH;
-  const int64_t b = blockIdx.y;
-  const int64_t seg = blockIdx.z;
+  // Workgroups are dispatched to the 8 XCDs round-robin by linear id. A CH-channel tile reads
+  // half of each 128-byte line at CH = 32, so tiles 2k and 2k+1 are given linear ids 8 apart
+  // (same XCD, same L2) to fetch each line from HBM once.
+  int64_t tile, b, seg;
+  {
+    const int64_t gx = gridDim.x, gxy = gx * gridDim.y;
+    const int64_t lin = blockIdx.x + gx * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+    const int64_t total = gxy * gridDim.z;
+    int64_t logical = lin;
+    if (CH < 64 && (lin | 15) < total) {
+      const int64_t r = lin & 15;
+      logical = (lin & ~(int64_t)15) + 2 * (r & 7) + (r >> 3);
+    }
+    tile = logical % gx;
+    b = (logical / gx) % gridDim.y;
+    seg = logical / gxy;
+  }
+  const int64_t c0 = tile * CH;
   const int64_t t_begin = seg * p.seg_len;
   const int64_t t_end = (t_begin + p.seg_len < L) ? t_begin + p.seg_len : L;
   const int ntiles = (int)((t_end - t_begin + T - 1) / T);

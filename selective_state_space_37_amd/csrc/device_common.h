@@ -43,6 +43,11 @@ template <typename T> struct IoTraits;
 
 template <> struct IoTraits<float> {
   __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+  // one element's raw bits (conversion deferred so the load can stay in flight)
+  __device__ __forceinline__ static uint32_t load_bits(const float* p, int64_t i) {
+    return __float_as_uint(p[i]);
+  }
+  __device__ __forceinline__ static float from_bits(uint32_t v) { return __uint_as_float(v); }
   __device__ __forceinline__ static void store(float* p, int64_t i, float v) { p[i] = v; }
   // four consecutive elements (16-byte aligned)
   __device__ __forceinline__ static void load4(const float* p, int64_t i, float out[4]) {
@@ -61,10 +66,14 @@ template <> struct IoTraits<float> {
     out[2] = __uint_as_float(r.z); out[3] = __uint_as_float(r.w);
   }
   __device__ __forceinline__ static raw4 zero4() { return make_uint4(0, 0, 0, 0); }
+  // a 16-byte chunk: four elements
+  __device__ __forceinline__ static void unpack_chunk(uint4 r, float out[4]) { unpack4(r, out); }
 };
 
 template <> struct IoTraits<bf16_t> {
   __device__ __forceinline__ static float load(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i].bits); }
+  __device__ __forceinline__ static uint32_t load_bits(const bf16_t* p, int64_t i) { return p[i].bits; }
+  __device__ __forceinline__ static float from_bits(uint32_t v) { return __uint_as_float(v << 16); }
   __device__ __forceinline__ static void store(bf16_t* p, int64_t i, float v) { p[i].bits = f32_to_bf16(v); }
   using raw4 = uint2;
   // four consecutive elements (8-byte aligned)
@@ -83,6 +92,11 @@ template <> struct IoTraits<bf16_t> {
     *reinterpret_cast<uint2*>(p + i) = make_uint2(lo, hi);
   }
   __device__ __forceinline__ static raw4 zero4() { return make_uint2(0, 0); }
+  // a 16-byte chunk: eight elements
+  __device__ __forceinline__ static void unpack_chunk(uint4 r, float out[8]) {
+    out[0] = bf16_lo(r.x); out[1] = bf16_hi(r.x); out[2] = bf16_lo(r.y); out[3] = bf16_hi(r.y);
+    out[4] = bf16_lo(r.z); out[5] = bf16_hi(r.z); out[6] = bf16_lo(r.w); out[7] = bf16_hi(r.w);
+  }
 };
 
 }  // namespace ssm

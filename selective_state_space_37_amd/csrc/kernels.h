@@ -69,7 +69,7 @@ struct SsdParams {
   float* h_last;           // nullable
   int delta_softplus;
   void* ws_hin;            // bf16 [B, nchunks, H, P, N]: state entering each chunk
-  float* ws_G;             // [B, nchunks, Q, Q]: C_i . B_j inside each chunk
+  void* ws_G;              // bf16 [B, nchunks, Q, Q]: C_i . B_j inside each chunk
   void* ws_Bt;             // bf16 [B, nchunks, N, Q]: B of each chunk, transposed
   float2* ws_sphi;         // [B, nchunks, H, Q]: (inclusive cumulative Delta, ZOH input scale)
 };

@@ -44,6 +44,18 @@ struct ScanCfg {
   static constexpr int kBCPerThr = (kBC + kThreads - 1) / kThreads;
 };
 
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their maximum (no wait).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// 16-byte chunking of a tile's B (and C) block in storage type io_t.
+template <typename io_t, int T, int N, int kThreads>
+struct BCChunks {
+  static constexpr int kPerChunk = 16 / (int)sizeof(io_t);          // elements per 16 bytes
+  static constexpr int kChunks = T * N / kPerChunk;
+  static_assert((T * N) % kPerChunk == 0, "a tile's B block is whole 16-byte chunks");
+  static_assert(kChunks <= kThreads, "one chunk per loading thread");
+};
+
 // OCC = waves per SIMD the launch plan needs resident (five at N = 16: <= 102 VGPRs per lane).
 template <typename io_t, int CH, int NS, int KS, int T, int N, bool FULL, int OCC>
 __global__ __launch_bounds__(CH * KS)
@@ -56,7 +68,10 @@ void scan_kernel(ScanParams p) {
   __shared__ __attribute__((aligned(16))) float2 s_dx[2][T][CH];          // (Delta, x)
   __shared__ __attribute__((aligned(16))) raw4 s_z[FULL ? 2 : 1][FULL ? T : 1][CH / 4];
   __shared__ __attribute__((aligned(16))) float s_bc[2][T][N][2];          // (B_n, C_n)
-  __shared__ float s_y[FULL ? KS : 1][FULL ? T : 1][CH];
+  // partial readouts per slice; at CH = 32 a wave holds two slices, whose rows are offset by 32
+  // banks so their writes do not collide
+  constexpr int kYStride = FULL ? T * CH + (CH < 64 ? 32 : 0) : 1;
+  __shared__ float s_y[FULL ? KS : 1][kYStride];
 
   const int tid = threadIdx.x;
   const int64_t D = p.D, L = p.L;
@@ -99,39 +114,63 @@ void scan_kernel(ScanParams p) {
     for (int k = 0; k < 4; ++k) bias4[k] = p.delta_bias[cgl + k];
 
   raw4 rx[Cfg::kGroupsPerThr], rd[Cfg::kGroupsPerThr], rz[Cfg::kGroupsPerThr];
-  float rB[Cfg::kBCPerThr], rC[Cfg::kBCPerThr];
+  // B and C of a whole tile are T * N consecutive elements: full tiles move them as 16-byte
+  // chunks (threads below kBCChunks), the ragged last tile element by element.
+  // B and C of a tile are T * N consecutive elements. When a row of N elements is whole 16-byte
+  // chunks they move as chunks (threads below kChunks, a chunk never straddles a row, so the
+  // ragged last tile only drops whole chunks); otherwise element by element. Either way the
+  // registers keep the raw storage bits until the tile is committed, so the loads of tile i+1
+  // stay in flight while tile i runs.
+  using BCC = BCChunks<io_t, T, N, Cfg::kThreads>;
+  constexpr bool kChunkBC = N * (int)sizeof(io_t) >= 16;
+  uint4 rbv, rcv;
+  uint32_t rB[Cfg::kBCPerThr], rC[Cfg::kBCPerThr];
+  // element offset of this thread's first loader row in the segment; tiles advance it by T D
+  const int64_t seg_row0 = b * L + t_begin;
+  const int64_t ld_base = (seg_row0 + tid / (CH / 4)) * D + cgl;
 
   auto issue_loads = [&](int tile) {
     const int64_t t0 = t_begin + (int64_t)tile * T;
+    const int64_t tile_off = (int64_t)tile * T * D;
+    const bool full_tile = t0 + T <= t_end;   // uniform: only the ragged last tile predicates rows
 #pragma unroll
     for (int k = 0; k < Cfg::kGroupsPerThr; ++k) {
       const int g = tid + k * Cfg::kThreads;
       const int r = g / (CH / 4);
-      const bool ok = (g < Cfg::kGroups) && cg_ok && (t0 + r < t_end);
-      const int64_t off = ((b * L) + t0 + r) * D + cgl;
+      const bool ok = (g < Cfg::kGroups) && cg_ok && (full_tile || t0 + r < t_end);
+      const int64_t off = ld_base + tile_off + (int64_t)(k * Cfg::kThreads / (CH / 4)) * D;
       rx[k] = ok ? Io::load4_raw(xg, off) : Io::zero4();
       rd[k] = ok ? Io::load4_raw(dg, off) : Io::zero4();
       if (has_z) rz[k] = ok ? Io::load4_raw(zg, off) : Io::zero4();
     }
+    const int64_t bc_off = (seg_row0 + (int64_t)tile * T) * N;
+    if constexpr (kChunkBC) {
+      const int r = tid * BCC::kPerChunk / N;   // the chunk's row in the tile
+      const bool ok = tid < BCC::kChunks && (full_tile || t0 + r < t_end);
+      const int64_t off = bc_off + tid * BCC::kPerChunk;
+      rbv = ok ? *reinterpret_cast<const uint4*>(Bg + off) : make_uint4(0, 0, 0, 0);
+      if (FULL) rcv = ok ? *reinterpret_cast<const uint4*>(Cg + off) : make_uint4(0, 0, 0, 0);
+    } else {
 #pragma unroll
-    for (int k = 0; k < Cfg::kBCPerThr; ++k) {
-      const int e = tid + k * Cfg::kThreads;
-      const int r = e / N;
-      const bool ok = (e < Cfg::kBC) && (t0 + r < t_end);
-      const int64_t off = ((b * L) + t0) * N + e;
-      rB[k] = ok ? Io::load(Bg, off) : 0.f;
-      if (FULL) rC[k] = ok ? Io::load(Cg, off) : 0.f;
+      for (int k = 0; k < Cfg::kBCPerThr; ++k) {
+        const int e = tid + k * Cfg::kThreads;
+        const int r = e / N;
+        const bool ok = (e < Cfg::kBC) && (full_tile || t0 + r < t_end);
+        rB[k] = ok ? Io::load_bits(Bg, bc_off + e) : 0u;
+        if (FULL) rC[k] = ok ? Io::load_bits(Cg, bc_off + e) : 0u;
+      }
     }
   };
 
   auto commit_tile = [&](int tile, int buf) {
     const int64_t t0 = t_begin + (int64_t)tile * T;
+    const bool full_tile = t0 + T <= t_end;
 #pragma unroll
     for (int k = 0; k < Cfg::kGroupsPerThr; ++k) {
       const int g = tid + k * Cfg::kThreads;
       if (g < Cfg::kGroups) {
         const int r = g / (CH / 4);
-        const bool valid = (t0 + r < t_end);
+        const bool valid = full_tile || (t0 + r < t_end);
         float xv[4], dv[4];
         Io::unpack4(rx[k], xv);
         Io::unpack4(rd[k], dv);
@@ -147,13 +186,26 @@ void scan_kernel(ScanParams p) {
         if (has_z) s_z[buf][r][cg] = rz[k];
       }
     }
+    if constexpr (kChunkBC) {
+      if (tid < BCC::kChunks) {
+        // kPerChunk consecutive (B, C) elements -> interleaved (B_n, C_n) pairs
+        float bv[BCC::kPerChunk], cv[BCC::kPerChunk];
+        Io::unpack_chunk(rbv, bv);
+        if (FULL) Io::unpack_chunk(rcv, cv);
+        float4* bc = reinterpret_cast<float4*>(&s_bc[buf][0][0][0] + 2 * tid * BCC::kPerChunk);
 #pragma unroll
-    for (int k = 0; k < Cfg::kBCPerThr; ++k) {
-      const int e = tid + k * Cfg::kThreads;
-      if (e < Cfg::kBC) {
-        float* bc = &s_bc[buf][0][0][0] + 2 * e;
-        bc[0] = rB[k];
-        if (FULL) bc[1] = rC[k];
+        for (int q = 0; q < BCC::kPerChunk / 2; ++q)
+          bc[q] = make_float4(bv[2 * q], FULL ? cv[2 * q] : 0.f, bv[2 * q + 1], FULL ? cv[2 * q + 1] : 0.f);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < Cfg::kBCPerThr; ++k) {
+        const int e = tid + k * Cfg::kThreads;
+        if (e < Cfg::kBC) {
+          float* bc = &s_bc[buf][0][0][0] + 2 * e;
+          bc[0] = Io::from_bits(rB[k]);
+          if (FULL) bc[1] = Io::from_bits(rC[k]);
+        }
       }
     }
   };
@@ -188,6 +240,7 @@ void scan_kernel(ScanParams p) {
   //      slice, slice + KS, ... of each tile (the same channel as its recurrence lane)
   const float dsk = (FULL && p.Dskip && c_ok) ? p.Dskip[c] : 0.f;
   io_t* __restrict__ yg = static_cast<io_t*>(p.y);
+  const int64_t y_base = (seg_row0 + slice) * D + c;   // token t_begin + slice; tiles add T D
 
   if (ntiles > 0) {
     issue_loads(0);
@@ -229,26 +282,37 @@ void scan_kernel(ScanParams p) {
           h[j] = fmaf(abar_t[i][j], h[j], u_t[i][j]);
           if (FULL) yp = (j == 0) ? bc[1] * h[0] : fmaf(bc[2 * j + 1], h[j], yp);
         }
-        if (FULL) s_y[slice][t0 + i][chl] = yp;
+        if (FULL) s_y[slice][(t0 + i) * CH + chl] = yp;
       }
     }
 
+    // ---- combine the KS partial readouts, D term, gate. The stores are issued only after the
+    //      next tile is committed: stores count in the same memory counter as loads, so a store
+    //      issued before the commit would make the commit wait for it as well.
+    float yout[FULL ? T / KS : 1];
     if (FULL) {
       __syncthreads();
-      // ---- combine the KS partial readouts, D term, gate, store
-      const int64_t t0 = t_begin + (int64_t)tile * T;
 #pragma unroll
       for (int k = 0; k < T / KS; ++k) {
         const int t = slice + k * KS;
-        float yv = 0.f;
+        float yv = s_y[0][t * CH + chl];
 #pragma unroll
-        for (int q = 0; q < KS; ++q) yv += s_y[q][t][chl];
+        for (int q = 1; q < KS; ++q) yv += s_y[q][t * CH + chl];
         yv = fmaf(dsk, s_dx[buf][t][chl].y, yv);
         if (has_z) yv *= silu(Io::load(reinterpret_cast<const io_t*>(&s_z[buf][t][0]), chl));
-        if (c_ok && t0 + t < t_end) Io::store(yg, ((b * L) + t0 + t) * D + c, yv);
+        yout[k] = yv;
       }
     }
+    // every wave waits for the next tile's loads here, on every path (also waves that load
+    // nothing, and the last tile), so no other point of the loop waits for memory operations
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     if (tile + 1 < ntiles) commit_tile(tile + 1, buf ^ 1);
+    if (FULL) {
+      const int64_t t0 = t_begin + (int64_t)tile * T;
+#pragma unroll
+      for (int k = 0; k < T / KS; ++k)
+        if (c_ok && t0 + slice + k * KS < t_end) Io::store(yg, y_base + ((int64_t)tile * T + k * KS) * D, yout[k]);
+    }
     __syncthreads();
   }
 

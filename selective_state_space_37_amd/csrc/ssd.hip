@@ -8,7 +8,7 @@
 // phi_j = expm1(a Delta_j) / a, and with S the inclusive cumulative sum of Delta in the chunk:
 //   prep kernel  : per (batch, chunk), G = C B^T (Q x Q, MFMA, shared by all heads) and a
 //                  transposed copy of B for the state kernel's operand layout
-//   state kernel : per (batch, head, quarter of P), sequential over the chunks with the state
+//   state kernel : per (batch, head), sequential over the chunks with the state
 //                  in MFMA accumulators: store h_{c-1} (bf16, the carry the outputs need), then
 //                  h_c = exp(a S_last) h_{c-1} + sum_j exp(a (S_last - S_j)) phi_j x_j B_j^T
 //   output kernel: per (batch, chunk, head),
@@ -22,7 +22,8 @@
 //   A (16 x 32, M x K): row l % 16, k = 8g .. 8g+7;  B (32 x 16, K x N): col l % 16, k = 8g .. 8g+7;
 //   D (16 x 16): col l % 16, rows 4g .. 4g+3.
 // The K order inside one product is free as long as A and B agree; the output kernel uses that
-// to feed a G^T tile pair straight from the D layout into the A operand of the next product.
+// to take two 16-token tiles of j (four tokens of each per lane) in one product. The A and B
+// layouts mirror each other, so swapping the operands yields the transposed product.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -112,6 +113,28 @@ __device__ void stage_x_transposed(const SsdParams& p, int64_t b, int64_t c, int
   }
 }
 
+// Stage x[b, chunk, h, :] transposed into LDS without conversion: two consecutive tokens' 16-bit
+// values of one channel are combined into one 32-bit LDS word with a byte permute.
+template <int Q>
+__device__ void stage_x_transposed_raw(const SsdParams& p, int64_t b, int64_t c, int64_t h, __bf16* Xt) {
+  const bf16_t* xg = static_cast<const bf16_t*>(p.x);
+  uint32_t* X32 = reinterpret_cast<uint32_t*>(Xt);
+  for (int g = threadIdx.x; g < (Q / 2) * (kP / 8); g += blockDim.x) {
+    const int jp = g / (kP / 8), pg = g % (kP / 8);
+    const int64_t t = c * Q + 2 * jp;
+    uint4 r0 = make_uint4(0, 0, 0, 0), r1 = r0;
+    if (t < p.L) r0 = *reinterpret_cast<const uint4*>(xg + ((b * p.L + t) * p.H + h) * kP + pg * 8);
+    if (t + 1 < p.L) r1 = *reinterpret_cast<const uint4*>(xg + ((b * p.L + t + 1) * p.H + h) * kP + pg * 8);
+    const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w}, w1[4] = {r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      // low halves (channel 2k) and high halves (channel 2k+1) of the two tokens
+      X32[(pg * 8 + 2 * k) * ((Q + 8) / 2) + jp] = __builtin_amdgcn_perm(w1[k], w0[k], 0x05040100u);
+      X32[(pg * 8 + 2 * k + 1) * ((Q + 8) / 2) + jp] = __builtin_amdgcn_perm(w1[k], w0[k], 0x07060302u);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------- step sizes
 // grid (H, chunks, B): per chunk and head, the inclusive cumulative sum S_j of the step sizes and
 // the ZOH input scale phi_j = expm1(a Delta_j) / a, for the state and output kernels.
@@ -156,7 +179,7 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
   // G tiles
   const int lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
   constexpr int NIB = Q / 16, KS = N / 32, NTILES = NIB * (NIB + 1) / 2;
-  float* G = p.ws_G + (b * nch + c) * (int64_t)(Q * Q);
+  bf16_t* G = static_cast<bf16_t*>(p.ws_G) + (b * nch + c) * (int64_t)(Q * Q);
   for (int k = part * 4 + w; k < NTILES; k += 16) {
     int ib = 0, rem = k;
     while (rem > ib) { rem -= ib + 1; ++ib; }
@@ -170,7 +193,7 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
       acc = mfma16(ca, bb, acc);  // D[i][j] = sum_n C_i[n] B_j[n]
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) G[(int64_t)(ib * 16 + 4 * g + r) * Q + jt * 16 + r16] = acc[r];
+    for (int r = 0; r < 4; ++r) G[(int64_t)(ib * 16 + 4 * g + r) * Q + jt * 16 + r16].bits = f32_to_bf16(acc[r]);
   }
 }
 
@@ -325,14 +348,14 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
       sCp[tid] = exp2_fast(a2 * (sp[tid | 15].x - v.x)) * v.y;
     }
   }
-  stage_x_transposed<Q>(p, b, c, h, Xt, nullptr);
+  stage_x_transposed_raw<Q>(p, b, c, h, Xt);
   __syncthreads();
 
   const int lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
   constexpr int NIB = Q / 16;   // 16-row blocks of the chunk
   constexpr int KS = N / 32;    // K steps over the state dimension
   const bf16_t* Cg = static_cast<const bf16_t*>(p.Cm);
-  const float* G = p.ws_G + (b * nch + c) * (int64_t)(Q * Q);
+  const bf16_t* G = static_cast<const bf16_t*>(p.ws_G) + (b * nch + c) * (int64_t)(Q * Q);
   const bf16_t* hin = static_cast<const bf16_t*>(p.ws_hin) + ((b * nch + c) * p.H + h) * (int64_t)(kP * N);
   const float dsk = p.Dskip ? p.Dskip[h] : 0.f;
   const bf16_t* zg = static_cast<const bf16_t*>(p.z);
@@ -345,7 +368,9 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
     const int pair = w + 4 * (kb >> 1);
     return (kb & 1) ? (NIB - 1 - pair) : pair;
   };
-  // carried-state fragments (the B operand of the carried term), the same for every row block
+  // carried-state fragments (the A operand of the carried term), the same for every row block;
+  // every product here is computed transposed (channels x tokens) so a lane ends up holding four
+  // consecutive channels of one token
   bf16x8 hf[KS][4];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
@@ -367,9 +392,9 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
     for (int ks = 0; ks < KS; ++ks) cf[ks] = cnext[ks];
     if (kb + 1 < kBlocksPerWave) load_c(block_of(kb + 1), cnext);
     const int i0 = ib * 16;
-    const int il = i0 + r16;                  // this lane's row of M (A operand)
+    const int il = i0 + r16;                  // this lane's token row of M (B operand)
     const float Si = sS[il];
-    const float* Grow = G + (int64_t)il * Q;  // G[il][j]: the lane's four j of a tile are contiguous
+    const bf16_t* Grow = G + (int64_t)il * Q;  // G[il][j]: the lane's four j of a tile are contiguous
 
     f32x4 acc[4];
 #pragma unroll
@@ -384,24 +409,25 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) av[q] = (__bf16)((float)cf[ks][q] * eSi);
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16(av, hf[ks][pt], acc[pt]);
+        for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16(hf[ks][pt], av, acc[pt]);
       }
     }
 
-    // within the chunk: masked G_ij decay phi_j times x_j, two 16-token j tiles per product
-    float4 gcur[2], gnext[2];
-    gcur[0] = *reinterpret_cast<const float4*>(Grow + 4 * g);
-    gcur[1] = ib >= 1 ? *reinterpret_cast<const float4*>(Grow + 16 + 4 * g) : make_float4(0.f, 0.f, 0.f, 0.f);
+    // within the chunk: masked G_ij decay phi_j times x_j, two 16-token j tiles per product;
+    // the G tiles of the next pair are requested while the current pair is processed
+    auto load_g = [&](int jt) {
+      return jt <= ib ? *reinterpret_cast<const uint2*>(Grow + jt * 16 + 4 * g) : make_uint2(0, 0);
+    };
+    uint2 gcur[2] = {load_g(0), load_g(1)}, gnext[2];
     for (int jp = 0; 2 * jp <= ib; ++jp) {
-      gnext[0] = (2 * jp + 2 <= ib) ? *reinterpret_cast<const float4*>(Grow + (2 * jp + 2) * 16 + 4 * g)
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
-      gnext[1] = (2 * jp + 3 <= ib) ? *reinterpret_cast<const float4*>(Grow + (2 * jp + 3) * 16 + 4 * g)
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+      gnext[0] = load_g(2 * jp + 2);
+      gnext[1] = load_g(2 * jp + 3);
       float m[8];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int jt = 2 * jp + half;
-        const float gv[4] = {gcur[half].x, gcur[half].y, gcur[half].z, gcur[half].w};
+        const uint2 gw = gcur[half];
+        const float gv[4] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y)};
         const int j0 = jt * 16 + 4 * g;
         if (jt < ib) {
           const float r = exp2_fast(a2 * (Si - sS[jt * 16 + 15]));
@@ -430,27 +456,39 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
         const uint2 lo = *reinterpret_cast<const uint2*>(&Xt[(pt * 16 + r16) * (Q + 8) + jb + 4 * g]);
         const uint2 hi = *reinterpret_cast<const uint2*>(&Xt[(pt * 16 + r16) * (Q + 8) + jb + 16 + 4 * g]);
         const uint4 pk = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        acc[pt] = mfma16(av, __builtin_bit_cast(bf16x8, pk), acc[pt]);
+        acc[pt] = mfma16(__builtin_bit_cast(bf16x8, pk), av, acc[pt]);
       }
       gcur[0] = gnext[0];
       gcur[1] = gnext[1];
     }
 
-    // epilogue: D term, gate, store y[b, t, h, p]
+    // epilogue: D term, gate, store. acc[pt][r] = y[i0 + r16][pt * 16 + 4 g + r], so each lane
+    // finishes four consecutive channels of one token (8-byte loads of x and z, 8-byte store).
+    const int64_t t = c * Q + i0 + r16;
+    if (t < p.L) {
+      const int64_t orow = ((b * p.L + t) * p.H + h) * kP + 4 * g;
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = i0 + 4 * g + r;
-        const int pp = pt * 16 + r16;
-        const int64_t t = c * Q + i;
-        if (t < p.L) {
-          float v = acc[pt][r];
-          v = fmaf(dsk, (float)Xt[pp * (Q + 8) + i], v);
-          const int64_t o = ((b * p.L + t) * p.H + h) * kP + pp;
-          if (zg) v *= silu(bf16_to_f32(zg[o].bits));
-          yg[o].bits = f32_to_bf16(v);
+      for (int pt = 0; pt < 4; ++pt) {
+        const int64_t o = orow + pt * 16;
+        float v[4] = {acc[pt][0], acc[pt][1], acc[pt][2], acc[pt][3]};
+        if (p.Dskip) {
+          const uint2 xr = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(p.x) + o);
+          v[0] = fmaf(dsk, bf16_lo(xr.x), v[0]);
+          v[1] = fmaf(dsk, bf16_hi(xr.x), v[1]);
+          v[2] = fmaf(dsk, bf16_lo(xr.y), v[2]);
+          v[3] = fmaf(dsk, bf16_hi(xr.y), v[3]);
         }
+        if (zg) {
+          const uint2 zr = *reinterpret_cast<const uint2*>(zg + o);
+          v[0] *= silu(bf16_lo(zr.x));
+          v[1] *= silu(bf16_hi(zr.x));
+          v[2] *= silu(bf16_lo(zr.y));
+          v[3] *= silu(bf16_hi(zr.y));
+        }
+        uint2 out;
+        out.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        out.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *reinterpret_cast<uint2*>(yg + o) = out;
       }
     }
   }
@@ -470,13 +508,13 @@ hipError_t launch_qn(const SsdParams& p, hipStream_t stream) {
 
 }  // namespace
 
-// Workspace: carried states (bf16), G per chunk (float), transposed B per chunk (bf16),
+// Workspace: carried states (bf16), G per chunk (bf16), transposed B per chunk (bf16),
 // (S, phi) per chunk, head and token (float2), each 256-byte aligned.
 static size_t ssd_align(size_t n) { return (n + 255) & ~(size_t)255; }
 
 size_t ssd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t Q) {
   const int64_t nch = (L + Q - 1) / Q;
-  return ssd_align((size_t)(B * nch * H * P * N) * 2) + ssd_align((size_t)(B * nch * Q * Q) * 4) +
+  return ssd_align((size_t)(B * nch * H * P * N) * 2) + ssd_align((size_t)(B * nch * Q * Q) * 2) +
          ssd_align((size_t)(B * nch * N * Q) * 2) + ssd_align((size_t)(B * nch * H * Q) * 8);
 }
 
@@ -485,8 +523,8 @@ void ssd_workspace_carve(SsdParams& p, void* ws) {
   char* base = static_cast<char*>(ws);
   p.ws_hin = base;
   base += ssd_align((size_t)(p.B * nch * p.H * p.P * p.N) * 2);
-  p.ws_G = reinterpret_cast<float*>(base);
-  base += ssd_align((size_t)(p.B * nch * p.Q * p.Q) * 4);
+  p.ws_G = base;
+  base += ssd_align((size_t)(p.B * nch * p.Q * p.Q) * 2);
   p.ws_Bt = base;
   base += ssd_align((size_t)(p.B * nch * p.N * p.Q) * 2);
   p.ws_sphi = reinterpret_cast<float2*>(base);

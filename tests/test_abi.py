@@ -89,8 +89,8 @@ def test_workspace_queries(lib):
     nseg = (1000 + 99) // 100
     assert lib.ssm_scan_fwd_segmented_workspace_bytes(2, 1000, 64, 16, 100) >= 2 * nseg * 64 * 17 * 4
     nch = 8192 // 256
-    # carried bf16 state per chunk and head, G per chunk (fp32), transposed B per chunk
-    assert lib.ssd_chunk_fwd_workspace_bytes(2, 8192, 80, 64, 128, 256, BF16) >= 2 * nch * (80 * 64 * 128 * 2 + 256 * 256 * 4 + 128 * 256 * 2)
+    # carried bf16 state per chunk and head, G and transposed B per chunk (bf16)
+    assert lib.ssd_chunk_fwd_workspace_bytes(2, 8192, 80, 64, 128, 256, BF16) >= 2 * nch * (80 * 64 * 128 * 2 + 256 * 256 * 2 + 128 * 256 * 2)
 
 
 def step_call(lib, B=4, D=64, N=16, W=4, io=BF16, x=A_, delta=2 * A_, A=3 * A_, Bm=4 * A_, Cm=5 * A_,

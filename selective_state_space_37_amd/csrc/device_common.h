@@ -35,8 +35,35 @@ __device__ __forceinline__ float silu(float zv) {
   return zv * rcp_fast(1.0f + exp2_fast(-zv * kLog2e));
 }
 
-// softplus with the accurate library log1p/exp; the identity above 20 (error < 2.1e-9).
-__device__ __forceinline__ float softplus_f32(float u) { return u > 20.0f ? u : log1pf(expf(u)); }
+// softplus(u) = log(1 + e^u) = max(u, 0) + log1p(e) with e = exp(-|u|) in (0, 1].
+//  * e: the base-2 exponent t = -|u| log2(e) is carried as t_hi + t_lo (t_lo from an fma and the
+//    tail of log2(e)), and exp2(t_hi + t_lo) = exp2(t_hi) (1 + t_lo ln 2), so the rounding of
+//    the argument does not grow with |u|.
+//  * log1p(e) = 2 atanh(s) with s = e / (2 + e) in (0, 1/3], summed as the odd power series
+//    2 s (1 + s^2/3 + s^4/5 + ... + s^12/13); the omitted tail is below 2^-24 relative for
+//    s <= 1/3. About a dozen VALU operations and two hardware transcendentals.
+// Inputs below -150 give 0 (the true value underflows), +inf gives +inf, NaN stays NaN.
+__device__ __forceinline__ float softplus_f32(float u) {
+  constexpr float kLog2eTail = 1.925963033e-8f;  // log2(e) - (float)log2(e)
+  constexpr float kLn2 = 0.6931471806f;
+  const float x = fmaxf(-fabsf(u), -150.0f);
+  const float t_hi = x * kLog2e;
+  const float t_lo = fmaf(x, kLog2e, -t_hi) + x * kLog2eTail;
+  float e = exp2_fast(t_hi);
+  e = fmaf(e, t_lo * kLn2, e);
+  const float s = e * rcp_fast(2.0f + e);
+  const float s2 = s * s;
+  float q = 1.0f / 13.0f;
+  q = fmaf(q, s2, 1.0f / 11.0f);
+  q = fmaf(q, s2, 1.0f / 9.0f);
+  q = fmaf(q, s2, 1.0f / 7.0f);
+  q = fmaf(q, s2, 1.0f / 5.0f);
+  q = fmaf(q, s2, 1.0f / 3.0f);
+  q = fmaf(q, s2, 1.0f);
+  const float l = 2.0f * s * q;
+  const float r = fmaxf(u, 0.0f) + l;
+  return u != u ? u : r;
+}
 
 // Element loads/stores of the per-token tensors in either storage type.
 template <typename T> struct IoTraits;

@@ -7,10 +7,11 @@
 // h = Abar h + expm1(Delta A)/A B u, y = C . h + D u), then the gate.
 //
 // The step is a single streaming pass bound by the state traffic (h read and written, 128 B
-// per channel at N = 16). One lane owns one channel and all N of its states, so every byte is
-// loaded once and in wide pieces: h and A as 16-byte vectors, the width-4 bf16 conv register as
-// one 8-byte load, the conv weights as one 16-byte load. A wave covers 64 consecutive channels,
-// i.e. 4 KiB of contiguous state at N = 16.
+// per channel at N = 16). The state of a channel is split over N / 4 lanes (4 states each, one
+// 16-byte load), so consecutive lanes hold consecutive 16-byte pieces of h and A and a wave's
+// load covers 1 KiB of contiguous state. The lanes of a channel share x, Delta, z and the conv
+// register (same addresses, one fetch), each forms its part of C . h, and the parts are added
+// across the lanes with DPP quad permutes. At N < 4 one lane owns the whole channel.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -46,95 +47,163 @@ struct Vec {
   }
 };
 
-template <typename io_t, int N>
+// Sum over the LPC lanes of a channel (aligned groups of 1, 2 or 4 consecutive lanes).
+template <int LPC>
+__device__ __forceinline__ float sum_channel_lanes(float v) {
+  if constexpr (LPC >= 2) {
+    // quad_perm [1, 0, 3, 2]: swap neighbouring lanes
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  }
+  if constexpr (LPC >= 4) {
+    // quad_perm [2, 3, 0, 1]: swap lane pairs
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  }
+  return v;
+}
+
+// CONV: 0 = no conv register, 4 = width 4 (vector loads), -1 = any width 1..8.
+// All loads of a lane are issued before any arithmetic, so a wave pays one memory round trip.
+template <typename io_t, int N, int CONV>
 __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
   using Io = IoTraits<io_t>;
-  const int64_t ch = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // b * D + d
-  if (ch >= p.B * p.D) return;
-  const int64_t d = ch % p.D;
-  const int64_t b = ch / p.D;
-
-  // ---- conv register: shift, insert x, depthwise causal convolution
-  float u = Io::load(static_cast<const io_t*>(p.x), ch);
-  if (p.conv_state) {
-    io_t* cs = static_cast<io_t*>(p.conv_state) + ch * p.W;
-    float reg[kMaxW];
-    if (p.W == 4) {
-      float old[4], wv[4];
-      Io::load4(cs, 0, old);
-      const float4 w4 = *reinterpret_cast<const float4*>(p.conv_w + d * 4);
-      reg[0] = old[1]; reg[1] = old[2]; reg[2] = old[3]; reg[3] = u;
-      wv[0] = w4.x; wv[1] = w4.y; wv[2] = w4.z; wv[3] = w4.w;
-      float acc = p.conv_b ? p.conv_b[d] : 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) acc = fmaf(wv[k], reg[k], acc);
-      Io::store4(cs, 0, reg);
-      u = acc;
-    } else {
-#pragma unroll
-      for (int k = 0; k < kMaxW; ++k) {
-        if (k + 1 < p.W) reg[k] = Io::load(cs, k + 1);
-        else if (k + 1 == p.W) reg[k] = u;
-      }
-      float acc = p.conv_b ? p.conv_b[d] : 0.f;
-#pragma unroll
-      for (int k = 0; k < kMaxW; ++k)
-        if (k < p.W) acc = fmaf(p.conv_w[d * p.W + k], reg[k], acc);
-#pragma unroll
-      for (int k = 0; k < kMaxW; ++k)
-        if (k < p.W) Io::store(cs, k, reg[k]);
-      u = acc;
-    }
+  using raw4 = typename Io::raw4;
+  constexpr int SPL = N >= 4 ? 4 : N;   // states per lane
+  constexpr int LPC = N / SPL;          // lanes per channel
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (b * D + d) * LPC + q
+  // the grid is whole channels: LPC divides the block size, so a channel's lanes are all
+  // present or all absent and the DPP sums below only combine lanes of one channel
+  if (gid >= p.B * p.D * LPC) return;
+  const int64_t ch = gid / LPC;
+  const int q = (int)(gid % LPC);
+  int64_t b, d;
+  if (p.B * p.D <= 0x7fffffff) {   // uniform: 32-bit division when the channel count allows
+    const uint32_t c32 = (uint32_t)ch, D32 = (uint32_t)p.D;
+    const uint32_t b32 = c32 / D32;
+    b = b32;
+    d = c32 - b32 * D32;
+  } else {
+    b = ch / p.D;
+    d = ch - b * p.D;
   }
+  const int n0 = q * SPL;
 
-  float dt = Io::load(static_cast<const io_t*>(p.delta), ch) + (p.delta_bias ? p.delta_bias[d] : 0.f);
-  if (p.delta_softplus) dt = softplus_f32(dt);
-
-  // ---- one scan step on u for the N states of the channel
-  const io_t* Bg = static_cast<const io_t*>(p.Bm) + b * N;
-  const io_t* Cg = static_cast<const io_t*>(p.Cm) + b * N;
-  float* hp = p.h + ch * N;
-  float h[N], A[N], Bv[N], Cv[N];
-  Vec<N>::load(hp, h);
-  Vec<N>::load(p.A + d * N, A);
-  if constexpr (N % 4 == 0) {
-#pragma unroll
-    for (int k = 0; k < N / 4; ++k) {
-      Io::load4(Bg, 4 * k, &Bv[4 * k]);
-      Io::load4(Cg, 4 * k, &Cv[4 * k]);
-    }
+  // ---- loads
+  const io_t* xg = static_cast<const io_t*>(p.x);
+  const io_t* dg = static_cast<const io_t*>(p.delta);
+  const io_t* zg = static_cast<const io_t*>(p.z);
+  // optional tensors are read through a valid stand-in address when absent and the value is
+  // dropped afterwards: no branch around a load, so no wait is forced before the join
+  const uint32_t x_bits = Io::load_bits(xg, ch);
+  const uint32_t d_bits = Io::load_bits(dg, ch);
+  const uint32_t z_bits = Io::load_bits(zg ? zg : xg, ch);
+  const float* fstand = p.A;   // any float array with at least D entries
+  const float bias_v = (p.delta_bias ? p.delta_bias : fstand)[d];
+  const float dsk_v = (p.Dskip ? p.Dskip : fstand)[d];
+  io_t* cs = static_cast<io_t*>(p.conv_state) + ch * (CONV == 0 ? 0 : p.W);
+  raw4 creg = Io::zero4();
+  float4 cw4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  float cb = 0.f;
+  if constexpr (CONV == 4) {
+    creg = Io::load4_raw(cs, 0);
+    cw4 = *reinterpret_cast<const float4*>(p.conv_w + d * 4);
+  }
+  if constexpr (CONV != 0) cb = (p.conv_b ? p.conv_b : fstand)[d];
+  float h[SPL], A[SPL];
+  Vec<SPL>::load(p.h + ch * N + n0, h);
+  Vec<SPL>::load(p.A + d * N + n0, A);
+  const io_t* Bg = static_cast<const io_t*>(p.Bm) + b * N + n0;
+  const io_t* Cg = static_cast<const io_t*>(p.Cm) + b * N + n0;
+  float Bv[SPL], Cv[SPL];
+  if constexpr (SPL == 4) {
+    const raw4 br = Io::load4_raw(Bg, 0), cr = Io::load4_raw(Cg, 0);
+    Io::unpack4(br, Bv);
+    Io::unpack4(cr, Cv);
   } else {
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
+    for (int n = 0; n < SPL; ++n) {
       Bv[n] = Io::load(Bg, n);
       Cv[n] = Io::load(Cg, n);
     }
   }
+
+  // ---- conv register: shift, insert x, depthwise causal convolution (every lane of the
+  //      channel computes u; lane 0 writes the register back)
+  const float bias = p.delta_bias ? bias_v : 0.f;
+  const float dsk = p.Dskip ? dsk_v : 0.f;
+  if constexpr (CONV != 0) cb = p.conv_b ? cb : 0.f;
+  float u = Io::from_bits(x_bits);
+  if constexpr (CONV == 4) {
+    float old[4];
+    Io::unpack4(creg, old);
+    const float reg[4] = {old[1], old[2], old[3], u};
+    float acc = cb;
+    acc = fmaf(cw4.x, reg[0], acc);
+    acc = fmaf(cw4.y, reg[1], acc);
+    acc = fmaf(cw4.z, reg[2], acc);
+    acc = fmaf(cw4.w, reg[3], acc);
+    if (q == 0) Io::store4(cs, 0, reg);
+    u = acc;
+  } else if constexpr (CONV == -1) {
+    float reg[kMaxW];
+#pragma unroll
+    for (int k = 0; k < kMaxW; ++k) {
+      if (k + 1 < p.W) reg[k] = Io::load(cs, k + 1);
+      else if (k + 1 == p.W) reg[k] = u;
+    }
+    float acc = cb;
+#pragma unroll
+    for (int k = 0; k < kMaxW; ++k)
+      if (k < p.W) acc = fmaf(p.conv_w[d * p.W + k], reg[k], acc);
+    if (q == 0) {
+#pragma unroll
+      for (int k = 0; k < kMaxW; ++k)
+        if (k < p.W) Io::store(cs, k, reg[k]);
+    }
+    u = acc;
+  }
+
+  float dt = Io::from_bits(d_bits) + bias;
+  if (p.delta_softplus) dt = softplus_f32(dt);
+
+  // ---- one scan step on u for this lane's SPL states (n = q SPL ..)
   float yv = 0.f;
 #pragma unroll
-  for (int n = 0; n < N; ++n) {
+  for (int n = 0; n < SPL; ++n) {
     const float ia = 1.0f / A[n];
     const float abar = exp2_fast(dt * A[n] * kLog2e);
     const float coef = fmaf(abar, ia, -ia);
     h[n] = fmaf(abar, h[n], coef * (Bv[n] * u));
     yv = fmaf(Cv[n], h[n], yv);
   }
-  Vec<N>::store(hp, h);
-  if (p.Dskip) yv = fmaf(p.Dskip[d], u, yv);
-  if (p.z) yv *= silu(Io::load(static_cast<const io_t*>(p.z), ch));
+  Vec<SPL>::store(p.h + ch * N + n0, h);
+  yv = sum_channel_lanes<LPC>(yv);
+  if (q != 0) return;
+  yv = fmaf(dsk, u, yv);
+  if (zg) yv *= silu(Io::from_bits(z_bits));
   Io::store(static_cast<io_t*>(p.y), ch, yv);
+}
+
+template <typename io_t, int N>
+void launch_n(const StepParams& p, hipStream_t stream) {
+  constexpr int LPC = N >= 4 ? N / 4 : 1;
+  const int64_t total = p.B * p.D * LPC;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (!p.conv_state)
+    hipLaunchKernelGGL((step_kernel<io_t, N, 0>), grid, dim3(256), 0, stream, p);
+  else if (p.W == 4)
+    hipLaunchKernelGGL((step_kernel<io_t, N, 4>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((step_kernel<io_t, N, -1>), grid, dim3(256), 0, stream, p);
 }
 
 template <typename io_t>
 hipError_t launch_io(const StepParams& p, hipStream_t stream) {
-  const int64_t total = p.B * p.D;
-  const dim3 grid((unsigned)((total + 255) / 256));
   switch (p.N) {
-    case 1: hipLaunchKernelGGL((step_kernel<io_t, 1>), grid, dim3(256), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((step_kernel<io_t, 2>), grid, dim3(256), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((step_kernel<io_t, 4>), grid, dim3(256), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((step_kernel<io_t, 8>), grid, dim3(256), 0, stream, p); break;
-    case 16: hipLaunchKernelGGL((step_kernel<io_t, 16>), grid, dim3(256), 0, stream, p); break;
+    case 1: launch_n<io_t, 1>(p, stream); break;
+    case 2: launch_n<io_t, 2>(p, stream); break;
+    case 4: launch_n<io_t, 4>(p, stream); break;
+    case 8: launch_n<io_t, 8>(p, stream); break;
+    case 16: launch_n<io_t, 16>(p, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -81,40 +81,19 @@ __device__ void chunk_prologue(const SsdParams& p, int64_t b, int64_t c, int64_t
   __syncthreads();
 }
 
-// Stage x[b, chunk, h, :] transposed into LDS as bf16 Xt[p][j] (row stride Q + 8), optionally
-// scaled per token by sScale[j]. Each thread takes two consecutive tokens so that every LDS write
-// is one 32-bit word holding the pair (j, j + 1) of one row p.
+// LDS layout of a transposed x tile (rows = channels p, columns = tokens j, row stride Q + 8
+// bf16): the 4-byte word column of row p is XORed with 8 ((p >> 4) & 3) (kept inside the row).
+// The staging writes (8 channel groups x 8 token pairs per wave) then fall on 64 different banks
+// instead of 16, while a reader that takes 16 consecutive rows of one 16-row group sees a
+// uniform XOR: its bank pattern and 8-byte alignment are those of the plain layout.
 template <int Q>
-__device__ void stage_x_transposed(const SsdParams& p, int64_t b, int64_t c, int64_t h,
-                                   __bf16* Xt, const float* sScale) {
-  const bf16_t* xg = static_cast<const bf16_t*>(p.x);
-  uint32_t* X32 = reinterpret_cast<uint32_t*>(Xt);
-  for (int g = threadIdx.x; g < (Q / 2) * (kP / 8); g += blockDim.x) {
-    const int jp = g / (kP / 8), pg = g % (kP / 8);
-    const int j = 2 * jp;
-    uint32_t w0[4] = {0, 0, 0, 0}, w1[4] = {0, 0, 0, 0};
-    const int64_t t = c * Q + j;
-    if (t < p.L) {
-      const uint4 r = *reinterpret_cast<const uint4*>(xg + ((b * p.L + t) * p.H + h) * kP + pg * 8);
-      w0[0] = r.x; w0[1] = r.y; w0[2] = r.z; w0[3] = r.w;
-    }
-    if (t + 1 < p.L) {
-      const uint4 r = *reinterpret_cast<const uint4*>(xg + ((b * p.L + t + 1) * p.H + h) * kP + pg * 8);
-      w1[0] = r.x; w1[1] = r.y; w1[2] = r.z; w1[3] = r.w;
-    }
-    const float s0 = sScale ? sScale[j] : 1.0f, s1 = sScale ? sScale[j + 1] : 1.0f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float f0 = (q & 1) ? bf16_hi(w0[q >> 1]) : bf16_lo(w0[q >> 1]);
-      const float f1 = (q & 1) ? bf16_hi(w1[q >> 1]) : bf16_lo(w1[q >> 1]);
-      X32[(pg * 8 + q) * ((Q + 8) / 2) + jp] =
-          (uint32_t)f32_to_bf16(f0 * s0) | ((uint32_t)f32_to_bf16(f1 * s1) << 16);
-    }
-  }
+__device__ __forceinline__ int xt_swizzle_words(int row) {
+  return (8 * ((row >> 4) & 3)) & (Q / 2 - 1);
 }
 
-// Stage x[b, chunk, h, :] transposed into LDS without conversion: two consecutive tokens' 16-bit
-// values of one channel are combined into one 32-bit LDS word with a byte permute.
+// Stage x[b, chunk, h, :] transposed into LDS without conversion: each thread takes two
+// consecutive tokens, and the two 16-bit values of one channel go into one 32-bit LDS word with a
+// byte permute.
 template <int Q>
 __device__ void stage_x_transposed_raw(const SsdParams& p, int64_t b, int64_t c, int64_t h, __bf16* Xt) {
   const bf16_t* xg = static_cast<const bf16_t*>(p.x);
@@ -129,8 +108,9 @@ __device__ void stage_x_transposed_raw(const SsdParams& p, int64_t b, int64_t c,
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       // low halves (channel 2k) and high halves (channel 2k+1) of the two tokens
-      X32[(pg * 8 + 2 * k) * ((Q + 8) / 2) + jp] = __builtin_amdgcn_perm(w1[k], w0[k], 0x05040100u);
-      X32[(pg * 8 + 2 * k + 1) * ((Q + 8) / 2) + jp] = __builtin_amdgcn_perm(w1[k], w0[k], 0x07060302u);
+      const int r0 = pg * 8 + 2 * k, r1 = r0 + 1;
+      X32[r0 * ((Q + 8) / 2) + (jp ^ xt_swizzle_words<Q>(r0))] = __builtin_amdgcn_perm(w1[k], w0[k], 0x05040100u);
+      X32[r1 * ((Q + 8) / 2) + (jp ^ xt_swizzle_words<Q>(r1))] = __builtin_amdgcn_perm(w1[k], w0[k], 0x07060302u);
     }
   }
 }
@@ -199,18 +179,28 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
 
 // ---------------------------------------------------------------------------- chunk states
 // grid (H, B), 512 threads: one head, sequential over the chunks. Wave w owns the state block
-// p in [16 pq, 16 pq + 16) x n in [NH w2 .. NH (w2 + 1)) with pq = w / 2, w2 = w % 2 and
-// NH = N / 2, as NTW = N / 32 MFMA D tiles: acc[k][r] = h[p = 16 pq + 4 g + r][n = (w2 NTW + k) 16
-// + lane % 16]. Per chunk the transposed B (shared by every head) and the scaled, transposed x of
-// the head are staged in LDS once for all eight waves; the next chunk's inputs are loaded into
-// registers while the current chunk's products run.
+// p in [16 pq, 16 pq + 16) x n in [NH w2, NH (w2 + 1)) with pq = w / 2, w2 = w % 2, NH = N / 2,
+// as NTW = N / 32 MFMA tiles computed transposed (states x channels), so that
+// acc[k][r] = h[p = 16 pq + lane % 16][n = (w2 NTW + k) 16 + 4 g + r]: four consecutive states
+// per lane, stored as one 8-byte (bf16) or 16-byte (float) piece. Per chunk the transposed B
+// (shared by every head) and the scaled, transposed x of the head are staged in LDS once for all
+// eight waves.
+//
+// Inputs are loaded two chunks ahead into two register buffers used in turn (the loop is
+// unrolled by two; no buffer is copied). Every global load and store of the loop is issued
+// unconditionally -- rows past L are read from the last token, whose weight phi is 0 for padded
+// tokens anyway, and the prefetch index is clamped -- so the compiler's count of outstanding
+// memory operations stays exact and the waits for a buffer do not also wait for the loads of
+// the other.
 template <int Q, int N>
 __global__ __launch_bounds__(512) void ssd_state_kernel(SsdParams p) {
   constexpr int KQ = Q / 32;                 // K steps over a chunk
   constexpr int NTW = N / 32;                // state tiles per wave
   constexpr int XPAIRS = Q / 2 * 4;          // (token pair, 16-channel group) items of x
   constexpr int BT16 = N * Q / 8;            // 16-byte pieces of B^T
-  constexpr int BT_PER = (BT16 + 511) / 512;
+  static_assert(BT16 % 512 == 0, "B^T pieces divide over the threads");
+  static_assert(512 % XPAIRS == 0, "x items repeat evenly over the threads");
+  constexpr int BT_PER = BT16 / 512;
   __shared__ __attribute__((aligned(16))) __bf16 Xs[kP * (Q + 8)];
   __shared__ __attribute__((aligned(16))) __bf16 Bs[N * (Q + 8)];
   const int64_t h = blockIdx.x, b = blockIdx.y;
@@ -220,107 +210,124 @@ __global__ __launch_bounds__(512) void ssd_state_kernel(SsdParams p) {
   const int pq = w >> 1, w2 = w & 1;
   const float a2 = p.A[h] * kLog2e;
   const int64_t PN = (int64_t)kP * N;
-  auto st_idx = [&](int k, int r) { return (int64_t)(16 * pq + 4 * g + r) * N + (w2 * NTW + k) * 16 + r16; };
+  // first of the four consecutive states of tile k
+  auto st_idx = [&](int k) { return (int64_t)(16 * pq + r16) * N + (w2 * NTW + k) * 16 + 4 * g; };
 
   f32x4 acc[NTW];
 #pragma unroll
-  for (int k = 0; k < NTW; ++k)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[k][r] = p.h0 ? p.h0[(b * p.H + h) * PN + st_idx(k, r)] : 0.f;
+  for (int k = 0; k < NTW; ++k) {
+    acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (p.h0) {
+      const float4 v = *reinterpret_cast<const float4*>(p.h0 + (b * p.H + h) * PN + st_idx(k));
+      acc[k] = f32x4{v.x, v.y, v.z, v.w};
+    }
+  }
   const bf16_t* xg = static_cast<const bf16_t*>(p.x);
   bf16_t* hin_all = static_cast<bf16_t*>(p.ws_hin);
   const bf16_t* Bt_all = static_cast<const bf16_t*>(p.ws_Bt);
 
-  // x item of this thread: tokens (2 jp, 2 jp + 1), channels [16 pg, 16 pg + 16)
-  const int jp = tid >> 2, pg = tid & 3;
-  const bool x_item = tid < XPAIRS;
+  // x item of this thread: tokens (2 jp, 2 jp + 1), channels [16 pg, 16 pg + 16). With fewer
+  // items than threads, threads tid and tid + XPAIRS take the same item and write the same
+  // values to the same LDS words.
+  const int item = tid % XPAIRS;
+  const int jp = item >> 2, pg = item & 3;
+  // native vector fields: plain register loads and stores (a struct-typed copy becomes a memcpy,
+  // which keeps the buffer out of registers)
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
   struct ChunkIn {
-    uint4 x[2][2];      // two tokens x 16 channels
-    float2 sphi[2];     // (S_j, phi_j) of the two tokens
+    u32x4 x[2][2];      // two tokens x 16 channels
+    f32x2 sphi[2];      // (S_j, phi_j) of the two tokens
     float s_last;
-    uint4 bt[BT_PER];   // pieces of the chunk's B^T
+    u32x4 bt[BT_PER];   // pieces of the chunk's B^T
   };
-  auto load_chunk = [&](int64_t c, ChunkIn& in) {
+  // (both lambdas are forced inline: the buffers they take by reference must stay in registers)
+  auto load_chunk = [&](int64_t c, ChunkIn& in) __attribute__((always_inline)) {
     const float2* sp = p.ws_sphi + ((b * nch + c) * p.H + h) * Q;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int j = 2 * jp + u;
-      const int64_t t = c * Q + j;
-      const bool ok = x_item && t < p.L;
-      in.x[u][0] = in.x[u][1] = make_uint4(0, 0, 0, 0);
-      if (ok) {
-        const uint4* src = reinterpret_cast<const uint4*>(xg + ((b * p.L + t) * p.H + h) * kP + 16 * pg);
-        in.x[u][0] = src[0];
-        in.x[u][1] = src[1];
-      }
-      in.sphi[u] = x_item ? sp[j] : make_float2(0.f, 0.f);
+      const int64_t t = c * Q + j < p.L ? c * Q + j : p.L - 1;
+      const u32x4* src = reinterpret_cast<const u32x4*>(xg + ((b * p.L + t) * p.H + h) * kP + 16 * pg);
+      in.x[u][0] = src[0];
+      in.x[u][1] = src[1];
+      in.sphi[u] = reinterpret_cast<const f32x2*>(sp)[j];
     }
     in.s_last = sp[Q - 1].x;
-    const uint4* bt = reinterpret_cast<const uint4*>(Bt_all + (b * nch + c) * (int64_t)(N * Q));
+    const u32x4* bt = reinterpret_cast<const u32x4*>(Bt_all + (b * nch + c) * (int64_t)(N * Q));
 #pragma unroll
-    for (int k = 0; k < BT_PER; ++k) {
-      const int e = tid + 512 * k;
-      in.bt[k] = e < BT16 ? bt[e] : make_uint4(0, 0, 0, 0);
-    }
+    for (int k = 0; k < BT_PER; ++k) in.bt[k] = bt[tid + 512 * k];
   };
 
-  ChunkIn cur, nxt;
-  load_chunk(0, cur);
-  for (int64_t c = 0; c < nch; ++c) {
+  auto process = [&](int64_t c, ChunkIn& cur) __attribute__((always_inline)) {
     // stage B^T and the decay-scaled x^T of chunk c
 #pragma unroll
     for (int k = 0; k < BT_PER; ++k) {
       const int e = tid + 512 * k;
-      if (e < BT16) {
-        const int n = e / (Q / 8), j8 = (e % (Q / 8)) * 8;
-        *reinterpret_cast<uint4*>(&Bs[n * (Q + 8) + j8]) = cur.bt[k];
-      }
+      const int n = e / (Q / 8), j8 = (e % (Q / 8)) * 8;
+      *reinterpret_cast<u32x4*>(&Bs[n * (Q + 8) + j8]) = cur.bt[k];
     }
-    if (x_item) {
+    {
       float wj[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) wj[u] = exp2_fast(a2 * (cur.s_last - cur.sphi[u].x)) * cur.sphi[u].y;
       uint32_t* X32 = reinterpret_cast<uint32_t*>(Xs);
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const uint4 v0 = cur.x[0][q >> 3], v1 = cur.x[1][q >> 3];
+        const u32x4 v0 = cur.x[0][q >> 3], v1 = cur.x[1][q >> 3];
         const uint32_t u0 = ((q & 7) >> 1) == 0 ? v0.x : ((q & 7) >> 1) == 1 ? v0.y : ((q & 7) >> 1) == 2 ? v0.z : v0.w;
         const uint32_t u1 = ((q & 7) >> 1) == 0 ? v1.x : ((q & 7) >> 1) == 1 ? v1.y : ((q & 7) >> 1) == 2 ? v1.z : v1.w;
         const float f0 = (q & 1) ? bf16_hi(u0) : bf16_lo(u0);
         const float f1 = (q & 1) ? bf16_hi(u1) : bf16_lo(u1);
-        X32[(16 * pg + q) * ((Q + 8) / 2) + jp] =
+        // word column XORed with 16 pg (inside the row): the four channel groups of a wave
+        // write to four different 16-bank ranges
+        X32[(16 * pg + q) * ((Q + 8) / 2) + (jp ^ ((16 * pg) & (Q / 2 - 1)))] =
             (uint32_t)f32_to_bf16(f0 * wj[0]) | ((uint32_t)f32_to_bf16(f1 * wj[1]) << 16);
       }
     }
     const float decay = exp2_fast(a2 * cur.s_last);
-    if (c + 1 < nch) load_chunk(c + 1, nxt);
+    load_chunk(c + 2 < nch ? c + 2 : nch - 1, cur);
     // the state entering chunk c, for the output kernel; then decay it over the chunk
     bf16_t* hin = hin_all + ((b * nch + c) * p.H + h) * PN;
 #pragma unroll
-    for (int k = 0; k < NTW; ++k)
+    for (int k = 0; k < NTW; ++k) {
+      const uint32_t lo = (uint32_t)f32_to_bf16(acc[k][0]) | ((uint32_t)f32_to_bf16(acc[k][1]) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16(acc[k][2]) | ((uint32_t)f32_to_bf16(acc[k][3]) << 16);
+      *reinterpret_cast<uint2*>(hin + st_idx(k)) = make_uint2(lo, hi);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        hin[st_idx(k, r)].bits = f32_to_bf16(acc[k][r]);
-        acc[k][r] *= decay;
-      }
+      for (int r = 0; r < 4; ++r) acc[k][r] *= decay;
+    }
     __syncthreads();
 #pragma unroll
     for (int kq = 0; kq < KQ; ++kq) {
-      const bf16x8 xa = *reinterpret_cast<const bf16x8*>(&Xs[(16 * pq + r16) * (Q + 8) + kq * 32 + 8 * g]);
+      const bf16x8 xb = *reinterpret_cast<const bf16x8*>(
+          &Xs[(16 * pq + r16) * (Q + 8) + ((kq * 32 + 8 * g) ^ ((32 * pq) & (Q - 1)))]);
 #pragma unroll
       for (int k = 0; k < NTW; ++k) {
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&Bs[((w2 * NTW + k) * 16 + r16) * (Q + 8) + kq * 32 + 8 * g]);
-        acc[k] = mfma16(xa, bv, acc[k]);
+        const bf16x8 ba = *reinterpret_cast<const bf16x8*>(&Bs[((w2 * NTW + k) * 16 + r16) * (Q + 8) + kq * 32 + 8 * g]);
+        acc[k] = mfma16(ba, xb, acc[k]);   // (states x tokens) . (tokens x channels)
       }
     }
     __syncthreads();
-    cur = nxt;
+  };
+
+  ChunkIn buf0, buf1;   // even chunks in buf0, odd chunks in buf1
+  if (nch > 0) {
+    load_chunk(0, buf0);
+    load_chunk(nch > 1 ? 1 : 0, buf1);
   }
+  int64_t c = 0;
+  for (; c + 1 < nch; c += 2) {
+    process(c, buf0);
+    process(c + 1, buf1);
+  }
+  if (c < nch) process(c, buf0);
+
   if (p.h_last) {
 #pragma unroll
     for (int k = 0; k < NTW; ++k)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p.h_last[(b * p.H + h) * PN + st_idx(k, r)] = acc[k][r];
+      *reinterpret_cast<float4*>(p.h_last + (b * p.H + h) * PN + st_idx(k)) =
+          make_float4(acc[k][0], acc[k][1], acc[k][2], acc[k][3]);
   }
 }
 
@@ -453,8 +460,9 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
       const int jb = jp * 32;
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(&Xt[(pt * 16 + r16) * (Q + 8) + jb + 4 * g]);
-        const uint2 hi = *reinterpret_cast<const uint2*>(&Xt[(pt * 16 + r16) * (Q + 8) + jb + 16 + 4 * g]);
+        const int sw = 2 * xt_swizzle_words<Q>(pt * 16);   // in bf16 elements, uniform over the wave
+        const uint2 lo = *reinterpret_cast<const uint2*>(&Xt[(pt * 16 + r16) * (Q + 8) + ((jb + 4 * g) ^ sw)]);
+        const uint2 hi = *reinterpret_cast<const uint2*>(&Xt[(pt * 16 + r16) * (Q + 8) + ((jb + 16 + 4 * g) ^ sw)]);
         const uint4 pk = make_uint4(lo.x, lo.y, hi.x, hi.y);
         acc[pt] = mfma16(__builtin_bit_cast(bf16x8, pk), av, acc[pt]);
       }

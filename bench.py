@@ -18,6 +18,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -90,6 +91,69 @@ def timed(fn, steps, warmup, torch):
     return wall_ms, e0.elapsed_time(e1) / steps
 
 
+def per_launch_ms(fn, steps, torch):
+    """Duration of each launch alone: an event pair around every launch on the current stream.
+    Returns (median, min) in ms."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    d = sorted(a.elapsed_time(b) for a, b in evs)
+    return d[len(d) // 2], d[0]
+
+
+def copy_ceiling_gbs(torch, nbytes=1 << 30, reps=10):
+    """Read+write GB/s of a plain device-to-device copy of nbytes (torch copy_), the practical
+    HBM ceiling beside the published peak."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def smi_during(fn, torch, max_s=20.0):
+    """Socket power and clocks from amd-smi, sampled while fn is launched back to back (in
+    batches of 64 with a synchronisation between them, until amd-smi has answered or max_s has
+    passed). An "error" entry when amd-smi is not available."""
+    proc = None
+    try:
+        proc = subprocess.Popen(["amd-smi", "metric", "--power", "--clock", "--json"],
+                                stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+        i, t0 = 0, time.perf_counter()
+        while proc.poll() is None and time.perf_counter() - t0 < max_s:
+            for _ in range(64):
+                fn(i)
+                i += 1
+            torch.cuda.synchronize()
+        out, _ = proc.communicate(timeout=30)
+        g = json.loads(out)["gpu_data"][0]
+        val = lambda d: d["value"] if isinstance(d, dict) else None
+        gfx = [val(v["clk"]) for k, v in g["clock"].items() if k.startswith("gfx_") and isinstance(v, dict)]
+        gfx = [c for c in gfx if c is not None]
+        return {"socket_power_W": val(g["power"]["socket_power"]),
+                "gfx_clk_MHz_mean": round(sum(gfx) / len(gfx), 1) if gfx else None,
+                "gfx_clk_MHz_min": min(gfx) if gfx else None,
+                "mem_clk_MHz": val(g["clock"].get("mem_0", {}).get("clk")),
+                "launches_during_sample": i,
+                "sampled": "amd-smi metric, once, while the benchmark kernel ran back to back"}
+    except Exception as e:  # reporting only: a missing or changed tool must not stop the bench
+        torch.cuda.synchronize()
+        if proc is not None and proc.poll() is None:
+            proc.kill()
+        return {"error": type(e).__name__}
+
+
 def device_layer_set(torch, seed, B, L, D, N):
     """An extra independent input set drawn on the device with the same distributions as the
     layer workload (timing only; parity runs use the host generator)."""
@@ -109,6 +173,7 @@ def main():
     ap.add_argument("--sets", type=int, default=3, help="rotating independent input sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-smi", action="store_true", help="skip the amd-smi clock/power sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 512 MiB device copy three times (counter calibration)")
     args = ap.parse_args()
@@ -147,6 +212,7 @@ def main():
         ssm.scan_fwd(s["x"], s["delta"], A, s["Bm"], s["Cm"], Dskip=Dskip, z=s["z"], y=s["y"], h_last=s["h"])
 
     wall_ms, kern_ms = timed(step, args.steps, args.warmup, torch)
+    med_ms, min_ms = per_launch_ms(step, args.steps, torch)
     nbytes = scan_bytes(B, L, D, N, 2)
     elems = B * L * D
     value = nbytes / (wall_ms * 1e-3) / 1e9
@@ -172,8 +238,11 @@ def main():
                    "B": B, "L": L, "D": D, "N": N, "io_dtype": "bf16", "state_dtype": "f32",
                    "gate": True, "D_term": True, "final_state": True, "input_sets": len(sets)},
         "gelem_per_s": round(elems / (wall_ms * 1e-3) / 1e9, 2),
+        "state_updates_per_s_G": round(elems * N / (wall_ms * 1e-3) / 1e9, 1),
         "hbm_frac_of_peak": round(value / PEAK_HBM_GBS, 4),
         "kernel_ms": round(kern_ms, 5),
+        "kernel_ms_single_launch": {"median": round(med_ms, 5), "min": round(min_ms, 5),
+                                    "how": "event pair around each of %d further launches" % args.steps},
         # The scan kernel is bound by VALU issue (VALUBusy ~83%), not by HBM: the binding roofline
         # is the VALU lane-slot rate; the HBM figure for the same launches follows it.
         "roofline": {"bound": "alu", "achieved": round(valu_tslots, 3), "peak": round(PEAK_VALU_TOPS, 3),
@@ -185,6 +254,10 @@ def main():
                          "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                          "bytes_per_launch": nbytes},
     }
+
+    out["copy_ceiling_GB_s"] = round(copy_ceiling_gbs(torch), 1)
+    if not args.no_smi:
+        out["gpu_clocks_power"] = smi_during(step, torch)
 
     if not args.no_secondary:
         out["secondary"] = secondary(torch, np, inputs, ssm, dev)
@@ -256,7 +329,18 @@ def secondary(torch, np, inputs, ssm, dev):
         "us_per_step": round(per_step * 1e3, 3), "GB_s": round(nbytes / per_step / 1e6, 1),
         "hbm_frac": round(nbytes / per_step / 1e6 / PEAK_HBM_GBS, 4),
         "tokens_per_s_per_layer": round(B / (per_step * 1e-3), 1)}
-    del hs, cs, xs, ds, zs, Bs, Cs, ys, graph
+    # the same steps on one layer's state only (about 42 MB: it stays in the 256 MB last-level
+    # cache, so this is a cache figure, not an HBM one)
+    graph1 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph1):
+        for i in range(layers):
+            dec(0)
+    _, ms1 = timed(lambda i: graph1.replay(), 20, 3, torch)
+    per1 = ms1 / layers
+    res["decode_128x4096_n16_bf16_single_layer_cache_resident"] = {
+        "us_per_step": round(per1 * 1e3, 3), "GB_s": round(nbytes / per1 / 1e6, 1),
+        "note": "one layer's state reused every step: served from the last-level cache, not HBM"}
+    del hs, cs, xs, ds, zs, Bs, Cs, ys, graph, graph1
 
     # Mamba-2 SSD: batch 2, L 8192, 80 heads x 64, N 128, chunk 256, bf16
     B, L, H, P, N, Q = 2, 8192, 80, 64, 128, 256
@@ -289,10 +373,28 @@ def cpu_baseline(host, np, inputs):
     oracle.scan(x, d, host.A, Bm, Cm, Dskip=host.Dskip, z=z)
     dt = time.perf_counter() - t0
     nbytes = scan_bytes(B, L, D, N, 2)
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+    threads = oracle.num_threads()
+    # one core on a slice of the same workload (one sequence, 256 channels)
+    oracle.set_num_threads(1)
+    sl = (slice(0, 1), slice(None), slice(0, 256))
+    t1 = time.perf_counter()
+    oracle.scan(x[sl], d[sl], host.A[:256], Bm[:1], Cm[:1], Dskip=host.Dskip[:256], z=z[sl])
+    dt1 = time.perf_counter() - t1
+    oracle.set_num_threads(threads)
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 3), "gelem_per_s": round(B * L * D / dt / 1e9, 5),
             "sample": "the whole layer workload (8 x 2048 x 5120, N 16): fp64 recurrence, OpenMP over (b, d)",
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model,
+            "one_core_gelem_per_s": round(L * 256 / dt1 / 1e9, 6),
+            "one_core_sample": "1 x 2048 x 256 channels of the same inputs, one thread"}
 
 
 if __name__ == "__main__":

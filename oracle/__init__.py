@@ -58,6 +58,8 @@ def _configure(lib):
     lib.oracle_ssd.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ci
+    lib.oracle_set_num_threads.argtypes = [ci]
+    lib.oracle_set_num_threads.restype = None
     return lib
 
 
@@ -103,6 +105,11 @@ def source_text() -> str:
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of the following oracle calls (results do not depend on it)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def _f64(a, shape=None):

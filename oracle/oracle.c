@@ -188,6 +188,16 @@ void oracle_ssd(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t N,
   }
 }
 
+/* Thread count for the following OpenMP regions (n >= 1); used to time a single core. The
+   results do not depend on it. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* Number of threads an OpenMP region would use (reported beside CPU timings). */
 int oracle_num_threads(void) {
   int n = 1;

@@ -41,6 +41,54 @@ def test_step_matches_oracle(dtype, N, conv):
         assert np.array_equal(gu.host(creg), rc)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [4, 16])
+@pytest.mark.parametrize("W", [1, 2, 3, 5, 8])
+def test_step_conv_widths(W, N, dtype):
+    """Conv registers of every supported width (the width-4 path has its own vector loads; the
+    others take the general one). D = 100 leaves a ragged last workgroup."""
+    Bsz, D, seed = 2, 100, 70 + W
+    prm = inputs.decode_params(seed=seed, D=D, N=N, W=W)
+    h0 = inputs.draw_param(seed, 50, (Bsz, D, N), scale=0.5)
+    cb = inputs.draw_param(seed, 52, (D,), scale=0.1)
+    reg = inputs.conv_register(seed, Bsz, D, W, dtype)
+    st = inputs.decode_step(seed, 0, Bsz, D, N, dtype)
+    h, creg = gu.dev(h0), gu.dev(reg)
+    y = gu.step_on_gpu(st, gu.dev(prm["A"]), h, Dskip=gu.dev(prm["Dskip"]), conv_state=creg,
+                       conv_w=gu.dev(prm["conv_w"]), conv_b=gu.dev(cb), delta_softplus=True)
+    torch.cuda.synchronize()
+    w = lambda a: inputs.widen(a, dtype)
+    ry, rh, rc = oracle.step(w(st.x), w(st.delta), prm["A"], w(st.Bm), w(st.Cm), h0,
+                             delta_softplus=True, Dskip=prm["Dskip"], z=w(st.z), conv_state=w(reg),
+                             conv_w=prm["conv_w"], conv_b=cb)
+    tol = gu.TOL[dtype]
+    assert gu.rel_err(gu.host(y), ry) <= tol
+    assert gu.rel_err(gu.host(h), rh) <= tol
+    assert np.array_equal(gu.host(creg), rc)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [2, 16])
+def test_step_optional_inputs_absent(N, dtype):
+    """No gate, no D term, no step-size bias, no conv bias, no softplus: the kernel reads stand-in
+    addresses for absent tensors and must drop those values."""
+    Bsz, D, W, seed = 3, 72, 4, 80 + N
+    prm = inputs.decode_params(seed=seed, D=D, N=N, W=W)
+    h0 = inputs.draw_param(seed, 50, (Bsz, D, N), scale=0.5)
+    reg = inputs.conv_register(seed, Bsz, D, W, dtype)
+    st = inputs.decode_step(seed, 0, Bsz, D, N, dtype)
+    h, creg = gu.dev(h0), gu.dev(reg)
+    y = ssm.state_update(gu.dev(st.x), gu.dev(st.delta), gu.dev(prm["A"]), gu.dev(st.Bm), gu.dev(st.Cm), h,
+                         conv_state=creg, conv_w=gu.dev(prm["conv_w"]))
+    torch.cuda.synchronize()
+    w = lambda a: inputs.widen(a, dtype)
+    ry, rh, _ = oracle.step(w(st.x), w(st.delta), prm["A"], w(st.Bm), w(st.Cm), h0,
+                            conv_state=w(reg), conv_w=prm["conv_w"])
+    tol = gu.TOL[dtype]
+    assert gu.rel_err(gu.host(y), ry) <= tol
+    assert gu.rel_err(gu.host(h), rh) <= tol
+
+
 def test_repeated_steps_equal_scan():
     """L decode steps without the conv register equal one scan over the L tokens."""
     inp = inputs.scan_small(seed=60, Bsz=2, L=37, D=64, h0=True)

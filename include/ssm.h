@@ -87,7 +87,7 @@ const char* ssm_last_error_detail(void);
  *   * Bm[b,t,n] * x[b,t,d]; y = sum_n Cm[b,t,n] h[n] + Dskip[d] x[b,t,d]; gate.
  *
  *   Requirements: B, L >= 0 (B == 0 or L == 0 is a no-op, except that with L == 0 h_last
- *   receives h0 or zeros); D >= 1 and D % 4 == 0; N in {1, 2, 4, 8, 16} (else
+ *   receives h0 or zeros); D >= 1 and D % 4 == 0; N in {1, 2, 4, 8, 16} and D <= 2^24 (else
  *   SSM_ERR_UNSUPPORTED); y must not overlap any input. workspace may be NULL when
  *   ssm_scan_fwd_workspace_bytes() returns 0.
  *

@@ -52,6 +52,9 @@ bool supported_scan_n(int64_t N) { return N == 1 || N == 2 || N == 4 || N == 8 |
 
 // The library targets MI355X (256 compute units); the plan depends only on the shapes, so the
 // workspace query needs no device.
+// The scan kernels address a 16-token tile with 32-bit per-lane byte offsets (16 rows of D
+// elements of at most 4 bytes): D up to 2^24 keeps them far below 2^32.
+constexpr int64_t kMaxScanD = int64_t(1) << 24;
 constexpr int64_t kPlanCUs = 256;
 constexpr int64_t kTile = 16;         // tokens per LDS tile of the scan kernels
 constexpr int64_t kMinSegment = 256;  // shortest automatic segment
@@ -80,6 +83,7 @@ ssm_status scan_common(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io,
   if (D < 1 || (D % 4) != 0) return fail(SSM_ERR_INVALID_ARGUMENT, "D=%lld must be >= 1 and a multiple of 4", (long long)D);
   if (!valid_dtype(io)) return fail(SSM_ERR_INVALID_ARGUMENT, "unknown io_dtype %d", (int)io);
   if (!supported_scan_n(N)) return fail(SSM_ERR_UNSUPPORTED, "N=%lld: supported state sizes are 1, 2, 4, 8, 16", (long long)N);
+  if (D > kMaxScanD) return fail(SSM_ERR_UNSUPPORTED, "D=%lld: at most %lld channels", (long long)D, (long long)kMaxScanD);
   if (seg_len < 1) return fail(SSM_ERR_INVALID_ARGUMENT, "segment_len=%lld must be >= 1", (long long)seg_len);
   if (B == 0) return ok();
   if (!A) return fail(SSM_ERR_INVALID_ARGUMENT, "A is NULL");

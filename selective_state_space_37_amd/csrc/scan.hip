@@ -26,6 +26,8 @@
 // segment's local end state and sum of Delta; a carry pass runs the segment recurrence
 // h_in[s+1] = exp(A sum Delta_s) h_in[s] + h_loc[s]; the full pass then starts every segment
 // from its carry. The pages' "only state passes between chunks".
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -113,9 +115,11 @@ void scan_kernel(ScanParams p) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) bias4[k] = p.delta_bias[cgl + k];
 
+  // Load registers are zeroed once; afterwards a lane whose load is predicated off keeps its last
+  // value, and the commit of the ragged last tile zeroes what it must (so no per-tile selects).
   raw4 rx[Cfg::kGroupsPerThr], rd[Cfg::kGroupsPerThr], rz[Cfg::kGroupsPerThr];
-  // B and C of a whole tile are T * N consecutive elements: full tiles move them as 16-byte
-  // chunks (threads below kBCChunks), the ragged last tile element by element.
+#pragma unroll
+  for (int k = 0; k < Cfg::kGroupsPerThr; ++k) rx[k] = rd[k] = rz[k] = Io::zero4();
   // B and C of a tile are T * N consecutive elements. When a row of N elements is whole 16-byte
   // chunks they move as chunks (threads below kChunks, a chunk never straddles a row, so the
   // ragged last tile only drops whole chunks); otherwise element by element. Either way the
@@ -123,62 +127,94 @@ void scan_kernel(ScanParams p) {
   // stay in flight while tile i runs.
   using BCC = BCChunks<io_t, T, N, Cfg::kThreads>;
   constexpr bool kChunkBC = N * (int)sizeof(io_t) >= 16;
-  uint4 rbv, rcv;
+  uint4 rbv = make_uint4(0, 0, 0, 0), rcv = make_uint4(0, 0, 0, 0);
   uint32_t rB[Cfg::kBCPerThr], rC[Cfg::kBCPerThr];
-  // element offset of this thread's first loader row in the segment; tiles advance it by T D
+#pragma unroll
+  for (int k = 0; k < Cfg::kBCPerThr; ++k) rB[k] = rC[k] = 0u;
+  // tiles [0, n_full) have all T rows inside the segment (uniform 32-bit test)
+  const int n_full = (int)((t_end - t_begin) / T);
+  // Addressing: a tile's block of x / delta / z (T rows of D, from channel c0) starts at a
+  // uniform address (scalar registers); each lane adds a 32-bit byte offset that is the same for
+  // every tile (T D < 2^31 is checked on the host). The loads then need no per-tile vector
+  // address arithmetic.
   const int64_t seg_row0 = b * L + t_begin;
-  const int64_t ld_base = (seg_row0 + tid / (CH / 4)) * D + cgl;
+  uint32_t ld_boff[Cfg::kGroupsPerThr];
+  bool ld_ok[Cfg::kGroupsPerThr];
+#pragma unroll
+  for (int k = 0; k < Cfg::kGroupsPerThr; ++k) {
+    const int g = tid + k * Cfg::kThreads;
+    ld_boff[k] = (uint32_t)(((g / (CH / 4)) * D + 4 * cg) * (int64_t)sizeof(io_t));
+    ld_ok[k] = (g < Cfg::kGroups) && cg_ok;
+  }
+  auto tile_ptr = [&](const io_t* base, int tile) {   // uniform
+    return reinterpret_cast<const char*>(base + (seg_row0 + (int64_t)tile * T) * D + c0);
+  };
+  auto bc_ptr = [&](const io_t* base, int tile) {     // uniform
+    return reinterpret_cast<const char*>(base + (seg_row0 + (int64_t)tile * T) * N);
+  };
+  using raw_t = raw4;
 
   auto issue_loads = [&](int tile) {
     const int64_t t0 = t_begin + (int64_t)tile * T;
-    const int64_t tile_off = (int64_t)tile * T * D;
-    const bool full_tile = t0 + T <= t_end;   // uniform: only the ragged last tile predicates rows
+    const bool full_tile = tile < n_full;   // uniform: only the ragged last tile predicates rows
+    const char* xb = tile_ptr(xg, tile);
+    const char* db = tile_ptr(dg, tile);
+    const char* zb = has_z ? tile_ptr(zg, tile) : nullptr;
 #pragma unroll
     for (int k = 0; k < Cfg::kGroupsPerThr; ++k) {
-      const int g = tid + k * Cfg::kThreads;
-      const int r = g / (CH / 4);
-      const bool ok = (g < Cfg::kGroups) && cg_ok && (full_tile || t0 + r < t_end);
-      const int64_t off = ld_base + tile_off + (int64_t)(k * Cfg::kThreads / (CH / 4)) * D;
-      rx[k] = ok ? Io::load4_raw(xg, off) : Io::zero4();
-      rd[k] = ok ? Io::load4_raw(dg, off) : Io::zero4();
-      if (has_z) rz[k] = ok ? Io::load4_raw(zg, off) : Io::zero4();
+      const int r = (tid + k * Cfg::kThreads) / (CH / 4);
+      const bool ok = ld_ok[k] && (full_tile || t0 + r < t_end);
+      if (ok) {
+        rx[k] = *reinterpret_cast<const raw_t*>(xb + ld_boff[k]);
+        rd[k] = *reinterpret_cast<const raw_t*>(db + ld_boff[k]);
+        if (has_z) rz[k] = *reinterpret_cast<const raw_t*>(zb + ld_boff[k]);
+      }
     }
-    const int64_t bc_off = (seg_row0 + (int64_t)tile * T) * N;
+    const char* bb = bc_ptr(Bg, tile);
+    const char* cb = bc_ptr(Cg, tile);
     if constexpr (kChunkBC) {
       const int r = tid * BCC::kPerChunk / N;   // the chunk's row in the tile
       const bool ok = tid < BCC::kChunks && (full_tile || t0 + r < t_end);
-      const int64_t off = bc_off + tid * BCC::kPerChunk;
-      rbv = ok ? *reinterpret_cast<const uint4*>(Bg + off) : make_uint4(0, 0, 0, 0);
-      if (FULL) rcv = ok ? *reinterpret_cast<const uint4*>(Cg + off) : make_uint4(0, 0, 0, 0);
+      const uint32_t boff = (uint32_t)tid * 16u;
+      if (ok) {
+        rbv = *reinterpret_cast<const uint4*>(bb + boff);
+        if (FULL) rcv = *reinterpret_cast<const uint4*>(cb + boff);
+      }
     } else {
 #pragma unroll
       for (int k = 0; k < Cfg::kBCPerThr; ++k) {
         const int e = tid + k * Cfg::kThreads;
         const int r = e / N;
         const bool ok = (e < Cfg::kBC) && (full_tile || t0 + r < t_end);
-        rB[k] = ok ? Io::load_bits(Bg, bc_off + e) : 0u;
-        if (FULL) rC[k] = ok ? Io::load_bits(Cg, bc_off + e) : 0u;
+        if (ok) {
+          rB[k] = Io::load_bits(reinterpret_cast<const io_t*>(bb), e);
+          if (FULL) rC[k] = Io::load_bits(reinterpret_cast<const io_t*>(cb), e);
+        }
       }
     }
   };
 
-  auto commit_tile = [&](int tile, int buf) {
+  // Rows past the segment end (ragged last tile) are committed as Delta = 0, x = 0, B = C = 0:
+  // the identity step, whatever the registers held. RAGGED is a compile-time switch so that
+  // full tiles carry no row tests at all.
+  auto commit_impl = [&](auto ragged_tag, int tile, int buf) {
+    constexpr bool RAGGED = decltype(ragged_tag)::value;
     const int64_t t0 = t_begin + (int64_t)tile * T;
-    const bool full_tile = t0 + T <= t_end;
 #pragma unroll
     for (int k = 0; k < Cfg::kGroupsPerThr; ++k) {
       const int g = tid + k * Cfg::kThreads;
       if (g < Cfg::kGroups) {
         const int r = g / (CH / 4);
-        const bool valid = full_tile || (t0 + r < t_end);
+        const bool valid = !RAGGED || (t0 + r < t_end);
         float xv[4], dv[4];
         Io::unpack4(rx[k], xv);
         Io::unpack4(rd[k], dv);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          float u = dv[q] + bias4[q];
+          float u = p.delta_bias ? dv[q] + bias4[q] : dv[q];
           if (p.delta_softplus) u = softplus_f32(u);
-          dv[q] = valid ? u : 0.f;  // padded token: Delta = 0 -> identity step
+          dv[q] = valid ? u : 0.f;
+          xv[q] = valid ? xv[q] : 0.f;
         }
         float4* dst = reinterpret_cast<float4*>(&s_dx[buf][r][4 * cg]);
         dst[0] = make_float4(dv[0], xv[0], dv[1], xv[1]);
@@ -190,8 +226,9 @@ void scan_kernel(ScanParams p) {
       if (tid < BCC::kChunks) {
         // kPerChunk consecutive (B, C) elements -> interleaved (B_n, C_n) pairs
         float bv[BCC::kPerChunk], cv[BCC::kPerChunk];
-        Io::unpack_chunk(rbv, bv);
-        if (FULL) Io::unpack_chunk(rcv, cv);
+        const bool valid = !RAGGED || t0 + tid * BCC::kPerChunk / N < t_end;
+        Io::unpack_chunk(valid ? rbv : make_uint4(0, 0, 0, 0), bv);
+        if (FULL) Io::unpack_chunk(valid ? rcv : make_uint4(0, 0, 0, 0), cv);
         float4* bc = reinterpret_cast<float4*>(&s_bc[buf][0][0][0] + 2 * tid * BCC::kPerChunk);
 #pragma unroll
         for (int q = 0; q < BCC::kPerChunk / 2; ++q)
@@ -202,12 +239,17 @@ void scan_kernel(ScanParams p) {
       for (int k = 0; k < Cfg::kBCPerThr; ++k) {
         const int e = tid + k * Cfg::kThreads;
         if (e < Cfg::kBC) {
+          const bool valid = !RAGGED || t0 + e / N < t_end;
           float* bc = &s_bc[buf][0][0][0] + 2 * e;
-          bc[0] = Io::from_bits(rB[k]);
-          if (FULL) bc[1] = Io::from_bits(rC[k]);
+          bc[0] = valid ? Io::from_bits(rB[k]) : 0.f;
+          if (FULL) bc[1] = valid ? Io::from_bits(rC[k]) : 0.f;
         }
       }
     }
+  };
+  auto commit_tile = [&](int tile, int buf) {
+    if (tile < n_full) commit_impl(std::false_type{}, tile, buf);
+    else commit_impl(std::true_type{}, tile, buf);
   };
 
   // ---- per-lane recurrence constants: channel c, states n0 .. n0+NS-1
@@ -240,7 +282,10 @@ void scan_kernel(ScanParams p) {
   //      slice, slice + KS, ... of each tile (the same channel as its recurrence lane)
   const float dsk = (FULL && p.Dskip && c_ok) ? p.Dskip[c] : 0.f;
   io_t* __restrict__ yg = static_cast<io_t*>(p.y);
-  const int64_t y_base = (seg_row0 + slice) * D + c;   // token t_begin + slice; tiles add T D
+  uint32_t y_boff[FULL ? T / KS : 1];   // byte offset of this thread's outputs inside a tile block
+#pragma unroll
+  for (int k = 0; k < (FULL ? T / KS : 1); ++k)
+    y_boff[k] = (uint32_t)(((slice + k * KS) * D + chl) * (int64_t)sizeof(io_t));
 
   if (ntiles > 0) {
     issue_loads(0);
@@ -309,9 +354,12 @@ void scan_kernel(ScanParams p) {
     if (tile + 1 < ntiles) commit_tile(tile + 1, buf ^ 1);
     if (FULL) {
       const int64_t t0 = t_begin + (int64_t)tile * T;
+      const bool full_tile = tile < n_full;
+      io_t* yb = yg + (seg_row0 + (int64_t)tile * T) * D + c0;   // uniform
 #pragma unroll
       for (int k = 0; k < T / KS; ++k)
-        if (c_ok && t0 + slice + k * KS < t_end) Io::store(yg, y_base + ((int64_t)tile * T + k * KS) * D, yout[k]);
+        if (c_ok && (full_tile || t0 + slice + k * KS < t_end))
+          Io::store(reinterpret_cast<io_t*>(reinterpret_cast<char*>(yb) + y_boff[k]), 0, yout[k]);
     }
     __syncthreads();
   }

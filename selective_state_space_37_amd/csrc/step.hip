@@ -62,138 +62,172 @@ __device__ __forceinline__ float sum_channel_lanes(float v) {
 }
 
 // CONV: 0 = no conv register, 4 = width 4 (vector loads), -1 = any width 1..8.
+// R: batch rows per thread. The thread handles channel d, state slice q of rows bq R .. bq R +
+// R - 1; the per-channel operands (A, conv weights, bias, D) are loaded once for the R rows.
 // All loads of a lane are issued before any arithmetic, so a wave pays one memory round trip.
-template <typename io_t, int N, int CONV>
+template <typename io_t, int N, int CONV, int R>
 __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
   using Io = IoTraits<io_t>;
   using raw4 = typename Io::raw4;
   constexpr int SPL = N >= 4 ? 4 : N;   // states per lane
   constexpr int LPC = N / SPL;          // lanes per channel
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (b * D + d) * LPC + q
+  const int64_t nbq = (p.B + R - 1) / R;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (bq * D + d) * LPC + q
   // the grid is whole channels: LPC divides the block size, so a channel's lanes are all
   // present or all absent and the DPP sums below only combine lanes of one channel
-  if (gid >= p.B * p.D * LPC) return;
-  const int64_t ch = gid / LPC;
+  if (gid >= nbq * p.D * LPC) return;
+  const int64_t cq = gid / LPC;   // bq * D + d
   const int q = (int)(gid % LPC);
-  int64_t b, d;
-  if (p.B * p.D <= 0x7fffffff) {   // uniform: 32-bit division when the channel count allows
-    const uint32_t c32 = (uint32_t)ch, D32 = (uint32_t)p.D;
+  int64_t bq, d;
+  if (nbq * p.D <= 0x7fffffff) {   // uniform: 32-bit division when the channel count allows
+    const uint32_t c32 = (uint32_t)cq, D32 = (uint32_t)p.D;
     const uint32_t b32 = c32 / D32;
-    b = b32;
+    bq = b32;
     d = c32 - b32 * D32;
   } else {
-    b = ch / p.D;
-    d = ch - b * p.D;
+    bq = cq / p.D;
+    d = cq - bq * p.D;
   }
   const int n0 = q * SPL;
+  // rows past B repeat the last row's loads and skip every store
+  int64_t ch[R], brow[R];
+  bool live[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t b = bq * R + r;
+    live[r] = b < p.B;
+    brow[r] = live[r] ? b : p.B - 1;
+    ch[r] = brow[r] * p.D + d;
+  }
 
-  // ---- loads
+  // ---- loads: per-channel operands once, per-row operands for each of the R rows
   const io_t* xg = static_cast<const io_t*>(p.x);
   const io_t* dg = static_cast<const io_t*>(p.delta);
   const io_t* zg = static_cast<const io_t*>(p.z);
   // optional tensors are read through a valid stand-in address when absent and the value is
   // dropped afterwards: no branch around a load, so no wait is forced before the join
-  const uint32_t x_bits = Io::load_bits(xg, ch);
-  const uint32_t d_bits = Io::load_bits(dg, ch);
-  const uint32_t z_bits = Io::load_bits(zg ? zg : xg, ch);
   const float* fstand = p.A;   // any float array with at least D entries
   const float bias_v = (p.delta_bias ? p.delta_bias : fstand)[d];
   const float dsk_v = (p.Dskip ? p.Dskip : fstand)[d];
-  io_t* cs = static_cast<io_t*>(p.conv_state) + ch * (CONV == 0 ? 0 : p.W);
-  raw4 creg = Io::zero4();
+  float A[SPL];
+  Vec<SPL>::load(p.A + d * N + n0, A);
   float4 cw4 = make_float4(0.f, 0.f, 0.f, 0.f);
   float cb = 0.f;
-  if constexpr (CONV == 4) {
-    creg = Io::load4_raw(cs, 0);
-    cw4 = *reinterpret_cast<const float4*>(p.conv_w + d * 4);
-  }
+  if constexpr (CONV == 4) cw4 = *reinterpret_cast<const float4*>(p.conv_w + d * 4);
   if constexpr (CONV != 0) cb = (p.conv_b ? p.conv_b : fstand)[d];
-  float h[SPL], A[SPL];
-  Vec<SPL>::load(p.h + ch * N + n0, h);
-  Vec<SPL>::load(p.A + d * N + n0, A);
-  const io_t* Bg = static_cast<const io_t*>(p.Bm) + b * N + n0;
-  const io_t* Cg = static_cast<const io_t*>(p.Cm) + b * N + n0;
-  float Bv[SPL], Cv[SPL];
-  if constexpr (SPL == 4) {
-    const raw4 br = Io::load4_raw(Bg, 0), cr = Io::load4_raw(Cg, 0);
-    Io::unpack4(br, Bv);
-    Io::unpack4(cr, Cv);
-  } else {
+  uint32_t x_bits[R], d_bits[R], z_bits[R];
+  raw4 creg[R];
+  float h[R][SPL], Bv[R][SPL], Cv[R][SPL];
 #pragma unroll
-    for (int n = 0; n < SPL; ++n) {
-      Bv[n] = Io::load(Bg, n);
-      Cv[n] = Io::load(Cg, n);
+  for (int r = 0; r < R; ++r) {
+    x_bits[r] = Io::load_bits(xg, ch[r]);
+    d_bits[r] = Io::load_bits(dg, ch[r]);
+    z_bits[r] = Io::load_bits(zg ? zg : xg, ch[r]);
+    creg[r] = Io::zero4();
+    if constexpr (CONV == 4) creg[r] = Io::load4_raw(static_cast<const io_t*>(p.conv_state) + ch[r] * 4, 0);
+    Vec<SPL>::load(p.h + ch[r] * N + n0, h[r]);
+    const io_t* Bg = static_cast<const io_t*>(p.Bm) + brow[r] * N + n0;
+    const io_t* Cg = static_cast<const io_t*>(p.Cm) + brow[r] * N + n0;
+    if constexpr (SPL == 4) {
+      const raw4 br = Io::load4_raw(Bg, 0), cr = Io::load4_raw(Cg, 0);
+      Io::unpack4(br, Bv[r]);
+      Io::unpack4(cr, Cv[r]);
+    } else {
+#pragma unroll
+      for (int n = 0; n < SPL; ++n) {
+        Bv[r][n] = Io::load(Bg, n);
+        Cv[r][n] = Io::load(Cg, n);
+      }
     }
   }
 
-  // ---- conv register: shift, insert x, depthwise causal convolution (every lane of the
-  //      channel computes u; lane 0 writes the register back)
   const float bias = p.delta_bias ? bias_v : 0.f;
   const float dsk = p.Dskip ? dsk_v : 0.f;
   if constexpr (CONV != 0) cb = p.conv_b ? cb : 0.f;
-  float u = Io::from_bits(x_bits);
-  if constexpr (CONV == 4) {
-    float old[4];
-    Io::unpack4(creg, old);
-    const float reg[4] = {old[1], old[2], old[3], u};
-    float acc = cb;
-    acc = fmaf(cw4.x, reg[0], acc);
-    acc = fmaf(cw4.y, reg[1], acc);
-    acc = fmaf(cw4.z, reg[2], acc);
-    acc = fmaf(cw4.w, reg[3], acc);
-    if (q == 0) Io::store4(cs, 0, reg);
-    u = acc;
-  } else if constexpr (CONV == -1) {
-    float reg[kMaxW];
-#pragma unroll
-    for (int k = 0; k < kMaxW; ++k) {
-      if (k + 1 < p.W) reg[k] = Io::load(cs, k + 1);
-      else if (k + 1 == p.W) reg[k] = u;
-    }
-    float acc = cb;
-#pragma unroll
-    for (int k = 0; k < kMaxW; ++k)
-      if (k < p.W) acc = fmaf(p.conv_w[d * p.W + k], reg[k], acc);
-    if (q == 0) {
-#pragma unroll
-      for (int k = 0; k < kMaxW; ++k)
-        if (k < p.W) Io::store(cs, k, reg[k]);
-    }
-    u = acc;
-  }
-
-  float dt = Io::from_bits(d_bits) + bias;
-  if (p.delta_softplus) dt = softplus_f32(dt);
-
-  // ---- one scan step on u for this lane's SPL states (n = q SPL ..)
-  float yv = 0.f;
+  float ia[SPL], a2[SPL];
 #pragma unroll
   for (int n = 0; n < SPL; ++n) {
-    const float ia = 1.0f / A[n];
-    const float abar = exp2_fast(dt * A[n] * kLog2e);
-    const float coef = fmaf(abar, ia, -ia);
-    h[n] = fmaf(abar, h[n], coef * (Bv[n] * u));
-    yv = fmaf(Cv[n], h[n], yv);
+    ia[n] = 1.0f / A[n];
+    a2[n] = A[n] * kLog2e;
   }
-  Vec<SPL>::store(p.h + ch * N + n0, h);
-  yv = sum_channel_lanes<LPC>(yv);
-  if (q != 0) return;
-  yv = fmaf(dsk, u, yv);
-  if (zg) yv *= silu(Io::from_bits(z_bits));
-  Io::store(static_cast<io_t*>(p.y), ch, yv);
+
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    // ---- conv register: shift, insert x, depthwise causal convolution (every lane of the
+    //      channel computes u; lane 0 writes the register back)
+    float u = Io::from_bits(x_bits[r]);
+    if constexpr (CONV == 4) {
+      float old[4];
+      Io::unpack4(creg[r], old);
+      const float reg[4] = {old[1], old[2], old[3], u};
+      float acc = cb;
+      acc = fmaf(cw4.x, reg[0], acc);
+      acc = fmaf(cw4.y, reg[1], acc);
+      acc = fmaf(cw4.z, reg[2], acc);
+      acc = fmaf(cw4.w, reg[3], acc);
+      if (q == 0 && live[r]) Io::store4(static_cast<io_t*>(p.conv_state) + ch[r] * 4, 0, reg);
+      u = acc;
+    } else if constexpr (CONV == -1) {
+      io_t* cs = static_cast<io_t*>(p.conv_state) + ch[r] * p.W;
+      float reg[kMaxW];
+#pragma unroll
+      for (int k = 0; k < kMaxW; ++k) {
+        if (k + 1 < p.W) reg[k] = Io::load(cs, k + 1);
+        else if (k + 1 == p.W) reg[k] = u;
+      }
+      float acc = cb;
+#pragma unroll
+      for (int k = 0; k < kMaxW; ++k)
+        if (k < p.W) acc = fmaf(p.conv_w[d * p.W + k], reg[k], acc);
+      if (q == 0 && live[r]) {
+#pragma unroll
+        for (int k = 0; k < kMaxW; ++k)
+          if (k < p.W) Io::store(cs, k, reg[k]);
+      }
+      u = acc;
+    }
+
+    float dt = Io::from_bits(d_bits[r]) + bias;
+    if (p.delta_softplus) dt = softplus_f32(dt);
+
+    // ---- one scan step on u for this lane's SPL states (n = q SPL ..)
+    float yv = 0.f;
+#pragma unroll
+    for (int n = 0; n < SPL; ++n) {
+      const float abar = exp2_fast(dt * a2[n]);
+      const float coef = fmaf(abar, ia[n], -ia[n]);
+      h[r][n] = fmaf(abar, h[r][n], coef * (Bv[r][n] * u));
+      yv = fmaf(Cv[r][n], h[r][n], yv);
+    }
+    if (live[r]) Vec<SPL>::store(p.h + ch[r] * N + n0, h[r]);
+    yv = sum_channel_lanes<LPC>(yv);
+    if (q == 0 && live[r]) {
+      yv = fmaf(dsk, u, yv);
+      if (zg) yv *= silu(Io::from_bits(z_bits[r]));
+      Io::store(static_cast<io_t*>(p.y), ch[r], yv);
+    }
+  }
+}
+
+// Rows per thread: 4 when the batch allows (fewer, longer-lived waves with more independent
+// loads in flight), else 1.
+template <typename io_t, int N, int R>
+void launch_nr(const StepParams& p, hipStream_t stream) {
+  constexpr int LPC = N >= 4 ? N / 4 : 1;
+  const int64_t total = (p.B + R - 1) / R * p.D * LPC;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (!p.conv_state)
+    hipLaunchKernelGGL((step_kernel<io_t, N, 0, R>), grid, dim3(256), 0, stream, p);
+  else if (p.W == 4)
+    hipLaunchKernelGGL((step_kernel<io_t, N, 4, R>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((step_kernel<io_t, N, -1, R>), grid, dim3(256), 0, stream, p);
 }
 
 template <typename io_t, int N>
 void launch_n(const StepParams& p, hipStream_t stream) {
-  constexpr int LPC = N >= 4 ? N / 4 : 1;
-  const int64_t total = p.B * p.D * LPC;
-  const dim3 grid((unsigned)((total + 255) / 256));
-  if (!p.conv_state)
-    hipLaunchKernelGGL((step_kernel<io_t, N, 0>), grid, dim3(256), 0, stream, p);
-  else if (p.W == 4)
-    hipLaunchKernelGGL((step_kernel<io_t, N, 4>), grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL((step_kernel<io_t, N, -1>), grid, dim3(256), 0, stream, p);
+  if (p.B >= 4) launch_nr<io_t, N, 4>(p, stream);
+  else launch_nr<io_t, N, 1>(p, stream);
 }
 
 template <typename io_t>

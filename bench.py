@@ -122,16 +122,31 @@ def copy_ceiling_gbs(torch, nbytes=1 << 30, reps=10):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def smi_during(fn, torch, max_s=20.0):
+def settle(fn, torch, seconds):
+    """Launch fn back to back (batches of 64, synchronised) for the given time. The GPU raises its
+    clocks only under sustained load: after several seconds idle (input generation) the first
+    milliseconds of work run about 10% slower, so the timed region must not start cold."""
+    i, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(64):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+    return i
+
+
+def smi_during(fn, torch, min_s=0.5, max_s=20.0):
     """Socket power and clocks from amd-smi, sampled while fn is launched back to back (in
-    batches of 64 with a synchronisation between them, until amd-smi has answered or max_s has
-    passed). An "error" entry when amd-smi is not available."""
+    batches of 64 with a synchronisation between them) for at least min_s and until amd-smi
+    has answered or max_s has passed. An "error" entry when amd-smi is not available."""
     proc = None
     try:
+        # the driver's metrics lag the load: amd-smi starts after a second of sustained work
+        settle(fn, torch, 1.0)
         proc = subprocess.Popen(["amd-smi", "metric", "--power", "--clock", "--json"],
                                 stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
         i, t0 = 0, time.perf_counter()
-        while proc.poll() is None and time.perf_counter() - t0 < max_s:
+        while (proc.poll() is None or time.perf_counter() - t0 < min_s) and time.perf_counter() - t0 < max_s:
             for _ in range(64):
                 fn(i)
                 i += 1
@@ -146,11 +161,13 @@ def smi_during(fn, torch, max_s=20.0):
                 "gfx_clk_MHz_min": min(gfx) if gfx else None,
                 "mem_clk_MHz": val(g["clock"].get("mem_0", {}).get("clk")),
                 "launches_during_sample": i,
-                "sampled": "amd-smi metric, once, while the benchmark kernel ran back to back"}
+                "sampled": "amd-smi metric, once, while the benchmark kernel ran back to back "
+                           "just before the timed region"}
     except Exception as e:  # reporting only: a missing or changed tool must not stop the bench
         torch.cuda.synchronize()
         if proc is not None and proc.poll() is None:
             proc.kill()
+        settle(fn, torch, min_s)
         return {"error": type(e).__name__}
 
 
@@ -211,6 +228,13 @@ def main():
         s = sets[i % len(sets)]
         ssm.scan_fwd(s["x"], s["delta"], A, s["Bm"], s["Cm"], Dskip=Dskip, z=s["z"], y=s["y"], h_last=s["h"])
 
+    # before the timed region: sustained load (the clock/power sample doubles as the settle
+    # phase), so the W warmup steps and K timed steps run at the clocks a busy GPU holds
+    if args.no_smi:
+        settle(step, torch, 0.5)
+        clocks = None
+    else:
+        clocks = smi_during(step, torch)
     wall_ms, kern_ms = timed(step, args.steps, args.warmup, torch)
     med_ms, min_ms = per_launch_ms(step, args.steps, torch)
     nbytes = scan_bytes(B, L, D, N, 2)
@@ -256,8 +280,8 @@ def main():
     }
 
     out["copy_ceiling_GB_s"] = round(copy_ceiling_gbs(torch), 1)
-    if not args.no_smi:
-        out["gpu_clocks_power"] = smi_during(step, torch)
+    if clocks is not None:
+        out["gpu_clocks_power"] = clocks
 
     if not args.no_secondary:
         out["secondary"] = secondary(torch, np, inputs, ssm, dev)

@@ -56,7 +56,7 @@ template <int Q>
 __device__ void chunk_prologue(const SsdParams& p, int64_t b, int64_t c, int64_t h, float a,
                                float* sS, float* sPhi, float* sTot) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t t = c * Q + tid;
   float dt = 0.f;
   if (tid < Q && t < p.L) {
@@ -157,7 +157,9 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
     *reinterpret_cast<uint4*>(Bt + (int64_t)n * Q + j0) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
   }
   // G tiles
-  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  // the wave index is the same for all lanes of a wave: readfirstlane lets the compiler keep it
+  // (and the row blocks derived from it) in scalar registers, so branches on it are not divergent
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 4, r16 = lane & 15;
   constexpr int NIB = Q / 16, KS = N / 32, NTILES = NIB * (NIB + 1) / 2;
   bf16_t* G = static_cast<bf16_t*>(p.ws_G) + (b * nch + c) * (int64_t)(Q * Q);
   for (int k = part * 4 + w; k < NTILES; k += 16) {
@@ -206,7 +208,9 @@ __global__ __launch_bounds__(512) void ssd_state_kernel(SsdParams p) {
   const int64_t h = blockIdx.x, b = blockIdx.y;
   const int64_t nch = (p.L + Q - 1) / Q;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  // the wave index is the same for all lanes of a wave: readfirstlane lets the compiler keep it
+  // (and the row blocks derived from it) in scalar registers, so branches on it are not divergent
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 4, r16 = lane & 15;
   const int pq = w >> 1, w2 = w & 1;
   const float a2 = p.A[h] * kLog2e;
   const int64_t PN = (int64_t)kP * N;
@@ -358,7 +362,9 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
   stage_x_transposed_raw<Q>(p, b, c, h, Xt);
   __syncthreads();
 
-  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  // the wave index is the same for all lanes of a wave: readfirstlane lets the compiler keep it
+  // (and the row blocks derived from it) in scalar registers, so branches on it are not divergent
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 4, r16 = lane & 15;
   constexpr int NIB = Q / 16;   // 16-row blocks of the chunk
   constexpr int KS = N / 32;    // K steps over the state dimension
   const bf16_t* Cg = static_cast<const bf16_t*>(p.Cm);

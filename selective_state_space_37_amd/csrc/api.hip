@@ -66,6 +66,8 @@ int64_t auto_segment_len(int64_t B, int64_t L, int64_t D, int64_t N) {
   const int64_t ch = scan_channels_per_wg(N);
   const int64_t wgs = ((D + ch - 1) / ch) * B;
   if (L <= kMinSegment || wgs >= 2 * kPlanCUs) return L;
+  // aim for one round of resident workgroups: four per CU (the state-only pass holds
+  // about 120 registers per lane, four waves per SIMD)
   int64_t nseg = (4 * kPlanCUs + wgs - 1) / wgs;
   int64_t seg = (L + nseg - 1) / nseg;
   seg = ((seg + kTile - 1) / kTile) * kTile;

@@ -72,7 +72,11 @@ void scan_kernel(ScanParams p) {
   __shared__ __attribute__((aligned(16))) float s_bc[2][T][N][2];          // (B_n, C_n)
   // partial readouts per slice; at CH = 32 a wave holds two slices, whose rows are offset by 32
   // banks so their writes do not collide
-  constexpr int kYStride = FULL ? T * CH + (CH < 64 ? 32 : 0) : 1;
+  // (only when the padding still lets OCC workgroups share a CU's 160 KB of LDS)
+  constexpr int kLdsUnpadded = 2 * T * CH * 8 + (FULL ? 2 * T * (CH / 4) * (int)sizeof(raw4) : 16) +
+                               2 * T * N * 8 + (FULL ? KS * T * CH * 4 : 4);
+  constexpr bool kPadY = FULL && CH < 64 && kLdsUnpadded + KS * 32 * 4 <= 163840 / OCC;
+  constexpr int kYStride = FULL ? T * CH + (kPadY ? 32 : 0) : 1;
   __shared__ float s_y[FULL ? KS : 1][kYStride];
 
   const int tid = threadIdx.x;
@@ -146,15 +150,16 @@ void scan_kernel(ScanParams p) {
     ld_boff[k] = (uint32_t)(((g / (CH / 4)) * D + 4 * cg) * (int64_t)sizeof(io_t));
     ld_ok[k] = (g < Cfg::kGroups) && cg_ok;
   }
-  auto tile_ptr = [&](const io_t* base, int tile) {   // uniform
+  auto tile_ptr = [&](const io_t* base, int tile) __attribute__((always_inline)) {   // uniform
     return reinterpret_cast<const char*>(base + (seg_row0 + (int64_t)tile * T) * D + c0);
   };
-  auto bc_ptr = [&](const io_t* base, int tile) {     // uniform
+  auto bc_ptr = [&](const io_t* base, int tile) __attribute__((always_inline)) {     // uniform
     return reinterpret_cast<const char*>(base + (seg_row0 + (int64_t)tile * T) * N);
   };
   using raw_t = raw4;
 
-  auto issue_loads = [&](int tile) {
+  // (the lambdas below are forced inline: what they capture by reference must stay in registers)
+  auto issue_loads = [&](int tile) __attribute__((always_inline)) {
     const int64_t t0 = t_begin + (int64_t)tile * T;
     const bool full_tile = tile < n_full;   // uniform: only the ragged last tile predicates rows
     const char* xb = tile_ptr(xg, tile);
@@ -197,7 +202,7 @@ void scan_kernel(ScanParams p) {
   // Rows past the segment end (ragged last tile) are committed as Delta = 0, x = 0, B = C = 0:
   // the identity step, whatever the registers held. RAGGED is a compile-time switch so that
   // full tiles carry no row tests at all.
-  auto commit_impl = [&](auto ragged_tag, int tile, int buf) {
+  auto commit_impl = [&](auto ragged_tag, int tile, int buf) __attribute__((always_inline)) {
     constexpr bool RAGGED = decltype(ragged_tag)::value;
     const int64_t t0 = t_begin + (int64_t)tile * T;
 #pragma unroll
@@ -247,7 +252,7 @@ void scan_kernel(ScanParams p) {
       }
     }
   };
-  auto commit_tile = [&](int tile, int buf) {
+  auto commit_tile = [&](int tile, int buf) __attribute__((always_inline)) {
     if (tile < n_full) commit_impl(std::false_type{}, tile, buf);
     else commit_impl(std::true_type{}, tile, buf);
   };

@@ -3,6 +3,7 @@ from __future__ import annotations
 
 import glob
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -19,28 +20,57 @@ ARCH = "gfx950"
 # Packed FP32 instructions are disabled on purpose; the compiler still vectorises scalar code.
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=" + ARCH, "-fPIC", "-I" + INCLUDE,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-Wall", "-Wno-unused-function"]
+         "-Wall", "-Wno-unused-function",
+         # per-kernel register / scratch / occupancy report (checked below, kept in _build/)
+         "-Rpass-analysis=kernel-resource-usage"]
+RESOURCES = os.path.join(OBJ_DIR, "kernel_resources.txt")
+_REMARK = re.compile(r"remark:\s+(Function Name|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|"
+                     r"Occupancy \[waves/SIMD\]|LDS Size \[bytes/block\]): (\S+)")
+
+
+def _resources(stderr: str):
+    """(kernel, {field: value}) from the compiler's kernel-resource-usage remarks."""
+    out, cur = [], None
+    for m in _REMARK.finditer(stderr):
+        k, v = m.group(1), m.group(2)
+        if k == "Function Name":
+            cur = (v, {})
+            out.append(cur)
+        elif cur is not None:
+            cur[1][k.split(" ")[0]] = v
+    return out
 
 
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def _compile(src: str) -> str:
+def _compile(src: str):
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
     cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed for %s" % src)
-    return obj
+    return obj, _resources(r.stderr)
 
 
 def build(verbose: bool = False) -> str:
     """Compile every csrc/*.hip for gfx950 and link selective_state_space_37_amd/libssm.so."""
     os.makedirs(OBJ_DIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, sources()))
+        results = list(ex.map(_compile, sources()))
+    objs = [o for o, _ in results]
+    kernels = [k for _, ks in results for k in ks]
+    with open(RESOURCES, "w") as f:
+        for name, res in kernels:
+            f.write("%s %s\n" % (name, " ".join("%s=%s" % kv for kv in sorted(res.items()))))
+    # every kernel keeps its working set in registers and LDS: a kernel that needs per-lane
+    # scratch memory (a spill, or a local array the compiler could not place in registers)
+    # is a performance bug, so the build stops
+    spilled = [n for n, res in kernels if res.get("ScratchSize", "0") != "0"]
+    if spilled:
+        raise RuntimeError("kernels using scratch memory: %s (see %s)" % (", ".join(spilled), RESOURCES))
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

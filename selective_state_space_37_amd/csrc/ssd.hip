@@ -91,11 +91,14 @@ __device__ __forceinline__ int xt_swizzle_words(int row) {
   return (8 * ((row >> 4) & 3)) & (Q / 2 - 1);
 }
 
-// Stage x[b, chunk, h, :] transposed into LDS without conversion: each thread takes two
-// consecutive tokens, and the two 16-bit values of one channel go into one 32-bit LDS word with a
-// byte permute.
+// Stage x[b, chunk, h, :] transposed into LDS (the layout above), each token's column scaled by
+//   cp_j = exp(a (S_e - S_j)) phi_j,   e = the last token of j's 16-token tile (S_e >= S_j),
+// computed from the chunk's (S, phi) table sp; a2 = a log2(e). Each thread takes two
+// consecutive tokens, so every LDS write is one 32-bit word holding the pair (j, j + 1) of one
+// channel; the scaled values are rounded to bf16 once. Tokens past L are staged as zeros.
 template <int Q>
-__device__ void stage_x_transposed_raw(const SsdParams& p, int64_t b, int64_t c, int64_t h, __bf16* Xt) {
+__device__ void stage_x_transposed_scaled(const SsdParams& p, int64_t b, int64_t c, int64_t h, __bf16* Xt,
+                                          const float2* sp, float a2) {
   const bf16_t* xg = static_cast<const bf16_t*>(p.x);
   uint32_t* X32 = reinterpret_cast<uint32_t*>(Xt);
   for (int g = threadIdx.x; g < (Q / 2) * (kP / 8); g += blockDim.x) {
@@ -104,13 +107,18 @@ __device__ void stage_x_transposed_raw(const SsdParams& p, int64_t b, int64_t c,
     uint4 r0 = make_uint4(0, 0, 0, 0), r1 = r0;
     if (t < p.L) r0 = *reinterpret_cast<const uint4*>(xg + ((b * p.L + t) * p.H + h) * kP + pg * 8);
     if (t + 1 < p.L) r1 = *reinterpret_cast<const uint4*>(xg + ((b * p.L + t + 1) * p.H + h) * kP + pg * 8);
+    const float2 v0 = sp[2 * jp], v1 = sp[2 * jp + 1];
+    const float se = sp[(2 * jp) | 15].x;
+    const float cp0 = exp2_fast(a2 * (se - v0.x)) * v0.y, cp1 = exp2_fast(a2 * (se - v1.x)) * v1.y;
     const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w}, w1[4] = {r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      // low halves (channel 2k) and high halves (channel 2k+1) of the two tokens
-      const int r0 = pg * 8 + 2 * k, r1 = r0 + 1;
-      X32[r0 * ((Q + 8) / 2) + (jp ^ xt_swizzle_words<Q>(r0))] = __builtin_amdgcn_perm(w1[k], w0[k], 0x05040100u);
-      X32[r1 * ((Q + 8) / 2) + (jp ^ xt_swizzle_words<Q>(r1))] = __builtin_amdgcn_perm(w1[k], w0[k], 0x07060302u);
+      // channels 2k (low halves) and 2k+1 (high halves) of the two tokens
+      const int ra = pg * 8 + 2 * k, rb = ra + 1;
+      X32[ra * ((Q + 8) / 2) + (jp ^ xt_swizzle_words<Q>(ra))] =
+          (uint32_t)f32_to_bf16(bf16_lo(w0[k]) * cp0) | ((uint32_t)f32_to_bf16(bf16_lo(w1[k]) * cp1) << 16);
+      X32[rb * ((Q + 8) / 2) + (jp ^ xt_swizzle_words<Q>(rb))] =
+          (uint32_t)f32_to_bf16(bf16_hi(w0[k]) * cp0) | ((uint32_t)f32_to_bf16(bf16_hi(w1[k]) * cp1) << 16);
     }
   }
 }
@@ -336,30 +344,35 @@ __global__ __launch_bounds__(512) void ssd_state_kernel(SsdParams p) {
 }
 
 // ---------------------------------------------------------------------------- outputs
-// Decay of a mask entry (i, j), j <= i: exp(a (S_i - S_j)) phi_j. For a tile whose 16 tokens j all
-// precede row i (off the diagonal) it factors through the tile's last token e:
-//   exp(a (S_i - S_e)) * [exp(a (S_e - S_j)) phi_j],
-// both exponents <= 0 (no overflow); the bracket depends on j only and is tabulated once per
-// chunk (sCp), the first factor is one exp per lane per tile. Diagonal tiles use the direct form.
+// Decay of a mask entry (i, j), j <= i: exp(a (S_i - S_j)) phi_j. It factors through the last
+// token e of j's 16-token tile:
+//   exp(a (S_i - S_e)) * [exp(a (S_e - S_j)) phi_j].
+// The bracket depends on j only and is folded into x^T when it is staged (exponent <= 0). The
+// first factor is one exp per lane and tile: <= 1 off the diagonal, and on the diagonal tile
+// (S_i <= S_e, at most 15 steps apart) at most exp(15 |a| max Delta), far inside the range of
+// float32 and bf16. So every mask entry is G_ij times a per-row factor, with the causal cut
+// j <= i on the diagonal tile.
 template <int Q, int N>
 __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 Xt[kP * (Q + 8)];
-  __shared__ __attribute__((aligned(16))) float sCp[Q];
-  __shared__ float sS[Q], sPhi[Q];
+  // the carried-in state h_{c-1} (P x N bf16), staged once for the four waves; rows padded by
+  // 8 elements so a wave's 16-byte fragment reads (16 rows apart by one row) hit 64 banks
+  __shared__ __attribute__((aligned(16))) __bf16 Hs[kP * (N + 8)];
+  __shared__ float sS[Q];
   const int64_t h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
   const int64_t nch = gridDim.y;
   const float a2 = p.A[h] * kLog2e;
   const int tid = threadIdx.x;
+  const float2* sp = p.ws_sphi + ((b * nch + c) * p.H + h) * Q;
+  if (tid < Q) sS[tid] = sp[tid].x;
+  stage_x_transposed_scaled<Q>(p, b, c, h, Xt, sp, a2);
   {
-    const float2* sp = p.ws_sphi + ((b * nch + c) * p.H + h) * Q;
-    if (tid < Q) {
-      const float2 v = sp[tid];
-      sS[tid] = v.x;
-      sPhi[tid] = v.y;
-      sCp[tid] = exp2_fast(a2 * (sp[tid | 15].x - v.x)) * v.y;
+    const bf16_t* hin = static_cast<const bf16_t*>(p.ws_hin) + ((b * nch + c) * p.H + h) * (int64_t)(kP * N);
+    for (int e = tid; e < kP * N / 8; e += blockDim.x) {   // 16-byte pieces
+      const int row = e / (N / 8), c8 = (e % (N / 8)) * 8;
+      *reinterpret_cast<uint4*>(&Hs[row * (N + 8) + c8]) = *reinterpret_cast<const uint4*>(hin + row * N + c8);
     }
   }
-  stage_x_transposed_raw<Q>(p, b, c, h, Xt);
   __syncthreads();
 
   // the wave index is the same for all lanes of a wave: readfirstlane lets the compiler keep it
@@ -369,7 +382,6 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
   constexpr int KS = N / 32;    // K steps over the state dimension
   const bf16_t* Cg = static_cast<const bf16_t*>(p.Cm);
   const bf16_t* G = static_cast<const bf16_t*>(p.ws_G) + (b * nch + c) * (int64_t)(Q * Q);
-  const bf16_t* hin = static_cast<const bf16_t*>(p.ws_hin) + ((b * nch + c) * p.H + h) * (int64_t)(kP * N);
   const float dsk = p.Dskip ? p.Dskip[h] : 0.f;
   const bf16_t* zg = static_cast<const bf16_t*>(p.z);
   bf16_t* yg = static_cast<bf16_t*>(p.y);
@@ -388,7 +400,8 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) hf[ks][pt] = load_frag(hin + (pt * 16 + r16) * N + ks * 32 + 8 * g);
+    for (int pt = 0; pt < 4; ++pt)
+      hf[ks][pt] = *reinterpret_cast<const bf16x8*>(&Hs[(pt * 16 + r16) * (N + 8) + ks * 32 + 8 * g]);
   auto load_c = [&](int ib, bf16x8 out[KS]) {
     const int64_t ti = c * Q + ib * 16 + r16;
 #pragma unroll
@@ -397,6 +410,9 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
   };
   bf16x8 cnext[KS];
   if (NIB >= 4 || w < NIB) load_c(block_of(0), cnext);
+  // fully unrolled: the C fragments loaded one block ahead are then renamed, not copied (a copy
+  // of registers with loads in flight would wait for them at the end of the previous block)
+#pragma unroll
   for (int kb = 0; kb < kBlocksPerWave; ++kb) {
     const int ib = block_of(kb);
     if (ib >= NIB) break;
@@ -431,8 +447,12 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
     auto load_g = [&](int jt) {
       return jt <= ib ? *reinterpret_cast<const uint2*>(Grow + jt * 16 + 4 * g) : make_uint2(0, 0);
     };
+    // fully unrolled (at most NIB / 2 pairs, leaving at the diagonal): the pair prefetched one
+    // step ahead is renamed rather than copied, so its loads overlap the current pair's work
     uint2 gcur[2] = {load_g(0), load_g(1)}, gnext[2];
-    for (int jp = 0; 2 * jp <= ib; ++jp) {
+#pragma unroll
+    for (int jp = 0; jp < (NIB + 1) / 2; ++jp) {
+      if (2 * jp > ib) break;   // uniform (ib is a scalar)
       gnext[0] = load_g(2 * jp + 2);
       gnext[1] = load_g(2 * jp + 3);
       float m[8];
@@ -444,17 +464,12 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
         const int j0 = jt * 16 + 4 * g;
         if (jt < ib) {
           const float r = exp2_fast(a2 * (Si - sS[jt * 16 + 15]));
-          const float4 cp = *reinterpret_cast<const float4*>(&sCp[j0]);
-          m[half * 4 + 0] = gv[0] * r * cp.x;
-          m[half * 4 + 1] = gv[1] * r * cp.y;
-          m[half * 4 + 2] = gv[2] * r * cp.z;
-          m[half * 4 + 3] = gv[3] * r * cp.w;
-        } else if (jt == ib) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = j0 + r;
-            m[half * 4 + r] = (j <= il) ? gv[r] * exp2_fast(a2 * (Si - sS[j])) * sPhi[j] : 0.f;
-          }
+          for (int q = 0; q < 4; ++q) m[half * 4 + q] = gv[q] * r;
+        } else if (jt == ib) {
+          const float r = exp2_fast(a2 * (Si - sS[jt * 16 + 15]));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) m[half * 4 + q] = (j0 + q <= il) ? gv[q] * r : 0.f;
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) m[half * 4 + r] = 0.f;

@@ -74,6 +74,19 @@ def test_segmented_plan(seg):
     assert err <= gu.TOL["f32"]
 
 
+@pytest.mark.parametrize("N", [1, 4, 8])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("seg", [37, 200])
+def test_segmented_plan_small_states(N, dtype, seg):
+    """The segmented plan for the smaller state sizes (64-channel tiles at N <= 4, element-wise
+    B/C loads at N = 1 and 4 in bf16): segment ends that fall inside a 16-token tile, a ragged
+    sequence end and a ragged channel tail (D = 136)."""
+    inp = _case(seed=25 + N, Bsz=2, L=517, D=136, N=N, dtype=dtype, h0=True)
+    err = gu.scan_parity(inp, gu.scan_on_gpu(inp, segment_len=seg))
+    print("N", N, dtype, "segment", seg, "err", err)
+    assert err <= gu.TOL[dtype]
+
+
 def test_split_handoff_matches_whole():
     inp = _case(seed=24, Bsz=1, L=300, D=64, h0=True)
     y, hl = gu.scan_on_gpu(inp)

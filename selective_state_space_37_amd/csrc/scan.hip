@@ -16,16 +16,18 @@
 //     on MI355X's 256 CUs, so no SIMD carries an extra wave at the end.
 //   * T-token tiles of (Delta, x) pairs (Delta activated once per element by the loader), z in
 //     its storage type, and (B_n, C_n) pairs are staged through LDS with wide coalesced loads,
-//     double buffered: the global loads of tile i+1 are in flight while tile i runs. Per token a
-//     lane then needs one 8-byte and one 16-byte LDS read.
+//     double buffered: the global loads of tile i+1 are in flight while tile i runs, and the loop
+//     waits for memory once per tile (at the commit of the next tile; the y stores of a tile are
+//     issued after that commit). Per token a lane then needs one 8-byte and one 16-byte LDS read.
 //   * each lane writes its partial readout to LDS; after a barrier the threads split the tile's
 //     (token, channel) outputs, add the KS partials in a fixed order (deterministic), add D x,
 //     gate, round and store y with coalesced row stores.
-//   * padded tokens (ragged L tail) get Delta = 0 and x = 0, which makes the step the identity.
+//   * padded tokens (ragged L tail) are committed with Delta = 0, x = 0 and B = C = 0, which
+//     makes the step the identity.
 // Long, narrow inputs (few channel tiles) are cut into L-segments: a state-only pass gives each
 // segment's local end state and sum of Delta; a carry pass runs the segment recurrence
 // h_in[s+1] = exp(A sum Delta_s) h_in[s] + h_loc[s]; the full pass then starts every segment
-// from its carry. The pages' "only state passes between chunks".
+// from its carry. Segments exchange nothing but the state, as the pages' chunked view says.
 #include <type_traits>
 
 #include "device_common.h"
@@ -48,6 +50,40 @@ struct ScanCfg {
 
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their maximum (no wait).
 constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Raw buffer access. A buffer descriptor holds a base address and a size in bytes; a load at an
+// offset at or past the size returns zero and a store there is dropped. The tile loops build one
+// descriptor per tile and tensor (scalar work) whose size ends with the tile's last row inside
+// the segment, so the rows of a ragged last tile read as zeros and their y stores vanish with no
+// per-lane row tests, and the lanes pass only a 32-bit byte offset. Word 3 selects the 32-bit
+// data format with untyped (raw) addressing.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRawRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRawRsrcWord3);
+}
+__device__ __forceinline__ void buf_load(Rsrc r, uint32_t off, uint2& out) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  out = make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ void buf_load(Rsrc r, uint32_t off, uint4& out) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  out = make_uint4(v[0], v[1], v[2], v[3]);
+}
+// one element's raw bits / one element store, in storage type io_t
+__device__ __forceinline__ uint32_t buf_load_bits(Rsrc r, uint32_t off, float*) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load_bits(Rsrc r, uint32_t off, bf16_t*) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store(Rsrc r, uint32_t off, float v, float*) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store(Rsrc r, uint32_t off, float v, bf16_t*) {
+  __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, off, 0, 0);
+}
 
 // 16-byte chunking of a tile's B (and C) block in storage type io_t.
 template <typename io_t, int T, int N, int kThreads>
@@ -119,14 +155,13 @@ void scan_kernel(ScanParams p) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) bias4[k] = p.delta_bias[cgl + k];
 
-  // Load registers are zeroed once; afterwards a lane whose load is predicated off keeps its last
-  // value, and the commit of the ragged last tile zeroes what it must (so no per-tile selects).
+  // Raw load registers (zeroed once for the threads that load nothing; z stays zero without z)
   raw4 rx[Cfg::kGroupsPerThr], rd[Cfg::kGroupsPerThr], rz[Cfg::kGroupsPerThr];
 #pragma unroll
   for (int k = 0; k < Cfg::kGroupsPerThr; ++k) rx[k] = rd[k] = rz[k] = Io::zero4();
   // B and C of a tile are T * N consecutive elements. When a row of N elements is whole 16-byte
-  // chunks they move as chunks (threads below kChunks, a chunk never straddles a row, so the
-  // ragged last tile only drops whole chunks); otherwise element by element. Either way the
+  // chunks they move as chunks (threads below kChunks, a chunk never straddles a row, so a row
+  // past the segment end reads as whole zero chunks); otherwise element by element. Either way the
   // registers keep the raw storage bits until the tile is committed, so the loads of tile i+1
   // stay in flight while tile i runs.
   using BCC = BCChunks<io_t, T, N, Cfg::kThreads>;
@@ -137,89 +172,82 @@ void scan_kernel(ScanParams p) {
   for (int k = 0; k < Cfg::kBCPerThr; ++k) rB[k] = rC[k] = 0u;
   // tiles [0, n_full) have all T rows inside the segment (uniform 32-bit test)
   const int n_full = (int)((t_end - t_begin) / T);
-  // Addressing: a tile's block of x / delta / z (T rows of D, from channel c0) starts at a
-  // uniform address (scalar registers); each lane adds a 32-bit byte offset that is the same for
-  // every tile (T D < 2^31 is checked on the host). The loads then need no per-tile vector
-  // address arithmetic.
+  // Addressing: a tile's block of x / delta / z / y (T rows of D, from channel c0) and of B / C
+  // (T rows of N) is one buffer descriptor (scalar registers, rebuilt per tile); each lane adds a
+  // 32-bit byte offset that is the same for every tile (T D size < 2^31 since D <= 2^24, checked
+  // on the host). Channel groups past D read the next row or zeros and are never stored.
   const int64_t seg_row0 = b * L + t_begin;
   uint32_t ld_boff[Cfg::kGroupsPerThr];
-  bool ld_ok[Cfg::kGroupsPerThr];
 #pragma unroll
   for (int k = 0; k < Cfg::kGroupsPerThr; ++k) {
     const int g = tid + k * Cfg::kThreads;
     ld_boff[k] = (uint32_t)(((g / (CH / 4)) * D + 4 * cg) * (int64_t)sizeof(io_t));
-    ld_ok[k] = (g < Cfg::kGroups) && cg_ok;
   }
-  auto tile_ptr = [&](const io_t* base, int tile) __attribute__((always_inline)) {   // uniform
-    return reinterpret_cast<const char*>(base + (seg_row0 + (int64_t)tile * T) * D + c0);
+  // rows of the tile inside the segment (T on the full tiles)
+  auto tile_rows = [&](int tile) __attribute__((always_inline)) {
+    return tile < n_full ? T : (int)(t_end - t_begin - (int64_t)tile * T);
   };
-  auto bc_ptr = [&](const io_t* base, int tile) __attribute__((always_inline)) {     // uniform
-    return reinterpret_cast<const char*>(base + (seg_row0 + (int64_t)tile * T) * N);
+  // descriptor of the tile's block of a [*, row_len] tensor from column col0, ending with the
+  // tile's last row inside the segment
+  auto tile_rsrc = [&](const void* base, int64_t row_len, int64_t col0, int tile, int rows)
+      __attribute__((always_inline)) {
+    const char* blk = static_cast<const char*>(base) +
+                      ((seg_row0 + (int64_t)tile * T) * row_len + col0) * (int64_t)sizeof(io_t);
+    return make_rsrc(blk, (int)((rows * row_len - col0) * (int64_t)sizeof(io_t)));
   };
-  using raw_t = raw4;
 
   // (the lambdas below are forced inline: what they capture by reference must stay in registers)
   auto issue_loads = [&](int tile) __attribute__((always_inline)) {
-    const int64_t t0 = t_begin + (int64_t)tile * T;
-    const bool full_tile = tile < n_full;   // uniform: only the ragged last tile predicates rows
-    const char* xb = tile_ptr(xg, tile);
-    const char* db = tile_ptr(dg, tile);
-    const char* zb = has_z ? tile_ptr(zg, tile) : nullptr;
+    const int rows = tile_rows(tile);
+    const Rsrc xr = tile_rsrc(xg, D, c0, tile, rows);
+    const Rsrc dr = tile_rsrc(dg, D, c0, tile, rows);
+    const Rsrc zr = has_z ? tile_rsrc(zg, D, c0, tile, rows) : xr;
 #pragma unroll
     for (int k = 0; k < Cfg::kGroupsPerThr; ++k) {
-      const int r = (tid + k * Cfg::kThreads) / (CH / 4);
-      const bool ok = ld_ok[k] && (full_tile || t0 + r < t_end);
-      if (ok) {
-        rx[k] = *reinterpret_cast<const raw_t*>(xb + ld_boff[k]);
-        rd[k] = *reinterpret_cast<const raw_t*>(db + ld_boff[k]);
-        if (has_z) rz[k] = *reinterpret_cast<const raw_t*>(zb + ld_boff[k]);
+      if (tid + k * Cfg::kThreads < Cfg::kGroups) {
+        buf_load(xr, ld_boff[k], rx[k]);
+        buf_load(dr, ld_boff[k], rd[k]);
+        if (has_z) buf_load(zr, ld_boff[k], rz[k]);
       }
     }
-    const char* bb = bc_ptr(Bg, tile);
-    const char* cb = bc_ptr(Cg, tile);
+    const Rsrc br = tile_rsrc(Bg, N, 0, tile, rows);
+    const Rsrc cr = tile_rsrc(Cg, N, 0, tile, rows);
     if constexpr (kChunkBC) {
-      const int r = tid * BCC::kPerChunk / N;   // the chunk's row in the tile
-      const bool ok = tid < BCC::kChunks && (full_tile || t0 + r < t_end);
-      const uint32_t boff = (uint32_t)tid * 16u;
-      if (ok) {
-        rbv = *reinterpret_cast<const uint4*>(bb + boff);
-        if (FULL) rcv = *reinterpret_cast<const uint4*>(cb + boff);
+      if (tid < BCC::kChunks) {
+        buf_load(br, (uint32_t)tid * 16u, rbv);
+        if (FULL) buf_load(cr, (uint32_t)tid * 16u, rcv);
       }
     } else {
 #pragma unroll
       for (int k = 0; k < Cfg::kBCPerThr; ++k) {
         const int e = tid + k * Cfg::kThreads;
-        const int r = e / N;
-        const bool ok = (e < Cfg::kBC) && (full_tile || t0 + r < t_end);
-        if (ok) {
-          rB[k] = Io::load_bits(reinterpret_cast<const io_t*>(bb), e);
-          if (FULL) rC[k] = Io::load_bits(reinterpret_cast<const io_t*>(cb), e);
+        if (e < Cfg::kBC) {
+          rB[k] = buf_load_bits(br, (uint32_t)e * (uint32_t)sizeof(io_t), (io_t*)nullptr);
+          if (FULL) rC[k] = buf_load_bits(cr, (uint32_t)e * (uint32_t)sizeof(io_t), (io_t*)nullptr);
         }
       }
     }
   };
 
-  // Rows past the segment end (ragged last tile) are committed as Delta = 0, x = 0, B = C = 0:
-  // the identity step, whatever the registers held. RAGGED is a compile-time switch so that
-  // full tiles carry no row tests at all.
+  // Rows past the segment end (ragged last tile) load as x = 0, B = C = 0 and Delta = 0, and Delta
+  // is committed as 0 after the bias and softplus as well: the identity step. RAGGED is a
+  // compile-time switch so that full tiles carry no row tests at all.
   auto commit_impl = [&](auto ragged_tag, int tile, int buf) __attribute__((always_inline)) {
     constexpr bool RAGGED = decltype(ragged_tag)::value;
-    const int64_t t0 = t_begin + (int64_t)tile * T;
+    const int rows = tile_rows(tile);
 #pragma unroll
     for (int k = 0; k < Cfg::kGroupsPerThr; ++k) {
       const int g = tid + k * Cfg::kThreads;
       if (g < Cfg::kGroups) {
         const int r = g / (CH / 4);
-        const bool valid = !RAGGED || (t0 + r < t_end);
         float xv[4], dv[4];
         Io::unpack4(rx[k], xv);
         Io::unpack4(rd[k], dv);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          float u = p.delta_bias ? dv[q] + bias4[q] : dv[q];
+          float u = dv[q] + bias4[q];   // bias4 is zero without a bias
           if (p.delta_softplus) u = softplus_f32(u);
-          dv[q] = valid ? u : 0.f;
-          xv[q] = valid ? xv[q] : 0.f;
+          dv[q] = (!RAGGED || r < rows) ? u : 0.f;
         }
         float4* dst = reinterpret_cast<float4*>(&s_dx[buf][r][4 * cg]);
         dst[0] = make_float4(dv[0], xv[0], dv[1], xv[1]);
@@ -227,13 +255,15 @@ void scan_kernel(ScanParams p) {
         if (has_z) s_z[buf][r][cg] = rz[k];
       }
     }
+  };
+  // B and C: rows past the segment end were loaded as zeros, so both tile kinds commit alike
+  auto commit_bc = [&](int buf) __attribute__((always_inline)) {
     if constexpr (kChunkBC) {
       if (tid < BCC::kChunks) {
         // kPerChunk consecutive (B, C) elements -> interleaved (B_n, C_n) pairs
         float bv[BCC::kPerChunk], cv[BCC::kPerChunk];
-        const bool valid = !RAGGED || t0 + tid * BCC::kPerChunk / N < t_end;
-        Io::unpack_chunk(valid ? rbv : make_uint4(0, 0, 0, 0), bv);
-        if (FULL) Io::unpack_chunk(valid ? rcv : make_uint4(0, 0, 0, 0), cv);
+        Io::unpack_chunk(rbv, bv);
+        if (FULL) Io::unpack_chunk(rcv, cv);
         float4* bc = reinterpret_cast<float4*>(&s_bc[buf][0][0][0] + 2 * tid * BCC::kPerChunk);
 #pragma unroll
         for (int q = 0; q < BCC::kPerChunk / 2; ++q)
@@ -244,10 +274,9 @@ void scan_kernel(ScanParams p) {
       for (int k = 0; k < Cfg::kBCPerThr; ++k) {
         const int e = tid + k * Cfg::kThreads;
         if (e < Cfg::kBC) {
-          const bool valid = !RAGGED || t0 + e / N < t_end;
           float* bc = &s_bc[buf][0][0][0] + 2 * e;
-          bc[0] = valid ? Io::from_bits(rB[k]) : 0.f;
-          if (FULL) bc[1] = valid ? Io::from_bits(rC[k]) : 0.f;
+          bc[0] = Io::from_bits(rB[k]);
+          if (FULL) bc[1] = Io::from_bits(rC[k]);
         }
       }
     }
@@ -255,6 +284,7 @@ void scan_kernel(ScanParams p) {
   auto commit_tile = [&](int tile, int buf) __attribute__((always_inline)) {
     if (tile < n_full) commit_impl(std::false_type{}, tile, buf);
     else commit_impl(std::true_type{}, tile, buf);
+    commit_bc(buf);
   };
 
   // ---- per-lane recurrence constants: channel c, states n0 .. n0+NS-1
@@ -358,13 +388,11 @@ void scan_kernel(ScanParams p) {
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     if (tile + 1 < ntiles) commit_tile(tile + 1, buf ^ 1);
     if (FULL) {
-      const int64_t t0 = t_begin + (int64_t)tile * T;
-      const bool full_tile = tile < n_full;
-      io_t* yb = yg + (seg_row0 + (int64_t)tile * T) * D + c0;   // uniform
+      // rows past the segment end fall outside the descriptor and are dropped
+      const Rsrc yr = tile_rsrc(yg, D, c0, tile, tile_rows(tile));
+      if (c_ok)
 #pragma unroll
-      for (int k = 0; k < T / KS; ++k)
-        if (c_ok && (full_tile || t0 + slice + k * KS < t_end))
-          Io::store(reinterpret_cast<io_t*>(reinterpret_cast<char*>(yb) + y_boff[k]), 0, yout[k]);
+        for (int k = 0; k < T / KS; ++k) buf_store(yr, y_boff[k], yout[k], (io_t*)nullptr);
     }
     __syncthreads();
   }

@@ -11,6 +11,8 @@ already widened to fp32/fp64 -- widening is exact) and return fp64 results.
                    discretisation of the continuous SSM and the discrete recurrence/readout of
                    "Beyond attention: exploring Mamba and state space models", section on
                    state-space basics; softplus step size from the selective-SSM section.
+* ``scan_bwd``  -- the gradients of ``scan`` (its reverse-mode derivative written out in C):
+                   every input's gradient from dL/dy and dL/dh_last.
 * ``step``      -- one decode token with the width-W causal conv register of the
                    "Mamba and state space models" page, section on the fixed-size state.
 * ``ssd``       -- Mamba-2 with a scalar A per head as the plain recurrence (same page, section
@@ -52,6 +54,8 @@ def _configure(lib):
     i64, ci, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
     lib.oracle_scan.argtypes = [i64, i64, i64, i64] + [vp, vp, vp, ci] + [vp] * 8
     lib.oracle_scan.restype = None
+    lib.oracle_scan_bwd.argtypes = [i64, i64, i64, i64] + [vp, vp, vp, ci] + [vp] * 17
+    lib.oracle_scan_bwd.restype = None
     lib.oracle_step.argtypes = [i64, i64, i64, i64] + [vp, vp, vp, ci] + [vp] * 10
     lib.oracle_step.restype = None
     lib.oracle_ssd.argtypes = [i64, i64, i64, i64, i64] + [vp, vp, vp, ci] + [vp] * 8
@@ -80,6 +84,9 @@ class Variant:
 
     def scan(self, *a, **k):
         return scan(*a, _lib=self._lib, **k)
+
+    def scan_bwd(self, *a, **k):
+        return scan_bwd(*a, _lib=self._lib, **k)
 
     def step(self, *a, **k):
         return step(*a, _lib=self._lib, **k)
@@ -148,6 +155,40 @@ def scan(x, delta, A, Bm, Cm, *, delta_bias=None, delta_softplus=False, Dskip=No
     (_lib or _load()).oracle_scan(Bsz, L, D, N, _p(x), _p(delta), _p(delta_bias), int(bool(delta_softplus)),
                         _p(A), _p(Bm), _p(Cm), _p(Dskip), _p(z), _p(h0), _p(y), _p(h_last))
     return (y, h_last) if return_state else y
+
+
+def scan_bwd(x, delta, A, Bm, Cm, dy, *, delta_bias=None, delta_softplus=False, Dskip=None, z=None,
+             h0=None, dh_last=None, _lib=None):
+    """Gradients of ``scan`` for the loss L with dL/dy = dy [B, L, D] and dL/dh_last = dh_last
+    [B, D, N] (None: zero). Returns a dict of fp64 arrays: dx, ddelta, dz (None without z)
+    [B, L, D]; dA [D, N]; dBm, dCm [B, L, N]; dDskip, ddelta_bias [D]; dh0 [B, D, N] (each the
+    gradient at the given value, at zero where the optional input is absent)."""
+    x = _f64(x)
+    if x.ndim != 3:
+        raise ValueError("oracle.scan_bwd: x must be [B, L, D]")
+    Bsz, L, D = x.shape
+    A = _f64(A)
+    N = A.shape[1]
+    delta = _f64(delta, (Bsz, L, D))
+    A = _f64(A, (D, N))
+    Bm = _f64(Bm, (Bsz, L, N))
+    Cm = _f64(Cm, (Bsz, L, N))
+    dy = _f64(dy, (Bsz, L, D))
+    delta_bias = _f64(delta_bias, (D,))
+    Dskip = _f64(Dskip, (D,))
+    z = _f64(z, (Bsz, L, D))
+    h0 = _f64(h0, (Bsz, D, N))
+    dh_last = _f64(dh_last, (Bsz, D, N))
+    out = dict(dx=np.empty((Bsz, L, D)), ddelta=np.empty((Bsz, L, D)), dA=np.empty((D, N)),
+               dBm=np.empty((Bsz, L, N)), dCm=np.empty((Bsz, L, N)), dDskip=np.empty(D),
+               ddelta_bias=np.empty(D), dz=np.empty((Bsz, L, D)) if z is not None else None,
+               dh0=np.empty((Bsz, D, N)))
+    (_lib or _load()).oracle_scan_bwd(
+        Bsz, L, D, N, _p(x), _p(delta), _p(delta_bias), int(bool(delta_softplus)), _p(A), _p(Bm),
+        _p(Cm), _p(Dskip), _p(z), _p(h0), _p(dy), _p(dh_last), _p(out["dx"]), _p(out["ddelta"]),
+        _p(out["dA"]), _p(out["dBm"]), _p(out["dCm"]), _p(out["dDskip"]), _p(out["ddelta_bias"]),
+        _p(out["dz"]), _p(out["dh0"]))
+    return out
 
 
 def step(x, delta, A, Bm, Cm, h, *, delta_bias=None, delta_softplus=False, Dskip=None, z=None,

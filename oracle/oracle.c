@@ -1,6 +1,6 @@
 /*
- * oracle.c -- plain, slow, fp64 CPU oracle for the selective state-space (S6) forward pass,
- * its one-token decode step, and the Mamba-2 scalar-A (SSD) layer.
+ * oracle.c -- plain, slow, fp64 CPU oracle for the selective state-space (S6) forward pass and
+ * its gradients, its one-token decode step, and the Mamba-2 scalar-A (SSD) layer.
  *
  * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU-baseline leg
  * may load this library. It shares no code, header, table or constant with the GPU library;
@@ -100,6 +100,116 @@ void oracle_scan(int64_t Bsz, int64_t L, int64_t D, int64_t N,
       free(h);
     }
   }
+}
+
+/*
+ * oracle_scan_bwd: gradients of oracle_scan (its reverse-mode derivative, written out).
+ *   inputs as oracle_scan, plus dy = dL/dy [Bsz, L, D] and dh_last = dL/dh_last [Bsz, D, N]
+ *   (NULL: zero);
+ *   outputs dx, ddelta, dz [Bsz, L, D]; dA [D, N]; dBm, dCm [Bsz, L, N]; dDskip, ddelta_bias [D];
+ *   dh0 [Bsz, D, N]. dz is written only when z is given; dDskip, ddelta_bias, dh0 may be NULL
+ *   (they are the gradients at the given values, also when Dskip, delta_bias or h0 is absent:
+ *   then at zero).
+ * Per (b, d) the forward recurrence is run again keeping every state h_t, then t walks
+ * backwards with the adjoint g = dL/dh_t: it takes C_t times the gradient reaching the readout,
+ * feeds the derivatives of h_t = Abar h_{t-1} + phi B_t x_t with respect to its inputs, and
+ * passes Abar_t g on to h_{t-1}. Derivatives used (a = A[d, n], Abar = exp(Delta a),
+ * phi = expm1(Delta a) / a):
+ *   d Abar / d Delta = a Abar,  d phi / d Delta = Abar,
+ *   d Abar / d a = Delta Abar,  d phi / d a = (Delta Abar - phi) / a  (Delta^2 / 2 at a = 0),
+ *   d softplus(u) / du = sigmoid(u),  d (z sigmoid(z)) / dz = sigmoid(z) (1 + z (1 - sigmoid(z))).
+ * OpenMP splits the batch rows only (dBm, dCm sum over channels inside one row); the parameter
+ * gradients are summed per row and then over rows in order, so the result is independent of
+ * the thread count.
+ */
+void oracle_scan_bwd(int64_t Bsz, int64_t L, int64_t D, int64_t N,
+                     const double* x, const double* delta, const double* delta_bias, int delta_softplus,
+                     const double* A, const double* Bm, const double* Cm, const double* Dskip,
+                     const double* z, const double* h0, const double* dy, const double* dh_last,
+                     double* dx, double* ddelta, double* dA, double* dBm, double* dCm,
+                     double* dDskip, double* ddelta_bias, double* dz, double* dh0) {
+  double* pA = (double*)calloc((size_t)(Bsz * D * N) + 1, sizeof(double));
+  double* pD = (double*)calloc((size_t)(Bsz * D) + 1, sizeof(double));
+  double* pb = (double*)calloc((size_t)(Bsz * D) + 1, sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t b = 0; b < Bsz; ++b) {
+    double* hs = (double*)malloc((size_t)((L + 1) * N) * sizeof(double));  /* hs[t+1] = h_t */
+    double* g = (double*)malloc((size_t)N * sizeof(double));
+    for (int64_t i = 0; i < L * N; ++i) dBm[b * L * N + i] = dCm[b * L * N + i] = 0.0;
+    for (int64_t d = 0; d < D; ++d) {
+      for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        const int64_t io = (b * L + t) * D + d;
+        const double* Bt = Bm + (b * L + t) * N;
+        const double dt = o_step_size(delta[io], delta_bias, d, delta_softplus);
+        for (int64_t n = 0; n < N; ++n) {
+          const double a = A[d * N + n];
+          hs[(t + 1) * N + n] = exp(dt * a) * hs[t * N + n] + o_zoh_scale(dt, a) * Bt[n] * x[io];
+        }
+      }
+      for (int64_t n = 0; n < N; ++n) g[n] = dh_last ? dh_last[(b * D + d) * N + n] : 0.0;
+      for (int64_t t = L - 1; t >= 0; --t) {
+        const int64_t io = (b * L + t) * D + d;
+        const double* Bt = Bm + (b * L + t) * N;
+        const double* Ct = Cm + (b * L + t) * N;
+        const double u = delta[io] + (delta_bias ? delta_bias[d] : 0.0);
+        const double dt = delta_softplus ? o_softplus(u) : u;
+        const double xt = x[io];
+        /* gradient reaching y before the gate; the gate's own derivative needs y */
+        double gy = dy[io];
+        if (z) {
+          double yt = 0.0;
+          for (int64_t n = 0; n < N; ++n) yt += Ct[n] * hs[(t + 1) * N + n];
+          if (Dskip) yt += Dskip[d] * xt;
+          const double zt = z[io], sg = o_sigmoid(zt);
+          dz[io] = dy[io] * yt * sg * (1.0 + zt * (1.0 - sg));
+          gy = dy[io] * zt * sg;
+        }
+        double gx = Dskip ? Dskip[d] * gy : 0.0;
+        double gdt = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          const double a = A[d * N + n];
+          const double abar = exp(dt * a);
+          const double phi = o_zoh_scale(dt, a);
+          const double hprev = hs[t * N + n];
+          const double gn = g[n] + Ct[n] * gy;          /* dL/dh_t */
+          dCm[(b * L + t) * N + n] += gy * hs[(t + 1) * N + n];
+          dBm[(b * L + t) * N + n] += gn * phi * xt;
+          gx += gn * phi * Bt[n];
+          gdt += gn * (a * abar * hprev + abar * Bt[n] * xt);
+          const double dphi_da = a == 0.0 ? 0.5 * dt * dt : (dt * abar - phi) / a;
+          pA[(b * D + d) * N + n] += gn * (dt * abar * hprev + dphi_da * Bt[n] * xt);
+          g[n] = abar * gn;                             /* on to dL/dh_{t-1} */
+        }
+        const double gu = delta_softplus ? gdt * o_sigmoid(u) : gdt;
+        dx[io] = gx;
+        ddelta[io] = gu;
+        pb[b * D + d] += gu;
+        pD[b * D + d] += gy * xt;
+      }
+      if (dh0)
+        for (int64_t n = 0; n < N; ++n) dh0[(b * D + d) * N + n] = g[n];
+    }
+    free(g);
+    free(hs);
+  }
+  for (int64_t d = 0; d < D; ++d) {
+    for (int64_t n = 0; n < N; ++n) {
+      double s = 0.0;
+      for (int64_t b = 0; b < Bsz; ++b) s += pA[(b * D + d) * N + n];
+      dA[d * N + n] = s;
+    }
+    double sD = 0.0, sb = 0.0;
+    for (int64_t b = 0; b < Bsz; ++b) {
+      sD += pD[b * D + d];
+      sb += pb[b * D + d];
+    }
+    if (dDskip) dDskip[d] = sD;
+    if (ddelta_bias) ddelta_bias[d] = sb;
+  }
+  free(pb);
+  free(pD);
+  free(pA);
 }
 
 /*

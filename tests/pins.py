@@ -354,3 +354,54 @@ def check_ssd_equals_scan(ssd, scan, seed=31):
     )
     ys, hs = scan(**sc)
     return max(rel_err(y.reshape(Bsz, L, H * P), ys), rel_err(hl.reshape(Bsz, H * P, N), hs))
+
+
+# ----------------------------------------------------------------------------- scan gradients
+_GRAD_OF = (("x", "dx"), ("delta", "ddelta"), ("A", "dA"), ("Bm", "dBm"), ("Cm", "dCm"),
+            ("Dskip", "dDskip"), ("delta_bias", "ddelta_bias"), ("z", "dz"), ("h0", "dh0"))
+
+
+def _fd_loss(scan, case, dy, dh_last):
+    y, hl = scan(**case)
+    return float(np.sum(y * dy)) + (float(np.sum(hl * dh_last)) if dh_last is not None else 0.0)
+
+
+def check_bwd_finite_differences(scan_bwd, scan, seed=40, eps=1e-6):
+    """The gradients are the derivative of the forward map. For the loss
+    sum(dy * y) + sum(dh_last * h_last), every gradient entry must equal the central difference
+    (loss(v + eps) - loss(v - eps)) / (2 eps) of the forward oracle: brute force, accurate to about
+    1e-9 relative at eps = 1e-6 in fp64. Cases: (i) softplus with bias, gate, D term, h0, dh_last
+    and one A entry of exactly zero (the limit of the ZOH scale); (ii) plain Delta with none of the
+    optional inputs -- there the gradients of the absent bias, D and h0 are compared with the
+    differences taken at explicit zeros, where the forward map is the same."""
+    worst = 0.0
+    for k, kw in enumerate((dict(), dict(softplus=False, gate=False, dskip=False, h0=False, a_zero=False))):
+        case = tiny_scan_case(seed + k, Bsz=2, L=6, D=3, N=3, **kw)
+        g = RNG(seed + 10 + k)
+        dy = g.standard_normal(case["x"].shape)
+        dh_last = g.standard_normal((2, 3, 3)) if k == 0 else None
+        grads = scan_bwd(dy=dy, dh_last=dh_last, **case)
+        full = dict(case)
+        Bsz, L, D = case["x"].shape
+        N = case["A"].shape[1]
+        for key, shape in (("delta_bias", (D,)), ("Dskip", (D,)), ("h0", (Bsz, D, N))):
+            if full[key] is None:
+                full[key] = np.zeros(shape)
+        for key, gkey in _GRAD_OF:
+            if full.get(key) is None:
+                continue
+            arr = full[key] = np.array(full[key], dtype=np.float64)
+            fd = np.zeros_like(arr)
+            for idx in np.ndindex(arr.shape):
+                v = arr[idx]
+                arr[idx] = v + eps
+                lp = _fd_loss(scan, full, dy, dh_last)
+                arr[idx] = v - eps
+                lm = _fd_loss(scan, full, dy, dh_last)
+                arr[idx] = v
+                fd[idx] = (lp - lm) / (2 * eps)
+            worst = max(worst, rel_err(grads[gkey], fd))
+    return worst
+
+
+BWD_FD_TOL = 1e-7

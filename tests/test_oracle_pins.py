@@ -24,6 +24,10 @@ def test_scan_pin(name, check):
     assert err <= pins.SCAN_TOL.get(name, pins.DEFAULT_TOL), (name, err)
 
 
+def test_scan_bwd_finite_differences():
+    assert pins.check_bwd_finite_differences(oracle.scan_bwd, oracle.scan) <= pins.BWD_FD_TOL
+
+
 def test_step_equals_scan():
     assert pins.check_step_equals_scan(oracle.step, oracle.scan) <= 1e-12
 
@@ -90,6 +94,25 @@ SCAN_MUTANTS = {
     "x_from_next_channel": [("const double xt = x[io];", "const double xt = x[(b * L + t) * D + (d + 1) % D];")],
 }
 
+BWD_MUTANTS = {
+    "bwd_gate_derivative_short": [("dz[io] = dy[io] * yt * sg * (1.0 + zt * (1.0 - sg));",
+                                   "dz[io] = dy[io] * yt * sg;")],
+    "bwd_adjoint_not_decayed": [("g[n] = abar * gn;", "g[n] = gn;")],
+    "bwd_dC_previous_state": [("dCm[(b * L + t) * N + n] += gy * hs[(t + 1) * N + n];",
+                               "dCm[(b * L + t) * N + n] += gy * hs[t * N + n];")],
+    "bwd_ddelta_drops_state_term": [("gdt += gn * (a * abar * hprev + abar * Bt[n] * xt);",
+                                     "gdt += gn * (abar * Bt[n] * xt);")],
+    "bwd_dA_zero_limit": [("a == 0.0 ? 0.5 * dt * dt : (dt * abar - phi) / a;",
+                           "a == 0.0 ? 0.0 : (dt * abar - phi) / a;")],
+    "bwd_softplus_derivative_dropped": [("delta_softplus ? gdt * o_sigmoid(u) : gdt;", "gdt;")],
+    "bwd_dD_ungated": [("pD[b * D + d] += gy * xt;", "pD[b * D + d] += dy[io] * xt;")],
+    "bwd_dx_drops_D": [("double gx = Dskip ? Dskip[d] * gy : 0.0;", "double gx = 0.0;")],
+    "bwd_dh_last_ignored": [("g[n] = dh_last ? dh_last[(b * D + d) * N + n] : 0.0;", "g[n] = 0.0;")],
+    "bwd_dB_missing_scale": [("dBm[(b * L + t) * N + n] += gn * phi * xt;",
+                              "dBm[(b * L + t) * N + n] += gn * dt * xt;")],
+    "bwd_readout_adjoint_late": [("const double gn = g[n] + Ct[n] * gy;", "const double gn = g[n];")],
+}
+
 STEP_MUTANTS = {
     "conv_shift_wrong_way": [("for (int64_t k = 0; k + 1 < W; ++k) reg[k] = reg[k + 1];\n        reg[W - 1] = x[io];",
                               "for (int64_t k = W - 1; k > 0; --k) reg[k] = reg[k - 1];\n        reg[0] = x[io];")],
@@ -150,3 +173,14 @@ def test_ssd_mutant_caught(tmp_path, name):
     v = _mutant(tmp_path, name, SSD_MUTANTS[name])
     errs = [pins.check_ssd_quadratic(v.ssd, oracle.ssd_quadratic), pins.check_ssd_equals_scan(v.ssd, oracle.scan)]
     assert max(errs) > 1e-12, name
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_bwd_mutant_caught(tmp_path, name):
+    import warnings
+    v = _mutant(tmp_path, name, BWD_MUTANTS[name])
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")
+        with np.errstate(all="ignore"):
+            err = pins.check_bwd_finite_differences(v.scan_bwd, oracle.scan)
+    assert not (err <= pins.BWD_FD_TOL), "planted mistake %s passed the gradient pin" % name

@@ -1,7 +1,7 @@
 /*
  * ssm.h -- C ABI of libssm: the selective state-space (S6) forward pass on MI355X (gfx950).
  *
- * Three operations, as the Mamba pages state them:
+ * Three operations, as the Mamba pages state them (and the gradients of the first):
  *
  *   ssm_scan_fwd      The selective scan. Page "Beyond attention: exploring Mamba and state
  *                     space models" (ai-lab.club), state-space basics section: zero-order-hold
@@ -118,6 +118,62 @@ ssm_status ssm_scan_fwd_segmented(int64_t B, int64_t L, int64_t D, int64_t N, ss
                                   const float* Dskip, const void* z, const float* h0, void* y,
                                   float* h_last, int64_t segment_len,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ssm_scan_bwd -- gradients of ssm_scan_fwd (training): the derivative of the forward map for
+ * a loss L, given dy = dL/dy and optionally dh_last = dL/dh_last. The forward is the
+ * recurrence of the page "Beyond attention: exploring Mamba and state space models"
+ * (state-space basics and selective-SSM sections); its state is recomputed from checkpoints
+ * instead of being stored, the recomputation named on the page "Mamba and state space
+ * models" (section "scan on the chip").
+ *
+ *   forward inputs : as ssm_scan_fwd (x, delta, delta_bias, delta_softplus, A, Bm, Cm, Dskip,
+ *                    z, h0), unchanged
+ *   dy             : [B, L, D]  io_dtype     dL/dy (y after the gate)
+ *   dh_last        : [B, D, N]  float32 or NULL (zero)
+ *   dx, ddelta     : [B, L, D]  io_dtype     (out) dL/dx, dL/ddelta (ddelta is the gradient of
+ *                                            the raw delta: through the softplus when it is on)
+ *   dz             : [B, L, D]  io_dtype     (out) dL/dz; required when z is given, else ignored
+ *   dA             : [D, N]     float32      (out)
+ *   dBm, dCm       : [B, L, N]  float32      (out; sums over channels are kept in float32)
+ *   dDskip         : [D]        float32 or NULL (out; the gradient at Dskip, at zero if Dskip
+ *                                            is NULL)
+ *   ddelta_bias    : [D]        float32 or NULL (out; likewise at delta_bias or zero)
+ *   dh0            : [B, D, N]  float32 or NULL (out; dL/dh0, at h0 or at the zero state)
+ *
+ *   Sums over channels (dBm, dCm) and over batch rows and time (dA, dDskip, ddelta_bias) are
+ *   formed in a fixed order, so repeated calls give identical bits.
+ *   Requirements: those of ssm_scan_fwd; no output may overlap an input or another output;
+ *   the workspace (ssm_scan_bwd_workspace_bytes(), about 4 N / (storage size) times the size
+ *   of x plus partial sums) is required whenever B, L > 0. B == 0 or L == 0 writes zeros to
+ *   dA, dDskip, ddelta_bias and (B > 0) dh0 = dh_last or zeros.
+ */
+size_t ssm_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io_dtype);
+
+ssm_status ssm_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io_dtype,
+                        const void* x, const void* delta, const float* delta_bias, int delta_softplus,
+                        const float* A, const void* Bm, const void* Cm, const float* Dskip,
+                        const void* z, const float* h0, const void* dy, const float* dh_last,
+                        void* dx, void* ddelta, float* dA, float* dBm, float* dCm, float* dDskip,
+                        float* ddelta_bias, void* dz, float* dh0,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ssm_scan_bwd_segmented -- ssm_scan_bwd with an explicit segment length along L (rounded up
+ * to a multiple of 16; >= L means one segment). Used to check that the gradients do not depend
+ * on the split.
+ */
+size_t ssm_scan_bwd_segmented_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
+                                              int64_t segment_len);
+
+ssm_status ssm_scan_bwd_segmented(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io_dtype,
+                                  const void* x, const void* delta, const float* delta_bias,
+                                  int delta_softplus, const float* A, const void* Bm, const void* Cm,
+                                  const float* Dskip, const void* z, const float* h0, const void* dy,
+                                  const float* dh_last, void* dx, void* ddelta, float* dA, float* dBm,
+                                  float* dCm, float* dDskip, float* ddelta_bias, void* dz, float* dh0,
+                                  int64_t segment_len, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /*
  * ssm_state_update -- one decode token for B sequences of D channels (N states each).

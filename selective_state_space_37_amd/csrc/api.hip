@@ -133,6 +133,83 @@ ssm_status scan_common(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io,
   return from_hip(ssm::launch_scan(p, st), "ssm_scan_fwd launch");
 }
 
+// Backward plan: the forward's automatic segments (multiples of 16 tokens); an explicit length
+// is rounded up to a multiple of 16.
+int64_t bwd_segment_len(int64_t L, int64_t seg_len) {
+  seg_len = ((seg_len + kTile - 1) / kTile) * kTile;
+  return seg_len >= L ? L : seg_len;
+}
+
+ssm_status scan_bwd_common(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io, const void* x,
+                           const void* delta, const float* delta_bias, int delta_softplus, const float* A,
+                           const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                           const float* h0, const void* dy, const float* dh_last, void* dx, void* ddelta,
+                           float* dA, float* dBm, float* dCm, float* dDskip, float* ddelta_bias, void* dz,
+                           float* dh0, int64_t seg_len, void* ws, size_t ws_bytes, void* stream) {
+  if (B < 0 || L < 0) return fail(SSM_ERR_INVALID_ARGUMENT, "B=%lld and L=%lld must be >= 0", (long long)B, (long long)L);
+  if (D < 1 || (D % 4) != 0) return fail(SSM_ERR_INVALID_ARGUMENT, "D=%lld must be >= 1 and a multiple of 4", (long long)D);
+  if (!valid_dtype(io)) return fail(SSM_ERR_INVALID_ARGUMENT, "unknown io_dtype %d", (int)io);
+  if (!supported_scan_n(N)) return fail(SSM_ERR_UNSUPPORTED, "N=%lld: supported state sizes are 1, 2, 4, 8, 16", (long long)N);
+  if (D > kMaxScanD) return fail(SSM_ERR_UNSUPPORTED, "D=%lld: at most %lld channels", (long long)D, (long long)kMaxScanD);
+  if (seg_len < 1) return fail(SSM_ERR_INVALID_ARGUMENT, "segment_len=%lld must be >= 1", (long long)seg_len);
+  if (!A || !dA) return fail(SSM_ERR_INVALID_ARGUMENT, "A and dA must not be NULL");
+  if (z && !dz) return fail(SSM_ERR_INVALID_ARGUMENT, "dz must be given with z");
+  const size_t es = io_size(io);
+  const size_t tok = (size_t)(B * L * D) * es, bc = (size_t)(B * L * N) * es;
+  const size_t bcg = (size_t)(B * L * N) * 4, stb = (size_t)(B * D * N) * 4;
+  const size_t pd = (size_t)(D * N) * 4, vd = (size_t)D * 4;
+  if (B > 0 && L > 0) {
+    if (!x || !delta || !Bm || !Cm || !dy || !dx || !ddelta || !dBm || !dCm)
+      return fail(SSM_ERR_INVALID_ARGUMENT, "x, delta, Bm, Cm, dy, dx, ddelta, dBm and dCm must not be NULL");
+    if (!aligned16(x) || !aligned16(delta) || !aligned16(Bm) || !aligned16(Cm) || !aligned16(dy) ||
+        !aligned16(dx) || !aligned16(ddelta) || (z && !aligned16(z)) || (dz && !aligned16(dz)))
+      return fail(SSM_ERR_INVALID_ARGUMENT, "per-token tensors must be 16-byte aligned");
+  }
+  // outputs overlap no input and no other output
+  const void* ins[] = {x, delta, z, Bm, Cm, dy, A, delta_bias, Dskip, h0, dh_last};
+  const size_t insz[] = {tok, tok, tok, bc, bc, tok, pd, vd, vd, stb, stb};
+  void* outs[] = {dx, ddelta, z ? dz : nullptr, dA, dBm, dCm, dDskip, ddelta_bias, dh0};
+  const size_t outsz[] = {tok, tok, tok, pd, bcg, bcg, vd, vd, stb};
+  for (int o = 0; o < 9; ++o) {
+    for (int k = 0; k < 11; ++k)
+      if (overlaps(outs[o], outsz[o], ins[k], insz[k]))
+        return fail(SSM_ERR_INVALID_ARGUMENT, "a gradient output overlaps an input");
+    for (int k = o + 1; k < 9; ++k)
+      if (overlaps(outs[o], outsz[o], outs[k], outsz[k]))
+        return fail(SSM_ERR_INVALID_ARGUMENT, "two gradient outputs overlap");
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (B == 0 || L == 0) {
+    // empty sums: parameter gradients are zero; dh0 is dh_last passed through (or zero)
+    hipError_t e = hipMemsetAsync(dA, 0, pd, st);
+    if (e == hipSuccess && dDskip) e = hipMemsetAsync(dDskip, 0, vd, st);
+    if (e == hipSuccess && ddelta_bias) e = hipMemsetAsync(ddelta_bias, 0, vd, st);
+    if (e == hipSuccess && dh0 && B > 0)
+      e = dh_last ? hipMemcpyAsync(dh0, dh_last, stb, hipMemcpyDeviceToDevice, st) : hipMemsetAsync(dh0, 0, stb, st);
+    return from_hip(e, "empty backward");
+  }
+  const int64_t sl = bwd_segment_len(L, seg_len);
+  const int64_t nseg = num_segments(L, sl);
+  const size_t need = ssm::scan_bwd_workspace_bytes(B, L, D, N, nseg);
+  if (!ws) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace is NULL; %zu bytes needed", need);
+  if (ws_bytes < need) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (!aligned16(ws)) return fail(SSM_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+
+  ssm::ScanBwdParams p{};
+  p.B = B; p.L = L; p.D = D; p.N = N;
+  p.io_bf16 = io == SSM_BF16;
+  p.delta_softplus = delta_softplus ? 1 : 0;
+  p.x = x; p.delta = delta; p.z = z; p.Bm = Bm; p.Cm = Cm; p.dy = dy;
+  p.delta_bias = delta_bias; p.A = A; p.Dskip = Dskip; p.h0 = h0; p.dh_last = dh_last;
+  p.dx = dx; p.ddelta = ddelta; p.dz = z ? dz : nullptr; p.dA = dA; p.dBm = dBm; p.dCm = dCm;
+  p.dDskip = dDskip; p.ddelta_bias = ddelta_bias; p.dh0 = dh0;
+  p.seg_len = sl; p.nseg = nseg;
+  const int64_t ch = ssm::scan_bwd_channels_per_wg(N);
+  p.nct = (D + ch - 1) / ch;
+  ssm::scan_bwd_workspace_carve(p, ws);
+  return from_hip(ssm::launch_scan_bwd(p, st), "ssm_scan_bwd launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -178,6 +255,42 @@ ssm_status ssm_scan_fwd_segmented(int64_t B, int64_t L, int64_t D, int64_t N, ss
                                   void* ws, size_t ws_bytes, void* stream) {
   return scan_common(B, L, D, N, io, x, delta, delta_bias, delta_softplus, A, Bm, Cm, Dskip, z, h0, y,
                      h_last, segment_len, ws, ws_bytes, stream);
+}
+
+size_t ssm_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype) {
+  if (B <= 0 || L <= 0 || D <= 0 || !supported_scan_n(N)) return 0;
+  const int64_t sl = bwd_segment_len(L, auto_segment_len(B, L, D, N));
+  return ssm::scan_bwd_workspace_bytes(B, L, D, N, num_segments(L, sl));
+}
+
+size_t ssm_scan_bwd_segmented_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int64_t segment_len) {
+  if (B <= 0 || L <= 0 || D <= 0 || !supported_scan_n(N) || segment_len < 1) return 0;
+  const int64_t sl = bwd_segment_len(L, segment_len);
+  return ssm::scan_bwd_workspace_bytes(B, L, D, N, num_segments(L, sl));
+}
+
+ssm_status ssm_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io, const void* x,
+                        const void* delta, const float* delta_bias, int delta_softplus, const float* A,
+                        const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
+                        const void* dy, const float* dh_last, void* dx, void* ddelta, float* dA, float* dBm,
+                        float* dCm, float* dDskip, float* ddelta_bias, void* dz, float* dh0, void* ws,
+                        size_t ws_bytes, void* stream) {
+  const int64_t seg = (B > 0 && L > 0 && D > 0) ? auto_segment_len(B, L, D, N) : 1;
+  return scan_bwd_common(B, L, D, N, io, x, delta, delta_bias, delta_softplus, A, Bm, Cm, Dskip, z, h0, dy,
+                         dh_last, dx, ddelta, dA, dBm, dCm, dDskip, ddelta_bias, dz, dh0, seg, ws, ws_bytes,
+                         stream);
+}
+
+ssm_status ssm_scan_bwd_segmented(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io, const void* x,
+                                  const void* delta, const float* delta_bias, int delta_softplus,
+                                  const float* A, const void* Bm, const void* Cm, const float* Dskip,
+                                  const void* z, const float* h0, const void* dy, const float* dh_last,
+                                  void* dx, void* ddelta, float* dA, float* dBm, float* dCm, float* dDskip,
+                                  float* ddelta_bias, void* dz, float* dh0, int64_t segment_len, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  return scan_bwd_common(B, L, D, N, io, x, delta, delta_bias, delta_softplus, A, Bm, Cm, Dskip, z, h0, dy,
+                         dh_last, dx, ddelta, dA, dBm, dCm, dDskip, ddelta_bias, dz, dh0, segment_len, ws,
+                         ws_bytes, stream);
 }
 
 ssm_status ssm_state_update(int64_t B, int64_t D, int64_t N, int64_t W, ssm_dtype io, const void* x,

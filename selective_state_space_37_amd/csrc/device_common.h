@@ -8,6 +8,9 @@ namespace ssm {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their maximum (no wait).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // bfloat16 storage: the 16 high bits of an IEEE float.
 struct bf16_t {
   uint16_t bits;
@@ -33,6 +36,32 @@ __device__ __forceinline__ float rcp_fast(float v) { return __builtin_amdgcn_rcp
 // negative z, which gives -0 (the limit).
 __device__ __forceinline__ float silu(float zv) {
   return zv * rcp_fast(1.0f + exp2_fast(-zv * kLog2e));
+}
+
+// sigmoid(v) = 1 / (1 + e^-v) with the hardware exp and reciprocal (0 and 1 in the limits).
+__device__ __forceinline__ float sigmoid_fast(float v) {
+  return rcp_fast(1.0f + exp2_fast(-v * kLog2e));
+}
+
+// Raw buffer access. A buffer descriptor holds a base address and a size in bytes; a load at an
+// offset at or past the size returns zero and a store there is dropped. The tile loops build one
+// descriptor per tile and tensor (scalar work) whose size ends with the tile's last row inside
+// the segment, so the rows of a ragged last tile read as zeros and their stores vanish with no
+// per-lane row tests, and the lanes pass only a 32-bit byte offset. Word 3 selects the 32-bit
+// data format with untyped (raw) addressing.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRawRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRawRsrcWord3);
+}
+__device__ __forceinline__ void buf_load(Rsrc r, uint32_t off, uint2& out) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  out = make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ void buf_load(Rsrc r, uint32_t off, uint4& out) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  out = make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 // softplus(u) = log(1 + e^u) = max(u, 0) + log1p(e) with e = exp(-|u|) in (0, 1].
@@ -125,5 +154,19 @@ template <> struct IoTraits<bf16_t> {
     out[4] = bf16_lo(r.z); out[5] = bf16_hi(r.z); out[6] = bf16_lo(r.w); out[7] = bf16_hi(r.w);
   }
 };
+
+// One element's raw bits / one element store in storage type io_t, through a descriptor.
+__device__ __forceinline__ uint32_t buf_load_bits(Rsrc r, uint32_t off, float*) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load_bits(Rsrc r, uint32_t off, bf16_t*) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store(Rsrc r, uint32_t off, float v, float*) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store(Rsrc r, uint32_t off, float v, bf16_t*) {
+  __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, off, 0, 0);
+}
 
 }  // namespace ssm

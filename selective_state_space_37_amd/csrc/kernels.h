@@ -33,6 +33,58 @@ size_t scan_workspace_bytes(int64_t B, int64_t D, int64_t N, int64_t nseg);
 // Enqueue the scan (one to three kernels) on the stream. Returns hipSuccess or the launch error.
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream);
 
+// Enqueue only the segment carries of a plan with nseg >= 2 (state-only pass and carry pass):
+// afterwards ws_h[b, s] holds the state entering segment s. The segment length is a multiple
+// of 16 tokens.
+hipError_t launch_scan_carries(const ScanParams& p, hipStream_t stream);
+
+// Selective-scan backward (gradients by state recomputation).
+struct ScanBwdParams {
+  int64_t B, L, D, N;
+  int io_bf16;
+  int delta_softplus;
+  const void* x;
+  const void* delta;
+  const void* z;           // nullable
+  const void* Bm;
+  const void* Cm;
+  const void* dy;          // dL/d(output) [B, L, D] io
+  const float* delta_bias; // nullable
+  const float* A;
+  const float* Dskip;      // nullable
+  const float* h0;         // nullable
+  const float* dh_last;    // nullable: dL/dh_last [B, D, N]
+  void* dx;                // [B, L, D] io
+  void* ddelta;            // [B, L, D] io
+  void* dz;                // [B, L, D] io (when z)
+  float* dA;               // [D, N]
+  float* dBm;              // [B, L, N]
+  float* dCm;              // [B, L, N]
+  float* dDskip;           // nullable [D]
+  float* ddelta_bias;      // nullable [D]
+  float* dh0;              // nullable [B, D, N]
+  int64_t seg_len;         // multiple of 16 (or >= L)
+  int64_t nseg;
+  int64_t nct;             // channel tiles (D / channels per workgroup, rounded up)
+  // workspace parts
+  float* ws_ck;            // [B, ceil(L/8), N / NS, D, NS] state at the start of every 8-token tile
+  float* ws_pq;            // [B, L, nct, N, 2]  (dB, dC) partial sums per channel tile
+  float* ws_pA;            // [B, nseg, D, N]
+  float* ws_pD;            // [B, nseg, D]
+  float* ws_pb;            // [B, nseg, D]
+  float* ws_h;             // [B, nseg, D, N]  state entering each segment   (nseg > 1)
+  float* ws_sum;           // [B, nseg, D]     forward pass: sum of Delta    (nseg > 1)
+  float* ws_q;             // [B, nseg, D, N]  local adjoint before the segment (nseg > 1)
+  float* ws_dsum;          // [B, nseg, D]     sum of Delta over each segment (nseg > 1)
+  float* ws_E;             // [B, nseg, D, N]  adjoint entering each segment from later tokens
+};
+
+// Channels per workgroup of the backward kernels for state size N.
+int64_t scan_bwd_channels_per_wg(int64_t N);
+size_t scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int64_t nseg);
+void scan_bwd_workspace_carve(ScanBwdParams& p, void* ws);
+hipError_t launch_scan_bwd(const ScanBwdParams& p, hipStream_t stream);
+
 struct StepParams {
   int64_t B, D, N, W;
   int io_bf16;

@@ -48,43 +48,6 @@ struct ScanCfg {
   static constexpr int kBCPerThr = (kBC + kThreads - 1) / kThreads;
 };
 
-// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their maximum (no wait).
-constexpr int kWaitVmcnt0 = 0x0F70;
-
-// Raw buffer access. A buffer descriptor holds a base address and a size in bytes; a load at an
-// offset at or past the size returns zero and a store there is dropped. The tile loops build one
-// descriptor per tile and tensor (scalar work) whose size ends with the tile's last row inside
-// the segment, so the rows of a ragged last tile read as zeros and their y stores vanish with no
-// per-lane row tests, and the lanes pass only a 32-bit byte offset. Word 3 selects the 32-bit
-// data format with untyped (raw) addressing.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-constexpr int kRawRsrcWord3 = 0x00020000;
-
-__device__ __forceinline__ Rsrc make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRawRsrcWord3);
-}
-__device__ __forceinline__ void buf_load(Rsrc r, uint32_t off, uint2& out) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-  out = make_uint2(v[0], v[1]);
-}
-__device__ __forceinline__ void buf_load(Rsrc r, uint32_t off, uint4& out) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  out = make_uint4(v[0], v[1], v[2], v[3]);
-}
-// one element's raw bits / one element store, in storage type io_t
-__device__ __forceinline__ uint32_t buf_load_bits(Rsrc r, uint32_t off, float*) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-__device__ __forceinline__ uint32_t buf_load_bits(Rsrc r, uint32_t off, bf16_t*) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-}
-__device__ __forceinline__ void buf_store(Rsrc r, uint32_t off, float v, float*) {
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
-}
-__device__ __forceinline__ void buf_store(Rsrc r, uint32_t off, float v, bf16_t*) {
-  __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, off, 0, 0);
-}
-
 // 16-byte chunking of a tile's B (and C) block in storage type io_t.
 template <typename io_t, int T, int N, int kThreads>
 struct BCChunks {
@@ -450,6 +413,32 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The segment carries alone: the state-only pass over segments 0 .. nseg-2 and the carry pass,
+// which leave ws_h[b, s] = the state entering segment s (s = 0 .. nseg-1).
+template <typename io_t, int CH, int NS, int KS, int N, int OCC>
+hipError_t launch_carries_typed(const ScanParams& p, hipStream_t stream) {
+  constexpr int T = 16;
+  const dim3 block(CH * KS);
+  const unsigned gx = (unsigned)((p.D + CH - 1) / CH);
+  const dim3 grid_a(gx, (unsigned)p.B, (unsigned)(p.nseg - 1));
+  hipLaunchKernelGGL((scan_kernel<io_t, CH, NS, KS, T, N, false, OCC>), grid_a, block, 0, stream, p);
+  const int64_t chains = p.B * p.D * p.N;
+  hipLaunchKernelGGL(scan_carry_kernel, dim3((unsigned)((chains + 255) / 256)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename io_t>
+hipError_t launch_carries_io(const ScanParams& p, hipStream_t stream) {
+  switch (p.N) {
+    case 1: return launch_carries_typed<io_t, 64, 1, 1, 1, 1>(p, stream);
+    case 2: return launch_carries_typed<io_t, 64, 2, 1, 2, 1>(p, stream);
+    case 4: return launch_carries_typed<io_t, 64, 2, 2, 4, 1>(p, stream);
+    case 8: return launch_carries_typed<io_t, 32, 2, 4, 8, 1>(p, stream);
+    case 16: return launch_carries_typed<io_t, 32, 2, 8, 16, 5>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename io_t>
 hipError_t launch_io(const ScanParams& p, hipStream_t stream) {
   switch (p.N) {
@@ -471,6 +460,11 @@ size_t scan_workspace_bytes(int64_t B, int64_t D, int64_t N, int64_t nseg) {
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream) {
   return p.io_bf16 ? launch_io<bf16_t>(p, stream) : launch_io<float>(p, stream);
+}
+
+hipError_t launch_scan_carries(const ScanParams& p, hipStream_t stream) {
+  if (p.nseg < 2) return hipErrorInvalidValue;
+  return p.io_bf16 ? launch_carries_io<bf16_t>(p, stream) : launch_carries_io<float>(p, stream);
 }
 
 }  // namespace ssm

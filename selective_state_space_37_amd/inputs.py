@@ -30,6 +30,7 @@ import numpy as np
 TOKEN_BLOCK = 8192
 TID_X, TID_DELTA, TID_B, TID_C, TID_Z, TID_D, TID_CONVW, TID_A, TID_CONVREG = range(9)
 TID_STEP0 = 100
+TID_DY, TID_DHLAST = 20, 21
 
 # 0.5 * ln(expm1(0.01)): the per-channel step-size bias of the oracle-sized workload.
 DELTA_BIAS_SMALL = 0.5 * math.log(math.expm1(0.01))
@@ -175,6 +176,15 @@ def scan_long(seed: int = 2, Bsz: int = 1, L: int = 1 << 20, D: int = 256, N: in
               dtype: str = "f32") -> ScanInputs:
     """Long, narrow sequence (the induction-task length 1,048,576): distributions of scan_small."""
     return scan_small(seed=seed, Bsz=Bsz, L=L, D=D, N=N, dtype=dtype)
+
+
+def scan_grads(seed: int, Bsz: int, L: int, D: int, N: int, dtype: str = "f32",
+               dh_last: bool = True):
+    """Upstream gradients for the scan backward: dL/dy ~ N(0, 1) stored like the per-token
+    tensors [B, L, D], and dL/dh_last ~ N(0, 1) fp32 [B, D, N] (or None)."""
+    dy = store(draw_tokens(seed, TID_DY, Bsz, L, D), dtype)
+    dhl = draw_param(seed, TID_DHLAST, (Bsz, D, N)) if dh_last else None
+    return dy, dhl
 
 
 @dataclass

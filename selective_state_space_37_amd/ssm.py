@@ -21,6 +21,8 @@ STATUS = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARGUMENT", 2: "SSM_ERR_UNSUPPORTED",
 EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_last_error_detail",
            "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd",
            "ssm_scan_fwd_segmented_workspace_bytes", "ssm_scan_fwd_segmented",
+           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd",
+           "ssm_scan_bwd_segmented_workspace_bytes", "ssm_scan_bwd_segmented",
            "ssm_state_update", "ssd_chunk_fwd_workspace_bytes", "ssd_chunk_fwd")
 
 _lib = None
@@ -55,6 +57,15 @@ def load(path: str = LIB_PATH):
     lib.ssm_scan_fwd.restype = ci
     lib.ssm_scan_fwd_segmented.argtypes = scan_args + [i64, vp, sz, vp]
     lib.ssm_scan_fwd_segmented.restype = ci
+    lib.ssm_scan_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
+    lib.ssm_scan_bwd_workspace_bytes.restype = sz
+    lib.ssm_scan_bwd_segmented_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    lib.ssm_scan_bwd_segmented_workspace_bytes.restype = sz
+    bwd_args = [i64, i64, i64, i64, ci, vp, vp, vp, ci] + [vp] * 17
+    lib.ssm_scan_bwd.argtypes = bwd_args + [vp, sz, vp]
+    lib.ssm_scan_bwd.restype = ci
+    lib.ssm_scan_bwd_segmented.argtypes = bwd_args + [i64, vp, sz, vp]
+    lib.ssm_scan_bwd_segmented.restype = ci
     lib.ssm_state_update.argtypes = [i64, i64, i64, i64, ci, vp, vp, vp, ci, vp, vp, vp, vp, vp,
                                      vp, vp, vp, vp, vp, vp]
     lib.ssm_state_update.restype = ci
@@ -143,6 +154,53 @@ def scan_fwd(x, delta, A, Bm, Cm, *, delta_bias=None, delta_softplus=False, Dski
         st = lib.ssm_scan_fwd_segmented(*args, int(segment_len), _p(ws), nb, _stream(x))
     _check(st)
     return y, h_last
+
+
+def scan_bwd(x, delta, A, Bm, Cm, dy, *, delta_bias=None, delta_softplus=False, Dskip=None, z=None,
+             h0=None, dh_last=None, segment_len: Optional[int] = None,
+             ws: Optional[torch.Tensor] = None) -> dict:
+    """Gradients of ``scan_fwd`` given dy = dL/dy [B, L, D] (and dh_last = dL/dh_last [B, D, N]).
+    Returns a dict: dx, ddelta, dz (None without z) [B, L, D] in the storage type of x; dA [D, N],
+    dBm, dCm [B, L, N], dDskip, ddelta_bias [D], dh0 [B, D, N] in float32."""
+    lib = load()
+    Bsz, L, D = x.shape
+    N = A.shape[1]
+    io = x.dtype
+    dev = x.device
+    _dev(x, "x")
+    _dev(delta, "delta", io, (Bsz, L, D))
+    _dev(z, "z", io, (Bsz, L, D))
+    _dev(Bm, "Bm", io, (Bsz, L, N))
+    _dev(Cm, "Cm", io, (Bsz, L, N))
+    _dev(dy, "dy", io, (Bsz, L, D))
+    _dev(A, "A", torch.float32, (D, N))
+    _dev(delta_bias, "delta_bias", torch.float32, (D,))
+    _dev(Dskip, "Dskip", torch.float32, (D,))
+    _dev(h0, "h0", torch.float32, (Bsz, D, N))
+    _dev(dh_last, "dh_last", torch.float32, (Bsz, D, N))
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dx=torch.empty_like(x), ddelta=torch.empty_like(x),
+               dz=torch.empty_like(x) if z is not None else None,
+               dA=torch.empty((D, N), **f32), dBm=torch.empty((Bsz, L, N), **f32),
+               dCm=torch.empty((Bsz, L, N), **f32), dDskip=torch.empty((D,), **f32),
+               ddelta_bias=torch.empty((D,), **f32), dh0=torch.empty((Bsz, D, N), **f32))
+    code = _io_code(x)
+    if segment_len is None:
+        nb = lib.ssm_scan_bwd_workspace_bytes(Bsz, L, D, N, code)
+    else:
+        nb = lib.ssm_scan_bwd_segmented_workspace_bytes(Bsz, L, D, N, int(segment_len))
+    if ws is None or ws.numel() < nb:
+        ws = workspace(nb, dev)
+    args = [Bsz, L, D, N, code, _p(x), _p(delta), _p(delta_bias), int(bool(delta_softplus)), _p(A),
+            _p(Bm), _p(Cm), _p(Dskip), _p(z), _p(h0), _p(dy), _p(dh_last), _p(out["dx"]),
+            _p(out["ddelta"]), _p(out["dA"]), _p(out["dBm"]), _p(out["dCm"]), _p(out["dDskip"]),
+            _p(out["ddelta_bias"]), _p(out["dz"]), _p(out["dh0"])]
+    if segment_len is None:
+        st = lib.ssm_scan_bwd(*args, _p(ws), nb, _stream(x))
+    else:
+        st = lib.ssm_scan_bwd_segmented(*args, int(segment_len), _p(ws), nb, _stream(x))
+    _check(st)
+    return out
 
 
 def state_update(x, delta, A, Bm, Cm, h, *, delta_bias=None, delta_softplus=False, Dskip=None,

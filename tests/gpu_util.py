@@ -66,6 +66,54 @@ def scan_parity(inp, gpu_out, channels=None) -> float:
     return e
 
 
+# ----------------------------------------------------------------------------- scan backward
+BWD_KEYS = ("dx", "ddelta", "dz", "dA", "dBm", "dCm", "dDskip", "ddelta_bias", "dh0")
+
+
+def scan_bwd_on_gpu(inp: inputs.ScanInputs, dy, dh_last=None, segment_len=None):
+    out = ssm.scan_bwd(dev(inp.x), dev(inp.delta), dev(inp.A), dev(inp.Bm), dev(inp.Cm), dev(dy),
+                       delta_bias=dev(inp.delta_bias), delta_softplus=inp.delta_softplus,
+                       Dskip=dev(inp.Dskip), z=dev(inp.z), h0=dev(inp.h0), dh_last=dev(dh_last),
+                       segment_len=segment_len)
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in out.items()}
+
+
+def scan_bwd_oracle(inp: inputs.ScanInputs, dy, dh_last=None, channels=None, rows=None):
+    """Oracle gradients; channels restricts to a channel subset (everything but dBm, dCm then
+    matches the full problem's values on those channels), rows to a batch-row subset (everything
+    but dA, dDskip, ddelta_bias then matches on those rows)."""
+    w = lambda a: inputs.widen(a, inp.dtype)
+    ch = (lambda a, ax: a if a is None or channels is None else np.take(a, channels, axis=ax))
+    rw = (lambda a: a if a is None or rows is None else np.take(a, rows, axis=0))
+    return oracle.scan_bwd(rw(ch(w(inp.x), 2)), rw(ch(w(inp.delta), 2)), ch(inp.A, 0),
+                           rw(w(inp.Bm)), rw(w(inp.Cm)), rw(ch(w(dy), 2)),
+                           delta_bias=ch(inp.delta_bias, 0), delta_softplus=inp.delta_softplus,
+                           Dskip=ch(inp.Dskip, 0), z=rw(ch(w(inp.z), 2)), h0=rw(ch(inp.h0, 1)),
+                           dh_last=rw(ch(dh_last, 1)))
+
+
+def scan_bwd_errors(gpu: dict, ref: dict, channels=None, rows=None) -> dict:
+    """Per-gradient error (the parity metric); with channels / rows, only the entries that the
+    restricted oracle call determines are compared."""
+    errs = {}
+    for k in BWD_KEYS:
+        g, r = gpu.get(k), ref.get(k)
+        if r is None or g is None:
+            continue
+        if channels is not None:
+            if k in ("dBm", "dCm"):
+                continue
+            ax = {"dx": 2, "ddelta": 2, "dz": 2, "dA": 0, "dDskip": 0, "ddelta_bias": 0, "dh0": 1}[k]
+            g = np.take(g, channels, axis=ax)
+        if rows is not None:
+            if k in ("dA", "dDskip", "ddelta_bias"):
+                continue
+            g = np.take(g, rows, axis=0)
+        errs[k] = rel_err(g, r)
+    return errs
+
+
 # ----------------------------------------------------------------------------- decode step
 def step_on_gpu(step: inputs.DecodeStep, A, h, *, Dskip=None, conv_state=None, conv_w=None,
                 conv_b=None, delta_bias=None, delta_softplus=False):

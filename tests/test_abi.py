@@ -94,6 +94,43 @@ def test_workspace_queries(lib):
     assert lib.ssd_chunk_fwd_workspace_bytes(2, 8192, 80, 64, 128, 256, BF16) >= 2 * nch * (80 * 64 * 128 * 2 + 256 * 256 * 2 + 128 * 256 * 2)
 
 
+def bwd_call(lib, B=1, L=16, D=64, N=16, io=F32, x=A_, delta=2 * A_, A=3 * A_, Bm=4 * A_, Cm=5 * A_,
+             z=None, dy=6 * A_, dx=7 * A_, ddelta=8 * A_, dA=9 * A_, dBm=10 * A_, dCm=11 * A_,
+             dDskip=None, dz=None, dh0=None, ws=20 * A_, wsb=1 << 40, segment_len=None):
+    f = lambda v: fake(v) if v else None
+    args = [B, L, D, N, io, f(x), f(delta), None, 0, f(A), f(Bm), f(Cm), None, f(z), None, f(dy), None,
+            f(dx), f(ddelta), f(dA), f(dBm), f(dCm), f(dDskip), None, f(dz), f(dh0)]
+    if segment_len is None:
+        return lib.ssm_scan_bwd(*args, f(ws), wsb, None)
+    return lib.ssm_scan_bwd_segmented(*args, segment_len, f(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(N=3), UNSUPPORTED), (dict(D=6), INVALID), (dict(L=-1), INVALID), (dict(io=5), INVALID),
+    (dict(dA=0), INVALID), (dict(A=0), INVALID), (dict(dy=0), INVALID), (dict(dBm=0), INVALID),
+    (dict(z=12 * A_), INVALID),                        # z without dz
+    (dict(dx=A_ + 32), INVALID),                       # dx overlaps x
+    (dict(dCm=10 * A_ + 64), INVALID),                # dCm overlaps dBm
+    (dict(dDskip=9 * A_ + 16), INVALID),               # dDskip overlaps dA
+    (dict(ddelta=8 * A_ + 2), INVALID),                # misaligned
+    (dict(ws=None), WS_SMALL), (dict(wsb=100), WS_SMALL), (dict(ws=20 * A_ + 8), INVALID),
+    (dict(segment_len=0), INVALID), (dict(D=(1 << 24) + 4), UNSUPPORTED),
+])
+def test_scan_bwd_rejects(lib, kw, expect):
+    assert bwd_call(lib, **kw) == expect
+    assert lib.ssm_last_error_detail().decode() != ""
+
+
+def test_scan_bwd_workspace(lib):
+    B, L, D, N = 8, 2048, 5120, 16
+    nb = lib.ssm_scan_bwd_workspace_bytes(B, L, D, N, BF16)
+    # checkpoints every 8 tokens, (dB, dC) partial sums per 32-channel tile
+    assert nb >= 4 * (B * ((L + 7) // 8) * N * D + B * L * (D // 32) * 2 * N)
+    assert lib.ssm_scan_bwd_segmented_workspace_bytes(2, 1000, 64, 16, 100) > \
+        lib.ssm_scan_bwd_segmented_workspace_bytes(2, 1000, 64, 16, 1000)
+    assert lib.ssm_scan_bwd_workspace_bytes(0, L, D, N, BF16) == 0
+
+
 def step_call(lib, B=4, D=64, N=16, W=4, io=BF16, x=A_, delta=2 * A_, A=3 * A_, Bm=4 * A_, Cm=5 * A_,
               conv=None, conv_w=None, h=6 * A_, y=7 * A_):
     return lib.ssm_state_update(B, D, N, W, io, fake(x) if x else None, fake(delta), None, 0,

@@ -47,18 +47,22 @@ __global__ __launch_bounds__(CH * KS) void scan_bwd_kernel(ScanBwdParams p) {
   constexpr int kEl = (T * CH + kThreads - 1) / kThreads;  // (token, channel) elements per thread
   constexpr int kBC = T * N;                               // B (and C) elements per tile
   static_assert(kBC <= kThreads, "one B/C element per loading thread");
-  constexpr int kOut = T / KS;                              // outputs per thread per tile
 
-  // (Delta, x, gy, sigmoid(u)) per token and channel; ckpt uses (Delta, x), adj (Delta, gy)
-  __shared__ __attribute__((aligned(16))) float4 s_in[2][T][CH];
+  // per token and channel: (Delta, x) for the recurrence, (gy, sigmoid(u)) for the adjoint
+  __shared__ __attribute__((aligned(16))) float2 s_dx[2][T][CH];
+  __shared__ __attribute__((aligned(16))) float2 s_g[kCkpt ? 1 : 2][kCkpt ? 1 : T][CH];
   __shared__ float s_dzc[kFull ? 2 : 1][kFull ? T : 1][CH];        // dz = y * s_dzc
   __shared__ __attribute__((aligned(16))) float2 s_bc[2][T][N];     // (B_n, C_n)
-  // partials over the slices: dx, dDelta, y; two slices share a wave at CH = 32, so their rows
-  // are 32 banks apart
-  constexpr int kPStride = T * CH + 32;
+  // partials over the slices (half a tile): dx, dDelta, y; two slices share a wave at CH = 32,
+  // so their rows are 32 banks apart
+  constexpr int kPStride = (T / 2) * CH + 32;
   __shared__ float s_p[kFull ? 3 : 1][kFull ? KS : 1][kFull ? kPStride : 1];
-  // partials over the channels: row (i N + n) 2 + {0: dB, 1: dC}, one column per channel
-  constexpr int kQRows = T * N * 2, kQStride = CH + 4;
+  // partials over the channels (half a tile), one column per channel. The lane of slice s, token i, state
+  // n0 + j writes dB / dC (bc = 0 / 1) to q = (i NS + j) 2 + bc of its slice, stored at row
+  // ((q / 8) KS + s) 8 + q % 8: the two slices of a wave write rows 8 apart (32 banks apart with
+  // the row stride CH + 4), and rows of stride CH + 4 read as float4 hit distinct banks.
+  constexpr int kQRows = (T / 2) * N * 2, kQStride = CH + 4;
+  static_assert(((T / 2) * NS * 2) % 8 == 0, "row blocks of 8");
   __shared__ __attribute__((aligned(16))) float s_q[kFull ? kQRows : 1][kFull ? kQStride : 4];
 
   const int tid = threadIdx.x;
@@ -186,11 +190,11 @@ __global__ __launch_bounds__(CH * KS) void scan_bwd_kernel(ScanBwdParams p) {
         const bool ok = el_col_ok[k] && r < rows;
         const float u = IoTraits<io_t>::from_bits(rd[k]) + el_bias[k];
         const float dt = ok ? (p.delta_softplus ? softplus_f32(u) : u) : 0.f;
-        float4 v;
+        float2 v, w;
         v.x = dt;
         v.y = ok && !kAdj ? IoTraits<io_t>::from_bits(rx[k]) : 0.f;
-        v.z = 0.f;
-        v.w = 1.f;
+        w.x = 0.f;
+        w.y = 1.f;
         if constexpr (!kCkpt) {
           const float dyv = ok ? IoTraits<io_t>::from_bits(rg[k]) : 0.f;
           float gy = dyv, dzc = 0.f;
@@ -200,11 +204,12 @@ __global__ __launch_bounds__(CH * KS) void scan_bwd_kernel(ScanBwdParams p) {
             gy = dyv * zv * sg;
             dzc = dyv * sg * fmaf(zv, 1.0f - sg, 1.0f);
           }
-          v.z = gy;
-          if (p.delta_softplus) v.w = sigmoid_fast(u);
+          w.x = gy;
+          if (p.delta_softplus) w.y = sigmoid_fast(u);
           if constexpr (kFull) s_dzc[buf][r][col] = dzc;
+          s_g[buf][r][col] = w;
         }
-        s_in[buf][r][col] = v;
+        s_dx[buf][r][col] = v;
       }
     }
     if (tid < kBC) {
@@ -246,7 +251,7 @@ __global__ __launch_bounds__(CH * KS) void scan_bwd_kernel(ScanBwdParams p) {
       for (int j = 0; j < NS; ++j) hst[j] = h[j];
 #pragma unroll
       for (int i = 0; i < T; ++i) {
-        const float4 v = s_in[buf][i][chl];
+        const float2 v = s_dx[buf][i][chl];
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
           const float2 bc = s_bc[buf][i][n0 + j];
@@ -288,9 +293,6 @@ __global__ __launch_bounds__(CH * KS) void scan_bwd_kernel(ScanBwdParams p) {
   io_t* __restrict__ dxg = static_cast<io_t*>(p.dx);
   io_t* __restrict__ ddg = static_cast<io_t*>(p.ddelta);
   io_t* __restrict__ dzg = static_cast<io_t*>(p.dz);
-  uint32_t o_off[kOut];
-#pragma unroll
-  for (int k = 0; k < kOut; ++k) o_off[k] = (uint32_t)(((slice + k * KS) * D + chl) * (int64_t)sizeof(io_t));
 
   if (ntiles > 0) {
     issue_loads(ntiles - 1);
@@ -306,15 +308,29 @@ __global__ __launch_bounds__(CH * KS) void scan_bwd_kernel(ScanBwdParams p) {
     if constexpr (kAdj) {
 #pragma unroll
       for (int i = T - 1; i >= 0; --i) {
-        const float4 v = s_in[buf][i][chl];
+        const float dt = s_dx[buf][i][chl].x;
+        const float gy = s_g[buf][i][chl].x;
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-          const float abar = exp2_fast(v.x * a2[j]);
-          g[j] = abar * fmaf(s_bc[buf][i][n0 + j].y, v.z, g[j]);
+          const float abar = exp2_fast(dt * a2[j]);
+          g[j] = abar * fmaf(s_bc[buf][i][n0 + j].y, gy, g[j]);
         }
-        dsum += v.x;
+        dsum += dt;
       }
-    } else if constexpr (kFull) {
+    }
+
+    // ---- full: the tile backwards in two halves of TH tokens; after each half the partials
+    //      over the slices (dx, dDelta, y) and over the channels (dB, dC) are added from LDS
+    //      (half-sized buffers: three workgroups fit a CU). Outputs are kept in registers and
+    //      stored after the next tile's commit.
+    constexpr int TH = T / 2;
+    constexpr int kOutH = (TH + KS - 1) / KS;
+    constexpr int kQRowsH = TH * N * 2;
+    constexpr int kQPerThrH = (kQRowsH + kThreads - 1) / kThreads;
+    float o_dx[kFull ? 2 : 1][kOutH], o_dd[kFull ? 2 : 1][kOutH], o_dz[kFull ? 2 : 1][kOutH];
+    float o_q[kFull ? 2 : 1][kQPerThrH];
+    const int rows = tile_rows(tile);
+    if constexpr (kFull) {
       // forward recompute of the tile from its checkpoint, keeping h_t and Abar_t
       float H[T][NS], AB[T][NS];
       {
@@ -323,8 +339,7 @@ __global__ __launch_bounds__(CH * KS) void scan_bwd_kernel(ScanBwdParams p) {
         for (int j = 0; j < NS; ++j) h[j] = hck[j];
 #pragma unroll
         for (int i = 0; i < T; ++i) {
-          const float4 v = s_in[buf][i][chl];
-          float yp = 0.f;
+          const float2 v = s_dx[buf][i][chl];
 #pragma unroll
           for (int j = 0; j < NS; ++j) {
             const float2 bc = s_bc[buf][i][n0 + j];
@@ -332,81 +347,85 @@ __global__ __launch_bounds__(CH * KS) void scan_bwd_kernel(ScanBwdParams p) {
             h[j] = fmaf(abar, h[j], fmaf(abar, ia[j], -ia[j]) * (bc.x * v.y));
             H[i][j] = h[j];
             AB[i][j] = abar;
-            yp = fmaf(bc.y, h[j], yp);
-          }
-          if (has_z) s_p[2][slice][i * CH + chl] = yp;
-        }
-      }
-      // the tile backwards
-#pragma unroll
-      for (int i = T - 1; i >= 0; --i) {
-        const float4 v = s_in[buf][i][chl];
-        float dxp = 0.f, ddp = 0.f;
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-          const float2 bc = s_bc[buf][i][n0 + j];
-          const float hprev = i > 0 ? H[i - 1][j] : hck[j];
-          const float abar = AB[i][j];
-          const float gn = fmaf(bc.y, v.z, g[j]);             // dL/dh_t
-          const int row = (i * N + n0 + j) * 2;
-          s_q[row + 1][chl] = v.z * H[i][j];                  // dC partial
-          const float gphi = gn * fmaf(abar, ia[j], -ia[j]);
-          s_q[row][chl] = gphi * v.y;                         // dB partial
-          dxp = fmaf(gphi, bc.x, dxp);
-          const float bx = bc.x * v.y;
-          const float w = fmaf(av[j], hprev, bx);
-          const float ga = gn * abar;
-          const float vv = ga * w;
-          ddp += vv;
-          dAr[j] = fmaf(v.x, vv, dAr[j]);
-          dAr[j] = fmaf(-gphi, bx, dAr[j]);
-          g[j] = ga;                                          // on to dL/dh_{t-1}
-        }
-        s_p[0][slice][i * CH + chl] = dxp;
-        s_p[1][slice][i * CH + chl] = ddp;
-      }
-    }
-
-    // ---- combine (full): outputs of this thread are tokens slice + k KS of channel chl
-    float o_dx[kFull ? kOut : 1], o_dd[kFull ? kOut : 1], o_dz[kFull ? kOut : 1];
-    constexpr int kQPerThr = (kQRows + kThreads - 1) / kThreads;
-    float o_q[kFull ? kQPerThr : 1];
-    const int rows = tile_rows(tile);
-    if constexpr (kFull) {
-      __syncthreads();
-#pragma unroll
-      for (int k = 0; k < kOut; ++k) {
-        const int i = slice + k * KS;
-        float sx = s_p[0][0][i * CH + chl], sd = s_p[1][0][i * CH + chl];
-        float sy = has_z ? s_p[2][0][i * CH + chl] : 0.f;
-#pragma unroll
-        for (int q = 1; q < KS; ++q) {
-          sx += s_p[0][q][i * CH + chl];
-          sd += s_p[1][q][i * CH + chl];
-          if (has_z) sy += s_p[2][q][i * CH + chl];
-        }
-        const float4 v = s_in[buf][i][chl];
-        o_dx[k] = fmaf(dsk, v.z, sx);
-        o_dd[k] = sd * v.w;
-        o_dz[k] = has_z ? fmaf(dsk, v.y, sy) * s_dzc[buf][i][chl] : 0.f;
-        if (i < rows) {
-          accD = fmaf(v.z, v.y, accD);
-          accb += o_dd[k];
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < kQPerThr; ++m) {
-        const int r = tid + m * kThreads;
-        float s = 0.f;
-        if (r < kQRows) {
-          const float4* row = reinterpret_cast<const float4*>(&s_q[r][0]);
-#pragma unroll
-          for (int k = 0; k < CH / 4; ++k) {
-            const float4 q4 = row[k];
-            s += (q4.x + q4.y) + (q4.z + q4.w);
           }
         }
-        o_q[m] = s;
+      }
+#pragma unroll
+      for (int hf = 1; hf >= 0; --hf) {
+#pragma unroll
+        for (int il = TH - 1; il >= 0; --il) {
+          const int i = hf * TH + il;
+          const float2 v = s_dx[buf][i][chl];
+          const float gy = s_g[buf][i][chl].x;
+          float dxp = 0.f, ddp = 0.f, yp = 0.f;
+#pragma unroll
+          for (int j = 0; j < NS; ++j) {
+            const float2 bc = s_bc[buf][i][n0 + j];
+            const float hprev = i > 0 ? H[i - 1][j] : hck[j];
+            const float abar = AB[i][j];
+            const float gn = fmaf(bc.y, gy, g[j]);              // dL/dh_t
+            const int q = (il * NS + j) * 2;
+            const int row = ((q >> 3) * KS + slice) * 8 + (q & 7);
+            s_q[row + 1][chl] = gy * H[i][j];                   // dC partial
+            const float gphi = gn * fmaf(abar, ia[j], -ia[j]);
+            s_q[row][chl] = gphi * v.y;                         // dB partial
+            dxp = fmaf(gphi, bc.x, dxp);
+            const float bx = bc.x * v.y;
+            const float w = fmaf(av[j], hprev, bx);
+            const float ga = gn * abar;
+            const float vv = ga * w;
+            ddp += vv;
+            dAr[j] = fmaf(v.x, vv, dAr[j]);
+            dAr[j] = fmaf(-gphi, bx, dAr[j]);
+            g[j] = ga;                                          // on to dL/dh_{t-1}
+            yp = fmaf(bc.y, H[i][j], yp);
+          }
+          s_p[0][slice][il * CH + chl] = dxp;
+          s_p[1][slice][il * CH + chl] = ddp;
+          if (has_z) s_p[2][slice][il * CH + chl] = yp;
+        }
+        __syncthreads();
+        // outputs of this thread: tokens hf TH + slice + k KS of channel chl
+#pragma unroll
+        for (int k = 0; k < kOutH; ++k) {
+          const int il = slice + k * KS;
+          o_dx[hf][k] = o_dd[hf][k] = o_dz[hf][k] = 0.f;
+          if (il < TH) {
+            const int i = hf * TH + il;
+            float sx = s_p[0][0][il * CH + chl], sd = s_p[1][0][il * CH + chl];
+            float sy = has_z ? s_p[2][0][il * CH + chl] : 0.f;
+#pragma unroll
+            for (int q = 1; q < KS; ++q) {
+              sx += s_p[0][q][il * CH + chl];
+              sd += s_p[1][q][il * CH + chl];
+              if (has_z) sy += s_p[2][q][il * CH + chl];
+            }
+            const float xv = s_dx[buf][i][chl].y;
+            const float2 w = s_g[buf][i][chl];
+            o_dx[hf][k] = fmaf(dsk, w.x, sx);
+            o_dd[hf][k] = sd * w.y;
+            o_dz[hf][k] = has_z ? fmaf(dsk, xv, sy) * s_dzc[buf][i][chl] : 0.f;
+            if (i < rows) {
+              accD = fmaf(w.x, xv, accD);
+              accb += o_dd[hf][k];
+            }
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < kQPerThrH; ++m) {
+          const int r = tid + m * kThreads;
+          float sum = 0.f;
+          if (r < kQRowsH) {
+            const float4* row = reinterpret_cast<const float4*>(&s_q[r][0]);
+#pragma unroll
+            for (int k = 0; k < CH / 4; ++k) {
+              const float4 q4 = row[k];
+              sum += (q4.x + q4.y) + (q4.z + q4.w);
+            }
+          }
+          o_q[hf][m] = sum;
+        }
+        if (hf == 1) __syncthreads();   // the second half reuses the buffers
       }
     }
     // every wave waits for the next tile's loads here (stores are issued after the commit:
@@ -416,26 +435,31 @@ __global__ __launch_bounds__(CH * KS) void scan_bwd_kernel(ScanBwdParams p) {
     if constexpr (kFull) {
       const Rsrc xr = tile_rsrc(dxg, D, c0, tile, rows);
       const Rsrc dr = tile_rsrc(ddg, D, c0, tile, rows);
-      if (c_ok) {
+      const Rsrc zr = has_z ? tile_rsrc(dzg, D, c0, tile, rows) : xr;
 #pragma unroll
-        for (int k = 0; k < kOut; ++k) {
-          buf_store(xr, o_off[k], o_dx[k], (io_t*)nullptr);
-          buf_store(dr, o_off[k], o_dd[k], (io_t*)nullptr);
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int k = 0; k < kOutH; ++k) {
+          const int il = slice + k * KS;
+          if (c_ok && il < TH) {
+            const uint32_t off = (uint32_t)(((hf * TH + il) * D + chl) * (int64_t)sizeof(io_t));
+            buf_store(xr, off, o_dx[hf][k], (io_t*)nullptr);
+            buf_store(dr, off, o_dd[hf][k], (io_t*)nullptr);
+            if (has_z) buf_store(zr, off, o_dz[hf][k], (io_t*)nullptr);
+          }
         }
-        if (has_z) {
-          const Rsrc zr = tile_rsrc(dzg, D, c0, tile, rows);
+        // (dB, dC) partials of this channel tile: ws_pq[((b L + t) nct + tile_c) 2N + (n 2 + bc)]
 #pragma unroll
-          for (int k = 0; k < kOut; ++k) buf_store(zr, o_off[k], o_dz[k], (io_t*)nullptr);
-        }
-      }
-      // (dB, dC) partials of this channel tile: ws_pq[((b L + t) nct + tile_c) 2N + (n 2 + bc)]
-#pragma unroll
-      for (int m = 0; m < kQPerThr; ++m) {
-        const int r = tid + m * kThreads;
-        const int i = r / (2 * N);
-        if (r < kQRows && i < rows) {
-          const int64_t t = seg_row0 + (int64_t)tile * T + i;
-          p.ws_pq[(t * p.nct + tile_c) * (2 * N) + (r % (2 * N))] = o_q[m];
+        for (int m = 0; m < kQPerThrH; ++m) {
+          // row r of s_q back to (token, state n, bc)
+          const int r = tid + m * kThreads;
+          const int q = (r / (8 * KS)) * 8 + (r & 7);
+          const int i = hf * TH + q / (2 * NS);
+          const int n = ((r >> 3) % KS) * NS + (q >> 1) % NS;
+          if (r < kQRowsH && i < rows) {
+            const int64_t t = seg_row0 + (int64_t)tile * T + i;
+            p.ws_pq[(t * p.nct + tile_c) * (2 * N) + 2 * n + (q & 1)] = o_q[hf][m];
+          }
         }
       }
     }

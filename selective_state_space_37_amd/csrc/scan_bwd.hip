@@ -48,11 +48,15 @@ __global__ __launch_bounds__(CH * KS) void scan_bwd_kernel(ScanBwdParams p) {
   constexpr int kBC = T * N;                               // B (and C) elements per tile
   static_assert(kBC <= kThreads, "one B/C element per loading thread");
 
+  // Staged tile operands. The full pass keeps one copy (a barrier separates the last read of
+  // a tile from the commit of the next, whose global loads were in flight meanwhile): 40 KB
+  // per workgroup; the other passes double-buffer.
+  constexpr int kNB = kFull ? 1 : 2;
   // per token and channel: (Delta, x) for the recurrence, (gy, sigmoid(u)) for the adjoint
-  __shared__ __attribute__((aligned(16))) float2 s_dx[2][T][CH];
-  __shared__ __attribute__((aligned(16))) float2 s_g[kCkpt ? 1 : 2][kCkpt ? 1 : T][CH];
-  __shared__ float s_dzc[kFull ? 2 : 1][kFull ? T : 1][CH];        // dz = y * s_dzc
-  __shared__ __attribute__((aligned(16))) float2 s_bc[2][T][N];     // (B_n, C_n)
+  __shared__ __attribute__((aligned(16))) float2 s_dx[kNB][T][CH];
+  __shared__ __attribute__((aligned(16))) float2 s_g[kCkpt ? 1 : kNB][kCkpt ? 1 : T][CH];
+  __shared__ float s_dzc[kFull ? kNB : 1][kFull ? T : 1][CH];      // dz = y * s_dzc
+  __shared__ __attribute__((aligned(16))) float2 s_bc[kNB][T][N];   // (B_n, C_n)
   // partials over the slices (half a tile): dx, dDelta, y; two slices share a wave at CH = 32,
   // so their rows are 32 banks apart
   constexpr int kPStride = (T / 2) * CH + 32;
@@ -302,7 +306,7 @@ __global__ __launch_bounds__(CH * KS) void scan_bwd_kernel(ScanBwdParams p) {
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int tile = ntiles - 1 - it;
-    const int buf = it & 1;
+    const int buf = kFull ? 0 : (it & 1);
     if (tile > 0) issue_loads(tile - 1);
 
     if constexpr (kAdj) {
@@ -430,8 +434,9 @@ __global__ __launch_bounds__(CH * KS) void scan_bwd_kernel(ScanBwdParams p) {
     }
     // every wave waits for the next tile's loads here (stores are issued after the commit:
     // they count in the same memory counter)
+    if constexpr (kFull) __syncthreads();   // single-buffered operands: all reads done
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    if (tile > 0) commit(tile - 1, buf ^ 1);
+    if (tile > 0) commit(tile - 1, kFull ? 0 : buf ^ 1);
     if constexpr (kFull) {
       const Rsrc xr = tile_rsrc(dxg, D, c0, tile, rows);
       const Rsrc dr = tile_rsrc(ddg, D, c0, tile, rows);
@@ -530,9 +535,17 @@ __global__ __launch_bounds__(256) void scan_bwd_reduce_bc_kernel(ScanBwdParams p
   if (i >= p.B * p.L * N2) return;
   const int64_t row = i / N2, r = i % N2;
   const float* src = p.ws_pq + row * p.nct * N2 + r;
-  float s = 0.f;
-  for (int64_t k = 0; k < p.nct; ++k) s += src[k * N2];
-  (r & 1 ? p.dCm : p.dBm)[row * p.N + (r >> 1)] = s;
+  // four independent partial sums (k mod 4) keep four loads in flight; fixed order throughout
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  int64_t k = 0;
+  for (; k + 4 <= p.nct; k += 4) {
+    s0 += src[k * N2];
+    s1 += src[(k + 1) * N2];
+    s2 += src[(k + 2) * N2];
+    s3 += src[(k + 3) * N2];
+  }
+  for (; k < p.nct; ++k) s0 += src[k * N2];
+  (r & 1 ? p.dCm : p.dBm)[row * p.N + (r >> 1)] = (s0 + s1) + (s2 + s3);
 }
 
 // dA, dD, dbias: sum over batch rows and segments in order, one thread per (d, n).

@@ -293,7 +293,8 @@ def main():
 
 
 def secondary(torch, np, inputs, ssm, dev):
-    """Long-sequence scan, decode step and SSD layer: kernel-time throughput (HIP events)."""
+    """Long-sequence scan, scan backward, decode step and SSD layer: kernel-time throughput (HIP
+    events)."""
     res = {}
     g = torch.Generator(device="cuda").manual_seed(7)
     r = lambda *s: torch.randn(*s, generator=g, device="cuda", dtype=torch.float32)
@@ -318,6 +319,30 @@ def secondary(torch, np, inputs, ssm, dev):
                                            "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
                                            "gelem_s": round(B * L * D / ms / 1e6, 1)}
     del x, z, delta, Bm, Cm, y
+
+    # scan backward at the layer shape: 8 x 2048 x 5120, N 16, bf16, gate and D term
+    B, L, D, N = LAYER["B"], LAYER["L"], LAYER["D"], LAYER["N"]
+    bf = torch.bfloat16
+    x, z, dy = r(B, L, D).to(bf), r(B, L, D).to(bf), r(B, L, D).to(bf)
+    delta = torch.clamp(torch.nn.functional.softplus(r(B, L, D) - 4), 1e-3, 0.1).to(bf)
+    Bm, Cm = r(B, L, N).to(bf), r(B, L, N).to(bf)
+    A = dev(inputs.structured_A(D, N))
+    Dk = r(D)
+    nb = ssm.load().ssm_scan_bwd_workspace_bytes(B, L, D, N, ssm.SSM_BF16)
+    ws = ssm.workspace(nb, "cuda")
+    fn = lambda i: ssm.scan_bwd(x, delta, A, Bm, Cm, dy, Dskip=Dk, z=z, ws=ws)
+    _, ms = timed(fn, 10, 3, torch)
+    # essential I/O: x, delta, z, dy, B, C in; dx, ddelta, dz (bf16), dB, dC (fp32) out
+    nbytes = 7 * B * L * D * 2 + 2 * B * L * N * 2 + 2 * B * L * N * 4 + 2 * D * N * 4 + 2 * D * 4
+    steps = B * L * D * N
+    # VALU model: checkpoint pass 5 single-rate + 1 half-rate exp (7 slots), main pass forward
+    # recompute 6 + exp (8 slots) and reverse walk 14 single-rate ops: 29 slots per state-step
+    res["scan_bwd_8x2048x5120_n16_bf16"] = {
+        "ms": round(ms, 4), "GB_s_essential_io": round(nbytes / ms / 1e6, 1),
+        "gelem_s": round(B * L * D / ms / 1e6, 1),
+        "valu_slot_frac": round(steps * 29 / (ms * 1e-3) / (PEAK_VALU_TOPS * 1e12), 4),
+        "workspace_MB": round(nb / 1e6, 1)}
+    del x, z, dy, delta, Bm, Cm, ws
 
     # decode: batch 128, d_inner 4096, N 16, bf16 I/O, conv width 4; 16 layers' states rotate
     B, D, N, W, layers = 128, 4096, 16, 4, 16

@@ -13,6 +13,8 @@ already widened to fp32/fp64 -- widening is exact) and return fp64 results.
                    state-space basics; softplus step size from the selective-SSM section.
 * ``scan_bwd``  -- the gradients of ``scan`` (its reverse-mode derivative written out in C):
                    every input's gradient from dL/dy and dL/dh_last.
+* ``conv1d``    -- the decode state's causal convolution run over a whole sequence (prefill),
+                   and ``scan_conv`` = that convolution followed by ``scan`` on its output.
 * ``step``      -- one decode token with the width-W causal conv register of the
                    "Mamba and state space models" page, section on the fixed-size state.
 * ``ssd``       -- Mamba-2 with a scalar A per head as the plain recurrence (same page, section
@@ -56,6 +58,8 @@ def _configure(lib):
     lib.oracle_scan.restype = None
     lib.oracle_scan_bwd.argtypes = [i64, i64, i64, i64] + [vp, vp, vp, ci] + [vp] * 17
     lib.oracle_scan_bwd.restype = None
+    lib.oracle_conv1d.argtypes = [i64, i64, i64, i64] + [vp] * 6
+    lib.oracle_conv1d.restype = None
     lib.oracle_step.argtypes = [i64, i64, i64, i64] + [vp, vp, vp, ci] + [vp] * 10
     lib.oracle_step.restype = None
     lib.oracle_ssd.argtypes = [i64, i64, i64, i64, i64] + [vp, vp, vp, ci] + [vp] * 8
@@ -90,6 +94,12 @@ class Variant:
 
     def step(self, *a, **k):
         return step(*a, _lib=self._lib, **k)
+
+    def scan_conv(self, *a, **k):
+        return scan_conv(*a, _lib=self._lib, **k)
+
+    def conv1d(self, *a, **k):
+        return conv1d(*a, _lib=self._lib, **k)
 
     def ssd(self, *a, **k):
         return ssd(*a, _lib=self._lib, **k)
@@ -189,6 +199,34 @@ def scan_bwd(x, delta, A, Bm, Cm, dy, *, delta_bias=None, delta_softplus=False, 
         _p(out["dA"]), _p(out["dBm"]), _p(out["dCm"]), _p(out["dDskip"]), _p(out["ddelta_bias"]),
         _p(out["dz"]), _p(out["dh0"]))
     return out
+
+
+def conv1d(x, conv_w, *, conv_b=None, conv_state=None, _lib=None):
+    """Causal depthwise convolution over [B, L, D] with weights [D, W] (the last one on the newest
+    input), optional bias [D] and register [B, D, W] of earlier raw inputs (oldest first; zeros if
+    None). Returns (u [B, L, D], register after the last token [B, D, W]) in fp64."""
+    x = _f64(x)
+    Bsz, L, D = x.shape
+    conv_w = _f64(conv_w)
+    W = conv_w.shape[1]
+    conv_w = _f64(conv_w, (D, W))
+    conv_b = _f64(conv_b, (D,))
+    conv_state = _f64(conv_state, (Bsz, D, W))
+    u = np.empty((Bsz, L, D))
+    reg = np.empty((Bsz, D, W))
+    (_lib or _load()).oracle_conv1d(Bsz, L, D, W, _p(x), _p(conv_w), _p(conv_b), _p(conv_state),
+                                    _p(u), _p(reg))
+    return u, reg
+
+
+def scan_conv(x, delta, A, Bm, Cm, conv_w, *, conv_b=None, conv_state=None, delta_bias=None,
+              delta_softplus=False, Dskip=None, z=None, h0=None, _lib=None):
+    """Prefill: ``conv1d`` of x, then ``scan`` with the convolution output as the SSM input (also
+    in the D term), as the decode step does token by token. Returns (y, h_last, register)."""
+    u, reg = conv1d(x, conv_w, conv_b=conv_b, conv_state=conv_state, _lib=_lib)
+    y, hl = scan(u, delta, A, Bm, Cm, delta_bias=delta_bias, delta_softplus=delta_softplus,
+                 Dskip=Dskip, z=z, h0=h0, _lib=_lib)
+    return y, hl, reg
 
 
 def step(x, delta, A, Bm, Cm, h, *, delta_bias=None, delta_softplus=False, Dskip=None, z=None,

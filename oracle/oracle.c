@@ -213,6 +213,38 @@ void oracle_scan_bwd(int64_t Bsz, int64_t L, int64_t D, int64_t N,
 }
 
 /*
+ * oracle_conv1d: the depthwise causal convolution the decode state keeps (page "Mamba and state
+ * space models", section "fixed-size state": a short convolution over the last inputs), run over
+ * a whole sequence for the prefill.
+ *   x, u        : [Bsz, L, D]    conv_w : [D, W] (conv_w[d, W-1] multiplies the newest input)
+ *   conv_b      : [D] or NULL    conv_in, conv_out : [Bsz, D, W] (oldest input first) or NULL
+ * u[b, t, d] = sum_k conv_w[d, k] * r_t[k] (+ conv_b[d]), where r_t holds the W raw inputs up to
+ * and including x_t, oldest first; inputs before the sequence come from conv_in (zeros if NULL).
+ * conv_out receives the register after the last token.
+ */
+void oracle_conv1d(int64_t Bsz, int64_t L, int64_t D, int64_t W, const double* x,
+                   const double* conv_w, const double* conv_b, const double* conv_in,
+                   double* u, double* conv_out) {
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t b = 0; b < Bsz; ++b) {
+    for (int64_t d = 0; d < D; ++d) {
+      double* reg = (double*)malloc((size_t)W * sizeof(double));
+      for (int64_t k = 0; k < W; ++k) reg[k] = conv_in ? conv_in[(b * D + d) * W + k] : 0.0;
+      for (int64_t t = 0; t < L; ++t) {
+        for (int64_t k = 0; k + 1 < W; ++k) reg[k] = reg[k + 1];
+        reg[W - 1] = x[(b * L + t) * D + d];
+        double acc = conv_b ? conv_b[d] : 0.0;
+        for (int64_t k = 0; k < W; ++k) acc += conv_w[d * W + k] * reg[k];
+        u[(b * L + t) * D + d] = acc;
+      }
+      if (conv_out)
+        for (int64_t k = 0; k < W; ++k) conv_out[(b * D + d) * W + k] = reg[k];
+      free(reg);
+    }
+  }
+}
+
+/*
  * oracle_step: one decode token per (b, d).
  *   x, delta, z, y : [Bsz, D]   Bm, Cm : [Bsz, N]   A : [D, N]   h : [Bsz, D, N] (in/out)
  *   conv_state     : [Bsz, D, W] (in/out; oldest input first, newest last) or NULL

@@ -306,6 +306,47 @@ def check_step_conv(step, scan, seed=21, L=11, W=4):
     return max(rel_err(np.stack(ys, axis=1), y_ref), rel_err(h, h_ref), e_reg)
 
 
+def check_conv_prefill(conv1d, scan_conv, step, seed=22, L=13, W=4):
+    """The prefill's convolution is the decode state's convolution run over the sequence:
+    (i) with zero history it is numpy.convolve of the raw inputs with the weights reversed;
+    (ii) with a register of earlier inputs it equals the tail of the zero-history convolution of
+        those inputs followed by the sequence (the register carries the history exactly);
+    (iii) conv then scan equals L decode steps (the step oracle, pinned on its own) started from
+        the same register and state, for y, the final state and the final register;
+    (iv) with L < W the final register mixes the old register and the new inputs."""
+    c = tiny_scan_case(seed, L=L)
+    Bsz, _, D = c["x"].shape
+    g = RNG(seed + 1)
+    w = g.standard_normal((D, W))
+    cb = g.standard_normal(D)
+    hist = g.standard_normal((Bsz, D, W))
+    e = 0.0
+    u0, _ = conv1d(c["x"], w, conv_b=cb)
+    ref = np.zeros_like(c["x"])
+    for b in range(Bsz):
+        for d in range(D):
+            ref[b, :, d] = np.convolve(c["x"][b, :, d], w[d, ::-1])[:L] + cb[d]
+    e = max(e, rel_err(u0, ref))
+    u1, r1 = conv1d(c["x"], w, conv_b=cb, conv_state=hist)
+    xx = np.concatenate([np.moveaxis(hist, 2, 1), c["x"]], axis=1)
+    u2, r2 = conv1d(xx, w, conv_b=cb)
+    e = max(e, rel_err(u1, u2[:, W:]), rel_err(r1, r2))
+    y, hl, reg = scan_conv(conv_w=w, conv_b=cb, conv_state=hist, **c)
+    h, rg = c["h0"].copy(), hist.copy()
+    ys = []
+    for t in range(L):
+        yt, h, rg = step(x=c["x"][:, t], delta=c["delta"][:, t], A=c["A"], Bm=c["Bm"][:, t],
+                         Cm=c["Cm"][:, t], h=h, delta_bias=c["delta_bias"],
+                         delta_softplus=c["delta_softplus"], Dskip=c["Dskip"], z=c["z"][:, t],
+                         conv_state=rg, conv_w=w, conv_b=cb)
+        ys.append(yt)
+    e = max(e, rel_err(y, np.stack(ys, axis=1)), rel_err(hl, h), rel_err(reg, rg))
+    _, r3 = conv1d(c["x"][:, :2], w, conv_state=hist)
+    want = np.concatenate([hist[:, :, 2:], np.moveaxis(c["x"][:, :2], 1, 2)], axis=2)
+    e = max(e, rel_err(r3, want))
+    return e
+
+
 # ----------------------------------------------------------------------------- SSD
 def tiny_ssd_case(seed, Bsz=2, L=20, H=2, P=3, N=4, gate=True, dskip=True, softplus=True):
     g = RNG(seed)

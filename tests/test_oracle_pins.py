@@ -28,6 +28,10 @@ def test_scan_bwd_finite_differences():
     assert pins.check_bwd_finite_differences(oracle.scan_bwd, oracle.scan) <= pins.BWD_FD_TOL
 
 
+def test_conv_prefill():
+    assert pins.check_conv_prefill(oracle.conv1d, oracle.scan_conv, oracle.step) <= 1e-12
+
+
 def test_step_equals_scan():
     assert pins.check_step_equals_scan(oracle.step, oracle.scan) <= 1e-12
 
@@ -92,6 +96,14 @@ SCAN_MUTANTS = {
     "zoh_limit_zero": [("return a == 0.0 ? dt : expm1(dt * a) / a;", "return a == 0.0 ? 0.0 : expm1(dt * a) / a;")],
     "h_last_reversed": [("h_last[(b * D + d) * N + n] = h[n];", "h_last[(b * D + d) * N + (N - 1 - n)] = h[n];")],
     "x_from_next_channel": [("const double xt = x[io];", "const double xt = x[(b * L + t) * D + (d + 1) % D];")],
+}
+
+CONV_MUTANTS = {
+    "conv_shift_reversed": [("for (int64_t k = 0; k + 1 < W; ++k) reg[k] = reg[k + 1];\n        reg[W - 1] = x[(b * L + t) * D + d];",
+                             "for (int64_t k = W - 1; k > 0; --k) reg[k] = reg[k - 1];\n        reg[0] = x[(b * L + t) * D + d];")],
+    "conv_weights_reversed": [("acc += conv_w[d * W + k] * reg[k];", "acc += conv_w[d * W + (W - 1 - k)] * reg[k];")],
+    "conv_bias_dropped": [("double acc = conv_b ? conv_b[d] : 0.0;", "double acc = 0.0;")],
+    "conv_history_ignored": [("reg[k] = conv_in ? conv_in[(b * D + d) * W + k] : 0.0;", "reg[k] = 0.0;")],
 }
 
 BWD_MUTANTS = {
@@ -184,3 +196,10 @@ def test_bwd_mutant_caught(tmp_path, name):
         with np.errstate(all="ignore"):
             err = pins.check_bwd_finite_differences(v.scan_bwd, oracle.scan)
     assert not (err <= pins.BWD_FD_TOL), "planted mistake %s passed the gradient pin" % name
+
+
+@pytest.mark.parametrize("name", sorted(CONV_MUTANTS))
+def test_conv_mutant_caught(tmp_path, name):
+    v = _mutant(tmp_path, name, CONV_MUTANTS[name])
+    err = pins.check_conv_prefill(v.conv1d, v.scan_conv, oracle.step)
+    assert err > 1e-12, name

@@ -120,6 +120,38 @@ ssm_status ssm_scan_fwd_segmented(int64_t B, int64_t L, int64_t D, int64_t N, ss
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ssm_scan_fwd_conv -- prefill: the depthwise causal convolution that the decode state keeps
+ * (page "Mamba and state space models", section "fixed-size state": a short convolution over the
+ * last few inputs), fused in front of ssm_scan_fwd. The scan input of channel d at token t is
+ * u = sum_k conv_w[d, k] * r_t[k] + conv_b[d], where r_t holds the conv_width raw inputs up to and
+ * including x_t, oldest first; u replaces x in the recurrence and in the D term, exactly as in
+ * ssm_state_update, so a prefill followed by decode steps is one consistent sequence.
+ *
+ *   forward arguments : as ssm_scan_fwd (x holds the raw, unconvolved inputs)
+ *   conv_width        : 1 .. 4 (else SSM_ERR_UNSUPPORTED)
+ *   conv_w            : [D, conv_width] float32, conv_w[d, conv_width-1] on the newest input
+ *   conv_b            : [D] float32 or NULL
+ *   conv_state        : [B, D, conv_width] io_dtype, 16-byte aligned, or NULL. On entry: the raw
+ *                       inputs before x (oldest first; NULL = zeros). On return: the register
+ *                       after the last token (the last conv_width raw inputs), ready for
+ *                       ssm_state_update.
+ *   segment_len       : 0 = automatic plan; else the segment length along L, rounded up to a
+ *                       multiple of 16 (workspace from ssm_scan_fwd_conv_workspace_bytes()).
+ *
+ *   Requirements: those of ssm_scan_fwd; conv_state overlaps no other tensor.
+ */
+size_t ssm_scan_fwd_conv_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
+                                         int64_t segment_len);
+
+ssm_status ssm_scan_fwd_conv(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io_dtype,
+                             const void* x, const void* delta, const float* delta_bias,
+                             int delta_softplus, const float* A, const void* Bm, const void* Cm,
+                             const float* Dskip, const void* z, const float* h0, int64_t conv_width,
+                             const float* conv_w, const float* conv_b, void* conv_state, void* y,
+                             float* h_last, int64_t segment_len, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * ssm_scan_bwd -- gradients of ssm_scan_fwd (training): the derivative of the forward map for
  * a loss L, given dy = dL/dy and optionally dh_last = dL/dh_last. The forward is the
  * recurrence of the page "Beyond attention: exploring Mamba and state space models"

@@ -80,13 +80,19 @@ int64_t num_segments(int64_t L, int64_t seg_len) { return seg_len >= L ? 1 : (L 
 ssm_status scan_common(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io, const void* x,
                        const void* delta, const float* delta_bias, int delta_softplus, const float* A,
                        const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
-                       void* y, float* h_last, int64_t seg_len, void* ws, size_t ws_bytes, void* stream) {
+                       void* y, float* h_last, int64_t seg_len, void* ws, size_t ws_bytes, void* stream,
+                       int64_t conv_W = 0, const float* conv_w = nullptr, const float* conv_b = nullptr,
+                       void* conv_state = nullptr) {
   if (B < 0 || L < 0) return fail(SSM_ERR_INVALID_ARGUMENT, "B=%lld and L=%lld must be >= 0", (long long)B, (long long)L);
   if (D < 1 || (D % 4) != 0) return fail(SSM_ERR_INVALID_ARGUMENT, "D=%lld must be >= 1 and a multiple of 4", (long long)D);
   if (!valid_dtype(io)) return fail(SSM_ERR_INVALID_ARGUMENT, "unknown io_dtype %d", (int)io);
   if (!supported_scan_n(N)) return fail(SSM_ERR_UNSUPPORTED, "N=%lld: supported state sizes are 1, 2, 4, 8, 16", (long long)N);
   if (D > kMaxScanD) return fail(SSM_ERR_UNSUPPORTED, "D=%lld: at most %lld channels", (long long)D, (long long)kMaxScanD);
   if (seg_len < 1) return fail(SSM_ERR_INVALID_ARGUMENT, "segment_len=%lld must be >= 1", (long long)seg_len);
+  if (conv_w && (conv_W < 1 || conv_W > 4))
+    return fail(SSM_ERR_UNSUPPORTED, "conv_width=%lld: the fused prefill convolution supports 1..4", (long long)conv_W);
+  if (conv_w && conv_state && !aligned16(conv_state))
+    return fail(SSM_ERR_INVALID_ARGUMENT, "conv_state must be 16-byte aligned");
   if (B == 0) return ok();
   if (!A) return fail(SSM_ERR_INVALID_ARGUMENT, "A is NULL");
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -110,6 +116,17 @@ ssm_status scan_common(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io,
   for (int k = 0; k < 9; ++k)
     if (overlaps(y, tok, ins[k], insz[k])) return fail(SSM_ERR_INVALID_ARGUMENT, "y overlaps an input");
   if (h_last && overlaps(h_last, stb, y, tok)) return fail(SSM_ERR_INVALID_ARGUMENT, "h_last overlaps y");
+  if (conv_w) {
+    const size_t reg = (size_t)(B * D * conv_W) * es;
+    const void* cins[] = {x, delta, z, Bm, Cm, A, delta_bias, Dskip, h0, h_last, y, conv_w, conv_b};
+    const size_t cinsz[] = {tok, tok, tok, bc, bc, (size_t)(D * N) * 4, (size_t)D * 4, (size_t)D * 4, stb, stb,
+                            tok, (size_t)(D * conv_W) * 4, (size_t)D * 4};
+    for (int k = 0; k < 13; ++k)
+      if (overlaps(conv_state, reg, cins[k], cinsz[k]))
+        return fail(SSM_ERR_INVALID_ARGUMENT, "conv_state overlaps another tensor");
+    if (overlaps(y, tok, conv_w, cinsz[11]) || overlaps(y, tok, conv_b, cinsz[12]))
+      return fail(SSM_ERR_INVALID_ARGUMENT, "y overlaps an input");
+  }
 
   const int64_t nseg = num_segments(L, seg_len);
   const size_t need = ssm::scan_workspace_bytes(B, D, N, nseg);
@@ -129,6 +146,10 @@ ssm_status scan_common(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io,
   if (nseg > 1) {
     p.ws_h = static_cast<float*>(ws);
     p.ws_sum = p.ws_h + B * nseg * D * N;
+  }
+  if (conv_w) {
+    p.conv_w = conv_w; p.conv_b = conv_b; p.conv_W = (int)conv_W;
+    p.conv_in = conv_state; p.conv_out = conv_state;
   }
   return from_hip(ssm::launch_scan(p, st), "ssm_scan_fwd launch");
 }
@@ -246,6 +267,28 @@ ssm_status ssm_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io
   const int64_t seg = (B > 0 && L > 0 && D > 0) ? auto_segment_len(B, L, D, N) : 1;
   return scan_common(B, L, D, N, io, x, delta, delta_bias, delta_softplus, A, Bm, Cm, Dskip, z, h0, y,
                      h_last, seg, ws, ws_bytes, stream);
+}
+
+size_t ssm_scan_fwd_conv_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int64_t segment_len) {
+  if (B <= 0 || L <= 0 || D <= 0 || N <= 0 || segment_len < 0) return 0;
+  int64_t seg = auto_segment_len(B, L, D, N);
+  if (segment_len > 0) seg = segment_len >= L ? L : ((segment_len + kTile - 1) / kTile) * kTile;
+  return ssm::scan_workspace_bytes(B, D, N, num_segments(L, seg));
+}
+
+ssm_status ssm_scan_fwd_conv(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io, const void* x,
+                             const void* delta, const float* delta_bias, int delta_softplus, const float* A,
+                             const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                             const float* h0, int64_t conv_width, const float* conv_w, const float* conv_b,
+                             void* conv_state, void* y, float* h_last, int64_t segment_len, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (!conv_w) return fail(SSM_ERR_INVALID_ARGUMENT, "conv_w is NULL");
+  if (segment_len < 0) return fail(SSM_ERR_INVALID_ARGUMENT, "segment_len=%lld must be >= 0", (long long)segment_len);
+  // segments must start on 16-token tiles (the convolution reads the three rows before a tile)
+  int64_t seg = (B > 0 && L > 0 && D > 0) ? auto_segment_len(B, L, D, N) : 1;
+  if (segment_len > 0) seg = segment_len >= L ? L : ((segment_len + kTile - 1) / kTile) * kTile;
+  return scan_common(B, L, D, N, io, x, delta, delta_bias, delta_softplus, A, Bm, Cm, Dskip, z, h0, y,
+                     h_last, seg, ws, ws_bytes, stream, conv_width, conv_w, conv_b, conv_state);
 }
 
 ssm_status ssm_scan_fwd_segmented(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io, const void* x,

@@ -25,6 +25,12 @@ struct ScanParams {
   int64_t nseg;            // number of segments (1: single pass)
   float* ws_h;             // [B, nseg, D, N]   (nseg > 1)
   float* ws_sum;           // [B, nseg, D]      (nseg > 1)
+  // causal convolution in front of the scan (prefill); conv_w == nullptr: none
+  const float* conv_w;     // [D, conv_W], conv_w[d, W-1] on the newest input
+  const float* conv_b;     // nullable [D]
+  const void* conv_in;     // nullable [B, D, conv_W] io: raw inputs before the sequence
+  void* conv_out;          // nullable [B, D, conv_W] io: the register after the sequence
+  int conv_W;              // 1 .. 4
 };
 
 // Workspace bytes for a plan with nseg segments (0 when nseg == 1).

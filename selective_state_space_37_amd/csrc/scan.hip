@@ -58,7 +58,9 @@ struct BCChunks {
 };
 
 // OCC = waves per SIMD the launch plan needs resident (five at N = 16: <= 102 VGPRs per lane).
-template <typename io_t, int CH, int NS, int KS, int T, int N, bool FULL, int OCC>
+// CONV: the SSM input is the causal depthwise convolution (width <= 4) of x, formed by the loader
+// (prefill in front of the decode step's convolution register).
+template <typename io_t, int CH, int NS, int KS, int T, int N, bool FULL, int OCC, bool CONV = false>
 __global__ __launch_bounds__(CH * KS)
 void scan_kernel(ScanParams p) {
   using Cfg = ScanCfg<CH, NS, KS, T, N>;
@@ -77,6 +79,11 @@ void scan_kernel(ScanParams p) {
   constexpr bool kPadY = FULL && CH < 64 && kLdsUnpadded + KS * 32 * 4 <= 163840 / OCC;
   constexpr int kYStride = FULL ? T * CH + (kPadY ? 32 : 0) : 1;
   __shared__ float s_y[FULL ? KS : 1][kYStride];
+  // convolution: per channel the weights by lag (lag 0 = the newest input; zero past the width),
+  // the bias, and the last three raw inputs before the sequence (newest first)
+  __shared__ __attribute__((aligned(16))) float4 s_cw[CONV ? CH : 1];
+  __shared__ __attribute__((aligned(16))) float s_cb[CONV ? CH : 4];
+  __shared__ float s_cin[CONV ? 3 : 1][CONV ? CH : 1];
 
   const int tid = threadIdx.x;
   const int64_t D = p.D, L = p.L;
@@ -122,6 +129,31 @@ void scan_kernel(ScanParams p) {
   raw4 rx[Cfg::kGroupsPerThr], rd[Cfg::kGroupsPerThr], rz[Cfg::kGroupsPerThr];
 #pragma unroll
   for (int k = 0; k < Cfg::kGroupsPerThr; ++k) rx[k] = rd[k] = rz[k] = Io::zero4();
+  // convolution: the three x rows before each loaded row (lags 1..3)
+  raw4 rxh[CONV ? Cfg::kGroupsPerThr : 1][3];
+#pragma unroll
+  for (int k = 0; k < (CONV ? Cfg::kGroupsPerThr : 1); ++k) rxh[k][0] = rxh[k][1] = rxh[k][2] = Io::zero4();
+  if constexpr (CONV) {
+    if (tid < CH) {
+      const int64_t cc = c0 + tid;
+      const bool ok = cc < D;
+      const int W = p.conv_W;
+      float wl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wl[j] = (ok && j < W) ? p.conv_w[cc * W + (W - 1 - j)] : 0.f;
+      s_cw[tid] = make_float4(wl[0], wl[1], wl[2], wl[3]);
+      s_cb[tid] = (ok && p.conv_b) ? p.conv_b[cc] : 0.f;
+#pragma unroll
+      for (int m = 0; m < 3; ++m) {
+        // raw input m + 1 steps before the sequence: register entry W - 1 - m (oldest first)
+        float v = 0.f;
+        if (ok && p.conv_in && m < W)
+          v = Io::load(static_cast<const io_t*>(p.conv_in), (b * D + cc) * W + (W - 1 - m));
+        s_cin[m][tid] = v;
+      }
+    }
+    __syncthreads();
+  }
   // B and C of a tile are T * N consecutive elements. When a row of N elements is whole 16-byte
   // chunks they move as chunks (threads below kChunks, a chunk never straddles a row, so a row
   // past the segment end reads as whole zero chunks); otherwise element by element. Either way the
@@ -173,6 +205,33 @@ void scan_kernel(ScanParams p) {
         if (has_z) buf_load(zr, ld_boff[k], rz[k]);
       }
     }
+    if constexpr (CONV) {
+      // rows r-1 .. r-3 of x for the convolution. Segments start at multiples of 16 tokens, so a
+      // tile either starts the sequence or has three rows of x before it.
+      constexpr uint32_t kRow = sizeof(io_t);
+      const uint32_t row_b = (uint32_t)D * kRow;
+      if (t_begin + (int64_t)tile * T > 0) {
+        const char* blk = reinterpret_cast<const char*>(xg) +
+                          ((seg_row0 + (int64_t)tile * T - 3) * D + c0) * (int64_t)kRow;
+        const Rsrc hr = make_rsrc(blk, (int)(((rows + 3) * D - c0) * (int64_t)kRow));
+#pragma unroll
+        for (int k = 0; k < Cfg::kGroupsPerThr; ++k)
+          if (tid + k * Cfg::kThreads < Cfg::kGroups)
+#pragma unroll
+            for (int j = 1; j <= 3; ++j) buf_load(hr, ld_boff[k] + (uint32_t)(3 - j) * row_b, rxh[k][j - 1]);
+      } else {
+        // the sequence's first tile: earlier rows of the tile itself; rows before the sequence
+        // come from the register (in LDS) at commit
+#pragma unroll
+        for (int k = 0; k < Cfg::kGroupsPerThr; ++k) {
+          const int g = tid + k * Cfg::kThreads;
+          if (g < Cfg::kGroups)
+#pragma unroll
+            for (int j = 1; j <= 3; ++j)
+              if (g / (CH / 4) >= j) buf_load(xr, ld_boff[k] - (uint32_t)j * row_b, rxh[k][j - 1]);
+        }
+      }
+    }
     const Rsrc br = tile_rsrc(Bg, N, 0, tile, rows);
     const Rsrc cr = tile_rsrc(Cg, N, 0, tile, rows);
     if constexpr (kChunkBC) {
@@ -211,6 +270,30 @@ void scan_kernel(ScanParams p) {
           float u = dv[q] + bias4[q];   // bias4 is zero without a bias
           if (p.delta_softplus) u = softplus_f32(u);
           dv[q] = (!RAGGED || r < rows) ? u : 0.f;
+        }
+        if constexpr (CONV) {
+          // SSM input = bias + sum over lags j of w_j x_{t-j} (weights zero past the width and
+          // for channels past D); rows before the sequence come from the register
+          float xs[3][4];
+#pragma unroll
+          for (int j = 0; j < 3; ++j) Io::unpack4(rxh[k][j], xs[j]);
+          if (t_begin + (int64_t)tile * T == 0) {
+#pragma unroll
+            for (int j = 1; j <= 3; ++j)
+              if (r < j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) xs[j - 1][q] = s_cin[j - r - 1][4 * cg + q];
+          }
+          const float4 cb4 = *reinterpret_cast<const float4*>(&s_cb[4 * cg]);
+          const float cbv[4] = {cb4.x, cb4.y, cb4.z, cb4.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 w = s_cw[4 * cg + q];
+            float u = fmaf(w.x, xv[q], cbv[q]);
+            u = fmaf(w.y, xs[0][q], u);
+            u = fmaf(w.z, xs[1][q], u);
+            xv[q] = fmaf(w.w, xs[2][q], u);
+          }
         }
         float4* dst = reinterpret_cast<float4*>(&s_dx[buf][r][4 * cg]);
         dst[0] = make_float4(dv[0], xv[0], dv[1], xv[1]);
@@ -397,19 +480,47 @@ __global__ __launch_bounds__(256) void scan_carry_kernel(ScanParams p) {
   p.ws_h[((b * p.nseg + p.nseg - 1) * D + c) * N + n] = h;
 }
 
-template <typename io_t, int CH, int NS, int KS, int N, int OCC>
+// The convolution register after the prefill: the last W raw inputs, oldest first (earlier
+// register entries shifted in when L < W). One thread per (b, d); it runs after the scan, so the
+// register may be updated in place.
+template <typename io_t>
+__global__ __launch_bounds__(256) void conv_register_kernel(ScanParams p) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= p.B * p.D) return;
+  const int64_t b = i / p.D, d = i % p.D;
+  const int W = p.conv_W;
+  using Io = IoTraits<io_t>;
+  io_t* out = static_cast<io_t*>(p.conv_out) + i * W;
+  const io_t* in = static_cast<const io_t*>(p.conv_in);
+  for (int k = 0; k < W; ++k) {
+    const int64_t t = p.L - W + k;
+    if (t >= 0) {
+      out[k] = static_cast<const io_t*>(p.x)[(b * p.L + t) * p.D + d];
+    } else {
+      // entries move left by L places; in place this reads index k + L > k before it is written
+      const float v = in ? Io::load(in, i * W + k + p.L) : 0.f;
+      Io::store(out, k, v);
+    }
+  }
+}
+
+template <typename io_t, int CH, int NS, int KS, int N, int OCC, bool CONV>
 hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
   constexpr int T = 16;
   const dim3 block(CH * KS);
   const unsigned gx = (unsigned)((p.D + CH - 1) / CH);
   if (p.nseg > 1) {
     const dim3 grid_a(gx, (unsigned)p.B, (unsigned)(p.nseg - 1));
-    hipLaunchKernelGGL((scan_kernel<io_t, CH, NS, KS, T, N, false, OCC>), grid_a, block, 0, stream, p);
+    hipLaunchKernelGGL((scan_kernel<io_t, CH, NS, KS, T, N, false, OCC, CONV>), grid_a, block, 0, stream, p);
     const int64_t chains = p.B * p.D * p.N;
     hipLaunchKernelGGL(scan_carry_kernel, dim3((unsigned)((chains + 255) / 256)), dim3(256), 0, stream, p);
   }
   const dim3 grid(gx, (unsigned)p.B, (unsigned)p.nseg);
-  hipLaunchKernelGGL((scan_kernel<io_t, CH, NS, KS, T, N, true, OCC>), grid, block, 0, stream, p);
+  hipLaunchKernelGGL((scan_kernel<io_t, CH, NS, KS, T, N, true, OCC, CONV>), grid, block, 0, stream, p);
+  if (CONV && p.conv_out) {
+    const int64_t n = p.B * p.D;
+    hipLaunchKernelGGL(conv_register_kernel<io_t>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
@@ -439,14 +550,14 @@ hipError_t launch_carries_io(const ScanParams& p, hipStream_t stream) {
   }
 }
 
-template <typename io_t>
+template <typename io_t, bool CONV>
 hipError_t launch_io(const ScanParams& p, hipStream_t stream) {
   switch (p.N) {
-    case 1: return launch_typed<io_t, 64, 1, 1, 1, 1>(p, stream);
-    case 2: return launch_typed<io_t, 64, 2, 1, 2, 1>(p, stream);
-    case 4: return launch_typed<io_t, 64, 2, 2, 4, 1>(p, stream);
-    case 8: return launch_typed<io_t, 32, 2, 4, 8, 1>(p, stream);
-    case 16: return launch_typed<io_t, 32, 2, 8, 16, 5>(p, stream);
+    case 1: return launch_typed<io_t, 64, 1, 1, 1, 1, CONV>(p, stream);
+    case 2: return launch_typed<io_t, 64, 2, 1, 2, 1, CONV>(p, stream);
+    case 4: return launch_typed<io_t, 64, 2, 2, 4, 1, CONV>(p, stream);
+    case 8: return launch_typed<io_t, 32, 2, 4, 8, 1, CONV>(p, stream);
+    case 16: return launch_typed<io_t, 32, 2, 8, 16, 5, CONV>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -459,7 +570,9 @@ size_t scan_workspace_bytes(int64_t B, int64_t D, int64_t N, int64_t nseg) {
 }
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream) {
-  return p.io_bf16 ? launch_io<bf16_t>(p, stream) : launch_io<float>(p, stream);
+  if (p.conv_w)
+    return p.io_bf16 ? launch_io<bf16_t, true>(p, stream) : launch_io<float, true>(p, stream);
+  return p.io_bf16 ? launch_io<bf16_t, false>(p, stream) : launch_io<float, false>(p, stream);
 }
 
 hipError_t launch_scan_carries(const ScanParams& p, hipStream_t stream) {

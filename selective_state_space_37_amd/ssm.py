@@ -21,6 +21,7 @@ STATUS = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARGUMENT", 2: "SSM_ERR_UNSUPPORTED",
 EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_last_error_detail",
            "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd",
            "ssm_scan_fwd_segmented_workspace_bytes", "ssm_scan_fwd_segmented",
+           "ssm_scan_fwd_conv_workspace_bytes", "ssm_scan_fwd_conv",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd",
            "ssm_scan_bwd_segmented_workspace_bytes", "ssm_scan_bwd_segmented",
            "ssm_state_update", "ssd_chunk_fwd_workspace_bytes", "ssd_chunk_fwd")
@@ -57,6 +58,11 @@ def load(path: str = LIB_PATH):
     lib.ssm_scan_fwd.restype = ci
     lib.ssm_scan_fwd_segmented.argtypes = scan_args + [i64, vp, sz, vp]
     lib.ssm_scan_fwd_segmented.restype = ci
+    lib.ssm_scan_fwd_conv_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
+    lib.ssm_scan_fwd_conv_workspace_bytes.restype = sz
+    lib.ssm_scan_fwd_conv.argtypes = [i64, i64, i64, i64, ci, vp, vp, vp, ci, vp, vp, vp, vp, vp, vp,
+                                      i64, vp, vp, vp, vp, vp, i64, vp, sz, vp]
+    lib.ssm_scan_fwd_conv.restype = ci
     lib.ssm_scan_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ci]
     lib.ssm_scan_bwd_workspace_bytes.restype = sz
     lib.ssm_scan_bwd_segmented_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
@@ -152,6 +158,45 @@ def scan_fwd(x, delta, A, Bm, Cm, *, delta_bias=None, delta_softplus=False, Dski
         st = lib.ssm_scan_fwd(*args, _p(ws), nb, _stream(x))
     else:
         st = lib.ssm_scan_fwd_segmented(*args, int(segment_len), _p(ws), nb, _stream(x))
+    _check(st)
+    return y, h_last
+
+
+def scan_fwd_conv(x, delta, A, Bm, Cm, conv_w, *, conv_b=None, conv_state=None, delta_bias=None,
+                  delta_softplus=False, Dskip=None, z=None, h0=None, return_state=True,
+                  segment_len: int = 0, y=None, h_last=None,
+                  ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Prefill: causal depthwise convolution (conv_w [D, W], W <= 4) of the raw x, then the scan on
+    its output. conv_state [B, D, W] (storage type of x) is read as the inputs before x and
+    overwritten with the register after the last token. -> (y, h_last)."""
+    lib = load()
+    Bsz, L, D = x.shape
+    N = A.shape[1]
+    W = conv_w.shape[1]
+    io = x.dtype
+    _dev(x, "x")
+    _dev(delta, "delta", io, (Bsz, L, D))
+    _dev(z, "z", io, (Bsz, L, D))
+    _dev(Bm, "Bm", io, (Bsz, L, N))
+    _dev(Cm, "Cm", io, (Bsz, L, N))
+    _dev(A, "A", torch.float32, (D, N))
+    _dev(conv_w, "conv_w", torch.float32, (D, W))
+    _dev(conv_b, "conv_b", torch.float32, (D,))
+    _dev(conv_state, "conv_state", io, (Bsz, D, W))
+    _dev(delta_bias, "delta_bias", torch.float32, (D,))
+    _dev(Dskip, "Dskip", torch.float32, (D,))
+    _dev(h0, "h0", torch.float32, (Bsz, D, N))
+    if y is None:
+        y = torch.empty_like(x)
+    if h_last is None and return_state:
+        h_last = torch.empty((Bsz, D, N), dtype=torch.float32, device=x.device)
+    nb = lib.ssm_scan_fwd_conv_workspace_bytes(Bsz, L, D, N, int(segment_len))
+    if ws is None or ws.numel() < nb:
+        ws = workspace(nb, x.device)
+    st = lib.ssm_scan_fwd_conv(Bsz, L, D, N, _io_code(x), _p(x), _p(delta), _p(delta_bias),
+                               int(bool(delta_softplus)), _p(A), _p(Bm), _p(Cm), _p(Dskip), _p(z),
+                               _p(h0), W, _p(conv_w), _p(conv_b), _p(conv_state), _p(y), _p(h_last),
+                               int(segment_len), _p(ws), nb, _stream(x))
     _check(st)
     return y, h_last
 

@@ -66,6 +66,29 @@ def scan_parity(inp, gpu_out, channels=None) -> float:
     return e
 
 
+# ----------------------------------------------------------------------------- prefill with conv
+def scan_conv_on_gpu(inp: inputs.ScanInputs, conv_w, conv_b=None, conv_state=None, segment_len=0):
+    """ssm_scan_fwd_conv; conv_state (storage type) is updated in place. Returns (y, h_last,
+    register) on the host; the register as raw storage values (bf16 bits widened exactly)."""
+    reg = dev(conv_state) if conv_state is not None else None
+    y, hl = ssm.scan_fwd_conv(dev(inp.x), dev(inp.delta), dev(inp.A), dev(inp.Bm), dev(inp.Cm),
+                              dev(conv_w), conv_b=dev(conv_b), conv_state=reg,
+                              delta_bias=dev(inp.delta_bias), delta_softplus=inp.delta_softplus,
+                              Dskip=dev(inp.Dskip), z=dev(inp.z), h0=dev(inp.h0),
+                              segment_len=segment_len)
+    torch.cuda.synchronize()
+    return host(y), host(hl), host(reg)
+
+
+def scan_conv_oracle(inp: inputs.ScanInputs, conv_w, conv_b=None, conv_state=None, channels=None):
+    w = lambda a: inputs.widen(a, inp.dtype)
+    sel = (lambda a, ax: a if a is None or channels is None else np.take(a, channels, axis=ax))
+    return oracle.scan_conv(sel(w(inp.x), 2), sel(w(inp.delta), 2), sel(inp.A, 0), w(inp.Bm), w(inp.Cm),
+                            sel(conv_w, 0), conv_b=sel(conv_b, 0), conv_state=sel(w(conv_state), 1),
+                            delta_bias=sel(inp.delta_bias, 0), delta_softplus=inp.delta_softplus,
+                            Dskip=sel(inp.Dskip, 0), z=sel(w(inp.z), 2), h0=sel(inp.h0, 1))
+
+
 # ----------------------------------------------------------------------------- scan backward
 BWD_KEYS = ("dx", "ddelta", "dz", "dA", "dBm", "dCm", "dDskip", "ddelta_bias", "dh0")
 

@@ -52,8 +52,14 @@ __device__ __forceinline__ float sigmoid_fast(float v) {
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRawRsrcWord3 = 0x00020000;
 
+// base and bytes are uniform over the wave; readfirstlane says so to the compiler (otherwise a
+// value it cannot prove uniform makes it wrap each buffer access in a loop over distinct values).
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRawRsrcWord3);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* u = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, __builtin_amdgcn_readfirstlane(bytes), kRawRsrcWord3);
 }
 __device__ __forceinline__ void buf_load(Rsrc r, uint32_t off, uint2& out) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);

@@ -57,7 +57,8 @@ struct BCChunks {
   static_assert(kChunks <= kThreads, "one chunk per loading thread");
 };
 
-// OCC = waves per SIMD the launch plan needs resident (five at N = 16: <= 102 VGPRs per lane).
+// OCC = waves per SIMD the launch plan needs resident (five at N = 16: <= 96 VGPRs per lane, as
+// registers are allocated in blocks of 8 out of 512).
 // CONV: the SSM input is the causal depthwise convolution (width <= 4) of x, formed by the loader
 // (prefill in front of the decode step's convolution register).
 template <typename io_t, int CH, int NS, int KS, int T, int N, bool FULL, int OCC, bool CONV = false>
@@ -75,15 +76,18 @@ void scan_kernel(ScanParams p) {
   // banks so their writes do not collide
   // (only when the padding still lets OCC workgroups share a CU's 160 KB of LDS)
   constexpr int kLdsUnpadded = 2 * T * CH * 8 + (FULL ? 2 * T * (CH / 4) * (int)sizeof(raw4) : 16) +
-                               2 * T * N * 8 + (FULL ? KS * T * CH * 4 : 4);
+                               2 * T * N * 8 + (FULL ? KS * T * CH * 4 : 4) +
+                               (CONV ? CH * 16 + CH * 4 + 3 * CH * 4 + CH * 4 : 0);
   constexpr bool kPadY = FULL && CH < 64 && kLdsUnpadded + KS * 32 * 4 <= 163840 / OCC;
   constexpr int kYStride = FULL ? T * CH + (kPadY ? 32 : 0) : 1;
   __shared__ float s_y[FULL ? KS : 1][kYStride];
-  // convolution: per channel the weights by lag (lag 0 = the newest input; zero past the width),
-  // the bias, and the last three raw inputs before the sequence (newest first)
+  // convolution: per channel the weights by lag (lag 0 = the newest input; zero past the width
+  // or past D) and the bias, and the raw inputs before the sequence (the incoming register),
+  // newest first
   __shared__ __attribute__((aligned(16))) float4 s_cw[CONV ? CH : 1];
   __shared__ __attribute__((aligned(16))) float s_cb[CONV ? CH : 4];
   __shared__ float s_cin[CONV ? 3 : 1][CONV ? CH : 1];
+  __shared__ __attribute__((aligned(16))) float s_db[CONV ? CH : 4];
 
   const int tid = threadIdx.x;
   const int64_t D = p.D, L = p.L;
@@ -100,9 +104,11 @@ void scan_kernel(ScanParams p) {
       const int64_t r = lin & 15;
       logical = (lin & ~(int64_t)15) + 2 * (r & 7) + (r >> 3);
     }
-    tile = logical % gx;
-    b = (logical / gx) % gridDim.y;
-    seg = logical / gxy;
+    // uniform over the workgroup: keep them in scalar registers (the 64-bit divisions above
+    // partly run on the vector unit)
+    tile = __builtin_amdgcn_readfirstlane((uint32_t)(logical % gx));
+    b = __builtin_amdgcn_readfirstlane((uint32_t)((logical / gx) % gridDim.y));
+    seg = __builtin_amdgcn_readfirstlane((uint32_t)(logical / gxy));
   }
   const int64_t c0 = tile * CH;
   const int64_t t_begin = seg * p.seg_len;
@@ -120,8 +126,9 @@ void scan_kernel(ScanParams p) {
   const int cg = tid % (CH / 4);
   const int64_t cgl = c0 + 4 * cg;
   const bool cg_ok = cgl < D;  // D % 4 == 0: a group is wholly in or out
+  // (the convolution variant keeps the step-size bias in LDS instead: registers for its halo rows)
   float bias4[4] = {0.f, 0.f, 0.f, 0.f};
-  if (p.delta_bias && cg_ok)
+  if (!CONV && p.delta_bias && cg_ok)
 #pragma unroll
     for (int k = 0; k < 4; ++k) bias4[k] = p.delta_bias[cgl + k];
 
@@ -129,27 +136,30 @@ void scan_kernel(ScanParams p) {
   raw4 rx[Cfg::kGroupsPerThr], rd[Cfg::kGroupsPerThr], rz[Cfg::kGroupsPerThr];
 #pragma unroll
   for (int k = 0; k < Cfg::kGroupsPerThr; ++k) rx[k] = rd[k] = rz[k] = Io::zero4();
-  // convolution: the three x rows before each loaded row (lags 1..3)
+  // convolution: the x rows r-1 .. r-3 of each loaded row (lags 1..3) in registers; weights, bias
+  // and the register entries before the sequence in LDS
   raw4 rxh[CONV ? Cfg::kGroupsPerThr : 1][3];
 #pragma unroll
   for (int k = 0; k < (CONV ? Cfg::kGroupsPerThr : 1); ++k) rxh[k][0] = rxh[k][1] = rxh[k][2] = Io::zero4();
   if constexpr (CONV) {
+    const int W = p.conv_W;
     if (tid < CH) {
-      const int64_t cc = c0 + tid;
-      const bool ok = cc < D;
-      const int W = p.conv_W;
+      const bool ok = c0 + tid < D;
       float wl[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wl[j] = (ok && j < W) ? p.conv_w[cc * W + (W - 1 - j)] : 0.f;
+      for (int j = 0; j < 4; ++j) wl[j] = (ok && j < W) ? p.conv_w[(c0 + tid) * W + (W - 1 - j)] : 0.f;
       s_cw[tid] = make_float4(wl[0], wl[1], wl[2], wl[3]);
-      s_cb[tid] = (ok && p.conv_b) ? p.conv_b[cc] : 0.f;
+      s_cb[tid] = (ok && p.conv_b) ? p.conv_b[c0 + tid] : 0.f;
+      s_db[tid] = (ok && p.delta_bias) ? p.delta_bias[c0 + tid] : 0.f;
+      // read through a descriptor with a uniform base (no per-lane copy of a shared address)
+      constexpr int kEs = (int)sizeof(io_t);
+      const Rsrc hc = make_rsrc(static_cast<const char*>(p.conv_in) + (b * D + c0) * W * kEs,
+                                p.conv_in ? (int)((D - c0) * W * kEs) : 0);
 #pragma unroll
       for (int m = 0; m < 3; ++m) {
-        // raw input m + 1 steps before the sequence: register entry W - 1 - m (oldest first)
         float v = 0.f;
-        if (ok && p.conv_in && m < W)
-          v = Io::load(static_cast<const io_t*>(p.conv_in), (b * D + cc) * W + (W - 1 - m));
-        s_cin[m][tid] = v;
+        if (m < W) v = Io::from_bits(buf_load_bits(hc, (uint32_t)((tid * W + (W - 1 - m)) * kEs), (io_t*)nullptr));
+        s_cin[m][tid] = (c0 + tid < D) ? v : 0.f;
       }
     }
     __syncthreads();
@@ -208,29 +218,22 @@ void scan_kernel(ScanParams p) {
     if constexpr (CONV) {
       // rows r-1 .. r-3 of x for the convolution. Segments start at multiples of 16 tokens, so a
       // tile either starts the sequence or has three rows of x before it.
-      constexpr uint32_t kRow = sizeof(io_t);
-      const uint32_t row_b = (uint32_t)D * kRow;
-      if (t_begin + (int64_t)tile * T > 0) {
-        const char* blk = reinterpret_cast<const char*>(xg) +
-                          ((seg_row0 + (int64_t)tile * T - 3) * D + c0) * (int64_t)kRow;
-        const Rsrc hr = make_rsrc(blk, (int)(((rows + 3) * D - c0) * (int64_t)kRow));
+      // At the sequence's first tile the descriptor starts at the tile and the offsets of rows
+      // before it wrap past 2^31: out of range, they read zero (the register supplies them at
+      // commit).
+      constexpr uint32_t kEs = sizeof(io_t);
+      const uint32_t row_b = (uint32_t)D * kEs;
+      const bool first = t_begin + (int64_t)tile * T == 0;
+      const int64_t hrow = seg_row0 + (int64_t)tile * T - (first ? 0 : 3);
+      const Rsrc hr = make_rsrc(reinterpret_cast<const char*>(xg) + (hrow * D + c0) * (int64_t)kEs,
+                                (int)(((rows + (first ? 0 : 3)) * D - c0) * (int64_t)kEs));
+      const uint32_t hoff = first ? 3u * row_b : 0u;
 #pragma unroll
-        for (int k = 0; k < Cfg::kGroupsPerThr; ++k)
-          if (tid + k * Cfg::kThreads < Cfg::kGroups)
+      for (int k = 0; k < Cfg::kGroupsPerThr; ++k)
+        if (tid + k * Cfg::kThreads < Cfg::kGroups)
 #pragma unroll
-            for (int j = 1; j <= 3; ++j) buf_load(hr, ld_boff[k] + (uint32_t)(3 - j) * row_b, rxh[k][j - 1]);
-      } else {
-        // the sequence's first tile: earlier rows of the tile itself; rows before the sequence
-        // come from the register (in LDS) at commit
-#pragma unroll
-        for (int k = 0; k < Cfg::kGroupsPerThr; ++k) {
-          const int g = tid + k * Cfg::kThreads;
-          if (g < Cfg::kGroups)
-#pragma unroll
-            for (int j = 1; j <= 3; ++j)
-              if (g / (CH / 4) >= j) buf_load(xr, ld_boff[k] - (uint32_t)j * row_b, rxh[k][j - 1]);
-        }
-      }
+          for (int j = 1; j <= 3; ++j)
+            buf_load(hr, ld_boff[k] + (uint32_t)(3 - j) * row_b - hoff, rxh[k][j - 1]);
     }
     const Rsrc br = tile_rsrc(Bg, N, 0, tile, rows);
     const Rsrc cr = tile_rsrc(Cg, N, 0, tile, rows);
@@ -254,46 +257,56 @@ void scan_kernel(ScanParams p) {
   // Rows past the segment end (ragged last tile) load as x = 0, B = C = 0 and Delta = 0, and Delta
   // is committed as 0 after the bias and softplus as well: the identity step. RAGGED is a
   // compile-time switch so that full tiles carry no row tests at all.
-  auto commit_impl = [&](auto ragged_tag, int tile, int buf) __attribute__((always_inline)) {
+  // FIRST: the sequence's first tile (only ever the prologue's commit), whose rows before the
+  // sequence take the register for the convolution.
+  auto commit_impl = [&](auto ragged_tag, auto first_tag, int tile, int buf) __attribute__((always_inline)) {
     constexpr bool RAGGED = decltype(ragged_tag)::value;
+    constexpr bool FIRST = decltype(first_tag)::value;
     const int rows = tile_rows(tile);
 #pragma unroll
     for (int k = 0; k < Cfg::kGroupsPerThr; ++k) {
       const int g = tid + k * Cfg::kThreads;
       if (g < Cfg::kGroups) {
         const int r = g / (CH / 4);
-        float xv[4], dv[4];
+        float xv[4];
         Io::unpack4(rx[k], xv);
-        Io::unpack4(rd[k], dv);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float u = dv[q] + bias4[q];   // bias4 is zero without a bias
-          if (p.delta_softplus) u = softplus_f32(u);
-          dv[q] = (!RAGGED || r < rows) ? u : 0.f;
-        }
+        // (the convolution first: its halo registers are free before the step-size arithmetic)
         if constexpr (CONV) {
-          // SSM input = bias + sum over lags j of w_j x_{t-j} (weights zero past the width and
-          // for channels past D); rows before the sequence come from the register
+          // SSM input = bias + sum over lags j of w_j x_{t-j}; rows before the sequence come from
+          // the register
           float xs[3][4];
 #pragma unroll
           for (int j = 0; j < 3; ++j) Io::unpack4(rxh[k][j], xs[j]);
-          if (t_begin + (int64_t)tile * T == 0) {
+          if constexpr (FIRST) {
 #pragma unroll
             for (int j = 1; j <= 3; ++j)
               if (r < j)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) xs[j - 1][q] = s_cin[j - r - 1][4 * cg + q];
           }
-          const float4 cb4 = *reinterpret_cast<const float4*>(&s_cb[4 * cg]);
-          const float cbv[4] = {cb4.x, cb4.y, cb4.z, cb4.w};
+          const float4 b4 = *reinterpret_cast<const float4*>(&s_cb[4 * cg]);
+          const float bq[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float4 w = s_cw[4 * cg + q];
-            float u = fmaf(w.x, xv[q], cbv[q]);
+            float u = fmaf(w.x, xv[q], bq[q]);
             u = fmaf(w.y, xs[0][q], u);
             u = fmaf(w.z, xs[1][q], u);
             xv[q] = fmaf(w.w, xs[2][q], u);
           }
+        }
+        float dv[4];
+        Io::unpack4(rd[k], dv);
+        float db[4] = {bias4[0], bias4[1], bias4[2], bias4[3]};
+        if constexpr (CONV) {
+          const float4 v = *reinterpret_cast<const float4*>(&s_db[4 * cg]);
+          db[0] = v.x; db[1] = v.y; db[2] = v.z; db[3] = v.w;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float u = dv[q] + db[q];   // zero without a bias
+          if (p.delta_softplus) u = softplus_f32(u);
+          dv[q] = (!RAGGED || r < rows) ? u : 0.f;
         }
         float4* dst = reinterpret_cast<float4*>(&s_dx[buf][r][4 * cg]);
         dst[0] = make_float4(dv[0], xv[0], dv[1], xv[1]);
@@ -328,9 +341,18 @@ void scan_kernel(ScanParams p) {
     }
   };
   auto commit_tile = [&](int tile, int buf) __attribute__((always_inline)) {
-    if (tile < n_full) commit_impl(std::false_type{}, tile, buf);
-    else commit_impl(std::true_type{}, tile, buf);
+    if (tile < n_full) commit_impl(std::false_type{}, std::false_type{}, tile, buf);
+    else commit_impl(std::true_type{}, std::false_type{}, tile, buf);
     commit_bc(buf);
+  };
+  auto commit_first_tile = [&]() __attribute__((always_inline)) {
+    if (CONV && t_begin == 0) {
+      if (0 < n_full) commit_impl(std::false_type{}, std::true_type{}, 0, 0);
+      else commit_impl(std::true_type{}, std::true_type{}, 0, 0);
+      commit_bc(0);
+    } else {
+      commit_tile(0, 0);
+    }
   };
 
   // ---- per-lane recurrence constants: channel c, states n0 .. n0+NS-1
@@ -370,7 +392,7 @@ void scan_kernel(ScanParams p) {
 
   if (ntiles > 0) {
     issue_loads(0);
-    commit_tile(0, 0);
+    commit_first_tile();
   }
   __syncthreads();
 
@@ -382,7 +404,9 @@ void scan_kernel(ScanParams p) {
     //      phase 1 forms Abar and the input term of every token of the sub-tile (independent
     //      work, so several exps are in flight); phase 2 is the serial part, h = Abar h + u,
     //      and the readout.
-    constexpr int PH = T < 4 ? T : 4;
+    // (the convolution variant holds three more raw rows: two-token sub-tiles keep it at the
+    // same occupancy)
+    constexpr int PH = T < 4 ? T : (CONV ? 2 : 4);
     static_assert(T % PH == 0, "sub-tiles must cover the tile");
 #pragma unroll
     for (int t0 = 0; t0 < T; t0 += PH) {

@@ -82,9 +82,11 @@ __global__ __launch_bounds__(CH * KS) void scan_bwd_kernel(ScanBwdParams p) {
       const int64_t r = lin & 15;
       logical = (lin & ~(int64_t)15) + 2 * (r & 7) + (r >> 3);
     }
-    tile_c = logical % gx;
-    b = (logical / gx) % gridDim.y;
-    seg = logical / gxy;
+    // uniform over the workgroup: keep them in scalar registers (the 64-bit divisions above
+    // partly run on the vector unit)
+    tile_c = __builtin_amdgcn_readfirstlane((uint32_t)(logical % gx));
+    b = __builtin_amdgcn_readfirstlane((uint32_t)((logical / gx) % gridDim.y));
+    seg = __builtin_amdgcn_readfirstlane((uint32_t)(logical / gxy));
   }
   const int64_t c0 = tile_c * CH;
   const int64_t t_begin = seg * p.seg_len;

@@ -293,8 +293,8 @@ def main():
 
 
 def secondary(torch, np, inputs, ssm, dev):
-    """Long-sequence scan, scan backward, decode step and SSD layer: kernel-time throughput (HIP
-    events)."""
+    """Long-sequence scan, scan backward, prefill with the fused convolution, decode step and SSD
+    layer: kernel-time throughput (HIP events)."""
     res = {}
     g = torch.Generator(device="cuda").manual_seed(7)
     r = lambda *s: torch.randn(*s, generator=g, device="cuda", dtype=torch.float32)
@@ -343,6 +343,25 @@ def secondary(torch, np, inputs, ssm, dev):
         "valu_slot_frac": round(steps * 29 / (ms * 1e-3) / (PEAK_VALU_TOPS * 1e12), 4),
         "workspace_MB": round(nb / 1e6, 1)}
     del x, z, dy, delta, Bm, Cm, ws
+
+    # prefill with the fused width-4 causal convolution: batch 128, 2048 prompt tokens, d_inner 4096,
+    # N 16, bf16 (the generation workload's prompt), register returned for the decode steps
+    B, L, D, N, W = 128, 2048, 4096, 16, 4
+    x, z = r(B, L, D).to(bf), r(B, L, D).to(bf)
+    delta = torch.clamp(torch.nn.functional.softplus(r(B, L, D) - 4), 1e-3, 0.1).to(bf)
+    Bm, Cm = r(B, L, N).to(bf), r(B, L, N).to(bf)
+    A = dev(inputs.structured_A(D, N))
+    Dk, cw = r(D), r(D, W) * 0.5
+    reg = torch.zeros(B, D, W, dtype=bf, device="cuda")
+    y = torch.empty_like(x)
+    hl = torch.empty((B, D, N), device="cuda")
+    fn = lambda i: ssm.scan_fwd_conv(x, delta, A, Bm, Cm, cw, conv_state=reg, Dskip=Dk, z=z, y=y, h_last=hl)
+    _, ms = timed(fn, 5, 3, torch)
+    nbytes = scan_bytes(B, L, D, N, 2) + D * W * 4 + 2 * B * D * W * 2
+    res["prefill_conv_128x2048x4096_n16_bf16"] = {
+        "ms": round(ms, 4), "GB_s": round(nbytes / ms / 1e6, 1),
+        "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4), "gelem_s": round(B * L * D / ms / 1e6, 1)}
+    del x, z, delta, Bm, Cm, y, reg
 
     # decode: batch 128, d_inner 4096, N 16, bf16 I/O, conv width 4; 16 layers' states rotate
     B, D, N, W, layers = 128, 4096, 16, 4, 16

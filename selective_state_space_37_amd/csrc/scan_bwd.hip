@@ -56,16 +56,19 @@ __global__ __launch_bounds__(CH * KS) void scan_bwd_kernel(ScanBwdParams p) {
   __shared__ __attribute__((aligned(16))) float2 s_dx[kNB][T][CH];
   __shared__ __attribute__((aligned(16))) float2 s_g[kCkpt ? 1 : kNB][kCkpt ? 1 : T][CH];
   __shared__ float s_dzc[kFull ? kNB : 1][kFull ? T : 1][CH];      // dz = y * s_dzc
-  __shared__ __attribute__((aligned(16))) float2 s_bc[kNB][T][N];   // (B_n, C_n)
+  // B_n and C_n of each token, apart: the recomputed forward reads B only
+  __shared__ __attribute__((aligned(16))) float s_b[kNB][T][N];
+  __shared__ __attribute__((aligned(16))) float s_c[kNB][T][N];
   // partials over the slices (half a tile): dx, dDelta, y; two slices share a wave at CH = 32,
   // so their rows are 32 banks apart
   constexpr int kPStride = (T / 2) * CH + 32;
   __shared__ float s_p[kFull ? 3 : 1][kFull ? KS : 1][kFull ? kPStride : 1];
-  // partials over the channels (half a tile), one column per channel. The lane of slice s, token i, state
-  // n0 + j writes dB / dC (bc = 0 / 1) to q = (i NS + j) 2 + bc of its slice, stored at row
+  // partials over the channels (half a tile), one column per channel. The lane of slice s, token i,
+  // state n0 + j writes dB / dC (bc = 0 / 1) to q = (i NS + j) 2 + bc of its slice, stored at row
   // ((q / 8) KS + s) 8 + q % 8: the two slices of a wave write rows 8 apart (32 banks apart with
   // the row stride CH + 4), and rows of stride CH + 4 read as float4 hit distinct banks.
-  constexpr int kQRows = (T / 2) * N * 2, kQStride = CH + 4;
+  constexpr int kQCols = CH;
+  constexpr int kQRows = (T / 2) * N * 2, kQStride = kQCols + 4;
   static_assert(((T / 2) * NS * 2) % 8 == 0, "row blocks of 8");
   __shared__ __attribute__((aligned(16))) float s_q[kFull ? kQRows : 1][kFull ? kQStride : 4];
 
@@ -219,10 +222,8 @@ __global__ __launch_bounds__(CH * KS) void scan_bwd_kernel(ScanBwdParams p) {
       }
     }
     if (tid < kBC) {
-      float2 bc;
-      bc.x = kAdj ? 0.f : IoTraits<io_t>::from_bits(rB);
-      bc.y = kCkpt ? 0.f : IoTraits<io_t>::from_bits(rC);
-      s_bc[buf][tid / N][tid % N] = bc;
+      if (!kAdj) s_b[buf][tid / N][tid % N] = IoTraits<io_t>::from_bits(rB);
+      if (!kCkpt) s_c[buf][tid / N][tid % N] = IoTraits<io_t>::from_bits(rC);
     }
     if constexpr (kFull) {
 #pragma unroll
@@ -260,9 +261,9 @@ __global__ __launch_bounds__(CH * KS) void scan_bwd_kernel(ScanBwdParams p) {
         const float2 v = s_dx[buf][i][chl];
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-          const float2 bc = s_bc[buf][i][n0 + j];
+          const float bn = s_b[buf][i][n0 + j];
           const float abar = exp2_fast(v.x * a2[j]);
-          h[j] = fmaf(abar, h[j], fmaf(abar, ia[j], -ia[j]) * (bc.x * v.y));
+          h[j] = fmaf(abar, h[j], fmaf(abar, ia[j], -ia[j]) * (bn * v.y));
         }
       }
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -319,7 +320,7 @@ __global__ __launch_bounds__(CH * KS) void scan_bwd_kernel(ScanBwdParams p) {
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
           const float abar = exp2_fast(dt * a2[j]);
-          g[j] = abar * fmaf(s_bc[buf][i][n0 + j].y, gy, g[j]);
+          g[j] = abar * fmaf(s_c[buf][i][n0 + j], gy, g[j]);
         }
         dsum += dt;
       }
@@ -348,9 +349,9 @@ __global__ __launch_bounds__(CH * KS) void scan_bwd_kernel(ScanBwdParams p) {
           const float2 v = s_dx[buf][i][chl];
 #pragma unroll
           for (int j = 0; j < NS; ++j) {
-            const float2 bc = s_bc[buf][i][n0 + j];
+            const float bn = s_b[buf][i][n0 + j];
             const float abar = exp2_fast(v.x * a2[j]);
-            h[j] = fmaf(abar, h[j], fmaf(abar, ia[j], -ia[j]) * (bc.x * v.y));
+            h[j] = fmaf(abar, h[j], fmaf(abar, ia[j], -ia[j]) * (bn * v.y));
             H[i][j] = h[j];
             AB[i][j] = abar;
           }
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(CH * KS) void scan_bwd_kernel(ScanBwdParams p) {
           float dxp = 0.f, ddp = 0.f, yp = 0.f;
 #pragma unroll
           for (int j = 0; j < NS; ++j) {
-            const float2 bc = s_bc[buf][i][n0 + j];
+            const float2 bc = make_float2(s_b[buf][i][n0 + j], s_c[buf][i][n0 + j]);
             const float hprev = i > 0 ? H[i - 1][j] : hck[j];
             const float abar = AB[i][j];
             const float gn = fmaf(bc.y, gy, g[j]);              // dL/dh_t
@@ -424,7 +425,7 @@ __global__ __launch_bounds__(CH * KS) void scan_bwd_kernel(ScanBwdParams p) {
           if (r < kQRowsH) {
             const float4* row = reinterpret_cast<const float4*>(&s_q[r][0]);
 #pragma unroll
-            for (int k = 0; k < CH / 4; ++k) {
+            for (int k = 0; k < kQCols / 4; ++k) {
               const float4 q4 = row[k];
               sum += (q4.x + q4.y) + (q4.z + q4.w);
             }

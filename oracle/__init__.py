@@ -62,7 +62,7 @@ def _configure(lib):
     lib.oracle_conv1d.restype = None
     lib.oracle_step.argtypes = [i64, i64, i64, i64] + [vp, vp, vp, ci] + [vp] * 10
     lib.oracle_step.restype = None
-    lib.oracle_ssd.argtypes = [i64, i64, i64, i64, i64] + [vp, vp, vp, ci] + [vp] * 8
+    lib.oracle_ssd.argtypes = [i64, i64, i64, i64, i64, i64] + [vp, vp, vp, ci] + [vp] * 4 + [ci] + [vp] * 4
     lib.oracle_ssd.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ci
@@ -263,23 +263,31 @@ def step(x, delta, A, Bm, Cm, h, *, delta_bias=None, delta_softplus=False, Dskip
 def ssd(x, delta, A, Bm, Cm, *, delta_bias=None, delta_softplus=False, Dskip=None, z=None, h0=None,
         _lib=None):
     """Mamba-2 scalar-A layer as the plain recurrence. x, z: [B, L, H, P]; delta: [B, L, H];
-    A, delta_bias, Dskip: [H]; Bm, Cm: [B, L, N]; h0: [B, H, P, N]. Returns (y, h_last) in fp64."""
+    A, delta_bias: [H]; Bm, Cm: [B, L, N] (shared by all heads) or [B, L, G, N] (G groups of H/G
+    consecutive heads); Dskip: [H] (per head) or [H, P] (per channel); h0: [B, H, P, N].
+    Returns (y, h_last) in fp64."""
     x = _f64(x)
     Bsz, L, H, P = x.shape
     Bm = _f64(Bm)
-    N = Bm.shape[2]
+    if Bm.ndim == 3:
+        Bm = Bm[:, :, None, :]
+    G, N = Bm.shape[2], Bm.shape[3]
+    if H % G:
+        raise ValueError("oracle.ssd: the head count must be a multiple of the group count")
+    Bm = _f64(Bm, (Bsz, L, G, N))
+    Cm = _f64(Cm)
+    Cm = _f64(Cm[:, :, None, :] if Cm.ndim == 3 else Cm, (Bsz, L, G, N))
     delta = _f64(delta, (Bsz, L, H))
     A = _f64(A, (H,))
-    Bm = _f64(Bm, (Bsz, L, N))
-    Cm = _f64(Cm, (Bsz, L, N))
     delta_bias = _f64(delta_bias, (H,))
-    Dskip = _f64(Dskip, (H,))
+    dpc = Dskip is not None and np.ndim(Dskip) == 2
+    Dskip = _f64(Dskip, (H, P) if dpc else (H,))
     z = _f64(z, (Bsz, L, H, P))
     h0 = _f64(h0, (Bsz, H, P, N))
     y = np.empty((Bsz, L, H, P), dtype=np.float64)
     h_last = np.empty((Bsz, H, P, N), dtype=np.float64)
-    (_lib or _load()).oracle_ssd(Bsz, L, H, P, N, _p(x), _p(delta), _p(delta_bias), int(bool(delta_softplus)),
-                       _p(A), _p(Bm), _p(Cm), _p(Dskip), _p(z), _p(h0), _p(y), _p(h_last))
+    (_lib or _load()).oracle_ssd(Bsz, L, H, P, N, G, _p(x), _p(delta), _p(delta_bias), int(bool(delta_softplus)),
+                                 _p(A), _p(Bm), _p(Cm), _p(Dskip), int(dpc), _p(z), _p(h0), _p(y), _p(h_last))
     return y, h_last
 
 
@@ -287,24 +295,28 @@ def ssd_quadratic(x, delta, A, Bm, Cm, *, delta_bias=None, delta_softplus=False,
                   Dskip=None, z=None):
     """Mamba-2 layer as one lower-triangular matrix per (batch, head), tiny inputs only.
 
-    Per the "Mamba-2: two algorithms" section: entry (i, j), j <= i, is C_i . B_j times all decay
-    between step j and step i, i.e. exp(a * (sum of Delta over steps j+1..i)), times the
-    zero-order-hold input scale expm1(a Delta_j) / a of step j. y = M x, then D term and gate.
-    Zero initial state.
+    Per the "Mamba-2: two algorithms" section: entry (i, j), j <= i, is C_i . B_j (B and C of the
+    head's group) times all decay between step j and step i, i.e. exp(a * (sum of Delta over
+    steps j+1..i)), times the zero-order-hold input scale expm1(a Delta_j) / a of step j. y = M x,
+    then the D term (per head [H] or per channel [H, P]) and the gate. Zero initial state.
     """
     x = _f64(x)
     Bsz, L, H, P = x.shape
     if L > 512:
         raise ValueError("ssd_quadratic is for tiny inputs (L <= 512)")
     Bm, Cm = _f64(Bm), _f64(Cm)
+    if Bm.ndim == 3:
+        Bm, Cm = Bm[:, :, None, :], Cm[:, :, None, :]
+    G = Bm.shape[2]
     delta = _f64(delta, (Bsz, L, H))
     A = _f64(A, (H,))
     u = delta + (0.0 if delta_bias is None else _f64(delta_bias, (H,))[None, None, :])
     dt = np.logaddexp(0.0, u) if delta_softplus else u
     y = np.zeros((Bsz, L, H, P), dtype=np.float64)
     for b in range(Bsz):
-        G = Cm[b] @ Bm[b].T  # [L, L]: C_i . B_j
         for hd in range(H):
+            grp = hd // (H // G)
+            Gm = Cm[b, :, grp] @ Bm[b, :, grp].T  # [L, L]: C_i . B_j of the head's group
             a = A[hd]
             d = dt[b, :, hd]
             M = np.zeros((L, L))
@@ -312,10 +324,11 @@ def ssd_quadratic(x, delta, A, Bm, Cm, *, delta_bias=None, delta_softplus=False,
                 for j in range(i + 1):
                     decay = np.exp(a * d[j + 1:i + 1].sum())
                     scale = d[j] if a == 0.0 else np.expm1(a * d[j]) / a
-                    M[i, j] = G[i, j] * decay * scale
+                    M[i, j] = Gm[i, j] * decay * scale
             y[b, :, hd, :] = M @ x[b, :, hd, :]
     if Dskip is not None:
-        y += _f64(Dskip, (H,))[None, None, :, None] * x
+        Dk = _f64(Dskip)
+        y += (Dk[None, None] if Dk.ndim == 2 else Dk[None, None, :, None]) * x
     if z is not None:
         zz = _f64(z, (Bsz, L, H, P))
         y *= zz / (1.0 + np.exp(-zz))

@@ -288,27 +288,31 @@ void oracle_step(int64_t Bsz, int64_t D, int64_t N, int64_t W,
 /*
  * oracle_ssd: Mamba-2 layer with one scalar A per head, run as the plain recurrence
  * (the chunk size plays no part in the result).
- *   x, z, y : [Bsz, L, H, P]   delta : [Bsz, L, H]   delta_bias, A, Dskip : [H]
- *   Bm, Cm  : [Bsz, L, N] (shared by all heads)       h0, h_last : [Bsz, H, P, N]
+ *   x, z, y : [Bsz, L, H, P]   delta : [Bsz, L, H]   delta_bias, A : [H]
+ *   Bm, Cm  : [Bsz, L, G, N]: G groups of heads share one B and C (head hd uses group
+ *             hd / (H / G); G = 1: shared by all heads)
+ *   Dskip   : [H] (one D per head) or, with dskip_per_channel, [H, P]
+ *   h0, h_last : [Bsz, H, P, N]
  * State per (b, h): S[p, n] <- exp(Delta a) S[p, n] + expm1(Delta a)/a * x[p] * B[n];
- * y[p] = sum_n C[n] S[p, n] (+ Dskip[h] x[p]), then the optional gate.
+ * y[p] = sum_n C[n] S[p, n] (+ D x[p]), then the optional gate.
  */
-void oracle_ssd(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t N,
+void oracle_ssd(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
                 const double* x, const double* delta, const double* delta_bias, int delta_softplus,
                 const double* A, const double* Bm, const double* Cm, const double* Dskip,
-                const double* z, const double* h0, double* y, double* h_last) {
+                int dskip_per_channel, const double* z, const double* h0, double* y, double* h_last) {
 #pragma omp parallel for collapse(2) schedule(dynamic, 1)
   for (int64_t b = 0; b < Bsz; ++b) {
     for (int64_t hd = 0; hd < H; ++hd) {
       double* S = (double*)malloc((size_t)(P * N) * sizeof(double));
       for (int64_t i = 0; i < P * N; ++i) S[i] = h0 ? h0[(b * H + hd) * P * N + i] : 0.0;
       const double a = A[hd];
+      const int64_t grp = hd / (H / G);
       for (int64_t t = 0; t < L; ++t) {
         const double dt = o_step_size(delta[(b * L + t) * H + hd], delta_bias, hd, delta_softplus);
         const double abar = exp(dt * a);
         const double phi = o_zoh_scale(dt, a);
-        const double* Bt = Bm + (b * L + t) * N;
-        const double* Ct = Cm + (b * L + t) * N;
+        const double* Bt = Bm + ((b * L + t) * G + grp) * N;
+        const double* Ct = Cm + ((b * L + t) * G + grp) * N;
         const double* xt = x + ((b * L + t) * H + hd) * P;
         const double* zt = z ? z + ((b * L + t) * H + hd) * P : NULL;
         double* yt = y + ((b * L + t) * H + hd) * P;
@@ -318,7 +322,7 @@ void oracle_ssd(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t N,
             S[p * N + n] = abar * S[p * N + n] + phi * xt[p] * Bt[n];
             out += Ct[n] * S[p * N + n];
           }
-          if (Dskip) out += Dskip[hd] * xt[p];
+          if (Dskip) out += (dskip_per_channel ? Dskip[hd * P + p] : Dskip[hd]) * xt[p];
           if (zt) out *= zt[p] * o_sigmoid(zt[p]);
           yt[p] = out;
         }

@@ -348,17 +348,19 @@ def check_conv_prefill(conv1d, scan_conv, step, seed=22, L=13, W=4):
 
 
 # ----------------------------------------------------------------------------- SSD
-def tiny_ssd_case(seed, Bsz=2, L=20, H=2, P=3, N=4, gate=True, dskip=True, softplus=True):
+def tiny_ssd_case(seed, Bsz=2, L=20, H=2, P=3, N=4, gate=True, dskip=True, softplus=True, groups=None,
+                  dskip_per_channel=False):
     g = RNG(seed)
+    bc = (Bsz, L, N) if groups is None else (Bsz, L, groups, N)
     return dict(
         x=g.standard_normal((Bsz, L, H, P)),
         delta=g.standard_normal((Bsz, L, H)) * 0.6,
         A=-g.uniform(0.3, 4.0, H),
-        Bm=g.standard_normal((Bsz, L, N)),
-        Cm=g.standard_normal((Bsz, L, N)),
+        Bm=g.standard_normal(bc),
+        Cm=g.standard_normal(bc),
         delta_bias=g.standard_normal(H) * 0.2,
         delta_softplus=softplus,
-        Dskip=g.standard_normal(H) if dskip else None,
+        Dskip=(g.standard_normal((H, P)) if dskip_per_channel else g.standard_normal(H)) if dskip else None,
         z=g.standard_normal((Bsz, L, H, P)) if gate else None,
     )
 
@@ -366,10 +368,35 @@ def tiny_ssd_case(seed, Bsz=2, L=20, H=2, P=3, N=4, gate=True, dskip=True, softp
 def check_ssd_quadratic(ssd, ssd_quadratic, seed=30):
     """[MS] Mamba-2: the recurrence equals multiplication by the lower-triangular matrix."""
     e = 0.0
-    for s, kw in ((seed, {}), (seed + 1, dict(gate=False, dskip=False, L=33, N=6, P=2))):
+    for s, kw in ((seed, {}), (seed + 1, dict(gate=False, dskip=False, L=33, N=6, P=2)),
+                  (seed + 2, dict(H=6, groups=3, dskip_per_channel=True)),
+                  (seed + 3, dict(H=4, groups=4, L=17))):
         c = tiny_ssd_case(s, **kw)
         y, _ = ssd(**c)
         e = max(e, rel_err(y, ssd_quadratic(**c)))
+    return e
+
+
+def check_ssd_groups(ssd, seed=32):
+    """G groups of heads each with their own B, C: every group's heads give the same outputs and
+    states as a layer holding only those heads with that group's B, C shared by all of them; D per
+    channel equals per-head D where it is constant over a head's channels."""
+    c = tiny_ssd_case(seed, H=6, groups=3, dskip_per_channel=True)
+    Bsz, L, H, P = c["x"].shape
+    g = RNG(seed + 1)
+    h0 = g.standard_normal((Bsz, H, P, c["Bm"].shape[3]))
+    y, hl = ssd(h0=h0, **c)
+    e = 0.0
+    per = H // 3
+    for grp in range(3):
+        hs = slice(grp * per, (grp + 1) * per)
+        cg = dict(c, x=c["x"][:, :, hs], delta=c["delta"][:, :, hs], A=c["A"][hs], Bm=c["Bm"][:, :, grp],
+                  Cm=c["Cm"][:, :, grp], delta_bias=c["delta_bias"][hs], Dskip=c["Dskip"][hs], z=c["z"][:, :, hs])
+        yg, hg = ssd(h0=h0[:, hs], **cg)
+        e = max(e, rel_err(y[:, :, hs], yg), rel_err(hl[:, hs], hg))
+    d1 = dict(c, Dskip=c["Dskip"][:, 0])
+    d2 = dict(c, Dskip=np.repeat(c["Dskip"][:, :1], P, axis=1))
+    e = max(e, rel_err(ssd(**d1)[0], ssd(**d2)[0]))
     return e
 
 

@@ -139,7 +139,10 @@ SSD_MUTANTS = {
     "ssd_euler": [("const double phi = o_zoh_scale(dt, a);", "const double phi = dt;")],
     "ssd_readout_B": [("out += Ct[n] * S[p * N + n];", "out += Bt[n] * S[p * N + n];")],
     "ssd_x_index": [("phi * xt[p] * Bt[n];", "phi * xt[0] * Bt[n];")],
-    "ssd_D_head": [("if (Dskip) out += Dskip[hd] * xt[p];", "if (Dskip) out += Dskip[0] * xt[p];")],
+    "ssd_D_head": [("(dskip_per_channel ? Dskip[hd * P + p] : Dskip[hd])", "(dskip_per_channel ? Dskip[hd * P + p] : Dskip[0])")],
+    "ssd_D_channel": [("(dskip_per_channel ? Dskip[hd * P + p] : Dskip[hd])", "(dskip_per_channel ? Dskip[hd * P] : Dskip[hd])")],
+    "ssd_group_of_head": [("const int64_t grp = hd / (H / G);", "const int64_t grp = hd % G;")],
+    "ssd_C_group": [("const double* Ct = Cm + ((b * L + t) * G + grp) * N;", "const double* Ct = Cm + ((b * L + t) * G) * N;")],
     "ssd_delta_head": [("delta[(b * L + t) * H + hd]", "delta[(b * L + t) * H]")],
 }
 
@@ -185,6 +188,10 @@ def test_ssd_mutant_caught(tmp_path, name):
     v = _mutant(tmp_path, name, SSD_MUTANTS[name])
     errs = [pins.check_ssd_quadratic(v.ssd, oracle.ssd_quadratic), pins.check_ssd_equals_scan(v.ssd, oracle.scan)]
     assert max(errs) > 1e-12, name
+
+
+def test_ssd_groups():
+    assert pins.check_ssd_groups(oracle.ssd) <= 1e-12
 
 
 @pytest.mark.parametrize("name", sorted(BWD_MUTANTS))

@@ -19,6 +19,11 @@
  *                     (C_i . B_j times all decay between steps j and i); the sequence is cut
  *                     into chunks, each chunk is a masked matrix product, and only the state
  *                     passes between chunks.
+ *   ssd_chunk_fwd_grouped  the same layer with B and C given per group of heads and D per head
+ *                     or per channel. The page likens the layer to masked attention (C as the
+ *                     queries, B as the keys, the input as the values); groups let several heads
+ *                     share one B and C, as heads can share keys and queries. The pages do not
+ *                     spell groups out: head h uses group h / (H / G), G = 1 is ssd_chunk_fwd.
  *
  * Conventions shared by every entry point
  *   - Sizes are int64_t. Tensors are dense, row-major, contiguous; no strides.
@@ -249,7 +254,8 @@ ssm_status ssm_state_update(int64_t B, int64_t D, int64_t N, int64_t conv_width,
  *   cores (bf16 operands, float32 accumulation); between chunks the float32 state.
  *
  *   Requirements: io_dtype SSM_BF16; P == 64; N in {64, 128}; chunk in {64, 128, 256};
- *   B, L >= 0 (0 is a no-op; with L == 0 h_last receives h0 or zeros); H >= 1.
+ *   B, L >= 0 (0 is a no-op; with L == 0 h_last receives h0 or zeros); 1 <= H <= 65535,
+ *   B <= 65535 and at most 65535 chunks (grid dimensions).
  */
 size_t ssd_chunk_fwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N,
                                      int64_t chunk, ssm_dtype io_dtype);
@@ -260,6 +266,31 @@ ssm_status ssd_chunk_fwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, 
                          const void* Bm, const void* Cm, const float* Dskip, const void* z,
                          const float* h0, void* y, float* h_last, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * ssd_chunk_fwd_grouped -- ssd_chunk_fwd with G groups of B and C and an optional per-channel D.
+ *
+ *   Bm, Cm         : [B, L, G, N]   io_dtype; head h reads group h / (H / G) (heads
+ *                                   [k H/G, (k+1) H/G) share group k)
+ *   Dskip          : NULL, [H] float32 (dskip_per_channel == 0) or [H, P] float32
+ *                    (dskip_per_channel != 0: y[.., h, p] += Dskip[h, p] x[.., h, p]; then
+ *                    16-byte aligned)
+ *   every other argument as in ssd_chunk_fwd.
+ *
+ *   Requirements: those of ssd_chunk_fwd; G >= 1 and G divides H; B * G <= 65535, H <= 65535
+ *   and at most 65535 chunks. The workspace grows with G (C B^T and B per chunk are kept per
+ *   group); query it with ssd_chunk_fwd_grouped_workspace_bytes.
+ */
+size_t ssd_chunk_fwd_grouped_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N,
+                                             int64_t G, int64_t chunk, ssm_dtype io_dtype);
+
+ssm_status ssd_chunk_fwd_grouped(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
+                                 int64_t chunk, ssm_dtype io_dtype, const void* x,
+                                 const void* delta, const float* delta_bias, int delta_softplus,
+                                 const float* A, const void* Bm, const void* Cm,
+                                 const float* Dskip, int dskip_per_channel, const void* z,
+                                 const float* h0, void* y, float* h_last, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

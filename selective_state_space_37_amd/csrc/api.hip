@@ -373,21 +373,39 @@ ssm_status ssm_state_update(int64_t B, int64_t D, int64_t N, int64_t W, ssm_dtyp
 size_t ssd_chunk_fwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t chunk,
                                      ssm_dtype) {
   if (B <= 0 || L <= 0 || H <= 0 || P <= 0 || N <= 0 || chunk <= 0) return 0;
-  return ssm::ssd_workspace_bytes(B, L, H, P, N, chunk);
+  return ssm::ssd_workspace_bytes(B, L, H, P, N, 1, chunk);
 }
 
-ssm_status ssd_chunk_fwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t chunk, ssm_dtype io,
-                         const void* x, const void* delta, const float* delta_bias, int delta_softplus,
-                         const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
-                         const float* h0, void* y, float* h_last, void* ws, size_t ws_bytes, void* stream) {
+size_t ssd_chunk_fwd_grouped_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
+                                             int64_t chunk, ssm_dtype) {
+  if (B <= 0 || L <= 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || chunk <= 0) return 0;
+  return ssm::ssd_workspace_bytes(B, L, H, P, N, G, chunk);
+}
+
+}  // extern "C"
+
+namespace {
+
+ssm_status ssd_common(const char* fn, int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
+                      int64_t chunk, ssm_dtype io, const void* x, const void* delta, const float* delta_bias,
+                      int delta_softplus, const float* A, const void* Bm, const void* Cm, const float* Dskip,
+                      int dskip_per_channel, const void* z, const float* h0, void* y, float* h_last, void* ws,
+                      size_t ws_bytes, void* stream) {
   if (B < 0 || L < 0) return fail(SSM_ERR_INVALID_ARGUMENT, "B and L must be >= 0");
   if (H < 1) return fail(SSM_ERR_INVALID_ARGUMENT, "H=%lld must be >= 1", (long long)H);
+  if (G < 1 || H % G != 0)
+    return fail(SSM_ERR_INVALID_ARGUMENT, "G=%lld must be >= 1 and divide H=%lld", (long long)G, (long long)H);
   if (!valid_dtype(io)) return fail(SSM_ERR_INVALID_ARGUMENT, "unknown io_dtype %d", (int)io);
-  if (io != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "ssd_chunk_fwd supports io_dtype SSM_BF16 only");
+  if (io != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "%s supports io_dtype SSM_BF16 only", fn);
   if (P != 64) return fail(SSM_ERR_UNSUPPORTED, "P=%lld: supported head dim is 64", (long long)P);
   if (N != 64 && N != 128) return fail(SSM_ERR_UNSUPPORTED, "N=%lld: supported 64, 128", (long long)N);
   if (chunk != 64 && chunk != 128 && chunk != 256)
     return fail(SSM_ERR_UNSUPPORTED, "chunk=%lld: supported 64, 128, 256", (long long)chunk);
+  // grid limits: chunks and batch rows x groups index grid dimensions y and z, heads x
+  if ((L + chunk - 1) / chunk > 65535)
+    return fail(SSM_ERR_UNSUPPORTED, "L=%lld: at most 65535 chunks of %lld tokens", (long long)L, (long long)chunk);
+  if (B * G > 65535 || H > 65535)
+    return fail(SSM_ERR_UNSUPPORTED, "B*G=%lld and H=%lld must each be <= 65535", (long long)(B * G), (long long)H);
   if (B == 0) return ok();
   if (!A) return fail(SSM_ERR_INVALID_ARGUMENT, "A is NULL");
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -400,26 +418,49 @@ ssm_status ssd_chunk_fwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, 
     return from_hip(e, "L == 0 state copy");
   }
   if (!x || !delta || !Bm || !Cm || !y) return fail(SSM_ERR_INVALID_ARGUMENT, "x, delta, Bm, Cm and y must not be NULL");
-  if (!aligned16(x) || !aligned16(y) || !aligned16(Bm) || !aligned16(Cm) || (z && !aligned16(z)))
-    return fail(SSM_ERR_INVALID_ARGUMENT, "per-token tensors must be 16-byte aligned");
+  if (!aligned16(x) || !aligned16(y) || !aligned16(Bm) || !aligned16(Cm) || (z && !aligned16(z)) ||
+      (Dskip && dskip_per_channel && !aligned16(Dskip)))
+    return fail(SSM_ERR_INVALID_ARGUMENT, "per-token tensors and a per-channel Dskip must be 16-byte aligned");
   const size_t tok = (size_t)(B * L * H * P) * 2;
+  const size_t bc = (size_t)(B * L * G * N) * 2;
   const void* ins[] = {x, delta, z, Bm, Cm, A, h0};
-  const size_t insz[] = {tok, (size_t)(B * L * H) * 2, tok, (size_t)(B * L * N) * 2, (size_t)(B * L * N) * 2,
-                         (size_t)H * 4, stb};
+  const size_t insz[] = {tok, (size_t)(B * L * H) * 2, tok, bc, bc, (size_t)H * 4, stb};
   for (int k = 0; k < 7; ++k)
     if (overlaps(y, tok, ins[k], insz[k])) return fail(SSM_ERR_INVALID_ARGUMENT, "y overlaps an input");
-  const size_t need = ssm::ssd_workspace_bytes(B, L, H, P, N, chunk);
+  const size_t need = ssm::ssd_workspace_bytes(B, L, H, P, N, G, chunk);
   if (!ws) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace is NULL; %zu bytes needed", need);
   if (ws_bytes < need) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, need);
   if (!aligned16(ws)) return fail(SSM_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
   if (overlaps(ws, need, y, tok)) return fail(SSM_ERR_INVALID_ARGUMENT, "workspace overlaps y");
   ssm::SsdParams p{};
-  p.B = B; p.L = L; p.H = H; p.P = P; p.N = N; p.Q = chunk;
+  p.B = B; p.L = L; p.H = H; p.P = P; p.N = N; p.Q = chunk; p.G = G;
   p.x = x; p.delta = delta; p.z = z; p.Bm = Bm; p.Cm = Cm;
   p.delta_bias = delta_bias; p.A = A; p.Dskip = Dskip; p.h0 = h0;
+  p.dskip_per_channel = Dskip && dskip_per_channel ? 1 : 0;
   p.y = y; p.h_last = h_last; p.delta_softplus = delta_softplus ? 1 : 0;
   ssm::ssd_workspace_carve(p, ws);
-  return from_hip(ssm::launch_ssd(p, st), "ssd_chunk_fwd launch");
+  return from_hip(ssm::launch_ssd(p, st), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status ssd_chunk_fwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t chunk, ssm_dtype io,
+                         const void* x, const void* delta, const float* delta_bias, int delta_softplus,
+                         const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                         const float* h0, void* y, float* h_last, void* ws, size_t ws_bytes, void* stream) {
+  return ssd_common("ssd_chunk_fwd", B, L, H, P, N, 1, chunk, io, x, delta, delta_bias, delta_softplus, A, Bm, Cm,
+                    Dskip, 0, z, h0, y, h_last, ws, ws_bytes, stream);
+}
+
+ssm_status ssd_chunk_fwd_grouped(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t chunk,
+                                 ssm_dtype io, const void* x, const void* delta, const float* delta_bias,
+                                 int delta_softplus, const float* A, const void* Bm, const void* Cm,
+                                 const float* Dskip, int dskip_per_channel, const void* z, const float* h0, void* y,
+                                 float* h_last, void* ws, size_t ws_bytes, void* stream) {
+  return ssd_common("ssd_chunk_fwd_grouped", B, L, H, P, N, G, chunk, io, x, delta, delta_bias, delta_softplus, A,
+                    Bm, Cm, Dskip, dskip_per_channel, z, h0, y, h_last, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

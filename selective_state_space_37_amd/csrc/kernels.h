@@ -114,25 +114,27 @@ hipError_t launch_state_update(const StepParams& p, hipStream_t stream);
 
 struct SsdParams {
   int64_t B, L, H, P, N, Q;  // Q = chunk length
+  int64_t G;               // groups of B and C: head h reads group h / (H / G)
   const void* x;           // bf16 [B, L, H, P]
   const void* delta;       // bf16 [B, L, H]
   const void* z;           // nullable
-  const void* Bm;          // bf16 [B, L, N]
+  const void* Bm;          // bf16 [B, L, G, N]
   const void* Cm;
   const float* delta_bias; // nullable [H]
   const float* A;          // [H]
-  const float* Dskip;      // nullable [H]
+  const float* Dskip;      // nullable: [H] per head, or [H, P] per channel
+  int dskip_per_channel;
   const float* h0;         // nullable [B, H, P, N]
   void* y;
   float* h_last;           // nullable
   int delta_softplus;
   void* ws_hin;            // bf16 [B, nchunks, H, P, N]: state entering each chunk
-  void* ws_G;              // bf16 [B, nchunks, Q, Q]: C_i . B_j inside each chunk
-  void* ws_Bt;             // bf16 [B, nchunks, N, Q]: B of each chunk, transposed
+  void* ws_G;              // bf16 [B, G, nchunks, Q, Q]: C_i . B_j inside each chunk
+  void* ws_Bt;             // bf16 [B, G, nchunks, N, Q]: B of each chunk, transposed
   float2* ws_sphi;         // [B, nchunks, H, Q]: (inclusive cumulative Delta, ZOH input scale)
 };
 
-size_t ssd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t Q);
+size_t ssd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);
 // Point the workspace fields of p at their parts of ws (ssd_workspace_bytes() bytes).
 void ssd_workspace_carve(SsdParams& p, void* ws);
 hipError_t launch_ssd(const SsdParams& p, hipStream_t stream);

@@ -6,8 +6,8 @@
 // chunks of Q tokens; inside a chunk that masked product runs on the matrix cores, and only the
 // state passes between chunks. With zero-order hold the input of step j enters with the scale
 // phi_j = expm1(a Delta_j) / a, and with S the inclusive cumulative sum of Delta in the chunk:
-//   prep kernel  : per (batch, chunk), G = C B^T (Q x Q, MFMA, shared by all heads) and a
-//                  transposed copy of B for the state kernel's operand layout
+//   prep kernel  : per (batch, chunk, group), G = C B^T (Q x Q, MFMA, shared by the group's
+//                  heads) and a transposed copy of B for the state kernel's operand layout
 //   state kernel : per (batch, head), sequential over the chunks with the state
 //                  in MFMA accumulators: store h_{c-1} (bf16, the carry the outputs need), then
 //                  h_c = exp(a S_last) h_{c-1} + sum_j exp(a (S_last - S_j)) phi_j x_j B_j^T
@@ -17,6 +17,8 @@
 //                      (+ D x_i, gate)
 // Decays are always formed from differences of cumulative sums inside one chunk, so no
 // intermediate exponential can overflow. Operands are bf16, accumulation float32.
+// B and C come in G groups ([B, L, G, N]); head h reads group h / (H / G) (G = 1: one B and C
+// for all heads). The skip weight D is per head or per channel of a head.
 //
 // MFMA v_mfma_f32_16x16x32_bf16 lane layout (lane l, g = l / 16):
 //   A (16 x 32, M x K): row l % 16, k = 8g .. 8g+7;  B (32 x 16, K x N): col l % 16, k = 8g .. 8g+7;
@@ -137,18 +139,21 @@ __global__ __launch_bounds__(256) void ssd_cumsum_kernel(SsdParams p) {
 }
 
 // ---------------------------------------------------------------------------- prep
-// grid (4, chunks, B): part `part` transposes states [part N/4, (part+1) N/4) of B and computes
-// every fourth lower-triangular 16 x 16 tile of G (row blocks ib, column tiles jt <= ib).
+// grid (4, chunks, B G): part `part` transposes states [part N/4, (part+1) N/4) of one group's B
+// and computes every fourth lower-triangular 16 x 16 tile of that group's G (row blocks ib,
+// column tiles jt <= ib). Token t's row of the group starts at element (t G + grp) N.
 template <int Q, int N>
 __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
   const int part = blockIdx.x;
-  const int64_t c = blockIdx.y, b = blockIdx.z;
+  const int64_t c = blockIdx.y, bg = blockIdx.z;   // bg = b G + grp
+  const int64_t b = bg / p.G, grp = bg % p.G;
   const int64_t nch = gridDim.y;
   const int tid = threadIdx.x;
-  const bf16_t* Bg = static_cast<const bf16_t*>(p.Bm);
-  const bf16_t* Cg = static_cast<const bf16_t*>(p.Cm);
+  const int64_t rs = p.G * N;                      // token row stride of B and C
+  const bf16_t* Bg = static_cast<const bf16_t*>(p.Bm) + b * p.L * rs + grp * N;
+  const bf16_t* Cg = static_cast<const bf16_t*>(p.Cm) + b * p.L * rs + grp * N;
   // transposed B: Bt[n][j], 8 tokens per 16-byte store
-  bf16_t* Bt = static_cast<bf16_t*>(p.ws_Bt) + (b * nch + c) * (int64_t)(N * Q);
+  bf16_t* Bt = static_cast<bf16_t*>(p.ws_Bt) + (bg * nch + c) * (int64_t)(N * Q);
   constexpr int NQ = N / 4;
   for (int it = tid; it < NQ * (Q / 8); it += 256) {
     const int n = part * NQ + it / (Q / 8);
@@ -158,8 +163,8 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
     for (int q = 0; q < 4; ++q) {
       uint32_t lo = 0, hi = 0;
       const int64_t t0 = c * Q + j0 + 2 * q;
-      if (t0 < p.L) lo = Bg[(b * p.L + t0) * N + n].bits;
-      if (t0 + 1 < p.L) hi = Bg[(b * p.L + t0 + 1) * N + n].bits;
+      if (t0 < p.L) lo = Bg[t0 * rs + n].bits;
+      if (t0 + 1 < p.L) hi = Bg[(t0 + 1) * rs + n].bits;
       wv[q] = lo | (hi << 16);
     }
     *reinterpret_cast<uint4*>(Bt + (int64_t)n * Q + j0) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
@@ -169,17 +174,17 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
   // (and the row blocks derived from it) in scalar registers, so branches on it are not divergent
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 4, r16 = lane & 15;
   constexpr int NIB = Q / 16, KS = N / 32, NTILES = NIB * (NIB + 1) / 2;
-  bf16_t* G = static_cast<bf16_t*>(p.ws_G) + (b * nch + c) * (int64_t)(Q * Q);
+  bf16_t* G = static_cast<bf16_t*>(p.ws_G) + (bg * nch + c) * (int64_t)(Q * Q);
   for (int k = part * 4 + w; k < NTILES; k += 16) {
     int ib = 0, rem = k;
     while (rem > ib) { rem -= ib + 1; ++ib; }
     const int jt = rem;
-    const int64_t ti = c * Q + ib * 16 + r16, tj = c * Q + jt * 16 + r16;
+    const int64_t ti = c * Q + ib * 16 + r16, tj = c * Q + jt * 16 + r16;   // tokens in the row
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 ca = ti < p.L ? load_frag(Cg + (b * p.L + ti) * N + ks * 32 + 8 * g) : zero_frag();
-      const bf16x8 bb = tj < p.L ? load_frag(Bg + (b * p.L + tj) * N + ks * 32 + 8 * g) : zero_frag();
+      const bf16x8 ca = ti < p.L ? load_frag(Cg + ti * rs + ks * 32 + 8 * g) : zero_frag();
+      const bf16x8 bb = tj < p.L ? load_frag(Bg + tj * rs + ks * 32 + 8 * g) : zero_frag();
       acc = mfma16(ca, bb, acc);  // D[i][j] = sum_n C_i[n] B_j[n]
     }
 #pragma unroll
@@ -193,8 +198,8 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
 // as NTW = N / 32 MFMA tiles computed transposed (states x channels), so that
 // acc[k][r] = h[p = 16 pq + lane % 16][n = (w2 NTW + k) 16 + 4 g + r]: four consecutive states
 // per lane, stored as one 8-byte (bf16) or 16-byte (float) piece. Per chunk the transposed B
-// (shared by every head) and the scaled, transposed x of the head are staged in LDS once for all
-// eight waves.
+// (shared by the heads of a group) and the scaled, transposed x of the head are staged in LDS
+// once for all eight waves.
 //
 // Inputs are loaded two chunks ahead into two register buffers used in turn (the loop is
 // unrolled by two; no buffer is copied). Every global load and store of the loop is issued
@@ -236,7 +241,8 @@ __global__ __launch_bounds__(512) void ssd_state_kernel(SsdParams p) {
   }
   const bf16_t* xg = static_cast<const bf16_t*>(p.x);
   bf16_t* hin_all = static_cast<bf16_t*>(p.ws_hin);
-  const bf16_t* Bt_all = static_cast<const bf16_t*>(p.ws_Bt);
+  const int64_t bg = b * p.G + h / (p.H / p.G);   // this head's (batch, group)
+  const bf16_t* Bt_all = static_cast<const bf16_t*>(p.ws_Bt) + bg * nch * (int64_t)(N * Q);
 
   // x item of this thread: tokens (2 jp, 2 jp + 1), channels [16 pg, 16 pg + 16). With fewer
   // items than threads, threads tid and tid + XPAIRS take the same item and write the same
@@ -266,7 +272,7 @@ __global__ __launch_bounds__(512) void ssd_state_kernel(SsdParams p) {
       in.sphi[u] = reinterpret_cast<const f32x2*>(sp)[j];
     }
     in.s_last = sp[Q - 1].x;
-    const u32x4* bt = reinterpret_cast<const u32x4*>(Bt_all + (b * nch + c) * (int64_t)(N * Q));
+    const u32x4* bt = reinterpret_cast<const u32x4*>(Bt_all + c * (int64_t)(N * Q));
 #pragma unroll
     for (int k = 0; k < BT_PER; ++k) in.bt[k] = bt[tid + 512 * k];
   };
@@ -380,9 +386,10 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 4, r16 = lane & 15;
   constexpr int NIB = Q / 16;   // 16-row blocks of the chunk
   constexpr int KS = N / 32;    // K steps over the state dimension
-  const bf16_t* Cg = static_cast<const bf16_t*>(p.Cm);
-  const bf16_t* G = static_cast<const bf16_t*>(p.ws_G) + (b * nch + c) * (int64_t)(Q * Q);
-  const float dsk = p.Dskip ? p.Dskip[h] : 0.f;
+  const int64_t grp = h / (p.H / p.G), rs = p.G * N;   // this head's group, token row stride of C
+  const bf16_t* Cg = static_cast<const bf16_t*>(p.Cm) + b * p.L * rs + grp * N;
+  const bf16_t* G = static_cast<const bf16_t*>(p.ws_G) + ((b * p.G + grp) * nch + c) * (int64_t)(Q * Q);
+  const float dsk = p.Dskip && !p.dskip_per_channel ? p.Dskip[h] : 0.f;
   const bf16_t* zg = static_cast<const bf16_t*>(p.z);
   bf16_t* yg = static_cast<bf16_t*>(p.y);
 
@@ -406,7 +413,7 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
     const int64_t ti = c * Q + ib * 16 + r16;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      out[ks] = ti < p.L ? load_frag(Cg + (b * p.L + ti) * N + ks * 32 + 8 * g) : zero_frag();
+      out[ks] = ti < p.L ? load_frag(Cg + ti * rs + ks * 32 + 8 * g) : zero_frag();
   };
   bf16x8 cnext[KS];
   if (NIB >= 4 || w < NIB) load_c(block_of(0), cnext);
@@ -502,10 +509,15 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
         float v[4] = {acc[pt][0], acc[pt][1], acc[pt][2], acc[pt][3]};
         if (p.Dskip) {
           const uint2 xr = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(p.x) + o);
-          v[0] = fmaf(dsk, bf16_lo(xr.x), v[0]);
-          v[1] = fmaf(dsk, bf16_hi(xr.x), v[1]);
-          v[2] = fmaf(dsk, bf16_lo(xr.y), v[2]);
-          v[3] = fmaf(dsk, bf16_hi(xr.y), v[3]);
+          float d[4] = {dsk, dsk, dsk, dsk};
+          if (p.dskip_per_channel) {   // channels pt 16 + 4 g .. + 3 of head h
+            const float4 dv = *reinterpret_cast<const float4*>(p.Dskip + h * kP + pt * 16 + 4 * g);
+            d[0] = dv.x; d[1] = dv.y; d[2] = dv.z; d[3] = dv.w;
+          }
+          v[0] = fmaf(d[0], bf16_lo(xr.x), v[0]);
+          v[1] = fmaf(d[1], bf16_hi(xr.x), v[1]);
+          v[2] = fmaf(d[2], bf16_lo(xr.y), v[2]);
+          v[3] = fmaf(d[3], bf16_hi(xr.y), v[3]);
         }
         if (zg) {
           const uint2 zr = *reinterpret_cast<const uint2*>(zg + o);
@@ -528,7 +540,8 @@ hipError_t launch_qn(const SsdParams& p, hipStream_t stream) {
   const int64_t nch = (p.L + Q - 1) / Q;
   hipLaunchKernelGGL((ssd_cumsum_kernel<Q>), dim3((unsigned)p.H, (unsigned)nch, (unsigned)p.B), dim3(256), 0,
                      stream, p);
-  hipLaunchKernelGGL((ssd_prep_kernel<Q, N>), dim3(4, (unsigned)nch, (unsigned)p.B), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((ssd_prep_kernel<Q, N>), dim3(4, (unsigned)nch, (unsigned)(p.B * p.G)), dim3(256), 0, stream,
+                     p);
   hipLaunchKernelGGL((ssd_state_kernel<Q, N>), dim3((unsigned)p.H, (unsigned)p.B), dim3(512), 0, stream, p);
   hipLaunchKernelGGL((ssd_out_kernel<Q, N>), dim3((unsigned)p.H, (unsigned)nch, (unsigned)p.B), dim3(256), 0,
                      stream, p);
@@ -537,14 +550,14 @@ hipError_t launch_qn(const SsdParams& p, hipStream_t stream) {
 
 }  // namespace
 
-// Workspace: carried states (bf16), G per chunk (bf16), transposed B per chunk (bf16),
-// (S, phi) per chunk, head and token (float2), each 256-byte aligned.
+// Workspace: carried states (bf16), G per chunk and group (bf16), transposed B per chunk and
+// group (bf16), (S, phi) per chunk, head and token (float2), each 256-byte aligned.
 static size_t ssd_align(size_t n) { return (n + 255) & ~(size_t)255; }
 
-size_t ssd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t Q) {
+size_t ssd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q) {
   const int64_t nch = (L + Q - 1) / Q;
-  return ssd_align((size_t)(B * nch * H * P * N) * 2) + ssd_align((size_t)(B * nch * Q * Q) * 2) +
-         ssd_align((size_t)(B * nch * N * Q) * 2) + ssd_align((size_t)(B * nch * H * Q) * 8);
+  return ssd_align((size_t)(B * nch * H * P * N) * 2) + ssd_align((size_t)(B * G * nch * Q * Q) * 2) +
+         ssd_align((size_t)(B * G * nch * N * Q) * 2) + ssd_align((size_t)(B * nch * H * Q) * 8);
 }
 
 void ssd_workspace_carve(SsdParams& p, void* ws) {
@@ -553,9 +566,9 @@ void ssd_workspace_carve(SsdParams& p, void* ws) {
   p.ws_hin = base;
   base += ssd_align((size_t)(p.B * nch * p.H * p.P * p.N) * 2);
   p.ws_G = base;
-  base += ssd_align((size_t)(p.B * nch * p.Q * p.Q) * 2);
+  base += ssd_align((size_t)(p.B * p.G * nch * p.Q * p.Q) * 2);
   p.ws_Bt = base;
-  base += ssd_align((size_t)(p.B * nch * p.N * p.Q) * 2);
+  base += ssd_align((size_t)(p.B * p.G * nch * p.N * p.Q) * 2);
   p.ws_sphi = reinterpret_cast<float2*>(base);
 }
 

@@ -228,32 +228,41 @@ class SSDInputs:
     x: np.ndarray        # [B, L, H, P]
     delta: np.ndarray    # [B, L, H]
     A: np.ndarray        # [H] fp32
-    Bm: np.ndarray       # [B, L, N]
-    Cm: np.ndarray       # [B, L, N]
+    Bm: np.ndarray       # [B, L, N] (one group) or [B, L, G, N]
+    Cm: np.ndarray       # as Bm
     delta_bias: Optional[np.ndarray] = None
     delta_softplus: bool = False
-    Dskip: Optional[np.ndarray] = None   # [H]
+    Dskip: Optional[np.ndarray] = None   # [H] or [H, P]
     z: Optional[np.ndarray] = None       # [B, L, H, P]
     h0: Optional[np.ndarray] = None      # [B, H, P, N]
 
     @property
     def shape(self):
         Bsz, L, H, P = self.x.shape
-        return Bsz, L, H, P, self.Bm.shape[2]
+        return Bsz, L, H, P, self.Bm.shape[-1]
+
+    @property
+    def groups(self) -> int:
+        return self.Bm.shape[2] if self.Bm.ndim == 4 else 1
 
 
 def ssd_layer(seed: int = 4, Bsz: int = 2, L: int = 8192, H: int = 80, P: int = 64, N: int = 128,
               dtype: str = "bf16", gate: bool = False, dskip: bool = False,
-              h0: bool = False) -> SSDInputs:
+              h0: bool = False, groups: Optional[int] = None,
+              dskip_per_channel: bool = False) -> SSDInputs:
     """Mamba-2 chunked-form workload: x, B, C ~ N(0, 1); delta per (b, t, head) as scan_layer;
-    A_h = -U(1, 16)."""
+    A_h = -U(1, 16). groups=None gives B, C as [B, L, N]; groups=G gives [B, L, G, N].
+    dskip_per_channel draws D as [H, P] (implies a D term)."""
     x = draw_tokens(seed, TID_X, Bsz, L, H * P).reshape(Bsz, L, H, P)
     delta = clipped_softplus_normal(draw_tokens(seed, TID_DELTA, Bsz, L, H, loc=-4.0))
-    Bm = draw_tokens(seed, TID_B, Bsz, L, N)
-    Cm = draw_tokens(seed, TID_C, Bsz, L, N)
+    G = 1 if groups is None else groups
+    Bm = draw_tokens(seed, TID_B, Bsz, L, G * N)
+    Cm = draw_tokens(seed, TID_C, Bsz, L, G * N)
+    if groups is not None:
+        Bm, Cm = Bm.reshape(Bsz, L, G, N), Cm.reshape(Bsz, L, G, N)
     A = -draw_param(seed, TID_A, (H,), kind="uniform", loc=1.0, scale=16.0)
     z = draw_tokens(seed, TID_Z, Bsz, L, H * P).reshape(Bsz, L, H, P) if gate else None
-    Dp = draw_param(seed, TID_D, (H,)) if dskip else None
+    Dp = draw_param(seed, TID_D, (H, P) if dskip_per_channel else (H,)) if dskip or dskip_per_channel else None
     hinit = draw_param(seed, TID_CONVREG + 1, (Bsz, H, P, N), scale=0.5) if h0 else None
     return SSDInputs(dtype=dtype, x=store(x, dtype), delta=store(delta, dtype), A=A,
                      Bm=store(Bm, dtype), Cm=store(Cm, dtype), Dskip=Dp,

@@ -24,7 +24,8 @@ EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_last_error_detail",
            "ssm_scan_fwd_conv_workspace_bytes", "ssm_scan_fwd_conv",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd",
            "ssm_scan_bwd_segmented_workspace_bytes", "ssm_scan_bwd_segmented",
-           "ssm_state_update", "ssd_chunk_fwd_workspace_bytes", "ssd_chunk_fwd")
+           "ssm_state_update", "ssd_chunk_fwd_workspace_bytes", "ssd_chunk_fwd",
+           "ssd_chunk_fwd_grouped_workspace_bytes", "ssd_chunk_fwd_grouped")
 
 _lib = None
 
@@ -80,6 +81,11 @@ def load(path: str = LIB_PATH):
     lib.ssd_chunk_fwd.argtypes = [i64, i64, i64, i64, i64, i64, ci, vp, vp, vp, ci, vp, vp, vp, vp,
                                   vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_chunk_fwd.restype = ci
+    lib.ssd_chunk_fwd_grouped_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i64, ci]
+    lib.ssd_chunk_fwd_grouped_workspace_bytes.restype = sz
+    lib.ssd_chunk_fwd_grouped.argtypes = [i64, i64, i64, i64, i64, i64, i64, ci, vp, vp, vp, ci, vp, vp,
+                                          vp, vp, ci, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_chunk_fwd_grouped.restype = ci
     _lib = lib
     return lib
 
@@ -307,5 +313,41 @@ def ssd_chunk_fwd(x, delta, A, Bm, Cm, *, chunk: int = 256, delta_bias=None, del
     st = lib.ssd_chunk_fwd(Bsz, L, H, P, N, chunk, code, _p(x), _p(delta), _p(delta_bias),
                            int(bool(delta_softplus)), _p(A), _p(Bm), _p(Cm), _p(Dskip), _p(z),
                            _p(h0), _p(y), _p(h_last), _p(ws), nb, _stream(x))
+    _check(st)
+    return y, h_last
+
+
+def ssd_chunk_fwd_grouped(x, delta, A, Bm, Cm, *, chunk: int = 256, delta_bias=None,
+                          delta_softplus=False, Dskip=None, z=None, h0=None, return_state=True, y=None,
+                          ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Mamba-2 layer with grouped B and C: x, z [B, L, H, P]; delta [B, L, H]; A [H];
+    Bm, Cm [B, L, G, N] (head h reads group h // (H // G)); Dskip [H] or [H, P] -> (y, h_last)."""
+    lib = load()
+    Bsz, L, H, P = x.shape
+    if Bm.dim() != 4:
+        raise ValueError("Bm must be [B, L, G, N]")
+    G, N = Bm.shape[2], Bm.shape[3]
+    io = x.dtype
+    _dev(x, "x")
+    _dev(delta, "delta", io, (Bsz, L, H))
+    _dev(z, "z", io, (Bsz, L, H, P))
+    _dev(Bm, "Bm", io, (Bsz, L, G, N))
+    _dev(Cm, "Cm", io, (Bsz, L, G, N))
+    _dev(A, "A", torch.float32, (H,))
+    _dev(delta_bias, "delta_bias", torch.float32, (H,))
+    per_channel = Dskip is not None and Dskip.dim() == 2
+    _dev(Dskip, "Dskip", torch.float32, (H, P) if per_channel else (H,))
+    _dev(h0, "h0", torch.float32, (Bsz, H, P, N))
+    if y is None:
+        y = torch.empty_like(x)
+    h_last = torch.empty((Bsz, H, P, N), dtype=torch.float32, device=x.device) if return_state else None
+    code = _io_code(x)
+    nb = lib.ssd_chunk_fwd_grouped_workspace_bytes(Bsz, L, H, P, N, G, chunk, code)
+    if ws is None or ws.numel() < nb:
+        ws = workspace(nb, x.device)
+    st = lib.ssd_chunk_fwd_grouped(Bsz, L, H, P, N, G, chunk, code, _p(x), _p(delta), _p(delta_bias),
+                                   int(bool(delta_softplus)), _p(A), _p(Bm), _p(Cm), _p(Dskip),
+                                   int(per_channel), _p(z), _p(h0), _p(y), _p(h_last), _p(ws), nb,
+                                   _stream(x))
     _check(st)
     return y, h_last

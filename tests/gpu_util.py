@@ -163,21 +163,45 @@ def step_smoke(Bsz=4, D=64, N=16, dtype="bf16", seed=3):
 
 
 # ----------------------------------------------------------------------------- SSD
-def ssd_on_gpu(inp: inputs.SSDInputs, chunk=256, return_state=True):
-    y, hl = ssm.ssd_chunk_fwd(dev(inp.x), dev(inp.delta), dev(inp.A), dev(inp.Bm), dev(inp.Cm),
-                              chunk=chunk, delta_bias=dev(inp.delta_bias),
-                              delta_softplus=inp.delta_softplus, Dskip=dev(inp.Dskip), z=dev(inp.z),
-                              h0=dev(inp.h0), return_state=return_state)
+def ssd_on_gpu(inp: inputs.SSDInputs, chunk=256, return_state=True, grouped=None):
+    """grouped=None: ssd_chunk_fwd_grouped for grouped B/C or per-channel D, else ssd_chunk_fwd."""
+    if grouped is None:
+        grouped = inp.Bm.ndim == 4 or (inp.Dskip is not None and inp.Dskip.ndim == 2)
+    Bm, Cm = inp.Bm, inp.Cm
+    if grouped and Bm.ndim == 3:
+        Bm, Cm = Bm[:, :, None], Cm[:, :, None]
+    fn = ssm.ssd_chunk_fwd_grouped if grouped else ssm.ssd_chunk_fwd
+    y, hl = fn(dev(inp.x), dev(inp.delta), dev(inp.A), dev(Bm), dev(Cm),
+               chunk=chunk, delta_bias=dev(inp.delta_bias),
+               delta_softplus=inp.delta_softplus, Dskip=dev(inp.Dskip), z=dev(inp.z),
+               h0=dev(inp.h0), return_state=return_state)
     torch.cuda.synchronize()
     return host(y), host(hl)
 
 
 def ssd_oracle(inp: inputs.SSDInputs, heads=None):
+    """The oracle on every head, or on the listed heads only (each with its own group's B, C)."""
     w = lambda a: inputs.widen(a, inp.dtype)
-    sel = (lambda a, ax: a if a is None or heads is None else np.take(a, heads, axis=ax))
-    return oracle.ssd(sel(w(inp.x), 2), sel(w(inp.delta), 2), sel(inp.A, 0), w(inp.Bm), w(inp.Cm),
-                      delta_bias=sel(inp.delta_bias, 0), delta_softplus=inp.delta_softplus,
-                      Dskip=sel(inp.Dskip, 0), z=sel(w(inp.z), 2), h0=sel(inp.h0, 1))
+    H = inp.x.shape[2]
+    hs = np.arange(H) if heads is None else np.asarray(heads)
+    G = inp.groups
+    if heads is None or G == 1:
+        sel = (lambda a, ax: a if a is None or heads is None else np.take(a, hs, axis=ax))
+        Bm, Cm = w(inp.Bm), w(inp.Cm)
+        return oracle.ssd(sel(w(inp.x), 2), sel(w(inp.delta), 2), sel(inp.A, 0), Bm, Cm,
+                          delta_bias=sel(inp.delta_bias, 0), delta_softplus=inp.delta_softplus,
+                          Dskip=sel(inp.Dskip, 0), z=sel(w(inp.z), 2), h0=sel(inp.h0, 1))
+    ys, hls = [], []
+    for h in hs:
+        grp = h // (H // G)
+        one = lambda a, ax: None if a is None else np.take(a, [h], axis=ax)
+        y, hl = oracle.ssd(one(w(inp.x), 2), one(w(inp.delta), 2), one(inp.A, 0),
+                           w(inp.Bm)[:, :, grp], w(inp.Cm)[:, :, grp],
+                           delta_bias=one(inp.delta_bias, 0), delta_softplus=inp.delta_softplus,
+                           Dskip=one(inp.Dskip, 0), z=one(w(inp.z), 2), h0=one(inp.h0, 1))
+        ys.append(y)
+        hls.append(hl)
+    return np.concatenate(ys, axis=2), np.concatenate(hls, axis=1)
 
 
 def ssd_parity(inp, gpu_out, heads=None) -> float:

@@ -171,6 +171,31 @@ def test_ssd_rejects(lib, kw, expect):
     assert ssd_call(lib, **kw) == expect
 
 
+def ssd_grouped_call(lib, B=1, L=512, H=4, P=64, N=128, G=2, chunk=256, io=BF16, Dskip=None, dpc=0, wsb=1 << 40):
+    return lib.ssd_chunk_fwd_grouped(B, L, H, P, N, G, chunk, io, fake(A_), fake(2 * A_), None, 0, fake(3 * A_),
+                                     fake(4 * A_), fake(5 * A_), fake(Dskip) if Dskip else None, dpc, None, None,
+                                     fake(6 * A_), None, fake(9 * A_), wsb, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(G=0), INVALID), (dict(G=3), INVALID), (dict(G=8), INVALID), (dict(B=40000, G=2), UNSUPPORTED),
+    (dict(L=65536 * 64 + 1, chunk=64), UNSUPPORTED), (dict(Dskip=7 * A_ + 4, dpc=1), INVALID),
+    (dict(wsb=16), WS_SMALL), (dict(N=96), UNSUPPORTED),
+])
+def test_ssd_grouped_rejects(lib, kw, expect):
+    assert ssd_grouped_call(lib, **kw) == expect
+
+
+def test_ssd_grouped_workspace(lib):
+    """Per group: C B^T and transposed B per chunk; G = 1 is the ungrouped layout."""
+    one = lib.ssd_chunk_fwd_workspace_bytes(2, 8192, 80, 64, 128, 256, BF16)
+    assert lib.ssd_chunk_fwd_grouped_workspace_bytes(2, 8192, 80, 64, 128, 1, 256, BF16) == one
+    nch = 8192 // 256
+    g8 = lib.ssd_chunk_fwd_grouped_workspace_bytes(2, 8192, 80, 64, 128, 8, 256, BF16)
+    assert g8 - one >= 2 * 7 * nch * (256 * 256 * 2 + 128 * 256 * 2)
+    assert lib.ssd_chunk_fwd_grouped_workspace_bytes(2, 8192, 80, 64, 128, 0, 256, BF16) == 0
+
+
 def test_binding_refuses_host_tensors(lib):
     import torch
     x = torch.zeros(1, 16, 64)

@@ -64,6 +64,8 @@ def _configure(lib):
     lib.oracle_step.restype = None
     lib.oracle_ssd.argtypes = [i64, i64, i64, i64, i64, i64] + [vp, vp, vp, ci] + [vp] * 4 + [ci] + [vp] * 4
     lib.oracle_ssd.restype = None
+    lib.oracle_ssd_bwd.argtypes = [i64] * 6 + [vp, vp, vp, ci] + [vp] * 4 + [ci] + [vp] * 13
+    lib.oracle_ssd_bwd.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ci
     lib.oracle_set_num_threads.argtypes = [ci]
@@ -103,6 +105,9 @@ class Variant:
 
     def ssd(self, *a, **k):
         return ssd(*a, _lib=self._lib, **k)
+
+    def ssd_bwd(self, *a, **k):
+        return ssd_bwd(*a, _lib=self._lib, **k)
 
 
 def compile_source(src_text: str, so_path: str) -> str:
@@ -289,6 +294,48 @@ def ssd(x, delta, A, Bm, Cm, *, delta_bias=None, delta_softplus=False, Dskip=Non
     (_lib or _load()).oracle_ssd(Bsz, L, H, P, N, G, _p(x), _p(delta), _p(delta_bias), int(bool(delta_softplus)),
                                  _p(A), _p(Bm), _p(Cm), _p(Dskip), int(dpc), _p(z), _p(h0), _p(y), _p(h_last))
     return y, h_last
+
+
+def ssd_bwd(x, delta, A, Bm, Cm, dy, *, delta_bias=None, delta_softplus=False, Dskip=None, z=None,
+            h0=None, dh_last=None, _lib=None):
+    """Gradients of ``ssd`` for the loss L with dL/dy = dy [B, L, H, P] and dL/dh_last = dh_last
+    [B, H, P, N] (None: zero). Returns a dict of fp64 arrays: dx, dz (None without z) [B, L, H, P];
+    ddelta [B, L, H]; dA, ddelta_bias [H]; dBm, dCm shaped like Bm, Cm (summed over the heads of
+    each group); dDskip [H] or [H, P] like Dskip ([H] when Dskip is None); dh0 [B, H, P, N]. Each is
+    the gradient at the given value, at zero where the optional input is absent."""
+    x = _f64(x)
+    Bsz, L, H, P = x.shape
+    Bm = _f64(Bm)
+    grouped = Bm.ndim == 4
+    if not grouped:
+        Bm = Bm[:, :, None, :]
+    G, N = Bm.shape[2], Bm.shape[3]
+    if H % G:
+        raise ValueError("oracle.ssd_bwd: the head count must be a multiple of the group count")
+    Bm = _f64(Bm, (Bsz, L, G, N))
+    Cm = _f64(Cm)
+    Cm = _f64(Cm[:, :, None, :] if Cm.ndim == 3 else Cm, (Bsz, L, G, N))
+    delta = _f64(delta, (Bsz, L, H))
+    A = _f64(A, (H,))
+    delta_bias = _f64(delta_bias, (H,))
+    dpc = Dskip is not None and np.ndim(Dskip) == 2
+    Dskip = _f64(Dskip, (H, P) if dpc else (H,))
+    z = _f64(z, (Bsz, L, H, P))
+    h0 = _f64(h0, (Bsz, H, P, N))
+    dy = _f64(dy, (Bsz, L, H, P))
+    dh_last = _f64(dh_last, (Bsz, H, P, N))
+    out = dict(dx=np.empty((Bsz, L, H, P)), ddelta=np.empty((Bsz, L, H)), dA=np.empty(H),
+               dBm=np.empty((Bsz, L, G, N)), dCm=np.empty((Bsz, L, G, N)),
+               dDskip=np.empty((H, P) if dpc else H), ddelta_bias=np.empty(H),
+               dz=np.empty((Bsz, L, H, P)) if z is not None else None, dh0=np.empty((Bsz, H, P, N)))
+    (_lib or _load()).oracle_ssd_bwd(
+        Bsz, L, H, P, N, G, _p(x), _p(delta), _p(delta_bias), int(bool(delta_softplus)), _p(A), _p(Bm),
+        _p(Cm), _p(Dskip), int(dpc), _p(z), _p(h0), _p(dy), _p(dh_last), _p(out["dx"]), _p(out["ddelta"]),
+        _p(out["dA"]), _p(out["dBm"]), _p(out["dCm"]), _p(out["dDskip"]), _p(out["ddelta_bias"]),
+        _p(out["dz"]), _p(out["dh0"]))
+    if not grouped:
+        out["dBm"], out["dCm"] = out["dBm"][:, :, 0], out["dCm"][:, :, 0]
+    return out
 
 
 def ssd_quadratic(x, delta, A, Bm, Cm, *, delta_bias=None, delta_softplus=False,

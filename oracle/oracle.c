@@ -1,6 +1,7 @@
 /*
  * oracle.c -- plain, slow, fp64 CPU oracle for the selective state-space (S6) forward pass and
- * its gradients, its one-token decode step, and the Mamba-2 scalar-A (SSD) layer.
+ * its gradients, its one-token decode step, and the Mamba-2 scalar-A (SSD) layer and its
+ * gradients.
  *
  * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU-baseline leg
  * may load this library. It shares no code, header, table or constant with the GPU library;
@@ -26,7 +27,8 @@
  * Readings taken where the pages are silent (each is listed in the design notes):
  *   - A is diagonal, given as A[d, n] (the pages' discretisation specialised to diagonal A:
  *     Bbar_n = expm1(Delta A_n) / A_n * B_n, with the limit Delta * B_n when A_n == 0).
- *   - B_t and C_t are N-wide per token and shared by all channels (and by all SSD heads).
+ *   - B_t and C_t are N-wide per token and shared by all channels (and by all SSD heads, or
+ *     by the heads of one group when the SSD layer has G groups: head h uses group h / (H / G)).
  *   - D multiplies the SSM input of the channel; NULL means no D term.
  *   - The optional gate is applied after the D term: y <- y * z * sigmoid(z). NULL z: no gate.
  *   - The initial state is zero unless h0 is given.
@@ -35,6 +37,7 @@
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -332,6 +335,175 @@ void oracle_ssd(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t N, int64_t
       free(S);
     }
   }
+}
+
+/*
+ * oracle_ssd_bwd: the gradients of oracle_ssd's map (B and C in G groups of heads, D per head or
+ * per channel) for a loss with dL/dy = dy (the gated output) and dL/dh_last = dh_last (NULL: 0).
+ * Reverse mode of the plain recurrence, as oracle_scan_bwd does for the selective scan, with the
+ * state of a head a P x N matrix: per (b, head) the states are rebuilt from checkpoints kept every
+ * 64 steps, then time is walked backwards with g = dL/dh_t:
+ *   dL/dh_t   = g + ybar_t C_t^T            (ybar = dy before the gate's factor z sigma(z))
+ *   dC_t     += h_t^T ybar_t                dB_t += phi (dL/dh_t)^T x_t
+ *   dx_t      = phi (dL/dh_t) B_t + D ybar_t
+ *   dDelta_t  = sum (dL/dh_t) o (a abar h_{t-1} + abar x_t B_t^T)
+ *   dA       += sum (dL/dh_t) o (Delta abar h_{t-1} + dphi/da x_t B_t^T)
+ *   g         = abar dL/dh_t
+ * with abar = exp(Delta a), phi = expm1(Delta a) / a, dphi/da = (Delta abar - phi) / a
+ * (Delta^2 / 2 at a = 0); ddelta is taken through the softplus when it is on. dB and dC are
+ * summed over the heads of a group, dA, dD and ddelta_bias over batch rows (and tokens), each in
+ * a fixed order.
+ *   dx, dz : [Bsz, L, H, P]   ddelta : [Bsz, L, H]   dA, ddelta_bias : [H]
+ *   dBm, dCm : [Bsz, L, G, N]   dDskip : as Dskip   dh0 : [Bsz, H, P, N]
+ * Gradients of absent optional inputs (dz without z, dDskip without D, ...) may be NULL; those
+ * given for absent inputs are the derivatives at zero.
+ */
+void oracle_ssd_bwd(int64_t Bsz, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
+                    const double* x, const double* delta, const double* delta_bias, int delta_softplus,
+                    const double* A, const double* Bm, const double* Cm, const double* Dskip,
+                    int dskip_per_channel, const double* z, const double* h0, const double* dy,
+                    const double* dh_last, double* dx, double* ddelta, double* dA, double* dBm,
+                    double* dCm, double* dDskip, double* ddelta_bias, double* dz, double* dh0) {
+  const int64_t K = 64;                        /* checkpoint spacing */
+  const int64_t nck = (L + K - 1) / K;
+  const int64_t PN = P * N;
+  /* per (b, head) partial sums, reduced in a fixed order at the end */
+  double* pB = (double*)calloc((size_t)(Bsz * H * L * N) + 1, sizeof(double));
+  double* pC = (double*)calloc((size_t)(Bsz * H * L * N) + 1, sizeof(double));
+  double* pA = (double*)calloc((size_t)(Bsz * H) + 1, sizeof(double));
+  double* pb = (double*)calloc((size_t)(Bsz * H) + 1, sizeof(double));
+  double* pD = (double*)calloc((size_t)(Bsz * H * P) + 1, sizeof(double));
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int64_t b = 0; b < Bsz; ++b) {
+    for (int64_t hd = 0; hd < H; ++hd) {
+      const double a = A[hd];
+      const int64_t grp = hd / (H / G);
+      double* ck = (double*)malloc((size_t)(nck * PN + 1) * sizeof(double));  /* state before token s K */
+      double* hs = (double*)malloc((size_t)((K + 1) * PN) * sizeof(double));  /* hs[k] = state before token s K + k */
+      double* g = (double*)malloc((size_t)PN * sizeof(double));
+      double* ybar = (double*)malloc((size_t)P * sizeof(double));
+      double* gx = (double*)malloc((size_t)P * sizeof(double));
+      for (int64_t i = 0; i < PN; ++i) hs[i] = h0 ? h0[(b * H + hd) * PN + i] : 0.0;
+      /* forward: keep the checkpoints */
+      for (int64_t t = 0; t < L; ++t) {
+        if (t % K == 0) memcpy(ck + (t / K) * PN, hs, (size_t)PN * sizeof(double));
+        const double dt = o_step_size(delta[(b * L + t) * H + hd], delta_bias, hd, delta_softplus);
+        const double abar = exp(dt * a), phi = o_zoh_scale(dt, a);
+        const double* Bt = Bm + ((b * L + t) * G + grp) * N;
+        const double* xt = x + ((b * L + t) * H + hd) * P;
+        for (int64_t p = 0; p < P; ++p)
+          for (int64_t n = 0; n < N; ++n) hs[p * N + n] = abar * hs[p * N + n] + phi * xt[p] * Bt[n];
+      }
+      for (int64_t i = 0; i < PN; ++i) g[i] = dh_last ? dh_last[(b * H + hd) * PN + i] : 0.0;
+      /* backward, one checkpoint segment at a time */
+      for (int64_t sgm = nck - 1; sgm >= 0; --sgm) {
+        const int64_t t0 = sgm * K, t1 = t0 + K < L ? t0 + K : L;
+        memcpy(hs, ck + sgm * PN, (size_t)PN * sizeof(double));
+        for (int64_t t = t0; t < t1; ++t) {
+          const double dt = o_step_size(delta[(b * L + t) * H + hd], delta_bias, hd, delta_softplus);
+          const double abar = exp(dt * a), phi = o_zoh_scale(dt, a);
+          const double* Bt = Bm + ((b * L + t) * G + grp) * N;
+          const double* xt = x + ((b * L + t) * H + hd) * P;
+          double* hn = hs + (t - t0 + 1) * PN;
+          const double* hp = hs + (t - t0) * PN;
+          for (int64_t p = 0; p < P; ++p)
+            for (int64_t n = 0; n < N; ++n) hn[p * N + n] = abar * hp[p * N + n] + phi * xt[p] * Bt[n];
+        }
+        for (int64_t t = t1 - 1; t >= t0; --t) {
+          const int64_t it = (b * L + t) * H + hd;      /* token-head index */
+          const double u = delta[it] + (delta_bias ? delta_bias[hd] : 0.0);
+          const double dt = delta_softplus ? o_softplus(u) : u;
+          const double abar = exp(dt * a), phi = o_zoh_scale(dt, a);
+          const double dphi_da = a == 0.0 ? 0.5 * dt * dt : (dt * abar - phi) / a;
+          const double* Bt = Bm + ((b * L + t) * G + grp) * N;
+          const double* Ct = Cm + ((b * L + t) * G + grp) * N;
+          const double* xt = x + it * P;
+          const double* hcur = hs + (t - t0 + 1) * PN;
+          const double* hprev = hs + (t - t0) * PN;
+          double* pBt = pB + ((b * H + hd) * L + t) * N;
+          double* pCt = pC + ((b * H + hd) * L + t) * N;
+          for (int64_t p = 0; p < P; ++p) {
+            const double Dp = Dskip ? (dskip_per_channel ? Dskip[hd * P + p] : Dskip[hd]) : 0.0;
+            const double g_out = dy[it * P + p];
+            ybar[p] = g_out;
+            if (z) {
+              double yp = Dp * xt[p];
+              for (int64_t n = 0; n < N; ++n) yp += Ct[n] * hcur[p * N + n];
+              const double zt = z[it * P + p], sg = o_sigmoid(zt);
+              if (dz) dz[it * P + p] = g_out * yp * sg * (1.0 + zt * (1.0 - sg));
+              ybar[p] = g_out * zt * sg;
+            }
+            gx[p] = Dp * ybar[p];
+            pD[(b * H + hd) * P + p] += ybar[p] * xt[p];
+          }
+          double gdt = 0.0, ga = 0.0;
+          for (int64_t p = 0; p < P; ++p) {
+            for (int64_t n = 0; n < N; ++n) {
+              const double gn = g[p * N + n] + Ct[n] * ybar[p];   /* dL/dh_t */
+              pCt[n] += ybar[p] * hcur[p * N + n];
+              pBt[n] += gn * phi * xt[p];
+              gx[p] += gn * phi * Bt[n];
+              gdt += gn * (a * abar * hprev[p * N + n] + abar * xt[p] * Bt[n]);
+              ga += gn * (dt * abar * hprev[p * N + n] + dphi_da * xt[p] * Bt[n]);
+              g[p * N + n] = abar * gn;                         /* on to dL/dh_{t-1} */
+            }
+          }
+          for (int64_t p = 0; p < P; ++p) dx[it * P + p] = gx[p];
+          const double gu = delta_softplus ? gdt * o_sigmoid(u) : gdt;
+          ddelta[it] = gu;
+          pb[b * H + hd] += gu;
+          pA[b * H + hd] += ga;
+        }
+      }
+      if (dh0)
+        for (int64_t i = 0; i < PN; ++i) dh0[(b * H + hd) * PN + i] = g[i];
+      free(gx);
+      free(ybar);
+      free(g);
+      free(hs);
+      free(ck);
+    }
+  }
+  for (int64_t b = 0; b < Bsz; ++b)
+    for (int64_t t = 0; t < L; ++t)
+      for (int64_t k = 0; k < G; ++k)
+        for (int64_t n = 0; n < N; ++n) {
+          double sb = 0.0, sc = 0.0;
+          for (int64_t hd = k * (H / G); hd < (k + 1) * (H / G); ++hd) {
+            sb += pB[((b * H + hd) * L + t) * N + n];
+            sc += pC[((b * H + hd) * L + t) * N + n];
+          }
+          dBm[((b * L + t) * G + k) * N + n] = sb;
+          dCm[((b * L + t) * G + k) * N + n] = sc;
+        }
+  for (int64_t hd = 0; hd < H; ++hd) {
+    double sa = 0.0, sb = 0.0;
+    for (int64_t b = 0; b < Bsz; ++b) {
+      sa += pA[b * H + hd];
+      sb += pb[b * H + hd];
+    }
+    dA[hd] = sa;
+    if (ddelta_bias) ddelta_bias[hd] = sb;
+    if (dDskip) {
+      if (dskip_per_channel) {
+        for (int64_t p = 0; p < P; ++p) {
+          double s = 0.0;
+          for (int64_t b = 0; b < Bsz; ++b) s += pD[(b * H + hd) * P + p];
+          dDskip[hd * P + p] = s;
+        }
+      } else {
+        double s = 0.0;
+        for (int64_t b = 0; b < Bsz; ++b)
+          for (int64_t p = 0; p < P; ++p) s += pD[(b * H + hd) * P + p];
+        dDskip[hd] = s;
+      }
+    }
+  }
+  free(pD);
+  free(pb);
+  free(pA);
+  free(pC);
+  free(pB);
 }
 
 /* Thread count for the following OpenMP regions (n >= 1); used to time a single core. The

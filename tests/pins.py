@@ -473,3 +473,84 @@ def check_bwd_finite_differences(scan_bwd, scan, seed=40, eps=1e-6):
 
 
 BWD_FD_TOL = 1e-7
+
+
+# ----------------------------------------------------------------------------- SSD gradients
+def check_ssd_bwd_finite_differences(ssd_bwd, ssd, seed=50, eps=3e-6):
+    """The SSD gradients are the derivative of the forward map: every entry of every gradient
+    equals the central difference of the forward oracle's loss sum(dy * y) + sum(dh_last * h_last).
+    Cases: (i) 4 heads in 2 groups, per-channel D, softplus with bias, gate, h0, dh_last, one A of
+    exactly zero, and L = 70 so that the state is rebuilt from more than one checkpoint (every 64
+    steps); (ii) one group given as [B, L, N], plain Delta, per-head D, no gate, h0 or dh_last --
+    the gradients of the absent bias and h0 are compared with differences taken at zeros.
+    eps = 3e-6: the loss sums hundreds of outputs, and at 1e-6 its fp64 rounding over 2 eps reaches
+    1e-8 of the small dA of case (ii); agreement is then within SSD_BWD_FD_TOL."""
+    worst = 0.0
+    cases = (dict(L=70, H=4, P=2, N=3, groups=2, dskip_per_channel=True),
+             dict(L=9, H=2, P=3, N=2, gate=False, softplus=False))
+    for k, kw in enumerate(cases):
+        case = tiny_ssd_case(seed + k, Bsz=2, **kw)
+        Bsz, L, H, P = case["x"].shape
+        N = case["Bm"].shape[-1]
+        g = RNG(seed + 10 + k)
+        if k == 0:
+            case["A"][1] = 0.0
+            case["h0"] = g.standard_normal((Bsz, H, P, N))
+        else:
+            case["delta"] = np.abs(case["delta"]) * 0.3 + 0.05
+            case["delta_bias"] = None
+        dy = g.standard_normal(case["x"].shape)
+        dh_last = g.standard_normal((Bsz, H, P, N)) if k == 0 else None
+        grads = ssd_bwd(dy=dy, dh_last=dh_last, **case)
+        full = dict(case)
+        for key, shape in (("delta_bias", (H,)), ("h0", (Bsz, H, P, N))):
+            if full.get(key) is None:
+                full[key] = np.zeros(shape)
+        for key, gkey in _GRAD_OF:
+            if full.get(key) is None:
+                continue
+            arr = full[key] = np.array(full[key], dtype=np.float64)
+            fd = np.zeros_like(arr)
+            for idx in np.ndindex(arr.shape):
+                v = arr[idx]
+                arr[idx] = v + eps
+                lp = _fd_loss(ssd, full, dy, dh_last)
+                arr[idx] = v - eps
+                lm = _fd_loss(ssd, full, dy, dh_last)
+                arr[idx] = v
+                fd[idx] = (lp - lm) / (2 * eps)
+            worst = max(worst, rel_err(grads[gkey], fd))
+    return worst
+
+
+def check_ssd_bwd_equals_scan_bwd(ssd_bwd, scan_bwd, seed=52):
+    """The SSD layer is the selective scan with A[d, n] = A_h and Delta[b, t, d] = Delta[b, t, h]
+    for the channels d = (h, p) of head h, so its gradients are the scan's gathered per head:
+    dx, dz, dB, dC, dh0 equal; ddelta, dA, ddelta_bias, dD (per head) are the scan's sums over the
+    head's channels (and over the N states for dA)."""
+    c = tiny_ssd_case(seed, L=23)
+    Bsz, L, H, P = c["x"].shape
+    N = c["Bm"].shape[2]
+    g = RNG(seed + 1)
+    h0 = g.standard_normal((Bsz, H, P, N))
+    dy = g.standard_normal(c["x"].shape)
+    dhl = g.standard_normal((Bsz, H, P, N))
+    gs = ssd_bwd(h0=h0, dy=dy, dh_last=dhl, **c)
+    sc = dict(x=c["x"].reshape(Bsz, L, H * P), delta=np.repeat(c["delta"], P, axis=2),
+              A=np.repeat(c["A"], P)[:, None] * np.ones((1, N)), Bm=c["Bm"], Cm=c["Cm"],
+              delta_bias=np.repeat(c["delta_bias"], P), delta_softplus=c["delta_softplus"],
+              Dskip=np.repeat(c["Dskip"], P), z=c["z"].reshape(Bsz, L, H * P), h0=h0.reshape(Bsz, H * P, N))
+    gc = scan_bwd(dy=dy.reshape(Bsz, L, H * P), dh_last=dhl.reshape(Bsz, H * P, N), **sc)
+    per_head = lambda a, ax: a.reshape(a.shape[:ax] + (H, P) + a.shape[ax + 1:]).sum(axis=ax + 1)
+    return max(
+        rel_err(gs["dx"].reshape(Bsz, L, H * P), gc["dx"]),
+        rel_err(gs["dz"].reshape(Bsz, L, H * P), gc["dz"]),
+        rel_err(gs["dBm"], gc["dBm"]), rel_err(gs["dCm"], gc["dCm"]),
+        rel_err(gs["dh0"].reshape(Bsz, H * P, N), gc["dh0"]),
+        rel_err(gs["ddelta"], per_head(gc["ddelta"], 2)),
+        rel_err(gs["dA"], per_head(gc["dA"].sum(axis=1), 0)),
+        rel_err(gs["ddelta_bias"], per_head(gc["ddelta_bias"], 0)),
+        rel_err(gs["dDskip"], per_head(gc["dDskip"], 0)))
+
+
+SSD_BWD_FD_TOL = 2e-7

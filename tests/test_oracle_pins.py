@@ -125,6 +125,20 @@ BWD_MUTANTS = {
     "bwd_readout_adjoint_late": [("const double gn = g[n] + Ct[n] * gy;", "const double gn = g[n];")],
 }
 
+SSD_BWD_MUTANTS = {
+    "ssd_bwd_dC_previous_state": [("pCt[n] += ybar[p] * hcur[p * N + n];", "pCt[n] += ybar[p] * hprev[p * N + n];")],
+    "ssd_bwd_group_members": [("for (int64_t hd = k * (H / G); hd < (k + 1) * (H / G); ++hd) {",
+                               "for (int64_t hd = k; hd < H; hd += G) {")],
+    "ssd_bwd_checkpoint_stale": [("memcpy(hs, ck + sgm * PN, (size_t)PN * sizeof(double));",
+                                  "memcpy(hs, ck, (size_t)PN * sizeof(double));")],
+    "ssd_bwd_adjoint_not_decayed": [("g[p * N + n] = abar * gn;", "g[p * N + n] = gn;")],
+    "ssd_bwd_dD_channel_index": [("for (int64_t b = 0; b < Bsz; ++b) s += pD[(b * H + hd) * P + p];",
+                                  "for (int64_t b = 0; b < Bsz; ++b) s += pD[(b * H + hd) * P];")],
+    "ssd_bwd_ddelta_drops_input_term": [("gdt += gn * (a * abar * hprev[p * N + n] + abar * xt[p] * Bt[n]);",
+                                         "gdt += gn * (a * abar * hprev[p * N + n]);")],
+    "ssd_bwd_dz_without_D": [("double yp = Dp * xt[p];", "double yp = 0.0;")],
+}
+
 STEP_MUTANTS = {
     "conv_shift_wrong_way": [("for (int64_t k = 0; k + 1 < W; ++k) reg[k] = reg[k + 1];\n        reg[W - 1] = x[io];",
                               "for (int64_t k = W - 1; k > 0; --k) reg[k] = reg[k - 1];\n        reg[0] = x[io];")],
@@ -194,6 +208,14 @@ def test_ssd_groups():
     assert pins.check_ssd_groups(oracle.ssd) <= 1e-12
 
 
+def test_ssd_bwd_finite_differences():
+    assert pins.check_ssd_bwd_finite_differences(oracle.ssd_bwd, oracle.ssd) <= pins.SSD_BWD_FD_TOL
+
+
+def test_ssd_bwd_equals_scan_bwd():
+    assert pins.check_ssd_bwd_equals_scan_bwd(oracle.ssd_bwd, oracle.scan_bwd) <= 1e-12
+
+
 @pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
 def test_bwd_mutant_caught(tmp_path, name):
     import warnings
@@ -210,3 +232,10 @@ def test_conv_mutant_caught(tmp_path, name):
     v = _mutant(tmp_path, name, CONV_MUTANTS[name])
     err = pins.check_conv_prefill(v.conv1d, v.scan_conv, oracle.step)
     assert err > 1e-12, name
+
+
+@pytest.mark.parametrize("name", sorted(SSD_BWD_MUTANTS))
+def test_ssd_bwd_mutant_caught(tmp_path, name):
+    v = _mutant(tmp_path, name, SSD_BWD_MUTANTS[name])
+    err = pins.check_ssd_bwd_finite_differences(v.ssd_bwd, oracle.ssd)
+    assert not (err <= pins.SSD_BWD_FD_TOL), "planted mistake %s passed the gradient pin" % name

@@ -19,6 +19,9 @@
  *                     (C_i . B_j times all decay between steps j and i); the sequence is cut
  *                     into chunks, each chunk is a masked matrix product, and only the state
  *                     passes between chunks.
+ *   ssd_chunk_bwd     gradients of ssd_chunk_fwd_grouped, with the same chunked split: within a
+ *                     chunk every contraction is a masked matrix product on the matrix cores;
+ *                     between chunks only the state (forwards) and its adjoint (backwards) pass.
  *   ssd_chunk_fwd_grouped  the same layer with B and C given per group of heads and D per head
  *                     or per channel. The page likens the layer to masked attention (C as the
  *                     queries, B as the keys, the input as the values); groups let several heads
@@ -291,6 +294,49 @@ ssm_status ssd_chunk_fwd_grouped(int64_t B, int64_t L, int64_t H, int64_t P, int
                                  const float* Dskip, int dskip_per_channel, const void* z,
                                  const float* h0, void* y, float* h_last, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/*
+ * ssd_chunk_bwd -- gradients of ssd_chunk_fwd_grouped (training): the derivative of the forward
+ * map for a loss L, given dy = dL/dy and optionally dh_last = dL/dh_last. Same page and section
+ * as ssd_chunk_fwd: inside each chunk the products are masked matrix products; between chunks
+ * the state is carried forwards and its adjoint backwards. The state entering each chunk is
+ * recomputed, not taken from the forward call.
+ *
+ *   forward inputs : as ssd_chunk_fwd_grouped (x, delta, delta_bias, delta_softplus, A, Bm, Cm
+ *                    [B, L, G, N], Dskip with dskip_per_channel, z, h0), unchanged
+ *   dy             : [B, L, H, P]  io_dtype     dL/dy (y after the gate)
+ *   dh_last        : [B, H, P, N]  float32 or NULL (zero)
+ *   dx, dz         : [B, L, H, P]  io_dtype     (out) dz required when z is given, else ignored
+ *   ddelta         : [B, L, H]     io_dtype     (out) gradient of the raw delta (through the
+ *                                               softplus when it is on)
+ *   dA             : [H]           float32      (out)
+ *   dBm, dCm       : [B, L, G, N]  float32      (out) summed over the heads of each group
+ *   dDskip         : float32 or NULL (out) [H, P] when dskip_per_channel, else [H]; the
+ *                    gradient at Dskip, at zero if Dskip is NULL
+ *   ddelta_bias    : [H] float32 or NULL (out; at delta_bias or zero)
+ *   dh0            : [B, H, P, N] float32 or NULL (out; at h0 or at the zero state)
+ *
+ *   The backward works in chunks of 64 tokens whatever chunk the forward used (the result does
+ *   not depend on the chunk). Sums over heads (dBm, dCm), over batch rows and time (dA, dDskip,
+ *   ddelta_bias) are formed in a fixed order, so repeated calls give identical bits.
+ *   Requirements: io_dtype SSM_BF16; P == 64; N in {64, 128}; G >= 1 divides H; B * G <= 65535,
+ *   H <= 65535, at most 65535 chunks of 64 tokens; no output may overlap an input or another
+ *   output; the workspace (ssd_chunk_bwd_workspace_bytes(): two bf16 states per chunk and
+ *   head, per-head float32 partial dB and dC, and small per-chunk terms) is required whenever
+ *   B, L > 0. B == 0 or L == 0 writes zeros to dA, dDskip, ddelta_bias and (B > 0) dh0 =
+ *   dh_last or zeros.
+ */
+size_t ssd_chunk_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N,
+                                     int64_t G, ssm_dtype io_dtype);
+
+ssm_status ssd_chunk_bwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
+                         ssm_dtype io_dtype, const void* x, const void* delta,
+                         const float* delta_bias, int delta_softplus, const float* A,
+                         const void* Bm, const void* Cm, const float* Dskip,
+                         int dskip_per_channel, const void* z, const float* h0, const void* dy,
+                         const float* dh_last, void* dx, void* ddelta, float* dA, float* dBm,
+                         float* dCm, float* dDskip, float* ddelta_bias, void* dz, float* dh0,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -231,6 +231,14 @@ ssm_status scan_bwd_common(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype
   return from_hip(ssm::launch_scan_bwd(p, st), "ssm_scan_bwd launch");
 }
 
+// Heads per workgroup in the SSD backward's main pass (their dB and dC are summed in registers
+// before one partial per workgroup is written): a divisor of the heads per group.
+int64_t ssd_bwd_heads_per_wg(int64_t H, int64_t G) {
+  (void)H;
+  (void)G;
+  return 1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -382,6 +390,11 @@ size_t ssd_chunk_fwd_grouped_workspace_bytes(int64_t B, int64_t L, int64_t H, in
   return ssm::ssd_workspace_bytes(B, L, H, P, N, G, chunk);
 }
 
+size_t ssd_chunk_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, ssm_dtype) {
+  if (B <= 0 || L <= 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0) return 0;
+  return ssm::ssd_bwd_workspace_bytes(B, L, H, P, N, G, ssd_bwd_heads_per_wg(H, G));
+}
+
 }  // extern "C"
 
 namespace {
@@ -461,6 +474,82 @@ ssm_status ssd_chunk_fwd_grouped(int64_t B, int64_t L, int64_t H, int64_t P, int
                                  float* h_last, void* ws, size_t ws_bytes, void* stream) {
   return ssd_common("ssd_chunk_fwd_grouped", B, L, H, P, N, G, chunk, io, x, delta, delta_bias, delta_softplus, A,
                     Bm, Cm, Dskip, dskip_per_channel, z, h0, y, h_last, ws, ws_bytes, stream);
+}
+
+ssm_status ssd_chunk_bwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, ssm_dtype io,
+                         const void* x, const void* delta, const float* delta_bias, int delta_softplus,
+                         const float* A, const void* Bm, const void* Cm, const float* Dskip, int dskip_per_channel,
+                         const void* z, const float* h0, const void* dy, const float* dh_last, void* dx,
+                         void* ddelta, float* dA, float* dBm, float* dCm, float* dDskip, float* ddelta_bias,
+                         void* dz, float* dh0, void* ws, size_t ws_bytes, void* stream) {
+  if (B < 0 || L < 0) return fail(SSM_ERR_INVALID_ARGUMENT, "B and L must be >= 0");
+  if (H < 1) return fail(SSM_ERR_INVALID_ARGUMENT, "H=%lld must be >= 1", (long long)H);
+  if (G < 1 || H % G != 0)
+    return fail(SSM_ERR_INVALID_ARGUMENT, "G=%lld must be >= 1 and divide H=%lld", (long long)G, (long long)H);
+  if (!valid_dtype(io)) return fail(SSM_ERR_INVALID_ARGUMENT, "unknown io_dtype %d", (int)io);
+  if (io != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "ssd_chunk_bwd supports io_dtype SSM_BF16 only");
+  if (P != 64) return fail(SSM_ERR_UNSUPPORTED, "P=%lld: supported head dim is 64", (long long)P);
+  if (N != 64 && N != 128) return fail(SSM_ERR_UNSUPPORTED, "N=%lld: supported 64, 128", (long long)N);
+  const int64_t Q = ssm::kSsdBwdQ;
+  if ((L + Q - 1) / Q > 65535)
+    return fail(SSM_ERR_UNSUPPORTED, "L=%lld: at most 65535 chunks of %lld tokens", (long long)L, (long long)Q);
+  if (B * G > 65535 || H > 65535)
+    return fail(SSM_ERR_UNSUPPORTED, "B*G=%lld and H=%lld must each be <= 65535", (long long)(B * G), (long long)H);
+  if (!A || !dA) return fail(SSM_ERR_INVALID_ARGUMENT, "A and dA must not be NULL");
+  if (z && !dz) return fail(SSM_ERR_INVALID_ARGUMENT, "dz must be given with z");
+  const bool dpc = dskip_per_channel != 0;
+  const size_t tok = (size_t)(B * L * H * P) * 2, th = (size_t)(B * L * H) * 2;
+  const size_t bc = (size_t)(B * L * G * N) * 2, bcg = (size_t)(B * L * G * N) * 4;
+  const size_t stb = (size_t)(B * H * P * N) * 4, vh = (size_t)H * 4;
+  const size_t vd = (size_t)(dpc ? H * P : H) * 4;
+  if (B > 0 && L > 0) {
+    if (!x || !delta || !Bm || !Cm || !dy || !dx || !ddelta || !dBm || !dCm)
+      return fail(SSM_ERR_INVALID_ARGUMENT, "x, delta, Bm, Cm, dy, dx, ddelta, dBm and dCm must not be NULL");
+    if (!aligned16(x) || !aligned16(Bm) || !aligned16(Cm) || !aligned16(dy) || !aligned16(dx) ||
+        !aligned16(dBm) || !aligned16(dCm) || (z && !aligned16(z)) || (dz && !aligned16(dz)) ||
+        (Dskip && dpc && !aligned16(Dskip)))
+      return fail(SSM_ERR_INVALID_ARGUMENT, "per-token tensors must be 16-byte aligned");
+  }
+  const void* ins[] = {x, delta, z, Bm, Cm, dy, A, delta_bias, Dskip, h0, dh_last};
+  const size_t insz[] = {tok, th, tok, bc, bc, tok, vh, vh, vd, stb, stb};
+  void* outs[] = {dx, ddelta, z ? dz : nullptr, dA, dBm, dCm, dDskip, ddelta_bias, dh0};
+  const size_t outsz[] = {tok, th, tok, vh, bcg, bcg, vd, vh, stb};
+  for (int o = 0; o < 9; ++o) {
+    for (int k = 0; k < 11; ++k)
+      if (overlaps(outs[o], outsz[o], ins[k], insz[k]))
+        return fail(SSM_ERR_INVALID_ARGUMENT, "a gradient output overlaps an input");
+    for (int k = o + 1; k < 9; ++k)
+      if (overlaps(outs[o], outsz[o], outs[k], outsz[k]))
+        return fail(SSM_ERR_INVALID_ARGUMENT, "two gradient outputs overlap");
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (B == 0 || L == 0) {
+    // empty sums: parameter gradients are zero; dh0 is dh_last passed through (or zero)
+    hipError_t e = hipMemsetAsync(dA, 0, vh, st);
+    if (e == hipSuccess && dDskip) e = hipMemsetAsync(dDskip, 0, vd, st);
+    if (e == hipSuccess && ddelta_bias) e = hipMemsetAsync(ddelta_bias, 0, vh, st);
+    if (e == hipSuccess && dh0 && B > 0)
+      e = dh_last ? hipMemcpyAsync(dh0, dh_last, stb, hipMemcpyDeviceToDevice, st) : hipMemsetAsync(dh0, 0, stb, st);
+    return from_hip(e, "empty backward");
+  }
+  const int64_t hb = ssd_bwd_heads_per_wg(H, G);
+  const size_t need = ssm::ssd_bwd_workspace_bytes(B, L, H, P, N, G, hb);
+  if (!ws) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace is NULL; %zu bytes needed", need);
+  if (ws_bytes < need) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (!aligned16(ws)) return fail(SSM_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  ssm::SsdBwdParams bp{};
+  ssm::SsdParams& p = bp.f;
+  p.B = B; p.L = L; p.H = H; p.P = P; p.N = N; p.Q = Q; p.G = G;
+  p.x = x; p.delta = delta; p.z = z; p.Bm = Bm; p.Cm = Cm;
+  p.delta_bias = delta_bias; p.A = A; p.Dskip = Dskip; p.h0 = h0;
+  p.dskip_per_channel = Dskip && dpc ? 1 : 0;
+  p.delta_softplus = delta_softplus ? 1 : 0;
+  p.h_last = nullptr;
+  p.dy = dy; p.dh_last = dh_last; p.dh0 = dh0;
+  bp.dx = dx; bp.ddelta = ddelta; bp.dz = z ? dz : nullptr; bp.dA = dA; bp.dBm = dBm; bp.dCm = dCm;
+  bp.dDskip = dDskip; bp.ddelta_bias = ddelta_bias; bp.hb = hb;
+  ssm::ssd_bwd_workspace_carve(bp, ws);
+  return from_hip(ssm::launch_ssd_bwd(bp, st), "ssd_chunk_bwd launch");
 }
 
 }  // extern "C"

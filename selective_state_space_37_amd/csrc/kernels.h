@@ -132,11 +132,44 @@ struct SsdParams {
   void* ws_G;              // bf16 [B, G, nchunks, Q, Q]: C_i . B_j inside each chunk
   void* ws_Bt;             // bf16 [B, G, nchunks, N, Q]: B of each chunk, transposed
   float2* ws_sphi;         // [B, nchunks, H, Q]: (inclusive cumulative Delta, ZOH input scale)
+  // backward only (NULL in the forward)
+  const void* dy;          // bf16 [B, L, H, P]: dL/dy
+  const float* dh_last;    // nullable [B, H, P, N]
+  float* dh0;              // nullable [B, H, P, N] (out)
+  void* ws_gout;           // bf16 [B, nchunks, H, P, N]: dL/d(state leaving each chunk)
+  void* ws_Ct;             // bf16 [B, G, nchunks, N, Q]: C of each chunk, transposed
+  void* ws_GT;             // float [B, G, nchunks, Q, Q]: G transposed (B_j . C_i at [j][i]);
+                           // in the backward ws_G holds G in float as well
 };
 
 size_t ssd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);
 // Point the workspace fields of p at their parts of ws (ssd_workspace_bytes() bytes).
 void ssd_workspace_carve(SsdParams& p, void* ws);
 hipError_t launch_ssd(const SsdParams& p, hipStream_t stream);
+
+// Gradients of the SSD layer. The backward cuts the sequence into chunks of its own (kSsdBwdQ
+// tokens), independent of the forward's chunk length.
+constexpr int64_t kSsdBwdQ = 64;
+struct SsdBwdParams {
+  SsdParams f;             // forward inputs, dy, dh_last, dh0 and the shared workspace parts
+  void* dx;                // bf16 [B, L, H, P] (out)
+  void* ddelta;            // bf16 [B, L, H] (out)
+  void* dz;                // bf16 [B, L, H, P] (out) when z is given
+  float* dA;               // [H] (out)
+  float* dBm;              // [B, L, G, N] (out)
+  float* dCm;
+  float* dDskip;           // nullable (out): [H] or [H, P] (dskip_per_channel)
+  float* ddelta_bias;      // nullable [H] (out)
+  int64_t hb;              // heads per workgroup in the main pass (divides H / G)
+  float* ws_dBp;           // [B, H / hb, L, N]: dB summed over each workgroup's heads
+  float* ws_dCp;
+  float* ws_pA;            // [B, nchunks, H] partial dA
+  float* ws_pb;            // [B, nchunks, H] partial ddelta_bias
+  float* ws_pD;            // [B, nchunks, H, P] partial dD (per channel)
+};
+
+size_t ssd_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t hb);
+void ssd_bwd_workspace_carve(SsdBwdParams& p, void* ws);
+hipError_t launch_ssd_bwd(const SsdBwdParams& p, hipStream_t stream);
 
 }  // namespace ssm

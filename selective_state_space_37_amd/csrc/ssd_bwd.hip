@@ -1,0 +1,720 @@
+// Gradients of the Mamba-2 (SSD) layer on gfx950: MFMA for every contraction inside a chunk.
+//
+// Page "Mamba and state space models", section "Mamba-2: two algorithms": the layer is a
+// lower-triangular matrix applied chunk by chunk, and only the state passes between chunks. The
+// backward keeps that split. Per chunk of Q = 64 tokens, with S the inclusive cumulative sum of
+// Delta in the chunk, phi_j = expm1(a Delta_j) / a, ybar = dy times the gate factor z sigmoid(z),
+// H_c the state entering the chunk and Gc the adjoint of the state leaving it:
+//   h_t     = exp(a S_t) H_c + sum_{j<=t} exp(a (S_t - S_j)) phi_j x_j B_j^T
+//   dL/dh_t = exp(a (S_Q - S_t)) Gc + sum_{i>=t} exp(a (S_i - S_t)) ybar_i C_i^T
+// Both are needed only through contractions, never per token:
+//   U_ij  = ybar_i . x_j,  W_ij = exp(a (S_i - S_j)) phi_j U_ij (i >= j),  K_ij = (C_i . B_j) W_ij
+//   dC_i  = sum_j W_ij B_j + exp(a S_i) H_c^T ybar_i                   (summed over the group)
+//   dB_j  = sum_i W_ij C_i + exp(a (S_Q - S_j)) phi_j Gc^T x_j
+//   w_j   = sum_{i>=j} (C_i . B_j) exp(a (S_i - S_j)) ybar_i + exp(a (S_Q - S_j)) Gc B_j
+//   dx_j  = phi_j w_j + D ybar_j
+//   dDelta_t = a <dL/dh_t, h_t> + x_t . w_t     (derivative of exp(a Delta) and phi together)
+//   <dL/dh_t, h_t> = exp(a S_Q) <Gc, H_c> + sum_{i>=t} ybar_i . Yoff_i
+//                    + sum_{j<=t} phi_j x_j . (exp(a (S_Q - S_j)) Gc B_j) + sum_{j<=t<=i} K_ij
+//   dA    = sum_t Delta_t <dL/dh_t, h_t> + (Delta_t - phi_t) / a  x_t . w_t
+// with Yoff_i = exp(a S_i) H_c C_i (the carried-state part of y_i), and dz from the recomputed
+// pre-gate output. The passes:
+//   cumsum, prep (G = C B^T and its transpose, B^T, C^T per chunk and group), the forward state
+//   pass (H_c for every chunk, bf16), the adjoint state pass (Gc for every chunk, bf16, and dh0),
+//   the main kernel below, and two reductions in a fixed order (dB and dC over heads, the
+//   parameter gradients over batch rows and chunks).
+#include <algorithm>
+
+#include "ssd_device.h"
+
+namespace ssm {
+namespace {
+
+constexpr int kQb = (int)kSsdBwdQ;
+static_assert(kQb == 64, "the main kernel's wave layout assumes 64-token chunks");
+
+__device__ __forceinline__ bf16x8 pack8(const float v[8]) {
+  bf16x8 o;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) o[q] = (__bf16)v[q];
+  return o;
+}
+
+__device__ __forceinline__ bf16x8 frag_from_pieces(uint2 lo, uint2 hi) {
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+__device__ __forceinline__ void unpack8(uint4 v, float out[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    out[2 * k] = bf16_lo(w[k]);
+    out[2 * k + 1] = bf16_hi(w[k]);
+  }
+}
+
+// grid (H / hb, chunks, B), 256 threads. Wave w owns token tile w (tokens 16 w .. 16 w + 15 of the
+// chunk) in both roles: as the rows i of dC, y and dz and as the columns j of dB, dx and w. The
+// MFMA products are oriented so that the outputs come out with four consecutive states or
+// channels per lane (one 8- or 16-byte store), and a product that feeds another (W) comes out in
+// the operand layout of the next one: two 16-token tiles per K = 32 step, four tokens of each per
+// lane, the same K order on both operands. dB and dC are summed over the workgroup's hb heads
+// (consecutive heads of one group) in registers.
+template <int N>
+__global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
+  constexpr int Q = kQb;
+  constexpr int NT = N / 16;   // 16-state tiles
+  constexpr int KSN = N / 32;  // K steps over the states
+  constexpr int RS = Q + 8;    // row stride (bf16) of the transposed token tiles
+  constexpr int RSP = kP + 8;  // row stride (bf16) of the transposed states
+  constexpr int KST = Q + 1;   // row stride (float) of K
+  __shared__ __attribute__((aligned(16))) __bf16 YT[kP * RS];    // ybar^T [p][i]
+  __shared__ __attribute__((aligned(16))) __bf16 XT[kP * RS];    // (phi x)^T [p][j] (gate only)
+  __shared__ __attribute__((aligned(16))) __bf16 HT[N * RSP];    // H_c^T [n][p]
+  __shared__ __attribute__((aligned(16))) __bf16 GcT[N * RSP];   // Gc^T [n][p]
+  __shared__ float sK[Q * KST];
+  __shared__ float sS[Q], sPhi[Q], sQv[Q], sRv[Q], sVv[Q], sRt[Q], sRed[4];
+  __shared__ float sDD[4][kP];
+
+  const SsdParams& p = bp.f;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  // the wave index is the same for all lanes of a wave: readfirstlane lets the compiler keep it
+  // (and the tile loops over it) in scalar registers, so branches on it are not divergent
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t hblk = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
+  const int64_t nch = gridDim.y;
+  const int64_t L = p.L, H = p.H;
+  const int64_t grp = hblk * bp.hb / (H / p.G);
+  const int64_t bg = b * p.G + grp;
+  const int64_t rs = p.G * N;   // token row stride of B and C
+  const bf16_t* Bg = static_cast<const bf16_t*>(p.Bm) + b * L * rs + grp * N;
+  const bf16_t* Cg = static_cast<const bf16_t*>(p.Cm) + b * L * rs + grp * N;
+  // G = C B^T of the chunk and its transpose, float32 (only tiles on / below the diagonal of G)
+  const float* Gm = static_cast<const float*>(p.ws_G) + (bg * nch + c) * (int64_t)(Q * Q);
+  const float* GTm = static_cast<const float*>(p.ws_GT) + (bg * nch + c) * (int64_t)(Q * Q);
+  const bf16_t* Btm = static_cast<const bf16_t*>(p.ws_Bt) + (bg * nch + c) * (int64_t)(N * Q);
+  const bf16_t* Ctm = static_cast<const bf16_t*>(p.ws_Ct) + (bg * nch + c) * (int64_t)(N * Q);
+  const int64_t tc0 = c * Q;      // first token of the chunk
+  const int i0 = w * 16;          // this wave's token tile
+  const int il = i0 + r16;        // this lane's token in the chunk (column role)
+  const int64_t tl = tc0 + il;
+  const bool lane_valid = tl < L;
+  const int64_t tstride = H * kP;  // token stride of x, dy, z
+
+  f32x4 dC[NT], dB[NT];
+#pragma unroll
+  for (int k = 0; k < NT; ++k) dC[k] = dB[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t kh = 0; kh < bp.hb; ++kh) {
+    const int64_t h = hblk * bp.hb + kh;
+    const float a = p.A[h], a2 = a * kLog2e;
+    const bf16_t* xh = static_cast<const bf16_t*>(p.x) + (b * L * H + h) * kP;
+    const bf16_t* dyh = static_cast<const bf16_t*>(p.dy) + (b * L * H + h) * kP;
+    const bf16_t* zh = p.z ? static_cast<const bf16_t*>(p.z) + (b * L * H + h) * kP : nullptr;
+    const float2* sp = p.ws_sphi + ((b * nch + c) * H + h) * Q;
+    const bf16_t* hin = static_cast<const bf16_t*>(p.ws_hin) + ((b * nch + c) * H + h) * (int64_t)(kP * N);
+    const bf16_t* gout = static_cast<const bf16_t*>(p.ws_gout) + ((b * nch + c) * H + h) * (int64_t)(kP * N);
+    const bool dpc = p.Dskip && p.dskip_per_channel;
+    const float dhead = p.Dskip && !p.dskip_per_channel ? p.Dskip[h] : 0.f;
+    auto dskip = [&](int ch) { return dpc ? p.Dskip[h * kP + ch] : dhead; };
+
+    // ybar (dy times the gate factor) of token t, channels p0 .. p0 + 7, as two MFMA fragments
+    // whose sum is ybar to about 16 bits (hi = ybar rounded to bf16, lo = the rounding error
+    // rounded): products with x (exactly bf16) then lose nothing to the operand rounding
+    auto ybar8 = [&](int64_t t, int p0, bf16x8& hi, bf16x8& lo) {
+      if (t >= L) {
+        hi = lo = zero_frag();
+        return;
+      }
+      const uint4 d = *reinterpret_cast<const uint4*>(dyh + t * tstride + p0);
+      if (!zh) {
+        hi = __builtin_bit_cast(bf16x8, d);
+        lo = zero_frag();
+        return;
+      }
+      float dv[8], zv[8];
+      unpack8(d, dv);
+      unpack8(*reinterpret_cast<const uint4*>(zh + t * tstride + p0), zv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float v = dv[q] * silu(zv[q]);
+        hi[q] = (__bf16)v;
+        lo[q] = (__bf16)(v - (float)hi[q]);
+      }
+    };
+    auto x8 = [&](int64_t t, int p0) -> bf16x8 {
+      return t < L ? load_frag(xh + t * tstride + p0) : zero_frag();
+    };
+
+    // ------------------------------------------------------------------ staging
+    if (tid < Q) {
+      const float2 v = sp[tid];
+      sS[tid] = v.x;
+      sPhi[tid] = v.y;
+    }
+    {
+      // ybar^T (and (phi x)^T with a gate): token pair ip, channels 8 pg8 .. 8 pg8 + 7. Lanes
+      // 0..31 of a wave write 32 consecutive words of a row, lanes 32..63 the rows 8 further
+      // (288 words on): the 64 writes fall on 64 banks.
+      const int ip = tid & 31, pg8 = tid >> 5;
+      float y0[8], y1[8];
+      const int64_t t = tc0 + 2 * ip;
+      const uint4 zero4 = make_uint4(0, 0, 0, 0);
+      const uint4 d0 = t < L ? *reinterpret_cast<const uint4*>(dyh + t * tstride + 8 * pg8) : zero4;
+      const uint4 d1 = t + 1 < L ? *reinterpret_cast<const uint4*>(dyh + (t + 1) * tstride + 8 * pg8) : zero4;
+      unpack8(d0, y0);
+      unpack8(d1, y1);
+      if (zh) {
+        const uint4 z0 = t < L ? *reinterpret_cast<const uint4*>(zh + t * tstride + 8 * pg8) : zero4;
+        const uint4 z1 = t + 1 < L ? *reinterpret_cast<const uint4*>(zh + (t + 1) * tstride + 8 * pg8) : zero4;
+        float zv0[8], zv1[8];
+        unpack8(z0, zv0);
+        unpack8(z1, zv1);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          y0[k] *= silu(zv0[k]);
+          y1[k] *= silu(zv1[k]);
+        }
+        // (phi x)^T for the recomputed within-chunk output
+        const uint4 xa = t < L ? *reinterpret_cast<const uint4*>(xh + t * tstride + 8 * pg8) : zero4;
+        const uint4 xb = t + 1 < L ? *reinterpret_cast<const uint4*>(xh + (t + 1) * tstride + 8 * pg8) : zero4;
+        float xv0[8], xv1[8];
+        unpack8(xa, xv0);
+        unpack8(xb, xv1);
+        const float ph0 = sp[2 * ip].y, ph1 = sp[2 * ip + 1].y;
+        uint32_t* X32 = reinterpret_cast<uint32_t*>(XT);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          X32[(8 * pg8 + k) * (RS / 2) + ip] =
+              (uint32_t)f32_to_bf16(ph0 * xv0[k]) | ((uint32_t)f32_to_bf16(ph1 * xv1[k]) << 16);
+      }
+      uint32_t* Y32 = reinterpret_cast<uint32_t*>(YT);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        Y32[(8 * pg8 + k) * (RS / 2) + ip] = (uint32_t)f32_to_bf16(y0[k]) | ((uint32_t)f32_to_bf16(y1[k]) << 16);
+    }
+    float dot = 0.f;   // <Gc, H_c> over this thread's pieces
+    for (int item = tid; item < 32 * (N / 8); item += 256) {
+      // channels (2 pp, 2 pp + 1), states 8 ng .. 8 ng + 7 of H_c and Gc, written transposed
+      const int pp = item & 31, ng = item >> 5;
+      float h0v[8], h1v[8], g0v[8], g1v[8];
+      unpack8(*reinterpret_cast<const uint4*>(hin + (2 * pp) * N + 8 * ng), h0v);
+      unpack8(*reinterpret_cast<const uint4*>(hin + (2 * pp + 1) * N + 8 * ng), h1v);
+      unpack8(*reinterpret_cast<const uint4*>(gout + (2 * pp) * N + 8 * ng), g0v);
+      unpack8(*reinterpret_cast<const uint4*>(gout + (2 * pp + 1) * N + 8 * ng), g1v);
+      uint32_t* H32 = reinterpret_cast<uint32_t*>(HT);
+      uint32_t* G32 = reinterpret_cast<uint32_t*>(GcT);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        H32[(8 * ng + k) * (RSP / 2) + pp] = (uint32_t)f32_to_bf16(h0v[k]) | ((uint32_t)f32_to_bf16(h1v[k]) << 16);
+        G32[(8 * ng + k) * (RSP / 2) + pp] = (uint32_t)f32_to_bf16(g0v[k]) | ((uint32_t)f32_to_bf16(g1v[k]) << 16);
+        dot += h0v[k] * g0v[k] + h1v[k] * g1v[k];
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+    if (lane == 0) sRed[w] = dot;
+    __syncthreads();
+
+    const float Sq = sS[Q - 1];
+    const float Sl = sS[il], phil = sPhi[il];   // this lane's token (column role)
+    // this lane's token: ybar and x fragments over the 64 channels (two K steps)
+    bf16x8 yb_own[2], yb_lo[2], x_own[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      ybar8(tl, 32 * kk + 8 * g, yb_own[kk], yb_lo[kk]);
+      x_own[kk] = x8(tl, 32 * kk + 8 * g);
+    }
+
+    // ------------------------------------------------------------------ dC (rows i = own tile)
+    {
+      // U^T tiles (j tile jt <= w, i = own): D[j][i] = sum_p x_j[p] ybar_i[p]; the lane holds
+      // U[il][jt 16 + 4 g + r]. W (as the B operand of the next product) and K (to LDS).
+      bf16x8 wmA[2] = {zero_frag(), zero_frag()};
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        if (jt > w) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sK[il * KST + jt * 16 + 4 * g + r] = 0.f;
+          continue;
+        }
+        f32x4 u = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const bf16x8 xa = x8(tc0 + jt * 16 + r16, 32 * kk + 8 * g);
+          u = mfma16(xa, yb_own[kk], u);
+          u = mfma16(xa, yb_lo[kk], u);
+        }
+        const float4 g4 = *reinterpret_cast<const float4*>(Gm + il * Q + jt * 16 + 4 * g);
+        const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = jt * 16 + 4 * g + r;
+          const float wm = j <= il ? exp2_fast(a2 * (Sl - sS[j])) * sPhi[j] * u[r] : 0.f;
+          sK[il * KST + j] = gv[r] * wm;
+          wmA[jt >> 1][(jt & 1) * 4 + r] = (__bf16)wm;
+        }
+      }
+      // ybar of the own token scaled by exp(a S_i) for the carried-state term
+      const float eSi = exp2_fast(a2 * Sl);
+      bf16x8 yb_sc[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) yb_sc[kk][q] = (__bf16)(((float)yb_own[kk][q] + (float)yb_lo[kk][q]) * eSi);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        f32x4 acc = dC[nt];
+        const int n = nt * 16 + r16;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          if (2 * kk > w) break;   // the pair holds no tile j <= i
+          const uint2 lo = *reinterpret_cast<const uint2*>(Btm + n * Q + 32 * kk + 4 * g);
+          const uint2 hi = *reinterpret_cast<const uint2*>(Btm + n * Q + 32 * kk + 16 + 4 * g);
+          acc = mfma16(frag_from_pieces(lo, hi), wmA[kk], acc);   // D[n][i] = sum_j B_j[n] W_ij
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          acc = mfma16(*reinterpret_cast<const bf16x8*>(&HT[n * RSP + 32 * kk + 8 * g]), yb_sc[kk], acc);
+        dC[nt] = acc;
+      }
+    }
+
+    // ------------------------------------------------------------------ dB (columns j = own tile)
+    // vin: this lane's part of x_j . sum_{i>=j} (C_i . B_j) exp(a (S_i - S_j)) ybar_i, formed in
+    // float32 from U (the within-chunk part of x_j . w_j, for dDelta)
+    float vin = 0.f;
+    {
+      // U tiles (i tile it >= w, j = own): D[i][j] = sum_p ybar_i[p] x_j[p]; the lane holds
+      // U[it 16 + 4 g + r][il].
+      bf16x8 wmB[2] = {zero_frag(), zero_frag()};
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        if (it < w) continue;
+        f32x4 u = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          bf16x8 yh, yl;
+          ybar8(tc0 + it * 16 + r16, 32 * kk + 8 * g, yh, yl);
+          u = mfma16(yh, x_own[kk], u);
+          u = mfma16(yl, x_own[kk], u);
+        }
+        const float4 g4 = *reinterpret_cast<const float4*>(GTm + il * Q + it * 16 + 4 * g);   // G[i][il]
+        const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = it * 16 + 4 * g + r;
+          const float e = i >= il ? exp2_fast(a2 * (sS[i] - Sl)) : 0.f;
+          vin += gv[r] * e * u[r];
+          wmB[it >> 1][(it & 1) * 4 + r] = (__bf16)(e * phil * u[r]);
+        }
+      }
+      const float eq = exp2_fast(a2 * (Sq - Sl)) * phil;
+      bf16x8 x_sc[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) x_sc[kk][q] = (__bf16)((float)x_own[kk][q] * eq);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        f32x4 acc = dB[nt];
+        const int n = nt * 16 + r16;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          if (2 * kk + 1 < w) continue;   // the pair holds no tile i >= j
+          const uint2 lo = *reinterpret_cast<const uint2*>(Ctm + n * Q + 32 * kk + 4 * g);
+          const uint2 hi = *reinterpret_cast<const uint2*>(Ctm + n * Q + 32 * kk + 16 + 4 * g);
+          acc = mfma16(frag_from_pieces(lo, hi), wmB[kk], acc);   // D[n][j] = sum_i C_i[n] W_ij
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          acc = mfma16(*reinterpret_cast<const bf16x8*>(&GcT[n * RSP + 32 * kk + 8 * g]), x_sc[kk], acc);
+        dB[nt] = acc;
+      }
+    }
+
+    // ------------------------------------------------------------------ y (rows i = own tile)
+    // Yoff[p][i] = exp(a S_i) sum_n H_c[p][n] C_i[n]; with a gate also the within-chunk part
+    // Ydiag[p][i] = sum_{j<=i} (C_i . B_j) exp(a (S_i - S_j)) phi_j x_j[p] for the pre-gate output.
+    f32x4 yo[4], yd[4];
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) yo[pt] = yd[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+      const float eSi = exp2_fast(a2 * Sl);
+#pragma unroll
+      for (int ks = 0; ks < KSN; ++ks) {
+        bf16x8 cf = lane_valid ? load_frag(Cg + tl * rs + 32 * ks + 8 * g) : zero_frag();
+#pragma unroll
+        for (int q = 0; q < 8; ++q) cf[q] = (__bf16)((float)cf[q] * eSi);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+          yo[pt] = mfma16(load_frag(hin + (pt * 16 + r16) * N + 32 * ks + 8 * g), cf, yo[pt]);
+      }
+    }
+    if (zh) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        if (2 * kk > w) break;
+        float gl[8];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int jt = 2 * kk + half;
+          if (jt <= w) {
+            const float4 g4 = *reinterpret_cast<const float4*>(Gm + il * Q + jt * 16 + 4 * g);
+            const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int j = jt * 16 + 4 * g + r;
+              gl[half * 4 + r] = j <= il ? gv[r] * exp2_fast(a2 * (Sl - sS[j])) : 0.f;
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gl[half * 4 + r] = 0.f;
+          }
+        }
+        const bf16x8 glf = pack8(gl);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          const uint2 lo = *reinterpret_cast<const uint2*>(&XT[(pt * 16 + r16) * RS + 32 * kk + 4 * g]);
+          const uint2 hi = *reinterpret_cast<const uint2*>(&XT[(pt * 16 + r16) * RS + 32 * kk + 16 + 4 * g]);
+          yd[pt] = mfma16(frag_from_pieces(lo, hi), glf, yd[pt]);
+        }
+      }
+    }
+    // epilogue: the lane holds channels pt 16 + 4 g + r of token il
+    float ybv[4][4], xv[4][4];
+    float qpart = 0.f;
+    {
+      float dd[4][4];
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const int64_t o = tl * tstride + pt * 16 + 4 * g;
+        const uint2 dr = lane_valid ? *reinterpret_cast<const uint2*>(dyh + o) : make_uint2(0, 0);
+        const uint2 xr = lane_valid ? *reinterpret_cast<const uint2*>(xh + o) : make_uint2(0, 0);
+        const float dv[4] = {bf16_lo(dr.x), bf16_hi(dr.x), bf16_lo(dr.y), bf16_hi(dr.y)};
+        const float xx[4] = {bf16_lo(xr.x), bf16_hi(xr.x), bf16_lo(xr.y), bf16_hi(xr.y)};
+        float zv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (zh) {
+          const uint2 zr = lane_valid ? *reinterpret_cast<const uint2*>(zh + o) : make_uint2(0, 0);
+          zv[0] = bf16_lo(zr.x); zv[1] = bf16_hi(zr.x); zv[2] = bf16_lo(zr.y); zv[3] = bf16_hi(zr.y);
+        }
+        float dzv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ch = pt * 16 + 4 * g + r;
+          xv[pt][r] = xx[r];
+          const float yb = zh ? dv[r] * silu(zv[r]) : dv[r];
+          ybv[pt][r] = yb;
+          qpart += yb * yo[pt][r];
+          dd[pt][r] = yb * xx[r];
+          if (zh) {
+            const float ypre = yo[pt][r] + yd[pt][r] + dskip(ch) * xx[r];
+            const float sg = sigmoid_fast(zv[r]);
+            dzv[r] = dv[r] * ypre * sg * (1.f + zv[r] * (1.f - sg));
+          }
+        }
+        if (zh && lane_valid) {
+          uint2 out;
+          out.x = (uint32_t)f32_to_bf16(dzv[0]) | ((uint32_t)f32_to_bf16(dzv[1]) << 16);
+          out.y = (uint32_t)f32_to_bf16(dzv[2]) | ((uint32_t)f32_to_bf16(dzv[3]) << 16);
+          *reinterpret_cast<uint2*>(static_cast<bf16_t*>(bp.dz) + (b * L * H + h) * kP + o) = out;
+        }
+      }
+      // dD per channel: sum over the 16 tokens of the tile (lanes with the same g)
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = dd[pt][r];
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, 64);
+          if (r16 == 0) sDD[w][pt * 16 + 4 * g + r] = v;
+        }
+    }
+
+    // ------------------------------------------------------------------ dx (columns j = own tile)
+    // w_j[p] = sum_{i>=j} (C_i . B_j) exp(a (S_i - S_j)) ybar_i[p]   +   exp(a (S_Q - S_j)) (Gc B_j)[p]
+    f32x4 wi[4], vo[4];
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) wi[pt] = vo[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      if (2 * kk + 1 < w) continue;
+      float gl[8];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int it = 2 * kk + half;
+        if (it >= w) {
+          const float4 g4 = *reinterpret_cast<const float4*>(GTm + il * Q + it * 16 + 4 * g);   // G[i][j], i = it 16 + 4 g ..
+          const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = it * 16 + 4 * g + r;
+            gl[half * 4 + r] = i >= il ? gv[r] * exp2_fast(a2 * (sS[i] - Sl)) : 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) gl[half * 4 + r] = 0.f;
+        }
+      }
+      const bf16x8 glf = pack8(gl);
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(&YT[(pt * 16 + r16) * RS + 32 * kk + 4 * g]);
+        const uint2 hi = *reinterpret_cast<const uint2*>(&YT[(pt * 16 + r16) * RS + 32 * kk + 16 + 4 * g]);
+        wi[pt] = mfma16(frag_from_pieces(lo, hi), glf, wi[pt]);   // D[p][j] = sum_i ybar_i[p] GL_ij
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KSN; ++ks) {
+      const bf16x8 bf = lane_valid ? load_frag(Bg + tl * rs + 32 * ks + 8 * g) : zero_frag();
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+        vo[pt] = mfma16(load_frag(gout + (pt * 16 + r16) * N + 32 * ks + 8 * g), bf, vo[pt]);
+    }
+    float vvp = vin, rp = 0.f;
+    {
+      const float eq = exp2_fast(a2 * (Sq - Sl));
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        float dxv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = eq * vo[pt][r];
+          const float wv = wi[pt][r] + v;
+          dxv[r] = phil * wv + dskip(pt * 16 + 4 * g + r) * ybv[pt][r];
+          rp += xv[pt][r] * v;
+        }
+        if (lane_valid) {
+          uint2 out;
+          out.x = (uint32_t)f32_to_bf16(dxv[0]) | ((uint32_t)f32_to_bf16(dxv[1]) << 16);
+          out.y = (uint32_t)f32_to_bf16(dxv[2]) | ((uint32_t)f32_to_bf16(dxv[3]) << 16);
+          *reinterpret_cast<uint2*>(static_cast<bf16_t*>(bp.dx) + (b * L * H + h) * kP + tl * tstride + pt * 16 + 4 * g) = out;
+        }
+      }
+      vvp += rp;   // x_j . (exp(a (S_Q - S_j)) Gc B_j)
+      rp *= phil;
+    }
+    // per-token sums over the channels: lanes l, l ^ 16, l ^ 32, l ^ 48 hold the same token
+#pragma unroll
+    for (int off = 16; off < 64; off <<= 1) {
+      qpart += __shfl_xor(qpart, off, 64);
+      vvp += __shfl_xor(vvp, off, 64);
+      rp += __shfl_xor(rp, off, 64);
+    }
+    if (g == 0) {
+      sQv[il] = qpart;
+      sVv[il] = vvp;
+      sRv[il] = rp;
+    }
+    __syncthreads();
+
+    // ------------------------------------------------------------------ sum of K over j <= t <= i
+    {
+      // prefix over j of each row i (four 16-column pieces per row, one per thread)
+      const int i = tid >> 2, seg = tid & 3;
+      float run[16];
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        acc += sK[i * KST + 16 * seg + k];
+        run[k] = acc;
+      }
+      const int base = lane & ~3;
+      const float t0 = __shfl(acc, base, 64), t1v = __shfl(acc, base + 1, 64), t2 = __shfl(acc, base + 2, 64);
+      const float off = (seg > 0 ? t0 : 0.f) + (seg > 1 ? t1v : 0.f) + (seg > 2 ? t2 : 0.f);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) sK[i * KST + 16 * seg + k] = run[k] + off;
+    }
+    __syncthreads();
+    {
+      // R_t = sum_{i>=t} prefix_i(t): rows 16 seg .. 16 seg + 15 per thread
+      const int t = tid >> 2, seg = tid & 3;
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int i = 16 * seg + k;
+        if (i >= t) acc += sK[i * KST + t];
+      }
+      acc += __shfl_xor(acc, 1, 64);
+      acc += __shfl_xor(acc, 2, 64);
+      if (seg == 0) sRt[t] = acc;
+    }
+    __syncthreads();
+
+    // ------------------------------------------------------------------ per-token: dDelta
+    if (w == 0) {
+      const int t = lane;
+      float sq = sQv[t];   // suffix sum over i >= t
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_down(sq, off, 64);
+        if (t + off < 64) sq += o;
+      }
+      float pr = sRv[t];   // prefix sum over j <= t
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_up(pr, off, 64);
+        if (t >= off) pr += o;
+      }
+      const float t1 = exp2_fast(a2 * Sq) * (sRed[0] + sRed[1] + sRed[2] + sRed[3]);
+      const float u = t1 + sq + pr + sRt[t];
+      const float vv = sVv[t];
+      const float ddt = a * u + vv;
+      const int64_t tt = tc0 + t;
+      float pa = 0.f, pb = 0.f;
+      if (tt < L) {
+        const float raw = bf16_to_f32(static_cast<const bf16_t*>(p.delta)[(b * L + tt) * H + h].bits) +
+                          (p.delta_bias ? p.delta_bias[h] : 0.f);
+        const float dt = p.delta_softplus ? softplus_f32(raw) : raw;
+        const float gu = p.delta_softplus ? ddt * sigmoid_fast(raw) : ddt;
+        static_cast<bf16_t*>(bp.ddelta)[(b * L + tt) * H + h].bits = f32_to_bf16(gu);
+        // (Delta - phi) / a = (a Delta - expm1(a Delta)) / a^2
+        const float xa = a * dt;
+        pa = dt * u + (xa - expm1f(xa)) / (a * a) * vv;
+        pb = gu;
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        pa += __shfl_xor(pa, off, 64);
+        pb += __shfl_xor(pb, off, 64);
+      }
+      const int64_t pidx = (b * nch + c) * H + h;
+      if (t == 0) {
+        bp.ws_pA[pidx] = pa;
+        bp.ws_pb[pidx] = pb;
+      }
+      bp.ws_pD[pidx * kP + t] = sDD[0][t] + sDD[1][t] + sDD[2][t] + sDD[3][t];
+    }
+    __syncthreads();   // the next head restages the LDS tiles
+  }
+
+  // dB and dC of this workgroup's heads: the lane holds states nt 16 + 4 g .. + 3 of token il
+  if (lane_valid) {
+    const int64_t orow = ((b * (H / bp.hb) + hblk) * L + tl) * N + 4 * g;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      *reinterpret_cast<float4*>(bp.ws_dCp + orow + nt * 16) = make_float4(dC[nt][0], dC[nt][1], dC[nt][2], dC[nt][3]);
+      *reinterpret_cast<float4*>(bp.ws_dBp + orow + nt * 16) = make_float4(dB[nt][0], dB[nt][1], dB[nt][2], dB[nt][3]);
+    }
+  }
+}
+
+// dB, dC [B, L, G, N] = sums over each group's head blocks, in block order; 4 states per thread.
+__global__ __launch_bounds__(256) void ssd_bwd_reduce_bc_kernel(SsdBwdParams bp) {
+  const SsdParams& p = bp.f;
+  const int64_t nblk = p.H / bp.hb, per = nblk / p.G;   // head blocks, per group
+  const int64_t total = p.B * p.L * p.G * (p.N / 4);
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t n4 = e % (p.N / 4);
+    int64_t rest = e / (p.N / 4);
+    const int64_t grp = rest % p.G;
+    rest /= p.G;
+    const int64_t t = rest % p.L, b = rest / p.L;
+    float4 sb = make_float4(0.f, 0.f, 0.f, 0.f), sc = sb;
+    for (int64_t k = 0; k < per; ++k) {
+      const int64_t src = ((b * nblk + grp * per + k) * p.L + t) * p.N + 4 * n4;
+      const float4 vb = *reinterpret_cast<const float4*>(bp.ws_dBp + src);
+      const float4 vc = *reinterpret_cast<const float4*>(bp.ws_dCp + src);
+      sb.x += vb.x; sb.y += vb.y; sb.z += vb.z; sb.w += vb.w;
+      sc.x += vc.x; sc.y += vc.y; sc.z += vc.z; sc.w += vc.w;
+    }
+    const int64_t dst = ((b * p.L + t) * p.G + grp) * p.N + 4 * n4;
+    *reinterpret_cast<float4*>(bp.dBm + dst) = sb;
+    *reinterpret_cast<float4*>(bp.dCm + dst) = sc;
+  }
+}
+
+// dA, ddelta_bias [H] and dD ([H] or [H, P]): sums over batch rows and chunks, in order.
+// One thread per (head, channel); the channel-0 thread of a head also forms the per-head sums.
+__global__ __launch_bounds__(64) void ssd_bwd_reduce_param_kernel(SsdBwdParams bp, int64_t nch) {
+  const SsdParams& p = bp.f;
+  const int64_t h = blockIdx.x;
+  const int ch = threadIdx.x;
+  float sd = 0.f;
+  for (int64_t b = 0; b < p.B; ++b)
+    for (int64_t c = 0; c < nch; ++c) sd += bp.ws_pD[((b * nch + c) * p.H + h) * kP + ch];
+  if (bp.dDskip && p.dskip_per_channel) bp.dDskip[h * kP + ch] = sd;
+  float tot = sd;   // per-head dD: channels summed in a fixed tree order
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
+  if (ch == 0) {
+    float sa = 0.f, sb = 0.f;
+    for (int64_t b = 0; b < p.B; ++b)
+      for (int64_t c = 0; c < nch; ++c) {
+        sa += bp.ws_pA[(b * nch + c) * p.H + h];
+        sb += bp.ws_pb[(b * nch + c) * p.H + h];
+      }
+    bp.dA[h] = sa;
+    if (bp.ddelta_bias) bp.ddelta_bias[h] = sb;
+    if (bp.dDskip && !p.dskip_per_channel) bp.dDskip[h] = tot;
+  }
+}
+
+template <int N>
+hipError_t launch_n(const SsdBwdParams& bp, hipStream_t stream) {
+  constexpr int Q = kQb;
+  const SsdParams& p = bp.f;
+  const int64_t nch = (p.L + Q - 1) / Q;
+  const dim3 chunks((unsigned)p.H, (unsigned)nch, (unsigned)p.B);
+  hipLaunchKernelGGL((ssd_cumsum_kernel<Q>), chunks, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((ssd_prep_kernel<Q, N, true>), dim3(4, (unsigned)nch, (unsigned)(p.B * p.G)), dim3(256), 0,
+                     stream, p);
+  hipLaunchKernelGGL((ssd_state_kernel<Q, N, false>), dim3((unsigned)p.H, (unsigned)p.B), dim3(512), 0, stream, p);
+  hipLaunchKernelGGL((ssd_state_kernel<Q, N, true>), dim3((unsigned)p.H, (unsigned)p.B), dim3(512), 0, stream, p);
+  hipLaunchKernelGGL((ssd_bwd_main_kernel<N>), dim3((unsigned)(p.H / bp.hb), (unsigned)nch, (unsigned)p.B),
+                     dim3(256), 0, stream, bp);
+  const int64_t total = p.B * p.L * p.G * (p.N / 4);
+  const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(ssd_bwd_reduce_bc_kernel, dim3(blocks), dim3(256), 0, stream, bp);
+  hipLaunchKernelGGL(ssd_bwd_reduce_param_kernel, dim3((unsigned)p.H), dim3(64), 0, stream, bp, nch);
+  return hipGetLastError();
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+}  // namespace
+
+size_t ssd_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t hb) {
+  const int64_t Q = kQb, nch = (L + Q - 1) / Q;
+  const size_t st = align256((size_t)(B * nch * H * P * N) * 2);
+  const size_t gg = align256((size_t)(B * G * nch * Q * Q) * 4);
+  const size_t bt = align256((size_t)(B * G * nch * N * Q) * 2);
+  const size_t sp = align256((size_t)(B * nch * H * Q) * 8);
+  const size_t part = align256((size_t)(B * (H / hb) * L * N) * 4);
+  const size_t ph = align256((size_t)(B * nch * H) * 4);
+  const size_t pd = align256((size_t)(B * nch * H * P) * 4);
+  return 2 * st + 2 * gg + 2 * bt + sp + 2 * part + 2 * ph + pd;
+}
+
+void ssd_bwd_workspace_carve(SsdBwdParams& bp, void* ws) {
+  SsdParams& p = bp.f;
+  const int64_t Q = kQb, nch = (p.L + Q - 1) / Q;
+  const size_t st = align256((size_t)(p.B * nch * p.H * p.P * p.N) * 2);
+  const size_t gg = align256((size_t)(p.B * p.G * nch * Q * Q) * 4);
+  const size_t bt = align256((size_t)(p.B * p.G * nch * p.N * Q) * 2);
+  const size_t sp = align256((size_t)(p.B * nch * p.H * Q) * 8);
+  const size_t part = align256((size_t)(p.B * (p.H / bp.hb) * p.L * p.N) * 4);
+  const size_t ph = align256((size_t)(p.B * nch * p.H) * 4);
+  char* base = static_cast<char*>(ws);
+  p.ws_hin = base; base += st;
+  p.ws_gout = base; base += st;
+  p.ws_G = base; base += gg;
+  p.ws_GT = base; base += gg;
+  p.ws_Bt = base; base += bt;
+  p.ws_Ct = base; base += bt;
+  p.ws_sphi = reinterpret_cast<float2*>(base); base += sp;
+  bp.ws_dBp = reinterpret_cast<float*>(base); base += part;
+  bp.ws_dCp = reinterpret_cast<float*>(base); base += part;
+  bp.ws_pA = reinterpret_cast<float*>(base); base += ph;
+  bp.ws_pb = reinterpret_cast<float*>(base); base += ph;
+  bp.ws_pD = reinterpret_cast<float*>(base);
+}
+
+hipError_t launch_ssd_bwd(const SsdBwdParams& bp, hipStream_t stream) {
+  if (bp.f.N == 128) return launch_n<128>(bp, stream);
+  if (bp.f.N == 64) return launch_n<64>(bp, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ssm

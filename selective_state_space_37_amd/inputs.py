@@ -187,6 +187,15 @@ def scan_grads(seed: int, Bsz: int, L: int, D: int, N: int, dtype: str = "f32",
     return dy, dhl
 
 
+def ssd_grads(seed: int, Bsz: int, L: int, H: int, P: int, N: int, dtype: str = "bf16",
+              dh_last: bool = True):
+    """Upstream gradients for the SSD backward: dL/dy ~ N(0, 1) stored like x [B, L, H, P], and
+    dL/dh_last ~ N(0, 1) fp32 [B, H, P, N] (or None)."""
+    dy = store(draw_tokens(seed, TID_DY, Bsz, L, H * P).reshape(Bsz, L, H, P), dtype)
+    dhl = draw_param(seed, TID_DHLAST, (Bsz, H, P, N)) if dh_last else None
+    return dy, dhl
+
+
 @dataclass
 class DecodeStep:
     x: np.ndarray       # [B, D]

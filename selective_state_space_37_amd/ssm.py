@@ -25,7 +25,8 @@ EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_last_error_detail",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd",
            "ssm_scan_bwd_segmented_workspace_bytes", "ssm_scan_bwd_segmented",
            "ssm_state_update", "ssd_chunk_fwd_workspace_bytes", "ssd_chunk_fwd",
-           "ssd_chunk_fwd_grouped_workspace_bytes", "ssd_chunk_fwd_grouped")
+           "ssd_chunk_fwd_grouped_workspace_bytes", "ssd_chunk_fwd_grouped",
+           "ssd_chunk_bwd_workspace_bytes", "ssd_chunk_bwd")
 
 _lib = None
 
@@ -86,6 +87,10 @@ def load(path: str = LIB_PATH):
     lib.ssd_chunk_fwd_grouped.argtypes = [i64, i64, i64, i64, i64, i64, i64, ci, vp, vp, vp, ci, vp, vp,
                                           vp, vp, ci, vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_chunk_fwd_grouped.restype = ci
+    lib.ssd_chunk_bwd_workspace_bytes.argtypes = [i64] * 6 + [ci]
+    lib.ssd_chunk_bwd_workspace_bytes.restype = sz
+    lib.ssd_chunk_bwd.argtypes = [i64] * 6 + [ci, vp, vp, vp, ci, vp, vp, vp, vp, ci] + [vp] * 13 + [vp, sz, vp]
+    lib.ssd_chunk_bwd.restype = ci
     _lib = lib
     return lib
 
@@ -351,3 +356,49 @@ def ssd_chunk_fwd_grouped(x, delta, A, Bm, Cm, *, chunk: int = 256, delta_bias=N
                                    _stream(x))
     _check(st)
     return y, h_last
+
+
+def ssd_chunk_bwd(x, delta, A, Bm, Cm, dy, *, delta_bias=None, delta_softplus=False, Dskip=None, z=None,
+                  h0=None, dh_last=None, want_dh0=True, ws: Optional[torch.Tensor] = None) -> dict:
+    """Gradients of ssd_chunk_fwd_grouped. Bm, Cm: [B, L, G, N] (or [B, L, N] for one group);
+    Dskip [H] or [H, P]. Returns a dict: dx, dz (None without z) [B, L, H, P] and ddelta [B, L, H]
+    in the input dtype; dA, ddelta_bias [H], dDskip (shaped like Dskip, [H] without it), dBm,
+    dCm (shaped like Bm) and dh0 [B, H, P, N] in float32."""
+    lib = load()
+    Bsz, L, H, P = x.shape
+    one_group = Bm.dim() == 3
+    if one_group:
+        Bm, Cm = Bm.unsqueeze(2), Cm.unsqueeze(2)
+    G, N = Bm.shape[2], Bm.shape[3]
+    io = x.dtype
+    _dev(x, "x")
+    _dev(delta, "delta", io, (Bsz, L, H))
+    _dev(z, "z", io, (Bsz, L, H, P))
+    _dev(Bm, "Bm", io, (Bsz, L, G, N))
+    _dev(Cm, "Cm", io, (Bsz, L, G, N))
+    _dev(dy, "dy", io, (Bsz, L, H, P))
+    _dev(A, "A", torch.float32, (H,))
+    _dev(delta_bias, "delta_bias", torch.float32, (H,))
+    per_channel = Dskip is not None and Dskip.dim() == 2
+    _dev(Dskip, "Dskip", torch.float32, (H, P) if per_channel else (H,))
+    _dev(h0, "h0", torch.float32, (Bsz, H, P, N))
+    _dev(dh_last, "dh_last", torch.float32, (Bsz, H, P, N))
+    f32 = dict(dtype=torch.float32, device=x.device)
+    out = dict(dx=torch.empty_like(x), ddelta=torch.empty_like(delta), dz=torch.empty_like(x) if z is not None else None,
+               dA=torch.empty(H, **f32), dBm=torch.empty((Bsz, L, G, N), **f32), dCm=torch.empty((Bsz, L, G, N), **f32),
+               dDskip=torch.empty((H, P) if per_channel else (H,), **f32), ddelta_bias=torch.empty(H, **f32),
+               dh0=torch.empty((Bsz, H, P, N), **f32) if want_dh0 else None)
+    code = _io_code(x)
+    nb = lib.ssd_chunk_bwd_workspace_bytes(Bsz, L, H, P, N, G, code)
+    if ws is None or ws.numel() < nb:
+        ws = workspace(nb, x.device)
+    st = lib.ssd_chunk_bwd(Bsz, L, H, P, N, G, code, _p(x), _p(delta), _p(delta_bias), int(bool(delta_softplus)),
+                           _p(A), _p(Bm), _p(Cm), _p(Dskip), int(per_channel), _p(z), _p(h0), _p(dy), _p(dh_last),
+                           _p(out["dx"]), _p(out["ddelta"]), _p(out["dA"]), _p(out["dBm"]), _p(out["dCm"]),
+                           _p(out["dDskip"]), _p(out["ddelta_bias"]), _p(out["dz"]), _p(out["dh0"]), _p(ws), nb,
+                           _stream(x))
+    _check(st)
+    if one_group:
+        out["dBm"], out["dCm"] = out["dBm"][:, :, 0], out["dCm"][:, :, 0]
+    return out
+

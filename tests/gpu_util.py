@@ -204,6 +204,54 @@ def ssd_oracle(inp: inputs.SSDInputs, heads=None):
     return np.concatenate(ys, axis=2), np.concatenate(hls, axis=1)
 
 
+def ssd_bwd_on_gpu(inp: inputs.SSDInputs, dy, dh_last=None):
+    out = ssm.ssd_chunk_bwd(dev(inp.x), dev(inp.delta), dev(inp.A), dev(inp.Bm), dev(inp.Cm), dev(dy),
+                            delta_bias=dev(inp.delta_bias), delta_softplus=inp.delta_softplus,
+                            Dskip=dev(inp.Dskip), z=dev(inp.z), h0=dev(inp.h0), dh_last=dev(dh_last))
+    torch.cuda.synchronize()
+    return {k: host(v) for k, v in out.items()}
+
+
+def ssd_bwd_oracle(inp: inputs.SSDInputs, dy, dh_last=None, heads=None):
+    """Oracle gradients; heads restricts to a head subset, each run with its own group's B and C
+    (everything but dBm, dCm then matches the full problem's values on those heads)."""
+    w = lambda a: inputs.widen(a, inp.dtype)
+    H = inp.x.shape[2]
+    kw = dict(delta_softplus=inp.delta_softplus)
+    if heads is None:
+        return oracle.ssd_bwd(w(inp.x), w(inp.delta), inp.A, w(inp.Bm), w(inp.Cm), w(dy),
+                              delta_bias=inp.delta_bias, Dskip=inp.Dskip, z=w(inp.z), h0=inp.h0,
+                              dh_last=dh_last, **kw)
+    G = inp.groups
+    outs = []
+    for h in heads:
+        grp = h // (H // G)
+        one = lambda a, ax: None if a is None else np.take(a, [h], axis=ax)
+        Bm = w(inp.Bm)[:, :, grp] if inp.Bm.ndim == 4 else w(inp.Bm)
+        Cm = w(inp.Cm)[:, :, grp] if inp.Cm.ndim == 4 else w(inp.Cm)
+        outs.append(oracle.ssd_bwd(one(w(inp.x), 2), one(w(inp.delta), 2), one(inp.A, 0), Bm, Cm,
+                                   one(w(dy), 2), delta_bias=one(inp.delta_bias, 0), Dskip=one(inp.Dskip, 0),
+                                   z=one(w(inp.z), 2), h0=one(inp.h0, 1), dh_last=one(dh_last, 1), **kw))
+    ax = {"dx": 2, "ddelta": 2, "dz": 2, "dA": 0, "dDskip": 0, "ddelta_bias": 0, "dh0": 1}
+    return {k: (None if outs[0][k] is None else np.concatenate([o[k] for o in outs], axis=a))
+            for k, a in ax.items()}
+
+
+def ssd_bwd_errors(gpu: dict, ref: dict, heads=None) -> dict:
+    errs = {}
+    ax = {"dx": 2, "ddelta": 2, "dz": 2, "dA": 0, "dDskip": 0, "ddelta_bias": 0, "dh0": 1}
+    for k in BWD_KEYS:
+        g, r = gpu.get(k), ref.get(k)
+        if r is None or g is None:
+            continue
+        if heads is not None:
+            if k in ("dBm", "dCm"):
+                continue
+            g = np.take(g, heads, axis=ax[k])
+        errs[k] = rel_err(g, r)
+    return errs
+
+
 def ssd_parity(inp, gpu_out, heads=None) -> float:
     y, hl = gpu_out
     ry, rh = ssd_oracle(inp, heads)

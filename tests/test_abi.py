@@ -186,6 +186,32 @@ def test_ssd_grouped_rejects(lib, kw, expect):
     assert ssd_grouped_call(lib, **kw) == expect
 
 
+def ssd_bwd_call(lib, B=1, L=100, H=4, P=64, N=128, G=2, io=BF16, z=None, dz=None, dDskip=None, dx=20 * A_,
+                 ws=40 * A_, wsb=1 << 40, A=3 * A_, dA=30 * A_):
+    f = lambda v: fake(v) if v else None
+    return lib.ssd_chunk_bwd(B, L, H, P, N, G, io, fake(A_), fake(2 * A_), None, 0, f(A), fake(4 * A_), fake(5 * A_),
+                             None, 0, f(z), None, fake(6 * A_), None, f(dx), fake(21 * A_), f(dA), fake(31 * A_),
+                             fake(32 * A_), f(dDskip), None, f(dz), None, f(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(io=F32), UNSUPPORTED), (dict(P=32), UNSUPPORTED), (dict(N=16), UNSUPPORTED), (dict(G=3), INVALID),
+    (dict(G=0), INVALID), (dict(A=0), INVALID), (dict(dA=0), INVALID), (dict(dx=0), INVALID),
+    (dict(z=7 * A_), INVALID), (dict(dx=A_), INVALID), (dict(dDskip=21 * A_), INVALID),
+    (dict(ws=0, wsb=0), WS_SMALL), (dict(wsb=64), WS_SMALL), (dict(dx=20 * A_ + 4), INVALID),
+    (dict(L=65536 * 64 + 1), UNSUPPORTED),
+])
+def test_ssd_bwd_rejects(lib, kw, expect):
+    assert ssd_bwd_call(lib, **kw) == expect
+
+
+def test_ssd_bwd_workspace(lib):
+    """Per 64-token chunk and head: the entering state and the adjoint of the leaving one (bf16)."""
+    nb = lib.ssd_chunk_bwd_workspace_bytes(2, 8192, 80, 64, 128, 1, BF16)
+    assert nb >= 2 * (2 * 128 * 80 * 64 * 128 * 2)
+    assert lib.ssd_chunk_bwd_workspace_bytes(2, 8192, 80, 64, 128, 3, BF16) == 0   # 3 does not divide 80
+
+
 def test_ssd_grouped_workspace(lib):
     """Per group: C B^T and transposed B per chunk; G = 1 is the ungrouped layout."""
     one = lib.ssd_chunk_fwd_workspace_bytes(2, 8192, 80, 64, 128, 256, BF16)

@@ -232,11 +232,10 @@ ssm_status scan_bwd_common(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype
 }
 
 // Heads per workgroup in the SSD backward's main pass (their dB and dC are summed in registers
-// before one partial per workgroup is written): a divisor of the heads per group.
+// before one partial per workgroup is written): a divisor of the heads per group. Four cut the
+// partial sums' traffic fourfold and measured fastest at 80 heads (1, 2, 4, 5, 8, 10 tried).
 int64_t ssd_bwd_heads_per_wg(int64_t H, int64_t G) {
-  (void)H;
-  (void)G;
-  return 1;
+  return (H / G) % 4 == 0 ? 4 : 1;
 }
 
 }  // namespace

@@ -53,27 +53,35 @@ __device__ __forceinline__ void unpack8(uint4 v, float out[8]) {
   }
 }
 
-// grid (H / hb, chunks, B), 256 threads. Wave w owns token tile w (tokens 16 w .. 16 w + 15 of the
-// chunk) in both roles: as the rows i of dC, y and dz and as the columns j of dB, dx and w. The
-// MFMA products are oriented so that the outputs come out with four consecutive states or
-// channels per lane (one 8- or 16-byte store), and a product that feeds another (W) comes out in
-// the operand layout of the next one: two 16-token tiles per K = 32 step, four tokens of each per
+// grid (H / hb, chunks, B), 512 threads. Token tile tt = w % 4 (tokens 16 tt .. 16 tt + 15 of the
+// chunk) belongs to waves tt and tt + 4, which split the work by halves (hf = w / 4): of the
+// states n for dB and dC, of the channels p for y, dz, dx. Each of the two computes the U tiles
+// its products need itself (a few MFMAs) rather than passing them through LDS. A tile is used in
+// both roles: as the rows i of dC, y and dz and as the columns j of dB, dx and w. The MFMA
+// products are oriented so that the outputs come out with four consecutive states or channels
+// per lane (one 8- or 16-byte store), and a product that feeds another (W) comes out in the
+// operand layout of the next one: two 16-token tiles per K = 32 step, four tokens of each per
 // lane, the same K order on both operands. dB and dC are summed over the workgroup's hb heads
 // (consecutive heads of one group) in registers.
 template <int N>
-__global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
+__global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
   constexpr int Q = kQb;
   constexpr int NT = N / 16;   // 16-state tiles
+  constexpr int NTH = NT / 2;  // per half
   constexpr int KSN = N / 32;  // K steps over the states
-  constexpr int RS = Q + 8;    // row stride (bf16) of the transposed token tiles
+  constexpr int RS = Q + 8;    // row stride (bf16) of the token tiles
   constexpr int RSP = kP + 8;  // row stride (bf16) of the transposed states
   constexpr int KST = Q + 1;   // row stride (float) of K
+  __shared__ __attribute__((aligned(16))) __bf16 Xn[Q * RS];     // x [j][p]
+  __shared__ __attribute__((aligned(16))) __bf16 Yhi[Q * RS];    // ybar [i][p], bf16 rounded
+  __shared__ __attribute__((aligned(16))) __bf16 Ylo[Q * RS];    // ybar - Yhi, bf16 rounded
   __shared__ __attribute__((aligned(16))) __bf16 YT[kP * RS];    // ybar^T [p][i]
   __shared__ __attribute__((aligned(16))) __bf16 XT[kP * RS];    // (phi x)^T [p][j] (gate only)
   __shared__ __attribute__((aligned(16))) __bf16 HT[N * RSP];    // H_c^T [n][p]
   __shared__ __attribute__((aligned(16))) __bf16 GcT[N * RSP];   // Gc^T [n][p]
   __shared__ float sK[Q * KST];
-  __shared__ float sS[Q], sPhi[Q], sQv[Q], sRv[Q], sVv[Q], sRt[Q], sRed[4];
+  __shared__ float sS[Q], sPhi[Q], sRt[Q], sRed[8];
+  __shared__ float sQv[2][Q], sRv[2][Q], sVv[2][Q];
   __shared__ float sDD[4][kP];
 
   const SsdParams& p = bp.f;
@@ -81,6 +89,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
   // the wave index is the same for all lanes of a wave: readfirstlane lets the compiler keep it
   // (and the tile loops over it) in scalar registers, so branches on it are not divergent
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tt = w & 3, hf = w >> 2;
   const int64_t hblk = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
   const int64_t nch = gridDim.y;
   const int64_t L = p.L, H = p.H;
@@ -95,15 +104,21 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
   const bf16_t* Btm = static_cast<const bf16_t*>(p.ws_Bt) + (bg * nch + c) * (int64_t)(N * Q);
   const bf16_t* Ctm = static_cast<const bf16_t*>(p.ws_Ct) + (bg * nch + c) * (int64_t)(N * Q);
   const int64_t tc0 = c * Q;      // first token of the chunk
-  const int i0 = w * 16;          // this wave's token tile
-  const int il = i0 + r16;        // this lane's token in the chunk (column role)
+  const int il = tt * 16 + r16;   // this lane's token in the chunk (column role)
   const int64_t tl = tc0 + il;
   const bool lane_valid = tl < L;
   const int64_t tstride = H * kP;  // token stride of x, dy, z
 
-  f32x4 dC[NT], dB[NT];
+  // fragments of the staged tiles: token row t of the chunk, channels p0 .. p0 + 7. ybar is held
+  // as hi + lo (hi = ybar rounded to bf16, lo = the rounding error rounded), so products with x
+  // (exactly bf16) lose nothing to the operand rounding.
+  auto x8 = [&](int t, int p0) { return *reinterpret_cast<const bf16x8*>(&Xn[t * RS + p0]); };
+  auto yhi8 = [&](int t, int p0) { return *reinterpret_cast<const bf16x8*>(&Yhi[t * RS + p0]); };
+  auto ylo8 = [&](int t, int p0) { return *reinterpret_cast<const bf16x8*>(&Ylo[t * RS + p0]); };
+
+  f32x4 dC[NTH], dB[NTH];
 #pragma unroll
-  for (int k = 0; k < NT; ++k) dC[k] = dB[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < NTH; ++k) dC[k] = dB[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int64_t kh = 0; kh < bp.hb; ++kh) {
     const int64_t h = hblk * bp.hb + kh;
@@ -118,48 +133,23 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
     const float dhead = p.Dskip && !p.dskip_per_channel ? p.Dskip[h] : 0.f;
     auto dskip = [&](int ch) { return dpc ? p.Dskip[h * kP + ch] : dhead; };
 
-    // ybar (dy times the gate factor) of token t, channels p0 .. p0 + 7, as two MFMA fragments
-    // whose sum is ybar to about 16 bits (hi = ybar rounded to bf16, lo = the rounding error
-    // rounded): products with x (exactly bf16) then lose nothing to the operand rounding
-    auto ybar8 = [&](int64_t t, int p0, bf16x8& hi, bf16x8& lo) {
-      if (t >= L) {
-        hi = lo = zero_frag();
-        return;
-      }
-      const uint4 d = *reinterpret_cast<const uint4*>(dyh + t * tstride + p0);
-      if (!zh) {
-        hi = __builtin_bit_cast(bf16x8, d);
-        lo = zero_frag();
-        return;
-      }
-      float dv[8], zv[8];
-      unpack8(d, dv);
-      unpack8(*reinterpret_cast<const uint4*>(zh + t * tstride + p0), zv);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float v = dv[q] * silu(zv[q]);
-        hi[q] = (__bf16)v;
-        lo[q] = (__bf16)(v - (float)hi[q]);
-      }
-    };
-    auto x8 = [&](int64_t t, int p0) -> bf16x8 {
-      return t < L ? load_frag(xh + t * tstride + p0) : zero_frag();
-    };
-
     // ------------------------------------------------------------------ staging
     if (tid < Q) {
       const float2 v = sp[tid];
       sS[tid] = v.x;
       sPhi[tid] = v.y;
     }
-    {
-      // ybar^T (and (phi x)^T with a gate): token pair ip, channels 8 pg8 .. 8 pg8 + 7. Lanes
-      // 0..31 of a wave write 32 consecutive words of a row, lanes 32..63 the rows 8 further
-      // (288 words on): the 64 writes fall on 64 banks.
+    float dot = 0.f;   // <Gc, H_c> over this thread's pieces
+    if (tid < 256) {
+      // token pair ip, channels 8 pg8 .. 8 pg8 + 7: x and ybar (natural, and ybar^T; (phi x)^T
+      // with a gate). Lanes 0..31 of a wave write 32 consecutive words of a transposed row, lanes
+      // 32..63 the rows 8 further (288 words on): the 64 writes fall on 64 banks.
       const int ip = tid & 31, pg8 = tid >> 5;
       float y0[8], y1[8];
       const int64_t t = tc0 + 2 * ip;
       const uint4 zero4 = make_uint4(0, 0, 0, 0);
+      const uint4 xa = t < L ? *reinterpret_cast<const uint4*>(xh + t * tstride + 8 * pg8) : zero4;
+      const uint4 xb = t + 1 < L ? *reinterpret_cast<const uint4*>(xh + (t + 1) * tstride + 8 * pg8) : zero4;
       const uint4 d0 = t < L ? *reinterpret_cast<const uint4*>(dyh + t * tstride + 8 * pg8) : zero4;
       const uint4 d1 = t + 1 < L ? *reinterpret_cast<const uint4*>(dyh + (t + 1) * tstride + 8 * pg8) : zero4;
       unpack8(d0, y0);
@@ -176,8 +166,6 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
           y1[k] *= silu(zv1[k]);
         }
         // (phi x)^T for the recomputed within-chunk output
-        const uint4 xa = t < L ? *reinterpret_cast<const uint4*>(xh + t * tstride + 8 * pg8) : zero4;
-        const uint4 xb = t + 1 < L ? *reinterpret_cast<const uint4*>(xh + (t + 1) * tstride + 8 * pg8) : zero4;
         float xv0[8], xv1[8];
         unpack8(xa, xv0);
         unpack8(xb, xv1);
@@ -192,23 +180,37 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
 #pragma unroll
       for (int k = 0; k < 8; ++k)
         Y32[(8 * pg8 + k) * (RS / 2) + ip] = (uint32_t)f32_to_bf16(y0[k]) | ((uint32_t)f32_to_bf16(y1[k]) << 16);
-    }
-    float dot = 0.f;   // <Gc, H_c> over this thread's pieces
-    for (int item = tid; item < 32 * (N / 8); item += 256) {
-      // channels (2 pp, 2 pp + 1), states 8 ng .. 8 ng + 7 of H_c and Gc, written transposed
-      const int pp = item & 31, ng = item >> 5;
-      float h0v[8], h1v[8], g0v[8], g1v[8];
-      unpack8(*reinterpret_cast<const uint4*>(hin + (2 * pp) * N + 8 * ng), h0v);
-      unpack8(*reinterpret_cast<const uint4*>(hin + (2 * pp + 1) * N + 8 * ng), h1v);
-      unpack8(*reinterpret_cast<const uint4*>(gout + (2 * pp) * N + 8 * ng), g0v);
-      unpack8(*reinterpret_cast<const uint4*>(gout + (2 * pp + 1) * N + 8 * ng), g1v);
-      uint32_t* H32 = reinterpret_cast<uint32_t*>(HT);
-      uint32_t* G32 = reinterpret_cast<uint32_t*>(GcT);
+      float h0[8], h1[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        H32[(8 * ng + k) * (RSP / 2) + pp] = (uint32_t)f32_to_bf16(h0v[k]) | ((uint32_t)f32_to_bf16(h1v[k]) << 16);
-        G32[(8 * ng + k) * (RSP / 2) + pp] = (uint32_t)f32_to_bf16(g0v[k]) | ((uint32_t)f32_to_bf16(g1v[k]) << 16);
-        dot += h0v[k] * g0v[k] + h1v[k] * g1v[k];
+        h0[k] = (float)(__bf16)y0[k];
+        h1[k] = (float)(__bf16)y1[k];
+        y0[k] -= h0[k];
+        y1[k] -= h1[k];
+      }
+      *reinterpret_cast<bf16x8*>(&Yhi[(2 * ip) * RS + 8 * pg8]) = pack8(h0);
+      *reinterpret_cast<bf16x8*>(&Yhi[(2 * ip + 1) * RS + 8 * pg8]) = pack8(h1);
+      *reinterpret_cast<bf16x8*>(&Ylo[(2 * ip) * RS + 8 * pg8]) = pack8(y0);
+      *reinterpret_cast<bf16x8*>(&Ylo[(2 * ip + 1) * RS + 8 * pg8]) = pack8(y1);
+      *reinterpret_cast<uint4*>(&Xn[(2 * ip) * RS + 8 * pg8]) = xa;
+      *reinterpret_cast<uint4*>(&Xn[(2 * ip + 1) * RS + 8 * pg8]) = xb;
+    } else {
+      for (int item = tid - 256; item < 32 * (N / 8); item += 256) {
+        // channels (2 pp, 2 pp + 1), states 8 ng .. 8 ng + 7 of H_c and Gc, written transposed
+        const int pp = item & 31, ng = item >> 5;
+        float h0v[8], h1v[8], g0v[8], g1v[8];
+        unpack8(*reinterpret_cast<const uint4*>(hin + (2 * pp) * N + 8 * ng), h0v);
+        unpack8(*reinterpret_cast<const uint4*>(hin + (2 * pp + 1) * N + 8 * ng), h1v);
+        unpack8(*reinterpret_cast<const uint4*>(gout + (2 * pp) * N + 8 * ng), g0v);
+        unpack8(*reinterpret_cast<const uint4*>(gout + (2 * pp + 1) * N + 8 * ng), g1v);
+        uint32_t* H32 = reinterpret_cast<uint32_t*>(HT);
+        uint32_t* G32 = reinterpret_cast<uint32_t*>(GcT);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          H32[(8 * ng + k) * (RSP / 2) + pp] = (uint32_t)f32_to_bf16(h0v[k]) | ((uint32_t)f32_to_bf16(h1v[k]) << 16);
+          G32[(8 * ng + k) * (RSP / 2) + pp] = (uint32_t)f32_to_bf16(g0v[k]) | ((uint32_t)f32_to_bf16(g1v[k]) << 16);
+          dot += h0v[k] * g0v[k] + h1v[k] * g1v[k];
+        }
       }
     }
 #pragma unroll
@@ -222,26 +224,30 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
     bf16x8 yb_own[2], yb_lo[2], x_own[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      ybar8(tl, 32 * kk + 8 * g, yb_own[kk], yb_lo[kk]);
-      x_own[kk] = x8(tl, 32 * kk + 8 * g);
+      yb_own[kk] = yhi8(il, 32 * kk + 8 * g);
+      yb_lo[kk] = ylo8(il, 32 * kk + 8 * g);
+      x_own[kk] = x8(il, 32 * kk + 8 * g);
     }
 
     // ------------------------------------------------------------------ dC (rows i = own tile)
     {
-      // U^T tiles (j tile jt <= w, i = own): D[j][i] = sum_p x_j[p] ybar_i[p]; the lane holds
-      // U[il][jt 16 + 4 g + r]. W (as the B operand of the next product) and K (to LDS).
+      // U^T tiles (j tile jt <= tt, i = own): D[j][i] = sum_p x_j[p] ybar_i[p]; the lane holds
+      // U[il][jt 16 + 4 g + r]. W (as the B operand of the next product) and K (to LDS, by the
+      // first half).
       bf16x8 wmA[2] = {zero_frag(), zero_frag()};
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt) {
-        if (jt > w) {
+        if (jt > tt) {
+          if (hf == 0) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sK[il * KST + jt * 16 + 4 * g + r] = 0.f;
+            for (int r = 0; r < 4; ++r) sK[il * KST + jt * 16 + 4 * g + r] = 0.f;
+          }
           continue;
         }
         f32x4 u = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 xa = x8(tc0 + jt * 16 + r16, 32 * kk + 8 * g);
+          const bf16x8 xa = x8(jt * 16 + r16, 32 * kk + 8 * g);
           u = mfma16(xa, yb_own[kk], u);
           u = mfma16(xa, yb_lo[kk], u);
         }
@@ -251,7 +257,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
         for (int r = 0; r < 4; ++r) {
           const int j = jt * 16 + 4 * g + r;
           const float wm = j <= il ? exp2_fast(a2 * (Sl - sS[j])) * sPhi[j] * u[r] : 0.f;
-          sK[il * KST + j] = gv[r] * wm;
+          if (hf == 0) sK[il * KST + j] = gv[r] * wm;
           wmA[jt >> 1][(jt & 1) * 4 + r] = (__bf16)wm;
         }
       }
@@ -263,12 +269,12 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) yb_sc[kk][q] = (__bf16)(((float)yb_own[kk][q] + (float)yb_lo[kk][q]) * eSi);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        f32x4 acc = dC[nt];
-        const int n = nt * 16 + r16;
+      for (int k = 0; k < NTH; ++k) {
+        f32x4 acc = dC[k];
+        const int n = (hf * NTH + k) * 16 + r16;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          if (2 * kk > w) break;   // the pair holds no tile j <= i
+          if (2 * kk > tt) break;   // the pair holds no tile j <= i
           const uint2 lo = *reinterpret_cast<const uint2*>(Btm + n * Q + 32 * kk + 4 * g);
           const uint2 hi = *reinterpret_cast<const uint2*>(Btm + n * Q + 32 * kk + 16 + 4 * g);
           acc = mfma16(frag_from_pieces(lo, hi), wmA[kk], acc);   // D[n][i] = sum_j B_j[n] W_ij
@@ -276,28 +282,26 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
           acc = mfma16(*reinterpret_cast<const bf16x8*>(&HT[n * RSP + 32 * kk + 8 * g]), yb_sc[kk], acc);
-        dC[nt] = acc;
+        dC[k] = acc;
       }
     }
 
     // ------------------------------------------------------------------ dB (columns j = own tile)
     // vin: this lane's part of x_j . sum_{i>=j} (C_i . B_j) exp(a (S_i - S_j)) ybar_i, formed in
-    // float32 from U (the within-chunk part of x_j . w_j, for dDelta)
+    // float32 from U (the within-chunk part of x_j . w_j, for dDelta; kept by the first half)
     float vin = 0.f;
     {
-      // U tiles (i tile it >= w, j = own): D[i][j] = sum_p ybar_i[p] x_j[p]; the lane holds
+      // U tiles (i tile it >= tt, j = own): D[i][j] = sum_p ybar_i[p] x_j[p]; the lane holds
       // U[it 16 + 4 g + r][il].
       bf16x8 wmB[2] = {zero_frag(), zero_frag()};
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-        if (it < w) continue;
+        if (it < tt) continue;
         f32x4 u = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          bf16x8 yh, yl;
-          ybar8(tc0 + it * 16 + r16, 32 * kk + 8 * g, yh, yl);
-          u = mfma16(yh, x_own[kk], u);
-          u = mfma16(yl, x_own[kk], u);
+          u = mfma16(yhi8(it * 16 + r16, 32 * kk + 8 * g), x_own[kk], u);
+          u = mfma16(ylo8(it * 16 + r16, 32 * kk + 8 * g), x_own[kk], u);
         }
         const float4 g4 = *reinterpret_cast<const float4*>(GTm + il * Q + it * 16 + 4 * g);   // G[i][il]
         const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
@@ -309,6 +313,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
           wmB[it >> 1][(it & 1) * 4 + r] = (__bf16)(e * phil * u[r]);
         }
       }
+      if (hf != 0) vin = 0.f;
       const float eq = exp2_fast(a2 * (Sq - Sl)) * phil;
       bf16x8 x_sc[2];
 #pragma unroll
@@ -316,12 +321,12 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) x_sc[kk][q] = (__bf16)((float)x_own[kk][q] * eq);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        f32x4 acc = dB[nt];
-        const int n = nt * 16 + r16;
+      for (int k = 0; k < NTH; ++k) {
+        f32x4 acc = dB[k];
+        const int n = (hf * NTH + k) * 16 + r16;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          if (2 * kk + 1 < w) continue;   // the pair holds no tile i >= j
+          if (2 * kk + 1 < tt) continue;   // the pair holds no tile i >= j
           const uint2 lo = *reinterpret_cast<const uint2*>(Ctm + n * Q + 32 * kk + 4 * g);
           const uint2 hi = *reinterpret_cast<const uint2*>(Ctm + n * Q + 32 * kk + 16 + 4 * g);
           acc = mfma16(frag_from_pieces(lo, hi), wmB[kk], acc);   // D[n][j] = sum_i C_i[n] W_ij
@@ -329,16 +334,17 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
           acc = mfma16(*reinterpret_cast<const bf16x8*>(&GcT[n * RSP + 32 * kk + 8 * g]), x_sc[kk], acc);
-        dB[nt] = acc;
+        dB[k] = acc;
       }
     }
 
     // ------------------------------------------------------------------ y (rows i = own tile)
     // Yoff[p][i] = exp(a S_i) sum_n H_c[p][n] C_i[n]; with a gate also the within-chunk part
     // Ydiag[p][i] = sum_{j<=i} (C_i . B_j) exp(a (S_i - S_j)) phi_j x_j[p] for the pre-gate output.
-    f32x4 yo[4], yd[4];
+    // This half's channel tiles: pt = 2 hf, 2 hf + 1.
+    f32x4 yo[2], yd[2];
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) yo[pt] = yd[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < 2; ++k) yo[k] = yd[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
       const float eSi = exp2_fast(a2 * Sl);
 #pragma unroll
@@ -347,19 +353,19 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) cf[q] = (__bf16)((float)cf[q] * eSi);
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-          yo[pt] = mfma16(load_frag(hin + (pt * 16 + r16) * N + 32 * ks + 8 * g), cf, yo[pt]);
+        for (int k = 0; k < 2; ++k)
+          yo[k] = mfma16(load_frag(hin + ((2 * hf + k) * 16 + r16) * N + 32 * ks + 8 * g), cf, yo[k]);
       }
     }
     if (zh) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        if (2 * kk > w) break;
+        if (2 * kk > tt) break;
         float gl[8];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int jt = 2 * kk + half;
-          if (jt <= w) {
+          if (jt <= tt) {
             const float4 g4 = *reinterpret_cast<const float4*>(Gm + il * Q + jt * 16 + 4 * g);
             const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
@@ -374,41 +380,48 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
         }
         const bf16x8 glf = pack8(gl);
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-          const uint2 lo = *reinterpret_cast<const uint2*>(&XT[(pt * 16 + r16) * RS + 32 * kk + 4 * g]);
-          const uint2 hi = *reinterpret_cast<const uint2*>(&XT[(pt * 16 + r16) * RS + 32 * kk + 16 + 4 * g]);
-          yd[pt] = mfma16(frag_from_pieces(lo, hi), glf, yd[pt]);
+        for (int k = 0; k < 2; ++k) {
+          const int row = ((2 * hf + k) * 16 + r16) * RS;
+          const uint2 lo = *reinterpret_cast<const uint2*>(&XT[row + 32 * kk + 4 * g]);
+          const uint2 hi = *reinterpret_cast<const uint2*>(&XT[row + 32 * kk + 16 + 4 * g]);
+          yd[k] = mfma16(frag_from_pieces(lo, hi), glf, yd[k]);
         }
       }
     }
-    // epilogue: the lane holds channels pt 16 + 4 g + r of token il
-    float ybv[4][4], xv[4][4];
+    // epilogue: the lane holds channels pt 16 + 4 g + r (pt = 2 hf + k) of token il
+    float ybv[2][4], xv[2][4];
     float qpart = 0.f;
     {
-      float dd[4][4];
+      float dd[2][4];
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
+      for (int k = 0; k < 2; ++k) {
+        const int pt = 2 * hf + k;
         const int64_t o = tl * tstride + pt * 16 + 4 * g;
-        const uint2 dr = lane_valid ? *reinterpret_cast<const uint2*>(dyh + o) : make_uint2(0, 0);
-        const uint2 xr = lane_valid ? *reinterpret_cast<const uint2*>(xh + o) : make_uint2(0, 0);
-        const float dv[4] = {bf16_lo(dr.x), bf16_hi(dr.x), bf16_lo(dr.y), bf16_hi(dr.y)};
+        const int lo = il * RS + pt * 16 + 4 * g;
+        const uint2 xr = *reinterpret_cast<const uint2*>(&Xn[lo]);
+        const uint2 yhr = *reinterpret_cast<const uint2*>(&Yhi[lo]);
+        const uint2 ylr = *reinterpret_cast<const uint2*>(&Ylo[lo]);
         const float xx[4] = {bf16_lo(xr.x), bf16_hi(xr.x), bf16_lo(xr.y), bf16_hi(xr.y)};
-        float zv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (zh) {
-          const uint2 zr = lane_valid ? *reinterpret_cast<const uint2*>(zh + o) : make_uint2(0, 0);
+        const float ybr[4] = {bf16_lo(yhr.x) + bf16_lo(ylr.x), bf16_hi(yhr.x) + bf16_hi(ylr.x),
+                              bf16_lo(yhr.y) + bf16_lo(ylr.y), bf16_hi(yhr.y) + bf16_hi(ylr.y)};
+        float dv[4] = {0.f, 0.f, 0.f, 0.f}, zv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (zh && lane_valid) {
+          const uint2 dr = *reinterpret_cast<const uint2*>(dyh + o);
+          const uint2 zr = *reinterpret_cast<const uint2*>(zh + o);
+          dv[0] = bf16_lo(dr.x); dv[1] = bf16_hi(dr.x); dv[2] = bf16_lo(dr.y); dv[3] = bf16_hi(dr.y);
           zv[0] = bf16_lo(zr.x); zv[1] = bf16_hi(zr.x); zv[2] = bf16_lo(zr.y); zv[3] = bf16_hi(zr.y);
         }
         float dzv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int ch = pt * 16 + 4 * g + r;
-          xv[pt][r] = xx[r];
-          const float yb = zh ? dv[r] * silu(zv[r]) : dv[r];
-          ybv[pt][r] = yb;
-          qpart += yb * yo[pt][r];
-          dd[pt][r] = yb * xx[r];
+          xv[k][r] = xx[r];
+          const float yb = ybr[r];
+          ybv[k][r] = yb;
+          qpart += yb * yo[k][r];
+          dd[k][r] = yb * xx[r];
           if (zh) {
-            const float ypre = yo[pt][r] + yd[pt][r] + dskip(ch) * xx[r];
+            const float ypre = yo[k][r] + yd[k][r] + dskip(ch) * xx[r];
             const float sg = sigmoid_fast(zv[r]);
             dzv[r] = dv[r] * ypre * sg * (1.f + zv[r] * (1.f - sg));
           }
@@ -422,29 +435,29 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
       }
       // dD per channel: sum over the 16 tokens of the tile (lanes with the same g)
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
+      for (int k = 0; k < 2; ++k)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float v = dd[pt][r];
+          float v = dd[k][r];
 #pragma unroll
           for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, 64);
-          if (r16 == 0) sDD[w][pt * 16 + 4 * g + r] = v;
+          if (r16 == 0) sDD[tt][(2 * hf + k) * 16 + 4 * g + r] = v;
         }
     }
 
     // ------------------------------------------------------------------ dx (columns j = own tile)
     // w_j[p] = sum_{i>=j} (C_i . B_j) exp(a (S_i - S_j)) ybar_i[p]   +   exp(a (S_Q - S_j)) (Gc B_j)[p]
-    f32x4 wi[4], vo[4];
+    f32x4 wi[2], vo[2];
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) wi[pt] = vo[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < 2; ++k) wi[k] = vo[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      if (2 * kk + 1 < w) continue;
+      if (2 * kk + 1 < tt) continue;
       float gl[8];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int it = 2 * kk + half;
-        if (it >= w) {
+        if (it >= tt) {
           const float4 g4 = *reinterpret_cast<const float4*>(GTm + il * Q + it * 16 + 4 * g);   // G[i][j], i = it 16 + 4 g ..
           const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
@@ -459,31 +472,33 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
       }
       const bf16x8 glf = pack8(gl);
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(&YT[(pt * 16 + r16) * RS + 32 * kk + 4 * g]);
-        const uint2 hi = *reinterpret_cast<const uint2*>(&YT[(pt * 16 + r16) * RS + 32 * kk + 16 + 4 * g]);
-        wi[pt] = mfma16(frag_from_pieces(lo, hi), glf, wi[pt]);   // D[p][j] = sum_i ybar_i[p] GL_ij
+      for (int k = 0; k < 2; ++k) {
+        const int row = ((2 * hf + k) * 16 + r16) * RS;
+        const uint2 lo = *reinterpret_cast<const uint2*>(&YT[row + 32 * kk + 4 * g]);
+        const uint2 hi = *reinterpret_cast<const uint2*>(&YT[row + 32 * kk + 16 + 4 * g]);
+        wi[k] = mfma16(frag_from_pieces(lo, hi), glf, wi[k]);   // D[p][j] = sum_i ybar_i[p] GL_ij
       }
     }
 #pragma unroll
     for (int ks = 0; ks < KSN; ++ks) {
       const bf16x8 bf = lane_valid ? load_frag(Bg + tl * rs + 32 * ks + 8 * g) : zero_frag();
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
-        vo[pt] = mfma16(load_frag(gout + (pt * 16 + r16) * N + 32 * ks + 8 * g), bf, vo[pt]);
+      for (int k = 0; k < 2; ++k)
+        vo[k] = mfma16(load_frag(gout + ((2 * hf + k) * 16 + r16) * N + 32 * ks + 8 * g), bf, vo[k]);
     }
     float vvp = vin, rp = 0.f;
     {
       const float eq = exp2_fast(a2 * (Sq - Sl));
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
+      for (int k = 0; k < 2; ++k) {
+        const int pt = 2 * hf + k;
         float dxv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float v = eq * vo[pt][r];
-          const float wv = wi[pt][r] + v;
-          dxv[r] = phil * wv + dskip(pt * 16 + 4 * g + r) * ybv[pt][r];
-          rp += xv[pt][r] * v;
+          const float v = eq * vo[k][r];
+          const float wv = wi[k][r] + v;
+          dxv[r] = phil * wv + dskip(pt * 16 + 4 * g + r) * ybv[k][r];
+          rp += xv[k][r] * v;
         }
         if (lane_valid) {
           uint2 out;
@@ -495,7 +510,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
       vvp += rp;   // x_j . (exp(a (S_Q - S_j)) Gc B_j)
       rp *= phil;
     }
-    // per-token sums over the channels: lanes l, l ^ 16, l ^ 32, l ^ 48 hold the same token
+    // per-token sums over this half's channels: lanes l, l ^ 16, l ^ 32, l ^ 48 hold the same token
 #pragma unroll
     for (int off = 16; off < 64; off <<= 1) {
       qpart += __shfl_xor(qpart, off, 64);
@@ -503,41 +518,47 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
       rp += __shfl_xor(rp, off, 64);
     }
     if (g == 0) {
-      sQv[il] = qpart;
-      sVv[il] = vvp;
-      sRv[il] = rp;
+      sQv[hf][il] = qpart;
+      sVv[hf][il] = vvp;
+      sRv[hf][il] = rp;
     }
     __syncthreads();
 
     // ------------------------------------------------------------------ sum of K over j <= t <= i
     {
-      // prefix over j of each row i (four 16-column pieces per row, one per thread)
-      const int i = tid >> 2, seg = tid & 3;
-      float run[16];
+      // prefix over j of each row i (eight 8-column pieces per row, one per thread)
+      const int i = tid >> 3, seg = tid & 7;
+      float run[8];
       float acc = 0.f;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        acc += sK[i * KST + 16 * seg + k];
+      for (int k = 0; k < 8; ++k) {
+        acc += sK[i * KST + 8 * seg + k];
         run[k] = acc;
       }
-      const int base = lane & ~3;
-      const float t0 = __shfl(acc, base, 64), t1v = __shfl(acc, base + 1, 64), t2 = __shfl(acc, base + 2, 64);
-      const float off = (seg > 0 ? t0 : 0.f) + (seg > 1 ? t1v : 0.f) + (seg > 2 ? t2 : 0.f);
+      // exclusive sum of the lower pieces of the row (lanes 8 apart hold other rows)
+      float off = 0.f;
+      const int base = lane & ~7;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) sK[i * KST + 16 * seg + k] = run[k] + off;
+      for (int k = 0; k < 7; ++k) {
+        const float v = __shfl(acc, base + k, 64);
+        if (k < seg) off += v;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sK[i * KST + 8 * seg + k] = run[k] + off;
     }
     __syncthreads();
     {
-      // R_t = sum_{i>=t} prefix_i(t): rows 16 seg .. 16 seg + 15 per thread
-      const int t = tid >> 2, seg = tid & 3;
+      // R_t = sum_{i>=t} prefix_i(t): rows 8 seg .. 8 seg + 7 per thread
+      const int t = tid >> 3, seg = tid & 7;
       float acc = 0.f;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int i = 16 * seg + k;
+      for (int k = 0; k < 8; ++k) {
+        const int i = 8 * seg + k;
         if (i >= t) acc += sK[i * KST + t];
       }
       acc += __shfl_xor(acc, 1, 64);
       acc += __shfl_xor(acc, 2, 64);
+      acc += __shfl_xor(acc, 4, 64);
       if (seg == 0) sRt[t] = acc;
     }
     __syncthreads();
@@ -545,30 +566,33 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
     // ------------------------------------------------------------------ per-token: dDelta
     if (w == 0) {
       const int t = lane;
-      float sq = sQv[t];   // suffix sum over i >= t
+      float sq = sQv[0][t] + sQv[1][t];   // suffix sum over i >= t
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float o = __shfl_down(sq, off, 64);
         if (t + off < 64) sq += o;
       }
-      float pr = sRv[t];   // prefix sum over j <= t
+      float pr = sRv[0][t] + sRv[1][t];   // prefix sum over j <= t
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float o = __shfl_up(pr, off, 64);
         if (t >= off) pr += o;
       }
-      const float t1 = exp2_fast(a2 * Sq) * (sRed[0] + sRed[1] + sRed[2] + sRed[3]);
+      float red = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) red += sRed[k];
+      const float t1 = exp2_fast(a2 * Sq) * red;
       const float u = t1 + sq + pr + sRt[t];
-      const float vv = sVv[t];
+      const float vv = sVv[0][t] + sVv[1][t];
       const float ddt = a * u + vv;
-      const int64_t tt = tc0 + t;
+      const int64_t tt2 = tc0 + t;
       float pa = 0.f, pb = 0.f;
-      if (tt < L) {
-        const float raw = bf16_to_f32(static_cast<const bf16_t*>(p.delta)[(b * L + tt) * H + h].bits) +
+      if (tt2 < L) {
+        const float raw = bf16_to_f32(static_cast<const bf16_t*>(p.delta)[(b * L + tt2) * H + h].bits) +
                           (p.delta_bias ? p.delta_bias[h] : 0.f);
         const float dt = p.delta_softplus ? softplus_f32(raw) : raw;
         const float gu = p.delta_softplus ? ddt * sigmoid_fast(raw) : ddt;
-        static_cast<bf16_t*>(bp.ddelta)[(b * L + tt) * H + h].bits = f32_to_bf16(gu);
+        static_cast<bf16_t*>(bp.ddelta)[(b * L + tt2) * H + h].bits = f32_to_bf16(gu);
         // (Delta - phi) / a = (a Delta - expm1(a Delta)) / a^2
         const float xa = a * dt;
         pa = dt * u + (xa - expm1f(xa)) / (a * a) * vv;
@@ -589,13 +613,14 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(SsdBwdParams bp) {
     __syncthreads();   // the next head restages the LDS tiles
   }
 
-  // dB and dC of this workgroup's heads: the lane holds states nt 16 + 4 g .. + 3 of token il
+  // dB and dC of this workgroup's heads: the lane holds states n .. n + 3 of token il
   if (lane_valid) {
     const int64_t orow = ((b * (H / bp.hb) + hblk) * L + tl) * N + 4 * g;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      *reinterpret_cast<float4*>(bp.ws_dCp + orow + nt * 16) = make_float4(dC[nt][0], dC[nt][1], dC[nt][2], dC[nt][3]);
-      *reinterpret_cast<float4*>(bp.ws_dBp + orow + nt * 16) = make_float4(dB[nt][0], dB[nt][1], dB[nt][2], dB[nt][3]);
+    for (int k = 0; k < NTH; ++k) {
+      const int n0 = (hf * NTH + k) * 16;
+      *reinterpret_cast<float4*>(bp.ws_dCp + orow + n0) = make_float4(dC[k][0], dC[k][1], dC[k][2], dC[k][3]);
+      *reinterpret_cast<float4*>(bp.ws_dBp + orow + n0) = make_float4(dB[k][0], dB[k][1], dB[k][2], dB[k][3]);
     }
   }
 }
@@ -625,29 +650,43 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_bc_kernel(SsdBwdParams bp)
   }
 }
 
-// dA, ddelta_bias [H] and dD ([H] or [H, P]): sums over batch rows and chunks, in order.
-// One thread per (head, channel); the channel-0 thread of a head also forms the per-head sums.
-__global__ __launch_bounds__(64) void ssd_bwd_reduce_param_kernel(SsdBwdParams bp, int64_t nch) {
+// dA, ddelta_bias [H] and dD ([H] or [H, P]): sums over the B x chunks partials of each head, in
+// a fixed order: thread t of the 256 takes entries t, t + 256, ... (dA, ddelta_bias) or, per
+// channel, entries t / 64, t / 64 + 4, ... (dD); the per-thread sums are combined by a fixed tree.
+__global__ __launch_bounds__(256) void ssd_bwd_reduce_param_kernel(SsdBwdParams bp, int64_t nch) {
+  __shared__ float sA[256], sB[256], sD[256];
   const SsdParams& p = bp.f;
-  const int64_t h = blockIdx.x;
-  const int ch = threadIdx.x;
-  float sd = 0.f;
-  for (int64_t b = 0; b < p.B; ++b)
-    for (int64_t c = 0; c < nch; ++c) sd += bp.ws_pD[((b * nch + c) * p.H + h) * kP + ch];
-  if (bp.dDskip && p.dskip_per_channel) bp.dDskip[h * kP + ch] = sd;
-  float tot = sd;   // per-head dD: channels summed in a fixed tree order
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off, 64);
-  if (ch == 0) {
-    float sa = 0.f, sb = 0.f;
-    for (int64_t b = 0; b < p.B; ++b)
-      for (int64_t c = 0; c < nch; ++c) {
-        sa += bp.ws_pA[(b * nch + c) * p.H + h];
-        sb += bp.ws_pb[(b * nch + c) * p.H + h];
-      }
-    bp.dA[h] = sa;
-    if (bp.ddelta_bias) bp.ddelta_bias[h] = sb;
-    if (bp.dDskip && !p.dskip_per_channel) bp.dDskip[h] = tot;
+  const int64_t h = blockIdx.x, nbc = p.B * nch;
+  const int tid = threadIdx.x, ch = tid & 63, q = tid >> 6;
+  float a = 0.f, b = 0.f, d = 0.f;
+  for (int64_t k = tid; k < nbc; k += 256) {
+    a += bp.ws_pA[k * p.H + h];
+    b += bp.ws_pb[k * p.H + h];
+  }
+  for (int64_t k = q; k < nbc; k += 4) d += bp.ws_pD[(k * p.H + h) * kP + ch];
+  sA[tid] = a;
+  sB[tid] = b;
+  sD[tid] = d;
+  __syncthreads();
+  for (int off = 128; off >= 1; off >>= 1) {
+    if (tid < off) {
+      sA[tid] += sA[tid + off];
+      sB[tid] += sB[tid + off];
+      if (off >= 64) sD[tid] += sD[tid + off];   // the four partials of each channel
+    }
+    __syncthreads();
+  }
+  // sD[0 .. 63] now hold the per-channel sums
+  if (bp.dDskip && p.dskip_per_channel && tid < 64) bp.dDskip[h * kP + tid] = sD[tid];
+  __syncthreads();
+  for (int off = 32; off >= 1; off >>= 1) {
+    if (tid < off) sD[tid] += sD[tid + off];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    bp.dA[h] = sA[0];
+    if (bp.ddelta_bias) bp.ddelta_bias[h] = sB[0];
+    if (bp.dDskip && !p.dskip_per_channel) bp.dDskip[h] = sD[0];
   }
 }
 
@@ -663,11 +702,11 @@ hipError_t launch_n(const SsdBwdParams& bp, hipStream_t stream) {
   hipLaunchKernelGGL((ssd_state_kernel<Q, N, false>), dim3((unsigned)p.H, (unsigned)p.B), dim3(512), 0, stream, p);
   hipLaunchKernelGGL((ssd_state_kernel<Q, N, true>), dim3((unsigned)p.H, (unsigned)p.B), dim3(512), 0, stream, p);
   hipLaunchKernelGGL((ssd_bwd_main_kernel<N>), dim3((unsigned)(p.H / bp.hb), (unsigned)nch, (unsigned)p.B),
-                     dim3(256), 0, stream, bp);
+                     dim3(512), 0, stream, bp);
   const int64_t total = p.B * p.L * p.G * (p.N / 4);
   const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
   hipLaunchKernelGGL(ssd_bwd_reduce_bc_kernel, dim3(blocks), dim3(256), 0, stream, bp);
-  hipLaunchKernelGGL(ssd_bwd_reduce_param_kernel, dim3((unsigned)p.H), dim3(64), 0, stream, bp, nch);
+  hipLaunchKernelGGL(ssd_bwd_reduce_param_kernel, dim3((unsigned)p.H), dim3(256), 0, stream, bp, nch);
   return hipGetLastError();
 }
 

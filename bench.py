@@ -427,6 +427,27 @@ def secondary(torch, np, inputs, ssm, dev):
     res["ssd_2x8192x80x64_n128_q256_bf16"] = {
         "ms": round(ms, 4), "GB_s": round(nbytes / ms / 1e6, 1), "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
         "TFLOP_s": round(flops / ms / 1e9, 1), "mfma_frac": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+
+    # its gradients (dx, ddelta, dA, dB, dC, dh0 for dy; no gate, no D, as the forward figure)
+    dy = r(B, L, H, P).to(bf)
+    nbw = ssm.load().ssd_chunk_bwd_workspace_bytes(B, L, H, P, N, 1, ssm.SSM_BF16)
+    wsb = ssm.workspace(nbw, "cuda")
+    Bg, Cg = Bm.unsqueeze(2), Cm.unsqueeze(2)
+    fnb = lambda i: ssm.ssd_chunk_bwd(x, delta, Ah, Bg, Cg, dy, ws=wsb)
+    _, msb = timed(fnb, 10, 3, torch)
+    # essential I/O: x, dy, dx; delta, ddelta (bf16); B, C (bf16) and dB, dC (float32); dh0
+    nbytes_b = 3 * B * L * H * P * 2 + 2 * B * L * H * 2 + 2 * B * L * N * 2 + 2 * B * L * N * 4 + B * H * P * N * 4
+    Qb = 64
+    nchb = L // Qb
+    # per chunk and head: U (Q^2 P), the within-chunk dB, dC (2 Q^2 N) and w (Q^2 P), the carried
+    # terms of dB, dC, y and w (4 Q P N), the two state passes (2 Q P N); G once per chunk
+    flops_b = B * nchb * H * 2 * (2 * Qb * Qb * P + 2 * Qb * Qb * N + 6 * Qb * P * N) + B * nchb * 2 * Qb * Qb * N
+    res["ssd_bwd_2x8192x80x64_n128_bf16"] = {
+        "ms": round(msb, 4), "GB_s_essential_io": round(nbytes_b / msb / 1e6, 1),
+        "hbm_frac": round(nbytes_b / msb / 1e6 / PEAK_HBM_GBS, 4),
+        "TFLOP_s": round(flops_b / msb / 1e9, 1), "mfma_frac": round(flops_b / msb / 1e9 / PEAK_BF16_TFLOPS, 4),
+        "workspace_MB": round(nbw / 1e6, 1)}
+    del dy, wsb
     return res
 
 

@@ -62,7 +62,8 @@ __device__ __forceinline__ void unpack8(uint4 v, float out[8]) {
 // per lane (one 8- or 16-byte store), and a product that feeds another (W) comes out in the
 // operand layout of the next one: two 16-token tiles per K = 32 step, four tokens of each per
 // lane, the same K order on both operands. dB and dC are summed over the workgroup's hb heads
-// (consecutive heads of one group) in registers.
+// (consecutive heads of one group) in registers; B^T and C^T, shared by those heads, are staged
+// in LDS once.
 template <int N>
 __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
   constexpr int Q = kQb;
@@ -79,6 +80,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
   __shared__ __attribute__((aligned(16))) __bf16 XT[kP * RS];    // (phi x)^T [p][j] (gate only)
   __shared__ __attribute__((aligned(16))) __bf16 HT[N * RSP];    // H_c^T [n][p]
   __shared__ __attribute__((aligned(16))) __bf16 GcT[N * RSP];   // Gc^T [n][p]
+  __shared__ __attribute__((aligned(16))) __bf16 BtS[N * RS];    // B^T [n][j] of the chunk (all heads)
+  __shared__ __attribute__((aligned(16))) __bf16 CtS[N * RS];    // C^T [n][i]
   __shared__ float sK[Q * KST];
   __shared__ float sS[Q], sPhi[Q], sRt[Q], sRed[8];
   __shared__ float sQv[2][Q], sRv[2][Q], sVv[2][Q];
@@ -119,6 +122,14 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
   f32x4 dC[NTH], dB[NTH];
 #pragma unroll
   for (int k = 0; k < NTH; ++k) dC[k] = dB[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // B^T and C^T of the chunk are the same for the workgroup's heads: staged once (visible after
+  // the first head's staging barrier)
+  for (int e = tid; e < N * Q / 8; e += 512) {
+    const int n = e / (Q / 8), j8 = (e % (Q / 8)) * 8;
+    *reinterpret_cast<uint4*>(&BtS[n * RS + j8]) = *reinterpret_cast<const uint4*>(Btm + n * Q + j8);
+    *reinterpret_cast<uint4*>(&CtS[n * RS + j8]) = *reinterpret_cast<const uint4*>(Ctm + n * Q + j8);
+  }
 
   for (int64_t kh = 0; kh < bp.hb; ++kh) {
     const int64_t h = hblk * bp.hb + kh;
@@ -275,8 +286,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           if (2 * kk > tt) break;   // the pair holds no tile j <= i
-          const uint2 lo = *reinterpret_cast<const uint2*>(Btm + n * Q + 32 * kk + 4 * g);
-          const uint2 hi = *reinterpret_cast<const uint2*>(Btm + n * Q + 32 * kk + 16 + 4 * g);
+          const uint2 lo = *reinterpret_cast<const uint2*>(&BtS[n * RS + 32 * kk + 4 * g]);
+          const uint2 hi = *reinterpret_cast<const uint2*>(&BtS[n * RS + 32 * kk + 16 + 4 * g]);
           acc = mfma16(frag_from_pieces(lo, hi), wmA[kk], acc);   // D[n][i] = sum_j B_j[n] W_ij
         }
 #pragma unroll
@@ -327,8 +338,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           if (2 * kk + 1 < tt) continue;   // the pair holds no tile i >= j
-          const uint2 lo = *reinterpret_cast<const uint2*>(Ctm + n * Q + 32 * kk + 4 * g);
-          const uint2 hi = *reinterpret_cast<const uint2*>(Ctm + n * Q + 32 * kk + 16 + 4 * g);
+          const uint2 lo = *reinterpret_cast<const uint2*>(&CtS[n * RS + 32 * kk + 4 * g]);
+          const uint2 hi = *reinterpret_cast<const uint2*>(&CtS[n * RS + 32 * kk + 16 + 4 * g]);
           acc = mfma16(frag_from_pieces(lo, hi), wmB[kk], acc);   // D[n][j] = sum_i C_i[n] W_ij
         }
 #pragma unroll

@@ -138,8 +138,7 @@ struct SsdParams {
   float* dh0;              // nullable [B, H, P, N] (out)
   void* ws_gout;           // bf16 [B, nchunks, H, P, N]: dL/d(state leaving each chunk)
   void* ws_Ct;             // bf16 [B, G, nchunks, N, Q]: C of each chunk, transposed
-  void* ws_GT;             // float [B, G, nchunks, Q, Q]: G transposed (B_j . C_i at [j][i]);
-                           // in the backward ws_G holds G in float as well
+                           // (in the backward ws_G holds G in float32)
 };
 
 size_t ssd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);

@@ -19,7 +19,7 @@
 //   dA    = sum_t Delta_t <dL/dh_t, h_t> + (Delta_t - phi_t) / a  x_t . w_t
 // with Yoff_i = exp(a S_i) H_c C_i (the carried-state part of y_i), and dz from the recomputed
 // pre-gate output. The passes:
-//   cumsum, prep (G = C B^T and its transpose, B^T, C^T per chunk and group), the forward state
+//   cumsum, prep (G = C B^T, B^T, C^T per chunk and group), the forward state
 //   pass (H_c for every chunk, bf16), the adjoint state pass (Gc for every chunk, bf16, and dh0),
 //   the main kernel below, and two reductions in a fixed order (dB and dC over heads, the
 //   parameter gradients over batch rows and chunks).
@@ -73,6 +73,9 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
   constexpr int RS = Q + 8;    // row stride (bf16) of the token tiles
   constexpr int RSP = kP + 8;  // row stride (bf16) of the transposed states
   constexpr int KST = Q + 1;   // row stride (float) of K
+  // row stride (float) of G: rows stay 16-byte aligned for float4 reads of a row, and a wave's
+  // column reads (16 columns x 4 row groups) fall on 64 different banks
+  constexpr int GST = Q + 4;
   __shared__ __attribute__((aligned(16))) __bf16 Xn[Q * RS];     // x [j][p]
   __shared__ __attribute__((aligned(16))) __bf16 Yhi[Q * RS];    // ybar [i][p], bf16 rounded
   __shared__ __attribute__((aligned(16))) __bf16 Ylo[Q * RS];    // ybar - Yhi, bf16 rounded
@@ -82,6 +85,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
   __shared__ __attribute__((aligned(16))) __bf16 GcT[N * RSP];   // Gc^T [n][p]
   __shared__ __attribute__((aligned(16))) __bf16 BtS[N * RS];    // B^T [n][j] of the chunk (all heads)
   __shared__ __attribute__((aligned(16))) __bf16 CtS[N * RS];    // C^T [n][i]
+  __shared__ __attribute__((aligned(16))) float GS[Q * GST];     // G [i][j], float32 (all heads)
   __shared__ float sK[Q * KST];
   __shared__ float sS[Q], sPhi[Q], sRt[Q], sRed[8];
   __shared__ float sQv[2][Q], sRv[2][Q], sVv[2][Q];
@@ -101,9 +105,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
   const int64_t rs = p.G * N;   // token row stride of B and C
   const bf16_t* Bg = static_cast<const bf16_t*>(p.Bm) + b * L * rs + grp * N;
   const bf16_t* Cg = static_cast<const bf16_t*>(p.Cm) + b * L * rs + grp * N;
-  // G = C B^T of the chunk and its transpose, float32 (only tiles on / below the diagonal of G)
+  // G = C B^T of the chunk, float32 (only tiles on / below the diagonal are written and read)
   const float* Gm = static_cast<const float*>(p.ws_G) + (bg * nch + c) * (int64_t)(Q * Q);
-  const float* GTm = static_cast<const float*>(p.ws_GT) + (bg * nch + c) * (int64_t)(Q * Q);
   const bf16_t* Btm = static_cast<const bf16_t*>(p.ws_Bt) + (bg * nch + c) * (int64_t)(N * Q);
   const bf16_t* Ctm = static_cast<const bf16_t*>(p.ws_Ct) + (bg * nch + c) * (int64_t)(N * Q);
   const int64_t tc0 = c * Q;      // first token of the chunk
@@ -123,8 +126,17 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
 #pragma unroll
   for (int k = 0; k < NTH; ++k) dC[k] = dB[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // B^T and C^T of the chunk are the same for the workgroup's heads: staged once (visible after
-  // the first head's staging barrier)
+  // B^T, C^T and G of the chunk are the same for the workgroup's heads: staged once (visible
+  // after the first head's staging barrier)
+  for (int e = tid; e < Q * Q / 4; e += 512) {
+    const int i = e / (Q / 4), j4 = (e % (Q / 4)) * 4;
+    *reinterpret_cast<float4*>(&GS[i * GST + j4]) = *reinterpret_cast<const float4*>(Gm + i * Q + j4);
+  }
+  // G[i][j .. j + 3] (a row piece) and G[i .. i + 3][j] (a column piece, G^T[j][i .. i + 3])
+  auto grow4 = [&](int i, int j) { return *reinterpret_cast<const float4*>(&GS[i * GST + j]); };
+  auto gcol4 = [&](int i, int j) {
+    return make_float4(GS[i * GST + j], GS[(i + 1) * GST + j], GS[(i + 2) * GST + j], GS[(i + 3) * GST + j]);
+  };
   for (int e = tid; e < N * Q / 8; e += 512) {
     const int n = e / (Q / 8), j8 = (e % (Q / 8)) * 8;
     *reinterpret_cast<uint4*>(&BtS[n * RS + j8]) = *reinterpret_cast<const uint4*>(Btm + n * Q + j8);
@@ -262,7 +274,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
           u = mfma16(xa, yb_own[kk], u);
           u = mfma16(xa, yb_lo[kk], u);
         }
-        const float4 g4 = *reinterpret_cast<const float4*>(Gm + il * Q + jt * 16 + 4 * g);
+        const float4 g4 = grow4(il, jt * 16 + 4 * g);
         const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -314,7 +326,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
           u = mfma16(yhi8(it * 16 + r16, 32 * kk + 8 * g), x_own[kk], u);
           u = mfma16(ylo8(it * 16 + r16, 32 * kk + 8 * g), x_own[kk], u);
         }
-        const float4 g4 = *reinterpret_cast<const float4*>(GTm + il * Q + it * 16 + 4 * g);   // G[i][il]
+        const float4 g4 = gcol4(it * 16 + 4 * g, il);   // G[i][il]
         const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -377,7 +389,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
         for (int half = 0; half < 2; ++half) {
           const int jt = 2 * kk + half;
           if (jt <= tt) {
-            const float4 g4 = *reinterpret_cast<const float4*>(Gm + il * Q + jt * 16 + 4 * g);
+            const float4 g4 = grow4(il, jt * 16 + 4 * g);
             const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -469,7 +481,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
       for (int half = 0; half < 2; ++half) {
         const int it = 2 * kk + half;
         if (it >= tt) {
-          const float4 g4 = *reinterpret_cast<const float4*>(GTm + il * Q + it * 16 + 4 * g);   // G[i][j], i = it 16 + 4 g ..
+          const float4 g4 = gcol4(it * 16 + 4 * g, il);   // G[i][j], i = it 16 + 4 g ..
           const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -734,7 +746,7 @@ size_t ssd_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64
   const size_t part = align256((size_t)(B * (H / hb) * L * N) * 4);
   const size_t ph = align256((size_t)(B * nch * H) * 4);
   const size_t pd = align256((size_t)(B * nch * H * P) * 4);
-  return 2 * st + 2 * gg + 2 * bt + sp + 2 * part + 2 * ph + pd;
+  return 2 * st + gg + 2 * bt + sp + 2 * part + 2 * ph + pd;
 }
 
 void ssd_bwd_workspace_carve(SsdBwdParams& bp, void* ws) {
@@ -750,7 +762,6 @@ void ssd_bwd_workspace_carve(SsdBwdParams& bp, void* ws) {
   p.ws_hin = base; base += st;
   p.ws_gout = base; base += st;
   p.ws_G = base; base += gg;
-  p.ws_GT = base; base += gg;
   p.ws_Bt = base; base += bt;
   p.ws_Ct = base; base += bt;
   p.ws_sphi = reinterpret_cast<float2*>(base); base += sp;

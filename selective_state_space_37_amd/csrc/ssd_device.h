@@ -121,9 +121,8 @@ __global__ __launch_bounds__(256) void ssd_cumsum_kernel(SsdParams p) {
 // grid (4, chunks, B G): part `part` transposes states [part N/4, (part+1) N/4) of one group's B
 // and computes every fourth lower-triangular 16 x 16 tile of that group's G (row blocks ib,
 // column tiles jt <= ib). Token t's row of the group starts at element (t G + grp) N.
-// BWD: C is transposed as well (ws_Ct), and G is stored in float32, as itself (ws_G) and
-// transposed (ws_GT), for the backward's elementwise use and operand layouts. Only the tiles on
-// and below the diagonal of G (on and above it in G^T) are written.
+// BWD: C is transposed as well (ws_Ct), and G is stored in float32 (ws_G) for the backward's
+// elementwise use. Only the tiles on and below the diagonal of G are written.
 template <int Q, int N, bool BWD = false>
 __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
   const int part = blockIdx.x;
@@ -177,10 +176,6 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
       float* G32 = static_cast<float*>(p.ws_G) + (bg * nch + c) * (int64_t)(Q * Q);
 #pragma unroll
       for (int r = 0; r < 4; ++r) G32[(int64_t)(ib * 16 + 4 * g + r) * Q + jt * 16 + r16] = acc[r];
-      // G^T[j][i .. i + 3] for j = jt 16 + r16, i = ib 16 + 4 g: one 16-byte piece
-      float* GT = static_cast<float*>(p.ws_GT) + (bg * nch + c) * (int64_t)(Q * Q);
-      *reinterpret_cast<float4*>(GT + (int64_t)(jt * 16 + r16) * Q + ib * 16 + 4 * g) =
-          make_float4(acc[0], acc[1], acc[2], acc[3]);
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r) G[(int64_t)(ib * 16 + 4 * g + r) * Q + jt * 16 + r16].bits = f32_to_bf16(acc[r]);

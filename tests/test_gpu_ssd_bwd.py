@@ -83,3 +83,13 @@ def test_ssd_bwd_layer_full_size_sampled():
     heads = np.array([0, 9, 10, 39, 40, 79])
     errs = gu.ssd_bwd_errors(gpu, gu.ssd_bwd_oracle(inp, dy, dhl, heads=heads), heads=heads)
     _check(errs)
+
+
+@pytest.mark.parametrize("H,G", [(8, 2), (8, 1), (16, 1)])
+def test_ssd_bwd_head_blocks(H, G):
+    """Heads per group a multiple of 4: the main pass sums dB and dC over 4 heads per workgroup and
+    the reduction adds the head blocks of a group (1, 2 and 4 blocks per group here)."""
+    inp = inputs.ssd_layer(seed=96 + H + G, Bsz=2, L=333, H=H, N=128, gate=True, dskip=True, h0=True,
+                           groups=G if G > 1 else None)
+    errs, _ = _run(inp, seed=13)
+    _check(errs)

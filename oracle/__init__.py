@@ -380,3 +380,61 @@ def ssd_quadratic(x, delta, A, Bm, Cm, *, delta_bias=None, delta_softplus=False,
         zz = _f64(z, (Bsz, L, H, P))
         y *= zz / (1.0 + np.exp(-zz))
     return y
+
+
+# ----------------------------------------------------------------------------- Mamba block
+# The block around the scan, for the generation workload. The pages leave it open; the reading
+# (stated where the design is documented) combines: the pre-norm residual block with LayerNorm of
+# the "Beyond attention" page's code overview; the gated block of the news write-up's
+# "architecture" section (the SSM branch and a gate branch from one input projection, multiplied,
+# then an output projection); the short causal convolution over the last 4 inputs of the "Mamba
+# and state space models" page ("fixed-size state") with a SiLU after it; and Delta, B, C as small
+# linear projections of the token (Delta through a rank-R factorisation, a bias and the softplus).
+# Weights (fp64 arrays): ln_w, ln_b [Dm]; W_x, W_z [Di, Dm]; conv_w [Di, W]; conv_b [Di];
+# W_dtin [R, Di]; W_B, W_C [N, Di]; W_dt [Di, R]; b_dt [Di]; A [Di, N]; D [Di]; W_out [Dm, Di].
+
+def layernorm(x, w, b, eps=1e-5):
+    """LayerNorm over the last axis: (x - mean) / sqrt(var + eps) * w + b (biased variance)."""
+    x = _f64(x)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * _f64(w) + _f64(b)
+
+
+def _silu(v):
+    return v / (1.0 + np.exp(-v))
+
+
+def block_seq(hidden, conv_state, h, wts, eps=1e-5, _lib=None):
+    """The block over a whole sequence: hidden [B, L, Dm] -> (hidden + block output, register
+    [B, Di, W] after the last token, state [B, Di, N]). Token-wise parts use library matmuls; the
+    convolution is ``conv1d`` and the SSM is ``scan`` (both pinned)."""
+    hidden = _f64(hidden)
+    w = {k: _f64(v) for k, v in wts.items()}
+    xn = layernorm(hidden, w["ln_w"], w["ln_b"], eps)
+    xi, zi = xn @ w["W_x"].T, xn @ w["W_z"].T
+    u, reg = conv1d(xi, w["conv_w"], conv_b=w["conv_b"], conv_state=conv_state, _lib=_lib)
+    u = _silu(u)
+    dt = (u @ w["W_dtin"].T) @ w["W_dt"].T
+    Bm, Cm = u @ w["W_B"].T, u @ w["W_C"].T
+    y, h_last = scan(u, dt, w["A"], Bm, Cm, delta_bias=w["b_dt"], delta_softplus=True, Dskip=w["D"], z=zi,
+                     h0=h, _lib=_lib)
+    return hidden + y @ w["W_out"].T, reg, h_last
+
+
+def block_step(hidden, conv_state, h, wts, eps=1e-5, _lib=None):
+    """One decode token through the block: hidden [B, Dm] -> (hidden + block output, register
+    [B, Di, W], state [B, Di, N]), with the convolution register and the SSM state carried in and
+    out; the SSM step is ``step`` (pinned)."""
+    hidden = _f64(hidden)
+    w = {k: _f64(v) for k, v in wts.items()}
+    xn = layernorm(hidden, w["ln_w"], w["ln_b"], eps)
+    xi, zi = xn @ w["W_x"].T, xn @ w["W_z"].T
+    u, reg = conv1d(xi[:, None, :], w["conv_w"], conv_b=w["conv_b"], conv_state=conv_state, _lib=_lib)
+    u = _silu(u[:, 0])
+    dt = (u @ w["W_dtin"].T) @ w["W_dt"].T
+    Bm, Cm = u @ w["W_B"].T, u @ w["W_C"].T
+    y, h_new, _ = step(u, dt, w["A"], Bm, Cm, h, delta_bias=w["b_dt"], delta_softplus=True, Dskip=w["D"], z=zi,
+                       _lib=_lib)
+    return hidden + y @ w["W_out"].T, reg, h_new
+

@@ -554,3 +554,47 @@ def check_ssd_bwd_equals_scan_bwd(ssd_bwd, scan_bwd, seed=52):
 
 
 SSD_BWD_FD_TOL = 2e-7
+
+
+# ----------------------------------------------------------------------------- Mamba block
+def tiny_block_weights(seed, Dm=8, Di=12, N=4, W=4, R=3):
+    g = RNG(seed)
+    return dict(ln_w=1 + 0.1 * g.standard_normal(Dm), ln_b=0.1 * g.standard_normal(Dm),
+                W_x=g.standard_normal((Di, Dm)) / np.sqrt(Dm), W_z=g.standard_normal((Di, Dm)) / np.sqrt(Dm),
+                conv_w=0.5 * g.standard_normal((Di, W)), conv_b=0.1 * g.standard_normal(Di),
+                W_dtin=g.standard_normal((R, Di)) / np.sqrt(Di), W_B=g.standard_normal((N, Di)) / np.sqrt(Di),
+                W_C=g.standard_normal((N, Di)) / np.sqrt(Di), W_dt=g.standard_normal((Di, R)) / np.sqrt(R),
+                b_dt=-2.0 + 0.3 * g.standard_normal(Di), A=-np.tile(np.arange(1.0, N + 1), (Di, 1)),
+                D=g.standard_normal(Di), W_out=g.standard_normal((Dm, Di)) / np.sqrt(Di))
+
+
+def check_layernorm_closed_form(layernorm, eps=1e-5):
+    """Rows mu + sigma * s with s = (+1, -1, +1, ...) have mean mu and variance sigma^2 exactly, so
+    LayerNorm gives s sigma / sqrt(sigma^2 + eps) * w + b."""
+    g = RNG(60)
+    Dm = 10
+    s = np.array([1.0, -1.0] * (Dm // 2))
+    mu, sig = g.standard_normal((3, 1)) * 3, np.array([[0.5], [2.0], [1e-3]])
+    w, b = g.standard_normal(Dm), g.standard_normal(Dm)
+    want = s * sig / np.sqrt(sig ** 2 + eps) * w + b
+    return rel_err(layernorm(mu + sig * s, w, b, eps), want)
+
+
+def check_block_step_equals_sequence(block_step, block_seq, seed=61):
+    """The block's state is the convolution register and the SSM state: L single-token steps from
+    a given register and state give the sequence form's outputs, register and state (the sequence
+    form uses the pinned full-sequence convolution and scan, the steps the pinned decode step)."""
+    g = RNG(seed)
+    Bsz, L, Dm, Di, N, W = 2, 9, 8, 12, 4, 4
+    wts = tiny_block_weights(seed)
+    hid = g.standard_normal((Bsz, L, Dm))
+    reg0 = g.standard_normal((Bsz, Di, W))
+    h0 = g.standard_normal((Bsz, Di, N))
+    out, reg, hl = block_seq(hid, reg0, h0, wts)
+    r, h = reg0, h0
+    outs = []
+    for t in range(L):
+        o, r, h = block_step(hid[:, t], r, h, wts)
+        outs.append(o)
+    return max(rel_err(np.stack(outs, axis=1), out), rel_err(r, reg), rel_err(h, hl))
+

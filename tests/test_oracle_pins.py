@@ -239,3 +239,12 @@ def test_ssd_bwd_mutant_caught(tmp_path, name):
     v = _mutant(tmp_path, name, SSD_BWD_MUTANTS[name])
     err = pins.check_ssd_bwd_finite_differences(v.ssd_bwd, oracle.ssd)
     assert not (err <= pins.SSD_BWD_FD_TOL), "planted mistake %s passed the gradient pin" % name
+
+
+def test_layernorm_closed_form():
+    assert pins.check_layernorm_closed_form(oracle.layernorm) <= 1e-13
+
+
+def test_block_step_equals_sequence():
+    assert pins.check_block_step_equals_sequence(oracle.block_step, oracle.block_seq) <= 1e-12
+

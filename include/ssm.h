@@ -22,6 +22,14 @@
  *   ssd_chunk_bwd     gradients of ssd_chunk_fwd_grouped, with the same chunked split: within a
  *                     chunk every contraction is a masked matrix product on the matrix cores;
  *                     between chunks only the state (forwards) and its adjoint (backwards) pass.
+ *   ssm_block_step    one decode token through a whole Mamba block for the generation workload
+ *                     ("Mamba and state space models", section "how much faster": tokens per
+ *                     second at batch 128): LayerNorm and residual (the code overview on "Beyond
+ *                     attention"), the gated projections (the news write-up's "architecture"
+ *                     section), the short convolution of the decode state ("fixed-size state")
+ *                     with SiLU, Delta / B / C from small projections, the selective state update.
+ *                     ssm_linear and ssm_layernorm are its products and its norm, exposed for the
+ *                     model around the blocks (final norm, LM head).
  *   ssd_chunk_fwd_grouped  the same layer with B and C given per group of heads and D per head
  *                     or per channel. The page likens the layer to masked attention (C as the
  *                     queries, B as the keys, the input as the values); groups let several heads
@@ -294,6 +302,64 @@ ssm_status ssd_chunk_fwd_grouped(int64_t B, int64_t L, int64_t H, int64_t P, int
                                  const float* Dskip, int dskip_per_channel, const void* z,
                                  const float* h0, void* y, float* h_last, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/*
+ * ssm_linear -- y = x W^T (+ residual) for a batch of token rows, the block's projections.
+ *   x        : [M, K] bf16       W : [Nout, K] bf16 (row n = output n)
+ *   residual : [M, Nout] bf16 or NULL; may equal y (then y += x W^T)
+ *   y        : [M, Nout] bf16 (out); float32 accumulation, rounded once
+ *   Requirements: 0 <= M <= 128 (M == 0 is a no-op); K a positive multiple of 128; Nout a positive
+ *   multiple of 4; x, W, y, residual 16-byte aligned; y overlaps neither x nor W. The workspace
+ *   (ssm_linear_workspace_bytes(), 0 when the product needs no split of K) holds float32 partial
+ *   sums. Sums over K are formed in a fixed order.
+ */
+size_t ssm_linear_workspace_bytes(int64_t M, int64_t K, int64_t Nout);
+
+ssm_status ssm_linear(int64_t M, int64_t K, int64_t Nout, const void* x, const void* W,
+                      const void* residual, void* y, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * ssm_layernorm -- per row, (x - mean) / sqrt(var + eps) * w + b (biased variance), float32
+ * arithmetic. x, y: [M, D] bf16 (y may equal x; 16-byte aligned); w, b: [D] float32; eps > 0;
+ * D a multiple of 8 up to 8192.
+ */
+ssm_status ssm_layernorm(int64_t M, int64_t D, const void* x, const float* w, const float* b,
+                         float eps, void* y, void* stream);
+
+/*
+ * ssm_block_step -- one decode token through a Mamba block, for B sequences:
+ *   xn = LayerNorm(hidden; ln_w, ln_b, eps)
+ *   xi = xn W_x^T,  zi = xn W_z^T                                   [B, d_inner]
+ *   u  = SiLU(conv(register with xi appended; conv_w, conv_b))        (register updated)
+ *   dt = (u W_dtin^T) W_dt^T,  Bt = u W_B^T,  Ct = u W_C^T             (rank-R Delta path)
+ *   y  = the selective state update of ssm_state_update on u with delta dt, delta_bias b_dt,
+ *        softplus, A, Bt, Ct, Dskip and gate zi (h updated in place)
+ *   hidden += y W_out^T
+ *
+ *   hidden     : [B, d_model] bf16, in/out        conv_state : [B, d_inner, W] bf16, in/out
+ *   h          : [B, d_inner, N] float32, in/out
+ *   ln_w, ln_b : [d_model] float32      W_x, W_z : [d_inner, d_model] bf16
+ *   conv_w     : [d_inner, W] float32   conv_b : [d_inner] float32 or NULL
+ *   W_dtin     : [R, d_inner] bf16      W_B, W_C : [N, d_inner] bf16    W_dt : [d_inner, R] bf16
+ *   b_dt       : [d_inner] float32      A : [d_inner, N] float32 (< 0)   Dskip : [d_inner] or NULL
+ *   W_out      : [d_model, d_inner] bf16
+ *   Intermediate activations are bf16 in the workspace (ssm_block_step_workspace_bytes()).
+ *   Requirements: 0 <= B <= 128 (0 is a no-op); d_model a multiple of 128 up to 8192; d_inner and
+ *   R multiples of 128; N in {4, 8, 16}; 1 <= W <= 8; eps > 0; the in/out tensors overlap no
+ *   weight, each other or the workspace; pointers of bf16 tensors, A, conv_state and h 16-byte
+ *   aligned.
+ */
+size_t ssm_block_step_workspace_bytes(int64_t B, int64_t d_model, int64_t d_inner, int64_t N,
+                                      int64_t W, int64_t R);
+
+ssm_status ssm_block_step(int64_t B, int64_t d_model, int64_t d_inner, int64_t N, int64_t W,
+                          int64_t R, void* hidden, const float* ln_w, const float* ln_b, float eps,
+                          const void* W_x, const void* W_z, const float* conv_w,
+                          const float* conv_b, const void* W_dtin, const void* W_B,
+                          const void* W_C, const void* W_dt, const float* b_dt, const float* A,
+                          const float* Dskip, const void* W_out, void* conv_state, float* h,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * ssd_chunk_bwd -- gradients of ssd_chunk_fwd_grouped (training): the derivative of the forward

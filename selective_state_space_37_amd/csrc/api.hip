@@ -389,6 +389,105 @@ size_t ssd_chunk_fwd_grouped_workspace_bytes(int64_t B, int64_t L, int64_t H, in
   return ssm::ssd_workspace_bytes(B, L, H, P, N, G, chunk);
 }
 
+size_t ssm_linear_workspace_bytes(int64_t M, int64_t K, int64_t Nout) {
+  if (M <= 0 || K <= 0 || Nout <= 0) return 0;
+  return ssm::gemm_workspace_bytes(M, K, Nout);
+}
+
+ssm_status ssm_linear(int64_t M, int64_t K, int64_t Nout, const void* x, const void* w, const void* residual, void* y,
+                      void* ws, size_t ws_bytes, void* stream) {
+  if (M < 0 || M > 128) return fail(SSM_ERR_UNSUPPORTED, "M=%lld: 0..128 token rows", (long long)M);
+  if (K < 128 || K % 128 != 0) return fail(SSM_ERR_UNSUPPORTED, "K=%lld must be a positive multiple of 128", (long long)K);
+  if (Nout < 4 || Nout % 4 != 0) return fail(SSM_ERR_UNSUPPORTED, "Nout=%lld must be a positive multiple of 4", (long long)Nout);
+  if ((Nout + 31) / 32 > 2147483647LL) return fail(SSM_ERR_UNSUPPORTED, "Nout too large");
+  if (M == 0) return ok();
+  if (!x || !w || !y) return fail(SSM_ERR_INVALID_ARGUMENT, "x, w and y must not be NULL");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (residual && !aligned16(residual)))
+    return fail(SSM_ERR_INVALID_ARGUMENT, "x, w, y and residual must be 16-byte aligned");
+  const size_t xb = (size_t)(M * K) * 2, wb = (size_t)(Nout * K) * 2, yb = (size_t)(M * Nout) * 2;
+  if (overlaps(y, yb, x, xb) || overlaps(y, yb, w, wb))
+    return fail(SSM_ERR_INVALID_ARGUMENT, "y overlaps x or w");
+  if (residual && residual != y && overlaps(residual, yb, y, yb))
+    return fail(SSM_ERR_INVALID_ARGUMENT, "residual partially overlaps y (it may only equal it)");
+  const size_t need = ssm::gemm_workspace_bytes(M, K, Nout);
+  if (need && (!ws || ws_bytes < need))
+    return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws ? ws_bytes : (size_t)0, need);
+  if (need && !aligned16(ws)) return fail(SSM_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  ssm::GemmParams g{};
+  g.M = M; g.K = K; g.Nout = Nout; g.x = x; g.ldx = K; g.w = w; g.y = y; g.ldy = Nout; g.residual = residual;
+  g.partial = static_cast<float*>(ws);
+  return from_hip(ssm::launch_gemm(g, static_cast<hipStream_t>(stream)), "ssm_linear launch");
+}
+
+ssm_status ssm_layernorm(int64_t M, int64_t D, const void* x, const float* w, const float* b, float eps, void* y,
+                         void* stream) {
+  if (M < 0) return fail(SSM_ERR_INVALID_ARGUMENT, "M=%lld must be >= 0", (long long)M);
+  if (D < 8 || D % 8 != 0 || D > 8192) return fail(SSM_ERR_UNSUPPORTED, "D=%lld: a multiple of 8 up to 8192", (long long)D);
+  if (!(eps > 0.f)) return fail(SSM_ERR_INVALID_ARGUMENT, "eps must be > 0");
+  if (M == 0) return ok();
+  if (M > 2147483647LL) return fail(SSM_ERR_UNSUPPORTED, "M too large");
+  if (!x || !w || !b || !y) return fail(SSM_ERR_INVALID_ARGUMENT, "x, w, b and y must not be NULL");
+  if (!aligned16(x) || !aligned16(y)) return fail(SSM_ERR_INVALID_ARGUMENT, "x and y must be 16-byte aligned");
+  const size_t rb = (size_t)(M * D) * 2;
+  if (y != x && overlaps(y, rb, x, rb)) return fail(SSM_ERR_INVALID_ARGUMENT, "y partially overlaps x (it may only equal it)");
+  return from_hip(ssm::launch_layernorm(M, D, x, w, b, eps, y, static_cast<hipStream_t>(stream)), "ssm_layernorm launch");
+}
+
+size_t ssm_block_step_workspace_bytes(int64_t B, int64_t d_model, int64_t d_inner, int64_t N, int64_t W, int64_t R) {
+  if (B <= 0 || d_model <= 0 || d_inner <= 0 || N <= 0 || W <= 0 || R <= 0) return 0;
+  return ssm::block_workspace_bytes(B, d_model, d_inner, N, R);
+}
+
+ssm_status ssm_block_step(int64_t B, int64_t d_model, int64_t d_inner, int64_t N, int64_t W, int64_t R, void* hidden,
+                          const float* ln_w, const float* ln_b, float eps, const void* W_x, const void* W_z,
+                          const float* conv_w, const float* conv_b, const void* W_dtin, const void* W_B,
+                          const void* W_C, const void* W_dt, const float* b_dt, const float* A, const float* Dskip,
+                          const void* W_out, void* conv_state, float* h, void* ws, size_t ws_bytes, void* stream) {
+  if (B < 0 || B > 128) return fail(SSM_ERR_UNSUPPORTED, "B=%lld: 0..128 sequences", (long long)B);
+  if (d_model < 128 || d_model % 128 != 0 || d_model > 8192)
+    return fail(SSM_ERR_UNSUPPORTED, "d_model=%lld: a multiple of 128 up to 8192", (long long)d_model);
+  if (d_inner < 128 || d_inner % 128 != 0) return fail(SSM_ERR_UNSUPPORTED, "d_inner=%lld: a multiple of 128", (long long)d_inner);
+  if (R < 128 || R % 128 != 0) return fail(SSM_ERR_UNSUPPORTED, "R=%lld: a multiple of 128", (long long)R);
+  if (N != 4 && N != 8 && N != 16) return fail(SSM_ERR_UNSUPPORTED, "N=%lld: supported 4, 8, 16", (long long)N);
+  if (W < 1 || W > 8) return fail(SSM_ERR_UNSUPPORTED, "W=%lld: supported 1..8", (long long)W);
+  if (!(eps > 0.f)) return fail(SSM_ERR_INVALID_ARGUMENT, "eps must be > 0");
+  if (B == 0) return ok();
+  const void* need_ptrs[] = {hidden, ln_w, ln_b, W_x, W_z, conv_w, W_dtin, W_B, W_C, W_dt, b_dt, A, W_out, conv_state, h};
+  for (const void* q : need_ptrs)
+    if (!q) return fail(SSM_ERR_INVALID_ARGUMENT, "a required pointer is NULL (only conv_b and Dskip may be)");
+  const void* al[] = {hidden, W_x, W_z, W_dtin, W_B, W_C, W_dt, W_out, conv_state, h, A};
+  for (const void* q : al)
+    if (!aligned16(q)) return fail(SSM_ERR_INVALID_ARGUMENT, "hidden, the weight matrices, A, conv_state and h must be 16-byte aligned");
+  // the in/out tensors overlap nothing else
+  const size_t hb = (size_t)(B * d_model) * 2, cb = (size_t)(B * d_inner * W) * 2, sb = (size_t)(B * d_inner * N) * 4;
+  const void* ins[] = {ln_w, ln_b, W_x, W_z, conv_w, conv_b, W_dtin, W_B, W_C, W_dt, b_dt, A, Dskip, W_out};
+  const size_t insz[] = {(size_t)d_model * 4, (size_t)d_model * 4, (size_t)(d_inner * d_model) * 2,
+                         (size_t)(d_inner * d_model) * 2, (size_t)(d_inner * W) * 4, (size_t)d_inner * 4,
+                         (size_t)(R * d_inner) * 2, (size_t)(N * d_inner) * 2, (size_t)(N * d_inner) * 2,
+                         (size_t)(d_inner * R) * 2, (size_t)d_inner * 4, (size_t)(d_inner * N) * 4, (size_t)d_inner * 4,
+                         (size_t)(d_model * d_inner) * 2};
+  void* io[] = {hidden, conv_state, h};
+  const size_t iosz[] = {hb, cb, sb};
+  for (int o = 0; o < 3; ++o) {
+    for (int k = 0; k < 14; ++k)
+      if (overlaps(io[o], iosz[o], ins[k], insz[k])) return fail(SSM_ERR_INVALID_ARGUMENT, "hidden, conv_state or h overlaps a weight");
+    for (int k = o + 1; k < 3; ++k)
+      if (overlaps(io[o], iosz[o], io[k], iosz[k])) return fail(SSM_ERR_INVALID_ARGUMENT, "hidden, conv_state and h overlap");
+  }
+  const size_t need = ssm::block_workspace_bytes(B, d_model, d_inner, N, R);
+  if (!ws) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace is NULL; %zu bytes needed", need);
+  if (ws_bytes < need) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (!aligned16(ws)) return fail(SSM_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  for (int o = 0; o < 3; ++o)
+    if (overlaps(ws, need, io[o], iosz[o])) return fail(SSM_ERR_INVALID_ARGUMENT, "workspace overlaps hidden, conv_state or h");
+  ssm::BlockParams p{};
+  p.B = B; p.Dm = d_model; p.Di = d_inner; p.N = N; p.W = W; p.R = R; p.eps = eps;
+  p.hidden = hidden; p.ln_w = ln_w; p.ln_b = ln_b; p.W_x = W_x; p.W_z = W_z; p.conv_w = conv_w; p.conv_b = conv_b;
+  p.W_dtin = W_dtin; p.W_B = W_B; p.W_C = W_C; p.W_dt = W_dt; p.b_dt = b_dt; p.A = A; p.Dskip = Dskip;
+  p.W_out = W_out; p.conv_state = conv_state; p.h = h;
+  return from_hip(ssm::launch_block_step(p, ws, static_cast<hipStream_t>(stream)), "ssm_block_step launch");
+}
+
 size_t ssd_chunk_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, ssm_dtype) {
   if (B <= 0 || L <= 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0) return 0;
   return ssm::ssd_bwd_workspace_bytes(B, L, H, P, N, G, ssd_bwd_heads_per_wg(H, G));

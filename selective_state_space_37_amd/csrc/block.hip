@@ -1,0 +1,329 @@
+// One decode token through a Mamba block, for the generation workload: LayerNorm, the input
+// projections, the short causal convolution with SiLU, the projections to Delta, B and C, the
+// selective state update (the decode kernel), the output projection and the residual.
+//
+// The block follows the pages as read for this workload: the pre-norm residual block with
+// LayerNorm of the code overview on "Beyond attention: exploring Mamba and state space models";
+// the gated block of the news write-up's "architecture" section (an SSM branch and a gate branch
+// from one input projection, multiplied, then an output projection); the convolution over the
+// last 4 inputs of "Mamba and state space models", section "fixed-size state"; Delta, B and C as
+// small linear projections of the token (same page, "decided by the token").
+//
+// At decode time every projection is a product of the batch's token rows (M <= 128) with a
+// weight matrix that is read once per step: the kernel streams the weights from HBM and keeps
+// the activations in L2. MFMA v_mfma_f32_16x16x32_bf16, lane layout as in the SSD kernels:
+//   A (16 x 32): row l % 16, k = 8g .. 8g+7;  B (32 x 16): col l % 16, k = 8g .. 8g+7;
+//   D (16 x 16): col l % 16, rows 4g .. 4g+3  (g = l / 16).
+#include <algorithm>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace ssm {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 zero8() {
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (__bf16)0.0f;
+  return v;
+}
+
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+  return make_uint2((uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16),
+                    (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16));
+}
+
+// ---------------------------------------------------------------------------- LayerNorm
+// One workgroup (256 threads) per row of D <= 8192 bf16 values (D % 8 == 0): each thread keeps up
+// to four 8-element pieces in registers; mean, then variance of the centred values, both summed
+// in float32 through a fixed tree (deterministic).
+__global__ __launch_bounds__(256) void layernorm_kernel(int64_t D, const bf16_t* x, const float* w, const float* b,
+                                                        float eps, bf16_t* y) {
+  __shared__ float red[8];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const bf16_t* xr = x + row * D;
+  float v[4][8];
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t c = (int64_t)(tid + 256 * k) * 8;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[k][q] = 0.f;
+    if (c < D) {
+      const uint4 u = *reinterpret_cast<const uint4*>(xr + c);
+      const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[k][2 * q] = bf16_lo(wd[q]);
+        v[k][2 * q + 1] = bf16_hi(wd[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s += v[k][q];
+    }
+  }
+  auto block_sum = [&](float t, int slot) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
+    if (lane == 0) red[slot * 4 + wv] = t;
+    __syncthreads();
+    return (red[slot * 4] + red[slot * 4 + 1]) + (red[slot * 4 + 2] + red[slot * 4 + 3]);
+  };
+  const float mean = block_sum(s, 0) / (float)D;
+  float s2 = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t c = (int64_t)(tid + 256 * k) * 8;
+    if (c < D) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float d = v[k][q] - mean;
+        s2 += d * d;
+      }
+    }
+  }
+  const float rstd = rsqrtf(block_sum(s2, 1) / (float)D + eps);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t c = (int64_t)(tid + 256 * k) * 8;
+    if (c < D) {
+      float o[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) o[q] = (v[k][q] - mean) * rstd * w[c + q] + b[c + q];
+      const uint2 lo = pack4(o[0], o[1], o[2], o[3]), hi = pack4(o[4], o[5], o[6], o[7]);
+      *reinterpret_cast<uint4*>(y + row * D + c) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- skinny GEMM
+// Y[m][n] = sum_k X[m][k] W[n][k] (+ R[m][n]) for M <= 128 token rows. grid (ceil(Nout / 32), S),
+// 256 threads. A workgroup owns 32 output columns and the K slice blockIdx.y of S; its four waves
+// take interleaved 32-wide K steps, each accumulating all MT row tiles x 2 column tiles computed
+// transposed (D[n][m]: A = W rows, B = X rows), so a lane ends with four consecutive outputs of
+// one row. The waves' sums meet in LDS in a fixed order; with S = 1 the workgroup applies the
+// epilogue (residual, bf16), otherwise it writes a float32 partial for the reduction kernel.
+template <int MT>
+__global__ __launch_bounds__(256) void gemm_xwt_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) float part[4][MT][2][64][4];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t col0 = (int64_t)blockIdx.x * 32;
+  const int64_t ks = blockIdx.y;
+  const int64_t kbeg = ks * p.kslice;
+  const bf16_t* W = static_cast<const bf16_t*>(p.w);
+  const bf16_t* X = static_cast<const bf16_t*>(p.x);
+
+  f32x4 acc[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bool nrow_ok[2];
+  const bf16_t* wrow[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int64_t n = col0 + nt * 16 + r16;
+    nrow_ok[nt] = n < p.Nout;
+    wrow[nt] = W + (nrow_ok[nt] ? n : 0) * p.K;
+  }
+  bool mrow_ok[MT];
+  const bf16_t* xrow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int64_t m = mt * 16 + r16;
+    mrow_ok[mt] = m < p.M;
+    xrow[mt] = X + (mrow_ok[mt] ? m : 0) * p.ldx;
+  }
+  const int64_t nsteps = p.kslice / 128;   // K steps of each wave
+#pragma unroll 2
+  for (int64_t i = 0; i < nsteps; ++i) {
+    const int64_t k0 = kbeg + (w + 4 * i) * 32 + 8 * g;
+    bf16x8 wf[2], xf[MT];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) wf[nt] = nrow_ok[nt] ? *reinterpret_cast<const bf16x8*>(wrow[nt] + k0) : zero8();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) xf[mt] = mrow_ok[mt] ? *reinterpret_cast<const bf16x8*>(xrow[mt] + k0) : zero8();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma16(wf[nt], xf[mt], acc[mt][nt]);
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+      *reinterpret_cast<float4*>(&part[w][mt][nt][lane][0]) =
+          make_float4(acc[mt][nt][0], acc[mt][nt][1], acc[mt][nt][2], acc[mt][nt][3]);
+  __syncthreads();
+  // (row tile, column tile, lane) groups of four outputs: n = col0 + nt 16 + 4 (lane / 16) + r,
+  // m = mt 16 + lane % 16
+  for (int e = tid; e < MT * 2 * 64; e += 256) {
+    const int mt = e / 128, nt = (e / 64) & 1, ln = e & 63;
+    const int64_t m = mt * 16 + (ln & 15);
+    const int64_t n = col0 + nt * 16 + 4 * (ln >> 4);
+    if (m >= p.M || n >= p.Nout) continue;
+    float4 s = *reinterpret_cast<const float4*>(&part[0][mt][nt][ln][0]);
+#pragma unroll
+    for (int k = 1; k < 4; ++k) {
+      const float4 t = *reinterpret_cast<const float4*>(&part[k][mt][nt][ln][0]);
+      s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+    }
+    if (p.S > 1) {
+      *reinterpret_cast<float4*>(p.partial + (ks * p.M + m) * p.Nout + n) = s;
+    } else {
+      if (p.residual) {
+        const uint2 rr = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(p.residual) + m * p.ldy + n);
+        s.x += bf16_lo(rr.x); s.y += bf16_hi(rr.x); s.z += bf16_lo(rr.y); s.w += bf16_hi(rr.y);
+      }
+      *reinterpret_cast<uint2*>(static_cast<bf16_t*>(p.y) + m * p.ldy + n) = pack4(s.x, s.y, s.z, s.w);
+    }
+  }
+}
+
+// Y = sum over the S partials in order (+ R), four outputs per thread.
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmParams p) {
+  const int64_t total = p.M * (p.Nout / 4);
+  for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int64_t m = e / (p.Nout / 4), n = (e % (p.Nout / 4)) * 4;
+    float4 s = *reinterpret_cast<const float4*>(p.partial + m * p.Nout + n);
+    for (int64_t k = 1; k < p.S; ++k) {
+      const float4 t = *reinterpret_cast<const float4*>(p.partial + (k * p.M + m) * p.Nout + n);
+      s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+    }
+    if (p.residual) {
+      const uint2 rr = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(p.residual) + m * p.ldy + n);
+      s.x += bf16_lo(rr.x); s.y += bf16_hi(rr.x); s.z += bf16_lo(rr.y); s.w += bf16_hi(rr.y);
+    }
+    *reinterpret_cast<uint2*>(static_cast<bf16_t*>(p.y) + m * p.ldy + n) = pack4(s.x, s.y, s.z, s.w);
+  }
+}
+
+// ---------------------------------------------------------------------------- conv + SiLU
+// Per (b, d): shift the register of the last W raw inputs (oldest first), append x, and
+// u = SiLU(sum_k w[d][k] reg[k] + bias[d]); w[d][W-1] multiplies the newest input.
+__global__ __launch_bounds__(256) void conv_silu_kernel(int64_t B, int64_t D, int64_t W, const bf16_t* x,
+                                                        bf16_t* reg, const float* cw, const float* cb, bf16_t* u) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= B * D) return;
+  const int64_t d = e % D;
+  bf16_t* r = reg + e * W;
+  float acc = cb ? cb[d] : 0.f;
+  for (int64_t k = 0; k + 1 < W; ++k) {
+    const bf16_t v = r[k + 1];
+    r[k] = v;
+    acc += cw[d * W + k] * bf16_to_f32(v.bits);
+  }
+  const bf16_t xn = x[e];
+  r[W - 1] = xn;
+  acc += cw[d * W + W - 1] * bf16_to_f32(xn.bits);
+  u[e].bits = f32_to_bf16(silu(acc));
+}
+
+}  // namespace
+
+// S (K splits) for a product: enough workgroups to fill the chip (about 512), each wave keeping
+// at least one 32-wide K step per split.
+int64_t gemm_splits(int64_t K, int64_t Nout) {
+  const int64_t tiles = (Nout + 31) / 32;
+  int64_t S = 1;
+  while (tiles * S < 512 && K % (S * 2 * 128) == 0) S *= 2;
+  return S;
+}
+
+size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t Nout) {
+  const int64_t S = gemm_splits(K, Nout);
+  return S > 1 ? (size_t)(S * M * Nout) * 4 : 0;
+}
+
+hipError_t launch_gemm(GemmParams p, hipStream_t stream) {
+  p.S = gemm_splits(p.K, p.Nout);
+  p.kslice = p.K / p.S;
+  const dim3 grid((unsigned)((p.Nout + 31) / 32), (unsigned)p.S);
+  const int mt = (int)((p.M + 15) / 16);
+  switch (mt) {
+    case 1: hipLaunchKernelGGL(gemm_xwt_kernel<1>, grid, dim3(256), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL(gemm_xwt_kernel<2>, grid, dim3(256), 0, stream, p); break;
+    case 3: case 4: hipLaunchKernelGGL(gemm_xwt_kernel<4>, grid, dim3(256), 0, stream, p); break;
+    default: hipLaunchKernelGGL(gemm_xwt_kernel<8>, grid, dim3(256), 0, stream, p); break;
+  }
+  if (p.S > 1) {
+    const int64_t total = p.M * (p.Nout / 4);
+    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)std::min<int64_t>((total + 255) / 256, 4096)), dim3(256), 0,
+                       stream, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_layernorm(int64_t M, int64_t D, const void* x, const float* w, const float* b, float eps, void* y,
+                            hipStream_t stream) {
+  hipLaunchKernelGGL(layernorm_kernel, dim3((unsigned)M), dim3(256), 0, stream, D, static_cast<const bf16_t*>(x), w,
+                     b, eps, static_cast<bf16_t*>(y));
+  return hipGetLastError();
+}
+
+// Workspace of one block step: xn [B, Dm], xi, zi, u, dt, y [B, Di], dtl [B, R], Bt, Ct [B, N]
+// (bf16, each 256-byte aligned) and the largest product's partial sums.
+static size_t blk_align(size_t n) { return (n + 255) & ~(size_t)255; }
+
+size_t block_workspace_bytes(int64_t B, int64_t Dm, int64_t Di, int64_t N, int64_t R) {
+  const size_t acts = blk_align(B * Dm * 2) + 5 * blk_align(B * Di * 2) + blk_align(B * R * 2) + 2 * blk_align(B * N * 2);
+  size_t part = 0;
+  const int64_t shapes[6][2] = {{Dm, Di}, {Di, R}, {Di, N}, {R, Di}, {Di, Dm}, {Dm, Di}};   // (K, Nout)
+  for (auto& s : shapes) part = std::max(part, gemm_workspace_bytes(B, s[0], s[1]));
+  return acts + blk_align(part);
+}
+
+hipError_t launch_block_step(const BlockParams& bp, void* ws, hipStream_t st) {
+  const int64_t B = bp.B, Dm = bp.Dm, Di = bp.Di, N = bp.N, R = bp.R;
+  char* base = static_cast<char*>(ws);
+  auto take = [&](size_t n) { void* q = base; base += blk_align(n); return q; };
+  void* xn = take(B * Dm * 2);
+  void* xi = take(B * Di * 2);
+  void* zi = take(B * Di * 2);
+  void* u = take(B * Di * 2);
+  void* dt = take(B * Di * 2);
+  void* y = take(B * Di * 2);
+  void* dtl = take(B * R * 2);
+  void* Bt = take(B * N * 2);
+  void* Ct = take(B * N * 2);
+  float* partial = reinterpret_cast<float*>(base);
+  auto gemm = [&](const void* x, int64_t K, const void* w, int64_t Nout, void* out, const void* res) {
+    GemmParams g{};
+    g.M = B; g.K = K; g.Nout = Nout; g.x = x; g.ldx = K; g.w = w; g.y = out; g.ldy = Nout; g.residual = res;
+    g.partial = partial;
+    return launch_gemm(g, st);
+  };
+  hipError_t e = launch_layernorm(B, Dm, bp.hidden, bp.ln_w, bp.ln_b, bp.eps, xn, st);
+  if (e == hipSuccess) e = gemm(xn, Dm, bp.W_x, Di, xi, nullptr);
+  if (e == hipSuccess) e = gemm(xn, Dm, bp.W_z, Di, zi, nullptr);
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(conv_silu_kernel, dim3((unsigned)((B * Di + 255) / 256)), dim3(256), 0, st, B, Di, bp.W,
+                       static_cast<const bf16_t*>(xi), static_cast<bf16_t*>(bp.conv_state), bp.conv_w, bp.conv_b,
+                       static_cast<bf16_t*>(u));
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = gemm(u, Di, bp.W_dtin, R, dtl, nullptr);
+  if (e == hipSuccess) e = gemm(u, Di, bp.W_B, N, Bt, nullptr);
+  if (e == hipSuccess) e = gemm(u, Di, bp.W_C, N, Ct, nullptr);
+  if (e == hipSuccess) e = gemm(dtl, R, bp.W_dt, Di, dt, nullptr);
+  if (e == hipSuccess) {
+    StepParams sp{};
+    sp.B = B; sp.D = Di; sp.N = N; sp.W = 0; sp.io_bf16 = 1;
+    sp.x = u; sp.delta = dt; sp.z = zi; sp.Bm = Bt; sp.Cm = Ct;
+    sp.delta_bias = bp.b_dt; sp.A = bp.A; sp.Dskip = bp.Dskip;
+    sp.conv_state = nullptr; sp.conv_w = nullptr; sp.conv_b = nullptr;
+    sp.h = bp.h; sp.y = y; sp.delta_softplus = 1;
+    e = launch_state_update(sp, st);
+  }
+  if (e == hipSuccess) e = gemm(y, Di, bp.W_out, Dm, bp.hidden, bp.hidden);
+  return e;
+}
+
+}  // namespace ssm

@@ -167,6 +167,48 @@ struct SsdBwdParams {
   float* ws_pD;            // [B, nchunks, H, P] partial dD (per channel)
 };
 
+// Products of M <= 128 token rows with a weight matrix: Y[m][n] = sum_k X[m][k] W[n][k] (+ R).
+struct GemmParams {
+  int64_t M, K, Nout;      // K % 128 == 0, Nout % 4 == 0
+  int64_t ldx, ldy;        // row strides (elements) of X and of Y / R
+  int64_t S, kslice;       // K splits and their length (set by launch_gemm)
+  const void* x;           // bf16 [M, ldx]
+  const void* w;           // bf16 [Nout, K]
+  void* y;                 // bf16 [M, ldy]
+  const void* residual;    // nullable bf16 [M, ldy]; may equal y
+  float* partial;          // float [S, M, Nout] when S > 1
+};
+int64_t gemm_splits(int64_t K, int64_t Nout);
+size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t Nout);
+hipError_t launch_gemm(GemmParams p, hipStream_t stream);
+hipError_t launch_layernorm(int64_t M, int64_t D, const void* x, const float* w, const float* b, float eps, void* y,
+                            hipStream_t stream);
+
+// One decode token through a Mamba block (see block.hip).
+struct BlockParams {
+  int64_t B, Dm, Di, N, W, R;
+  float eps;
+  void* hidden;                       // bf16 [B, Dm], in/out (the residual stream)
+  const float* ln_w;                  // [Dm]
+  const float* ln_b;                  // [Dm]
+  const void* W_x;                    // bf16 [Di, Dm]
+  const void* W_z;                    // bf16 [Di, Dm]
+  const float* conv_w;                // [Di, W]
+  const float* conv_b;                // nullable [Di]
+  const void* W_dtin;                 // bf16 [R, Di]
+  const void* W_B;                    // bf16 [N, Di]
+  const void* W_C;                    // bf16 [N, Di]
+  const void* W_dt;                   // bf16 [Di, R]
+  const float* b_dt;                  // [Di]
+  const float* A;                     // [Di, N]
+  const float* Dskip;                 // nullable [Di]
+  const void* W_out;                  // bf16 [Dm, Di]
+  void* conv_state;                   // bf16 [B, Di, W], in/out
+  float* h;                           // [B, Di, N], in/out
+};
+size_t block_workspace_bytes(int64_t B, int64_t Dm, int64_t Di, int64_t N, int64_t R);
+hipError_t launch_block_step(const BlockParams& p, void* ws, hipStream_t stream);
+
 size_t ssd_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t hb);
 void ssd_bwd_workspace_carve(SsdBwdParams& p, void* ws);
 hipError_t launch_ssd_bwd(const SsdBwdParams& p, hipStream_t stream);

@@ -196,6 +196,36 @@ def ssd_grads(seed: int, Bsz: int, L: int, H: int, P: int, N: int, dtype: str = 
     return dy, dhl
 
 
+TID_BLOCK = 200   # + layer index: the weights of one block
+
+
+def block_weights(seed: int, Dm: int, Di: int, N: int = 16, W: int = 4, R: int = 128, layer: int = 0) -> dict:
+    """Synthetic weights of one Mamba block (no trained values exist here): projections ~ N(0, 1/fan_in)
+    stored in bf16; LayerNorm w = 1 + 0.1 N(0,1), b = 0.1 N(0,1); conv_w ~ N(0, 1/W), conv_b ~ 0.1 N(0,1);
+    b_dt = softplus^-1 of a log-uniform step in [1e-3, 0.1]; W_dt scaled by 0.1 so the steps stay near
+    that range; A[d, n] = -(n + 1) (the pages' -1 .. -16); D = 1."""
+    g = _rng(seed, TID_BLOCK + layer)
+    nrm = lambda shape, fan: (g.standard_normal(shape) / np.sqrt(fan)).astype(np.float32)
+    step = np.exp(g.uniform(np.log(1e-3), np.log(0.1), Di))
+    return dict(
+        ln_w=(1 + 0.1 * g.standard_normal(Dm)).astype(np.float32), ln_b=(0.1 * g.standard_normal(Dm)).astype(np.float32),
+        W_x=store(nrm((Di, Dm), Dm), "bf16"), W_z=store(nrm((Di, Dm), Dm), "bf16"),
+        conv_w=nrm((Di, W), W), conv_b=(0.1 * g.standard_normal(Di)).astype(np.float32),
+        W_dtin=store(nrm((R, Di), Di), "bf16"), W_B=store(nrm((N, Di), Di), "bf16"), W_C=store(nrm((N, Di), Di), "bf16"),
+        W_dt=store(0.1 * nrm((Di, R), R), "bf16"), b_dt=np.log(np.expm1(step)).astype(np.float32),
+        A=-np.tile(np.arange(1, N + 1, dtype=np.float32), (Di, 1)), D=np.ones(Di, dtype=np.float32),
+        W_out=store(nrm((Dm, Di), Di), "bf16"))
+
+
+def block_state(seed: int, Bsz: int, Dm: int, Di: int, N: int = 16, W: int = 4):
+    """Decode inputs of a block: hidden ~ N(0, 1) (bf16 [B, Dm]), register ~ N(0, 1) (bf16 [B, Di, W]),
+    state ~ 0.5 N(0, 1) (fp32 [B, Di, N])."""
+    g = _rng(seed, TID_BLOCK - 1)
+    return (store(g.standard_normal((Bsz, Dm)).astype(np.float32), "bf16"),
+            store(g.standard_normal((Bsz, Di, W)).astype(np.float32), "bf16"),
+            (0.5 * g.standard_normal((Bsz, Di, N))).astype(np.float32))
+
+
 @dataclass
 class DecodeStep:
     x: np.ndarray       # [B, D]

@@ -26,7 +26,9 @@ EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_last_error_detail",
            "ssm_scan_bwd_segmented_workspace_bytes", "ssm_scan_bwd_segmented",
            "ssm_state_update", "ssd_chunk_fwd_workspace_bytes", "ssd_chunk_fwd",
            "ssd_chunk_fwd_grouped_workspace_bytes", "ssd_chunk_fwd_grouped",
-           "ssd_chunk_bwd_workspace_bytes", "ssd_chunk_bwd")
+           "ssd_chunk_bwd_workspace_bytes", "ssd_chunk_bwd",
+           "ssm_linear_workspace_bytes", "ssm_linear", "ssm_layernorm",
+           "ssm_block_step_workspace_bytes", "ssm_block_step")
 
 _lib = None
 
@@ -91,6 +93,16 @@ def load(path: str = LIB_PATH):
     lib.ssd_chunk_bwd_workspace_bytes.restype = sz
     lib.ssd_chunk_bwd.argtypes = [i64] * 6 + [ci, vp, vp, vp, ci, vp, vp, vp, vp, ci] + [vp] * 13 + [vp, sz, vp]
     lib.ssd_chunk_bwd.restype = ci
+    lib.ssm_linear_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.ssm_linear_workspace_bytes.restype = sz
+    lib.ssm_linear.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssm_linear.restype = ci
+    lib.ssm_layernorm.argtypes = [i64, i64, vp, vp, vp, ctypes.c_float, vp, vp]
+    lib.ssm_layernorm.restype = ci
+    lib.ssm_block_step_workspace_bytes.argtypes = [i64] * 6
+    lib.ssm_block_step_workspace_bytes.restype = sz
+    lib.ssm_block_step.argtypes = [i64] * 6 + [vp, vp, vp, ctypes.c_float] + [vp] * 14 + [vp, sz, vp]
+    lib.ssm_block_step.restype = ci
     _lib = lib
     return lib
 
@@ -401,4 +413,65 @@ def ssd_chunk_bwd(x, delta, A, Bm, Cm, dy, *, delta_bias=None, delta_softplus=Fa
     if one_group:
         out["dBm"], out["dCm"] = out["dBm"][:, :, 0], out["dCm"][:, :, 0]
     return out
+
+
+def linear(x, W, *, residual=None, y=None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = x W^T (+ residual): x [M, K] bf16, W [Nout, K] bf16 -> y [M, Nout] bf16."""
+    lib = load()
+    M, K = x.shape
+    Nout = W.shape[0]
+    _dev(x, "x", torch.bfloat16)
+    _dev(W, "W", torch.bfloat16, (Nout, K))
+    _dev(residual, "residual", torch.bfloat16, (M, Nout))
+    if y is None:
+        y = torch.empty((M, Nout), dtype=torch.bfloat16, device=x.device)
+    nb = lib.ssm_linear_workspace_bytes(M, K, Nout)
+    if nb and (ws is None or ws.numel() < nb):
+        ws = workspace(nb, x.device)
+    _check(lib.ssm_linear(M, K, Nout, _p(x), _p(W), _p(residual), _p(y), _p(ws) if nb else None, nb, _stream(x)))
+    return y
+
+
+def layernorm(x, w, b, *, eps: float = 1e-5, y=None) -> torch.Tensor:
+    """Row LayerNorm of x [M, D] bf16 with w, b [D] float32 -> y (bf16; may be x)."""
+    lib = load()
+    M, D = x.shape
+    _dev(x, "x", torch.bfloat16)
+    _dev(w, "w", torch.float32, (D,))
+    _dev(b, "b", torch.float32, (D,))
+    if y is None:
+        y = torch.empty_like(x)
+    _check(lib.ssm_layernorm(M, D, _p(x), _p(w), _p(b), float(eps), _p(y), _stream(x)))
+    return y
+
+
+BLOCK_WEIGHTS = ("ln_w", "ln_b", "W_x", "W_z", "conv_w", "conv_b", "W_dtin", "W_B", "W_C", "W_dt", "b_dt", "A",
+                 "D", "W_out")
+
+
+def block_step(hidden, conv_state, h, wts: dict, *, eps: float = 1e-5, ws: Optional[torch.Tensor] = None):
+    """One decode token through a Mamba block, in place on hidden [B, Dm] bf16, conv_state
+    [B, Di, W] bf16 and h [B, Di, N] float32. wts: the BLOCK_WEIGHTS tensors on the device."""
+    lib = load()
+    Bsz, Dm = hidden.shape
+    Di, W = wts["conv_w"].shape
+    N = wts["A"].shape[1]
+    R = wts["W_dt"].shape[1]
+    bf, f32 = torch.bfloat16, torch.float32
+    _dev(hidden, "hidden", bf)
+    _dev(conv_state, "conv_state", bf, (Bsz, Di, W))
+    _dev(h, "h", f32, (Bsz, Di, N))
+    shapes = dict(ln_w=(f32, (Dm,)), ln_b=(f32, (Dm,)), W_x=(bf, (Di, Dm)), W_z=(bf, (Di, Dm)), conv_w=(f32, (Di, W)),
+                  conv_b=(f32, (Di,)), W_dtin=(bf, (R, Di)), W_B=(bf, (N, Di)), W_C=(bf, (N, Di)), W_dt=(bf, (Di, R)),
+                  b_dt=(f32, (Di,)), A=(f32, (Di, N)), D=(f32, (Di,)), W_out=(bf, (Dm, Di)))
+    for k, (dt, shp) in shapes.items():
+        _dev(wts.get(k), k, dt, shp)
+    nb = lib.ssm_block_step_workspace_bytes(Bsz, Dm, Di, N, W, R)
+    if ws is None or ws.numel() < nb:
+        ws = workspace(nb, hidden.device)
+    w = lambda k: _p(wts.get(k))
+    _check(lib.ssm_block_step(Bsz, Dm, Di, N, W, R, _p(hidden), w("ln_w"), w("ln_b"), float(eps), w("W_x"), w("W_z"),
+                              w("conv_w"), w("conv_b"), w("W_dtin"), w("W_B"), w("W_C"), w("W_dt"), w("b_dt"), w("A"),
+                              w("D"), w("W_out"), _p(conv_state), _p(h), _p(ws), nb, _stream(hidden)))
+    return hidden
 

@@ -212,6 +212,51 @@ def test_ssd_bwd_workspace(lib):
     assert lib.ssd_chunk_bwd_workspace_bytes(2, 8192, 80, 64, 128, 3, BF16) == 0   # 3 does not divide 80
 
 
+def linear_call(lib, M=8, K=256, Nout=64, x=A_, w=2 * A_, res=None, y=3 * A_, ws=4 * A_, wsb=1 << 40):
+    f = lambda v: fake(v) if v else None
+    return lib.ssm_linear(M, K, Nout, f(x), f(w), f(res), f(y), f(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(M=129), UNSUPPORTED), (dict(K=100), UNSUPPORTED), (dict(Nout=6), UNSUPPORTED), (dict(x=0), INVALID),
+    (dict(y=A_ + 64), INVALID), (dict(x=A_ + 2), INVALID), (dict(res=3 * A_ + 16), INVALID), (dict(M=0), OK),
+])
+def test_linear_rejects(lib, kw, expect):
+    assert linear_call(lib, **kw) == expect
+
+
+def test_linear_workspace(lib):
+    # enough column tiles: no split of K, no workspace; few tiles: float32 partial sums
+    assert lib.ssm_linear_workspace_bytes(77, 2048, 50288) == 0
+    assert lib.ssm_linear_workspace_bytes(128, 4096, 2048) == 8 * 128 * 2048 * 4
+
+
+def test_layernorm_rejects(lib):
+    f = fake
+    assert lib.ssm_layernorm(4, 12, f(A_), f(2 * A_), f(3 * A_), 1e-5, f(4 * A_), None) == UNSUPPORTED
+    assert lib.ssm_layernorm(4, 16, f(A_), f(2 * A_), f(3 * A_), 0.0, f(4 * A_), None) == INVALID
+    assert lib.ssm_layernorm(4, 16, f(A_), f(2 * A_), f(3 * A_), 1e-5, f(A_ + 16), None) == INVALID
+    assert lib.ssm_layernorm(0, 16, None, None, None, 1e-5, None, None) == OK
+
+
+def block_call(lib, B=4, Dm=256, Di=512, N=16, W=4, R=128, hidden=A_, conv_state=40 * A_, h=50 * A_, ws=60 * A_,
+               wsb=1 << 40, W_x=2 * A_, Dskip=None):
+    f = lambda v: fake(v) if v else None
+    return lib.ssm_block_step(B, Dm, Di, N, W, R, f(hidden), f(20 * A_), f(21 * A_), 1e-5, f(W_x), f(3 * A_),
+                              f(22 * A_), None, f(4 * A_), f(5 * A_), f(6 * A_), f(7 * A_), f(23 * A_), f(24 * A_),
+                              f(Dskip), f(8 * A_), f(conv_state), f(h), f(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(B=129), UNSUPPORTED), (dict(Dm=200), UNSUPPORTED), (dict(Di=100), UNSUPPORTED), (dict(R=64), UNSUPPORTED),
+    (dict(N=2), UNSUPPORTED), (dict(W=9), UNSUPPORTED), (dict(hidden=0), INVALID), (dict(W_x=0), INVALID),
+    (dict(hidden=2 * A_), INVALID), (dict(h=40 * A_ + 64), INVALID), (dict(ws=0, wsb=0), WS_SMALL),
+    (dict(wsb=64), WS_SMALL), (dict(hidden=A_ + 4), INVALID), (dict(B=0), OK),
+])
+def test_block_step_rejects(lib, kw, expect):
+    assert block_call(lib, **kw) == expect
+
+
 def test_ssd_grouped_workspace(lib):
     """Per group: C B^T and transposed B per chunk; G = 1 is the ungrouped layout."""
     one = lib.ssd_chunk_fwd_workspace_bytes(2, 8192, 80, 64, 128, 256, BF16)

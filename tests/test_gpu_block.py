@@ -1,0 +1,92 @@
+"""GPU parity of the generation workload's pieces against the fp64 oracle: ssm_linear (the
+block's products, every K split the launcher picks, ragged batch sizes, the residual form),
+ssm_layernorm, and ssm_block_step (one Mamba block per decode token) over several consecutive
+tokens with the register and state carried, at a small shape and at the Mamba-1.4B layer shape
+(batch 128, d_model 2048, d_inner 4096, N 16, rank 128)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from selective_state_space_37_amd import inputs, ssm
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf(a):
+    return inputs.widen(a, "bf16")
+
+
+@pytest.mark.parametrize("M,K,Nout", [(1, 128, 4), (5, 256, 16), (16, 2048, 4096), (100, 4096, 160),
+                                      (128, 4096, 2048), (128, 128, 4096), (77, 2048, 50288)])
+def test_linear(M, K, Nout):
+    g = np.random.default_rng(M + K + Nout)
+    x = inputs.store(g.standard_normal((M, K)).astype(np.float32), "bf16")
+    w = inputs.store((g.standard_normal((Nout, K)) / np.sqrt(K)).astype(np.float32), "bf16")
+    y = gu.host(ssm.linear(gu.dev(x), gu.dev(w)))
+    ref = _bf(x) @ _bf(w).T
+    err = gu.rel_err(y, ref)
+    print("linear", M, K, Nout, "err %.2e" % err)
+    assert err <= gu.TOL["bf16"]
+
+
+def test_linear_residual_in_place():
+    g = np.random.default_rng(3)
+    M, K, Nout = 64, 4096, 2048
+    x = inputs.store(g.standard_normal((M, K)).astype(np.float32), "bf16")
+    w = inputs.store((g.standard_normal((Nout, K)) / np.sqrt(K)).astype(np.float32), "bf16")
+    r = inputs.store(g.standard_normal((M, Nout)).astype(np.float32), "bf16")
+    rd = gu.dev(r)
+    ssm.linear(gu.dev(x), gu.dev(w), residual=rd, y=rd)
+    assert gu.rel_err(gu.host(rd), _bf(r) + _bf(x) @ _bf(w).T) <= gu.TOL["bf16"]
+
+
+def test_layernorm():
+    g = np.random.default_rng(4)
+    for M, D in ((3, 8), (128, 2048), (7, 8192)):
+        x = inputs.store((2 + 3 * g.standard_normal((M, D))).astype(np.float32), "bf16")
+        w, b = g.standard_normal(D).astype(np.float32), g.standard_normal(D).astype(np.float32)
+        y = gu.host(ssm.layernorm(gu.dev(x), gu.dev(w), gu.dev(b)))
+        assert gu.rel_err(y, oracle.layernorm(_bf(x), w, b)) <= gu.TOL["bf16"], (M, D)
+
+
+def _block_run(Bsz, Dm, Di, N, steps, seed):
+    wts = inputs.block_weights(seed, Dm, Di, N)
+    hid, reg, h = inputs.block_state(seed, Bsz, Dm, Di, N)
+    dw = {k: gu.dev(v) for k, v in wts.items()}
+    dh, dreg, dst = gu.dev(hid), gu.dev(reg), gu.dev(h)
+    wf = {k: (_bf(v) if v.dtype == np.uint16 else v.astype(np.float64)) for k, v in wts.items()}
+    rh, rreg, rst = _bf(hid), _bf(reg), h.astype(np.float64)
+    g = np.random.default_rng(seed + 1)
+    errs = []
+    for t in range(steps):
+        ssm.block_step(dh, dreg, dst, dw)
+        torch.cuda.synchronize()
+        # the oracle continues from the GPU's own (bf16) hidden input of this token
+        rh, rreg, rst = oracle.block_step(rh, rreg, rst, wf)
+        errs.append((gu.rel_err(gu.host(dh), rh), gu.rel_err(gu.host(dreg), rreg), gu.rel_err(gu.host(dst), rst)))
+        # next token: a fresh input row added to the residual stream on both sides
+        nxt = inputs.store(g.standard_normal((Bsz, Dm)).astype(np.float32), "bf16")
+        dh = gu.dev(nxt)
+        rh = _bf(nxt)
+    return errs
+
+
+def test_block_step_small():
+    errs = _block_run(Bsz=5, Dm=256, Di=512, N=16, steps=4, seed=70)
+    print(errs)
+    assert max(max(e) for e in errs) <= gu.TOL["bf16"]
+
+
+@pytest.mark.parametrize("N", [4, 8])
+def test_block_step_state_sizes(N):
+    errs = _block_run(Bsz=3, Dm=128, Di=256, N=N, steps=2, seed=71 + N)
+    assert max(max(e) for e in errs) <= gu.TOL["bf16"]
+
+
+def test_block_step_mamba_1_4b_layer():
+    """Batch 128, d_model 2048, d_inner 4096, N 16, conv 4, rank 128: two tokens."""
+    errs = _block_run(Bsz=128, Dm=2048, Di=4096, N=16, steps=2, seed=72)
+    print(errs)
+    assert max(max(e) for e in errs) <= gu.TOL["bf16"]

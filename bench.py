@@ -448,7 +448,67 @@ def secondary(torch, np, inputs, ssm, dev):
         "TFLOP_s": round(flops_b / msb / 1e9, 1), "mfma_frac": round(flops_b / msb / 1e9 / PEAK_BF16_TFLOPS, 4),
         "workspace_MB": round(nbw / 1e6, 1)}
     del dy, wsb
+
+    res["generation_mamba_1.4b_b128"] = generation(torch, ssm, g)
     return res
+
+
+def generation(torch, ssm, g):
+    """Decode steps of a Mamba-1.4B-shaped model at batch 128 (the pages' generation setting):
+    48 blocks (d_model 2048, d_inner 4096, N 16, conv 4, rank 128) with synthetic weights drawn on
+    the device, then the final LayerNorm and the LM head (vocabulary 50280, padded to 50288).
+    One step = one token for each of the 128 sequences through the whole stack, captured in one
+    HIP graph. Sampling and the embedding lookup are not timed."""
+    layers, Bsz, Dm, Di, N, W, R, V = 48, 128, 2048, 4096, 16, 4, 128, 50288
+    bf, f32, dev = torch.bfloat16, torch.float32, "cuda"
+    nrm = lambda *shape, fan: (torch.randn(*shape, generator=g, device=dev) / fan ** 0.5).to(bf)
+    blocks = []
+    for _ in range(layers):
+        step = torch.exp(torch.empty(Di, device=dev).uniform_(-6.9, -2.3, generator=g))
+        blocks.append(dict(
+            ln_w=torch.ones(Dm, device=dev), ln_b=torch.zeros(Dm, device=dev),
+            W_in=nrm(2 * Di, Dm, fan=Dm),
+            conv_w=torch.randn(Di, W, generator=g, device=dev) / 2, conv_b=torch.zeros(Di, device=dev),
+            W_xp=nrm(R + 2 * N, Di, fan=Di),
+            W_dt=(nrm(Di, R, fan=R).float() * 0.1).to(bf), b_dt=torch.log(torch.expm1(step)),
+            A=-torch.arange(1, N + 1, device=dev, dtype=f32).repeat(Di, 1).contiguous(), D=torch.ones(Di, device=dev),
+            W_out=nrm(Dm, Di, fan=Di)))
+    regs = [torch.randn(Bsz, Di, W, generator=g, device=dev).to(bf) for _ in range(layers)]
+    hs = [torch.zeros(Bsz, Di, N, device=dev, dtype=f32) for _ in range(layers)]
+    ln_w, ln_b = torch.ones(Dm, device=dev), torch.zeros(Dm, device=dev)
+    W_lm = nrm(V, Dm, fan=Dm)
+    hidden = torch.randn(Bsz, Dm, generator=g, device=dev).to(bf)
+    hn = torch.empty_like(hidden)
+    logits = torch.empty(Bsz, V, device=dev, dtype=bf)
+    lib = ssm.load()
+    ws = ssm.workspace(max(lib.ssm_block_step_workspace_bytes(Bsz, Dm, Di, N, W, R),
+                           lib.ssm_linear_workspace_bytes(Bsz, Dm, V), 16), dev)
+
+    def one_step():
+        for l in range(layers):
+            ssm.block_step(hidden, regs[l], hs[l], blocks[l], ws=ws)
+        ssm.layernorm(hidden, ln_w, ln_b, y=hn)
+        ssm.linear(hn, W_lm, y=logits, ws=ws)
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        one_step()   # warm (and load) before capture
+    torch.cuda.current_stream().wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_step()
+    _, ms = timed(lambda i: graph.replay(), 20, 3, torch)
+    # HBM bytes per step: every weight once; the SSM state (float32) and the conv register (bf16)
+    # of every layer read and written; activations are small and mostly cache-resident
+    wbytes = layers * (2 * Di * Dm + R * Di + 2 * N * Di + Di * R + Dm * Di) * 2 + V * Dm * 2
+    sbytes = layers * Bsz * Di * (N * 4 + W * 2) * 2
+    gbs = (wbytes + sbytes) / ms / 1e6
+    del blocks, regs, hs, W_lm, graph
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(Bsz / (ms * 1e-3), 1),
+            "GB_s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "bytes_per_step": {"weights": wbytes, "states": sbytes},
+            "model": "48 blocks d_model 2048 d_inner 4096 N 16 conv 4 rank 128, vocab 50288, batch 128, bf16 weights"}
 
 
 def cpu_baseline(host, np, inputs):

@@ -330,18 +330,18 @@ ssm_status ssm_layernorm(int64_t M, int64_t D, const void* x, const float* w, co
 /*
  * ssm_block_step -- one decode token through a Mamba block, for B sequences:
  *   xn = LayerNorm(hidden; ln_w, ln_b, eps)
- *   xi = xn W_x^T,  zi = xn W_z^T                                   [B, d_inner]
+ *   [xi | zi] = xn W_in^T                                         [B, 2 d_inner]
  *   u  = SiLU(conv(register with xi appended; conv_w, conv_b))        (register updated)
- *   dt = (u W_dtin^T) W_dt^T,  Bt = u W_B^T,  Ct = u W_C^T             (rank-R Delta path)
+ *   [dl | Bt | Ct] = u W_xp^T,  dt = dl W_dt^T                        (rank-R Delta path)
  *   y  = the selective state update of ssm_state_update on u with delta dt, delta_bias b_dt,
  *        softplus, A, Bt, Ct, Dskip and gate zi (h updated in place)
  *   hidden += y W_out^T
  *
  *   hidden     : [B, d_model] bf16, in/out        conv_state : [B, d_inner, W] bf16, in/out
  *   h          : [B, d_inner, N] float32, in/out
- *   ln_w, ln_b : [d_model] float32      W_x, W_z : [d_inner, d_model] bf16
+ *   ln_w, ln_b : [d_model] float32      W_in : [2 d_inner, d_model] bf16 (SSM branch rows, then gate rows)
  *   conv_w     : [d_inner, W] float32   conv_b : [d_inner] float32 or NULL
- *   W_dtin     : [R, d_inner] bf16      W_B, W_C : [N, d_inner] bf16    W_dt : [d_inner, R] bf16
+ *   W_xp       : [R + 2 N, d_inner] bf16 (Delta rank rows, B rows, C rows)   W_dt : [d_inner, R] bf16
  *   b_dt       : [d_inner] float32      A : [d_inner, N] float32 (< 0)   Dskip : [d_inner] or NULL
  *   W_out      : [d_model, d_inner] bf16
  *   Intermediate activations are bf16 in the workspace (ssm_block_step_workspace_bytes()).
@@ -355,9 +355,8 @@ size_t ssm_block_step_workspace_bytes(int64_t B, int64_t d_model, int64_t d_inne
 
 ssm_status ssm_block_step(int64_t B, int64_t d_model, int64_t d_inner, int64_t N, int64_t W,
                           int64_t R, void* hidden, const float* ln_w, const float* ln_b, float eps,
-                          const void* W_x, const void* W_z, const float* conv_w,
-                          const float* conv_b, const void* W_dtin, const void* W_B,
-                          const void* W_C, const void* W_dt, const float* b_dt, const float* A,
+                          const void* W_in, const float* conv_w, const float* conv_b,
+                          const void* W_xp, const void* W_dt, const float* b_dt, const float* A,
                           const float* Dskip, const void* W_out, void* conv_state, float* h,
                           void* workspace, size_t workspace_bytes, void* stream);
 

@@ -439,10 +439,10 @@ size_t ssm_block_step_workspace_bytes(int64_t B, int64_t d_model, int64_t d_inne
 }
 
 ssm_status ssm_block_step(int64_t B, int64_t d_model, int64_t d_inner, int64_t N, int64_t W, int64_t R, void* hidden,
-                          const float* ln_w, const float* ln_b, float eps, const void* W_x, const void* W_z,
-                          const float* conv_w, const float* conv_b, const void* W_dtin, const void* W_B,
-                          const void* W_C, const void* W_dt, const float* b_dt, const float* A, const float* Dskip,
-                          const void* W_out, void* conv_state, float* h, void* ws, size_t ws_bytes, void* stream) {
+                          const float* ln_w, const float* ln_b, float eps, const void* W_in, const float* conv_w,
+                          const float* conv_b, const void* W_xp, const void* W_dt, const float* b_dt, const float* A,
+                          const float* Dskip, const void* W_out, void* conv_state, float* h, void* ws, size_t ws_bytes,
+                          void* stream) {
   if (B < 0 || B > 128) return fail(SSM_ERR_UNSUPPORTED, "B=%lld: 0..128 sequences", (long long)B);
   if (d_model < 128 || d_model % 128 != 0 || d_model > 8192)
     return fail(SSM_ERR_UNSUPPORTED, "d_model=%lld: a multiple of 128 up to 8192", (long long)d_model);
@@ -452,24 +452,23 @@ ssm_status ssm_block_step(int64_t B, int64_t d_model, int64_t d_inner, int64_t N
   if (W < 1 || W > 8) return fail(SSM_ERR_UNSUPPORTED, "W=%lld: supported 1..8", (long long)W);
   if (!(eps > 0.f)) return fail(SSM_ERR_INVALID_ARGUMENT, "eps must be > 0");
   if (B == 0) return ok();
-  const void* need_ptrs[] = {hidden, ln_w, ln_b, W_x, W_z, conv_w, W_dtin, W_B, W_C, W_dt, b_dt, A, W_out, conv_state, h};
+  const void* need_ptrs[] = {hidden, ln_w, ln_b, W_in, conv_w, W_xp, W_dt, b_dt, A, W_out, conv_state, h};
   for (const void* q : need_ptrs)
     if (!q) return fail(SSM_ERR_INVALID_ARGUMENT, "a required pointer is NULL (only conv_b and Dskip may be)");
-  const void* al[] = {hidden, W_x, W_z, W_dtin, W_B, W_C, W_dt, W_out, conv_state, h, A};
+  const void* al[] = {hidden, W_in, W_xp, W_dt, W_out, conv_state, h, A};
   for (const void* q : al)
     if (!aligned16(q)) return fail(SSM_ERR_INVALID_ARGUMENT, "hidden, the weight matrices, A, conv_state and h must be 16-byte aligned");
   // the in/out tensors overlap nothing else
   const size_t hb = (size_t)(B * d_model) * 2, cb = (size_t)(B * d_inner * W) * 2, sb = (size_t)(B * d_inner * N) * 4;
-  const void* ins[] = {ln_w, ln_b, W_x, W_z, conv_w, conv_b, W_dtin, W_B, W_C, W_dt, b_dt, A, Dskip, W_out};
-  const size_t insz[] = {(size_t)d_model * 4, (size_t)d_model * 4, (size_t)(d_inner * d_model) * 2,
-                         (size_t)(d_inner * d_model) * 2, (size_t)(d_inner * W) * 4, (size_t)d_inner * 4,
-                         (size_t)(R * d_inner) * 2, (size_t)(N * d_inner) * 2, (size_t)(N * d_inner) * 2,
+  const void* ins[] = {ln_w, ln_b, W_in, conv_w, conv_b, W_xp, W_dt, b_dt, A, Dskip, W_out};
+  const size_t insz[] = {(size_t)d_model * 4, (size_t)d_model * 4, (size_t)(2 * d_inner * d_model) * 2,
+                         (size_t)(d_inner * W) * 4, (size_t)d_inner * 4, (size_t)((R + 2 * N) * d_inner) * 2,
                          (size_t)(d_inner * R) * 2, (size_t)d_inner * 4, (size_t)(d_inner * N) * 4, (size_t)d_inner * 4,
                          (size_t)(d_model * d_inner) * 2};
   void* io[] = {hidden, conv_state, h};
   const size_t iosz[] = {hb, cb, sb};
   for (int o = 0; o < 3; ++o) {
-    for (int k = 0; k < 14; ++k)
+    for (int k = 0; k < 11; ++k)
       if (overlaps(io[o], iosz[o], ins[k], insz[k])) return fail(SSM_ERR_INVALID_ARGUMENT, "hidden, conv_state or h overlaps a weight");
     for (int k = o + 1; k < 3; ++k)
       if (overlaps(io[o], iosz[o], io[k], iosz[k])) return fail(SSM_ERR_INVALID_ARGUMENT, "hidden, conv_state and h overlap");
@@ -482,8 +481,8 @@ ssm_status ssm_block_step(int64_t B, int64_t d_model, int64_t d_inner, int64_t N
     if (overlaps(ws, need, io[o], iosz[o])) return fail(SSM_ERR_INVALID_ARGUMENT, "workspace overlaps hidden, conv_state or h");
   ssm::BlockParams p{};
   p.B = B; p.Dm = d_model; p.Di = d_inner; p.N = N; p.W = W; p.R = R; p.eps = eps;
-  p.hidden = hidden; p.ln_w = ln_w; p.ln_b = ln_b; p.W_x = W_x; p.W_z = W_z; p.conv_w = conv_w; p.conv_b = conv_b;
-  p.W_dtin = W_dtin; p.W_B = W_B; p.W_C = W_C; p.W_dt = W_dt; p.b_dt = b_dt; p.A = A; p.Dskip = Dskip;
+  p.hidden = hidden; p.ln_w = ln_w; p.ln_b = ln_b; p.W_in = W_in; p.conv_w = conv_w; p.conv_b = conv_b;
+  p.W_xp = W_xp; p.W_dt = W_dt; p.b_dt = b_dt; p.A = A; p.Dskip = Dskip;
   p.W_out = W_out; p.conv_state = conv_state; p.h = h;
   return from_hip(ssm::launch_block_step(p, ws, static_cast<hipStream_t>(stream)), "ssm_block_step launch");
 }

@@ -187,15 +187,24 @@ __global__ __launch_bounds__(256) void gemm_xwt_kernel(GemmParams p) {
   }
 }
 
-// Y = sum over the S partials in order (+ R), four outputs per thread.
+// Y = sum over the S partials in order (+ R), four outputs per thread. The partials are loaded
+// eight at a time before they are added, so a thread has several loads in flight.
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmParams p) {
   const int64_t total = p.M * (p.Nout / 4);
   for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
     const int64_t m = e / (p.Nout / 4), n = (e % (p.Nout / 4)) * 4;
-    float4 s = *reinterpret_cast<const float4*>(p.partial + m * p.Nout + n);
-    for (int64_t k = 1; k < p.S; ++k) {
-      const float4 t = *reinterpret_cast<const float4*>(p.partial + (k * p.M + m) * p.Nout + n);
-      s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+    const float* src = p.partial + m * p.Nout + n;
+    const int64_t stride = p.M * p.Nout;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t k0 = 0; k0 < p.S; k0 += 8) {
+      float4 t[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        t[k] = k0 + k < p.S ? *reinterpret_cast<const float4*>(src + (k0 + k) * stride) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        s.x += t[k].x; s.y += t[k].y; s.z += t[k].z; s.w += t[k].w;
+      }
     }
     if (p.residual) {
       const uint2 rr = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(p.residual) + m * p.ldy + n);
@@ -206,13 +215,13 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------- conv + SiLU
-// Per (b, d): shift the register of the last W raw inputs (oldest first), append x, and
-// u = SiLU(sum_k w[d][k] reg[k] + bias[d]); w[d][W-1] multiplies the newest input.
-__global__ __launch_bounds__(256) void conv_silu_kernel(int64_t B, int64_t D, int64_t W, const bf16_t* x,
+// Per (b, d): shift the register of the last W raw inputs (oldest first), append x[b][d] (row
+// stride ldx), and u = SiLU(sum_k w[d][k] reg[k] + bias[d]); w[d][W-1] multiplies the newest input.
+__global__ __launch_bounds__(256) void conv_silu_kernel(int64_t B, int64_t D, int64_t W, const bf16_t* x, int64_t ldx,
                                                         bf16_t* reg, const float* cw, const float* cb, bf16_t* u) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= B * D) return;
-  const int64_t d = e % D;
+  const int64_t d = e % D, b = e / D;
   bf16_t* r = reg + e * W;
   float acc = cb ? cb[d] : 0.f;
   for (int64_t k = 0; k + 1 < W; ++k) {
@@ -220,7 +229,7 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(int64_t B, int64_t D, in
     r[k] = v;
     acc += cw[d * W + k] * bf16_to_f32(v.bits);
   }
-  const bf16_t xn = x[e];
+  const bf16_t xn = x[b * ldx + d];
   r[W - 1] = xn;
   acc += cw[d * W + W - 1] * bf16_to_f32(xn.bits);
   u[e].bits = f32_to_bf16(silu(acc));
@@ -268,61 +277,57 @@ hipError_t launch_layernorm(int64_t M, int64_t D, const void* x, const float* w,
   return hipGetLastError();
 }
 
-// Workspace of one block step: xn [B, Dm], xi, zi, u, dt, y [B, Di], dtl [B, R], Bt, Ct [B, N]
-// (bf16, each 256-byte aligned) and the largest product's partial sums.
+// Workspace of one block step: xn [B, Dm], xz [B, 2 Di] (SSM branch and gate), u, dt, y [B, Di],
+// xp [B, R + 2 N] (Delta rank part, B, C) (bf16, each 256-byte aligned) and the largest product's
+// partial sums.
 static size_t blk_align(size_t n) { return (n + 255) & ~(size_t)255; }
 
 size_t block_workspace_bytes(int64_t B, int64_t Dm, int64_t Di, int64_t N, int64_t R) {
-  const size_t acts = blk_align(B * Dm * 2) + 5 * blk_align(B * Di * 2) + blk_align(B * R * 2) + 2 * blk_align(B * N * 2);
+  const size_t acts = blk_align(B * Dm * 2) + blk_align(B * 2 * Di * 2) + 3 * blk_align(B * Di * 2) +
+                      blk_align(B * (R + 2 * N) * 2);
   size_t part = 0;
-  const int64_t shapes[6][2] = {{Dm, Di}, {Di, R}, {Di, N}, {R, Di}, {Di, Dm}, {Dm, Di}};   // (K, Nout)
+  const int64_t shapes[4][2] = {{Dm, 2 * Di}, {Di, R + 2 * N}, {R, Di}, {Di, Dm}};   // (K, Nout)
   for (auto& s : shapes) part = std::max(part, gemm_workspace_bytes(B, s[0], s[1]));
   return acts + blk_align(part);
 }
 
 hipError_t launch_block_step(const BlockParams& bp, void* ws, hipStream_t st) {
-  const int64_t B = bp.B, Dm = bp.Dm, Di = bp.Di, N = bp.N, R = bp.R;
+  const int64_t B = bp.B, Dm = bp.Dm, Di = bp.Di, N = bp.N, R = bp.R, XP = R + 2 * N;
   char* base = static_cast<char*>(ws);
   auto take = [&](size_t n) { void* q = base; base += blk_align(n); return q; };
-  void* xn = take(B * Dm * 2);
-  void* xi = take(B * Di * 2);
-  void* zi = take(B * Di * 2);
-  void* u = take(B * Di * 2);
-  void* dt = take(B * Di * 2);
-  void* y = take(B * Di * 2);
-  void* dtl = take(B * R * 2);
-  void* Bt = take(B * N * 2);
-  void* Ct = take(B * N * 2);
+  bf16_t* xn = static_cast<bf16_t*>(take(B * Dm * 2));
+  bf16_t* xz = static_cast<bf16_t*>(take(B * 2 * Di * 2));
+  bf16_t* u = static_cast<bf16_t*>(take(B * Di * 2));
+  bf16_t* dt = static_cast<bf16_t*>(take(B * Di * 2));
+  bf16_t* y = static_cast<bf16_t*>(take(B * Di * 2));
+  bf16_t* xp = static_cast<bf16_t*>(take(B * XP * 2));
   float* partial = reinterpret_cast<float*>(base);
-  auto gemm = [&](const void* x, int64_t K, const void* w, int64_t Nout, void* out, const void* res) {
+  auto gemm = [&](const void* x, int64_t ldx, int64_t K, const void* w, int64_t Nout, void* out, const void* res) {
     GemmParams g{};
-    g.M = B; g.K = K; g.Nout = Nout; g.x = x; g.ldx = K; g.w = w; g.y = out; g.ldy = Nout; g.residual = res;
+    g.M = B; g.K = K; g.Nout = Nout; g.x = x; g.ldx = ldx; g.w = w; g.y = out; g.ldy = Nout; g.residual = res;
     g.partial = partial;
     return launch_gemm(g, st);
   };
   hipError_t e = launch_layernorm(B, Dm, bp.hidden, bp.ln_w, bp.ln_b, bp.eps, xn, st);
-  if (e == hipSuccess) e = gemm(xn, Dm, bp.W_x, Di, xi, nullptr);
-  if (e == hipSuccess) e = gemm(xn, Dm, bp.W_z, Di, zi, nullptr);
+  if (e == hipSuccess) e = gemm(xn, Dm, Dm, bp.W_in, 2 * Di, xz, nullptr);          // [x | z]
   if (e == hipSuccess) {
     hipLaunchKernelGGL(conv_silu_kernel, dim3((unsigned)((B * Di + 255) / 256)), dim3(256), 0, st, B, Di, bp.W,
-                       static_cast<const bf16_t*>(xi), static_cast<bf16_t*>(bp.conv_state), bp.conv_w, bp.conv_b,
-                       static_cast<bf16_t*>(u));
+                       xz, 2 * Di, static_cast<bf16_t*>(bp.conv_state), bp.conv_w, bp.conv_b, u);
     e = hipGetLastError();
   }
-  if (e == hipSuccess) e = gemm(u, Di, bp.W_dtin, R, dtl, nullptr);
-  if (e == hipSuccess) e = gemm(u, Di, bp.W_B, N, Bt, nullptr);
-  if (e == hipSuccess) e = gemm(u, Di, bp.W_C, N, Ct, nullptr);
-  if (e == hipSuccess) e = gemm(dtl, R, bp.W_dt, Di, dt, nullptr);
+  if (e == hipSuccess) e = gemm(u, Di, Di, bp.W_xp, XP, xp, nullptr);                // [Delta rank | B | C]
+  if (e == hipSuccess) e = gemm(xp, XP, R, bp.W_dt, Di, dt, nullptr);                // rank part only
   if (e == hipSuccess) {
     StepParams sp{};
     sp.B = B; sp.D = Di; sp.N = N; sp.W = 0; sp.io_bf16 = 1;
-    sp.x = u; sp.delta = dt; sp.z = zi; sp.Bm = Bt; sp.Cm = Ct;
+    sp.x = u; sp.delta = dt; sp.z = xz + Di; sp.z_stride = 2 * Di;
+    sp.Bm = xp + R; sp.Cm = xp + R + N; sp.bc_stride = XP;
     sp.delta_bias = bp.b_dt; sp.A = bp.A; sp.Dskip = bp.Dskip;
     sp.conv_state = nullptr; sp.conv_w = nullptr; sp.conv_b = nullptr;
     sp.h = bp.h; sp.y = y; sp.delta_softplus = 1;
     e = launch_state_update(sp, st);
   }
-  if (e == hipSuccess) e = gemm(y, Di, bp.W_out, Dm, bp.hidden, bp.hidden);
+  if (e == hipSuccess) e = gemm(y, Di, Di, bp.W_out, Dm, bp.hidden, bp.hidden);
   return e;
 }
 

@@ -108,6 +108,8 @@ struct StepParams {
   float* h;
   void* y;
   int delta_softplus;
+  int64_t bc_stride;       // row stride (elements) of Bm and Cm; 0: N
+  int64_t z_stride;        // row stride of z; 0: D
 };
 
 hipError_t launch_state_update(const StepParams& p, hipStream_t stream);
@@ -191,13 +193,10 @@ struct BlockParams {
   void* hidden;                       // bf16 [B, Dm], in/out (the residual stream)
   const float* ln_w;                  // [Dm]
   const float* ln_b;                  // [Dm]
-  const void* W_x;                    // bf16 [Di, Dm]
-  const void* W_z;                    // bf16 [Di, Dm]
+  const void* W_in;                   // bf16 [2 Di, Dm]: rows [0, Di) the SSM branch, [Di, 2 Di) the gate
   const float* conv_w;                // [Di, W]
   const float* conv_b;                // nullable [Di]
-  const void* W_dtin;                 // bf16 [R, Di]
-  const void* W_B;                    // bf16 [N, Di]
-  const void* W_C;                    // bf16 [N, Di]
+  const void* W_xp;                   // bf16 [R + 2 N, Di]: rows Delta (rank R), B, C
   const void* W_dt;                   // bf16 [Di, R]
   const float* b_dt;                  // [Di]
   const float* A;                     // [Di, N]

@@ -209,12 +209,24 @@ def block_weights(seed: int, Dm: int, Di: int, N: int = 16, W: int = 4, R: int =
     step = np.exp(g.uniform(np.log(1e-3), np.log(0.1), Di))
     return dict(
         ln_w=(1 + 0.1 * g.standard_normal(Dm)).astype(np.float32), ln_b=(0.1 * g.standard_normal(Dm)).astype(np.float32),
-        W_x=store(nrm((Di, Dm), Dm), "bf16"), W_z=store(nrm((Di, Dm), Dm), "bf16"),
+        W_in=store(nrm((2 * Di, Dm), Dm), "bf16"),            # rows: SSM branch, then gate
         conv_w=nrm((Di, W), W), conv_b=(0.1 * g.standard_normal(Di)).astype(np.float32),
-        W_dtin=store(nrm((R, Di), Di), "bf16"), W_B=store(nrm((N, Di), Di), "bf16"), W_C=store(nrm((N, Di), Di), "bf16"),
+        W_xp=store(nrm((R + 2 * N, Di), Di), "bf16"),         # rows: Delta rank part, B, C
         W_dt=store(0.1 * nrm((Di, R), R), "bf16"), b_dt=np.log(np.expm1(step)).astype(np.float32),
         A=-np.tile(np.arange(1, N + 1, dtype=np.float32), (Di, 1)), D=np.ones(Di, dtype=np.float32),
         W_out=store(nrm((Dm, Di), Di), "bf16"))
+
+
+def block_weights_split(wts: dict) -> dict:
+    """The same weights with the stacked projections as separate matrices (W_x, W_z; W_dtin, W_B,
+    W_C), the oracle's naming."""
+    Di = wts["conv_w"].shape[0]
+    N = wts["A"].shape[1]
+    R = wts["W_dt"].shape[1]
+    out = {k: v for k, v in wts.items() if k not in ("W_in", "W_xp")}
+    out.update(W_x=wts["W_in"][:Di], W_z=wts["W_in"][Di:], W_dtin=wts["W_xp"][:R], W_B=wts["W_xp"][R:R + N],
+               W_C=wts["W_xp"][R + N:])
+    return out
 
 
 def block_state(seed: int, Bsz: int, Dm: int, Di: int, N: int = 16, W: int = 4):

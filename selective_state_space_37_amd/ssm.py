@@ -101,7 +101,7 @@ def load(path: str = LIB_PATH):
     lib.ssm_layernorm.restype = ci
     lib.ssm_block_step_workspace_bytes.argtypes = [i64] * 6
     lib.ssm_block_step_workspace_bytes.restype = sz
-    lib.ssm_block_step.argtypes = [i64] * 6 + [vp, vp, vp, ctypes.c_float] + [vp] * 14 + [vp, sz, vp]
+    lib.ssm_block_step.argtypes = [i64] * 6 + [vp, vp, vp, ctypes.c_float] + [vp] * 11 + [vp, sz, vp]
     lib.ssm_block_step.restype = ci
     _lib = lib
     return lib
@@ -445,8 +445,7 @@ def layernorm(x, w, b, *, eps: float = 1e-5, y=None) -> torch.Tensor:
     return y
 
 
-BLOCK_WEIGHTS = ("ln_w", "ln_b", "W_x", "W_z", "conv_w", "conv_b", "W_dtin", "W_B", "W_C", "W_dt", "b_dt", "A",
-                 "D", "W_out")
+BLOCK_WEIGHTS = ("ln_w", "ln_b", "W_in", "conv_w", "conv_b", "W_xp", "W_dt", "b_dt", "A", "D", "W_out")
 
 
 def block_step(hidden, conv_state, h, wts: dict, *, eps: float = 1e-5, ws: Optional[torch.Tensor] = None):
@@ -458,20 +457,21 @@ def block_step(hidden, conv_state, h, wts: dict, *, eps: float = 1e-5, ws: Optio
     N = wts["A"].shape[1]
     R = wts["W_dt"].shape[1]
     bf, f32 = torch.bfloat16, torch.float32
+    XP = R + 2 * N
     _dev(hidden, "hidden", bf)
     _dev(conv_state, "conv_state", bf, (Bsz, Di, W))
     _dev(h, "h", f32, (Bsz, Di, N))
-    shapes = dict(ln_w=(f32, (Dm,)), ln_b=(f32, (Dm,)), W_x=(bf, (Di, Dm)), W_z=(bf, (Di, Dm)), conv_w=(f32, (Di, W)),
-                  conv_b=(f32, (Di,)), W_dtin=(bf, (R, Di)), W_B=(bf, (N, Di)), W_C=(bf, (N, Di)), W_dt=(bf, (Di, R)),
-                  b_dt=(f32, (Di,)), A=(f32, (Di, N)), D=(f32, (Di,)), W_out=(bf, (Dm, Di)))
+    shapes = dict(ln_w=(f32, (Dm,)), ln_b=(f32, (Dm,)), W_in=(bf, (2 * Di, Dm)), conv_w=(f32, (Di, W)),
+                  conv_b=(f32, (Di,)), W_xp=(bf, (XP, Di)), W_dt=(bf, (Di, R)), b_dt=(f32, (Di,)), A=(f32, (Di, N)),
+                  D=(f32, (Di,)), W_out=(bf, (Dm, Di)))
     for k, (dt, shp) in shapes.items():
         _dev(wts.get(k), k, dt, shp)
     nb = lib.ssm_block_step_workspace_bytes(Bsz, Dm, Di, N, W, R)
     if ws is None or ws.numel() < nb:
         ws = workspace(nb, hidden.device)
     w = lambda k: _p(wts.get(k))
-    _check(lib.ssm_block_step(Bsz, Dm, Di, N, W, R, _p(hidden), w("ln_w"), w("ln_b"), float(eps), w("W_x"), w("W_z"),
-                              w("conv_w"), w("conv_b"), w("W_dtin"), w("W_B"), w("W_C"), w("W_dt"), w("b_dt"), w("A"),
-                              w("D"), w("W_out"), _p(conv_state), _p(h), _p(ws), nb, _stream(hidden)))
+    _check(lib.ssm_block_step(Bsz, Dm, Di, N, W, R, _p(hidden), w("ln_w"), w("ln_b"), float(eps), w("W_in"),
+                              w("conv_w"), w("conv_b"), w("W_xp"), w("W_dt"), w("b_dt"), w("A"), w("D"), w("W_out"),
+                              _p(conv_state), _p(h), _p(ws), nb, _stream(hidden)))
     return hidden
 

@@ -242,9 +242,9 @@ def test_layernorm_rejects(lib):
 def block_call(lib, B=4, Dm=256, Di=512, N=16, W=4, R=128, hidden=A_, conv_state=40 * A_, h=50 * A_, ws=60 * A_,
                wsb=1 << 40, W_x=2 * A_, Dskip=None):
     f = lambda v: fake(v) if v else None
-    return lib.ssm_block_step(B, Dm, Di, N, W, R, f(hidden), f(20 * A_), f(21 * A_), 1e-5, f(W_x), f(3 * A_),
-                              f(22 * A_), None, f(4 * A_), f(5 * A_), f(6 * A_), f(7 * A_), f(23 * A_), f(24 * A_),
-                              f(Dskip), f(8 * A_), f(conv_state), f(h), f(ws), wsb, None)
+    return lib.ssm_block_step(B, Dm, Di, N, W, R, f(hidden), f(20 * A_), f(21 * A_), 1e-5, f(W_x), f(22 * A_), None,
+                              f(4 * A_), f(7 * A_), f(23 * A_), f(24 * A_), f(Dskip), f(8 * A_), f(conv_state), f(h),
+                              f(ws), wsb, None)
 
 
 @pytest.mark.parametrize("kw,expect", [

@@ -56,7 +56,7 @@ def _block_run(Bsz, Dm, Di, N, steps, seed):
     hid, reg, h = inputs.block_state(seed, Bsz, Dm, Di, N)
     dw = {k: gu.dev(v) for k, v in wts.items()}
     dh, dreg, dst = gu.dev(hid), gu.dev(reg), gu.dev(h)
-    wf = {k: (_bf(v) if v.dtype == np.uint16 else v.astype(np.float64)) for k, v in wts.items()}
+    wf = {k: (_bf(v) if v.dtype == np.uint16 else v.astype(np.float64)) for k, v in inputs.block_weights_split(wts).items()}
     rh, rreg, rst = _bf(hid), _bf(reg), h.astype(np.float64)
     g = np.random.default_rng(seed + 1)
     errs = []

@@ -105,84 +105,129 @@ __global__ __launch_bounds__(256) void layernorm_kernel(int64_t D, const bf16_t*
 }
 
 // ---------------------------------------------------------------------------- skinny GEMM
-// Y[m][n] = sum_k X[m][k] W[n][k] (+ R[m][n]) for M <= 128 token rows. grid (ceil(Nout / 32), S),
-// 256 threads. A workgroup owns 32 output columns and the K slice blockIdx.y of S; its four waves
-// take interleaved 32-wide K steps, each accumulating all MT row tiles x 2 column tiles computed
-// transposed (D[n][m]: A = W rows, B = X rows), so a lane ends with four consecutive outputs of
-// one row. The waves' sums meet in LDS in a fixed order; with S = 1 the workgroup applies the
-// epilogue (residual, bf16), otherwise it writes a float32 partial for the reduction kernel.
+// Y[m][n] = sum_k X[m][k] W[n][k] (+ R[m][n]) for M <= 128 token rows: every weight is read once
+// per step, so the kernel is built to keep enough weight bytes in flight.
+// grid (ceil(Nout / 64), row blocks, S), 256 threads. A workgroup owns 64 output columns (wave w
+// the 16-column tile w), the MT x 16 rows of its row block and the K slice blockIdx.z of S. The
+// row block's X slice goes through LDS in 64-wide K chunks (double-buffered, one barrier per
+// chunk) and is shared by the four waves; each wave streams its own W rows with PD chunks in
+// flight in a register ring (the loop is unrolled by PD so the ring is indexed statically). The
+// products are computed transposed (D[n][m]: A = W rows, B = X rows), so a lane ends with four
+// consecutive outputs of one row. With S = 1 the epilogue (residual, bf16) is applied in place;
+// otherwise a float32 partial goes to the reduction kernel. Splitting the rows into blocks
+// re-reads each weight tile once per block, from the cache when the blocks run side by side
+// (their workgroup ids are adjacent), so it is preferred to splitting K, whose partial sums cost
+// HBM traffic.
+constexpr int kGemmKC = 128;  // K chunk
+constexpr int kGemmXS = kGemmKC + 8;   // LDS row stride (bf16) of an X chunk
+constexpr int kGemmNW = 8;    // waves per workgroup: 16 output columns each
+
 template <int MT>
-__global__ __launch_bounds__(256) void gemm_xwt_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) float part[4][MT][2][64][4];
+__global__ __launch_bounds__(64 * kGemmNW) void gemm_xwt_kernel(GemmParams p) {
+  constexpr int kGemmPD = 2;   // W chunks in flight per wave (the loop is unrolled by this)
+  constexpr int NT = 64 * kGemmNW;
+  constexpr int ROWS = MT * 16;
+  constexpr int KS = kGemmKC / 32;                         // 32-wide steps per chunk
+  constexpr int XPIECES = ROWS * (kGemmKC / 8);            // 16-byte pieces of an X chunk
+  constexpr int XPER = (XPIECES + NT - 1) / NT;            // per thread
+  __shared__ __attribute__((aligned(16))) __bf16 xs[2][ROWS * kGemmXS];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t col0 = (int64_t)blockIdx.x * 32;
-  const int64_t ks = blockIdx.y;
+  const int64_t col0 = (int64_t)blockIdx.x * 16 * kGemmNW;
+  const int64_t m0 = (int64_t)blockIdx.y * ROWS;
+  const int64_t ks = blockIdx.z;
   const int64_t kbeg = ks * p.kslice;
+  const int64_t nchunks = p.kslice / kGemmKC;
   const bf16_t* W = static_cast<const bf16_t*>(p.w);
   const bf16_t* X = static_cast<const bf16_t*>(p.x);
 
-  f32x4 acc[MT][2];
+  // this wave's W rows (zero past Nout)
+  const int64_t nrow = col0 + w * 16 + r16;
+  const bool n_ok = nrow < p.Nout;
+  const bf16_t* wrow = W + (n_ok ? nrow : 0) * p.K + kbeg + 8 * g;
+  auto load_w = [&](int64_t c, bf16x8 out[KS]) __attribute__((always_inline)) {
+    const int64_t cc = c < nchunks ? c : nchunks - 1;   // past the end: a repeated, unused load
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt][0] = acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bool nrow_ok[2];
-  const bf16_t* wrow[2];
+    for (int s2 = 0; s2 < KS; ++s2)
+      out[s2] = n_ok ? *reinterpret_cast<const bf16x8*>(wrow + cc * kGemmKC + s2 * 32) : zero8();
+  };
+  // this thread's pieces of an X chunk: row e / (KC / 8), 8-element column group e % (KC / 8)
+  constexpr int PPR = kGemmKC / 8;
+  auto load_x = [&](int64_t c, uint4 out[XPER]) __attribute__((always_inline)) {
+    const int64_t cc = c < nchunks ? c : nchunks - 1;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int64_t n = col0 + nt * 16 + r16;
-    nrow_ok[nt] = n < p.Nout;
-    wrow[nt] = W + (nrow_ok[nt] ? n : 0) * p.K;
-  }
-  bool mrow_ok[MT];
-  const bf16_t* xrow[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int64_t m = mt * 16 + r16;
-    mrow_ok[mt] = m < p.M;
-    xrow[mt] = X + (mrow_ok[mt] ? m : 0) * p.ldx;
-  }
-  const int64_t nsteps = p.kslice / 128;   // K steps of each wave
-#pragma unroll 2
-  for (int64_t i = 0; i < nsteps; ++i) {
-    const int64_t k0 = kbeg + (w + 4 * i) * 32 + 8 * g;
-    bf16x8 wf[2], xf[MT];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) wf[nt] = nrow_ok[nt] ? *reinterpret_cast<const bf16x8*>(wrow[nt] + k0) : zero8();
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) xf[mt] = mrow_ok[mt] ? *reinterpret_cast<const bf16x8*>(xrow[mt] + k0) : zero8();
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma16(wf[nt], xf[mt], acc[mt][nt]);
-  }
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-      *reinterpret_cast<float4*>(&part[w][mt][nt][lane][0]) =
-          make_float4(acc[mt][nt][0], acc[mt][nt][1], acc[mt][nt][2], acc[mt][nt][3]);
-  __syncthreads();
-  // (row tile, column tile, lane) groups of four outputs: n = col0 + nt 16 + 4 (lane / 16) + r,
-  // m = mt 16 + lane % 16
-  for (int e = tid; e < MT * 2 * 64; e += 256) {
-    const int mt = e / 128, nt = (e / 64) & 1, ln = e & 63;
-    const int64_t m = mt * 16 + (ln & 15);
-    const int64_t n = col0 + nt * 16 + 4 * (ln >> 4);
-    if (m >= p.M || n >= p.Nout) continue;
-    float4 s = *reinterpret_cast<const float4*>(&part[0][mt][nt][ln][0]);
-#pragma unroll
-    for (int k = 1; k < 4; ++k) {
-      const float4 t = *reinterpret_cast<const float4*>(&part[k][mt][nt][ln][0]);
-      s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+    for (int k = 0; k < XPER; ++k) {
+      const int e = tid + NT * k;
+      const int64_t m = m0 + e / PPR;
+      out[k] = make_uint4(0, 0, 0, 0);
+      if (e < XPIECES && m < p.M)
+        out[k] = *reinterpret_cast<const uint4*>(X + m * p.ldx + kbeg + cc * kGemmKC + (e % PPR) * 8);
     }
-    if (p.S > 1) {
-      *reinterpret_cast<float4*>(p.partial + (ks * p.M + m) * p.Nout + n) = s;
-    } else {
-      if (p.residual) {
-        const uint2 rr = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(p.residual) + m * p.ldy + n);
-        s.x += bf16_lo(rr.x); s.y += bf16_hi(rr.x); s.z += bf16_lo(rr.y); s.w += bf16_hi(rr.y);
+  };
+  auto store_x = [&](int buf, const uint4 in[XPER]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < XPER; ++k) {
+      const int e = tid + NT * k;
+      if (e < XPIECES) *reinterpret_cast<uint4*>(&xs[buf][(e / PPR) * kGemmXS + (e % PPR) * 8]) = in[k];
+    }
+  };
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 wr[kGemmPD][KS];
+#pragma unroll
+  for (int k = 0; k < kGemmPD; ++k) load_w(k, wr[k]);
+  // X chunks two ahead in registers: xr[(c + 1) % 2] holds chunk c + 1 when chunk c is used
+  uint4 xr[2][XPER];
+  load_x(0, xr[0]);
+  store_x(0, xr[0]);
+  load_x(1, xr[1]);
+  load_x(2, xr[0]);
+  __syncthreads();
+
+  // chunk c: X from LDS buffer c % 2, W from ring slot c % PD (PD even, so slot parity = c parity)
+  auto step = [&](int64_t c, int slot) __attribute__((always_inline)) {
+    const int buf = (int)(c & 1);
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 xf = *reinterpret_cast<const bf16x8*>(&xs[buf][(mt * 16 + r16) * kGemmXS + s2 * 32 + 8 * g]);
+        acc[mt] = mfma16(wr[slot][s2], xf, acc[mt]);
       }
-      *reinterpret_cast<uint2*>(static_cast<bf16_t*>(p.y) + m * p.ldy + n) = pack4(s.x, s.y, s.z, s.w);
+    }
+    load_w(c + kGemmPD, wr[slot]);        // refill the slot just used
+    store_x(buf ^ 1, xr[(slot + 1) & 1]);  // chunk c + 1 (its buffer held chunk c - 1)
+    load_x(c + 3, xr[(slot + 1) & 1]);
+    __syncthreads();
+  };
+  int64_t c = 0;
+  for (; c + kGemmPD <= nchunks; c += kGemmPD) {
+#pragma unroll
+    for (int k = 0; k < kGemmPD; ++k) step(c + k, k);
+  }
+#pragma unroll
+  for (int k = 0; k < kGemmPD; ++k)
+    if (c + k < nchunks) step(c + k, k);
+
+  // epilogue: the lane holds n = col0 + w 16 + 4 g + r, m = m0 + mt 16 + r16
+  const int64_t n = col0 + w * 16 + 4 * g;
+  if (n < p.Nout) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int64_t m = m0 + mt * 16 + r16;
+      if (m >= p.M) continue;
+      float4 sv = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+      if (p.S > 1) {
+        *reinterpret_cast<float4*>(p.partial + (ks * p.M + m) * p.Nout + n) = sv;
+      } else {
+        if (p.residual) {
+          const uint2 rr = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(p.residual) + m * p.ldy + n);
+          sv.x += bf16_lo(rr.x); sv.y += bf16_hi(rr.x); sv.z += bf16_lo(rr.y); sv.w += bf16_hi(rr.y);
+        }
+        *reinterpret_cast<uint2*>(static_cast<bf16_t*>(p.y) + m * p.ldy + n) = pack4(sv.x, sv.y, sv.z, sv.w);
+      }
     }
   }
 }
@@ -237,30 +282,47 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(int64_t B, int64_t D, in
 
 }  // namespace
 
-// S (K splits) for a product: enough workgroups to fill the chip (about 512), each wave keeping
-// at least one 32-wide K step per split.
-int64_t gemm_splits(int64_t K, int64_t Nout) {
-  const int64_t tiles = (Nout + 31) / 32;
-  int64_t S = 1;
-  while (tiles * S < 512 && K % (S * 2 * 128) == 0) S *= 2;
-  return S;
+// Plan of a product: row tiles per workgroup (MT x 16 rows) and K splits S. About 256
+// workgroups fill the chip; rows are split first (down to two row tiles per workgroup), then K
+// (each split keeping whole 64-wide chunks).
+void gemm_plan(int64_t M, int64_t K, int64_t Nout, int* MT, int64_t* S) {
+  const int64_t tiles = (Nout + 16 * kGemmNW - 1) / (16 * kGemmNW);
+  int mt = 1;
+  while (mt * 16 < M) mt *= 2;        // 1, 2, 4, 8
+  int64_t blocks = (M + mt * 16 - 1) / (mt * 16), s = 1;
+  while (tiles * blocks * s < 256) {
+    if (mt > 2) {
+      mt /= 2;
+      blocks = (M + mt * 16 - 1) / (mt * 16);
+    } else if (K % (s * 2 * kGemmKC) == 0) {
+      s *= 2;
+    } else {
+      break;
+    }
+  }
+  *MT = mt;
+  *S = s;
 }
 
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t Nout) {
-  const int64_t S = gemm_splits(K, Nout);
+  int mt;
+  int64_t S;
+  gemm_plan(M, K, Nout, &mt, &S);
   return S > 1 ? (size_t)(S * M * Nout) * 4 : 0;
 }
 
 hipError_t launch_gemm(GemmParams p, hipStream_t stream) {
-  p.S = gemm_splits(p.K, p.Nout);
+  int mt;
+  gemm_plan(p.M, p.K, p.Nout, &mt, &p.S);
   p.kslice = p.K / p.S;
-  const dim3 grid((unsigned)((p.Nout + 31) / 32), (unsigned)p.S);
-  const int mt = (int)((p.M + 15) / 16);
+  const int64_t blocks = (p.M + mt * 16 - 1) / (mt * 16);
+  const dim3 grid((unsigned)((p.Nout + 16 * kGemmNW - 1) / (16 * kGemmNW)), (unsigned)blocks, (unsigned)p.S);
+  const dim3 block(64 * kGemmNW);
   switch (mt) {
-    case 1: hipLaunchKernelGGL(gemm_xwt_kernel<1>, grid, dim3(256), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(gemm_xwt_kernel<2>, grid, dim3(256), 0, stream, p); break;
-    case 3: case 4: hipLaunchKernelGGL(gemm_xwt_kernel<4>, grid, dim3(256), 0, stream, p); break;
-    default: hipLaunchKernelGGL(gemm_xwt_kernel<8>, grid, dim3(256), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL(gemm_xwt_kernel<1>, grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL(gemm_xwt_kernel<2>, grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL(gemm_xwt_kernel<4>, grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL(gemm_xwt_kernel<8>, grid, block, 0, stream, p); break;
   }
   if (p.S > 1) {
     const int64_t total = p.M * (p.Nout / 4);

@@ -171,7 +171,7 @@ struct SsdBwdParams {
 
 // Products of M <= 128 token rows with a weight matrix: Y[m][n] = sum_k X[m][k] W[n][k] (+ R).
 struct GemmParams {
-  int64_t M, K, Nout;      // K % 128 == 0, Nout % 4 == 0
+  int64_t M, K, Nout;      // K % 64 == 0, Nout % 4 == 0
   int64_t ldx, ldy;        // row strides (elements) of X and of Y / R
   int64_t S, kslice;       // K splits and their length (set by launch_gemm)
   const void* x;           // bf16 [M, ldx]
@@ -180,7 +180,7 @@ struct GemmParams {
   const void* residual;    // nullable bf16 [M, ldy]; may equal y
   float* partial;          // float [S, M, Nout] when S > 1
 };
-int64_t gemm_splits(int64_t K, int64_t Nout);
+void gemm_plan(int64_t M, int64_t K, int64_t Nout, int* MT, int64_t* S);
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t Nout);
 hipError_t launch_gemm(GemmParams p, hipStream_t stream);
 hipError_t launch_layernorm(int64_t M, int64_t D, const void* x, const float* w, const float* b, float eps, void* y,

@@ -226,9 +226,11 @@ def test_linear_rejects(lib, kw, expect):
 
 
 def test_linear_workspace(lib):
-    # enough column tiles: no split of K, no workspace; few tiles: float32 partial sums
+    # enough column tiles: no split of K, no workspace; few (2048 / 128 = 16 column tiles x 4 row
+    # blocks of 32): K split in 4, float32 partial sums
     assert lib.ssm_linear_workspace_bytes(77, 2048, 50288) == 0
-    assert lib.ssm_linear_workspace_bytes(128, 4096, 2048) == 8 * 128 * 2048 * 4
+    assert lib.ssm_linear_workspace_bytes(128, 2048, 8192) == 0
+    assert lib.ssm_linear_workspace_bytes(128, 4096, 2048) == 4 * 128 * 2048 * 4
 
 
 def test_layernorm_rejects(lib):

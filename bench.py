@@ -190,6 +190,8 @@ def main():
     ap.add_argument("--sets", type=int, default=3, help="rotating independent input sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-generation", action="store_true",
+                    help="leave the 48-block generation figure out of the secondary figures")
     ap.add_argument("--no-smi", action="store_true", help="skip the amd-smi clock/power sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 512 MiB device copy three times (counter calibration)")
@@ -284,7 +286,7 @@ def main():
         out["gpu_clocks_power"] = clocks
 
     if not args.no_secondary:
-        out["secondary"] = secondary(torch, np, inputs, ssm, dev)
+        out["secondary"] = secondary(torch, np, inputs, ssm, dev, generation_figure=not args.no_generation)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(host, np, inputs)
@@ -292,7 +294,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def secondary(torch, np, inputs, ssm, dev):
+def secondary(torch, np, inputs, ssm, dev, generation_figure=True):
     """Long-sequence scan, scan backward, prefill with the fused convolution, decode step and SSD
     layer: kernel-time throughput (HIP events)."""
     res = {}
@@ -449,7 +451,8 @@ def secondary(torch, np, inputs, ssm, dev):
         "workspace_MB": round(nbw / 1e6, 1)}
     del dy, wsb
 
-    res["generation_mamba_1.4b_b128"] = generation(torch, ssm, g)
+    if generation_figure:
+        res["generation_mamba_1.4b_b128"] = generation(torch, ssm, g)
     return res
 
 

@@ -44,31 +44,40 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
 // ---------------------------------------------------------------------------- LayerNorm
 // One workgroup (256 threads) per row of D <= 8192 bf16 values (D % 8 == 0): each thread keeps up
 // to four 8-element pieces in registers; mean, then variance of the centred values, both summed
-// in float32 through a fixed tree (deterministic).
+// in float32 through a fixed tree (deterministic). The row, w and b are all loaded before the
+// first sum (pieces past D read the last piece and are dropped: no branch around a load), so the
+// kernel pays one memory round trip.
 __global__ __launch_bounds__(256) void layernorm_kernel(int64_t D, const bf16_t* x, const float* w, const float* b,
                                                         float eps, bf16_t* y) {
   __shared__ float red[8];
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const bf16_t* xr = x + row * D;
+  uint4 xw[4];
+  float wt[4][8], bt[4][8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t c = std::min<int64_t>((int64_t)(tid + 256 * k) * 8, D - 8);
+    xw[k] = *reinterpret_cast<const uint4*>(xr + c);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      wt[k][q] = w[c + q];
+      bt[k][q] = b[c + q];
+    }
+  }
   float v[4][8];
   float s = 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int64_t c = (int64_t)(tid + 256 * k) * 8;
+    const bool in = (int64_t)(tid + 256 * k) * 8 < D;
+    const uint32_t wd[4] = {xw[k].x, xw[k].y, xw[k].z, xw[k].w};
 #pragma unroll
-    for (int q = 0; q < 8; ++q) v[k][q] = 0.f;
-    if (c < D) {
-      const uint4 u = *reinterpret_cast<const uint4*>(xr + c);
-      const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[k][2 * q] = bf16_lo(wd[q]);
-        v[k][2 * q + 1] = bf16_hi(wd[q]);
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) s += v[k][q];
+    for (int q = 0; q < 4; ++q) {
+      v[k][2 * q] = in ? bf16_lo(wd[q]) : 0.f;
+      v[k][2 * q + 1] = in ? bf16_hi(wd[q]) : 0.f;
     }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) s += v[k][q];
   }
   auto block_sum = [&](float t, int slot) {
 #pragma unroll
@@ -81,8 +90,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(int64_t D, const bf16_t*
   float s2 = 0.f;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int64_t c = (int64_t)(tid + 256 * k) * 8;
-    if (c < D) {
+    if ((int64_t)(tid + 256 * k) * 8 < D) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const float d = v[k][q] - mean;
@@ -97,7 +105,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(int64_t D, const bf16_t*
     if (c < D) {
       float o[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) o[q] = (v[k][q] - mean) * rstd * w[c + q] + b[c + q];
+      for (int q = 0; q < 8; ++q) o[q] = (v[k][q] - mean) * rstd * wt[k][q] + bt[k][q];
       const uint2 lo = pack4(o[0], o[1], o[2], o[3]), hi = pack4(o[4], o[5], o[6], o[7]);
       *reinterpret_cast<uint4*>(y + row * D + c) = make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
@@ -106,18 +114,17 @@ __global__ __launch_bounds__(256) void layernorm_kernel(int64_t D, const bf16_t*
 
 // ---------------------------------------------------------------------------- skinny GEMM
 // Y[m][n] = sum_k X[m][k] W[n][k] (+ R[m][n]) for M <= 128 token rows: every weight is read once
-// per step, so the kernel is built to keep enough weight bytes in flight.
-// grid (ceil(Nout / 64), row blocks, S), 256 threads. A workgroup owns 64 output columns (wave w
-// the 16-column tile w), the MT x 16 rows of its row block and the K slice blockIdx.z of S. The
-// row block's X slice goes through LDS in 64-wide K chunks (double-buffered, one barrier per
-// chunk) and is shared by the four waves; each wave streams its own W rows with PD chunks in
-// flight in a register ring (the loop is unrolled by PD so the ring is indexed statically). The
-// products are computed transposed (D[n][m]: A = W rows, B = X rows), so a lane ends with four
-// consecutive outputs of one row. With S = 1 the epilogue (residual, bf16) is applied in place;
-// otherwise a float32 partial goes to the reduction kernel. Splitting the rows into blocks
-// re-reads each weight tile once per block, from the cache when the blocks run side by side
-// (their workgroup ids are adjacent), so it is preferred to splitting K, whose partial sums cost
-// HBM traffic.
+// per step, so both kernels are built to keep enough weight bytes in flight. The products are
+// computed transposed (D[n][m]: A = W rows, B = X rows), so a lane ends with four consecutive
+// outputs of one row (one 8-byte store). With one K split the epilogue (residual, bf16) is applied
+// in place; otherwise float32 partials [S, M, Nout] go to gemm_reduce_kernel, which adds them in
+// split order.
+//
+// gemm_xwt_kernel (chunked): grid (ceil(Nout / 128), row blocks, S), 8 waves, wave w owns the
+// 16-column tile w. The row block's X slice goes through LDS in 128-wide K chunks (double-buffered,
+// one barrier per chunk, loaded two chunks ahead) and is shared by the waves; each wave streams
+// its own W rows two chunks ahead in a register ring (the loop is unrolled by 2 so the ring is
+// indexed statically). Used where the column tiles alone fill the GPU (the LM head).
 constexpr int kGemmKC = 128;  // K chunk
 constexpr int kGemmXS = kGemmKC + 8;   // LDS row stride (bf16) of an X chunk
 constexpr int kGemmNW = 8;    // waves per workgroup: 16 output columns each
@@ -232,8 +239,180 @@ __global__ __launch_bounds__(64 * kGemmNW) void gemm_xwt_kernel(GemmParams p) {
   }
 }
 
+// gemm_res_kernel (resident): grid (column blocks, S), 8 waves. A workgroup owns NC * CT * 16
+// output columns, every row (MT tiles) and the K slice blockIdx.y of length KR = KH * KW. Its X
+// slice is loaded into LDS once; wave w = (cg, kh) = (w % NC, w / NC) owns
+// CT column tiles of the column group cg and the KW-long part kh of the slice, and issues all of its
+// weight loads (CT * KW / 2 bytes per lane) right after the X loads, before the first product: the
+// workgroup's whole weight slice is in flight at once and no barrier interrupts the stream. Each X
+// fragment read from LDS feeds CT products. The KH part sums of each output fragment are added
+// through LDS in the order kh = 0, 1, ..., so the sum over K has a fixed order.
+template <int MT, int CT, int KH, int KW>
+struct ResShape {
+  static constexpr int NC = 8 / KH, KR = KH * KW, ROWS = MT * 16, XS = KR + 8, KSTEPS = KW / 32;
+  static constexpr int COLS = NC * CT * 16;
+  static constexpr int X_BYTES = ROWS * XS * 2;                      // row stride KR + 8: conflict-free reads
+  static constexpr int RED_BYTES = KH > 1 ? KH * NC * CT * MT * 64 * 16 : 0;
+  static constexpr int LDS = X_BYTES > RED_BYTES ? X_BYTES : RED_BYTES;
+};
+
+template <int MT, int CT, int KH, int KW>
+__global__ __launch_bounds__(512) void gemm_res_kernel(GemmParams p) {
+  using SH = ResShape<MT, CT, KH, KW>;
+  constexpr int NC = SH::NC, KR = SH::KR, ROWS = SH::ROWS, XS = SH::XS, KSTEPS = SH::KSTEPS;
+  static_assert(8 % KH == 0 && KW % 32 == 0 && CT * KW <= 512 && SH::LDS <= 160 * 1024, "resident GEMM shape");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[SH::LDS];
+  __bf16* xs = reinterpret_cast<__bf16*>(lds);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cg = w % NC, kh = w / NC;
+  const int64_t col0 = (int64_t)blockIdx.x * SH::COLS + cg * CT * 16;
+  const int64_t ks = blockIdx.y;
+  const int64_t kbeg = ks * KR;
+  const bf16_t* W = static_cast<const bf16_t*>(p.w);
+  const bf16_t* X = static_cast<const bf16_t*>(p.x);
+
+  // Every load is unconditional (a branch around a load makes the compiler wait for all loads in
+  // flight at the join): X rows past M read row M - 1 and W rows past Nout read row Nout - 1; they
+  // only feed outputs that are never stored. Threads past the last X piece repeat it.
+  // The X slice: 16-byte pieces, row e / (KR / 8), 8-element column group e % (KR / 8).
+  constexpr int PPR = KR / 8, XPIECES = ROWS * PPR, XPER = (XPIECES + 511) / 512;
+  uint4 xr[XPER];
+#pragma unroll
+  for (int k = 0; k < XPER; ++k) {
+    const int e = std::min(tid + 512 * k, XPIECES - 1);
+    const int64_t m = std::min<int64_t>(e / PPR, p.M - 1);
+    xr[k] = *reinterpret_cast<const uint4*>(X + m * p.ldx + kbeg + (e % PPR) * 8);
+  }
+  // this wave's weights: row n = col0 + 16 ct + r16, k = kh KW + 32 s + 8 g
+  bf16x8 wr[CT][KSTEPS];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int64_t n = std::min<int64_t>(col0 + ct * 16 + r16, p.Nout - 1);
+    const bf16_t* wrow = W + n * p.K + kbeg + kh * KW + 8 * g;
+#pragma unroll
+    for (int s2 = 0; s2 < KSTEPS; ++s2) wr[ct][s2] = *reinterpret_cast<const bf16x8*>(wrow + s2 * 32);
+  }
+#pragma unroll
+  for (int k = 0; k < XPER; ++k) {
+    const int e = std::min(tid + 512 * k, XPIECES - 1);
+    *reinterpret_cast<uint4*>(&xs[(e / PPR) * XS + (e % PPR) * 8]) = xr[k];
+  }
+  __syncthreads();
+
+  f32x4 acc[CT][MT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[ct][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s2 = 0; s2 < KSTEPS; ++s2) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const bf16x8 xf = *reinterpret_cast<const bf16x8*>(&xs[(mt * 16 + r16) * XS + kh * KW + s2 * 32 + 8 * g]);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) acc[ct][mt] = mfma16(wr[ct][s2], xf, acc[ct][mt]);
+    }
+  }
+
+  // epilogue for one 16 x 16 output fragment: the lane holds n = c0 + 4 g + r (r = 0..3), m = 16 mt + r16
+  auto store = [&](int64_t c0, int mt, f32x4 v) __attribute__((always_inline)) {
+    const int64_t n = c0 + 4 * g, m = mt * 16 + r16;
+    if (n >= p.Nout || m >= p.M) return;
+    float4 sv = make_float4(v[0], v[1], v[2], v[3]);
+    if (p.S > 1) {
+      *reinterpret_cast<float4*>(p.partial + (ks * p.M + m) * p.Nout + n) = sv;
+    } else {
+      if (p.residual) {
+        const uint2 rr = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(p.residual) + m * p.ldy + n);
+        sv.x += bf16_lo(rr.x); sv.y += bf16_hi(rr.x); sv.z += bf16_lo(rr.y); sv.w += bf16_hi(rr.y);
+      }
+      *reinterpret_cast<uint2*>(static_cast<bf16_t*>(p.y) + m * p.ldy + n) = pack4(sv.x, sv.y, sv.z, sv.w);
+    }
+  };
+  if constexpr (KH == 1) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) store(col0 + ct * 16, mt, acc[ct][mt]);
+  } else {
+    // every wave parks its part sums in LDS (the X slice is no longer read), then the NC * CT * MT
+    // fragments are shared out over the 8 waves, each adding the KH parts of its fragments in order
+    __syncthreads();
+    f32x4* red = reinterpret_cast<f32x4*>(lds);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) red[(((kh * NC + cg) * CT + ct) * MT + mt) * 64 + lane] = acc[ct][mt];
+    __syncthreads();
+    constexpr int F = NC * CT * MT;
+#pragma unroll 1
+    for (int f = w; f < F; f += 8) {
+      const int fcg = f / (CT * MT), fct = (f / MT) % CT, fmt = f % MT;
+      f32x4 v = red[((fcg * CT + fct) * MT + fmt) * 64 + lane];
+#pragma unroll
+      for (int part = 1; part < KH; ++part) v += red[(((part * NC + fcg) * CT + fct) * MT + fmt) * 64 + lane];
+      store((int64_t)blockIdx.x * SH::COLS + (fcg * CT + fct) * 16, fmt, v);
+    }
+  }
+}
+
 // Y = sum over the S partials in order (+ R), four outputs per thread. The partials are loaded
-// eight at a time before they are added, so a thread has several loads in flight.
+// eight at a time before they are added, so a thread has several loads in flight. With the conv
+// epilogue on, the four outputs of a thread below conv_D are four channels of the convolution
+// instead (conv_D is a multiple of 4, so a group never straddles it).
+// The conv + SiLU epilogue for channels n .. n + 3 of row m, given their product values v (the
+// same arithmetic as conv_silu_kernel: the new input is rounded to bf16 before it enters the
+// register and the sum).
+__device__ __forceinline__ void conv_silu4(const GemmParams& p, int64_t m, int64_t n, float4 v) {
+  const int64_t W = p.conv_W;
+  bf16_t* reg = static_cast<bf16_t*>(p.conv_state) + (m * p.conv_D + n) * W;
+  const float xv[4] = {v.x, v.y, v.z, v.w};
+  float uo[4];
+  if (W == 4) {
+    // 4 channels x 4 taps: 32 contiguous bytes of the register
+    const uint4 r0 = reinterpret_cast<const uint4*>(reg)[0], r1 = reinterpret_cast<const uint4*>(reg)[1];
+    const uint32_t wd[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    uint32_t out[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t xb = f32_to_bf16(xv[j]);
+      // taps oldest first: (lo, hi) of word 2j, then of word 2j + 1; shift by one and append x
+      const float t1 = bf16_hi(wd[2 * j]), t2 = bf16_lo(wd[2 * j + 1]), t3 = bf16_hi(wd[2 * j + 1]);
+      const float t4 = bf16_to_f32(xb);
+      const float* cw = p.conv_w + (n + j) * 4;
+      float acc = p.conv_b ? p.conv_b[n + j] : 0.f;
+      acc += cw[0] * t1;
+      acc += cw[1] * t2;
+      acc += cw[2] * t3;
+      acc += cw[3] * t4;
+      uo[j] = silu(acc);
+      out[2 * j] = (wd[2 * j] >> 16) | (wd[2 * j + 1] << 16);
+      out[2 * j + 1] = (wd[2 * j + 1] >> 16) | (xb << 16);
+    }
+    reinterpret_cast<uint4*>(reg)[0] = make_uint4(out[0], out[1], out[2], out[3]);
+    reinterpret_cast<uint4*>(reg)[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16_t* r = reg + j * W;
+      const float* cw = p.conv_w + (n + j) * W;
+      float acc = p.conv_b ? p.conv_b[n + j] : 0.f;
+      for (int64_t k = 0; k + 1 < W; ++k) {
+        const bf16_t t = r[k + 1];
+        r[k] = t;
+        acc += cw[k] * bf16_to_f32(t.bits);
+      }
+      bf16_t xb;
+      xb.bits = f32_to_bf16(xv[j]);
+      r[W - 1] = xb;
+      acc += cw[W - 1] * bf16_to_f32(xb.bits);
+      uo[j] = silu(acc);
+    }
+  }
+  *reinterpret_cast<uint2*>(static_cast<bf16_t*>(p.u) + m * p.conv_D + n) = pack4(uo[0], uo[1], uo[2], uo[3]);
+}
+
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmParams p) {
   const int64_t total = p.M * (p.Nout / 4);
   for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
@@ -250,6 +429,10 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmParams p) {
       for (int k = 0; k < 8; ++k) {
         s.x += t[k].x; s.y += t[k].y; s.z += t[k].z; s.w += t[k].w;
       }
+    }
+    if (p.conv_state && n < p.conv_D) {
+      conv_silu4(p, m, n, s);
+      continue;
     }
     if (p.residual) {
       const uint2 rr = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(p.residual) + m * p.ldy + n);
@@ -282,47 +465,87 @@ __global__ __launch_bounds__(256) void conv_silu_kernel(int64_t B, int64_t D, in
 
 }  // namespace
 
-// Plan of a product: row tiles per workgroup (MT x 16 rows) and K splits S. About 256
-// workgroups fill the chip; rows are split first (down to two row tiles per workgroup), then K
-// (each split keeping whole 64-wide chunks).
-void gemm_plan(int64_t M, int64_t K, int64_t Nout, int* MT, int64_t* S) {
-  const int64_t tiles = (Nout + 16 * kGemmNW - 1) / (16 * kGemmNW);
+// Configurations of gemm_res_kernel: (CT, KH, KW) -> NC * CT * 16 columns, a K slice of KH * KW.
+struct ResCfg {
+  int ct, kh, kw;
+};
+constexpr ResCfg kResCfgs[] = {{2, 2, 256}, {2, 4, 128}, {2, 8, 64}, {2, 4, 32}, {1, 4, 32}};
+
+static int row_tiles(int64_t M) {
   int mt = 1;
-  while (mt * 16 < M) mt *= 2;        // 1, 2, 4, 8
-  int64_t blocks = (M + mt * 16 - 1) / (mt * 16), s = 1;
-  while (tiles * blocks * s < 256) {
-    if (mt > 2) {
-      mt /= 2;
-      blocks = (M + mt * 16 - 1) / (mt * 16);
-    } else if (K % (s * 2 * kGemmKC) == 0) {
-      s *= 2;
-    } else {
-      break;
-    }
+  while (mt * 16 < M) mt *= 2;  // 1, 2, 4, 8
+  return mt;
+}
+
+// Plan of a product (M <= 128 rows, all in one row block). When the 128-column blocks alone
+// number 256 or more (the LM head), the chunked kernel streams the activations with no split of
+// K: split partials would cost as much traffic as the weights. Otherwise the resident kernel,
+// with K slices of 512 where K allows (else 128) and the widest column block whose grid still
+// reaches 256 workgroups (else the narrowest). Measured at 128 rows (kernel + reduction, weights
+// rotated through more than the last-level cache): 2048 -> 8192 20.7 us (chunked, rows in 4
+// blocks: 22.5), 4096 -> 2048 15.3 us (17.4), 4096 -> 160 8.6 us (10.1), 128 -> 4096 4.3 us
+// (4.7), 2048 -> 50288 chunked 74 us (resident with K in 4: 111).
+GemmChoice gemm_plan(int64_t M, int64_t K, int64_t Nout) {
+  const int mt = row_tiles(M);
+  // the column blocks alone fill the GPU: stream the activations, no split of K
+  if ((Nout + 16 * kGemmNW - 1) / (16 * kGemmNW) >= 256) return GemmChoice{0, mt, 0, 1};
+  const int order512[] = {0, 1, 2}, order128[] = {3, 4};
+  const bool k512 = K % 512 == 0;
+  const int* order = k512 ? order512 : order128;
+  const int n = k512 ? 3 : 2;
+  int i = 0;
+  for (; i < n - 1; ++i) {
+    const ResCfg& c = kResCfgs[order[i]];
+    const int64_t cols = (8 / c.kh) * c.ct * 16;
+    if ((Nout + cols - 1) / cols * (K / (c.kh * c.kw)) >= 256) break;
   }
-  *MT = mt;
-  *S = s;
+  const ResCfg& c = kResCfgs[order[i]];
+  return GemmChoice{1, mt, order[i], K / (c.kh * c.kw)};
 }
 
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t Nout) {
-  int mt;
-  int64_t S;
-  gemm_plan(M, K, Nout, &mt, &S);
-  return S > 1 ? (size_t)(S * M * Nout) * 4 : 0;
+  const GemmChoice c = gemm_plan(M, K, Nout);
+  return c.S > 1 ? (size_t)(c.S * M * Nout) * 4 : 0;
 }
 
-hipError_t launch_gemm(GemmParams p, hipStream_t stream) {
-  int mt;
-  gemm_plan(p.M, p.K, p.Nout, &mt, &p.S);
-  p.kslice = p.K / p.S;
-  const int64_t blocks = (p.M + mt * 16 - 1) / (mt * 16);
-  const dim3 grid((unsigned)((p.Nout + 16 * kGemmNW - 1) / (16 * kGemmNW)), (unsigned)blocks, (unsigned)p.S);
-  const dim3 block(64 * kGemmNW);
+template <int MT, int CT, int KH, int KW>
+static void launch_res(const GemmParams& p, hipStream_t stream) {
+  constexpr int COLS = ResShape<MT, CT, KH, KW>::COLS;
+  const dim3 grid((unsigned)((p.Nout + COLS - 1) / COLS), (unsigned)p.S);
+  hipLaunchKernelGGL((gemm_res_kernel<MT, CT, KH, KW>), grid, dim3(512), 0, stream, p);
+}
+
+template <int CT, int KH, int KW>
+static void launch_res_mt(const GemmParams& p, int mt, hipStream_t stream) {
   switch (mt) {
-    case 1: hipLaunchKernelGGL(gemm_xwt_kernel<1>, grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(gemm_xwt_kernel<2>, grid, block, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL(gemm_xwt_kernel<4>, grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL(gemm_xwt_kernel<8>, grid, block, 0, stream, p); break;
+    case 1: launch_res<1, CT, KH, KW>(p, stream); break;
+    case 2: launch_res<2, CT, KH, KW>(p, stream); break;
+    case 4: launch_res<4, CT, KH, KW>(p, stream); break;
+    default: launch_res<8, CT, KH, KW>(p, stream); break;
+  }
+}
+
+hipError_t launch_gemm_with(GemmParams p, const GemmChoice& c, hipStream_t stream) {
+  p.S = c.S;
+  p.kslice = p.K / p.S;
+  if (c.kind == 0) {
+    const int64_t blocks = (p.M + c.mt * 16 - 1) / (c.mt * 16);
+    const dim3 grid((unsigned)((p.Nout + 16 * kGemmNW - 1) / (16 * kGemmNW)), (unsigned)blocks, (unsigned)p.S);
+    const dim3 block(64 * kGemmNW);
+    switch (c.mt) {
+      case 1: hipLaunchKernelGGL(gemm_xwt_kernel<1>, grid, block, 0, stream, p); break;
+      case 2: hipLaunchKernelGGL(gemm_xwt_kernel<2>, grid, block, 0, stream, p); break;
+      case 4: hipLaunchKernelGGL(gemm_xwt_kernel<4>, grid, block, 0, stream, p); break;
+      default: hipLaunchKernelGGL(gemm_xwt_kernel<8>, grid, block, 0, stream, p); break;
+    }
+  } else {
+    switch (c.cfg) {
+      case 0: launch_res_mt<2, 2, 256>(p, c.mt, stream); break;
+      case 1: launch_res_mt<2, 4, 128>(p, c.mt, stream); break;
+      case 2: launch_res_mt<2, 8, 64>(p, c.mt, stream); break;
+      case 3: launch_res_mt<2, 4, 32>(p, c.mt, stream); break;
+      default: launch_res_mt<1, 4, 32>(p, c.mt, stream); break;
+    }
   }
   if (p.S > 1) {
     const int64_t total = p.M * (p.Nout / 4);
@@ -330,6 +553,10 @@ hipError_t launch_gemm(GemmParams p, hipStream_t stream) {
                        stream, p);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm(GemmParams p, hipStream_t stream) {
+  return launch_gemm_with(p, gemm_plan(p.M, p.K, p.Nout), stream);
 }
 
 hipError_t launch_layernorm(int64_t M, int64_t D, const void* x, const float* w, const float* b, float eps, void* y,
@@ -371,11 +598,24 @@ hipError_t launch_block_step(const BlockParams& bp, void* ws, hipStream_t st) {
     return launch_gemm(g, st);
   };
   hipError_t e = launch_layernorm(B, Dm, bp.hidden, bp.ln_w, bp.ln_b, bp.eps, xn, st);
-  if (e == hipSuccess) e = gemm(xn, Dm, Dm, bp.W_in, 2 * Di, xz, nullptr);          // [x | z]
+  // [x | z]; when K is split, the reduction applies conv + SiLU to the x half on its way out
   if (e == hipSuccess) {
-    hipLaunchKernelGGL(conv_silu_kernel, dim3((unsigned)((B * Di + 255) / 256)), dim3(256), 0, st, B, Di, bp.W,
-                       xz, 2 * Di, static_cast<bf16_t*>(bp.conv_state), bp.conv_w, bp.conv_b, u);
-    e = hipGetLastError();
+    GemmParams g{};
+    g.M = B; g.K = Dm; g.Nout = 2 * Di; g.x = xn; g.ldx = Dm; g.w = bp.W_in; g.y = xz; g.ldy = 2 * Di;
+    g.partial = partial;
+    const GemmChoice c = gemm_plan(B, Dm, 2 * Di);
+    if (c.S > 1) {
+      g.conv_state = bp.conv_state; g.conv_w = bp.conv_w; g.conv_b = bp.conv_b; g.u = u;
+      g.conv_D = Di; g.conv_W = bp.W;
+      e = launch_gemm_with(g, c, st);
+    } else {
+      e = launch_gemm_with(g, c, st);
+      if (e == hipSuccess) {
+        hipLaunchKernelGGL(conv_silu_kernel, dim3((unsigned)((B * Di + 255) / 256)), dim3(256), 0, st, B, Di, bp.W,
+                           xz, 2 * Di, static_cast<bf16_t*>(bp.conv_state), bp.conv_w, bp.conv_b, u);
+        e = hipGetLastError();
+      }
+    }
   }
   if (e == hipSuccess) e = gemm(u, Di, Di, bp.W_xp, XP, xp, nullptr);                // [Delta rank | B | C]
   if (e == hipSuccess) e = gemm(xp, XP, R, bp.W_dt, Di, dt, nullptr);                // rank part only

@@ -171,7 +171,7 @@ struct SsdBwdParams {
 
 // Products of M <= 128 token rows with a weight matrix: Y[m][n] = sum_k X[m][k] W[n][k] (+ R).
 struct GemmParams {
-  int64_t M, K, Nout;      // K % 64 == 0, Nout % 4 == 0
+  int64_t M, K, Nout;      // M <= 128, K % 128 == 0, Nout % 4 == 0
   int64_t ldx, ldy;        // row strides (elements) of X and of Y / R
   int64_t S, kslice;       // K splits and their length (set by launch_gemm)
   const void* x;           // bf16 [M, ldx]
@@ -179,10 +179,27 @@ struct GemmParams {
   void* y;                 // bf16 [M, ldy]
   const void* residual;    // nullable bf16 [M, ldy]; may equal y
   float* partial;          // float [S, M, Nout] when S > 1
+  // Optional conv + SiLU epilogue of the split-K reduction (gemm_reduce_kernel only) for the
+  // outputs n < conv_D: the register conv_state[m][n][0 .. conv_W - 1] (bf16) is shifted, the
+  // output (rounded to bf16) appended, and u[m][n] = SiLU(sum_k conv_w[n][k] reg[k] + conv_b[n])
+  // stored (row stride conv_D); the outputs n >= conv_D go to y as usual. conv_state NULL = off.
+  void* conv_state;
+  const float* conv_w;     // [conv_D, conv_W]
+  const float* conv_b;     // [conv_D] or NULL
+  void* u;                 // bf16 [M, conv_D]
+  int64_t conv_D, conv_W;
 };
-void gemm_plan(int64_t M, int64_t K, int64_t Nout, int* MT, int64_t* S);
+// How a product runs. kind 0: the activations stream through LDS in K chunks (gemm_xwt_kernel, MT
+// row tiles per row block, S splits of K). kind 1: the activation slice is resident in LDS
+// (gemm_res_kernel, all rows in MT tiles, configuration cfg of kResCfgs, S = K / its slice).
+struct GemmChoice {
+  int kind, mt, cfg;
+  int64_t S;
+};
+GemmChoice gemm_plan(int64_t M, int64_t K, int64_t Nout);
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t Nout);
 hipError_t launch_gemm(GemmParams p, hipStream_t stream);
+hipError_t launch_gemm_with(GemmParams p, const GemmChoice& c, hipStream_t stream);
 hipError_t launch_layernorm(int64_t M, int64_t D, const void* x, const float* w, const float* b, float eps, void* y,
                             hipStream_t stream);
 

@@ -226,11 +226,14 @@ def test_linear_rejects(lib, kw, expect):
 
 
 def test_linear_workspace(lib):
-    # enough column tiles: no split of K, no workspace; few (2048 / 128 = 16 column tiles x 4 row
-    # blocks of 32): K split in 4, float32 partial sums
+    # 393 column blocks of 128: no split of K, no workspace. Otherwise K slices of 512 (128 where
+    # K is not a multiple of 512), float32 partials per slice: 2048 -> 8192 in 4 slices, 4096 ->
+    # 2048 in 8, 128 -> 4096 in one (no workspace), 384 -> 20 in 3 slices of 128
     assert lib.ssm_linear_workspace_bytes(77, 2048, 50288) == 0
-    assert lib.ssm_linear_workspace_bytes(128, 2048, 8192) == 0
-    assert lib.ssm_linear_workspace_bytes(128, 4096, 2048) == 4 * 128 * 2048 * 4
+    assert lib.ssm_linear_workspace_bytes(128, 2048, 8192) == 4 * 128 * 8192 * 4
+    assert lib.ssm_linear_workspace_bytes(128, 4096, 2048) == 8 * 128 * 2048 * 4
+    assert lib.ssm_linear_workspace_bytes(128, 128, 4096) == 0
+    assert lib.ssm_linear_workspace_bytes(7, 384, 20) == 3 * 7 * 20 * 4
 
 
 def test_layernorm_rejects(lib):

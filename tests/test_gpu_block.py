@@ -18,8 +18,14 @@ def _bf(a):
     return inputs.widen(a, "bf16")
 
 
+# the plans these take: (1, 128, 4), (5, 256, 16), (128, 128, 4096) the resident kernel with
+# 32-column blocks and 128-long K slices (1, 2, 1 slices); (16, 2048, 4096) 64-column blocks, K in
+# 4; (100, 4096, 160) and (33, 1024, 1000) 32-column blocks, K in 8 and 2 (ragged rows, a ragged
+# column tile); (128, 4096, 2048) 64 columns, K in 8; (128, 2048, 8192) 128 columns, K in 4;
+# (77, 2048, 50288) the chunked kernel, no split
 @pytest.mark.parametrize("M,K,Nout", [(1, 128, 4), (5, 256, 16), (16, 2048, 4096), (100, 4096, 160),
-                                      (128, 4096, 2048), (128, 128, 4096), (77, 2048, 50288)])
+                                      (128, 4096, 2048), (128, 128, 4096), (77, 2048, 50288),
+                                      (128, 2048, 8192), (33, 1024, 1000)])
 def test_linear(M, K, Nout):
     g = np.random.default_rng(M + K + Nout)
     x = inputs.store(g.standard_normal((M, K)).astype(np.float32), "bf16")
@@ -51,9 +57,9 @@ def test_layernorm():
         assert gu.rel_err(y, oracle.layernorm(_bf(x), w, b)) <= gu.TOL["bf16"], (M, D)
 
 
-def _block_run(Bsz, Dm, Di, N, steps, seed):
-    wts = inputs.block_weights(seed, Dm, Di, N)
-    hid, reg, h = inputs.block_state(seed, Bsz, Dm, Di, N)
+def _block_run(Bsz, Dm, Di, N, steps, seed, W=4):
+    wts = inputs.block_weights(seed, Dm, Di, N, W=W)
+    hid, reg, h = inputs.block_state(seed, Bsz, Dm, Di, N, W=W)
     dw = {k: gu.dev(v) for k, v in wts.items()}
     dh, dreg, dst = gu.dev(hid), gu.dev(reg), gu.dev(h)
     wf = {k: (_bf(v) if v.dtype == np.uint16 else v.astype(np.float64)) for k, v in inputs.block_weights_split(wts).items()}
@@ -82,6 +88,16 @@ def test_block_step_small():
 @pytest.mark.parametrize("N", [4, 8])
 def test_block_step_state_sizes(N):
     errs = _block_run(Bsz=3, Dm=128, Di=256, N=N, steps=2, seed=71 + N)
+    assert max(max(e) for e in errs) <= gu.TOL["bf16"]
+
+
+@pytest.mark.parametrize("Dm,W", [(256, 3), (128, 2), (1024, 4)])
+def test_block_step_conv_widths(Dm, W):
+    """Where the input projection splits K (= d_model) its reduction applies conv + SiLU: d_model
+    256 (two 128-long slices) with register width 3 (the element path), d_model 1024 (two
+    512-long slices) with width 4 (the vector path); d_model 128 is not split and runs the
+    separate conv kernel, here with width 2."""
+    errs = _block_run(Bsz=6, Dm=Dm, Di=256, N=16, steps=3, seed=80 + W, W=W)
     assert max(max(e) for e in errs) <= gu.TOL["bf16"]
 
 

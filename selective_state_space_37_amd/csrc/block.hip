@@ -1,6 +1,9 @@
 // One decode token through a Mamba block, for the generation workload: LayerNorm, the input
 // projections, the short causal convolution with SiLU, the projections to Delta, B and C, the
-// selective state update (the decode kernel), the output projection and the residual.
+// selective state update, the output projection and the residual. Launches per block step:
+// LayerNorm; the input projection with conv + SiLU in its epilogue; the x projection + its
+// reduction; the Delta projection fused with the state update (block_ssm_kernel); the output
+// projection with the residual (+ its reduction).
 //
 // The block follows the pages as read for this workload: the pre-norm residual block with
 // LayerNorm of the code overview on "Beyond attention: exploring Mamba and state space models";
@@ -125,6 +128,58 @@ __global__ __launch_bounds__(256) void layernorm_kernel(int64_t D, const bf16_t*
 // one barrier per chunk, loaded two chunks ahead) and is shared by the waves; each wave streams
 // its own W rows two chunks ahead in a register ring (the loop is unrolled by 2 so the ring is
 // indexed statically). Used where the column tiles alone fill the GPU (the LM head).
+// The conv + SiLU epilogue for channels n .. n + 3 of row m, given their product values v: per
+// channel the register of the last W inputs (oldest first) is shifted, the new input (rounded to
+// bf16, the register's type) appended, and u = SiLU(sum_k w[k] reg[k] + bias), the newest input
+// multiplied by w[W - 1]. At width 4 the caller has loaded the 32 register bytes (r0, r1).
+__device__ __forceinline__ void conv_silu4(const GemmParams& p, int64_t m, int64_t n, float4 v, uint4 r0, uint4 r1) {
+  const int64_t W = p.conv_W;
+  bf16_t* reg = static_cast<bf16_t*>(p.conv_state) + (m * p.conv_D + n) * W;
+  const float xv[4] = {v.x, v.y, v.z, v.w};
+  float uo[4];
+  if (W == 4) {
+    // 4 channels x 4 taps: 32 contiguous bytes of the register
+    const uint32_t wd[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    uint32_t out[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t xb = f32_to_bf16(xv[j]);
+      // taps oldest first: (lo, hi) of word 2j, then of word 2j + 1; shift by one and append x
+      const float t1 = bf16_hi(wd[2 * j]), t2 = bf16_lo(wd[2 * j + 1]), t3 = bf16_hi(wd[2 * j + 1]);
+      const float t4 = bf16_to_f32(xb);
+      const float* cw = p.conv_w + (n + j) * 4;
+      float acc = p.conv_b ? p.conv_b[n + j] : 0.f;
+      acc += cw[0] * t1;
+      acc += cw[1] * t2;
+      acc += cw[2] * t3;
+      acc += cw[3] * t4;
+      uo[j] = silu(acc);
+      out[2 * j] = (wd[2 * j] >> 16) | (wd[2 * j + 1] << 16);
+      out[2 * j + 1] = (wd[2 * j + 1] >> 16) | (xb << 16);
+    }
+    reinterpret_cast<uint4*>(reg)[0] = make_uint4(out[0], out[1], out[2], out[3]);
+    reinterpret_cast<uint4*>(reg)[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16_t* r = reg + j * W;
+      const float* cw = p.conv_w + (n + j) * W;
+      float acc = p.conv_b ? p.conv_b[n + j] : 0.f;
+      for (int64_t k = 0; k + 1 < W; ++k) {
+        const bf16_t t = r[k + 1];
+        r[k] = t;
+        acc += cw[k] * bf16_to_f32(t.bits);
+      }
+      bf16_t xb;
+      xb.bits = f32_to_bf16(xv[j]);
+      r[W - 1] = xb;
+      acc += cw[W - 1] * bf16_to_f32(xb.bits);
+      uo[j] = silu(acc);
+    }
+  }
+  *reinterpret_cast<uint2*>(static_cast<bf16_t*>(p.u) + m * p.conv_D + n) = pack4(uo[0], uo[1], uo[2], uo[3]);
+}
+
 constexpr int kGemmKC = 128;  // K chunk
 constexpr int kGemmXS = kGemmKC + 8;   // LDS row stride (bf16) of an X chunk
 constexpr int kGemmNW = 8;    // waves per workgroup: 16 output columns each
@@ -179,6 +234,28 @@ __global__ __launch_bounds__(64 * kGemmNW) void gemm_xwt_kernel(GemmParams p) {
     }
   };
 
+  // conv epilogue (no split of K, width 4): the register words of this lane's outputs, loaded
+  // before the stream when the tile is small (a lane past conv_D or past M reads a valid
+  // stand-in and drops it), else in the epilogue
+  constexpr bool kRegEarly = MT <= 2;
+  const int64_t ne = col0 + w * 16 + 4 * g;
+  auto reg_words = [&](int mt, uint4& r0, uint4& r1) __attribute__((always_inline)) {
+    const int64_t me = std::min<int64_t>(m0 + mt * 16 + r16, p.M - 1);
+    const uint4* rp = reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(p.conv_state) +
+                                                     (me * p.conv_D + std::min<int64_t>(ne, p.conv_D - 4)) * 4);
+    r0 = rp[0];
+    r1 = rp[1];
+  };
+  uint4 rg[kRegEarly ? MT : 1][2];
+#pragma unroll
+  for (int mt = 0; mt < (kRegEarly ? MT : 1); ++mt) rg[mt][0] = rg[mt][1] = make_uint4(0, 0, 0, 0);
+  if constexpr (kRegEarly) {
+    if (p.conv_state && p.conv_W == 4) {   // uniform
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) reg_words(mt, rg[mt][0], rg[mt][1]);
+    }
+  }
+
   f32x4 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -228,6 +305,13 @@ __global__ __launch_bounds__(64 * kGemmNW) void gemm_xwt_kernel(GemmParams p) {
       float4 sv = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
       if (p.S > 1) {
         *reinterpret_cast<float4*>(p.partial + (ks * p.M + m) * p.Nout + n) = sv;
+      } else if (p.conv_state && n < p.conv_D) {
+        if constexpr (kRegEarly) {
+          conv_silu4(p, m, n, sv, rg[mt][0], rg[mt][1]);
+        } else {
+          if (p.conv_W == 4) reg_words(mt, rg[0][0], rg[0][1]);
+          conv_silu4(p, m, n, sv, rg[0][0], rg[0][1]);
+        }
       } else {
         if (p.residual) {
           const uint2 rr = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(p.residual) + m * p.ldy + n);
@@ -357,110 +441,133 @@ __global__ __launch_bounds__(512) void gemm_res_kernel(GemmParams p) {
   }
 }
 
-// Y = sum over the S partials in order (+ R), four outputs per thread. The partials are loaded
-// eight at a time before they are added, so a thread has several loads in flight. With the conv
-// epilogue on, the four outputs of a thread below conv_D are four channels of the convolution
-// instead (conv_D is a multiple of 4, so a group never straddles it).
-// The conv + SiLU epilogue for channels n .. n + 3 of row m, given their product values v (the
-// same arithmetic as conv_silu_kernel: the new input is rounded to bf16 before it enters the
-// register and the sum).
-__device__ __forceinline__ void conv_silu4(const GemmParams& p, int64_t m, int64_t n, float4 v) {
-  const int64_t W = p.conv_W;
-  bf16_t* reg = static_cast<bf16_t*>(p.conv_state) + (m * p.conv_D + n) * W;
-  const float xv[4] = {v.x, v.y, v.z, v.w};
-  float uo[4];
-  if (W == 4) {
-    // 4 channels x 4 taps: 32 contiguous bytes of the register
-    const uint4 r0 = reinterpret_cast<const uint4*>(reg)[0], r1 = reinterpret_cast<const uint4*>(reg)[1];
-    const uint32_t wd[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-    uint32_t out[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t xb = f32_to_bf16(xv[j]);
-      // taps oldest first: (lo, hi) of word 2j, then of word 2j + 1; shift by one and append x
-      const float t1 = bf16_hi(wd[2 * j]), t2 = bf16_lo(wd[2 * j + 1]), t3 = bf16_hi(wd[2 * j + 1]);
-      const float t4 = bf16_to_f32(xb);
-      const float* cw = p.conv_w + (n + j) * 4;
-      float acc = p.conv_b ? p.conv_b[n + j] : 0.f;
-      acc += cw[0] * t1;
-      acc += cw[1] * t2;
-      acc += cw[2] * t3;
-      acc += cw[3] * t4;
-      uo[j] = silu(acc);
-      out[2 * j] = (wd[2 * j] >> 16) | (wd[2 * j + 1] << 16);
-      out[2 * j + 1] = (wd[2 * j + 1] >> 16) | (xb << 16);
-    }
-    reinterpret_cast<uint4*>(reg)[0] = make_uint4(out[0], out[1], out[2], out[3]);
-    reinterpret_cast<uint4*>(reg)[1] = make_uint4(out[4], out[5], out[6], out[7]);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16_t* r = reg + j * W;
-      const float* cw = p.conv_w + (n + j) * W;
-      float acc = p.conv_b ? p.conv_b[n + j] : 0.f;
-      for (int64_t k = 0; k + 1 < W; ++k) {
-        const bf16_t t = r[k + 1];
-        r[k] = t;
-        acc += cw[k] * bf16_to_f32(t.bits);
-      }
-      bf16_t xb;
-      xb.bits = f32_to_bf16(xv[j]);
-      r[W - 1] = xb;
-      acc += cw[W - 1] * bf16_to_f32(xb.bits);
-      uo[j] = silu(acc);
-    }
-  }
-  *reinterpret_cast<uint2*>(static_cast<bf16_t*>(p.u) + m * p.conv_D + n) = pack4(uo[0], uo[1], uo[2], uo[3]);
-}
-
+// Y = sum over the S partials in order (+ R), four outputs per thread. A thread issues its
+// residual and eight partials before any arithmetic (without a residual it reads a valid
+// stand-in and drops it; partials past S are masked by value), so no load sits behind a branch.
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmParams p) {
   const int64_t total = p.M * (p.Nout / 4);
   for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
     const int64_t m = e / (p.Nout / 4), n = (e % (p.Nout / 4)) * 4;
     const float* src = p.partial + m * p.Nout + n;
     const int64_t stride = p.M * p.Nout;
+    const bf16_t* rsrc = p.residual ? static_cast<const bf16_t*>(p.residual) + m * p.ldy + n
+                                    : reinterpret_cast<const bf16_t*>(src);
+    const uint2 rr = *reinterpret_cast<const uint2*>(rsrc);
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int64_t k0 = 0; k0 < p.S; k0 += 8) {
       float4 t[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        t[k] = k0 + k < p.S ? *reinterpret_cast<const float4*>(src + (k0 + k) * stride) : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k = 0; k < 8; ++k) t[k] = *reinterpret_cast<const float4*>(src + std::min<int64_t>(k0 + k, p.S - 1) * stride);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        s.x += t[k].x; s.y += t[k].y; s.z += t[k].z; s.w += t[k].w;
+        const bool in = k0 + k < p.S;   // a select on the values, not a branch
+        s.x += in ? t[k].x : 0.f; s.y += in ? t[k].y : 0.f; s.z += in ? t[k].z : 0.f; s.w += in ? t[k].w : 0.f;
       }
     }
-    if (p.conv_state && n < p.conv_D) {
-      conv_silu4(p, m, n, s);
-      continue;
-    }
     if (p.residual) {
-      const uint2 rr = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(p.residual) + m * p.ldy + n);
       s.x += bf16_lo(rr.x); s.y += bf16_hi(rr.x); s.z += bf16_lo(rr.y); s.w += bf16_hi(rr.y);
     }
     *reinterpret_cast<uint2*>(static_cast<bf16_t*>(p.y) + m * p.ldy + n) = pack4(s.x, s.y, s.z, s.w);
   }
 }
 
-// ---------------------------------------------------------------------------- conv + SiLU
-// Per (b, d): shift the register of the last W raw inputs (oldest first), append x[b][d] (row
-// stride ldx), and u = SiLU(sum_k w[d][k] reg[k] + bias[d]); w[d][W-1] multiplies the newest input.
-__global__ __launch_bounds__(256) void conv_silu_kernel(int64_t B, int64_t D, int64_t W, const bf16_t* x, int64_t ldx,
-                                                        bf16_t* reg, const float* cw, const float* cb, bf16_t* u) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= B * D) return;
-  const int64_t d = e % D, b = e / D;
-  bf16_t* r = reg + e * W;
-  float acc = cb ? cb[d] : 0.f;
-  for (int64_t k = 0; k + 1 < W; ++k) {
-    const bf16_t v = r[k + 1];
-    r[k] = v;
-    acc += cw[d * W + k] * bf16_to_f32(v.bits);
+// ---------------------------------------------------------------------------- Delta + state update
+// The block's SSM step with the Delta projection folded in. Grid (Di / 16, ceil(B / 32)), 4 waves:
+// a workgroup owns channels d0 .. d0 + 15 and batch rows b0 .. b0 + 31. Thread (b_off, c, q)
+// owns states 4q .. 4q + 3 of channel d0 + c for the rows b0 + b_off + BPP j, j < U (for one row
+// the 16 channels' states are 16 N contiguous floats, covered by consecutive threads); it issues
+// all of its state, B, C, u and gate loads first. Then waves 0 and 1 compute the pre-activation
+// of Delta for the 16 channels and rows b0 + 16 w .. b0 + 16 w + 15 as one MFMA tile per 32-wide
+// step of the rank (A = rows of W_dt, B = rows of the rank slice of xp), add the bias, apply the
+// softplus and park Delta in LDS, so both memory round trips overlap. Rows past B repeat row
+// B - 1 and store nothing. The state update is the decode kernel's arithmetic.
+struct BlockSsmParams {
+  int64_t B, Di, R, XP, z_stride;
+  const bf16_t* u;      // [B, Di]
+  const bf16_t* xp;     // [B, XP]: Delta rank part [0, R), B [R, R + N), C [R + N, R + 2N)
+  const bf16_t* z;      // gate, row stride z_stride
+  const bf16_t* W_dt;   // [Di, R]
+  const float* b_dt;    // [Di]
+  const float* A;       // [Di, N]
+  const float* Dskip;   // [Di] or NULL
+  float* h;             // [B, Di, N], in place
+  bf16_t* y;            // [B, Di]
+};
+
+template <int N>
+__global__ __launch_bounds__(256) void block_ssm_kernel(BlockSsmParams p) {
+  constexpr int LPC = N / 4;          // lanes per channel, 4 states each
+  constexpr int BPP = 16 / LPC;       // batch rows per pass of the 256 threads
+  constexpr int U = 32 / BPP;         // passes per workgroup (32 rows)
+  constexpr int DS = 17;              // LDS row stride of Delta (floats)
+  __shared__ float dts[32 * DS];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const int64_t d0 = (int64_t)blockIdx.x * 16, b0 = (int64_t)blockIdx.y * 32;
+  const int q = tid % LPC, c = (tid / LPC) % 16, boff = tid / (16 * LPC);
+  const int64_t d = d0 + c;
+  const int n0 = 4 * q;
+
+  float4 hv[U];
+  uint2 bv[U], cv[U];
+  float uv[U], zv[U];
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    const int64_t b = std::min<int64_t>(b0 + boff + BPP * j, p.B - 1);
+    hv[j] = *reinterpret_cast<const float4*>(p.h + (b * p.Di + d) * N + n0);
+    bv[j] = *reinterpret_cast<const uint2*>(p.xp + b * p.XP + p.R + n0);
+    cv[j] = *reinterpret_cast<const uint2*>(p.xp + b * p.XP + p.R + N + n0);
+    uv[j] = bf16_to_f32(p.u[b * p.Di + d].bits);
+    zv[j] = bf16_to_f32(p.z[b * p.z_stride + d].bits);
   }
-  const bf16_t xn = x[b * ldx + d];
-  r[W - 1] = xn;
-  acc += cw[d * W + W - 1] * bf16_to_f32(xn.bits);
-  u[e].bits = f32_to_bf16(silu(acc));
+  const float4 Av = *reinterpret_cast<const float4*>(p.A + d * N + n0);
+  const float dsk = p.Dskip ? p.Dskip[d] : 0.f;
+
+  if (w < 2) {   // wave-uniform
+    const bf16_t* wrow = p.W_dt + (d0 + r16) * p.R + 8 * g;
+    const bf16_t* xrow = p.xp + std::min<int64_t>(b0 + 16 * w + r16, p.B - 1) * p.XP + 8 * g;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int64_t k = 0; k < p.R; k += 128) {
+      bf16x8 a[4], b[4];
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        a[s2] = *reinterpret_cast<const bf16x8*>(wrow + k + 32 * s2);
+        b[s2] = *reinterpret_cast<const bf16x8*>(xrow + k + 32 * s2);
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) acc = mfma16(a[s2], b[s2], acc);
+    }
+    // the lane holds channels 4 g .. 4 g + 3 of row b0 + 16 w + r16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dts[(16 * w + r16) * DS + 4 * g + i] = softplus_f32(acc[i] + p.b_dt[d0 + 4 * g + i]);
+  }
+  const float a2[4] = {Av.x * kLog2e, Av.y * kLog2e, Av.z * kLog2e, Av.w * kLog2e};
+  const float ia[4] = {1.0f / Av.x, 1.0f / Av.y, 1.0f / Av.z, 1.0f / Av.w};
+  __syncthreads();
+
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    const int64_t b = b0 + boff + BPP * j;
+    const bool live = b < p.B;
+    const float dt = dts[(boff + BPP * j) * DS + c];
+    const float Bq[4] = {bf16_lo(bv[j].x), bf16_hi(bv[j].x), bf16_lo(bv[j].y), bf16_hi(bv[j].y)};
+    const float Cq[4] = {bf16_lo(cv[j].x), bf16_hi(cv[j].x), bf16_lo(cv[j].y), bf16_hi(cv[j].y)};
+    float hq[4] = {hv[j].x, hv[j].y, hv[j].z, hv[j].w};
+    float yv = 0.f;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const float abar = exp2_fast(dt * a2[n]);
+      const float coef = fmaf(abar, ia[n], -ia[n]);
+      hq[n] = fmaf(abar, hq[n], coef * (Bq[n] * uv[j]));
+      yv = fmaf(Cq[n], hq[n], yv);
+    }
+    if (live) *reinterpret_cast<float4*>(p.h + (b * p.Di + d) * N + n0) = make_float4(hq[0], hq[1], hq[2], hq[3]);
+    yv = sum_channel_lanes<LPC>(yv);
+    if (q == 0 && live) {
+      yv = fmaf(dsk, uv[j], yv);
+      yv *= silu(zv[j]);
+      p.y[b * p.Di + d].bits = f32_to_bf16(yv);
+    }
+  }
 }
 
 }  // namespace
@@ -566,16 +673,16 @@ hipError_t launch_layernorm(int64_t M, int64_t D, const void* x, const float* w,
   return hipGetLastError();
 }
 
-// Workspace of one block step: xn [B, Dm], xz [B, 2 Di] (SSM branch and gate), u, dt, y [B, Di],
+// Workspace of one block step: xn [B, Dm], xz [B, 2 Di] (SSM branch and gate), u, y [B, Di],
 // xp [B, R + 2 N] (Delta rank part, B, C) (bf16, each 256-byte aligned) and the largest product's
 // partial sums.
 static size_t blk_align(size_t n) { return (n + 255) & ~(size_t)255; }
 
 size_t block_workspace_bytes(int64_t B, int64_t Dm, int64_t Di, int64_t N, int64_t R) {
-  const size_t acts = blk_align(B * Dm * 2) + blk_align(B * 2 * Di * 2) + 3 * blk_align(B * Di * 2) +
+  const size_t acts = blk_align(B * Dm * 2) + blk_align(B * 2 * Di * 2) + 2 * blk_align(B * Di * 2) +
                       blk_align(B * (R + 2 * N) * 2);
-  size_t part = 0;
-  const int64_t shapes[4][2] = {{Dm, 2 * Di}, {Di, R + 2 * N}, {R, Di}, {Di, Dm}};   // (K, Nout)
+  size_t part = 0;   // the input projection runs with K whole: no partials
+  const int64_t shapes[2][2] = {{Di, R + 2 * N}, {Di, Dm}};   // (K, Nout)
   for (auto& s : shapes) part = std::max(part, gemm_workspace_bytes(B, s[0], s[1]));
   return acts + blk_align(part);
 }
@@ -587,7 +694,6 @@ hipError_t launch_block_step(const BlockParams& bp, void* ws, hipStream_t st) {
   bf16_t* xn = static_cast<bf16_t*>(take(B * Dm * 2));
   bf16_t* xz = static_cast<bf16_t*>(take(B * 2 * Di * 2));
   bf16_t* u = static_cast<bf16_t*>(take(B * Di * 2));
-  bf16_t* dt = static_cast<bf16_t*>(take(B * Di * 2));
   bf16_t* y = static_cast<bf16_t*>(take(B * Di * 2));
   bf16_t* xp = static_cast<bf16_t*>(take(B * XP * 2));
   float* partial = reinterpret_cast<float*>(base);
@@ -598,36 +704,28 @@ hipError_t launch_block_step(const BlockParams& bp, void* ws, hipStream_t st) {
     return launch_gemm(g, st);
   };
   hipError_t e = launch_layernorm(B, Dm, bp.hidden, bp.ln_w, bp.ln_b, bp.eps, xn, st);
-  // [x | z]; when K is split, the reduction applies conv + SiLU to the x half on its way out
+  // [x | z] with conv + SiLU applied to the x half in the product's epilogue: the chunked kernel
+  // with K whole (rows in blocks of 32), so no partial sums and no further launch
   if (e == hipSuccess) {
     GemmParams g{};
     g.M = B; g.K = Dm; g.Nout = 2 * Di; g.x = xn; g.ldx = Dm; g.w = bp.W_in; g.y = xz; g.ldy = 2 * Di;
-    g.partial = partial;
-    const GemmChoice c = gemm_plan(B, Dm, 2 * Di);
-    if (c.S > 1) {
-      g.conv_state = bp.conv_state; g.conv_w = bp.conv_w; g.conv_b = bp.conv_b; g.u = u;
-      g.conv_D = Di; g.conv_W = bp.W;
-      e = launch_gemm_with(g, c, st);
-    } else {
-      e = launch_gemm_with(g, c, st);
-      if (e == hipSuccess) {
-        hipLaunchKernelGGL(conv_silu_kernel, dim3((unsigned)((B * Di + 255) / 256)), dim3(256), 0, st, B, Di, bp.W,
-                           xz, 2 * Di, static_cast<bf16_t*>(bp.conv_state), bp.conv_w, bp.conv_b, u);
-        e = hipGetLastError();
-      }
-    }
+    g.conv_state = bp.conv_state; g.conv_w = bp.conv_w; g.conv_b = bp.conv_b; g.u = u;
+    g.conv_D = Di; g.conv_W = bp.W;
+    e = launch_gemm_with(g, GemmChoice{0, std::min(row_tiles(B), 2), 0, 1}, st);
   }
   if (e == hipSuccess) e = gemm(u, Di, Di, bp.W_xp, XP, xp, nullptr);                // [Delta rank | B | C]
-  if (e == hipSuccess) e = gemm(xp, XP, R, bp.W_dt, Di, dt, nullptr);                // rank part only
   if (e == hipSuccess) {
-    StepParams sp{};
-    sp.B = B; sp.D = Di; sp.N = N; sp.W = 0; sp.io_bf16 = 1;
-    sp.x = u; sp.delta = dt; sp.z = xz + Di; sp.z_stride = 2 * Di;
-    sp.Bm = xp + R; sp.Cm = xp + R + N; sp.bc_stride = XP;
-    sp.delta_bias = bp.b_dt; sp.A = bp.A; sp.Dskip = bp.Dskip;
-    sp.conv_state = nullptr; sp.conv_w = nullptr; sp.conv_b = nullptr;
-    sp.h = bp.h; sp.y = y; sp.delta_softplus = 1;
-    e = launch_state_update(sp, st);
+    BlockSsmParams sp{};
+    sp.B = B; sp.Di = Di; sp.R = R; sp.XP = XP; sp.z_stride = 2 * Di;
+    sp.u = u; sp.xp = xp; sp.z = xz + Di; sp.W_dt = static_cast<const bf16_t*>(bp.W_dt); sp.b_dt = bp.b_dt;
+    sp.A = bp.A; sp.Dskip = bp.Dskip; sp.h = bp.h; sp.y = y;
+    const dim3 grid((unsigned)(Di / 16), (unsigned)((B + 31) / 32));
+    switch (N) {
+      case 4: hipLaunchKernelGGL(block_ssm_kernel<4>, grid, dim3(256), 0, st, sp); break;
+      case 8: hipLaunchKernelGGL(block_ssm_kernel<8>, grid, dim3(256), 0, st, sp); break;
+      default: hipLaunchKernelGGL(block_ssm_kernel<16>, grid, dim3(256), 0, st, sp); break;
+    }
+    e = hipGetLastError();
   }
   if (e == hipSuccess) e = gemm(y, Di, Di, bp.W_out, Dm, bp.hidden, bp.hidden);
   return e;

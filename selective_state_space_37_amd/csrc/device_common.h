@@ -175,4 +175,18 @@ __device__ __forceinline__ void buf_store(Rsrc r, uint32_t off, float v, bf16_t*
   __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, off, 0, 0);
 }
 
+// Sum over the LPC lanes of a channel (aligned groups of 1, 2 or 4 consecutive lanes).
+template <int LPC>
+__device__ __forceinline__ float sum_channel_lanes(float v) {
+  if constexpr (LPC >= 2) {
+    // quad_perm [1, 0, 3, 2]: swap neighbouring lanes
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  }
+  if constexpr (LPC >= 4) {
+    // quad_perm [2, 3, 0, 1]: swap lane pairs
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  }
+  return v;
+}
+
 }  // namespace ssm

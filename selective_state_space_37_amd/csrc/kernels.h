@@ -179,10 +179,10 @@ struct GemmParams {
   void* y;                 // bf16 [M, ldy]
   const void* residual;    // nullable bf16 [M, ldy]; may equal y
   float* partial;          // float [S, M, Nout] when S > 1
-  // Optional conv + SiLU epilogue of the split-K reduction (gemm_reduce_kernel only) for the
-  // outputs n < conv_D: the register conv_state[m][n][0 .. conv_W - 1] (bf16) is shifted, the
-  // output (rounded to bf16) appended, and u[m][n] = SiLU(sum_k conv_w[n][k] reg[k] + conv_b[n])
-  // stored (row stride conv_D); the outputs n >= conv_D go to y as usual. conv_state NULL = off.
+  // Optional conv + SiLU epilogue (gemm_xwt_kernel with K not split) for the outputs n < conv_D:
+  // the register conv_state[m][n][0 .. conv_W - 1] (bf16) is shifted, the output (rounded to
+  // bf16) appended, and u[m][n] = SiLU(sum_k conv_w[n][k] reg[k] + conv_b[n]) stored (row stride
+  // conv_D); the outputs n >= conv_D go to y as usual. conv_state NULL = off.
   void* conv_state;
   const float* conv_w;     // [conv_D, conv_W]
   const float* conv_b;     // [conv_D] or NULL

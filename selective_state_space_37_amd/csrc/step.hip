@@ -47,20 +47,6 @@ struct Vec {
   }
 };
 
-// Sum over the LPC lanes of a channel (aligned groups of 1, 2 or 4 consecutive lanes).
-template <int LPC>
-__device__ __forceinline__ float sum_channel_lanes(float v) {
-  if constexpr (LPC >= 2) {
-    // quad_perm [1, 0, 3, 2]: swap neighbouring lanes
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-  }
-  if constexpr (LPC >= 4) {
-    // quad_perm [2, 3, 0, 1]: swap lane pairs
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-  }
-  return v;
-}
-
 // CONV: 0 = no conv register, 4 = width 4 (vector loads), -1 = any width 1..8.
 // R: batch rows per thread. The thread handles channel d, state slice q of rows bq R .. bq R +
 // R - 1; the per-channel operands (A, conv weights, bias, D) are loaded once for the R rows.

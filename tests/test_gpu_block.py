@@ -93,10 +93,9 @@ def test_block_step_state_sizes(N):
 
 @pytest.mark.parametrize("Dm,W", [(256, 3), (128, 2), (1024, 4)])
 def test_block_step_conv_widths(Dm, W):
-    """Where the input projection splits K (= d_model) its reduction applies conv + SiLU: d_model
-    256 (two 128-long slices) with register width 3 (the element path), d_model 1024 (two
-    512-long slices) with width 4 (the vector path); d_model 128 is not split and runs the
-    separate conv kernel, here with width 2."""
+    """The input projection applies conv + SiLU to the SSM half in its epilogue: register widths
+    3 and 2 take the element path, width 4 the vector path (register words loaded before the
+    product), at d_model 256, 128 and 1024 (2, 1 and 8 K chunks)."""
     errs = _block_run(Bsz=6, Dm=Dm, Di=256, N=16, steps=3, seed=80 + W, W=W)
     assert max(max(e) for e in errs) <= gu.TOL["bf16"]
 

@@ -344,7 +344,8 @@ ssm_status ssm_layernorm(int64_t M, int64_t D, const void* x, const float* w, co
  *   W_xp       : [R + 2 N, d_inner] bf16 (Delta rank rows, B rows, C rows)   W_dt : [d_inner, R] bf16
  *   b_dt       : [d_inner] float32      A : [d_inner, N] float32 (< 0)   Dskip : [d_inner] or NULL
  *   W_out      : [d_model, d_inner] bf16
- *   Intermediate activations are bf16 in the workspace (ssm_block_step_workspace_bytes()).
+ *   Intermediate activations (xn, zi, u, [dl | Bt | Ct], y) are bf16 in the workspace
+ *   (ssm_block_step_workspace_bytes()); dt stays float32 from the product to the softplus.
  *   Requirements: 0 <= B <= 128 (0 is a no-op); d_model a multiple of 128 up to 8192; d_inner and
  *   R multiples of 128; N in {4, 8, 16}; 1 <= W <= 8; eps > 0; the in/out tensors overlap no
  *   weight, each other or the workspace; pointers of bf16 tensors, A, conv_state and h 16-byte

@@ -475,12 +475,13 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmParams p) {
 // The block's SSM step with the Delta projection folded in. Grid (Di / 16, ceil(B / 32)), 4 waves:
 // a workgroup owns channels d0 .. d0 + 15 and batch rows b0 .. b0 + 31. Thread (b_off, c, q)
 // owns states 4q .. 4q + 3 of channel d0 + c for the rows b0 + b_off + BPP j, j < U (for one row
-// the 16 channels' states are 16 N contiguous floats, covered by consecutive threads); it issues
-// all of its state, B, C, u and gate loads first. Then waves 0 and 1 compute the pre-activation
-// of Delta for the 16 channels and rows b0 + 16 w .. b0 + 16 w + 15 as one MFMA tile per 32-wide
-// step of the rank (A = rows of W_dt, B = rows of the rank slice of xp), add the bias, apply the
-// softplus and park Delta in LDS, so both memory round trips overlap. Rows past B repeat row
-// B - 1 and store nothing. The state update is the decode kernel's arithmetic.
+// the 16 channels' states are 16 N contiguous floats, covered by consecutive threads). Waves 0
+// and 1 compute the pre-activation of Delta for the 16 channels and rows b0 + 16 w .. b0 + 16 w +
+// 15 as one MFMA tile per 32-wide step of the rank (A = rows of W_dt, B = rows of the rank slice
+// of xp), add the bias, apply the softplus and park Delta in LDS. Every thread issues the Delta
+// operands (the first 128 of the rank) first, then all of its state, B, C, u and gate loads, so
+// the Delta products wait only for their own operands and overlap the state loads. Rows past B
+// repeat row B - 1 and store nothing. The state update is the decode kernel's arithmetic.
 struct BlockSsmParams {
   int64_t B, Di, R, XP, z_stride;
   const bf16_t* u;      // [B, Di]
@@ -507,6 +508,19 @@ __global__ __launch_bounds__(256) void block_ssm_kernel(BlockSsmParams p) {
   const int64_t d = d0 + c;
   const int n0 = 4 * q;
 
+  // the first 128 of the rank for the Delta tile, issued before the state loads so that the
+  // Delta products wait only for these (loads complete in issue order); every wave loads them
+  // (waves 2 and 3 for the tiles of waves 0 and 1) so the loads sit behind no branch
+  const int dw = w & 1;
+  const bf16_t* wrow = p.W_dt + (d0 + r16) * p.R + 8 * g;
+  const bf16_t* xrow = p.xp + std::min<int64_t>(b0 + 16 * dw + r16, p.B - 1) * p.XP + 8 * g;
+  bf16x8 da[4], db[4];
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2) {
+    da[s2] = *reinterpret_cast<const bf16x8*>(wrow + 32 * s2);
+    db[s2] = *reinterpret_cast<const bf16x8*>(xrow + 32 * s2);
+  }
+
   float4 hv[U];
   uint2 bv[U], cv[U];
   float uv[U], zv[U];
@@ -523,10 +537,10 @@ __global__ __launch_bounds__(256) void block_ssm_kernel(BlockSsmParams p) {
   const float dsk = p.Dskip ? p.Dskip[d] : 0.f;
 
   if (w < 2) {   // wave-uniform
-    const bf16_t* wrow = p.W_dt + (d0 + r16) * p.R + 8 * g;
-    const bf16_t* xrow = p.xp + std::min<int64_t>(b0 + 16 * w + r16, p.B - 1) * p.XP + 8 * g;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int64_t k = 0; k < p.R; k += 128) {
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) acc = mfma16(da[s2], db[s2], acc);
+    for (int64_t k = 128; k < p.R; k += 128) {   // ranks past 128
       bf16x8 a[4], b[4];
 #pragma unroll
       for (int s2 = 0; s2 < 4; ++s2) {

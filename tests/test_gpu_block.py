@@ -91,6 +91,14 @@ def test_block_step_state_sizes(N):
     assert max(max(e) for e in errs) <= gu.TOL["bf16"]
 
 
+@pytest.mark.parametrize("N", [4, 8, 16])
+def test_block_step_two_row_blocks(N):
+    """40 sequences: the fused Delta + state-update kernel runs two blocks of 32 batch rows, the
+    second ragged (8 live rows), at every state size (1, 2 and 4 lanes per channel)."""
+    errs = _block_run(Bsz=40, Dm=256, Di=256, N=N, steps=2, seed=90 + N)
+    assert max(max(e) for e in errs) <= gu.TOL["bf16"]
+
+
 @pytest.mark.parametrize("Dm,W", [(256, 3), (128, 2), (1024, 4)])
 def test_block_step_conv_widths(Dm, W):
     """The input projection applies conv + SiLU to the SSM half in its epilogue: register widths

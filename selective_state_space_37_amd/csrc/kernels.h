@@ -108,8 +108,6 @@ struct StepParams {
   float* h;
   void* y;
   int delta_softplus;
-  int64_t bc_stride;       // row stride (elements) of Bm and Cm; 0: N
-  int64_t z_stride;        // row stride of z; 0: D
 };
 
 hipError_t launch_state_update(const StepParams& p, hipStream_t stream);

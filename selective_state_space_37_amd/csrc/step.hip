@@ -90,8 +90,6 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
   const io_t* xg = static_cast<const io_t*>(p.x);
   const io_t* dg = static_cast<const io_t*>(p.delta);
   const io_t* zg = static_cast<const io_t*>(p.z);
-  const int64_t bcs = p.bc_stride ? p.bc_stride : N;   // row strides of B, C and z
-  const int64_t zs = p.z_stride ? p.z_stride : p.D;
   // optional tensors are read through a valid stand-in address when absent and the value is
   // dropped afterwards: no branch around a load, so no wait is forced before the join
   const float* fstand = p.A;   // any float array with at least D entries
@@ -110,12 +108,12 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
   for (int r = 0; r < R; ++r) {
     x_bits[r] = Io::load_bits(xg, ch[r]);
     d_bits[r] = Io::load_bits(dg, ch[r]);
-    z_bits[r] = zg ? Io::load_bits(zg, brow[r] * zs + d) : Io::load_bits(xg, ch[r]);
+    z_bits[r] = Io::load_bits(zg ? zg : xg, ch[r]);
     creg[r] = Io::zero4();
     if constexpr (CONV == 4) creg[r] = Io::load4_raw(static_cast<const io_t*>(p.conv_state) + ch[r] * 4, 0);
     Vec<SPL>::load(p.h + ch[r] * N + n0, h[r]);
-    const io_t* Bg = static_cast<const io_t*>(p.Bm) + brow[r] * bcs + n0;
-    const io_t* Cg = static_cast<const io_t*>(p.Cm) + brow[r] * bcs + n0;
+    const io_t* Bg = static_cast<const io_t*>(p.Bm) + brow[r] * N + n0;
+    const io_t* Cg = static_cast<const io_t*>(p.Cm) + brow[r] * N + n0;
     if constexpr (SPL == 4) {
       const raw4 br = Io::load4_raw(Bg, 0), cr = Io::load4_raw(Cg, 0);
       Io::unpack4(br, Bv[r]);

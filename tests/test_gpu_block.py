@@ -22,10 +22,11 @@ def _bf(a):
 # 32-column blocks and 128-long K slices (1, 2, 1 slices); (16, 2048, 4096) 64-column blocks, K in
 # 4; (100, 4096, 160) and (33, 1024, 1000) 32-column blocks, K in 8 and 2 (ragged rows, a ragged
 # column tile); (128, 4096, 2048) 64 columns, K in 8; (128, 2048, 8192) 128 columns, K in 4;
-# (77, 2048, 50288) the chunked kernel, no split
+# (77, 2048, 50288) the chunked kernel, no split; (64, 384, 8192) 64-column blocks with 128-long
+# K slices, an odd number of them (3)
 @pytest.mark.parametrize("M,K,Nout", [(1, 128, 4), (5, 256, 16), (16, 2048, 4096), (100, 4096, 160),
                                       (128, 4096, 2048), (128, 128, 4096), (77, 2048, 50288),
-                                      (128, 2048, 8192), (33, 1024, 1000)])
+                                      (128, 2048, 8192), (33, 1024, 1000), (64, 384, 8192)])
 def test_linear(M, K, Nout):
     g = np.random.default_rng(M + K + Nout)
     x = inputs.store(g.standard_normal((M, K)).astype(np.float32), "bf16")

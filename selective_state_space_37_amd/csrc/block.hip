@@ -1,9 +1,9 @@
 // One decode token through a Mamba block, for the generation workload: LayerNorm, the input
 // projections, the short causal convolution with SiLU, the projections to Delta, B and C, the
 // selective state update, the output projection and the residual. Launches per block step:
-// LayerNorm; the input projection with conv + SiLU in its epilogue; the x projection + its
-// reduction; the Delta projection fused with the state update (block_ssm_kernel); the output
-// projection with the residual (+ its reduction).
+// LayerNorm; the input projection with conv + SiLU and the x projection's per-slice partials in
+// its epilogue; their reduction; the Delta projection fused with the state update
+// (block_ssm_kernel); the output projection with the residual (+ its reduction).
 //
 // The block follows the pages as read for this workload: the pre-norm residual block with
 // LayerNorm of the code overview on "Beyond attention: exploring Mamba and state space models";
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(int64_t D, const bf16_t*
 // channel the register of the last W inputs (oldest first) is shifted, the new input (rounded to
 // bf16, the register's type) appended, and u = SiLU(sum_k w[k] reg[k] + bias), the newest input
 // multiplied by w[W - 1]. At width 4 the caller has loaded the 32 register bytes (r0, r1).
-__device__ __forceinline__ void conv_silu4(const GemmParams& p, int64_t m, int64_t n, float4 v, uint4 r0, uint4 r1) {
+__device__ __forceinline__ float4 conv_silu4(const GemmParams& p, int64_t m, int64_t n, float4 v, uint4 r0, uint4 r1) {
   const int64_t W = p.conv_W;
   bf16_t* reg = static_cast<bf16_t*>(p.conv_state) + (m * p.conv_D + n) * W;
   const float xv[4] = {v.x, v.y, v.z, v.w};
@@ -178,6 +178,7 @@ __device__ __forceinline__ void conv_silu4(const GemmParams& p, int64_t m, int64
     }
   }
   *reinterpret_cast<uint2*>(static_cast<bf16_t*>(p.u) + m * p.conv_D + n) = pack4(uo[0], uo[1], uo[2], uo[3]);
+  return make_float4(uo[0], uo[1], uo[2], uo[3]);
 }
 
 constexpr int kGemmKC = 128;  // K chunk
@@ -295,7 +296,13 @@ __global__ __launch_bounds__(64 * kGemmNW) void gemm_xwt_kernel(GemmParams p) {
   for (int k = 0; k < kGemmPD; ++k)
     if (c + k < nchunks) step(c + k, k);
 
-  // epilogue: the lane holds n = col0 + w 16 + 4 g + r, m = m0 + mt 16 + r16
+  // epilogue: the lane holds n = col0 + w 16 + 4 g + r, m = m0 + mt 16 + r16. With the
+  // x-projection epilogue the u values of this workgroup (all in the conv range, as conv_D is a
+  // multiple of 128) are also parked in LDS as a [ROWS][kGemmXS] bf16 tile (the X buffers are free
+  // after the last chunk's barrier); rows past M are left as they are and only feed rows that are
+  // never stored.
+  const bool xp_on = MT <= 2 && p.xp_w && p.conv_state && p.S == 1 && col0 < p.conv_D;   // per workgroup
+  __bf16* ut = &xs[0][0];
   const int64_t n = col0 + w * 16 + 4 * g;
   if (n < p.Nout) {
 #pragma unroll
@@ -306,18 +313,50 @@ __global__ __launch_bounds__(64 * kGemmNW) void gemm_xwt_kernel(GemmParams p) {
       if (p.S > 1) {
         *reinterpret_cast<float4*>(p.partial + (ks * p.M + m) * p.Nout + n) = sv;
       } else if (p.conv_state && n < p.conv_D) {
+        float4 uv;
         if constexpr (kRegEarly) {
-          conv_silu4(p, m, n, sv, rg[mt][0], rg[mt][1]);
+          uv = conv_silu4(p, m, n, sv, rg[mt][0], rg[mt][1]);
         } else {
           if (p.conv_W == 4) reg_words(mt, rg[0][0], rg[0][1]);
-          conv_silu4(p, m, n, sv, rg[0][0], rg[0][1]);
+          uv = conv_silu4(p, m, n, sv, rg[0][0], rg[0][1]);
         }
+        if (xp_on)
+          *reinterpret_cast<uint2*>(&ut[(mt * 16 + r16) * kGemmXS + w * 16 + 4 * g]) = pack4(uv.x, uv.y, uv.z, uv.w);
       } else {
         if (p.residual) {
           const uint2 rr = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(p.residual) + m * p.ldy + n);
           sv.x += bf16_lo(rr.x); sv.y += bf16_hi(rr.x); sv.z += bf16_lo(rr.y); sv.w += bf16_hi(rr.y);
         }
         *reinterpret_cast<uint2*>(static_cast<bf16_t*>(p.y) + m * p.ldy + n) = pack4(sv.x, sv.y, sv.z, sv.w);
+      }
+    }
+  }
+
+  // x-projection partial of this 128-channel slice: D[r][m] = sum_k W_xp[r][col0 + k] u[m][k]
+  // (A = W_xp rows, rows past xp_n repeat the last; B = u rows from LDS), wave w taking the
+  // output fragments w, w + 8, ... of the (xp_n / 16) x MT grid
+  if constexpr (MT <= 2) {
+    if (xp_on) {   // uniform per workgroup
+      __syncthreads();
+      const int64_t slice = col0 / 128;
+      const bf16_t* Wx = static_cast<const bf16_t*>(p.xp_w);
+      const int RT = (int)((p.xp_n + 15) / 16);
+      for (int f = w; f < RT * MT; f += 8) {
+        const int rt = f / MT, mt = f % MT;
+        const bf16_t* wxr = Wx + std::min<int64_t>(16 * rt + r16, p.xp_n - 1) * p.conv_D + col0 + 8 * g;
+        bf16x8 a[4], b[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          a[s2] = *reinterpret_cast<const bf16x8*>(wxr + 32 * s2);
+          b[s2] = *reinterpret_cast<const bf16x8*>(&ut[(mt * 16 + r16) * kGemmXS + 32 * s2 + 8 * g]);
+        }
+        f32x4 acc4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) acc4 = mfma16(a[s2], b[s2], acc4);
+        const int64_t ro = 16 * rt + 4 * g, m = m0 + mt * 16 + r16;
+        if (ro < p.xp_n && m < p.M)
+          *reinterpret_cast<float4*>(p.xp_partial + (slice * p.M + m) * p.xp_n + ro) =
+              make_float4(acc4[0], acc4[1], acc4[2], acc4[3]);
       }
     }
   }
@@ -695,9 +734,10 @@ static size_t blk_align(size_t n) { return (n + 255) & ~(size_t)255; }
 size_t block_workspace_bytes(int64_t B, int64_t Dm, int64_t Di, int64_t N, int64_t R) {
   const size_t acts = blk_align(B * Dm * 2) + blk_align(B * 2 * Di * 2) + 2 * blk_align(B * Di * 2) +
                       blk_align(B * (R + 2 * N) * 2);
-  size_t part = 0;   // the input projection runs with K whole: no partials
-  const int64_t shapes[2][2] = {{Di, R + 2 * N}, {Di, Dm}};   // (K, Nout)
-  for (auto& s : shapes) part = std::max(part, gemm_workspace_bytes(B, s[0], s[1]));
+  // the input projection runs with K whole; its x-projection epilogue leaves one partial per
+  // 128-channel slice; the output projection splits K
+  size_t part = (size_t)(Di / 128) * B * (R + 2 * N) * 4;
+  part = std::max(part, gemm_workspace_bytes(B, Di, Dm));
   return acts + blk_align(part);
 }
 
@@ -718,16 +758,25 @@ hipError_t launch_block_step(const BlockParams& bp, void* ws, hipStream_t st) {
     return launch_gemm(g, st);
   };
   hipError_t e = launch_layernorm(B, Dm, bp.hidden, bp.ln_w, bp.ln_b, bp.eps, xn, st);
-  // [x | z] with conv + SiLU applied to the x half in the product's epilogue: the chunked kernel
-  // with K whole (rows in blocks of 32), so no partial sums and no further launch
+  // [x | z] with conv + SiLU applied to the x half in the product's epilogue (the chunked kernel
+  // with K whole, rows in blocks of 32), which also multiplies each 128-channel slice of u by the
+  // matching columns of W_xp
   if (e == hipSuccess) {
     GemmParams g{};
     g.M = B; g.K = Dm; g.Nout = 2 * Di; g.x = xn; g.ldx = Dm; g.w = bp.W_in; g.y = xz; g.ldy = 2 * Di;
     g.conv_state = bp.conv_state; g.conv_w = bp.conv_w; g.conv_b = bp.conv_b; g.u = u;
     g.conv_D = Di; g.conv_W = bp.W;
+    g.xp_w = bp.W_xp; g.xp_n = XP; g.xp_partial = partial;   // [Delta rank | B | C] per 128-channel slice
     e = launch_gemm_with(g, GemmChoice{0, std::min(row_tiles(B), 2), 0, 1}, st);
   }
-  if (e == hipSuccess) e = gemm(u, Di, Di, bp.W_xp, XP, xp, nullptr);                // [Delta rank | B | C]
+  if (e == hipSuccess) {   // xp = the sum of the Di / 128 slice partials
+    GemmParams r{};
+    r.M = B; r.Nout = XP; r.S = Di / 128; r.partial = partial; r.y = xp; r.ldy = XP;
+    const int64_t total = B * (XP / 4);
+    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)std::min<int64_t>((total + 255) / 256, 4096)), dim3(256), 0,
+                       st, r);
+    e = hipGetLastError();
+  }
   if (e == hipSuccess) {
     BlockSsmParams sp{};
     sp.B = B; sp.Di = Di; sp.R = R; sp.XP = XP; sp.z_stride = 2 * Di;

@@ -186,6 +186,13 @@ struct GemmParams {
   const float* conv_b;     // [conv_D] or NULL
   void* u;                 // bf16 [M, conv_D]
   int64_t conv_D, conv_W;
+  // Optional x-projection epilogue (gemm_xwt_kernel with the conv epilogue, up to 2 row tiles):
+  // each workgroup of the conv range multiplies its u tile (its rows x 128 channels) by the
+  // matching 128 columns of xp_w [xp_n, conv_D] and stores float32 partials
+  // xp_partial[conv_D / 128][M][xp_n], one per 128-channel slice, for gemm_reduce_kernel.
+  const void* xp_w;
+  int64_t xp_n;
+  float* xp_partial;
 };
 // How a product runs. kind 0: the activations stream through LDS in K chunks (gemm_xwt_kernel, MT
 // row tiles per row block, S splits of K). kind 1: the activation slice is resident in LDS

@@ -256,6 +256,24 @@ __global__ __launch_bounds__(64 * kGemmNW) void gemm_xwt_kernel(GemmParams p) {
       for (int mt = 0; mt < MT; ++mt) reg_words(mt, rg[mt][0], rg[mt][1]);
     }
   }
+  // x-projection epilogue: this wave's W_xp fragments (output fragments w + 8 i, i < kXpF, of the
+  // (xp_n / 16) x MT grid), loaded before the stream as well (rows past xp_n repeat the last)
+  constexpr int kXpF = MT <= 2 ? 3 : 1;
+  const bool xp_on = MT <= 2 && p.xp_w && p.conv_state && p.S == 1 && col0 < p.conv_D;   // per workgroup
+  const int xp_rt = (int)((p.xp_n + 15) / 16);
+  bf16x8 xpa[kXpF][4];
+  if constexpr (MT <= 2) {
+    if (xp_on) {   // uniform
+#pragma unroll
+      for (int i = 0; i < kXpF; ++i) {
+        const int f = std::min(w + 8 * i, xp_rt * MT - 1);
+        const bf16_t* wxr = static_cast<const bf16_t*>(p.xp_w) +
+                            std::min<int64_t>(16 * (f / MT) + r16, p.xp_n - 1) * p.conv_D + col0 + 8 * g;
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) xpa[i][s2] = *reinterpret_cast<const bf16x8*>(wxr + 32 * s2);
+      }
+    }
+  }
 
   f32x4 acc[MT];
 #pragma unroll
@@ -301,7 +319,6 @@ __global__ __launch_bounds__(64 * kGemmNW) void gemm_xwt_kernel(GemmParams p) {
   // multiple of 128) are also parked in LDS as a [ROWS][kGemmXS] bf16 tile (the X buffers are free
   // after the last chunk's barrier); rows past M are left as they are and only feed rows that are
   // never stored.
-  const bool xp_on = MT <= 2 && p.xp_w && p.conv_state && p.S == 1 && col0 < p.conv_D;   // per workgroup
   __bf16* ut = &xs[0][0];
   const int64_t n = col0 + w * 16 + 4 * g;
   if (n < p.Nout) {
@@ -333,23 +350,20 @@ __global__ __launch_bounds__(64 * kGemmNW) void gemm_xwt_kernel(GemmParams p) {
   }
 
   // x-projection partial of this 128-channel slice: D[r][m] = sum_k W_xp[r][col0 + k] u[m][k]
-  // (A = W_xp rows, rows past xp_n repeat the last; B = u rows from LDS), wave w taking the
-  // output fragments w, w + 8, ... of the (xp_n / 16) x MT grid
+  // (A = W_xp rows, rows past xp_n repeating the last; B = u rows from LDS), wave w taking the
+  // output fragments w, w + 8, ... of the (xp_n / 16) x MT grid: the first kXpF with the W_xp
+  // fragments loaded at the start, any further ones (xp_n > 192) loading theirs here
   if constexpr (MT <= 2) {
     if (xp_on) {   // uniform per workgroup
       __syncthreads();
       const int64_t slice = col0 / 128;
-      const bf16_t* Wx = static_cast<const bf16_t*>(p.xp_w);
-      const int RT = (int)((p.xp_n + 15) / 16);
-      for (int f = w; f < RT * MT; f += 8) {
+      const int nf = xp_rt * MT;
+      auto frag = [&](int f, const bf16x8 (&a)[4]) __attribute__((always_inline)) {
         const int rt = f / MT, mt = f % MT;
-        const bf16_t* wxr = Wx + std::min<int64_t>(16 * rt + r16, p.xp_n - 1) * p.conv_D + col0 + 8 * g;
-        bf16x8 a[4], b[4];
+        bf16x8 b[4];
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-          a[s2] = *reinterpret_cast<const bf16x8*>(wxr + 32 * s2);
+        for (int s2 = 0; s2 < 4; ++s2)
           b[s2] = *reinterpret_cast<const bf16x8*>(&ut[(mt * 16 + r16) * kGemmXS + 32 * s2 + 8 * g]);
-        }
         f32x4 acc4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) acc4 = mfma16(a[s2], b[s2], acc4);
@@ -357,6 +371,17 @@ __global__ __launch_bounds__(64 * kGemmNW) void gemm_xwt_kernel(GemmParams p) {
         if (ro < p.xp_n && m < p.M)
           *reinterpret_cast<float4*>(p.xp_partial + (slice * p.M + m) * p.xp_n + ro) =
               make_float4(acc4[0], acc4[1], acc4[2], acc4[3]);
+      };
+#pragma unroll
+      for (int i = 0; i < kXpF; ++i)
+        if (w + 8 * i < nf) frag(w + 8 * i, xpa[i]);   // uniform per wave
+      for (int f = w + 8 * kXpF; f < nf; f += 8) {
+        const bf16_t* wxr = static_cast<const bf16_t*>(p.xp_w) +
+                            std::min<int64_t>(16 * (f / MT) + r16, p.xp_n - 1) * p.conv_D + col0 + 8 * g;
+        bf16x8 a[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) a[s2] = *reinterpret_cast<const bf16x8*>(wxr + 32 * s2);
+        frag(f, a);
       }
     }
   }

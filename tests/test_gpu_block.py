@@ -58,8 +58,8 @@ def test_layernorm():
         assert gu.rel_err(y, oracle.layernorm(_bf(x), w, b)) <= gu.TOL["bf16"], (M, D)
 
 
-def _block_run(Bsz, Dm, Di, N, steps, seed, W=4):
-    wts = inputs.block_weights(seed, Dm, Di, N, W=W)
+def _block_run(Bsz, Dm, Di, N, steps, seed, W=4, R=128):
+    wts = inputs.block_weights(seed, Dm, Di, N, W=W, R=R)
     hid, reg, h = inputs.block_state(seed, Bsz, Dm, Di, N, W=W)
     dw = {k: gu.dev(v) for k, v in wts.items()}
     dh, dreg, dst = gu.dev(hid), gu.dev(reg), gu.dev(h)
@@ -97,6 +97,13 @@ def test_block_step_two_row_blocks(N):
     """40 sequences: the fused Delta + state-update kernel runs two blocks of 32 batch rows, the
     second ragged (8 live rows), at every state size (1, 2 and 4 lanes per channel)."""
     errs = _block_run(Bsz=40, Dm=256, Di=256, N=N, steps=2, seed=90 + N)
+    assert max(max(e) for e in errs) <= gu.TOL["bf16"]
+
+
+def test_block_step_rank_256():
+    """Rank 256: the x projection is 288 wide (18 x 2 output fragments per 128-channel slice,
+    more than the 24 whose weights the input projection loads before its stream)."""
+    errs = _block_run(Bsz=40, Dm=256, Di=512, N=16, steps=2, seed=99, R=256)
     assert max(max(e) for e in errs) <= gu.TOL["bf16"]
 
 

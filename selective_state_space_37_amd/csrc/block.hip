@@ -508,6 +508,9 @@ __global__ __launch_bounds__(512) void gemm_res_kernel(GemmParams p) {
 // Y = sum over the S partials in order (+ R), four outputs per thread. A thread issues its
 // residual and eight partials before any arithmetic (without a residual it reads a valid
 // stand-in and drops it; partials past S are masked by value), so no load sits behind a branch.
+// KB partials are loaded per batch before they are added (8, or 32 for long split lists such as
+// the x projection's 32 slices, which would otherwise take 4 round trips).
+template <int KB>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmParams p) {
   const int64_t total = p.M * (p.Nout / 4);
   for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
@@ -518,12 +521,13 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmParams p) {
                                     : reinterpret_cast<const bf16_t*>(src);
     const uint2 rr = *reinterpret_cast<const uint2*>(rsrc);
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int64_t k0 = 0; k0 < p.S; k0 += 8) {
-      float4 t[8];
+    for (int64_t k0 = 0; k0 < p.S; k0 += KB) {
+      float4 t[KB];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) t[k] = *reinterpret_cast<const float4*>(src + std::min<int64_t>(k0 + k, p.S - 1) * stride);
+      for (int k = 0; k < KB; ++k) t[k] = *reinterpret_cast<const float4*>(src + std::min<int64_t>(k0 + k, p.S - 1) * stride);
+      __builtin_amdgcn_sched_barrier(0);   // all KB loads leave before the first add waits
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < KB; ++k) {
         const bool in = k0 + k < p.S;   // a select on the values, not a branch
         s.x += in ? t[k].x : 0.f; s.y += in ? t[k].y : 0.f; s.z += in ? t[k].z : 0.f; s.w += in ? t[k].w : 0.f;
       }
@@ -710,6 +714,13 @@ static void launch_res_mt(const GemmParams& p, int mt, hipStream_t stream) {
   }
 }
 
+static void launch_reduce(const GemmParams& p, hipStream_t stream) {
+  const int64_t total = p.M * (p.Nout / 4);
+  const dim3 grid((unsigned)std::min<int64_t>((total + 255) / 256, 4096));
+  if (p.S > 8) hipLaunchKernelGGL(gemm_reduce_kernel<32>, grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(gemm_reduce_kernel<8>, grid, dim3(256), 0, stream, p);
+}
+
 hipError_t launch_gemm_with(GemmParams p, const GemmChoice& c, hipStream_t stream) {
   p.S = c.S;
   p.kslice = p.K / p.S;
@@ -733,9 +744,7 @@ hipError_t launch_gemm_with(GemmParams p, const GemmChoice& c, hipStream_t strea
     }
   }
   if (p.S > 1) {
-    const int64_t total = p.M * (p.Nout / 4);
-    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)std::min<int64_t>((total + 255) / 256, 4096)), dim3(256), 0,
-                       stream, p);
+    launch_reduce(p, stream);
   }
   return hipGetLastError();
 }
@@ -797,9 +806,7 @@ hipError_t launch_block_step(const BlockParams& bp, void* ws, hipStream_t st) {
   if (e == hipSuccess) {   // xp = the sum of the Di / 128 slice partials
     GemmParams r{};
     r.M = B; r.Nout = XP; r.S = Di / 128; r.partial = partial; r.y = xp; r.ldy = XP;
-    const int64_t total = B * (XP / 4);
-    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)std::min<int64_t>((total + 255) / 256, 4096)), dim3(256), 0,
-                       st, r);
+    launch_reduce(r, st);
     e = hipGetLastError();
   }
   if (e == hipSuccess) {

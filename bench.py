@@ -32,10 +32,6 @@ PEAK_VALU_TOPS = CUS * SIMDS * LANES * CLOCK / 1e12   # fp32 lane-ops/s without 
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_layer_8x2048x5120_bf16_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_37_amd", "csrc", f)
                   for f in ("scan.hip", "device_common.h")]
-# VALU issue model of the recurrence: per state-step 6 single-rate fp32 instructions (Delta*A,
-# expm1/A fma, B*x, product, h fma, readout fma) plus one v_exp_f32, which issues at half rate
-# (measured: 18.5 T/s against 34.6 T/s for FMA), i.e. 8 lane-slots.
-SLOTS_PER_STATE_STEP = 8
 
 LAYER = dict(B=8, L=2048, D=5120, N=16)
 
@@ -171,6 +167,39 @@ def smi_during(fn, torch, min_s=0.5, max_s=20.0):
         return {"error": type(e).__name__}
 
 
+def valu_rates(torch, blocks=8192, iters=64):
+    """Measured vector-ALU rates of this GPU from the probe library (probe/valu_rates.hip): lane
+    FMAs/s, lane v_exp_f32/s, and lane state-steps/s of the scan's per-state-step mix (Delta a,
+    2^t, (Abar - 1)/a, B x, product, h update, readout: 6 VALU + 1 exp, plus 0.25 VALU of token
+    bookkeeping in the probe). 8192 workgroups of 256 threads = 8 waves per SIMD; each probe kernel
+    is timed with HIP events on the stream it runs on, best of 5 after a warm launch."""
+    import ctypes
+    from selective_state_space_37_amd import build as b
+    lib = ctypes.CDLL(b.PROBE_LIB)
+    lib.probe_valu_rates.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 3
+    buf_in = torch.rand(16, device="cuda") + 0.5
+    buf_out = torch.empty(blocks * 256, device="cuda")
+    st = torch.cuda.current_stream()
+    ops = blocks * 256 * iters * 16 * 8
+    res = {}
+    for kind, name in ((0, "fma"), (1, "exp"), (2, "mix")):
+        run = lambda: lib.probe_valu_rates(kind, blocks, iters, buf_in.data_ptr(), buf_out.data_ptr(), st.cuda_stream)
+        assert run() == 0
+        best = None
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            run()
+            e1.record(st)
+            e1.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        res[name] = ops / (best * 1e-3)
+    return {"fma_T_lane_per_s": round(res["fma"] / 1e12, 3), "exp_T_lane_per_s": round(res["exp"] / 1e12, 3),
+            "mix_G_state_steps_per_s": round(res["mix"] / 1e9, 1),
+            "mix_fma_slots_per_state_step": round(res["fma"] / res["mix"], 3)}
+
+
 def device_layer_set(torch, seed, B, L, D, N):
     """An extra independent input set drawn on the device with the same distributions as the
     layer workload (timing only; parity runs use the host generator)."""
@@ -195,6 +224,8 @@ def main():
     ap.add_argument("--no-smi", action="store_true", help="skip the amd-smi clock/power sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 512 MiB device copy three times (counter calibration)")
+    ap.add_argument("--valu-rates-only", action="store_true",
+                    help="print only the measured vector-ALU rates (FMA, exp, the scan's mix) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         sys.stderr.write("bench.py measures one GPU: this library has no multi-GPU path "
@@ -206,6 +237,9 @@ def main():
     from selective_state_space_37_amd import inputs, ssm
     ssm.load()  # fails loudly without the built HIP library
     torch.cuda.set_device(0)
+    if args.valu_rates_only:
+        print(json.dumps({"valu_rates": valu_rates(torch)}), flush=True)
+        return
     if args.copy_calibration:
         src = torch.ones(1 << 27, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -244,8 +278,12 @@ def main():
     value = nbytes / (wall_ms * 1e-3) / 1e9
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     state_steps = elems * N
-    valu_tslots = state_steps * SLOTS_PER_STATE_STEP / (kern_ms * 1e-3) / 1e12
     traffic = read_traffic()
+    rates = valu_rates(torch)
+    # ALU ceiling: the general-A recurrence needs the probe's mix once per state-step, so at the
+    # measured mix rate the kernel cannot take less than floor_ms (the probe's mix carries 0.25
+    # VALU per state-step of its own bookkeeping, so this floor is slightly conservative)
+    floor_ms = state_steps / (rates["mix_G_state_steps_per_s"] * 1e9) * 1e3
 
     out = {
         "metric": "selective-scan HBM GB/s (% of peak) + Gelem/s at B=8,L=2048,D=5120,N=16",
@@ -258,7 +296,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) x/z/B/C, delta = clip(softplus(N(-4,1)), 1e-3, 0.1), A[d,n] = -(n+1))",
         "config": {"workload": "selective scan, Mamba-2.8B layer shape: batch 8, L 2048, d_inner 5120, N 16",
                    "B": B, "L": L, "D": D, "N": N, "io_dtype": "bf16", "state_dtype": "f32",
@@ -269,16 +307,18 @@ def main():
         "kernel_ms": round(kern_ms, 5),
         "kernel_ms_single_launch": {"median": round(med_ms, 5), "min": round(min_ms, 5),
                                     "how": "event pair around each of %d further launches" % args.steps},
-        # The scan kernel is bound by VALU issue (VALUBusy ~83%), not by HBM: the binding roofline
-        # is the VALU lane-slot rate; the HBM figure for the same launches follows it.
-        "roofline": {"bound": "alu", "achieved": round(valu_tslots, 3), "peak": round(PEAK_VALU_TOPS, 3),
-                     "unit": "T VALU lane-slots/s", "frac": round(valu_tslots / PEAK_VALU_TOPS, 4),
-                     "traffic": traffic, "slots_per_state_step": SLOTS_PER_STATE_STEP,
-                     "state_steps_per_launch": state_steps,
+        # The roofline of the metric: algorithmic HBM bytes per launch over the kernel's mean
+        # launch time (HIP events on the stream it runs on) against the published 8 TB/s.
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": nbytes, "kernel_ms": round(kern_ms, 5),
                      "kernel": "scan_kernel<bf16, CH=32, NS=2, KS=8, T=16, N=16, full>"},
-        "roofline_hbm": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                         "bytes_per_launch": nbytes},
+        # The second ceiling at N = 16: vector-ALU issue. From the measured rates of this GPU, the
+        # launch's state-steps at the scan mix's rate take floor_ms; at that time the HBM
+        # fraction would be hbm_frac_at_floor.
+        "alu_ceiling": dict(rates, state_steps_per_launch=state_steps, floor_ms=round(floor_ms, 5),
+                            hbm_frac_at_floor=round(nbytes / (floor_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                            kernel_frac_of_floor=round(floor_ms / kern_ms, 4)),
     }
 
     out["copy_ceiling_GB_s"] = round(copy_ceiling_gbs(torch), 1)

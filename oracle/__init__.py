@@ -23,8 +23,17 @@ already widened to fp32/fp64 -- widening is exact) and return fp64 results.
                    M[i, j] = (C_i . B_j) * (all decay from step j to step i) * (ZOH input scale
                    of step j), for tiny inputs only (numpy; O(L^2)).
 
+* ``layernorm``, ``block_seq``, ``block_step`` -- the Mamba block of the generation workload
+                   (pre-norm, gated input projection, causal conv + SiLU, Delta / B / C
+                   projections, the selective SSM, output projection, residual), composed from
+                   library matmuls, ``conv1d``, ``scan`` and ``step``.
+
 Every function here is pinned by ``tests/test_oracle_pins.py`` against closed forms, the
-continuous-time ODE, brute force and the pages' printed numbers.
+continuous-time ODE, brute force and the pages' printed numbers, with one exception: the block's
+composition (which projection feeds which, where SiLU sits, what the gate multiplies) is a reading
+of the pages' prose, which fixes no value for it. Its parts (``layernorm``, ``conv1d``, ``scan``,
+``step``) are pinned, and ``block_step`` repeated equals ``block_seq``, but a misreading shared by
+both would pass: the composition is PARITY UNPINNED.
 """
 from __future__ import annotations
 
@@ -408,7 +417,8 @@ def _silu(v):
 def block_seq(hidden, conv_state, h, wts, eps=1e-5, _lib=None):
     """The block over a whole sequence: hidden [B, L, Dm] -> (hidden + block output, register
     [B, Di, W] after the last token, state [B, Di, N]). Token-wise parts use library matmuls; the
-    convolution is ``conv1d`` and the SSM is ``scan`` (both pinned)."""
+    convolution is ``conv1d`` and the SSM is ``scan`` (both pinned). The composition itself is a
+    reading of the pages (parity unpinned)."""
     hidden = _f64(hidden)
     w = {k: _f64(v) for k, v in wts.items()}
     xn = layernorm(hidden, w["ln_w"], w["ln_b"], eps)
@@ -425,7 +435,8 @@ def block_seq(hidden, conv_state, h, wts, eps=1e-5, _lib=None):
 def block_step(hidden, conv_state, h, wts, eps=1e-5, _lib=None):
     """One decode token through the block: hidden [B, Dm] -> (hidden + block output, register
     [B, Di, W], state [B, Di, N]), with the convolution register and the SSM state carried in and
-    out; the SSM step is ``step`` (pinned)."""
+    out; the SSM step is ``step`` (pinned). The composition itself is a reading of the pages
+    (parity unpinned)."""
     hidden = _f64(hidden)
     w = {k: _f64(v) for k, v in wts.items()}
     xn = layernorm(hidden, w["ln_w"], w["ln_b"], eps)

@@ -55,6 +55,25 @@ def _compile(src: str):
     return obj, _resources(r.stderr)
 
 
+PROBE_SRC = os.path.join(PKG, "probe", "valu_rates.hip")
+PROBE_LIB = os.path.join(PKG, "probe", "libvalu_rates.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The vector-ALU rate probe (measurement support for the benchmark's ALU ceiling), a library
+    of its own so the selective-scan library exports only the path."""
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + [f for f in FLAGS if not f.startswith("-Rpass")] + ["-shared", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed for %s" % PROBE_SRC)
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print("built", PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(verbose: bool = False) -> str:
     """Compile every csrc/*.hip for gfx950 and link selective_state_space_37_amd/libssm.so."""
     os.makedirs(OBJ_DIR, exist_ok=True)
@@ -80,6 +99,7 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB_PATH)
     if verbose:
         print("built", LIB_PATH)
+    build_probe(verbose)
     return LIB_PATH
 
 

@@ -357,9 +357,11 @@ ssm_status ssm_state_update(int64_t B, int64_t D, int64_t N, int64_t W, ssm_dtyp
   if (!x || !delta || !A || !Bm || !Cm || !h || !y)
     return fail(SSM_ERR_INVALID_ARGUMENT, "x, delta, A, Bm, Cm, h and y must not be NULL");
   if (conv_state && !conv_w) return fail(SSM_ERR_INVALID_ARGUMENT, "conv_w is NULL while conv_state is given");
-  if (!aligned16(h) || !aligned16(x) || !aligned16(y) || !aligned16(A) ||
+  if (!aligned16(h) || !aligned16(x) || !aligned16(delta) || !aligned16(y) || !aligned16(A) ||
+      !aligned16(Bm) || !aligned16(Cm) || (z && !aligned16(z)) ||
       (conv_state && (!aligned16(conv_state) || !aligned16(conv_w))))
-    return fail(SSM_ERR_INVALID_ARGUMENT, "h, x, y, A, conv_state and conv_w must be 16-byte aligned");
+    return fail(SSM_ERR_INVALID_ARGUMENT,
+                "h, x, delta, z, Bm, Cm, y, A, conv_state and conv_w must be 16-byte aligned");
   const size_t es = io_size(io), tok = (size_t)(B * D) * es;
   const size_t stb = (size_t)(B * D * N) * 4;
   const void* ins[] = {x, delta, z, Bm, Cm, A, h, conv_state, conv_w};

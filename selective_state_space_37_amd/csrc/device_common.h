@@ -100,6 +100,30 @@ __device__ __forceinline__ float softplus_f32(float u) {
   return u != u ? u : r;
 }
 
+// ZOH input scale expm1(Delta a) / a from Abar = 2^t, t = Delta a log2(e), ia = 1 / a.
+// fma(Abar, ia, -ia) = (Abar - 1) / a loses relative accuracy as |Delta a| shrinks: Abar carries an
+// absolute rounding error of about 2^-24, so (Abar - 1) is off by about 6e-8 / |Delta a| relative.
+// That is far inside the bf16 tolerance but not the float32 one, so with ACCURATE (float32 I/O)
+// |Delta a| < 1/16 takes the series Delta (1 + z/2 + z^2/6 + z^3/24), z = Delta a = t ln 2, whose
+// truncation error is below z^4 / 120 < 1.3e-7 relative; above it the fma form is within 2e-6.
+template <bool ACCURATE>
+__device__ __forceinline__ float zoh_input_scale(float abar, float t, float dt, float ia) {
+  const float s = fmaf(abar, ia, -ia);
+  if constexpr (!ACCURATE) {
+    return s;
+  } else {
+    constexpr float kLn2 = 0.6931471805599453f;
+    constexpr float c1 = kLn2 / 2.0f;                       // ln2 / 2!
+    constexpr float c2 = kLn2 * kLn2 / 6.0f;                // ln2^2 / 3!
+    constexpr float c3 = kLn2 * kLn2 * kLn2 / 24.0f;        // ln2^3 / 4!
+    constexpr float kSmallT = 0.0625f / kLn2;               // |z| < 1/16
+    float q = fmaf(t, c3, c2);
+    q = fmaf(q, t, c1);
+    const float ser = fmaf(dt * t, q, dt);
+    return fabsf(t) < kSmallT ? ser : s;
+  }
+}
+
 // Element loads/stores of the per-token tensors in either storage type.
 template <typename T> struct IoTraits;
 

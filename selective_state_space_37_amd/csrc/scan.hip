@@ -417,9 +417,11 @@ void scan_kernel(ScanParams p) {
         const float* bc = &s_bc[buf][t0 + i][n0][0];
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-          const float abar = exp2_fast(dx.x * a2[j]);
+          const float tx = dx.x * a2[j];
+          const float abar = exp2_fast(tx);
           abar_t[i][j] = abar;
-          u_t[i][j] = fmaf(abar, ia[j], -ia[j]) * (bc[2 * j] * dx.y);  // expm1(Delta a)/a B x
+          // expm1(Delta a)/a B x
+          u_t[i][j] = zoh_input_scale<std::is_same<io_t, float>::value>(abar, tx, dx.x, ia[j]) * (bc[2 * j] * dx.y);
         }
         if (!FULL) dsum += dx.x;
       }

@@ -35,11 +35,15 @@ namespace {
 // Decay of a mask entry (i, j), j <= i: exp(a (S_i - S_j)) phi_j. It factors through the last
 // token e of j's 16-token tile:
 //   exp(a (S_i - S_e)) * [exp(a (S_e - S_j)) phi_j].
-// The bracket depends on j only and is folded into x^T when it is staged (exponent <= 0). The
-// first factor is one exp per lane and tile: <= 1 off the diagonal, and on the diagonal tile
-// (S_i <= S_e, at most 15 steps apart) at most exp(15 |a| max Delta), far inside the range of
-// float32 and bf16. So every mask entry is G_ij times a per-row factor, with the causal cut
-// j <= i on the diagonal tile.
+// The bracket depends on j only and is folded into x^T when it is staged, its exponent floored at
+// 2^-64 (kSsdStageExpFloor). Off the diagonal (S_i >= S_e) the first factor is one exp per lane and
+// tile, <= 1. On the diagonal tile (S_i <= S_e) it is not used: exp(a (S_i - S_e)) overflows once
+// |a| times the step sizes of up to 15 tokens exceeds about 88, while the staged bracket underflows.
+// There every entry divides the staged factor out of the direct difference instead,
+//   2^(a2 (S_i - S_j) - max(a2 (S_e - S_j), -64)),
+// whose exponent is at most 64 (it is a2 (S_i - S_e) <= 64 when the floor is not hit, and
+// a2 (S_i - S_j) + 64 <= 64 when it is, since S_i >= S_j). So every mask entry is G_ij times a
+// bounded factor, with the causal cut j <= i on the diagonal tile.
 template <int Q, int N>
 __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 Xt[kP * (Q + 8)];
@@ -156,9 +160,13 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) m[half * 4 + q] = gv[q] * r;
         } else if (jt == ib) {
-          const float r = exp2_fast(a2 * (Si - sS[jt * 16 + 15]));
+          const float Se = sS[jt * 16 + 15];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) m[half * 4 + q] = (j0 + q <= il) ? gv[q] * r : 0.f;
+          for (int q = 0; q < 4; ++q) {
+            const float Sj = sS[j0 + q];
+            const float r = exp2_fast(a2 * (Si - Sj) - fmaxf(a2 * (Se - Sj), kSsdStageExpFloor));
+            m[half * 4 + q] = (j0 + q <= il) ? gv[q] * r : 0.f;
+          }
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) m[half * 4 + r] = 0.f;

@@ -72,11 +72,19 @@ __device__ __forceinline__ int xt_swizzle_words(int row) {
   return (8 * ((row >> 4) & 3)) & (Q / 2 - 1);
 }
 
+// Floor of the base-2 exponent of the staged x scale (see below): 2^-64 keeps a scaled input far
+// inside the normal range of bf16 and float32, and the diagonal tile's compensating factor at most
+// 2^64.
+constexpr float kSsdStageExpFloor = -64.0f;
+
 // Stage x[b, chunk, h, :] transposed into LDS (the layout above), each token's column scaled by
-//   cp_j = exp(a (S_e - S_j)) phi_j,   e = the last token of j's 16-token tile (S_e >= S_j),
-// computed from the chunk's (S, phi) table sp; a2 = a log2(e). Each thread takes two
-// consecutive tokens, so every LDS write is one 32-bit word holding the pair (j, j + 1) of one
-// channel; the scaled values are rounded to bf16 once. Tokens past L are staged as zeros.
+//   cp_j = 2^max(a2 (S_e - S_j), -64) phi_j,   e = the last token of j's 16-token tile (S_e >= S_j),
+// computed from the chunk's (S, phi) table sp; a2 = a log2(e). The floor matters only where the
+// decay from j to the tile end is below 2^-64: rows after the tile then see the input at most
+// 2^-64 |phi_j x_j| too large (far below bf16 rounding), and the diagonal tile divides the same
+// floored factor out of each entry. Each thread takes two consecutive tokens, so every LDS write
+// is one 32-bit word holding the pair (j, j + 1) of one channel; the scaled values are rounded to
+// bf16 once. Tokens past L are staged as zeros.
 template <int Q>
 __device__ void stage_x_transposed_scaled(const SsdParams& p, int64_t b, int64_t c, int64_t h, __bf16* Xt,
                                           const float2* sp, float a2) {
@@ -90,7 +98,8 @@ __device__ void stage_x_transposed_scaled(const SsdParams& p, int64_t b, int64_t
     if (t + 1 < p.L) r1 = *reinterpret_cast<const uint4*>(xg + ((b * p.L + t + 1) * p.H + h) * kP + pg * 8);
     const float2 v0 = sp[2 * jp], v1 = sp[2 * jp + 1];
     const float se = sp[(2 * jp) | 15].x;
-    const float cp0 = exp2_fast(a2 * (se - v0.x)) * v0.y, cp1 = exp2_fast(a2 * (se - v1.x)) * v1.y;
+    const float cp0 = exp2_fast(fmaxf(a2 * (se - v0.x), kSsdStageExpFloor)) * v0.y;
+    const float cp1 = exp2_fast(fmaxf(a2 * (se - v1.x), kSsdStageExpFloor)) * v1.y;
     const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w}, w1[4] = {r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {

@@ -12,6 +12,8 @@
 // load covers 1 KiB of contiguous state. The lanes of a channel share x, Delta, z and the conv
 // register (same addresses, one fetch), each forms its part of C . h, and the parts are added
 // across the lanes with DPP quad permutes. At N < 4 one lane owns the whole channel.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -180,8 +182,9 @@ __global__ __launch_bounds__(256) void step_kernel(StepParams p) {
     float yv = 0.f;
 #pragma unroll
     for (int n = 0; n < SPL; ++n) {
-      const float abar = exp2_fast(dt * a2[n]);
-      const float coef = fmaf(abar, ia[n], -ia[n]);
+      const float tx = dt * a2[n];
+      const float abar = exp2_fast(tx);
+      const float coef = zoh_input_scale<std::is_same<io_t, float>::value>(abar, tx, dt, ia[n]);
       h[r][n] = fmaf(abar, h[r][n], coef * (Bv[r][n] * u));
       yv = fmaf(Cv[r][n], h[r][n], yv);
     }

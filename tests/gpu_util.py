@@ -36,6 +36,54 @@ def rel_err(a, ref) -> float:
     return float(np.max(np.abs(a - ref))) / max(float(np.max(np.abs(ref))), 1e-30)
 
 
+def elementwise_diag(a, ref):
+    """Element-wise relative error |a - ref| / (|ref| + 1e-3 max|ref|): its median, 99.9th
+    percentile and maximum (a diagnostic printed beside the max-norm metric, not a gate)."""
+    a = np.asarray(a, dtype=np.float64).ravel()
+    ref = np.asarray(ref, dtype=np.float64).ravel()
+    if ref.size == 0:
+        return 0.0, 0.0, 0.0
+    r = np.abs(a - ref) / (np.abs(ref) + 1e-3 * float(np.max(np.abs(ref))) + 1e-300)
+    q = np.quantile(r, [0.5, 0.999])
+    return float(q[0]), float(q[1]), float(np.max(r))
+
+
+def diag_str(a, ref) -> str:
+    m, p, x = elementwise_diag(a, ref)
+    return "elementwise median %.2e p99.9 %.2e max %.2e" % (m, p, x)
+
+
+class Accum:
+    """Max-norm error and element-wise diagnostic accumulated over blocks of one output tensor.
+
+    The diagnostic's normaliser needs max|ref| over the whole tensor, so the blocks' |a - ref| and
+    |ref| are kept (float32) and reduced at the end."""
+
+    def __init__(self):
+        self.maxdiff = 0.0
+        self.maxref = 0.0
+        self.diffs, self.refs = [], []
+
+    def add(self, a, ref):
+        a = np.asarray(a, dtype=np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        assert np.isfinite(a).all(), "non-finite output"
+        d = np.abs(a - ref)
+        self.maxdiff = max(self.maxdiff, float(d.max(initial=0.0)))
+        self.maxref = max(self.maxref, float(np.abs(ref).max(initial=0.0)))
+        self.diffs.append(d.astype(np.float32).ravel())
+        self.refs.append(np.abs(ref).astype(np.float32).ravel())
+
+    def err(self) -> float:
+        return self.maxdiff / max(self.maxref, 1e-30)
+
+    def diag(self) -> str:
+        d = np.concatenate(self.diffs).astype(np.float64)
+        r = d / (np.concatenate(self.refs).astype(np.float64) + 1e-3 * self.maxref + 1e-300)
+        q = np.quantile(r, [0.5, 0.999])
+        return "elementwise median %.2e p99.9 %.2e max %.2e" % (q[0], q[1], r.max())
+
+
 # ----------------------------------------------------------------------------- scan
 def scan_on_gpu(inp: inputs.ScanInputs, segment_len=None, return_state=True):
     y, hl = ssm.scan_fwd(dev(inp.x), dev(inp.delta), dev(inp.A), dev(inp.Bm), dev(inp.Cm),
@@ -64,6 +112,22 @@ def scan_parity(inp, gpu_out, channels=None) -> float:
     if hl is not None:
         e = max(e, rel_err(hl, rh))
     return e
+
+
+def scan_parity_blocks(inp, gpu_out, block: int):
+    """Whole-tensor parity of a scan result, the oracle run over channel blocks of `block` (the
+    channels' recurrences are independent, so each block is the full problem's exact answer on
+    those channels). Returns (Accum for y, Accum for h_last or None)."""
+    y, hl = gpu_out
+    D = inp.x.shape[2]
+    ay, ah = Accum(), (Accum() if hl is not None else None)
+    for c0 in range(0, D, block):
+        ch = np.arange(c0, min(D, c0 + block))
+        ry, rh = scan_oracle(inp, ch)
+        ay.add(y[:, :, ch], ry)
+        if ah is not None:
+            ah.add(hl[:, ch], rh)
+    return ay, ah
 
 
 # ----------------------------------------------------------------------------- prefill with conv
@@ -250,6 +314,21 @@ def ssd_bwd_errors(gpu: dict, ref: dict, heads=None) -> dict:
             g = np.take(g, heads, axis=ax[k])
         errs[k] = rel_err(g, r)
     return errs
+
+
+def ssd_parity_blocks(inp, gpu_out, block: int):
+    """Whole-tensor parity of an SSD result, the oracle run over blocks of `block` heads (each head
+    is independent given its group's B and C). Returns (Accum for y, Accum for h_last or None)."""
+    y, hl = gpu_out
+    H = inp.x.shape[2]
+    ay, ah = Accum(), (Accum() if hl is not None else None)
+    for h0 in range(0, H, block):
+        hs = np.arange(h0, min(H, h0 + block))
+        ry, rh = ssd_oracle(inp, hs)
+        ay.add(y[:, :, hs], ry)
+        if ah is not None:
+            ah.add(hl[:, hs], rh)
+    return ay, ah
 
 
 def ssd_parity(inp, gpu_out, heads=None) -> float:

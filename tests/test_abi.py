@@ -145,6 +145,8 @@ def step_call(lib, B=4, D=64, N=16, W=4, io=BF16, x=A_, delta=2 * A_, A=3 * A_, 
     (dict(conv=8 * A_, conv_w=None), INVALID), (dict(h=6 * A_ + 4), INVALID), (dict(y=A_), INVALID),
     (dict(A=3 * A_ + 4), INVALID), (dict(conv=8 * A_, conv_w=9 * A_ + 8), INVALID),
     (dict(io=3), INVALID),
+    (dict(Bm=4 * A_ + 8), INVALID), (dict(Cm=5 * A_ + 4), INVALID),   # B / C read as 16-byte vectors
+    (dict(delta=2 * A_ + 2), INVALID),
 ])
 def test_step_rejects(lib, kw, expect):
     assert step_call(lib, **kw) == expect

@@ -120,6 +120,34 @@ ssm_status ssm_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ssm_scan_fwd_noalloc -- ssm_scan_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments without
+ * workspace / workspace_bytes, same plan and kernels, same results. The only scratch the scan
+ * needs (the segment carries of a long, narrow input) lives in a device array inside the library,
+ * SSM_SCAN_NOALLOC_SCRATCH_BYTES (4 MiB) per GPU, held from the library's load until the process
+ * ends. The automatic plan splits L only while the channel tiles alone fill fewer than 512
+ * workgroups, into at most about 1024 workgroups' worth of segments, so its workspace
+ * (ssm_scan_fwd_workspace_bytes()) never exceeds about 3.4 MB.
+ *
+ *   Errors: those of ssm_scan_fwd; SSM_ERR_WORKSPACE_TOO_SMALL if a plan ever needed more than
+ *   SSM_SCAN_NOALLOC_SCRATCH_BYTES, checked on the host before anything is enqueued; SSM_ERR_HIP
+ *   if the array's address cannot be obtained on the current device.
+ *   It calls no hipMalloc, hipFree, hipMemsetAsync or hipMemcpyAsync (the empty-sequence state
+ *   copy is a kernel). The first call on a device looks the array's address up, a host-side query
+ *   that enqueues nothing; a caller that captures graphs can make one ordinary call first.
+ *   Every call on a GPU uses that GPU's one array and leaves its contents behind (nothing in it
+ *   needs to start at zero): calls that overlap on one GPU (other streams, other host threads)
+ *   race on it, and the caller must serialise them.
+ */
+#define SSM_SCAN_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+
+ssm_status ssm_scan_fwd_noalloc(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io_dtype,
+                                const void* x, const void* delta, const float* delta_bias,
+                                int delta_softplus, const float* A, const void* Bm, const void* Cm,
+                                const float* Dskip, const void* z, const float* h0, void* y,
+                                float* h_last, void* stream);
+
+/*
  * ssm_scan_fwd_segmented -- ssm_scan_fwd with an explicit segment length along L
  * (segment_len >= 1; segment_len >= L means one segment). The workspace size for it is
  * ssm_scan_fwd_segmented_workspace_bytes(). Used to check that results do not depend on the

@@ -6,10 +6,18 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/ssm.h"
 #include "kernels.h"
+
+// Scratch of ssm_scan_fwd_noalloc (the segment carries of a long, narrow input): a file-scope
+// device array, one copy per GPU, alive until the process ends. In host code this name is a
+// host-side stand-in, never a device address: host code uses only the address that
+// hipGetSymbolAddress returned for the current device (scratch_for_current_device below).
+constexpr size_t kNoallocScratchBytes = SSM_SCAN_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
 
 namespace {
 
@@ -36,6 +44,30 @@ ssm_status from_hip(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Device address of `scratch` on the current device, looked up once per device (with that device
+// current) and kept: each GPU holds its own copy of the array at its own address.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+ssm_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SSM_ERR_UNSUPPORTED, "device %d: the static scratch supports devices 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return from_hip(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(SSM_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SSM_OK;
+}
 
 size_t io_size(ssm_dtype t) { return t == SSM_BF16 ? 2 : 4; }
 
@@ -82,7 +114,7 @@ ssm_status scan_common(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io,
                        const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
                        void* y, float* h_last, int64_t seg_len, void* ws, size_t ws_bytes, void* stream,
                        int64_t conv_W = 0, const float* conv_w = nullptr, const float* conv_b = nullptr,
-                       void* conv_state = nullptr) {
+                       void* conv_state = nullptr, bool static_scratch = false) {
   if (B < 0 || L < 0) return fail(SSM_ERR_INVALID_ARGUMENT, "B=%lld and L=%lld must be >= 0", (long long)B, (long long)L);
   if (D < 1 || (D % 4) != 0) return fail(SSM_ERR_INVALID_ARGUMENT, "D=%lld must be >= 1 and a multiple of 4", (long long)D);
   if (!valid_dtype(io)) return fail(SSM_ERR_INVALID_ARGUMENT, "unknown io_dtype %d", (int)io);
@@ -101,6 +133,8 @@ ssm_status scan_common(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io,
     return fail(SSM_ERR_INVALID_ARGUMENT, "h_last partially overlaps h0 (it may only equal it)");
   if (L == 0) {
     if (!h_last || h_last == h0) return ok();
+    if (static_scratch)   // no memory-set or copy node: a kernel
+      return from_hip(ssm::launch_state_fill(h_last, h0, B * D * N, st), "L == 0 state fill");
     hipError_t e = h0 ? hipMemcpyAsync(h_last, h0, stb, hipMemcpyDeviceToDevice, st)
                       : hipMemsetAsync(h_last, 0, stb, st);
     return from_hip(e, "L == 0 state copy");
@@ -130,6 +164,15 @@ ssm_status scan_common(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io,
 
   const int64_t nseg = num_segments(L, seg_len);
   const size_t need = ssm::scan_workspace_bytes(B, D, N, nseg);
+  if (static_scratch && need > 0) {
+    if (need > kNoallocScratchBytes)
+      return fail(SSM_ERR_WORKSPACE_TOO_SMALL,
+                  "the plan for these sizes needs %zu bytes of scratch; the static scratch holds %zu "
+                  "(use ssm_scan_fwd with a workspace)", need, kNoallocScratchBytes);
+    const ssm_status sc = scratch_for_current_device(&ws);
+    if (sc != SSM_OK) return sc;
+    ws_bytes = kNoallocScratchBytes;
+  }
   if (need > 0) {
     if (!ws) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace is NULL; %zu bytes needed", need);
     if (ws_bytes < need) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, need);
@@ -296,6 +339,15 @@ ssm_status ssm_scan_fwd_conv(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dty
   if (segment_len > 0) seg = segment_len >= L ? L : ((segment_len + kTile - 1) / kTile) * kTile;
   return scan_common(B, L, D, N, io, x, delta, delta_bias, delta_softplus, A, Bm, Cm, Dskip, z, h0, y,
                      h_last, seg, ws, ws_bytes, stream, conv_width, conv_w, conv_b, conv_state);
+}
+
+ssm_status ssm_scan_fwd_noalloc(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io, const void* x,
+                                const void* delta, const float* delta_bias, int delta_softplus, const float* A,
+                                const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                                const float* h0, void* y, float* h_last, void* stream) {
+  const int64_t seg = (B > 0 && L > 0 && D > 0) ? auto_segment_len(B, L, D, N) : 1;
+  return scan_common(B, L, D, N, io, x, delta, delta_bias, delta_softplus, A, Bm, Cm, Dskip, z, h0, y, h_last,
+                     seg, nullptr, 0, stream, 0, nullptr, nullptr, nullptr, true);
 }
 
 ssm_status ssm_scan_fwd_segmented(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io, const void* x,

@@ -39,6 +39,9 @@ size_t scan_workspace_bytes(int64_t B, int64_t D, int64_t N, int64_t nseg);
 // Enqueue the scan (one to three kernels) on the stream. Returns hipSuccess or the launch error.
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream);
 
+// dst[0 .. n) = src (or zeros without src), by a kernel on the stream.
+hipError_t launch_state_fill(float* dst, const float* src, int64_t n, hipStream_t stream);
+
 // Enqueue only the segment carries of a plan with nseg >= 2 (state-only pass and carry pass):
 // afterwards ws_h[b, s] holds the state entering segment s. The segment length is a multiple
 // of 16 tokens.

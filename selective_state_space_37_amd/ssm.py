@@ -19,7 +19,7 @@ STATUS = {0: "SSM_OK", 1: "SSM_ERR_INVALID_ARGUMENT", 2: "SSM_ERR_UNSUPPORTED",
 
 # Every symbol include/ssm.h declares.
 EXPORTS = ("ssm_abi_version", "ssm_status_string", "ssm_last_error_detail",
-           "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd",
+           "ssm_scan_fwd_workspace_bytes", "ssm_scan_fwd", "ssm_scan_fwd_noalloc",
            "ssm_scan_fwd_segmented_workspace_bytes", "ssm_scan_fwd_segmented",
            "ssm_scan_fwd_conv_workspace_bytes", "ssm_scan_fwd_conv",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd",
@@ -60,6 +60,8 @@ def load(path: str = LIB_PATH):
     scan_args = [i64, i64, i64, i64, ci, vp, vp, vp, ci, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssm_scan_fwd.argtypes = scan_args + [vp, sz, vp]
     lib.ssm_scan_fwd.restype = ci
+    lib.ssm_scan_fwd_noalloc.argtypes = scan_args + [vp]
+    lib.ssm_scan_fwd_noalloc.restype = ci
     lib.ssm_scan_fwd_segmented.argtypes = scan_args + [i64, vp, sz, vp]
     lib.ssm_scan_fwd_segmented.restype = ci
     lib.ssm_scan_fwd_conv_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
@@ -183,6 +185,30 @@ def scan_fwd(x, delta, A, Bm, Cm, *, delta_bias=None, delta_softplus=False, Dski
         st = lib.ssm_scan_fwd_segmented(*args, int(segment_len), _p(ws), nb, _stream(x))
     _check(st)
     return y, h_last
+
+
+def scan_fwd_noalloc(x, delta, A, Bm, Cm, y, *, delta_bias=None, delta_softplus=False, Dskip=None, z=None,
+                     h0=None, h_last=None) -> None:
+    """ssm_scan_fwd_noalloc: the scan into caller-provided y (and h_last, or None) with no
+    workspace and no allocation at all (the library's static scratch holds the segment carries)."""
+    lib = load()
+    Bsz, L, D = x.shape
+    N = A.shape[1]
+    io = x.dtype
+    _dev(x, "x")
+    _dev(delta, "delta", io, (Bsz, L, D))
+    _dev(z, "z", io, (Bsz, L, D))
+    _dev(Bm, "Bm", io, (Bsz, L, N))
+    _dev(Cm, "Cm", io, (Bsz, L, N))
+    _dev(A, "A", torch.float32, (D, N))
+    _dev(delta_bias, "delta_bias", torch.float32, (D,))
+    _dev(Dskip, "Dskip", torch.float32, (D,))
+    _dev(h0, "h0", torch.float32, (Bsz, D, N))
+    _dev(y, "y", io, (Bsz, L, D))
+    _dev(h_last, "h_last", torch.float32, (Bsz, D, N))
+    _check(lib.ssm_scan_fwd_noalloc(Bsz, L, D, N, _io_code(x), _p(x), _p(delta), _p(delta_bias),
+                                    int(bool(delta_softplus)), _p(A), _p(Bm), _p(Cm), _p(Dskip), _p(z), _p(h0),
+                                    _p(y), _p(h_last), _stream(x)))
 
 
 def scan_fwd_conv(x, delta, A, Bm, Cm, conv_w, *, conv_b=None, conv_state=None, delta_bias=None,

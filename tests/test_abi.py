@@ -77,6 +77,38 @@ def test_scan_rejects(lib, kw, expect):
     assert lib.ssm_last_error_detail().decode() != ""
 
 
+NOALLOC_SCRATCH = 4 << 20
+
+
+def test_noalloc_scratch_covers_every_automatic_plan(lib):
+    """ssm_scan_fwd_noalloc keeps the segment carries in a static 4 MiB scratch: the automatic
+    plan's workspace stays below it for any shape (long and short, narrow and wide, every N)."""
+    worst = 0
+    for N in (1, 2, 4, 8, 16):
+        for B in (1, 2, 3, 7, 8, 64):
+            for D in (4, 8, 32, 36, 64, 100, 256, 512, 1024, 4096, 5120, 16384):
+                for L in (257, 1000, 4096, 65536, 1 << 20, 1 << 24, 1 << 30):
+                    for io in (F32, BF16):
+                        worst = max(worst, lib.ssm_scan_fwd_workspace_bytes(B, L, D, N, io))
+    assert 0 < worst <= NOALLOC_SCRATCH, worst
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(N=3), UNSUPPORTED), (dict(D=6), INVALID), (dict(x=0), INVALID), (dict(y=A_ + 64), INVALID),
+    (dict(x=A_ + 4), INVALID), (dict(h0=8 * A_, h_last=8 * A_ + 16), INVALID),
+])
+def test_noalloc_rejects(lib, kw, expect):
+    a = dict(B=1, L=16, D=64, N=16, io=F32, x=A_, delta=2 * A_, A=3 * A_, Bm=4 * A_, Cm=5 * A_, y=6 * A_,
+             h0=None, h_last=None)
+    a.update(kw)
+    f = lambda v: fake(v) if v else None
+    st = lib.ssm_scan_fwd_noalloc(a["B"], a["L"], a["D"], a["N"], a["io"], f(a["x"]), f(a["delta"]), None, 0,
+                                  f(a["A"]), f(a["Bm"]), f(a["Cm"]), None, None, f(a["h0"]), f(a["y"]),
+                                  f(a["h_last"]), None)
+    assert st == expect
+    assert lib.ssm_last_error_detail().decode() != ""
+
+
 def test_scan_noop_batch_zero(lib):
     assert scan_call(lib, B=0) == OK
 

@@ -91,15 +91,12 @@ constexpr int64_t kPlanCUs = 256;
 constexpr int64_t kTile = 16;         // tokens per LDS tile of the scan kernels
 constexpr int64_t kMinSegment = 256;  // shortest automatic segment
 
-// Channels per scan workgroup (the kernels use 32 for N >= 8, 64 below).
-int64_t scan_channels_per_wg(int64_t N) { return N >= 8 ? 32 : 64; }
-
 int64_t auto_segment_len(int64_t B, int64_t L, int64_t D, int64_t N) {
-  const int64_t ch = scan_channels_per_wg(N);
+  const int64_t ch = ssm::scan_channels_per_tile(N);
   const int64_t wgs = ((D + ch - 1) / ch) * B;
   if (L <= kMinSegment || wgs >= 2 * kPlanCUs) return L;
-  // aim for one round of resident workgroups: four per CU (the state-only pass holds
-  // about 120 registers per lane, four waves per SIMD)
+  // aim for four workgroups per CU (measured on the long, narrow fp32 scan: one round of four
+  // per CU, or two, beats one of five, whose segment pass ran slower per token)
   int64_t nseg = (4 * kPlanCUs + wgs - 1) / wgs;
   int64_t seg = (L + nseg - 1) / nseg;
   seg = ((seg + kTile - 1) / kTile) * kTile;
@@ -163,6 +160,9 @@ ssm_status scan_common(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io,
   }
 
   const int64_t nseg = num_segments(L, seg_len);
+  if (B > 65535 || nseg > 65535)
+    return fail(SSM_ERR_UNSUPPORTED, "B=%lld and the segment count %lld must each be <= 65535", (long long)B,
+                (long long)nseg);
   const size_t need = ssm::scan_workspace_bytes(B, D, N, nseg);
   if (static_scratch && need > 0) {
     if (need > kNoallocScratchBytes)
@@ -189,6 +189,7 @@ ssm_status scan_common(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io,
   if (nseg > 1) {
     p.ws_h = static_cast<float*>(ws);
     p.ws_sum = p.ws_h + B * nseg * D * N;
+    p.ws_neg = reinterpret_cast<int*>(p.ws_sum + B * nseg * D);
   }
   if (conv_w) {
     p.conv_w = conv_w; p.conv_b = conv_b; p.conv_W = (int)conv_W;
@@ -254,6 +255,9 @@ ssm_status scan_bwd_common(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype
   }
   const int64_t sl = bwd_segment_len(L, seg_len);
   const int64_t nseg = num_segments(L, sl);
+  if (B > 65535 || nseg > 65535)
+    return fail(SSM_ERR_UNSUPPORTED, "B=%lld and the segment count %lld must each be <= 65535", (long long)B,
+                (long long)nseg);
   const size_t need = ssm::scan_bwd_workspace_bytes(B, L, D, N, nseg);
   if (!ws) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace is NULL; %zu bytes needed", need);
   if (ws_bytes < need) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, need);

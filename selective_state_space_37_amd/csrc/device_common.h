@@ -106,6 +106,9 @@ __device__ __forceinline__ float softplus_f32(float u) {
 // That is far inside the bf16 tolerance but not the float32 one, so with ACCURATE (float32 I/O)
 // |Delta a| < 1/16 takes the series Delta (1 + z/2 + z^2/6 + z^3/24), z = Delta a = t ln 2, whose
 // truncation error is below z^4 / 120 < 1.3e-7 relative; above it the fma form is within 2e-6.
+// Base-2 exponent bound of the series: |t| < kZohSeriesT, i.e. |z| < 1/16.
+constexpr float kZohSeriesT = 0.0625f / 0.6931471805599453f;
+
 template <bool ACCURATE>
 __device__ __forceinline__ float zoh_input_scale(float abar, float t, float dt, float ia) {
   const float s = fmaf(abar, ia, -ia);
@@ -116,7 +119,7 @@ __device__ __forceinline__ float zoh_input_scale(float abar, float t, float dt, 
     constexpr float c1 = kLn2 / 2.0f;                       // ln2 / 2!
     constexpr float c2 = kLn2 * kLn2 / 6.0f;                // ln2^2 / 3!
     constexpr float c3 = kLn2 * kLn2 * kLn2 / 24.0f;        // ln2^3 / 4!
-    constexpr float kSmallT = 0.0625f / kLn2;               // |z| < 1/16
+    constexpr float kSmallT = kZohSeriesT;
     float q = fmaf(t, c3, c2);
     q = fmaf(q, t, c1);
     const float ser = fmaf(dt * t, q, dt);

@@ -25,6 +25,7 @@ struct ScanParams {
   int64_t nseg;            // number of segments (1: single pass)
   float* ws_h;             // [B, nseg, D, N]   (nseg > 1)
   float* ws_sum;           // [B, nseg, D]      (nseg > 1)
+  int* ws_neg;             // [B, nseg, channel tiles]: a segment's tile saw Delta < 0 (nseg > 1)
   // causal convolution in front of the scan (prefill); conv_w == nullptr: none
   const float* conv_w;     // [D, conv_W], conv_w[d, W-1] on the newest input
   const float* conv_b;     // nullable [D]
@@ -33,8 +34,17 @@ struct ScanParams {
   int conv_W;              // 1 .. 4
 };
 
-// Workspace bytes for a plan with nseg segments (0 when nseg == 1).
+// Channels per workgroup of the forward scan kernels for state size N.
+int64_t scan_channels_per_tile(int64_t N);
+
+// Workspace bytes for a plan with nseg segments (0 when nseg == 1): ws_h, ws_sum, ws_neg.
 size_t scan_workspace_bytes(int64_t B, int64_t D, int64_t N, int64_t nseg);
+
+// After the segment pass of a plan with nseg >= 2 (ws_h = local end states, ws_sum, ws_neg):
+// the carry scan over segments (ws_h then holds the state entering each segment, h_last the
+// final state) and the output correction of segments 1 .. nseg-1. ch_tile = channels per
+// workgroup of the segment pass (the granularity of ws_neg).
+hipError_t launch_scan_segment_fix(const ScanParams& p, int ch_tile, hipStream_t stream);
 
 // Enqueue the scan (one to three kernels) on the stream. Returns hipSuccess or the launch error.
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream);

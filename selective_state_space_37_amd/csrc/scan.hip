@@ -24,10 +24,14 @@
 //     gate, round and store y with coalesced row stores.
 //   * padded tokens (ragged L tail) are committed with Delta = 0, x = 0 and B = C = 0, which
 //     makes the step the identity.
-// Long, narrow inputs (few channel tiles) are cut into L-segments: a state-only pass gives each
-// segment's local end state and sum of Delta; a carry pass runs the segment recurrence
-// h_in[s+1] = exp(A sum Delta_s) h_in[s] + h_loc[s]; the full pass then starts every segment
-// from its carry. Segments exchange nothing but the state, as the pages' chunked view says.
+// Long, narrow inputs (few channel tiles) are cut into L-segments that run side by side. Every
+// segment after the first starts from the zero state (the first from h0); besides its outputs
+// it leaves its local end state h_loc and its sum of Delta. The state entering a segment then
+// follows from the affine segment maps h -> exp(A sum Delta_s) h + h_loc[s] (an associative scan
+// over segments), and the part of each output that the entering state contributes,
+// C_t . exp(A S_t) h_in (S_t = sum of Delta from the segment start through t), is added
+// afterwards for the tokens where that decay is still visible (scan_seg.hip). Segments exchange
+// nothing but the state, as the pages' chunked view says.
 #include <type_traits>
 
 #include "device_common.h"
@@ -37,15 +41,41 @@ namespace ssm {
 
 namespace {
 
-template <int CH, int NS, int KS, int T, int N>
+template <int CH, int NS, int KS, int T, int N, int GW>
 struct ScanCfg {
   static_assert(NS * KS == N, "slices must cover the state");
   static_assert(T % KS == 0, "post-processing splits a tile's tokens over the slices");
   static constexpr int kThreads = CH * KS;
-  static constexpr int kGroups = T * (CH / 4);                      // 4-channel groups per tensor
+  static constexpr int kGroups = T * (CH / GW);                     // GW-channel groups per tensor
   static constexpr int kGroupsPerThr = (kGroups + kThreads - 1) / kThreads;
   static constexpr int kBC = T * N;                                  // B (and C) elements per tile
   static constexpr int kBCPerThr = (kBC + kThreads - 1) / kThreads;
+};
+
+// Raw storage bits of GW consecutive elements of io_t (kept unconverted while a load is in
+// flight), with a buffer load and the conversion to float.
+template <typename io_t, int GW> struct RawGroup;
+template <> struct RawGroup<bf16_t, 2> {
+  using type = uint32_t;
+  __device__ __forceinline__ static type zero() { return 0u; }
+  __device__ __forceinline__ static void load(Rsrc r, uint32_t off, type& v) {
+    v = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+  __device__ __forceinline__ static void unpack(type v, float* out) { out[0] = bf16_lo(v); out[1] = bf16_hi(v); }
+};
+template <> struct RawGroup<float, 2> {
+  using type = uint2;
+  __device__ __forceinline__ static type zero() { return make_uint2(0, 0); }
+  __device__ __forceinline__ static void load(Rsrc r, uint32_t off, type& v) { buf_load(r, off, v); }
+  __device__ __forceinline__ static void unpack(type v, float* out) {
+    out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
+  }
+};
+template <typename io_t> struct RawGroup<io_t, 4> {
+  using type = typename IoTraits<io_t>::raw4;
+  __device__ __forceinline__ static type zero() { return IoTraits<io_t>::zero4(); }
+  __device__ __forceinline__ static void load(Rsrc r, uint32_t off, type& v) { buf_load(r, off, v); }
+  __device__ __forceinline__ static void unpack(type v, float* out) { IoTraits<io_t>::unpack4(v, out); }
 };
 
 // 16-byte chunking of a tile's B (and C) block in storage type io_t.
@@ -61,21 +91,33 @@ struct BCChunks {
 // registers are allocated in blocks of 8 out of 512).
 // CONV: the SSM input is the causal depthwise convolution (width <= 4) of x, formed by the loader
 // (prefill in front of the decode step's convolution register).
-template <typename io_t, int CH, int NS, int KS, int T, int N, bool FULL, int OCC, bool CONV = false>
+// SEG (with FULL): one segment of a multi-segment plan: segments after the first start from the
+// zero state; the local end state, the segment's sum of Delta and whether any Delta was negative
+// go to the workspace (the final state is the carry pass's).
+template <typename io_t, int CH, int NS, int KS, int T, int N, bool FULL, int OCC, bool CONV = false,
+          bool SEG = false>
 __global__ __launch_bounds__(CH * KS)
 void scan_kernel(ScanParams p) {
-  using Cfg = ScanCfg<CH, NS, KS, T, N>;
+  static_assert(FULL || !SEG, "the segment variant is a full pass");
+  // Loader groups: GW consecutive channels of one token row per thread and tensor. Two spread
+  // the loading and its conversion over every thread of the workgroup (all waves reach the tile
+  // barrier with the same work); the convolution variant keeps groups of four, whose three halo
+  // rows it also loads.
+  constexpr int GW = CONV ? 4 : 2;
+  using Cfg = ScanCfg<CH, NS, KS, T, N, GW>;
   using Io = IoTraits<io_t>;
   using raw4 = typename Io::raw4;
-  static_assert(Cfg::kThreads % (CH / 4) == 0, "a thread always loads the same channel group");
+  using RG = RawGroup<io_t, GW>;
+  using rawg = typename RG::type;
+  static_assert(Cfg::kThreads % (CH / GW) == 0, "a thread always loads the same channel group");
 
   __shared__ __attribute__((aligned(16))) float2 s_dx[2][T][CH];          // (Delta, x)
-  __shared__ __attribute__((aligned(16))) raw4 s_z[FULL ? 2 : 1][FULL ? T : 1][CH / 4];
+  __shared__ __attribute__((aligned(16))) rawg s_z[FULL ? 2 : 1][FULL ? T : 1][CH / GW];
   __shared__ __attribute__((aligned(16))) float s_bc[2][T][N][2];          // (B_n, C_n)
   // partial readouts per slice; at CH = 32 a wave holds two slices, whose rows are offset by 32
   // banks so their writes do not collide
   // (only when the padding still lets OCC workgroups share a CU's 160 KB of LDS)
-  constexpr int kLdsUnpadded = 2 * T * CH * 8 + (FULL ? 2 * T * (CH / 4) * (int)sizeof(raw4) : 16) +
+  constexpr int kLdsUnpadded = 2 * T * CH * 8 + (FULL ? 2 * T * (CH / GW) * (int)sizeof(rawg) : 16) +
                                2 * T * N * 8 + (FULL ? KS * T * CH * 4 : 4) +
                                (CONV ? CH * 16 + CH * 4 + 3 * CH * 4 + CH * 4 : 0);
   constexpr bool kPadY = FULL && CH < 64 && kLdsUnpadded + KS * 32 * 4 <= 163840 / OCC;
@@ -122,20 +164,28 @@ void scan_kernel(ScanParams p) {
   const io_t* __restrict__ Cg = static_cast<const io_t*>(p.Cm);
   const bool has_z = FULL && (zg != nullptr);
 
-  // ---- loader: this thread always handles channel group tid % (CH / 4)
-  const int cg = tid % (CH / 4);
-  const int64_t cgl = c0 + 4 * cg;
+  // ---- loader: this thread always handles channel group tid % (CH / GW)
+  const int cg = tid % (CH / GW);
+  const int64_t cgl = c0 + GW * cg;
   const bool cg_ok = cgl < D;  // D % 4 == 0: a group is wholly in or out
   // (the convolution variant keeps the step-size bias in LDS instead: registers for its halo rows)
-  float bias4[4] = {0.f, 0.f, 0.f, 0.f};
+  float biasg[GW];
+#pragma unroll
+  for (int k = 0; k < GW; ++k) biasg[k] = 0.f;
   if (!CONV && p.delta_bias && cg_ok)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) bias4[k] = p.delta_bias[cgl + k];
+    for (int k = 0; k < GW; ++k) biasg[k] = p.delta_bias[cgl + k];
 
-  // Raw load registers (zeroed once for the threads that load nothing; z stays zero without z)
-  raw4 rx[Cfg::kGroupsPerThr], rd[Cfg::kGroupsPerThr], rz[Cfg::kGroupsPerThr];
+  // segment variant: this thread's sum of the activated Delta of its channel group, and whether
+  // any was negative (rows past the segment end commit Delta = 0)
+  float dacc[SEG ? GW : 1];
 #pragma unroll
-  for (int k = 0; k < Cfg::kGroupsPerThr; ++k) rx[k] = rd[k] = rz[k] = Io::zero4();
+  for (int k = 0; k < (SEG ? GW : 1); ++k) dacc[k] = 0.f;
+  bool dneg = false;
+  // Raw load registers (zeroed once for the threads that load nothing; z stays zero without z)
+  rawg rx[Cfg::kGroupsPerThr], rd[Cfg::kGroupsPerThr], rz[Cfg::kGroupsPerThr];
+#pragma unroll
+  for (int k = 0; k < Cfg::kGroupsPerThr; ++k) rx[k] = rd[k] = rz[k] = RG::zero();
   // convolution: the x rows r-1 .. r-3 of each loaded row (lags 1..3) in registers; weights, bias
   // and the register entries before the sequence in LDS
   raw4 rxh[CONV ? Cfg::kGroupsPerThr : 1][3];
@@ -169,8 +219,19 @@ void scan_kernel(ScanParams p) {
   // past the segment end reads as whole zero chunks); otherwise element by element. Either way the
   // registers keep the raw storage bits until the tile is committed, so the loads of tile i+1
   // stay in flight while tile i runs.
+  // Outside the convolution variant, with N even, B and C move as element pairs instead, spread
+  // over the workgroup: slot s < T N / 2 is the pair 2s, 2s + 1 of B, the next T N / 2 slots those
+  // of C (a pair never straddles a row, so a row past the segment end reads as a zero pair).
   using BCC = BCChunks<io_t, T, N, Cfg::kThreads>;
-  constexpr bool kChunkBC = N * (int)sizeof(io_t) >= 16;
+  constexpr bool kPairBC = !CONV && N % 2 == 0;
+  constexpr int kBCPairs = T * N / 2;
+  constexpr int kBCSlots = FULL ? 2 * kBCPairs : kBCPairs;
+  constexpr int kBCSlotsPerThr = (kBCSlots + Cfg::kThreads - 1) / Cfg::kThreads;
+  using RP = RawGroup<io_t, 2>;
+  typename RP::type rbc[kPairBC ? kBCSlotsPerThr : 1];
+#pragma unroll
+  for (int k = 0; k < (kPairBC ? kBCSlotsPerThr : 1); ++k) rbc[k] = RP::zero();
+  constexpr bool kChunkBC = !kPairBC && N * (int)sizeof(io_t) >= 16;
   uint4 rbv = make_uint4(0, 0, 0, 0), rcv = make_uint4(0, 0, 0, 0);
   uint32_t rB[Cfg::kBCPerThr], rC[Cfg::kBCPerThr];
 #pragma unroll
@@ -186,7 +247,7 @@ void scan_kernel(ScanParams p) {
 #pragma unroll
   for (int k = 0; k < Cfg::kGroupsPerThr; ++k) {
     const int g = tid + k * Cfg::kThreads;
-    ld_boff[k] = (uint32_t)(((g / (CH / 4)) * D + 4 * cg) * (int64_t)sizeof(io_t));
+    ld_boff[k] = (uint32_t)(((g / (CH / GW)) * D + GW * cg) * (int64_t)sizeof(io_t));
   }
   // rows of the tile inside the segment (T on the full tiles)
   auto tile_rows = [&](int tile) __attribute__((always_inline)) {
@@ -210,9 +271,9 @@ void scan_kernel(ScanParams p) {
 #pragma unroll
     for (int k = 0; k < Cfg::kGroupsPerThr; ++k) {
       if (tid + k * Cfg::kThreads < Cfg::kGroups) {
-        buf_load(xr, ld_boff[k], rx[k]);
-        buf_load(dr, ld_boff[k], rd[k]);
-        if (has_z) buf_load(zr, ld_boff[k], rz[k]);
+        RG::load(xr, ld_boff[k], rx[k]);
+        RG::load(dr, ld_boff[k], rd[k]);
+        if (has_z) RG::load(zr, ld_boff[k], rz[k]);
       }
     }
     if constexpr (CONV) {
@@ -237,7 +298,16 @@ void scan_kernel(ScanParams p) {
     }
     const Rsrc br = tile_rsrc(Bg, N, 0, tile, rows);
     const Rsrc cr = tile_rsrc(Cg, N, 0, tile, rows);
-    if constexpr (kChunkBC) {
+    if constexpr (kPairBC) {
+#pragma unroll
+      for (int k = 0; k < kBCSlotsPerThr; ++k) {
+        const int sl = tid + k * Cfg::kThreads;
+        if (sl < kBCPairs)
+          RP::load(br, (uint32_t)(2 * sl * (int)sizeof(io_t)), rbc[k]);
+        else if (sl < kBCSlots)
+          RP::load(cr, (uint32_t)(2 * (sl - kBCPairs) * (int)sizeof(io_t)), rbc[k]);
+      }
+    } else if constexpr (kChunkBC) {
       if (tid < BCC::kChunks) {
         buf_load(br, (uint32_t)tid * 16u, rbv);
         if (FULL) buf_load(cr, (uint32_t)tid * 16u, rcv);
@@ -267,9 +337,9 @@ void scan_kernel(ScanParams p) {
     for (int k = 0; k < Cfg::kGroupsPerThr; ++k) {
       const int g = tid + k * Cfg::kThreads;
       if (g < Cfg::kGroups) {
-        const int r = g / (CH / 4);
-        float xv[4];
-        Io::unpack4(rx[k], xv);
+        const int r = g / (CH / GW);
+        float xv[GW];
+        RG::unpack(rx[k], xv);
         // (the convolution first: its halo registers are free before the step-size arithmetic)
         if constexpr (CONV) {
           // SSM input = bias + sum over lags j of w_j x_{t-j}; rows before the sequence come from
@@ -295,29 +365,49 @@ void scan_kernel(ScanParams p) {
             xv[q] = fmaf(w.w, xs[2][q], u);
           }
         }
-        float dv[4];
-        Io::unpack4(rd[k], dv);
-        float db[4] = {bias4[0], bias4[1], bias4[2], bias4[3]};
+        float dv[GW];
+        RG::unpack(rd[k], dv);
+        float db[GW];
+#pragma unroll
+        for (int q = 0; q < GW; ++q) db[q] = biasg[q];
         if constexpr (CONV) {
-          const float4 v = *reinterpret_cast<const float4*>(&s_db[4 * cg]);
-          db[0] = v.x; db[1] = v.y; db[2] = v.z; db[3] = v.w;
+#pragma unroll
+          for (int q = 0; q < GW; ++q) db[q] = s_db[GW * cg + q];
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < GW; ++q) {
           float u = dv[q] + db[q];   // zero without a bias
           if (p.delta_softplus) u = softplus_f32(u);
           dv[q] = (!RAGGED || r < rows) ? u : 0.f;
+          if constexpr (SEG) {
+            dacc[q] += dv[q];
+            dneg = dneg || dv[q] < 0.f;
+          }
         }
-        float4* dst = reinterpret_cast<float4*>(&s_dx[buf][r][4 * cg]);
-        dst[0] = make_float4(dv[0], xv[0], dv[1], xv[1]);
-        dst[1] = make_float4(dv[2], xv[2], dv[3], xv[3]);
+        float4* dst = reinterpret_cast<float4*>(&s_dx[buf][r][GW * cg]);
+#pragma unroll
+        for (int q = 0; q < GW / 2; ++q) dst[q] = make_float4(dv[2 * q], xv[2 * q], dv[2 * q + 1], xv[2 * q + 1]);
         if (has_z) s_z[buf][r][cg] = rz[k];
       }
     }
   };
   // B and C: rows past the segment end were loaded as zeros, so both tile kinds commit alike
   auto commit_bc = [&](int buf) __attribute__((always_inline)) {
-    if constexpr (kChunkBC) {
+    if constexpr (kPairBC) {
+#pragma unroll
+      for (int k = 0; k < kBCSlotsPerThr; ++k) {
+        const int sl = tid + k * Cfg::kThreads;
+        if (sl < kBCSlots) {
+          const int which = sl < kBCPairs ? 0 : 1;            // B or C
+          const int e = 2 * (sl - which * kBCPairs);           // first element of the pair
+          float v[2];
+          RP::unpack(rbc[k], v);
+          float* bc = &s_bc[buf][0][0][0] + 2 * e + which;      // (B_n, C_n) interleaved
+          bc[0] = v[0];
+          bc[2] = v[1];
+        }
+      }
+    } else if constexpr (kChunkBC) {
       if (tid < BCC::kChunks) {
         // kPerChunk consecutive (B, C) elements -> interleaved (B_n, C_n) pairs
         float bv[BCC::kPerChunk], cv[BCC::kPerChunk];
@@ -362,22 +452,23 @@ void scan_kernel(ScanParams p) {
   const bool c_ok = c < D;
   const int n0 = slice * NS;
   float a2[NS], ia[NS], h[NS];
+  float amin = INFINITY;
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const float a = c_ok ? p.A[c * N + n0 + j] : -1.0f;
     a2[j] = a * kLog2e;
     ia[j] = 1.0f / a;
     h[j] = 0.f;
+    amin = fminf(amin, fabsf(a2[j]));
   }
-  if (FULL && c_ok) {
-    const float* hin = nullptr;
-    if (p.nseg > 1)
-      hin = p.ws_h + ((b * p.nseg + seg) * D + c) * N + n0;
-    else if (p.h0)
-      hin = p.h0 + (b * D + c) * N + n0;
-    if (hin)
+  // |Delta| below this puts some state of the lane under the series bound |Delta a2| < kZohSeriesT
+  // (with a margin against rounding; a lane with a zero a2 always qualifies)
+  const float series_dmax = kZohSeriesT * 1.01f / amin;
+  // the sequence's first segment starts from h0, later segments of a segmented plan from zero
+  if (FULL && c_ok && p.h0 && (!SEG || seg == 0)) {
+    const float* hin = p.h0 + (b * D + c) * N + n0;
 #pragma unroll
-      for (int j = 0; j < NS; ++j) h[j] = hin[j];
+    for (int j = 0; j < NS; ++j) h[j] = hin[j];
   }
   float dsum = 0.f;
 
@@ -411,19 +502,36 @@ void scan_kernel(ScanParams p) {
 #pragma unroll
     for (int t0 = 0; t0 < T; t0 += PH) {
       float abar_t[PH][NS], u_t[PH][NS];
+      auto phase1 = [&](auto accurate_tag) __attribute__((always_inline)) {
+        constexpr bool ACCURATE = decltype(accurate_tag)::value;
 #pragma unroll
-      for (int i = 0; i < PH; ++i) {
-        const float2 dx = s_dx[buf][t0 + i][chl];
-        const float* bc = &s_bc[buf][t0 + i][n0][0];
+        for (int i = 0; i < PH; ++i) {
+          const float2 dx = s_dx[buf][t0 + i][chl];
+          const float* bc = &s_bc[buf][t0 + i][n0][0];
 #pragma unroll
-        for (int j = 0; j < NS; ++j) {
-          const float tx = dx.x * a2[j];
-          const float abar = exp2_fast(tx);
-          abar_t[i][j] = abar;
-          // expm1(Delta a)/a B x
-          u_t[i][j] = zoh_input_scale<std::is_same<io_t, float>::value>(abar, tx, dx.x, ia[j]) * (bc[2 * j] * dx.y);
+          for (int j = 0; j < NS; ++j) {
+            const float tx = dx.x * a2[j];
+            const float abar = exp2_fast(tx);
+            abar_t[i][j] = abar;
+            // expm1(Delta a)/a B x
+            u_t[i][j] = zoh_input_scale<ACCURATE>(abar, tx, dx.x, ia[j]) * (bc[2 * j] * dx.y);
+          }
+          if (!FULL) dsum += dx.x;
         }
-        if (!FULL) dsum += dx.x;
+      };
+      if constexpr (std::is_same<io_t, float>::value) {
+        // float32 I/O: the series of the input scale only where some state of the wave has
+        // |Delta a| < 1/16 in the sub-tile (a uniform branch; the per-state choice is still made
+        // inside), else the plain form
+        float dmin = fabsf(s_dx[buf][t0][chl].x);
+#pragma unroll
+        for (int i = 1; i < PH; ++i) dmin = fminf(dmin, fabsf(s_dx[buf][t0 + i][chl].x));
+        if (__any(!(dmin >= series_dmax) ? 1 : 0))
+          phase1(std::true_type{});
+        else
+          phase1(std::false_type{});
+      } else {
+        phase1(std::false_type{});
       }
 #pragma unroll
       for (int i = 0; i < PH; ++i) {
@@ -469,9 +577,40 @@ void scan_kernel(ScanParams p) {
     __syncthreads();
   }
 
+  if constexpr (SEG) {
+    // the segment's sum of Delta per channel: the loader threads of a channel group hold partial
+    // sums over their rows (the tile buffers are free after the loop's last barrier)
+    // (flags beside them; the readers of a channel are the first CH threads, all in wave 0)
+    static_assert(KS * kYStride >= Cfg::kThreads * (GW + 1), "the partial sums fit the readout buffer");
+    static_assert(CH <= 64, "the channel readers form one wave");
+    float* s_red = &s_y[0][0];
+    float* s_neg = s_red + Cfg::kThreads * GW;
+#pragma unroll
+    for (int q = 0; q < GW; ++q) s_red[tid * GW + q] = dacc[q];
+    s_neg[tid] = dneg ? 1.f : 0.f;
+    __syncthreads();
+    if (tid < CH) {
+      const int g0 = tid / GW, q = tid % GW;
+      float s = 0.f;
+      bool neg = false;
+      for (int j = g0; j < Cfg::kThreads; j += CH / GW) {
+        s += s_red[j * GW + q];
+        neg = neg || s_neg[j] != 0.f;
+      }
+      if (c0 + tid < D) p.ws_sum[(b * p.nseg + seg) * D + c0 + tid] = s;
+      const bool any_neg = __any(neg ? 1 : 0);
+      if (tid == 0) p.ws_neg[(b * p.nseg + seg) * (int64_t)gridDim.x + tile] = any_neg ? 1 : 0;
+    }
+    if (c_ok) {
+      float* hl = p.ws_h + ((b * p.nseg + seg) * D + c) * N + n0;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) hl[j] = h[j];
+    }
+    return;
+  }
   if (!c_ok) return;
   if (FULL) {
-    if (p.h_last && seg == p.nseg - 1) {
+    if (p.h_last) {
       float* hl = p.h_last + (b * D + c) * N + n0;
 #pragma unroll
       for (int j = 0; j < NS; ++j) hl[j] = h[j];
@@ -535,14 +674,14 @@ hipError_t launch_typed(const ScanParams& p, hipStream_t stream) {
   constexpr int T = 16;
   const dim3 block(CH * KS);
   const unsigned gx = (unsigned)((p.D + CH - 1) / CH);
-  if (p.nseg > 1) {
-    const dim3 grid_a(gx, (unsigned)p.B, (unsigned)(p.nseg - 1));
-    hipLaunchKernelGGL((scan_kernel<io_t, CH, NS, KS, T, N, false, OCC, CONV>), grid_a, block, 0, stream, p);
-    const int64_t chains = p.B * p.D * p.N;
-    hipLaunchKernelGGL(scan_carry_kernel, dim3((unsigned)((chains + 255) / 256)), dim3(256), 0, stream, p);
-  }
   const dim3 grid(gx, (unsigned)p.B, (unsigned)p.nseg);
-  hipLaunchKernelGGL((scan_kernel<io_t, CH, NS, KS, T, N, true, OCC, CONV>), grid, block, 0, stream, p);
+  if (p.nseg > 1) {
+    hipLaunchKernelGGL((scan_kernel<io_t, CH, NS, KS, T, N, true, OCC, CONV, true>), grid, block, 0, stream, p);
+    const hipError_t e = launch_scan_segment_fix(p, CH, stream);
+    if (e != hipSuccess) return e;
+  } else {
+    hipLaunchKernelGGL((scan_kernel<io_t, CH, NS, KS, T, N, true, OCC, CONV>), grid, block, 0, stream, p);
+  }
   if (CONV && p.conv_out) {
     const int64_t n = p.B * p.D;
     hipLaunchKernelGGL(conv_register_kernel<io_t>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p);
@@ -590,9 +729,13 @@ hipError_t launch_io(const ScanParams& p, hipStream_t stream) {
 
 }  // namespace
 
+int64_t scan_channels_per_tile(int64_t N) { return N >= 8 ? 32 : 64; }
+
 size_t scan_workspace_bytes(int64_t B, int64_t D, int64_t N, int64_t nseg) {
   if (nseg <= 1) return 0;
-  return (size_t)(B * nseg * D * N) * sizeof(float) + (size_t)(B * nseg * D) * sizeof(float) + 256;
+  const int64_t tiles = (D + scan_channels_per_tile(N) - 1) / scan_channels_per_tile(N);
+  return (size_t)(B * nseg * D * N) * sizeof(float) + (size_t)(B * nseg * D) * sizeof(float) +
+         (size_t)(B * nseg * tiles) * sizeof(int) + 256;
 }
 
 hipError_t launch_scan(const ScanParams& p, hipStream_t stream) {

@@ -69,6 +69,7 @@ def scan_call(lib, B=1, L=16, D=64, N=16, io=F32, x=A_, delta=2 * A_, bias=None,
     (dict(h0=8 * A_, h_last=8 * A_ + 16), INVALID),   # partial state overlap
     (dict(segment_len=0), INVALID),
     (dict(D=(1 << 24) + 4), UNSUPPORTED),            # beyond the 32-bit tile offsets
+    (dict(B=65536, L=1, D=4, N=1), UNSUPPORTED),      # beyond the launch grid's batch dimension
     (dict(L=4096, D=256, segment_len=256), WS_SMALL),
     (dict(L=4096, D=256, segment_len=256, ws=9 * A_, wsb=100), WS_SMALL),
 ])

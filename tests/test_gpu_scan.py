@@ -87,6 +87,51 @@ def test_segmented_plan_small_states(N, dtype, seg):
     assert err <= gu.TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_segmented_correction_stops_early(dtype):
+    """Large steps (0.05 .. 0.5): the entering state's part of the outputs falls below the
+    output precision a few hundred tokens into each 1024-token segment, where the correction
+    stops; outputs past that point and the final state still match the oracle."""
+    inp = inputs.scan_steps(31, 2, 4096, 96, 16, dtype, 0.05, 0.5, h0=True)
+    err = gu.scan_parity(inp, gu.scan_on_gpu(inp, segment_len=1024))
+    print(dtype, "err", err)
+    assert err <= gu.TOL[dtype]
+
+
+def test_segmented_negative_steps():
+    """Negative step sizes (no softplus) in some channels of one segment: the state can grow
+    again along a segment, so those channels' correction runs to the segment end."""
+    inp = inputs.scan_steps(32, 1, 3000, 136, 16, "f32", 0.05, 0.5, h0=True)
+    d = inp.delta.copy()
+    d[0, 1500:1520, 3:40] = -0.02
+    inp.delta = d
+    err = gu.scan_parity(inp, gu.scan_on_gpu(inp, segment_len=512))
+    print("err", err)
+    assert err <= gu.TOL["f32"]
+
+
+def test_segmented_slow_state():
+    """One state per channel that barely decays (A = -1e-4): its entering value stays visible
+    over the whole segment, so the correction never stops early."""
+    inp = inputs.scan_steps(33, 1, 2048, 64, 16, "f32", 0.01, 0.1, A_kind="random", h0=True)
+    A = inp.A.copy()
+    A[:, 5] = -1e-4
+    inp.A = A
+    err = gu.scan_parity(inp, gu.scan_on_gpu(inp, segment_len=400))
+    print("err", err)
+    assert err <= gu.TOL["f32"]
+
+
+def test_segmented_zero_entering_state():
+    """x = 0 and no h0: every entering state is zero and the correction adds nothing."""
+    inp = _case(seed=34, Bsz=1, L=700, D=64)
+    inp.x = np.zeros_like(inp.x)
+    y, hl = gu.scan_on_gpu(inp, segment_len=160)
+    ry, rh = gu.scan_oracle(inp)
+    assert np.abs(y).max() == 0.0 and np.abs(ry).max() == 0.0
+    assert np.abs(hl).max() == 0.0
+
+
 def test_split_handoff_matches_whole():
     inp = _case(seed=24, Bsz=1, L=300, D=64, h0=True)
     y, hl = gu.scan_on_gpu(inp)

@@ -44,8 +44,10 @@ namespace {
 // whose exponent is at most 64 (it is a2 (S_i - S_e) <= 64 when the floor is not hit, and
 // a2 (S_i - S_j) + 64 <= 64 when it is, since S_i >= S_j). So every mask entry is G_ij times a
 // bounded factor, with the causal cut j <= i on the diagonal tile.
+constexpr int kOutWaves = 8;   // waves per output workgroup
+
 template <int Q, int N>
-__global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
+__global__ __launch_bounds__(64 * kOutWaves) void ssd_out_kernel(SsdParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 Xt[kP * (Q + 8)];
   // the carried-in state h_{c-1} (P x N bf16), staged once for the four waves; rows padded by
   // 8 elements so a wave's 16-byte fragment reads (16 rows apart by one row) hit 64 banks
@@ -57,12 +59,22 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
   const int tid = threadIdx.x;
   const float2* sp = p.ws_sphi + ((b * nch + c) * p.H + h) * Q;
   if (tid < Q) sS[tid] = sp[tid].x;
-  stage_x_transposed_scaled<Q>(p, b, c, h, Xt, sp, a2);
   {
+    // the carried state's loads are issued first, to be in flight during the x staging
+    constexpr int kNT = 64 * kOutWaves, kHPer = kP * N / 8 / kNT;
+    static_assert((kP * N / 8) % kNT == 0, "the state's 16-byte pieces divide over the threads");
     const bf16_t* hin = static_cast<const bf16_t*>(p.ws_hin) + ((b * nch + c) * p.H + h) * (int64_t)(kP * N);
-    for (int e = tid; e < kP * N / 8; e += blockDim.x) {   // 16-byte pieces
-      const int row = e / (N / 8), c8 = (e % (N / 8)) * 8;
-      *reinterpret_cast<uint4*>(&Hs[row * (N + 8) + c8]) = *reinterpret_cast<const uint4*>(hin + row * N + c8);
+    uint4 hv[kHPer];
+#pragma unroll
+    for (int k = 0; k < kHPer; ++k) {
+      const int e = tid + k * kNT, row = e / (N / 8), c8 = (e % (N / 8)) * 8;
+      hv[k] = *reinterpret_cast<const uint4*>(hin + row * N + c8);
+    }
+    stage_x_transposed_scaled<Q, kNT>(p, b, c, h, Xt, sp, a2);
+#pragma unroll
+    for (int k = 0; k < kHPer; ++k) {
+      const int e = tid + k * kNT, row = e / (N / 8), c8 = (e % (N / 8)) * 8;
+      *reinterpret_cast<uint4*>(&Hs[row * (N + 8) + c8]) = hv[k];
     }
   }
   __syncthreads();
@@ -80,21 +92,19 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
   bf16_t* yg = static_cast<bf16_t*>(p.y);
 
   // Balanced triangle: block x and block NIB-1-x hold NIB+1 tiles together.
-  constexpr int kBlocksPerWave = NIB >= 8 ? NIB / 4 : 1;
+  constexpr int kBlocksPerWave = NIB >= 2 * kOutWaves ? NIB / kOutWaves : 1;
   auto block_of = [&](int kb) {
-    if (NIB < 8) return w;
-    const int pair = w + 4 * (kb >> 1);
+    if (NIB < 2 * kOutWaves) return w;
+    const int pair = w + kOutWaves * (kb >> 1);
     return (kb & 1) ? (NIB - 1 - pair) : pair;
   };
   // carried-state fragments (the A operand of the carried term), the same for every row block;
   // every product here is computed transposed (channels x tokens) so a lane ends up holding four
   // consecutive channels of one token
-  bf16x8 hf[KS][4];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
-      hf[ks][pt] = *reinterpret_cast<const bf16x8*>(&Hs[(pt * 16 + r16) * (N + 8) + ks * 32 + 8 * g]);
+  // (read from LDS at each use: kept in registers they would cost 16 KN / 8 VGPRs per lane)
+  auto hfrag = [&](int ks, int pt) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(&Hs[(pt * 16 + r16) * (N + 8) + ks * 32 + 8 * g]);
+  };
   auto load_c = [&](int ib, bf16x8 out[KS]) {
     const int64_t ti = c * Q + ib * 16 + r16;
 #pragma unroll
@@ -102,7 +112,7 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
       out[ks] = ti < p.L ? load_frag(Cg + ti * rs + ks * 32 + 8 * g) : zero_frag();
   };
   bf16x8 cnext[KS];
-  if (NIB >= 4 || w < NIB) load_c(block_of(0), cnext);
+  if (NIB >= kOutWaves || w < NIB) load_c(block_of(0), cnext);
   // fully unrolled: the C fragments loaded one block ahead are then renamed, not copied (a copy
   // of registers with loads in flight would wait for them at the end of the previous block)
 #pragma unroll
@@ -131,7 +141,7 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) av[q] = (__bf16)((float)cf[ks][q] * eSi);
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16(hf[ks][pt], av, acc[pt]);
+        for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16(hfrag(ks, pt), av, acc[pt]);
       }
     }
 
@@ -140,14 +150,22 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
     auto load_g = [&](int jt) {
       return jt <= ib ? *reinterpret_cast<const uint2*>(Grow + jt * 16 + 4 * g) : make_uint2(0, 0);
     };
-    // fully unrolled (at most NIB / 2 pairs, leaving at the diagonal): the pair prefetched one
-    // step ahead is renamed rather than copied, so its loads overlap the current pair's work
-    uint2 gcur[2] = {load_g(0), load_g(1)}, gnext[2];
+    // fully unrolled (at most NIB / 2 pairs, leaving at the diagonal): the G tiles are requested
+    // kGPairs pairs ahead into registers named by tile, so several tiles' loads are in flight
+    // while the current pair is processed
+    constexpr int kGPairs = 4;
+    uint2 gt[NIB + 2];
+#pragma unroll
+    for (int t = 0; t < 2 * kGPairs && t < NIB; ++t) gt[t] = load_g(t);
 #pragma unroll
     for (int jp = 0; jp < (NIB + 1) / 2; ++jp) {
       if (2 * jp > ib) break;   // uniform (ib is a scalar)
-      gnext[0] = load_g(2 * jp + 2);
-      gnext[1] = load_g(2 * jp + 3);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int t = 2 * (jp + kGPairs) + u;
+        if (t < NIB) gt[t] = load_g(t);
+      }
+      const uint2 gcur[2] = {gt[2 * jp], 2 * jp + 1 < NIB ? gt[2 * jp + 1] : make_uint2(0, 0)};
       float m[8];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -184,8 +202,6 @@ __global__ __launch_bounds__(256) void ssd_out_kernel(SsdParams p) {
         const uint4 pk = make_uint4(lo.x, lo.y, hi.x, hi.y);
         acc[pt] = mfma16(__builtin_bit_cast(bf16x8, pk), av, acc[pt]);
       }
-      gcur[0] = gnext[0];
-      gcur[1] = gnext[1];
     }
 
     // epilogue: D term, gate, store. acc[pt][r] = y[i0 + r16][pt * 16 + 4 g + r], so each lane
@@ -233,7 +249,7 @@ hipError_t launch_qn(const SsdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((ssd_prep_kernel<Q, N>), dim3(4, (unsigned)nch, (unsigned)(p.B * p.G)), dim3(256), 0, stream,
                      p);
   hipLaunchKernelGGL((ssd_state_kernel<Q, N>), dim3((unsigned)p.H, (unsigned)p.B), dim3(512), 0, stream, p);
-  hipLaunchKernelGGL((ssd_out_kernel<Q, N>), dim3((unsigned)p.H, (unsigned)nch, (unsigned)p.B), dim3(256), 0,
+  hipLaunchKernelGGL((ssd_out_kernel<Q, N>), dim3((unsigned)p.H, (unsigned)nch, (unsigned)p.B), dim3(64 * kOutWaves), 0,
                      stream, p);
   return hipGetLastError();
 }

@@ -85,30 +85,44 @@ constexpr float kSsdStageExpFloor = -64.0f;
 // floored factor out of each entry. Each thread takes two consecutive tokens, so every LDS write
 // is one 32-bit word holding the pair (j, j + 1) of one channel; the scaled values are rounded to
 // bf16 once. Tokens past L are staged as zeros.
-template <int Q>
+template <int Q, int NT>
 __device__ void stage_x_transposed_scaled(const SsdParams& p, int64_t b, int64_t c, int64_t h, __bf16* Xt,
                                           const float2* sp, float a2) {
+  // NT threads; every thread's loads are issued before any is used (one memory latency per stage)
+  constexpr int kItems = (Q / 2) * (kP / 8);
+  constexpr int kPer = (kItems + NT - 1) / NT;
+  static_assert(kItems % NT == 0 || kItems < NT, "the items divide over the threads");
   const bf16_t* xg = static_cast<const bf16_t*>(p.x);
   uint32_t* X32 = reinterpret_cast<uint32_t*>(Xt);
-  for (int g = threadIdx.x; g < (Q / 2) * (kP / 8); g += blockDim.x) {
+  uint4 r0[kPer], r1[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int g = threadIdx.x + k * NT;
     const int jp = g / (kP / 8), pg = g % (kP / 8);
     const int64_t t = c * Q + 2 * jp;
-    uint4 r0 = make_uint4(0, 0, 0, 0), r1 = r0;
-    if (t < p.L) r0 = *reinterpret_cast<const uint4*>(xg + ((b * p.L + t) * p.H + h) * kP + pg * 8);
-    if (t + 1 < p.L) r1 = *reinterpret_cast<const uint4*>(xg + ((b * p.L + t + 1) * p.H + h) * kP + pg * 8);
+    r0[k] = r1[k] = make_uint4(0, 0, 0, 0);
+    if (g >= kItems) continue;
+    if (t < p.L) r0[k] = *reinterpret_cast<const uint4*>(xg + ((b * p.L + t) * p.H + h) * kP + pg * 8);
+    if (t + 1 < p.L) r1[k] = *reinterpret_cast<const uint4*>(xg + ((b * p.L + t + 1) * p.H + h) * kP + pg * 8);
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int g = threadIdx.x + k * NT;
+    if (g >= kItems) continue;
+    const int jp = g / (kP / 8), pg = g % (kP / 8);
     const float2 v0 = sp[2 * jp], v1 = sp[2 * jp + 1];
     const float se = sp[(2 * jp) | 15].x;
     const float cp0 = exp2_fast(fmaxf(a2 * (se - v0.x), kSsdStageExpFloor)) * v0.y;
     const float cp1 = exp2_fast(fmaxf(a2 * (se - v1.x), kSsdStageExpFloor)) * v1.y;
-    const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w}, w1[4] = {r1.x, r1.y, r1.z, r1.w};
+    const uint32_t w0[4] = {r0[k].x, r0[k].y, r0[k].z, r0[k].w}, w1[4] = {r1[k].x, r1[k].y, r1[k].z, r1[k].w};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      // channels 2k (low halves) and 2k+1 (high halves) of the two tokens
-      const int ra = pg * 8 + 2 * k, rb = ra + 1;
+    for (int q = 0; q < 4; ++q) {
+      // channels 2q (low halves) and 2q+1 (high halves) of the two tokens
+      const int ra = pg * 8 + 2 * q, rb = ra + 1;
       X32[ra * ((Q + 8) / 2) + (jp ^ xt_swizzle_words<Q>(ra))] =
-          (uint32_t)f32_to_bf16(bf16_lo(w0[k]) * cp0) | ((uint32_t)f32_to_bf16(bf16_lo(w1[k]) * cp1) << 16);
+          (uint32_t)f32_to_bf16(bf16_lo(w0[q]) * cp0) | ((uint32_t)f32_to_bf16(bf16_lo(w1[q]) * cp1) << 16);
       X32[rb * ((Q + 8) / 2) + (jp ^ xt_swizzle_words<Q>(rb))] =
-          (uint32_t)f32_to_bf16(bf16_hi(w0[k]) * cp0) | ((uint32_t)f32_to_bf16(bf16_hi(w1[k]) * cp1) << 16);
+          (uint32_t)f32_to_bf16(bf16_hi(w0[q]) * cp0) | ((uint32_t)f32_to_bf16(bf16_hi(w1[q]) * cp1) << 16);
     }
   }
 }

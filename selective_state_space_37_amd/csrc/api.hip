@@ -69,9 +69,19 @@ ssm_status scratch_for_current_device(void** out) {
   return SSM_OK;
 }
 
-size_t io_size(ssm_dtype t) { return t == SSM_BF16 ? 2 : 4; }
+// The bits of an enum argument as an int. A C caller may pass any value, and reading an
+// out-of-range value as the C++ enum type is undefined, so entry points take the bits first.
+template <typename E>
+int enum_bits(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
 
-bool valid_dtype(ssm_dtype t) { return t == SSM_F32 || t == SSM_BF16; }
+size_t io_size(int t) { return t == SSM_BF16 ? 2 : 4; }
+
+bool valid_dtype(int t) { return t == SSM_F32 || t == SSM_BF16; }
 
 // [p, p + bytes) overlaps [q, q + qbytes)?
 bool overlaps(const void* p, size_t bytes, const void* q, size_t qbytes) {
@@ -106,7 +116,7 @@ int64_t auto_segment_len(int64_t B, int64_t L, int64_t D, int64_t N) {
 
 int64_t num_segments(int64_t L, int64_t seg_len) { return seg_len >= L ? 1 : (L + seg_len - 1) / seg_len; }
 
-ssm_status scan_common(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io, const void* x,
+ssm_status scan_common(int64_t B, int64_t L, int64_t D, int64_t N, int io, const void* x,
                        const void* delta, const float* delta_bias, int delta_softplus, const float* A,
                        const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
                        void* y, float* h_last, int64_t seg_len, void* ws, size_t ws_bytes, void* stream,
@@ -205,7 +215,7 @@ int64_t bwd_segment_len(int64_t L, int64_t seg_len) {
   return seg_len >= L ? L : seg_len;
 }
 
-ssm_status scan_bwd_common(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io, const void* x,
+ssm_status scan_bwd_common(int64_t B, int64_t L, int64_t D, int64_t N, int io, const void* x,
                            const void* delta, const float* delta_bias, int delta_softplus, const float* A,
                            const void* Bm, const void* Cm, const float* Dskip, const void* z,
                            const float* h0, const void* dy, const float* dh_last, void* dx, void* ddelta,
@@ -291,7 +301,11 @@ extern "C" {
 
 int ssm_abi_version(void) { return SSM_ABI_VERSION; }
 
-const char* ssm_status_string(ssm_status s) {
+const char* ssm_status_string(ssm_status status) {
+  // A C caller may pass any int; its bytes are read as an int (reading an out-of-range value as
+  // the enum type would be undefined in C++).
+  int s;
+  std::memcpy(&s, &status, sizeof s);
   switch (s) {
     case SSM_OK: return "SSM_OK";
     case SSM_ERR_INVALID_ARGUMENT: return "SSM_ERR_INVALID_ARGUMENT";
@@ -314,10 +328,11 @@ size_t ssm_scan_fwd_segmented_workspace_bytes(int64_t B, int64_t L, int64_t D, i
   return ssm::scan_workspace_bytes(B, D, N, num_segments(L, segment_len));
 }
 
-ssm_status ssm_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io, const void* x,
+ssm_status ssm_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io_arg, const void* x,
                         const void* delta, const float* delta_bias, int delta_softplus, const float* A,
                         const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
                         void* y, float* h_last, void* ws, size_t ws_bytes, void* stream) {
+  const int io = enum_bits(io_arg);
   const int64_t seg = (B > 0 && L > 0 && D > 0) ? auto_segment_len(B, L, D, N) : 1;
   return scan_common(B, L, D, N, io, x, delta, delta_bias, delta_softplus, A, Bm, Cm, Dskip, z, h0, y,
                      h_last, seg, ws, ws_bytes, stream);
@@ -330,12 +345,13 @@ size_t ssm_scan_fwd_conv_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_
   return ssm::scan_workspace_bytes(B, D, N, num_segments(L, seg));
 }
 
-ssm_status ssm_scan_fwd_conv(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io, const void* x,
+ssm_status ssm_scan_fwd_conv(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io_arg, const void* x,
                              const void* delta, const float* delta_bias, int delta_softplus, const float* A,
                              const void* Bm, const void* Cm, const float* Dskip, const void* z,
                              const float* h0, int64_t conv_width, const float* conv_w, const float* conv_b,
                              void* conv_state, void* y, float* h_last, int64_t segment_len, void* ws,
                              size_t ws_bytes, void* stream) {
+  const int io = enum_bits(io_arg);
   if (!conv_w) return fail(SSM_ERR_INVALID_ARGUMENT, "conv_w is NULL");
   if (segment_len < 0) return fail(SSM_ERR_INVALID_ARGUMENT, "segment_len=%lld must be >= 0", (long long)segment_len);
   // segments must start on 16-token tiles (the convolution reads the three rows before a tile)
@@ -345,20 +361,22 @@ ssm_status ssm_scan_fwd_conv(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dty
                      h_last, seg, ws, ws_bytes, stream, conv_width, conv_w, conv_b, conv_state);
 }
 
-ssm_status ssm_scan_fwd_noalloc(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io, const void* x,
+ssm_status ssm_scan_fwd_noalloc(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io_arg, const void* x,
                                 const void* delta, const float* delta_bias, int delta_softplus, const float* A,
                                 const void* Bm, const void* Cm, const float* Dskip, const void* z,
                                 const float* h0, void* y, float* h_last, void* stream) {
+  const int io = enum_bits(io_arg);
   const int64_t seg = (B > 0 && L > 0 && D > 0) ? auto_segment_len(B, L, D, N) : 1;
   return scan_common(B, L, D, N, io, x, delta, delta_bias, delta_softplus, A, Bm, Cm, Dskip, z, h0, y, h_last,
                      seg, nullptr, 0, stream, 0, nullptr, nullptr, nullptr, true);
 }
 
-ssm_status ssm_scan_fwd_segmented(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io, const void* x,
+ssm_status ssm_scan_fwd_segmented(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io_arg, const void* x,
                                   const void* delta, const float* delta_bias, int delta_softplus,
                                   const float* A, const void* Bm, const void* Cm, const float* Dskip,
                                   const void* z, const float* h0, void* y, float* h_last, int64_t segment_len,
                                   void* ws, size_t ws_bytes, void* stream) {
+  const int io = enum_bits(io_arg);
   return scan_common(B, L, D, N, io, x, delta, delta_bias, delta_softplus, A, Bm, Cm, Dskip, z, h0, y,
                      h_last, segment_len, ws, ws_bytes, stream);
 }
@@ -375,35 +393,38 @@ size_t ssm_scan_bwd_segmented_workspace_bytes(int64_t B, int64_t L, int64_t D, i
   return ssm::scan_bwd_workspace_bytes(B, L, D, N, num_segments(L, sl));
 }
 
-ssm_status ssm_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io, const void* x,
+ssm_status ssm_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io_arg, const void* x,
                         const void* delta, const float* delta_bias, int delta_softplus, const float* A,
                         const void* Bm, const void* Cm, const float* Dskip, const void* z, const float* h0,
                         const void* dy, const float* dh_last, void* dx, void* ddelta, float* dA, float* dBm,
                         float* dCm, float* dDskip, float* ddelta_bias, void* dz, float* dh0, void* ws,
                         size_t ws_bytes, void* stream) {
+  const int io = enum_bits(io_arg);
   const int64_t seg = (B > 0 && L > 0 && D > 0) ? auto_segment_len(B, L, D, N) : 1;
   return scan_bwd_common(B, L, D, N, io, x, delta, delta_bias, delta_softplus, A, Bm, Cm, Dskip, z, h0, dy,
                          dh_last, dx, ddelta, dA, dBm, dCm, dDskip, ddelta_bias, dz, dh0, seg, ws, ws_bytes,
                          stream);
 }
 
-ssm_status ssm_scan_bwd_segmented(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io, const void* x,
+ssm_status ssm_scan_bwd_segmented(int64_t B, int64_t L, int64_t D, int64_t N, ssm_dtype io_arg, const void* x,
                                   const void* delta, const float* delta_bias, int delta_softplus,
                                   const float* A, const void* Bm, const void* Cm, const float* Dskip,
                                   const void* z, const float* h0, const void* dy, const float* dh_last,
                                   void* dx, void* ddelta, float* dA, float* dBm, float* dCm, float* dDskip,
                                   float* ddelta_bias, void* dz, float* dh0, int64_t segment_len, void* ws,
                                   size_t ws_bytes, void* stream) {
+  const int io = enum_bits(io_arg);
   return scan_bwd_common(B, L, D, N, io, x, delta, delta_bias, delta_softplus, A, Bm, Cm, Dskip, z, h0, dy,
                          dh_last, dx, ddelta, dA, dBm, dCm, dDskip, ddelta_bias, dz, dh0, segment_len, ws,
                          ws_bytes, stream);
 }
 
-ssm_status ssm_state_update(int64_t B, int64_t D, int64_t N, int64_t W, ssm_dtype io, const void* x,
+ssm_status ssm_state_update(int64_t B, int64_t D, int64_t N, int64_t W, ssm_dtype io_arg, const void* x,
                             const void* delta, const float* delta_bias, int delta_softplus, const float* A,
                             const void* Bm, const void* Cm, const float* Dskip, const void* z,
                             void* conv_state, const float* conv_w, const float* conv_b, float* h, void* y,
                             void* stream) {
+  const int io = enum_bits(io_arg);
   if (B < 0) return fail(SSM_ERR_INVALID_ARGUMENT, "B=%lld must be >= 0", (long long)B);
   if (D < 1) return fail(SSM_ERR_INVALID_ARGUMENT, "D=%lld must be >= 1", (long long)D);
   if (!valid_dtype(io)) return fail(SSM_ERR_INVALID_ARGUMENT, "unknown io_dtype %d", (int)io);
@@ -555,7 +576,7 @@ size_t ssd_chunk_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P,
 namespace {
 
 ssm_status ssd_common(const char* fn, int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
-                      int64_t chunk, ssm_dtype io, const void* x, const void* delta, const float* delta_bias,
+                      int64_t chunk, int io, const void* x, const void* delta, const float* delta_bias,
                       int delta_softplus, const float* A, const void* Bm, const void* Cm, const float* Dskip,
                       int dskip_per_channel, const void* z, const float* h0, void* y, float* h_last, void* ws,
                       size_t ws_bytes, void* stream) {
@@ -614,29 +635,32 @@ ssm_status ssd_common(const char* fn, int64_t B, int64_t L, int64_t H, int64_t P
 
 extern "C" {
 
-ssm_status ssd_chunk_fwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t chunk, ssm_dtype io,
+ssm_status ssd_chunk_fwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t chunk, ssm_dtype io_arg,
                          const void* x, const void* delta, const float* delta_bias, int delta_softplus,
                          const float* A, const void* Bm, const void* Cm, const float* Dskip, const void* z,
                          const float* h0, void* y, float* h_last, void* ws, size_t ws_bytes, void* stream) {
+  const int io = enum_bits(io_arg);
   return ssd_common("ssd_chunk_fwd", B, L, H, P, N, 1, chunk, io, x, delta, delta_bias, delta_softplus, A, Bm, Cm,
                     Dskip, 0, z, h0, y, h_last, ws, ws_bytes, stream);
 }
 
 ssm_status ssd_chunk_fwd_grouped(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t chunk,
-                                 ssm_dtype io, const void* x, const void* delta, const float* delta_bias,
+                                 ssm_dtype io_arg, const void* x, const void* delta, const float* delta_bias,
                                  int delta_softplus, const float* A, const void* Bm, const void* Cm,
                                  const float* Dskip, int dskip_per_channel, const void* z, const float* h0, void* y,
                                  float* h_last, void* ws, size_t ws_bytes, void* stream) {
+  const int io = enum_bits(io_arg);
   return ssd_common("ssd_chunk_fwd_grouped", B, L, H, P, N, G, chunk, io, x, delta, delta_bias, delta_softplus, A,
                     Bm, Cm, Dskip, dskip_per_channel, z, h0, y, h_last, ws, ws_bytes, stream);
 }
 
-ssm_status ssd_chunk_bwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, ssm_dtype io,
+ssm_status ssd_chunk_bwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, ssm_dtype io_arg,
                          const void* x, const void* delta, const float* delta_bias, int delta_softplus,
                          const float* A, const void* Bm, const void* Cm, const float* Dskip, int dskip_per_channel,
                          const void* z, const float* h0, const void* dy, const float* dh_last, void* dx,
                          void* ddelta, float* dA, float* dBm, float* dCm, float* dDskip, float* ddelta_bias,
                          void* dz, float* dh0, void* ws, size_t ws_bytes, void* stream) {
+  const int io = enum_bits(io_arg);
   if (B < 0 || L < 0) return fail(SSM_ERR_INVALID_ARGUMENT, "B and L must be >= 0");
   if (H < 1) return fail(SSM_ERR_INVALID_ARGUMENT, "H=%lld must be >= 1", (long long)H);
   if (G < 1 || H % G != 0)

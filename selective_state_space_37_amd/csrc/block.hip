@@ -39,9 +39,12 @@ __device__ __forceinline__ bf16x8 zero8() {
   return v;
 }
 
+// Four floats rounded to bf16 (nearest even) as two words: one v_cvt_pk_bf16_f32 per pair.
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
-  return make_uint2((uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16),
-                    (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t)),
+                    __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){c, d}, bf16x2_t)));
 }
 
 // ---------------------------------------------------------------------------- LayerNorm

@@ -233,8 +233,8 @@ __global__ __launch_bounds__(64 * kOutWaves) void ssd_out_kernel(SsdParams p) {
           v[3] *= silu(bf16_hi(zr.y));
         }
         uint2 out;
-        out.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-        out.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        out.x = pack_bf16x2(v[0], v[1]);
+        out.y = pack_bf16x2(v[2], v[3]);
         *reinterpret_cast<uint2*>(yg + o) = out;
       }
     }

@@ -197,12 +197,12 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
 #pragma unroll
         for (int k = 0; k < 8; ++k)
           X32[(8 * pg8 + k) * (RS / 2) + ip] =
-              (uint32_t)f32_to_bf16(ph0 * xv0[k]) | ((uint32_t)f32_to_bf16(ph1 * xv1[k]) << 16);
+              pack_bf16x2(ph0 * xv0[k], ph1 * xv1[k]);
       }
       uint32_t* Y32 = reinterpret_cast<uint32_t*>(YT);
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        Y32[(8 * pg8 + k) * (RS / 2) + ip] = (uint32_t)f32_to_bf16(y0[k]) | ((uint32_t)f32_to_bf16(y1[k]) << 16);
+        Y32[(8 * pg8 + k) * (RS / 2) + ip] = pack_bf16x2(y0[k], y1[k]);
       float h0[8], h1[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -230,8 +230,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
         uint32_t* G32 = reinterpret_cast<uint32_t*>(GcT);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          H32[(8 * ng + k) * (RSP / 2) + pp] = (uint32_t)f32_to_bf16(h0v[k]) | ((uint32_t)f32_to_bf16(h1v[k]) << 16);
-          G32[(8 * ng + k) * (RSP / 2) + pp] = (uint32_t)f32_to_bf16(g0v[k]) | ((uint32_t)f32_to_bf16(g1v[k]) << 16);
+          H32[(8 * ng + k) * (RSP / 2) + pp] = pack_bf16x2(h0v[k], h1v[k]);
+          G32[(8 * ng + k) * (RSP / 2) + pp] = pack_bf16x2(g0v[k], g1v[k]);
           dot += h0v[k] * g0v[k] + h1v[k] * g1v[k];
         }
       }
@@ -451,8 +451,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
         }
         if (zh && lane_valid) {
           uint2 out;
-          out.x = (uint32_t)f32_to_bf16(dzv[0]) | ((uint32_t)f32_to_bf16(dzv[1]) << 16);
-          out.y = (uint32_t)f32_to_bf16(dzv[2]) | ((uint32_t)f32_to_bf16(dzv[3]) << 16);
+          out.x = pack_bf16x2(dzv[0], dzv[1]);
+          out.y = pack_bf16x2(dzv[2], dzv[3]);
           *reinterpret_cast<uint2*>(static_cast<bf16_t*>(bp.dz) + (b * L * H + h) * kP + o) = out;
         }
       }
@@ -525,8 +525,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
         }
         if (lane_valid) {
           uint2 out;
-          out.x = (uint32_t)f32_to_bf16(dxv[0]) | ((uint32_t)f32_to_bf16(dxv[1]) << 16);
-          out.y = (uint32_t)f32_to_bf16(dxv[2]) | ((uint32_t)f32_to_bf16(dxv[3]) << 16);
+          out.x = pack_bf16x2(dxv[0], dxv[1]);
+          out.y = pack_bf16x2(dxv[2], dxv[3]);
           *reinterpret_cast<uint2*>(static_cast<bf16_t*>(bp.dx) + (b * L * H + h) * kP + tl * tstride + pt * 16 + 4 * g) = out;
         }
       }

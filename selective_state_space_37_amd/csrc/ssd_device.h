@@ -25,6 +25,14 @@ __device__ __forceinline__ bf16x8 zero_frag() {
   return v;
 }
 
+// Two floats rounded to bf16 (nearest even) in one 32-bit word, lo in the low half: one
+// v_cvt_pk_bf16_f32 for the pair.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
 __device__ __forceinline__ bf16x8 load_frag(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
@@ -120,9 +128,9 @@ __device__ void stage_x_transposed_scaled(const SsdParams& p, int64_t b, int64_t
       // channels 2q (low halves) and 2q+1 (high halves) of the two tokens
       const int ra = pg * 8 + 2 * q, rb = ra + 1;
       X32[ra * ((Q + 8) / 2) + (jp ^ xt_swizzle_words<Q>(ra))] =
-          (uint32_t)f32_to_bf16(bf16_lo(w0[q]) * cp0) | ((uint32_t)f32_to_bf16(bf16_lo(w1[q]) * cp1) << 16);
+          pack_bf16x2(bf16_lo(w0[q]) * cp0, bf16_lo(w1[q]) * cp1);
       X32[rb * ((Q + 8) / 2) + (jp ^ xt_swizzle_words<Q>(rb))] =
-          (uint32_t)f32_to_bf16(bf16_hi(w0[q]) * cp0) | ((uint32_t)f32_to_bf16(bf16_hi(w1[q]) * cp1) << 16);
+          pack_bf16x2(bf16_hi(w0[q]) * cp0, bf16_hi(w1[q]) * cp1);
     }
   }
 }
@@ -350,7 +358,7 @@ __global__ __launch_bounds__(512) void ssd_state_kernel(SsdParams p) {
         // word column XORed with 16 pg (inside the row): the four channel groups of a wave
         // write to four different 16-bank ranges
         X32[(16 * pg + q) * ((Q + 8) / 2) + (jp ^ ((16 * pg) & (Q / 2 - 1)))] =
-            (uint32_t)f32_to_bf16(f0 * wj[0]) | ((uint32_t)f32_to_bf16(f1 * wj[1]) << 16);
+            pack_bf16x2(f0 * wj[0], f1 * wj[1]);
       }
     }
     const float decay = exp2_fast(a2 * cur.s_last);
@@ -360,8 +368,8 @@ __global__ __launch_bounds__(512) void ssd_state_kernel(SsdParams p) {
     bf16_t* hin = hin_all + ((b * nch + c) * p.H + h) * PN;
 #pragma unroll
     for (int k2 = 0; k2 < NTW; ++k2) {
-      const uint32_t lo = (uint32_t)f32_to_bf16(acc[k2][0]) | ((uint32_t)f32_to_bf16(acc[k2][1]) << 16);
-      const uint32_t hi = (uint32_t)f32_to_bf16(acc[k2][2]) | ((uint32_t)f32_to_bf16(acc[k2][3]) << 16);
+      const uint32_t lo = pack_bf16x2(acc[k2][0], acc[k2][1]);
+      const uint32_t hi = pack_bf16x2(acc[k2][2], acc[k2][3]);
       *reinterpret_cast<uint2*>(hin + st_idx(k2)) = make_uint2(lo, hi);
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[k2][r] *= decay;

@@ -245,8 +245,10 @@ __global__ __launch_bounds__(512) void ssd_state_kernel(SsdParams p) {
   static_assert(BT16 % 512 == 0, "B^T pieces divide over the threads");
   static_assert(512 % XPAIRS == 0, "x items repeat evenly over the threads");
   constexpr int BT_PER = BT16 / 512;
-  __shared__ __attribute__((aligned(16))) __bf16 Xs[kP * (Q + 8)];
-  __shared__ __attribute__((aligned(16))) __bf16 Bs[N * (Q + 8)];
+  // two buffers of each where they fit beside each other in LDS (chunks of up to 128 tokens)
+  constexpr bool kDoubleLds = Q <= 128;
+  __shared__ __attribute__((aligned(16))) __bf16 Xs[kDoubleLds ? 2 : 1][kP * (Q + 8)];
+  __shared__ __attribute__((aligned(16))) __bf16 Bs[kDoubleLds ? 2 : 1][N * (Q + 8)];
   const int64_t h = blockIdx.x, b = blockIdx.y;
   const int64_t nch = (p.L + Q - 1) / Q;
   const int tid = threadIdx.x;
@@ -322,70 +324,84 @@ __global__ __launch_bounds__(512) void ssd_state_kernel(SsdParams p) {
   // chunk of the k-th step: ascending in the forward, descending in the adjoint
   auto chunk_of = [&](int64_t k) { return ADJ ? nch - 1 - k : k; };
 
-  auto process = [&](int64_t k, ChunkIn& cur) __attribute__((always_inline)) {
-    const int64_t c = chunk_of(k);
-    // stage B^T (C^T) and the weighted, transposed x (ybar) of chunk c
+  // stage B^T (C^T) and the weighted, transposed x (ybar) of the chunk in `in` into the LDS
+  // buffers xsb, bsb; returns the chunk's decay exp(a S_last)
+  auto stage = [&](int64_t c, const ChunkIn& in, __bf16* xsb, __bf16* bsb) __attribute__((always_inline)) {
 #pragma unroll
     for (int k2 = 0; k2 < BT_PER; ++k2) {
       const int e = tid + 512 * k2;
       const int n = e / (Q / 8), j8 = (e % (Q / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&Bs[n * (Q + 8) + j8]) = cur.bt[k2];
+      *reinterpret_cast<u32x4*>(&bsb[n * (Q + 8) + j8]) = in.bt[k2];
     }
-    {
-      float wj[2];
+    float wj[2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        if constexpr (ADJ)
-          wj[u] = c * Q + 2 * jp + u < p.L ? exp2_fast(a2 * cur.sphi[u].x) : 0.f;
-        else
-          wj[u] = exp2_fast(a2 * (cur.s_last - cur.sphi[u].x)) * cur.sphi[u].y;
-      }
-      uint32_t* X32 = reinterpret_cast<uint32_t*>(Xs);
+    for (int u = 0; u < 2; ++u) {
+      if constexpr (ADJ)
+        wj[u] = c * Q + 2 * jp + u < p.L ? exp2_fast(a2 * in.sphi[u].x) : 0.f;
+      else
+        wj[u] = exp2_fast(a2 * (in.s_last - in.sphi[u].x)) * in.sphi[u].y;
+    }
+    uint32_t* X32 = reinterpret_cast<uint32_t*>(xsb);
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const uint32_t u0 = pick(cur.x[0][q >> 3], (q & 7) >> 1);
-        const uint32_t u1 = pick(cur.x[1][q >> 3], (q & 7) >> 1);
-        float f0 = (q & 1) ? bf16_hi(u0) : bf16_lo(u0);
-        float f1 = (q & 1) ? bf16_hi(u1) : bf16_lo(u1);
-        if constexpr (ADJ) {
-          if (zg) {
-            const uint32_t v0 = pick(cur.z[0][q >> 3], (q & 7) >> 1);
-            const uint32_t v1 = pick(cur.z[1][q >> 3], (q & 7) >> 1);
-            f0 *= silu((q & 1) ? bf16_hi(v0) : bf16_lo(v0));
-            f1 *= silu((q & 1) ? bf16_hi(v1) : bf16_lo(v1));
-          }
+    for (int q = 0; q < 16; ++q) {
+      const uint32_t u0 = pick(in.x[0][q >> 3], (q & 7) >> 1);
+      const uint32_t u1 = pick(in.x[1][q >> 3], (q & 7) >> 1);
+      float f0 = (q & 1) ? bf16_hi(u0) : bf16_lo(u0);
+      float f1 = (q & 1) ? bf16_hi(u1) : bf16_lo(u1);
+      if constexpr (ADJ) {
+        if (zg) {
+          const uint32_t v0 = pick(in.z[0][q >> 3], (q & 7) >> 1);
+          const uint32_t v1 = pick(in.z[1][q >> 3], (q & 7) >> 1);
+          f0 *= silu((q & 1) ? bf16_hi(v0) : bf16_lo(v0));
+          f1 *= silu((q & 1) ? bf16_hi(v1) : bf16_lo(v1));
         }
-        // word column XORed with 16 pg (inside the row): the four channel groups of a wave
-        // write to four different 16-bank ranges
-        X32[(16 * pg + q) * ((Q + 8) / 2) + (jp ^ ((16 * pg) & (Q / 2 - 1)))] =
-            pack_bf16x2(f0 * wj[0], f1 * wj[1]);
       }
+      // word column XORed with 16 pg (inside the row): the four channel groups of a wave
+      // write to four different 16-bank ranges
+      X32[(16 * pg + q) * ((Q + 8) / 2) + (jp ^ ((16 * pg) & (Q / 2 - 1)))] = pack_bf16x2(f0 * wj[0], f1 * wj[1]);
     }
-    const float decay = exp2_fast(a2 * cur.s_last);
-    load_chunk(chunk_of(k + 2 < nch ? k + 2 : nch - 1), cur);
-    // the state entering chunk c (the adjoint of the state leaving it), for the output kernel
-    // (the backward); then decay it over the chunk
+    return exp2_fast(a2 * in.s_last);
+  };
+  // the state entering chunk c (the adjoint of the state leaving it), for the output kernel
+  // (the backward); then decay it over the chunk
+  auto store_and_decay = [&](int64_t c, float decay) __attribute__((always_inline)) {
     bf16_t* hin = hin_all + ((b * nch + c) * p.H + h) * PN;
 #pragma unroll
     for (int k2 = 0; k2 < NTW; ++k2) {
-      const uint32_t lo = pack_bf16x2(acc[k2][0], acc[k2][1]);
-      const uint32_t hi = pack_bf16x2(acc[k2][2], acc[k2][3]);
-      *reinterpret_cast<uint2*>(hin + st_idx(k2)) = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(hin + st_idx(k2)) =
+          make_uint2(pack_bf16x2(acc[k2][0], acc[k2][1]), pack_bf16x2(acc[k2][2], acc[k2][3]));
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[k2][r] *= decay;
     }
-    __syncthreads();
+  };
+  // acc += (B^T of the chunk) (weighted x^T), operands read one K step ahead into a second
+  // register set; the scheduling barriers keep the reads of step kq + 1 ahead of the products
+  // of step kq (without them the compiler reuses one register set and waits for each read
+  // before its product)
+  auto products = [&](const __bf16* xsb, const __bf16* bsb) __attribute__((always_inline)) {
+    auto frag_x = [&](int kq) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8*>(&xsb[(16 * pq + r16) * (Q + 8) + ((kq * 32 + 8 * g) ^ ((32 * pq) & (Q - 1)))]);
+    };
+    auto frag_b = [&](int kq, int k2) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8*>(&bsb[((w2 * NTW + k2) * 16 + r16) * (Q + 8) + kq * 32 + 8 * g]);
+    };
+    bf16x8 xf[2], bfr[2][NTW];
+    xf[0] = frag_x(0);
+#pragma unroll
+    for (int k2 = 0; k2 < NTW; ++k2) bfr[0][k2] = frag_b(0, k2);
 #pragma unroll
     for (int kq = 0; kq < KQ; ++kq) {
-      const bf16x8 xb = *reinterpret_cast<const bf16x8*>(
-          &Xs[(16 * pq + r16) * (Q + 8) + ((kq * 32 + 8 * g) ^ ((32 * pq) & (Q - 1)))]);
+      const int cb = kq & 1;
+      if (kq + 1 < KQ) {
+        xf[cb ^ 1] = frag_x(kq + 1);
 #pragma unroll
-      for (int k2 = 0; k2 < NTW; ++k2) {
-        const bf16x8 ba = *reinterpret_cast<const bf16x8*>(&Bs[((w2 * NTW + k2) * 16 + r16) * (Q + 8) + kq * 32 + 8 * g]);
-        acc[k2] = mfma16(ba, xb, acc[k2]);   // (states x tokens) . (tokens x channels)
+        for (int k2 = 0; k2 < NTW; ++k2) bfr[cb ^ 1][k2] = frag_b(kq + 1, k2);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k2 = 0; k2 < NTW; ++k2) acc[k2] = mfma16(bfr[cb][k2], xf[cb], acc[k2]);   // (states x tokens) . (tokens x channels)
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
   };
 
   ChunkIn buf0, buf1;   // even steps in buf0, odd steps in buf1
@@ -393,12 +409,54 @@ __global__ __launch_bounds__(512) void ssd_state_kernel(SsdParams p) {
     load_chunk(chunk_of(0), buf0);
     load_chunk(chunk_of(nch > 1 ? 1 : 0), buf1);
   }
-  int64_t k = 0;
-  for (; k + 1 < nch; k += 2) {
-    process(k, buf0);
-    process(k + 1, buf1);
+  // wait for the entering state here, once: its loads are conditional, and a first use inside
+  // the loop would put a wait for every outstanding load at the head of each step
+#pragma unroll
+  for (int k = 0; k < NTW; ++k) asm volatile("" : "+v"(acc[k]));
+  if constexpr (!kDoubleLds) {
+    // one LDS buffer: stage, barrier, products, barrier
+    auto process = [&](int64_t k, ChunkIn& cur) __attribute__((always_inline)) {
+      const int64_t c = chunk_of(k);
+      const float decay = stage(c, cur, Xs[0], Bs[0]);
+      load_chunk(chunk_of(k + 2 < nch ? k + 2 : nch - 1), cur);
+      store_and_decay(c, decay);
+      __syncthreads();
+      products(Xs[0], Bs[0]);
+      __syncthreads();
+    };
+    int64_t k = 0;
+    for (; k + 1 < nch; k += 2) {
+      process(k, buf0);
+      process(k + 1, buf1);
+    }
+    if (k < nch) process(k, buf0);
+  } else {
+    // two LDS buffers: chunk k + 1 is staged while the products of chunk k run; one barrier
+    // per chunk (after it, the next chunk's operands are complete and this chunk's buffer free)
+    float dec = 0.f;
+    if (nch > 0) {
+      dec = stage(chunk_of(0), buf0, Xs[0], Bs[0]);
+      load_chunk(chunk_of(nch > 2 ? 2 : nch - 1), buf0);
+    }
+    __syncthreads();
+    // step k: the register buffer `nxt` holds chunk k + 1 (k + 1 < nch), refilled with k + 3
+    auto step = [&](int64_t k, ChunkIn& nxt) __attribute__((always_inline)) {
+      const int64_t c = chunk_of(k);
+      store_and_decay(c, dec);
+      if (k + 1 < nch) {
+        dec = stage(chunk_of(k + 1), nxt, Xs[(k + 1) & 1], Bs[(k + 1) & 1]);
+        load_chunk(chunk_of(k + 3 < nch ? k + 3 : nch - 1), nxt);
+      }
+      products(Xs[k & 1], Bs[k & 1]);
+      __syncthreads();
+    };
+    int64_t k = 0;
+    for (; k + 1 < nch; k += 2) {
+      step(k, buf1);
+      step(k + 1, buf0);
+    }
+    if (k < nch) step(k, buf1);
   }
-  if (k < nch) process(k, buf0);
 
   float* s_out = ADJ ? p.dh0 : p.h_last;
   if (s_out) {

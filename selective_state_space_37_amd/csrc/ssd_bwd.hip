@@ -64,7 +64,7 @@ __device__ __forceinline__ void unpack8(uint4 v, float out[8]) {
 // lane, the same K order on both operands. dB and dC are summed over the workgroup's hb heads
 // (consecutive heads of one group) in registers; B^T and C^T, shared by those heads, are staged
 // in LDS once.
-template <int N>
+template <int N, bool GATE>
 __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
   constexpr int Q = kQb;
   constexpr int NT = N / 16;   // 16-state tiles
@@ -143,66 +143,139 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
     *reinterpret_cast<uint4*>(&CtS[n * RS + j8]) = *reinterpret_cast<const uint4*>(Ctm + n * Q + j8);
   }
 
+  // Per-head global operands, loaded into registers one head ahead: the loads of head kh + 1 are
+  // issued in the last phase of head kh (per-token sums, few live registers) and used at the
+  // start of head kh + 1. Staging roles: threads 0..255 take x, threads 256..511 dy (and z);
+  // item (token pair sip, channels 8 spg .. 8 spg + 7). Thread tid < 32 (N / 8) also takes the
+  // H_c and Gc rows of channel pair hpp, states 8 hng .. 8 hng + 7. Every lane also takes the
+  // operands of its Gc B_j product (the rows of Gc of this half's channel tiles and B_j of its
+  // token, over the states), which is formed before the staging barrier.
+  constexpr bool gate = GATE;   // z given (one instantiation each way)
+  const int srole = w >> 2;   // wave-uniform
+  constexpr int NHG = 32 * (N / 8);
+  static_assert(NHG <= 512, "one H_c / Gc item per thread at most");
+  uint4 pv[4];     // x pair (role 0), or dy pair and z pair (role 1)
+  uint4 phg[4];    // H_c rows 2 hpp, 2 hpp + 1, then Gc rows 2 hpp, 2 hpp + 1
+  float4 pphi;     // (S, phi) of tokens 2 sip, 2 sip + 1 (role 0, with a gate)
+  float2 psp;      // (S, phi) of token tid (tid < Q)
+  uint32_t pdl;    // Delta bits of token tid of the chunk (wave 0)
+  bf16x8 pgc[2][KSN], pbj[KSN];
+  // Addresses are a wave-uniform base (scalar registers) plus a 32-bit per-lane byte offset, and
+  // the per-lane parts are formed from `tv`, the thread index passed through an empty asm in each
+  // head: neither 64-bit per-lane pointers nor per-lane LDS addresses are then carried across
+  // the head loop, where they would take registers from the products.
+  // the operands of the Gc B_j product: one head ahead without a gate; with one (more live
+  // registers in the gate's products) at the start of the head
+  constexpr bool kEarlyGcB = !GATE;
+  auto load_gcb = [&](int64_t kh, int tv) __attribute__((always_inline)) {
+    const int lane = tv & 63, g = lane >> 4, r16 = lane & 15;
+    const int64_t h = hblk * bp.hb + kh;
+    const bf16_t* gs = static_cast<const bf16_t*>(p.ws_gout) + ((b * nch + c) * H + h) * (int64_t)(kP * N);
+    const uint32_t foff = (uint32_t)(r16 * N + 8 * g) * 2u;
+    const uint32_t boff = (uint32_t)(r16 * rs + 8 * g) * 2u;
+    const bf16_t* bj0 = Bg + (tc0 + tt * 16) * rs;
+    const bool valid = tc0 + tt * 16 + r16 < L;
+#pragma unroll
+    for (int ks = 0; ks < KSN; ++ks) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) pgc[k][ks] = ld_at<bf16x8>(gs + (2 * hf + k) * 16 * N + 32 * ks, foff);
+      pbj[ks] = valid ? ld_at<bf16x8>(bj0 + 32 * ks, boff) : zero_frag();
+    }
+  };
+  auto prefetch = [&](int64_t kh, int tv) __attribute__((always_inline)) {
+    const int lane = tv & 63, g = lane >> 4, r16 = lane & 15;
+    const int sip = tv & 31, spg = (tv >> 5) & 7, hpp = tv & 31, hng = tv >> 5;
+    const int64_t h = hblk * bp.hb + kh;
+    const int64_t t = tc0 + 2 * sip;
+    const uint4 zero4 = make_uint4(0, 0, 0, 0);
+    const int64_t row0 = ((b * L + tc0) * H + h) * kP;   // element of (token tc0, head h, channel 0)
+    const uint32_t toff = (uint32_t)((2 * sip) * tstride + 8 * spg) * 2u;
+    const bf16_t* src = static_cast<const bf16_t*>(srole == 0 ? p.x : p.dy) + row0;
+    pv[0] = t < L ? ld_at<uint4>(src, toff) : zero4;
+    pv[1] = t + 1 < L ? ld_at<uint4>(src + tstride, toff) : zero4;
+    const float2* sp = p.ws_sphi + ((b * nch + c) * H + h) * Q;
+    if constexpr (gate) {
+      if (srole == 1) {
+        const bf16_t* zs = static_cast<const bf16_t*>(p.z) + row0;
+        pv[2] = t < L ? ld_at<uint4>(zs, toff) : zero4;
+        pv[3] = t + 1 < L ? ld_at<uint4>(zs + tstride, toff) : zero4;
+      } else {
+        pphi = ld_at<float4>(sp, (uint32_t)sip * 16u);
+      }
+    }
+    const int64_t so = ((b * nch + c) * H + h) * (int64_t)(kP * N);
+    const bf16_t* hs = static_cast<const bf16_t*>(p.ws_hin) + so;
+    const bf16_t* gs = static_cast<const bf16_t*>(p.ws_gout) + so;
+    if (tv < NHG) {
+      const uint32_t hoff = (uint32_t)((2 * hpp) * N + 8 * hng) * 2u;
+      phg[0] = ld_at<uint4>(hs, hoff);
+      phg[1] = ld_at<uint4>(hs + N, hoff);
+      phg[2] = ld_at<uint4>(gs, hoff);
+      phg[3] = ld_at<uint4>(gs + N, hoff);
+    }
+    if (tv < Q) psp = ld_at<float2>(sp, (uint32_t)tv * 8u);
+    if (w == 0) {
+      const bf16_t* dl0 = static_cast<const bf16_t*>(p.delta) + (b * L + tc0) * H + h;
+      pdl = tc0 + lane < L ? ld_at<uint16_t>(dl0, (uint32_t)(lane * H) * 2u) : 0u;
+    }
+    if constexpr (kEarlyGcB) load_gcb(kh, tv);
+  };
+  prefetch(0, tid);
+
   for (int64_t kh = 0; kh < bp.hb; ++kh) {
+    int tv = tid;
+    asm volatile("" : "+v"(tv));
+    const int lane = tv & 63, g = lane >> 4, r16 = lane & 15;
+    const int il = tt * 16 + r16;
+    const int64_t tl = tc0 + il;
+    const bool lane_valid = tl < L;
+    const int sip = tv & 31, spg = (tv >> 5) & 7, hpp = tv & 31, hng = tv >> 5;
+    const bool has_hg = tv < NHG;
     const int64_t h = hblk * bp.hb + kh;
     const float a = p.A[h], a2 = a * kLog2e;
-    const bf16_t* xh = static_cast<const bf16_t*>(p.x) + (b * L * H + h) * kP;
-    const bf16_t* dyh = static_cast<const bf16_t*>(p.dy) + (b * L * H + h) * kP;
-    const bf16_t* zh = p.z ? static_cast<const bf16_t*>(p.z) + (b * L * H + h) * kP : nullptr;
-    const float2* sp = p.ws_sphi + ((b * nch + c) * H + h) * Q;
+    // (first token of this wave's tile, head h, channel 0), and this lane's token and channel
+    // group 4 g relative to it
+    const int64_t trow = ((b * L + tc0 + tt * 16) * H + h) * kP;
+    const uint32_t toff = (uint32_t)(r16 * tstride + 4 * g) * 2u;
     const bf16_t* hin = static_cast<const bf16_t*>(p.ws_hin) + ((b * nch + c) * H + h) * (int64_t)(kP * N);
-    const bf16_t* gout = static_cast<const bf16_t*>(p.ws_gout) + ((b * nch + c) * H + h) * (int64_t)(kP * N);
     const bool dpc = p.Dskip && p.dskip_per_channel;
     const float dhead = p.Dskip && !p.dskip_per_channel ? p.Dskip[h] : 0.f;
     auto dskip = [&](int ch) { return dpc ? p.Dskip[h * kP + ch] : dhead; };
-
+    if constexpr (!kEarlyGcB) load_gcb(kh, tv);
     // ------------------------------------------------------------------ staging
-    if (tid < Q) {
-      const float2 v = sp[tid];
-      sS[tid] = v.x;
-      sPhi[tid] = v.y;
-    }
     float dot = 0.f;   // <Gc, H_c> over this thread's pieces
-    if (tid < 256) {
-      // token pair ip, channels 8 pg8 .. 8 pg8 + 7: x and ybar (natural, and ybar^T; (phi x)^T
-      // with a gate). Lanes 0..31 of a wave write 32 consecutive words of a transposed row, lanes
-      // 32..63 the rows 8 further (288 words on): the 64 writes fall on 64 banks.
-      const int ip = tid & 31, pg8 = tid >> 5;
+    if (srole == 0) {
+      // x (natural), and (phi x)^T with a gate for the recomputed within-chunk output. Lanes
+      // 0..31 of a wave write 32 consecutive words of a transposed row, lanes 32..63 the rows 8
+      // further (288 words on): the 64 writes fall on 64 banks.
+      *reinterpret_cast<uint4*>(&Xn[(2 * sip) * RS + 8 * spg]) = pv[0];
+      *reinterpret_cast<uint4*>(&Xn[(2 * sip + 1) * RS + 8 * spg]) = pv[1];
+      if constexpr (gate) {
+        float xv0[8], xv1[8];
+        unpack8(pv[0], xv0);
+        unpack8(pv[1], xv1);
+        uint32_t* X32 = reinterpret_cast<uint32_t*>(XT);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) X32[(8 * spg + k) * (RS / 2) + sip] = pack_bf16x2(pphi.y * xv0[k], pphi.w * xv1[k]);
+      }
+    } else {
+      // ybar (natural, as bf16 hi + lo) and ybar^T
       float y0[8], y1[8];
-      const int64_t t = tc0 + 2 * ip;
-      const uint4 zero4 = make_uint4(0, 0, 0, 0);
-      const uint4 xa = t < L ? *reinterpret_cast<const uint4*>(xh + t * tstride + 8 * pg8) : zero4;
-      const uint4 xb = t + 1 < L ? *reinterpret_cast<const uint4*>(xh + (t + 1) * tstride + 8 * pg8) : zero4;
-      const uint4 d0 = t < L ? *reinterpret_cast<const uint4*>(dyh + t * tstride + 8 * pg8) : zero4;
-      const uint4 d1 = t + 1 < L ? *reinterpret_cast<const uint4*>(dyh + (t + 1) * tstride + 8 * pg8) : zero4;
-      unpack8(d0, y0);
-      unpack8(d1, y1);
-      if (zh) {
-        const uint4 z0 = t < L ? *reinterpret_cast<const uint4*>(zh + t * tstride + 8 * pg8) : zero4;
-        const uint4 z1 = t + 1 < L ? *reinterpret_cast<const uint4*>(zh + (t + 1) * tstride + 8 * pg8) : zero4;
+      unpack8(pv[0], y0);
+      unpack8(pv[1], y1);
+      if constexpr (gate) {
         float zv0[8], zv1[8];
-        unpack8(z0, zv0);
-        unpack8(z1, zv1);
+        unpack8(pv[2], zv0);
+        unpack8(pv[3], zv1);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           y0[k] *= silu(zv0[k]);
           y1[k] *= silu(zv1[k]);
         }
-        // (phi x)^T for the recomputed within-chunk output
-        float xv0[8], xv1[8];
-        unpack8(xa, xv0);
-        unpack8(xb, xv1);
-        const float ph0 = sp[2 * ip].y, ph1 = sp[2 * ip + 1].y;
-        uint32_t* X32 = reinterpret_cast<uint32_t*>(XT);
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          X32[(8 * pg8 + k) * (RS / 2) + ip] =
-              pack_bf16x2(ph0 * xv0[k], ph1 * xv1[k]);
       }
       uint32_t* Y32 = reinterpret_cast<uint32_t*>(YT);
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        Y32[(8 * pg8 + k) * (RS / 2) + ip] = pack_bf16x2(y0[k], y1[k]);
+      for (int k = 0; k < 8; ++k) Y32[(8 * spg + k) * (RS / 2) + sip] = pack_bf16x2(y0[k], y1[k]);
       float h0[8], h1[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -211,31 +284,38 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
         y0[k] -= h0[k];
         y1[k] -= h1[k];
       }
-      *reinterpret_cast<bf16x8*>(&Yhi[(2 * ip) * RS + 8 * pg8]) = pack8(h0);
-      *reinterpret_cast<bf16x8*>(&Yhi[(2 * ip + 1) * RS + 8 * pg8]) = pack8(h1);
-      *reinterpret_cast<bf16x8*>(&Ylo[(2 * ip) * RS + 8 * pg8]) = pack8(y0);
-      *reinterpret_cast<bf16x8*>(&Ylo[(2 * ip + 1) * RS + 8 * pg8]) = pack8(y1);
-      *reinterpret_cast<uint4*>(&Xn[(2 * ip) * RS + 8 * pg8]) = xa;
-      *reinterpret_cast<uint4*>(&Xn[(2 * ip + 1) * RS + 8 * pg8]) = xb;
-    } else {
-      for (int item = tid - 256; item < 32 * (N / 8); item += 256) {
-        // channels (2 pp, 2 pp + 1), states 8 ng .. 8 ng + 7 of H_c and Gc, written transposed
-        const int pp = item & 31, ng = item >> 5;
-        float h0v[8], h1v[8], g0v[8], g1v[8];
-        unpack8(*reinterpret_cast<const uint4*>(hin + (2 * pp) * N + 8 * ng), h0v);
-        unpack8(*reinterpret_cast<const uint4*>(hin + (2 * pp + 1) * N + 8 * ng), h1v);
-        unpack8(*reinterpret_cast<const uint4*>(gout + (2 * pp) * N + 8 * ng), g0v);
-        unpack8(*reinterpret_cast<const uint4*>(gout + (2 * pp + 1) * N + 8 * ng), g1v);
-        uint32_t* H32 = reinterpret_cast<uint32_t*>(HT);
-        uint32_t* G32 = reinterpret_cast<uint32_t*>(GcT);
+      *reinterpret_cast<bf16x8*>(&Yhi[(2 * sip) * RS + 8 * spg]) = pack8(h0);
+      *reinterpret_cast<bf16x8*>(&Yhi[(2 * sip + 1) * RS + 8 * spg]) = pack8(h1);
+      *reinterpret_cast<bf16x8*>(&Ylo[(2 * sip) * RS + 8 * spg]) = pack8(y0);
+      *reinterpret_cast<bf16x8*>(&Ylo[(2 * sip + 1) * RS + 8 * spg]) = pack8(y1);
+    }
+    if (has_hg) {
+      // channels (2 hpp, 2 hpp + 1), states 8 hng .. 8 hng + 7 of H_c and Gc, written transposed
+      float h0v[8], h1v[8], g0v[8], g1v[8];
+      unpack8(phg[0], h0v);
+      unpack8(phg[1], h1v);
+      unpack8(phg[2], g0v);
+      unpack8(phg[3], g1v);
+      uint32_t* H32 = reinterpret_cast<uint32_t*>(HT);
+      uint32_t* G32 = reinterpret_cast<uint32_t*>(GcT);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          H32[(8 * ng + k) * (RSP / 2) + pp] = pack_bf16x2(h0v[k], h1v[k]);
-          G32[(8 * ng + k) * (RSP / 2) + pp] = pack_bf16x2(g0v[k], g1v[k]);
-          dot += h0v[k] * g0v[k] + h1v[k] * g1v[k];
-        }
+      for (int k = 0; k < 8; ++k) {
+        H32[(8 * hng + k) * (RSP / 2) + hpp] = pack_bf16x2(h0v[k], h1v[k]);
+        G32[(8 * hng + k) * (RSP / 2) + hpp] = pack_bf16x2(g0v[k], g1v[k]);
+        dot += h0v[k] * g0v[k] + h1v[k] * g1v[k];
       }
     }
+    if (tid < Q) {
+      sS[tid] = psp.x;
+      sPhi[tid] = psp.y;
+    }
+    const uint32_t dl = pdl;
+    // vo[p][j] = sum_n Gc[p][n] B_j[n] (this half's channel tiles, own token j)
+    f32x4 vo[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < KSN; ++ks)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) vo[k] = mfma16(pgc[k][ks], pbj[ks], vo[k]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
     if (lane == 0) sRed[w] = dot;
@@ -253,6 +333,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
     }
 
     // ------------------------------------------------------------------ dC (rows i = own tile)
+    float qpart = 0.f;   // this lane's part of ybar_i . Yoff_i (token il, this half's states)
     {
       // U^T tiles (j tile jt <= tt, i = own): D[j][i] = sum_p x_j[p] ybar_i[p]; the lane holds
       // U[il][jt 16 + 4 g + r]. W (as the B operand of the next product) and K (to LDS, by the
@@ -302,9 +383,18 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
           const uint2 hi = *reinterpret_cast<const uint2*>(&BtS[n * RS + 32 * kk + 16 + 4 * g]);
           acc = mfma16(frag_from_pieces(lo, hi), wmA[kk], acc);   // D[n][i] = sum_j B_j[n] W_ij
         }
+        // the carried-state part M[n][i] = exp(a S_i) sum_p H_c[p][n] ybar_i[p], kept apart
+        // first: sum_n C_i[n] M[n][i] is ybar_i . Yoff_i (this lane: states
+        // (hf NTH + k) 16 + 4 g + r of token il)
+        f32x4 m = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
-          acc = mfma16(*reinterpret_cast<const bf16x8*>(&HT[n * RSP + 32 * kk + 8 * g]), yb_sc[kk], acc);
+          m = mfma16(*reinterpret_cast<const bf16x8*>(&HT[n * RSP + 32 * kk + 8 * g]), yb_sc[kk], m);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          qpart += (float)CtS[((hf * NTH + k) * 16 + 4 * g + r) * RS + il] * m[r];
+          acc[r] += m[r];
+        }
         dC[k] = acc;
       }
     }
@@ -362,25 +452,24 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
     }
 
     // ------------------------------------------------------------------ y (rows i = own tile)
-    // Yoff[p][i] = exp(a S_i) sum_n H_c[p][n] C_i[n]; with a gate also the within-chunk part
-    // Ydiag[p][i] = sum_{j<=i} (C_i . B_j) exp(a (S_i - S_j)) phi_j x_j[p] for the pre-gate output.
+    // With a gate, the pre-gate output per channel: Yoff[p][i] = exp(a S_i) sum_n H_c[p][n] C_i[n]
+    // and the within-chunk part Ydiag[p][i] = sum_{j<=i} (C_i . B_j) exp(a (S_i - S_j)) phi_j x_j[p].
     // This half's channel tiles: pt = 2 hf, 2 hf + 1.
     f32x4 yo[2], yd[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) yo[k] = yd[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
+    if constexpr (gate) {
       const float eSi = exp2_fast(a2 * Sl);
 #pragma unroll
       for (int ks = 0; ks < KSN; ++ks) {
-        bf16x8 cf = lane_valid ? load_frag(Cg + tl * rs + 32 * ks + 8 * g) : zero_frag();
+        bf16x8 cf = lane_valid ? ld_at<bf16x8>(Cg + (tc0 + tt * 16) * rs + 32 * ks, (uint32_t)(r16 * rs + 8 * g) * 2u)
+                               : zero_frag();
 #pragma unroll
         for (int q = 0; q < 8; ++q) cf[q] = (__bf16)((float)cf[q] * eSi);
 #pragma unroll
         for (int k = 0; k < 2; ++k)
-          yo[k] = mfma16(load_frag(hin + ((2 * hf + k) * 16 + r16) * N + 32 * ks + 8 * g), cf, yo[k]);
+          yo[k] = mfma16(ld_at<bf16x8>(hin + (2 * hf + k) * 16 * N + 32 * ks, (uint32_t)(r16 * N + 8 * g) * 2u), cf, yo[k]);
       }
-    }
-    if (zh) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         if (2 * kk > tt) break;
@@ -413,13 +502,11 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
     }
     // epilogue: the lane holds channels pt 16 + 4 g + r (pt = 2 hf + k) of token il
     float ybv[2][4], xv[2][4];
-    float qpart = 0.f;
     {
       float dd[2][4];
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int pt = 2 * hf + k;
-        const int64_t o = tl * tstride + pt * 16 + 4 * g;
         const int lo = il * RS + pt * 16 + 4 * g;
         const uint2 xr = *reinterpret_cast<const uint2*>(&Xn[lo]);
         const uint2 yhr = *reinterpret_cast<const uint2*>(&Yhi[lo]);
@@ -428,9 +515,9 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
         const float ybr[4] = {bf16_lo(yhr.x) + bf16_lo(ylr.x), bf16_hi(yhr.x) + bf16_hi(ylr.x),
                               bf16_lo(yhr.y) + bf16_lo(ylr.y), bf16_hi(yhr.y) + bf16_hi(ylr.y)};
         float dv[4] = {0.f, 0.f, 0.f, 0.f}, zv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (zh && lane_valid) {
-          const uint2 dr = *reinterpret_cast<const uint2*>(dyh + o);
-          const uint2 zr = *reinterpret_cast<const uint2*>(zh + o);
+        if (gate && lane_valid) {
+          const uint2 dr = ld_at<uint2>(static_cast<const bf16_t*>(p.dy) + trow + pt * 16, toff);
+          const uint2 zr = ld_at<uint2>(static_cast<const bf16_t*>(p.z) + trow + pt * 16, toff);
           dv[0] = bf16_lo(dr.x); dv[1] = bf16_hi(dr.x); dv[2] = bf16_lo(dr.y); dv[3] = bf16_hi(dr.y);
           zv[0] = bf16_lo(zr.x); zv[1] = bf16_hi(zr.x); zv[2] = bf16_lo(zr.y); zv[3] = bf16_hi(zr.y);
         }
@@ -441,19 +528,18 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
           xv[k][r] = xx[r];
           const float yb = ybr[r];
           ybv[k][r] = yb;
-          qpart += yb * yo[k][r];
           dd[k][r] = yb * xx[r];
-          if (zh) {
+          if constexpr (gate) {
             const float ypre = yo[k][r] + yd[k][r] + dskip(ch) * xx[r];
             const float sg = sigmoid_fast(zv[r]);
             dzv[r] = dv[r] * ypre * sg * (1.f + zv[r] * (1.f - sg));
           }
         }
-        if (zh && lane_valid) {
+        if (gate && lane_valid) {
           uint2 out;
           out.x = pack_bf16x2(dzv[0], dzv[1]);
           out.y = pack_bf16x2(dzv[2], dzv[3]);
-          *reinterpret_cast<uint2*>(static_cast<bf16_t*>(bp.dz) + (b * L * H + h) * kP + o) = out;
+          st_at(static_cast<bf16_t*>(bp.dz) + trow + pt * 16, toff, out);
         }
       }
       // dD per channel: sum over the 16 tokens of the tile (lanes with the same g)
@@ -470,9 +556,9 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
 
     // ------------------------------------------------------------------ dx (columns j = own tile)
     // w_j[p] = sum_{i>=j} (C_i . B_j) exp(a (S_i - S_j)) ybar_i[p]   +   exp(a (S_Q - S_j)) (Gc B_j)[p]
-    f32x4 wi[2], vo[2];
+    f32x4 wi[2];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) wi[k] = vo[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < 2; ++k) wi[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       if (2 * kk + 1 < tt) continue;
@@ -502,13 +588,6 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
         wi[k] = mfma16(frag_from_pieces(lo, hi), glf, wi[k]);   // D[p][j] = sum_i ybar_i[p] GL_ij
       }
     }
-#pragma unroll
-    for (int ks = 0; ks < KSN; ++ks) {
-      const bf16x8 bf = lane_valid ? load_frag(Bg + tl * rs + 32 * ks + 8 * g) : zero_frag();
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-        vo[k] = mfma16(load_frag(gout + ((2 * hf + k) * 16 + r16) * N + 32 * ks + 8 * g), bf, vo[k]);
-    }
     float vvp = vin, rp = 0.f;
     {
       const float eq = exp2_fast(a2 * (Sq - Sl));
@@ -527,7 +606,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
           uint2 out;
           out.x = pack_bf16x2(dxv[0], dxv[1]);
           out.y = pack_bf16x2(dxv[2], dxv[3]);
-          *reinterpret_cast<uint2*>(static_cast<bf16_t*>(bp.dx) + (b * L * H + h) * kP + tl * tstride + pt * 16 + 4 * g) = out;
+          st_at(static_cast<bf16_t*>(bp.dx) + trow + pt * 16, toff, out);
         }
       }
       vvp += rp;   // x_j . (exp(a (S_Q - S_j)) Gc B_j)
@@ -545,6 +624,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
       sVv[hf][il] = vvp;
       sRv[hf][il] = rp;
     }
+    if (kh + 1 < bp.hb) prefetch(kh + 1, tv);
     __syncthreads();
 
     // ------------------------------------------------------------------ sum of K over j <= t <= i
@@ -611,11 +691,10 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
       const int64_t tt2 = tc0 + t;
       float pa = 0.f, pb = 0.f;
       if (tt2 < L) {
-        const float raw = bf16_to_f32(static_cast<const bf16_t*>(p.delta)[(b * L + tt2) * H + h].bits) +
-                          (p.delta_bias ? p.delta_bias[h] : 0.f);
+        const float raw = bf16_to_f32((uint16_t)dl) + (p.delta_bias ? p.delta_bias[h] : 0.f);
         const float dt = p.delta_softplus ? softplus_f32(raw) : raw;
         const float gu = p.delta_softplus ? ddt * sigmoid_fast(raw) : ddt;
-        static_cast<bf16_t*>(bp.ddelta)[(b * L + tt2) * H + h].bits = f32_to_bf16(gu);
+        st_at(static_cast<bf16_t*>(bp.ddelta) + (b * L + tc0) * H + h, (uint32_t)(t * H) * 2u, f32_to_bf16(gu));
         // (Delta - phi) / a = (a Delta - expm1(a Delta)) / a^2
         const float xa = a * dt;
         pa = dt * u + (xa - expm1f(xa)) / (a * a) * vv;
@@ -724,8 +803,11 @@ hipError_t launch_n(const SsdBwdParams& bp, hipStream_t stream) {
                      stream, p);
   hipLaunchKernelGGL((ssd_state_kernel<Q, N, false>), dim3((unsigned)p.H, (unsigned)p.B), dim3(512), 0, stream, p);
   hipLaunchKernelGGL((ssd_state_kernel<Q, N, true>), dim3((unsigned)p.H, (unsigned)p.B), dim3(512), 0, stream, p);
-  hipLaunchKernelGGL((ssd_bwd_main_kernel<N>), dim3((unsigned)(p.H / bp.hb), (unsigned)nch, (unsigned)p.B),
-                     dim3(512), 0, stream, bp);
+  const dim3 grid((unsigned)(p.H / bp.hb), (unsigned)nch, (unsigned)p.B);
+  if (p.z)
+    hipLaunchKernelGGL((ssd_bwd_main_kernel<N, true>), grid, dim3(512), 0, stream, bp);
+  else
+    hipLaunchKernelGGL((ssd_bwd_main_kernel<N, false>), grid, dim3(512), 0, stream, bp);
   const int64_t total = p.B * p.L * p.G * (p.N / 4);
   const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
   hipLaunchKernelGGL(ssd_bwd_reduce_bc_kernel, dim3(blocks), dim3(256), 0, stream, bp);

@@ -37,6 +37,17 @@ __device__ __forceinline__ bf16x8 load_frag(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
+// A load at a wave-uniform base plus a 32-bit per-lane byte offset (the scalar-base form of the
+// global load: one offset register per lane rather than a 64-bit address)
+template <class T, class E>
+__device__ __forceinline__ T ld_at(const E* base, uint32_t byte_off) {
+  return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+template <class T, class E>
+__device__ __forceinline__ void st_at(E* base, uint32_t byte_off, const T& v) {
+  *reinterpret_cast<T*>(reinterpret_cast<char*>(base) + byte_off) = v;
+}
+
 constexpr int kP = 64;  // head dim supported
 
 // Step sizes, inclusive cumulative sums and ZOH input scales of one chunk (Q <= 256 tokens),

@@ -288,11 +288,18 @@ ssm_status scan_bwd_common(int64_t B, int64_t L, int64_t D, int64_t N, int io, c
   return from_hip(ssm::launch_scan_bwd(p, st), "ssm_scan_bwd launch");
 }
 
-// Heads per workgroup in the SSD backward's main pass (their dB and dC are summed in registers
-// before one partial per workgroup is written): a divisor of the heads per group. Four cut the
-// partial sums' traffic fourfold and measured fastest at 80 heads (1, 2, 4, 5, 8, 10 tried).
-int64_t ssd_bwd_heads_per_wg(int64_t H, int64_t G) {
-  return (H / G) % 4 == 0 ? 4 : 1;
+// Heads per workgroup in the SSD backward's main pass: a divisor of the heads per group (the
+// workgroup's heads share the staged B, C and C B^T of the chunk, and their dB and dC are summed
+// in registers before one partial per workgroup is written). At least the largest divisor up to
+// 4, then the largest one up to 64 that still leaves four workgroups per compute unit of a
+// 256-CU device: at 80 heads, L = 8192, B = 2 that is 20 (4, 16, 20 and 40 measured 1.93, 1.80,
+// 1.79 and 1.78 ms for the whole backward).
+int64_t ssd_bwd_heads_per_wg(int64_t B, int64_t L, int64_t H, int64_t G) {
+  const int64_t hg = H / G, nch = (L + ssm::kSsdBwdQ - 1) / ssm::kSsdBwdQ;
+  int64_t best = 1;
+  for (int64_t hb = 2; hb <= hg && hb <= 64; ++hb)
+    if (hg % hb == 0 && (hb <= 4 || (H / hb) * nch * B >= 4 * 256)) best = hb;
+  return best;
 }
 
 }  // namespace
@@ -568,7 +575,7 @@ ssm_status ssm_block_step(int64_t B, int64_t d_model, int64_t d_inner, int64_t N
 
 size_t ssd_chunk_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, ssm_dtype) {
   if (B <= 0 || L <= 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0) return 0;
-  return ssm::ssd_bwd_workspace_bytes(B, L, H, P, N, G, ssd_bwd_heads_per_wg(H, G));
+  return ssm::ssd_bwd_workspace_bytes(B, L, H, P, N, G, ssd_bwd_heads_per_wg(B, L, H, G));
 }
 
 }  // extern "C"
@@ -711,7 +718,7 @@ ssm_status ssd_chunk_bwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, 
       e = dh_last ? hipMemcpyAsync(dh0, dh_last, stb, hipMemcpyDeviceToDevice, st) : hipMemsetAsync(dh0, 0, stb, st);
     return from_hip(e, "empty backward");
   }
-  const int64_t hb = ssd_bwd_heads_per_wg(H, G);
+  const int64_t hb = ssd_bwd_heads_per_wg(B, L, H, G);
   const size_t need = ssm::ssd_bwd_workspace_bytes(B, L, H, P, N, G, hb);
   if (!ws) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace is NULL; %zu bytes needed", need);
   if (ws_bytes < need) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, need);

@@ -72,13 +72,13 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
   constexpr int KSN = N / 32;  // K steps over the states
   constexpr int RS = Q + 8;    // row stride (bf16) of the token tiles
   constexpr int RSP = kP + 8;  // row stride (bf16) of the transposed states
-  constexpr int KST = Q + 1;   // row stride (float) of K
   // row stride (float) of G: rows stay 16-byte aligned for float4 reads of a row, and a wave's
   // column reads (16 columns x 4 row groups) fall on 64 different banks
   constexpr int GST = Q + 4;
   __shared__ __attribute__((aligned(16))) __bf16 Xn[Q * RS];     // x [j][p]
   __shared__ __attribute__((aligned(16))) __bf16 Yhi[Q * RS];    // ybar [i][p], bf16 rounded
-  __shared__ __attribute__((aligned(16))) __bf16 Ylo[Q * RS];    // ybar - Yhi, bf16 rounded
+  // ybar - Yhi, bf16 rounded (with a gate; without one ybar = dy is exactly bf16)
+  __shared__ __attribute__((aligned(16))) __bf16 Ylo[GATE ? Q * RS : 8];
   __shared__ __attribute__((aligned(16))) __bf16 YT[kP * RS];    // ybar^T [p][i]
   __shared__ __attribute__((aligned(16))) __bf16 XT[kP * RS];    // (phi x)^T [p][j] (gate only)
   __shared__ __attribute__((aligned(16))) __bf16 HT[N * RSP];    // H_c^T [n][p]
@@ -86,8 +86,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
   __shared__ __attribute__((aligned(16))) __bf16 BtS[N * RS];    // B^T [n][j] of the chunk (all heads)
   __shared__ __attribute__((aligned(16))) __bf16 CtS[N * RS];    // C^T [n][i]
   __shared__ __attribute__((aligned(16))) float GS[Q * GST];     // G [i][j], float32 (all heads)
-  __shared__ float sK[Q * KST];
-  __shared__ float sS[Q], sPhi[Q], sRt[Q], sRed[8];
+  __shared__ float sS[Q], sPhi[Q], sRed[8];
+  __shared__ float sKr[Q], sKc[Q];   // row and column sums of K (see the dDelta phase)
   __shared__ float sQv[2][Q], sRv[2][Q], sVv[2][Q];
   __shared__ float sDD[4][kP];
 
@@ -276,18 +276,23 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
       uint32_t* Y32 = reinterpret_cast<uint32_t*>(YT);
 #pragma unroll
       for (int k = 0; k < 8; ++k) Y32[(8 * spg + k) * (RS / 2) + sip] = pack_bf16x2(y0[k], y1[k]);
-      float h0[8], h1[8];
+      if constexpr (gate) {
+        float h0[8], h1[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        h0[k] = (float)(__bf16)y0[k];
-        h1[k] = (float)(__bf16)y1[k];
-        y0[k] -= h0[k];
-        y1[k] -= h1[k];
+        for (int k = 0; k < 8; ++k) {
+          h0[k] = (float)(__bf16)y0[k];
+          h1[k] = (float)(__bf16)y1[k];
+          y0[k] -= h0[k];
+          y1[k] -= h1[k];
+        }
+        *reinterpret_cast<bf16x8*>(&Yhi[(2 * sip) * RS + 8 * spg]) = pack8(h0);
+        *reinterpret_cast<bf16x8*>(&Yhi[(2 * sip + 1) * RS + 8 * spg]) = pack8(h1);
+        *reinterpret_cast<bf16x8*>(&Ylo[(2 * sip) * RS + 8 * spg]) = pack8(y0);
+        *reinterpret_cast<bf16x8*>(&Ylo[(2 * sip + 1) * RS + 8 * spg]) = pack8(y1);
+      } else {
+        *reinterpret_cast<uint4*>(&Yhi[(2 * sip) * RS + 8 * spg]) = pv[0];
+        *reinterpret_cast<uint4*>(&Yhi[(2 * sip + 1) * RS + 8 * spg]) = pv[1];
       }
-      *reinterpret_cast<bf16x8*>(&Yhi[(2 * sip) * RS + 8 * spg]) = pack8(h0);
-      *reinterpret_cast<bf16x8*>(&Yhi[(2 * sip + 1) * RS + 8 * spg]) = pack8(h1);
-      *reinterpret_cast<bf16x8*>(&Ylo[(2 * sip) * RS + 8 * spg]) = pack8(y0);
-      *reinterpret_cast<bf16x8*>(&Ylo[(2 * sip + 1) * RS + 8 * spg]) = pack8(y1);
     }
     if (has_hg) {
       // channels (2 hpp, 2 hpp + 1), states 8 hng .. 8 hng + 7 of H_c and Gc, written transposed
@@ -324,36 +329,32 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
     const float Sq = sS[Q - 1];
     const float Sl = sS[il], phil = sPhi[il];   // this lane's token (column role)
     // this lane's token: ybar and x fragments over the 64 channels (two K steps)
-    bf16x8 yb_own[2], yb_lo[2], x_own[2];
+    bf16x8 yb_own[2], yb_lo[2] = {zero_frag(), zero_frag()}, x_own[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       yb_own[kk] = yhi8(il, 32 * kk + 8 * g);
-      yb_lo[kk] = ylo8(il, 32 * kk + 8 * g);
+      if constexpr (gate) yb_lo[kk] = ylo8(il, 32 * kk + 8 * g);
       x_own[kk] = x8(il, 32 * kk + 8 * g);
     }
 
     // ------------------------------------------------------------------ dC (rows i = own tile)
     float qpart = 0.f;   // this lane's part of ybar_i . Yoff_i (token il, this half's states)
+    // this lane's parts of the row sum (token il as row i) and the column sum (token il as
+    // column j) of K_ij = (C_i . B_j) W_ij, kept by the first half
+    float krow = 0.f, kcol = 0.f;
     {
       // U^T tiles (j tile jt <= tt, i = own): D[j][i] = sum_p x_j[p] ybar_i[p]; the lane holds
-      // U[il][jt 16 + 4 g + r]. W (as the B operand of the next product) and K (to LDS, by the
-      // first half).
+      // U[il][jt 16 + 4 g + r]. W (as the B operand of the next product) and the row sum of K.
       bf16x8 wmA[2] = {zero_frag(), zero_frag()};
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt) {
-        if (jt > tt) {
-          if (hf == 0) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sK[il * KST + jt * 16 + 4 * g + r] = 0.f;
-          }
-          continue;
-        }
+        if (jt > tt) continue;
         f32x4 u = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           const bf16x8 xa = x8(jt * 16 + r16, 32 * kk + 8 * g);
           u = mfma16(xa, yb_own[kk], u);
-          u = mfma16(xa, yb_lo[kk], u);
+          if constexpr (gate) u = mfma16(xa, yb_lo[kk], u);
         }
         const float4 g4 = grow4(il, jt * 16 + 4 * g);
         const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
         for (int r = 0; r < 4; ++r) {
           const int j = jt * 16 + 4 * g + r;
           const float wm = j <= il ? exp2_fast(a2 * (Sl - sS[j])) * sPhi[j] * u[r] : 0.f;
-          if (hf == 0) sK[il * KST + j] = gv[r] * wm;
+          krow += gv[r] * wm;
           wmA[jt >> 1][(jt & 1) * 4 + r] = (__bf16)wm;
         }
       }
@@ -414,7 +415,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           u = mfma16(yhi8(it * 16 + r16, 32 * kk + 8 * g), x_own[kk], u);
-          u = mfma16(ylo8(it * 16 + r16, 32 * kk + 8 * g), x_own[kk], u);
+          if constexpr (gate) u = mfma16(ylo8(it * 16 + r16, 32 * kk + 8 * g), x_own[kk], u);
         }
         const float4 g4 = gcol4(it * 16 + 4 * g, il);   // G[i][il]
         const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
@@ -427,6 +428,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
         }
       }
       if (hf != 0) vin = 0.f;
+      kcol = vin * phil;   // sum_i K_ij = phi_j sum_i (C_i . B_j) exp(a (S_i - S_j)) U_ij
       const float eq = exp2_fast(a2 * (Sq - Sl)) * phil;
       bf16x8 x_sc[2];
 #pragma unroll
@@ -510,7 +512,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
         const int lo = il * RS + pt * 16 + 4 * g;
         const uint2 xr = *reinterpret_cast<const uint2*>(&Xn[lo]);
         const uint2 yhr = *reinterpret_cast<const uint2*>(&Yhi[lo]);
-        const uint2 ylr = *reinterpret_cast<const uint2*>(&Ylo[lo]);
+        const uint2 ylr = gate ? *reinterpret_cast<const uint2*>(&Ylo[lo]) : make_uint2(0u, 0u);
         const float xx[4] = {bf16_lo(xr.x), bf16_hi(xr.x), bf16_lo(xr.y), bf16_hi(xr.y)};
         const float ybr[4] = {bf16_lo(yhr.x) + bf16_lo(ylr.x), bf16_hi(yhr.x) + bf16_hi(ylr.x),
                               bf16_lo(yhr.y) + bf16_lo(ylr.y), bf16_hi(yhr.y) + bf16_hi(ylr.y)};
@@ -618,52 +620,21 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
       qpart += __shfl_xor(qpart, off, 64);
       vvp += __shfl_xor(vvp, off, 64);
       rp += __shfl_xor(rp, off, 64);
+      if (hf == 0) {
+        krow += __shfl_xor(krow, off, 64);
+        kcol += __shfl_xor(kcol, off, 64);
+      }
     }
     if (g == 0) {
       sQv[hf][il] = qpart;
       sVv[hf][il] = vvp;
       sRv[hf][il] = rp;
+      if (hf == 0) {
+        sKr[il] = krow;
+        sKc[il] = kcol;
+      }
     }
     if (kh + 1 < bp.hb) prefetch(kh + 1, tv);
-    __syncthreads();
-
-    // ------------------------------------------------------------------ sum of K over j <= t <= i
-    {
-      // prefix over j of each row i (eight 8-column pieces per row, one per thread)
-      const int i = tid >> 3, seg = tid & 7;
-      float run[8];
-      float acc = 0.f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        acc += sK[i * KST + 8 * seg + k];
-        run[k] = acc;
-      }
-      // exclusive sum of the lower pieces of the row (lanes 8 apart hold other rows)
-      float off = 0.f;
-      const int base = lane & ~7;
-#pragma unroll
-      for (int k = 0; k < 7; ++k) {
-        const float v = __shfl(acc, base + k, 64);
-        if (k < seg) off += v;
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) sK[i * KST + 8 * seg + k] = run[k] + off;
-    }
-    __syncthreads();
-    {
-      // R_t = sum_{i>=t} prefix_i(t): rows 8 seg .. 8 seg + 7 per thread
-      const int t = tid >> 3, seg = tid & 7;
-      float acc = 0.f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int i = 8 * seg + k;
-        if (i >= t) acc += sK[i * KST + t];
-      }
-      acc += __shfl_xor(acc, 1, 64);
-      acc += __shfl_xor(acc, 2, 64);
-      acc += __shfl_xor(acc, 4, 64);
-      if (seg == 0) sRt[t] = acc;
-    }
     __syncthreads();
 
     // ------------------------------------------------------------------ per-token: dDelta
@@ -681,11 +652,27 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
         const float o = __shfl_up(pr, off, 64);
         if (t >= off) pr += o;
       }
+      // sum_{j<=t<=i} K_ij = sum_{s<=t} (column sum)_s - sum_{s<t} (row sum)_s: the columns up
+      // to t hold every K_ij with j <= t, of which those in rows i < t are the rows before t
+      // (K_ij = 0 for j > i)
+      float kc = sKc[t];
+      const float krt = sKr[t];
+      float kr = krt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float oc = __shfl_up(kc, off, 64);
+        const float orr = __shfl_up(kr, off, 64);
+        if (t >= off) {
+          kc += oc;
+          kr += orr;
+        }
+      }
+      const float rt = kc - (kr - krt);
       float red = 0.f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) red += sRed[k];
       const float t1 = exp2_fast(a2 * Sq) * red;
-      const float u = t1 + sq + pr + sRt[t];
+      const float u = t1 + sq + pr + rt;
       const float vv = sVv[0][t] + sVv[1][t];
       const float ddt = a * u + vv;
       const int64_t tt2 = tc0 + t;

@@ -87,8 +87,9 @@ def test_ssd_bwd_layer_full_size_sampled():
 
 @pytest.mark.parametrize("H,G", [(8, 2), (8, 1), (16, 1)])
 def test_ssd_bwd_head_blocks(H, G):
-    """Heads per group a multiple of 4: the main pass sums dB and dC over 4 heads per workgroup and
-    the reduction adds the head blocks of a group (1, 2 and 4 blocks per group here)."""
+    """Heads per group a multiple of 4 and a grid too small for more: the main pass sums dB and dC
+    over 4 heads per workgroup and the reduction adds the head blocks of a group (1, 2 and 4
+    blocks per group here). The full-size case above takes 10 heads per workgroup."""
     inp = inputs.ssd_layer(seed=96 + H + G, Bsz=2, L=333, H=H, N=128, gate=True, dskip=True, h0=True,
                            groups=G if G > 1 else None)
     errs, _ = _run(inp, seed=13)

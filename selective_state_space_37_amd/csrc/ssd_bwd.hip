@@ -752,7 +752,16 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_param_kernel(SsdBwdParams 
     a += bp.ws_pA[k * p.H + h];
     b += bp.ws_pb[k * p.H + h];
   }
-  for (int64_t k = q; k < nbc; k += 4) d += bp.ws_pD[(k * p.H + h) * kP + ch];
+  // eight loads in flight per step, added in the same order as one at a time
+  int64_t k = q;
+  for (; k + 28 < nbc; k += 32) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = bp.ws_pD[((k + 4 * u) * p.H + h) * kP + ch];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) d += v[u];
+  }
+  for (; k < nbc; k += 4) d += bp.ws_pD[(k * p.H + h) * kP + ch];
   sA[tid] = a;
   sB[tid] = b;
   sD[tid] = d;

@@ -454,10 +454,10 @@ __global__ __launch_bounds__(512) void ssd_state_kernel(SsdParams p) {
     auto step = [&](int64_t k, ChunkIn& nxt) __attribute__((always_inline)) {
       const int64_t c = chunk_of(k);
       store_and_decay(c, dec);
-      if (k + 1 < nch) {
-        dec = stage(chunk_of(k + 1), nxt, Xs[(k + 1) & 1], Bs[(k + 1) & 1]);
-        load_chunk(chunk_of(k + 3 < nch ? k + 3 : nch - 1), nxt);
-      }
+      if (k + 1 < nch) dec = stage(chunk_of(k + 1), nxt, Xs[(k + 1) & 1], Bs[(k + 1) & 1]);
+      // (issued on the last step too, where it is not used: with every load of the loop
+      // unconditional the compiler's count of outstanding operations at the loop head is exact)
+      load_chunk(chunk_of(k + 3 < nch ? k + 3 : nch - 1), nxt);
       products(Xs[k & 1], Bs[k & 1]);
       __syncthreads();
     };

@@ -86,7 +86,10 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
   __shared__ __attribute__((aligned(16))) __bf16 BtS[N * RS];    // B^T [n][j] of the chunk (all heads)
   __shared__ __attribute__((aligned(16))) __bf16 CtS[N * RS];    // C^T [n][i]
   __shared__ __attribute__((aligned(16))) float GS[Q * GST];     // G [i][j], float32 (all heads)
-  __shared__ float sS[Q], sPhi[Q], sRed[8];
+  __shared__ float sS[Q], sPhi[Q];
+  // the per-wave parts of <Gc, H_c>, by head parity: wave 0 reads those of head kh in the per-token
+  // phase while the other waves may already stage head kh + 1
+  __shared__ float sRed[2][8];
   __shared__ float sKr[Q], sKc[Q];   // row and column sums of K (see the dDelta phase)
   __shared__ float sQv[2][Q], sRv[2][Q], sVv[2][Q];
   __shared__ float sDD[4][kP];
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
       for (int k = 0; k < 2; ++k) vo[k] = mfma16(pgc[k][ks], pbj[ks], vo[k]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
-    if (lane == 0) sRed[w] = dot;
+    if (lane == 0) sRed[kh & 1][w] = dot;
     __syncthreads();
 
     const float Sq = sS[Q - 1];
@@ -640,39 +643,25 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
     // ------------------------------------------------------------------ per-token: dDelta
     if (w == 0) {
       const int t = lane;
-      float sq = sQv[0][t] + sQv[1][t];   // suffix sum over i >= t
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_down(sq, off, 64);
-        if (t + off < 64) sq += o;
-      }
-      float pr = sRv[0][t] + sRv[1][t];   // prefix sum over j <= t
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(pr, off, 64);
-        if (t >= off) pr += o;
-      }
-      // sum_{j<=t<=i} K_ij = sum_{s<=t} (column sum)_s - sum_{s<t} (row sum)_s: the columns up
-      // to t hold every K_ij with j <= t, of which those in rows i < t are the rows before t
-      // (K_ij = 0 for j > i)
-      float kc = sKc[t];
+      // sq: suffix sum over i >= t of ybar_i . Yoff_i. pv: prefix sum over s <= t of the
+      // Gc B_j input term plus (column sum - row sum) of K: sum_{j<=t<=i} K_ij is the sum over
+      // the columns up to t less the rows before t (K_ij = 0 for j > i), the row sum of t itself
+      // added back below. The two scans run interleaved.
+      float sq = sQv[0][t] + sQv[1][t];
       const float krt = sKr[t];
-      float kr = krt;
+      float pv = sRv[0][t] + sRv[1][t] + sKc[t] - krt;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
-        const float oc = __shfl_up(kc, off, 64);
-        const float orr = __shfl_up(kr, off, 64);
-        if (t >= off) {
-          kc += oc;
-          kr += orr;
-        }
+        const float os = __shfl_down(sq, off, 64);
+        const float op = __shfl_up(pv, off, 64);
+        if (t + off < 64) sq += os;
+        if (t >= off) pv += op;
       }
-      const float rt = kc - (kr - krt);
       float red = 0.f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) red += sRed[k];
+      for (int k = 0; k < 8; ++k) red += sRed[kh & 1][k];
       const float t1 = exp2_fast(a2 * Sq) * red;
-      const float u = t1 + sq + pr + rt;
+      const float u = t1 + sq + pv + krt;
       const float vv = sVv[0][t] + sVv[1][t];
       const float ddt = a * u + vv;
       const int64_t tt2 = tc0 + t;
@@ -699,7 +688,9 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
       }
       bp.ws_pD[pidx * kP + t] = sDD[0][t] + sDD[1][t] + sDD[2][t] + sDD[3][t];
     }
-    __syncthreads();   // the next head restages the LDS tiles
+    // (no barrier here: the next head's staging writes none of what wave 0 reads above, and the
+    // arrays it reads are written again only after the next staging barrier, which wave 0 joins
+    // when done)
   }
 
   // dB and dC of this workgroup's heads: the lane holds states n .. n + 3 of token il

@@ -44,200 +44,275 @@ namespace {
 // whose exponent is at most 64 (it is a2 (S_i - S_e) <= 64 when the floor is not hit, and
 // a2 (S_i - S_j) + 64 <= 64 when it is, since S_i >= S_j). So every mask entry is G_ij times a
 // bounded factor, with the causal cut j <= i on the diagonal tile.
-constexpr int kOutWaves = 8;   // waves per output workgroup
+// One workgroup covers one chunk of one sequence and a run of consecutive heads of one group. The
+// chunk's C rows and its G tiles depend only on the group: each wave loads the C fragments of its
+// row block into registers once, and the G tiles on and below the diagonal (packed by the prep
+// kernel) are copied into LDS once, for every head of the run. Per head only x, the carried-in
+// state and the (S, phi) table are read. Those of the next head are loaded into registers while
+// the current head is computed; per head a wave computes the carried-state term of its rows,
+// waits at a barrier, stages the next head (x^T into the second of two buffers, the carried state,
+// whose single buffer all waves have finished reading), then computes the within-chunk term.
+template <int Q>
+struct SsdOutCfg {
+  static constexpr int NIB = Q / 16;                   // 16-row blocks of the chunk
+  static constexpr int NW = NIB >= 16 ? 16 : 8;        // waves: one row block each
+  static_assert(NIB <= NW, "one row block per wave");
+};
 
 template <int Q, int N>
-__global__ __launch_bounds__(64 * kOutWaves) void ssd_out_kernel(SsdParams p) {
-  __shared__ __attribute__((aligned(16))) __bf16 Xt[kP * (Q + 8)];
-  // the carried-in state h_{c-1} (P x N bf16), staged once for the four waves; rows padded by
-  // 8 elements so a wave's 16-byte fragment reads (16 rows apart by one row) hit 64 banks
-  __shared__ __attribute__((aligned(16))) __bf16 Hs[kP * (N + 8)];
-  __shared__ float sS[Q];
-  const int64_t h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
-  const int64_t nch = gridDim.y;
-  const float a2 = p.A[h] * kLog2e;
-  const int tid = threadIdx.x;
-  const float2* sp = p.ws_sphi + ((b * nch + c) * p.H + h) * Q;
-  if (tid < Q) sS[tid] = sp[tid].x;
-  {
-    // the carried state's loads are issued first, to be in flight during the x staging
-    constexpr int kNT = 64 * kOutWaves, kHPer = kP * N / 8 / kNT;
-    static_assert((kP * N / 8) % kNT == 0, "the state's 16-byte pieces divide over the threads");
-    const bf16_t* hin = static_cast<const bf16_t*>(p.ws_hin) + ((b * nch + c) * p.H + h) * (int64_t)(kP * N);
-    uint4 hv[kHPer];
-#pragma unroll
-    for (int k = 0; k < kHPer; ++k) {
-      const int e = tid + k * kNT, row = e / (N / 8), c8 = (e % (N / 8)) * 8;
-      hv[k] = *reinterpret_cast<const uint4*>(hin + row * N + c8);
-    }
-    stage_x_transposed_scaled<Q, kNT>(p, b, c, h, Xt, sp, a2);
-#pragma unroll
-    for (int k = 0; k < kHPer; ++k) {
-      const int e = tid + k * kNT, row = e / (N / 8), c8 = (e % (N / 8)) * 8;
-      *reinterpret_cast<uint4*>(&Hs[row * (N + 8) + c8]) = hv[k];
-    }
-  }
-  __syncthreads();
+__global__ __launch_bounds__(64 * SsdOutCfg<Q>::NW) void ssd_out_kernel(SsdParams p, int64_t hpw, int64_t wpg) {
+  constexpr int NIB = SsdOutCfg<Q>::NIB, NW = SsdOutCfg<Q>::NW;
+  constexpr int NT = 64 * NW;
+  constexpr int NTILES = NIB * (NIB + 1) / 2; // G tiles on and below the diagonal
+  constexpr int KS = N / 32;                  // K steps over the state dimension
+  constexpr int XS = Q + 8, HSTR = N + 8;     // LDS row strides (bf16) of x^T and of the state
+  constexpr int kItems = (Q / 2) * (kP / 8);  // (token pair, 8-channel group) items of x
+  constexpr int XPER = (kItems + NT - 1) / NT;
+  static_assert(kItems % NT == 0 || kItems < NT, "the x items divide over the threads");
+  constexpr int kHP = kP * N / 8;             // 16-byte pieces of the carried state
+  constexpr int HPER = (kHP + NT - 1) / NT;
+  static_assert(kHP % NT == 0 || kHP < NT, "the state's pieces divide over the threads");
+  __shared__ __attribute__((aligned(16))) __bf16 Gs[NTILES * 256];
+  __shared__ __attribute__((aligned(16))) __bf16 Xt[2][kP * XS];
+  // the carried-in state h_{c-1} (P x N bf16); rows padded by 8 elements so a wave's 16-byte
+  // fragment reads (16 rows apart by one row) hit 64 banks
+  __shared__ __attribute__((aligned(16))) __bf16 Hs[kP * HSTR];
+  __shared__ float sS[2][Q];
 
+  const int64_t c = blockIdx.y, b = blockIdx.z;
+  const int64_t nch = gridDim.y;
+  const int64_t hpg = p.H / p.G;                              // heads per group
+  const int64_t grp = blockIdx.x / wpg;
+  const int64_t h_begin = grp * hpg + (blockIdx.x % wpg) * hpw;
+  const int64_t h_end = std::min<int64_t>((grp + 1) * hpg, h_begin + hpw);
+  if (h_begin >= h_end) return;   // uniform
+  const int nh = (int)(h_end - h_begin);
+  const int tid = threadIdx.x;
   // the wave index is the same for all lanes of a wave: readfirstlane lets the compiler keep it
-  // (and the row blocks derived from it) in scalar registers, so branches on it are not divergent
+  // (and the row block derived from it) in scalar registers, so branches on it are not divergent
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 4, r16 = lane & 15;
-  constexpr int NIB = Q / 16;   // 16-row blocks of the chunk
-  constexpr int KS = N / 32;    // K steps over the state dimension
-  const int64_t grp = h / (p.H / p.G), rs = p.G * N;   // this head's group, token row stride of C
-  const bf16_t* Cg = static_cast<const bf16_t*>(p.Cm) + b * p.L * rs + grp * N;
-  const bf16_t* G = static_cast<const bf16_t*>(p.ws_G) + ((b * p.G + grp) * nch + c) * (int64_t)(Q * Q);
-  const float dsk = p.Dskip && !p.dskip_per_channel ? p.Dskip[h] : 0.f;
+  // This wave's row block. With 16 blocks over 16 waves, the four waves w = s, s + 4, s + 8,
+  // s + 12 take the blocks s, 7 - s, 8 + s, 15 - s (34 tiles of the triangle each), so that the
+  // waves sharing a SIMD (waves are dealt to the four SIMDs in turn) carry equal work.
+  int ib = w;
+  if constexpr (NIB == 16 && NW == 16) {
+    const int sm = w & 3, slot = w >> 2;
+    ib = slot == 0 ? sm : slot == 1 ? 7 - sm : slot == 2 ? 8 + sm : 15 - sm;
+  }
+  const bool active = ib < NIB;   // uniform
+  const int64_t L = p.L, H = p.H, rs = p.G * N;   // token row stride of B and C
+  const bf16_t* xg = static_cast<const bf16_t*>(p.x);
   const bf16_t* zg = static_cast<const bf16_t*>(p.z);
   bf16_t* yg = static_cast<bf16_t*>(p.y);
 
-  // Balanced triangle: block x and block NIB-1-x hold NIB+1 tiles together.
-  constexpr int kBlocksPerWave = NIB >= 2 * kOutWaves ? NIB / kOutWaves : 1;
-  auto block_of = [&](int kb) {
-    if (NIB < 2 * kOutWaves) return w;
-    const int pair = w + kOutWaves * (kb >> 1);
-    return (kb & 1) ? (NIB - 1 - pair) : pair;
+  // ---- per-head inputs, loaded one head ahead into registers. Every load is unconditional:
+  // tokens past L read the last token, whose phi is 0 when padded (its staged x is then 0), and
+  // threads past the x items repeat the last item (their LDS writes are skipped).
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  struct HeadIn {
+    u32x4 x0[XPER], x1[XPER];   // tokens 2 jp and 2 jp + 1, 8 channels each
+    f32x2 s0[XPER], s1[XPER];   // their (S, phi)
+    float se[XPER];             // S at the end of their 16-token tile
+    u32x4 hv[HPER];             // pieces of the carried-in state
   };
-  // carried-state fragments (the A operand of the carried term), the same for every row block;
-  // every product here is computed transposed (channels x tokens) so a lane ends up holding four
-  // consecutive channels of one token
-  // (read from LDS at each use: kept in registers they would cost 16 KN / 8 VGPRs per lane)
-  auto hfrag = [&](int ks, int pt) __attribute__((always_inline)) {
-    return *reinterpret_cast<const bf16x8*>(&Hs[(pt * 16 + r16) * (N + 8) + ks * 32 + 8 * g]);
+  // Addressing: per head a wave-uniform base (the chunk's first row of the head, its (S, phi)
+  // table, its carried state) plus per-lane 32-bit byte offsets that are the same for every head
+  // (tokens past L clamped to the last token). They stay below 2^31: a chunk of x spans
+  // Q H P 2 bytes with Q <= 256, P = 64 and H <= 65535 (checked on the host).
+  uint32_t xo0[XPER], xo1[XPER], so0[XPER];
+#pragma unroll
+  for (int k = 0; k < XPER; ++k) {
+    const int gi = std::min(tid + k * NT, kItems - 1);
+    const int jp = gi / (kP / 8), pg = gi % (kP / 8);
+    const int64_t t0 = std::min<int64_t>(c * Q + 2 * jp, L - 1) - c * Q;
+    const int64_t t1 = std::min<int64_t>(c * Q + 2 * jp + 1, L - 1) - c * Q;
+    xo0[k] = (uint32_t)((t0 * H * kP + pg * 8) * 2);
+    xo1[k] = (uint32_t)((t1 * H * kP + pg * 8) * 2);
+    so0[k] = (uint32_t)(2 * jp * 8);
+  }
+  const bf16_t* xchunk = xg + (b * L + c * Q) * H * kP;   // the chunk's first row, head 0
+  auto load_head = [&](int64_t hh, HeadIn& in) __attribute__((always_inline)) {
+    const float2* sp = p.ws_sphi + ((b * nch + c) * H + hh) * Q;
+    const bf16_t* xh = xchunk + hh * kP;
+#pragma unroll
+    for (int k = 0; k < XPER; ++k) {
+      in.x0[k] = ld_at<u32x4>(xh, xo0[k]);
+      in.x1[k] = ld_at<u32x4>(xh, xo1[k]);
+      in.s0[k] = ld_at<f32x2>(sp, so0[k]);
+      in.s1[k] = ld_at<f32x2>(sp, so0[k] + 8u);
+      in.se[k] = ld_at<float>(sp, so0[k] | 120u);   // token (2 jp) | 15
+    }
+    const bf16_t* hin = static_cast<const bf16_t*>(p.ws_hin) + ((b * nch + c) * H + hh) * (int64_t)(kP * N);
+#pragma unroll
+    for (int k = 0; k < HPER; ++k) in.hv[k] = ld_at<u32x4>(hin, (uint32_t)(std::min(tid + k * NT, kHP - 1) * 16));
   };
-  auto load_c = [&](int ib, bf16x8 out[KS]) {
-    const int64_t ti = c * Q + ib * 16 + r16;
+  // x^T of the head scaled by cp_j = 2^max(a2 (S_e - S_j), -64) phi_j (two tokens of one channel
+  // per 32-bit word, word column XORed by xt_swizzle_words) into buffer buf, S (written by the
+  // threads of the first channel group of each token pair) and the carried state
+  auto stage = [&](const HeadIn& in, int buf, float a2) __attribute__((always_inline)) {
+    uint32_t* X32 = reinterpret_cast<uint32_t*>(Xt[buf]);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      out[ks] = ti < p.L ? load_frag(Cg + ti * rs + ks * 32 + 8 * g) : zero_frag();
+    for (int k = 0; k < XPER; ++k) {
+      const int gi = tid + k * NT;
+      if (kItems < NT && gi >= kItems) continue;
+      const int jp = gi / (kP / 8), pg = gi % (kP / 8);
+      const float cp0 = exp2_fast(fmaxf(a2 * (in.se[k] - in.s0[k].x), kSsdStageExpFloor)) * in.s0[k].y;
+      const float cp1 = exp2_fast(fmaxf(a2 * (in.se[k] - in.s1[k].x), kSsdStageExpFloor)) * in.s1[k].y;
+      if (pg == 0) {
+        sS[buf][2 * jp] = in.s0[k].x;
+        sS[buf][2 * jp + 1] = in.s1[k].x;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // channels 2q (low halves) and 2q+1 (high halves) of the two tokens
+        const int ra = pg * 8 + 2 * q, rb = ra + 1;
+        X32[ra * (XS / 2) + (jp ^ xt_swizzle_words<Q>(ra))] = pack_bf16x2(bf16_lo(in.x0[k][q]) * cp0, bf16_lo(in.x1[k][q]) * cp1);
+        X32[rb * (XS / 2) + (jp ^ xt_swizzle_words<Q>(rb))] = pack_bf16x2(bf16_hi(in.x0[k][q]) * cp0, bf16_hi(in.x1[k][q]) * cp1);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < HPER; ++k) {
+      const int e = tid + k * NT, row = e / (N / 8), c8 = (e % (N / 8)) * 8;
+      if (kHP < NT && e >= kHP) continue;
+      *reinterpret_cast<u32x4*>(&Hs[row * HSTR + c8]) = in.hv[k];
+    }
   };
-  bf16x8 cnext[KS];
-  if (NIB >= kOutWaves || w < NIB) load_c(block_of(0), cnext);
-  // fully unrolled: the C fragments loaded one block ahead are then renamed, not copied (a copy
-  // of registers with loads in flight would wait for them at the end of the previous block)
-#pragma unroll
-  for (int kb = 0; kb < kBlocksPerWave; ++kb) {
-    const int ib = block_of(kb);
-    if (ib >= NIB) break;
-    bf16x8 cf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) cf[ks] = cnext[ks];
-    if (kb + 1 < kBlocksPerWave) load_c(block_of(kb + 1), cnext);
-    const int i0 = ib * 16;
-    const int il = i0 + r16;                  // this lane's token row of M (B operand)
-    const float Si = sS[il];
-    const bf16_t* Grow = G + (int64_t)il * Q;  // G[il][j]: the lane's four j of a tile are contiguous
 
+  // ---- the group's operands: this wave's C fragments (registers) and the packed G tiles (LDS)
+  HeadIn in;
+  load_head(h_begin, in);
+  bf16x8 cf[KS];   // C rows of the block (B operand of the carried term: column i, k = n)
+  {
+    const bf16_t* Cg = static_cast<const bf16_t*>(p.Cm) + b * L * rs + grp * N;
+    // rows past L take the last token's C: their outputs are never stored
+    const int64_t ti = std::min<int64_t>(c * Q + (active ? ib : 0) * 16 + r16, L - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) cf[ks] = load_frag(Cg + ti * rs + ks * 32 + 8 * g);
+    const u32x4* Gg = reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(p.ws_G) +
+                                                     ((b * p.G + grp) * nch + c) * (int64_t)(Q * Q));
+    constexpr int kG16 = NTILES * 256 / 8;   // 16-byte pieces
+    for (int e = tid; e < kG16; e += NT) reinterpret_cast<u32x4*>(Gs)[e] = Gg[e];
+  }
+  stage(in, 0, p.A[h_begin] * kLog2e);
+  load_head(h_begin + (nh > 1 ? 1 : 0), in);
+  __syncthreads();
+
+  // ---- the run of heads. Every product is computed transposed (channels x tokens), so a lane
+  // ends up holding four consecutive channels of one token: acc[pt][r] = y[il][pt 16 + 4 g + r].
+  const int il = (active ? ib : 0) * 16 + r16;   // this lane's token row of M (B operand)
+  // this lane's row of the block's G tiles: G[il][16 jt + 4 g .. + 3] at grow + 256 jt
+  const __bf16* grow = &Gs[((active ? ib : 0) * ((active ? ib : 0) + 1) / 2) * 256 + r16 * 16 + 4 * g];
+  for (int k = 0; k < nh; ++k) {
+    const int64_t hh = h_begin + k;
+    const int buf = k & 1;
+    const float a2 = p.A[hh] * kLog2e;
+    const float* S = sS[buf];
+    const float Si = S[il];
     f32x4 acc[4];
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // carried state: exp(a S_i) C_i . h_in[p, :]
-    {
+    // carried state: exp(a S_i) (C_i . h_in[p, :]), the row factor applied to the product
+    if (active) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+          acc[pt] = mfma16(*reinterpret_cast<const bf16x8*>(&Hs[(pt * 16 + r16) * HSTR + ks * 32 + 8 * g]), cf[ks],
+                           acc[pt]);
+    }
+    __syncthreads();   // every wave is done with the carried state of head k
+    if (k + 1 < nh) stage(in, buf ^ 1, p.A[hh + 1] * kLog2e);
+    // (issued on the last heads too, repeating the last head: with every load of the loop
+    // unconditional the compiler's count of outstanding memory operations stays exact)
+    load_head(h_begin + std::min(k + 2, nh - 1), in);
+    if (active) {
       const float eSi = exp2_fast(a2 * Si);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 av;
+      for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-        for (int q = 0; q < 8; ++q) av[q] = (__bf16)((float)cf[ks][q] * eSi);
+        for (int r = 0; r < 4; ++r) acc[pt][r] *= eSi;
+      const __bf16* X = Xt[buf];
+      // within the chunk: masked G_ij decay phi_j times x_j, two 16-token j tiles per product
+#pragma unroll 1
+      for (int jp = 0; 2 * jp <= ib; ++jp) {
+        float m[8];
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) acc[pt] = mfma16(hfrag(ks, pt), av, acc[pt]);
-      }
-    }
-
-    // within the chunk: masked G_ij decay phi_j times x_j, two 16-token j tiles per product;
-    // the G tiles of the next pair are requested while the current pair is processed
-    auto load_g = [&](int jt) {
-      return jt <= ib ? *reinterpret_cast<const uint2*>(Grow + jt * 16 + 4 * g) : make_uint2(0, 0);
-    };
-    // fully unrolled (at most NIB / 2 pairs, leaving at the diagonal): the G tiles are requested
-    // kGPairs pairs ahead into registers named by tile, so several tiles' loads are in flight
-    // while the current pair is processed
-    constexpr int kGPairs = 4;
-    uint2 gt[NIB + 2];
+        for (int half = 0; half < 2; ++half) {
+          const int jt = 2 * jp + half;
+          const int j0 = jt * 16 + 4 * g;
+          if (jt < ib) {
+            const uint2 gw = *reinterpret_cast<const uint2*>(grow + jt * 256);
+            const float r = exp2_fast(a2 * (Si - S[jt * 16 + 15]));
+            m[half * 4 + 0] = bf16_lo(gw.x) * r;
+            m[half * 4 + 1] = bf16_hi(gw.x) * r;
+            m[half * 4 + 2] = bf16_lo(gw.y) * r;
+            m[half * 4 + 3] = bf16_hi(gw.y) * r;
+          } else if (jt == ib) {
+            const uint2 gw = *reinterpret_cast<const uint2*>(grow + jt * 256);
+            const float gv[4] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y)};
+            const float Se = S[jt * 16 + 15];
 #pragma unroll
-    for (int t = 0; t < 2 * kGPairs && t < NIB; ++t) gt[t] = load_g(t);
+            for (int q = 0; q < 4; ++q) {
+              const float Sj = S[j0 + q];
+              const float r = exp2_fast(a2 * (Si - Sj) - fmaxf(a2 * (Se - Sj), kSsdStageExpFloor));
+              m[half * 4 + q] = (j0 + q <= il) ? gv[q] * r : 0.f;
+            }
+          } else {
 #pragma unroll
-    for (int jp = 0; jp < (NIB + 1) / 2; ++jp) {
-      if (2 * jp > ib) break;   // uniform (ib is a scalar)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int t = 2 * (jp + kGPairs) + u;
-        if (t < NIB) gt[t] = load_g(t);
-      }
-      const uint2 gcur[2] = {gt[2 * jp], 2 * jp + 1 < NIB ? gt[2 * jp + 1] : make_uint2(0, 0)};
-      float m[8];
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int jt = 2 * jp + half;
-        const uint2 gw = gcur[half];
-        const float gv[4] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y)};
-        const int j0 = jt * 16 + 4 * g;
-        if (jt < ib) {
-          const float r = exp2_fast(a2 * (Si - sS[jt * 16 + 15]));
-#pragma unroll
-          for (int q = 0; q < 4; ++q) m[half * 4 + q] = gv[q] * r;
-        } else if (jt == ib) {
-          const float Se = sS[jt * 16 + 15];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float Sj = sS[j0 + q];
-            const float r = exp2_fast(a2 * (Si - Sj) - fmaxf(a2 * (Se - Sj), kSsdStageExpFloor));
-            m[half * 4 + q] = (j0 + q <= il) ? gv[q] * r : 0.f;
+            for (int q = 0; q < 4; ++q) m[half * 4 + q] = 0.f;
           }
-        } else {
+        }
+        const bf16x8 av = __builtin_bit_cast(
+            bf16x8, make_uint4(pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3]), pack_bf16x2(m[4], m[5]),
+                               pack_bf16x2(m[6], m[7])));
+        const int jb = jp * 32;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) m[half * 4 + r] = 0.f;
+        for (int pt = 0; pt < 4; ++pt) {
+          const int sw = 2 * xt_swizzle_words<Q>(pt * 16);   // in bf16 elements, uniform over the wave
+          const uint2 lo = *reinterpret_cast<const uint2*>(&X[(pt * 16 + r16) * XS + ((jb + 4 * g) ^ sw)]);
+          const uint2 hi = *reinterpret_cast<const uint2*>(&X[(pt * 16 + r16) * XS + ((jb + 16 + 4 * g) ^ sw)]);
+          const uint4 pk = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          acc[pt] = mfma16(__builtin_bit_cast(bf16x8, pk), av, acc[pt]);
         }
       }
-      bf16x8 av;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) av[q] = (__bf16)m[q];
-      const int jb = jp * 32;
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const int sw = 2 * xt_swizzle_words<Q>(pt * 16);   // in bf16 elements, uniform over the wave
-        const uint2 lo = *reinterpret_cast<const uint2*>(&Xt[(pt * 16 + r16) * (Q + 8) + ((jb + 4 * g) ^ sw)]);
-        const uint2 hi = *reinterpret_cast<const uint2*>(&Xt[(pt * 16 + r16) * (Q + 8) + ((jb + 16 + 4 * g) ^ sw)]);
-        const uint4 pk = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        acc[pt] = mfma16(__builtin_bit_cast(bf16x8, pk), av, acc[pt]);
-      }
-    }
 
-    // epilogue: D term, gate, store. acc[pt][r] = y[i0 + r16][pt * 16 + 4 g + r], so each lane
-    // finishes four consecutive channels of one token (8-byte loads of x and z, 8-byte store).
-    const int64_t t = c * Q + i0 + r16;
-    if (t < p.L) {
-      const int64_t orow = ((b * p.L + t) * p.H + h) * kP + 4 * g;
+      // epilogue: D term, gate, store (8-byte loads of x and z, 8-byte store)
+      if (c * Q + il < L) {
+        const float dsk = p.Dskip && !p.dskip_per_channel ? p.Dskip[hh] : 0.f;
+        // byte offset of the lane's output row from the head's first row of the chunk
+        const uint32_t orow = (uint32_t)((il * H * kP + 4 * g) * 2);
+        const bf16_t* xh = xchunk + hh * kP;
+        bf16_t* yh = yg + (b * L + c * Q) * H * kP + hh * kP;
+        const bf16_t* zh = zg ? zg + (b * L + c * Q) * H * kP + hh * kP : nullptr;
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const int64_t o = orow + pt * 16;
-        float v[4] = {acc[pt][0], acc[pt][1], acc[pt][2], acc[pt][3]};
-        if (p.Dskip) {
-          const uint2 xr = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(p.x) + o);
-          float d[4] = {dsk, dsk, dsk, dsk};
-          if (p.dskip_per_channel) {   // channels pt 16 + 4 g .. + 3 of head h
-            const float4 dv = *reinterpret_cast<const float4*>(p.Dskip + h * kP + pt * 16 + 4 * g);
-            d[0] = dv.x; d[1] = dv.y; d[2] = dv.z; d[3] = dv.w;
+        for (int pt = 0; pt < 4; ++pt) {
+          const uint32_t o = orow + pt * 32;
+          float v[4] = {acc[pt][0], acc[pt][1], acc[pt][2], acc[pt][3]};
+          if (p.Dskip) {
+            const uint2 xr = ld_at<uint2>(xh, o);
+            float d[4] = {dsk, dsk, dsk, dsk};
+            if (p.dskip_per_channel) {   // channels pt 16 + 4 g .. + 3 of head hh
+              const float4 dv = *reinterpret_cast<const float4*>(p.Dskip + hh * kP + pt * 16 + 4 * g);
+              d[0] = dv.x; d[1] = dv.y; d[2] = dv.z; d[3] = dv.w;
+            }
+            v[0] = fmaf(d[0], bf16_lo(xr.x), v[0]);
+            v[1] = fmaf(d[1], bf16_hi(xr.x), v[1]);
+            v[2] = fmaf(d[2], bf16_lo(xr.y), v[2]);
+            v[3] = fmaf(d[3], bf16_hi(xr.y), v[3]);
           }
-          v[0] = fmaf(d[0], bf16_lo(xr.x), v[0]);
-          v[1] = fmaf(d[1], bf16_hi(xr.x), v[1]);
-          v[2] = fmaf(d[2], bf16_lo(xr.y), v[2]);
-          v[3] = fmaf(d[3], bf16_hi(xr.y), v[3]);
+          if (zh) {
+            const uint2 zr = ld_at<uint2>(zh, o);
+            v[0] *= silu(bf16_lo(zr.x));
+            v[1] *= silu(bf16_hi(zr.x));
+            v[2] *= silu(bf16_lo(zr.y));
+            v[3] *= silu(bf16_hi(zr.y));
+          }
+          st_at(yh, o, make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])));
         }
-        if (zg) {
-          const uint2 zr = *reinterpret_cast<const uint2*>(zg + o);
-          v[0] *= silu(bf16_lo(zr.x));
-          v[1] *= silu(bf16_hi(zr.x));
-          v[2] *= silu(bf16_lo(zr.y));
-          v[3] *= silu(bf16_hi(zr.y));
-        }
-        uint2 out;
-        out.x = pack_bf16x2(v[0], v[1]);
-        out.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(yg + o) = out;
       }
     }
+    __syncthreads();   // head k + 1 staged; every wave is done with x^T of head k
   }
 }
 
@@ -249,8 +324,14 @@ hipError_t launch_qn(const SsdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((ssd_prep_kernel<Q, N>), dim3(4, (unsigned)nch, (unsigned)(p.B * p.G)), dim3(256), 0, stream,
                      p);
   hipLaunchKernelGGL((ssd_state_kernel<Q, N>), dim3((unsigned)p.H, (unsigned)p.B), dim3(512), 0, stream, p);
-  hipLaunchKernelGGL((ssd_out_kernel<Q, N>), dim3((unsigned)p.H, (unsigned)nch, (unsigned)p.B), dim3(64 * kOutWaves), 0,
-                     stream, p);
+  // output workgroups: runs of hpw heads inside one group, wpg runs per group, aiming at one
+  // workgroup per CU (256) before splitting a group's heads further
+  const int64_t hpg = p.H / p.G;
+  int64_t wpg = std::min<int64_t>(hpg, std::max<int64_t>(1, (256 + p.B * nch * p.G - 1) / (p.B * nch * p.G)));
+  const int64_t hpw = (hpg + wpg - 1) / wpg;
+  wpg = (hpg + hpw - 1) / hpw;
+  hipLaunchKernelGGL((ssd_out_kernel<Q, N>), dim3((unsigned)(p.G * wpg), (unsigned)nch, (unsigned)p.B),
+                     dim3(64 * SsdOutCfg<Q>::NW), 0, stream, p, hpw, wpg);
   return hipGetLastError();
 }
 

@@ -163,8 +163,9 @@ __global__ __launch_bounds__(256) void ssd_cumsum_kernel(SsdParams p) {
 // grid (4, chunks, B G): part `part` transposes states [part N/4, (part+1) N/4) of one group's B
 // and computes every fourth lower-triangular 16 x 16 tile of that group's G (row blocks ib,
 // column tiles jt <= ib). Token t's row of the group starts at element (t G + grp) N.
-// BWD: C is transposed as well (ws_Ct), and G is stored in float32 (ws_G) for the backward's
-// elementwise use. Only the tiles on and below the diagonal of G are written.
+// BWD: C is transposed as well (ws_Ct), and G is stored in float32 (ws_G, [Q][Q]) for the
+// backward's elementwise use. Only the tiles on and below the diagonal of G are written; the
+// forward packs them (bf16) in row-block order for the output kernel's LDS copy.
 template <int Q, int N, bool BWD = false>
 __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
   const int part = blockIdx.x;
@@ -219,8 +220,11 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) G32[(int64_t)(ib * 16 + 4 * g + r) * Q + jt * 16 + r16] = acc[r];
     } else {
+      // forward: bf16, the lower-triangular tiles packed in row-block order (tile (ib, jt) is the
+      // 256 elements at ib (ib + 1) / 2 + jt, row-major)
+      bf16_t* Gt = G + (int64_t)(ib * (ib + 1) / 2 + jt) * 256;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) G[(int64_t)(ib * 16 + 4 * g + r) * Q + jt * 16 + r16].bits = f32_to_bf16(acc[r]);
+      for (int r = 0; r < 4; ++r) Gt[(4 * g + r) * 16 + r16].bits = f32_to_bf16(acc[r]);
     }
   }
 }

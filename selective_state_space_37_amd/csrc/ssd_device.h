@@ -176,9 +176,18 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
   const int64_t rs = p.G * N;                      // token row stride of B and C
   const bf16_t* Bg = static_cast<const bf16_t*>(p.Bm) + b * p.L * rs + grp * N;
   const bf16_t* Cg = static_cast<const bf16_t*>(p.Cm) + b * p.L * rs + grp * N;
-  // transposed B: Bt[n][j], 8 tokens per 16-byte store
+  // transposed B, 8 tokens per 16-byte store. Backward: Bt[n][j]. Forward: in the order the
+  // forward's chunk-state kernel reads its MFMA operands (v_mfma_f32_32x32x16_bf16, A = B^T): the
+  // piece (n, j0 .. j0 + 7) of 32-row tile nt = n / 32 and 16-token step s = j0 / 16 is lane
+  // n % 32 + 32 ((j0 / 8) % 2) of the 1 KB fragment (nt, s), fragments in the order
+  // nt Q / 16 + s, so that one fragment load of a wave is 1 KB of consecutive memory.
   bf16_t* Bt = static_cast<bf16_t*>(p.ws_Bt) + (bg * nch + c) * (int64_t)(N * Q);
   constexpr int NQ = N / 4;
+  auto piece_off = [](int n, int j0) -> int64_t {
+    if constexpr (BWD) return (int64_t)n * Q + j0;
+    const int frag = (n / 32) * (Q / 16) + j0 / 16, ln = n % 32 + 32 * ((j0 / 8) % 2);
+    return (int64_t)frag * 512 + ln * 8;
+  };
   auto transpose = [&](const bf16_t* src, bf16_t* dst) {
     for (int it = tid; it < NQ * (Q / 8); it += 256) {
       const int n = part * NQ + it / (Q / 8);
@@ -192,7 +201,7 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
         if (t0 + 1 < p.L) hi = src[(t0 + 1) * rs + n].bits;
         wv[q] = lo | (hi << 16);
       }
-      *reinterpret_cast<uint4*>(dst + (int64_t)n * Q + j0) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      *reinterpret_cast<uint4*>(dst + piece_off(n, j0)) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
     }
   };
   transpose(Bg, Bt);

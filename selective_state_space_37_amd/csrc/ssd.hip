@@ -234,35 +234,7 @@ __global__ __launch_bounds__(64 * SsdOutCfg<Q>::NW) void ssd_out_kernel(SsdParam
         for (int r = 0; r < 4; ++r) acc[pt][r] *= eSi;
       const __bf16* X = Xt[buf];
       // within the chunk: masked G_ij decay phi_j times x_j, two 16-token j tiles per product
-#pragma unroll 1
-      for (int jp = 0; 2 * jp <= ib; ++jp) {
-        float m[8];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int jt = 2 * jp + half;
-          const int j0 = jt * 16 + 4 * g;
-          if (jt < ib) {
-            const uint2 gw = *reinterpret_cast<const uint2*>(grow + jt * 256);
-            const float r = exp2_fast(a2 * (Si - S[jt * 16 + 15]));
-            m[half * 4 + 0] = bf16_lo(gw.x) * r;
-            m[half * 4 + 1] = bf16_hi(gw.x) * r;
-            m[half * 4 + 2] = bf16_lo(gw.y) * r;
-            m[half * 4 + 3] = bf16_hi(gw.y) * r;
-          } else if (jt == ib) {
-            const uint2 gw = *reinterpret_cast<const uint2*>(grow + jt * 256);
-            const float gv[4] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y)};
-            const float Se = S[jt * 16 + 15];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float Sj = S[j0 + q];
-              const float r = exp2_fast(a2 * (Si - Sj) - fmaxf(a2 * (Se - Sj), kSsdStageExpFloor));
-              m[half * 4 + q] = (j0 + q <= il) ? gv[q] * r : 0.f;
-            }
-          } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) m[half * 4 + q] = 0.f;
-          }
-        }
+      auto pair_product = [&](int jp, const float (&m)[8]) __attribute__((always_inline)) {
         const bf16x8 av = __builtin_bit_cast(
             bf16x8, make_uint4(pack_bf16x2(m[0], m[1]), pack_bf16x2(m[2], m[3]), pack_bf16x2(m[4], m[5]),
                                pack_bf16x2(m[6], m[7])));
@@ -275,6 +247,51 @@ __global__ __launch_bounds__(64 * SsdOutCfg<Q>::NW) void ssd_out_kernel(SsdParam
           const uint4 pk = make_uint4(lo.x, lo.y, hi.x, hi.y);
           acc[pt] = mfma16(__builtin_bit_cast(bf16x8, pk), av, acc[pt]);
         }
+      };
+      // an off-diagonal tile jt < ib: G_ij exp(a (S_i - S_e)), one exp per lane and tile
+      auto off_tile = [&](int jt, float* m) __attribute__((always_inline)) {
+        const uint2 gw = *reinterpret_cast<const uint2*>(grow + jt * 256);
+        const float r = exp2_fast(a2 * (Si - S[jt * 16 + 15]));
+        m[0] = bf16_lo(gw.x) * r;
+        m[1] = bf16_hi(gw.x) * r;
+        m[2] = bf16_lo(gw.y) * r;
+        m[3] = bf16_hi(gw.y) * r;
+      };
+      // pairs of two off-diagonal tiles
+#pragma unroll 1
+      for (int jp = 0; jp < ib / 2; ++jp) {
+        float m[8];
+        off_tile(2 * jp, m);
+        off_tile(2 * jp + 1, m + 4);
+        pair_product(jp, m);
+      }
+      // the pair holding the diagonal tile ib, whose other tile is off-diagonal (ib odd) or above
+      // the diagonal (ib even, zero); on the diagonal each entry is
+      // 2^(a2 (S_i - S_j) - max(a2 (S_e - S_j), -64)), cut at j <= i
+      {
+        float m[8];
+        const int jd = ib, hd = ib & 1;   // diagonal tile and its half of the pair
+        if (hd) off_tile(ib - 1, m);
+        const uint2 gw = *reinterpret_cast<const uint2*>(grow + jd * 256);
+        const float gv[4] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y)};
+        const float Se = S[jd * 16 + 15];
+        const int j0 = jd * 16 + 4 * g;
+        float md[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float Sj = S[j0 + q];
+          const float r = exp2_fast(a2 * (Si - Sj) - fmaxf(a2 * (Se - Sj), kSsdStageExpFloor));
+          md[q] = (j0 + q <= il) ? gv[q] * r : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (hd) m[4 + q] = md[q];
+          else {
+            m[q] = md[q];
+            m[4 + q] = 0.f;
+          }
+        }
+        pair_product(ib / 2, m);
       }
 
       // epilogue: D term, gate, store (8-byte loads of x and z, 8-byte store)

@@ -142,8 +142,10 @@ struct SsdParams {
   float* h_last;           // nullable
   int delta_softplus;
   void* ws_hin;            // bf16 [B, nchunks, H, P, N]: state entering each chunk
-  void* ws_G;              // bf16 [B, G, nchunks, Q, Q]: C_i . B_j inside each chunk
-  void* ws_Bt;             // bf16 [B, G, nchunks, N, Q]: B of each chunk, transposed
+  void* ws_G;              // forward: bf16 tiles of C_i . B_j on and below the diagonal, per chunk
+  void* ws_Bt;             // backward: bf16 [B, G, nchunks, N, Q]: B of each chunk, transposed
+  void* ws_Btf;            // bf16 [B, G, nchunks, N Q]: B^T of each chunk in MFMA fragment order
+  void* ws_Ctf;            // backward: the same for C
   float2* ws_sphi;         // [B, nchunks, H, Q]: (inclusive cumulative Delta, ZOH input scale)
   // backward only (NULL in the forward)
   const void* dy;          // bf16 [B, L, H, P]: dL/dy
@@ -151,7 +153,7 @@ struct SsdParams {
   float* dh0;              // nullable [B, H, P, N] (out)
   void* ws_gout;           // bf16 [B, nchunks, H, P, N]: dL/d(state leaving each chunk)
   void* ws_Ct;             // bf16 [B, G, nchunks, N, Q]: C of each chunk, transposed
-                           // (in the backward ws_G holds G in float32)
+                           // (in the backward ws_G holds G in float32, [Q][Q])
 };
 
 size_t ssd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);

@@ -333,199 +333,6 @@ __global__ __launch_bounds__(64 * SsdOutCfg<Q>::NW) void ssd_out_kernel(SsdParam
   }
 }
 
-// ---------------------------------------------------------------------------- chunk states
-// grid (H, B), N / 32 waves: one head, sequential over the chunks, with the P x N state in MFMA
-// accumulators. Wave w owns the states n in [32 w, 32 w + 32) for every channel p, as two
-// 32 x 32 tiles of D[n][p] (v_mfma_f32_32x32x16_bf16, computed transposed: states x channels).
-// Per chunk, in order:
-//   store h_{c-1} (bf16, the carried state the output kernel needs), decay it by exp(a S_last),
-//   stage the next chunk's x^T scaled by w_j = exp(a (S_last - S_j)) phi_j into the other of two
-//   LDS buffers, then h_c += sum_j B_j^T (w_j x_j) over the chunk (K = Q), one barrier.
-// The B^T operand (the prep kernel's transposed B, row n, eight consecutive tokens per lane) comes
-// straight from global memory into registers one chunk ahead; each wave reads only its own 32
-// rows, so nothing is loaded twice. x for chunk c + 2 is loaded into registers while chunk c runs.
-// 32 x 32 output layout (lane l, value v): column l % 32, row 8 (v / 4) + 4 (l / 32) + v % 4.
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-template <int Q, int N>
-__global__ __launch_bounds__(64 * (N / 32)) void ssd_state32_kernel(SsdParams p) {
-  constexpr int NW = N / 32, NT = 64 * NW;
-  constexpr int KQ = Q / 16;                 // 16-token steps per chunk
-  constexpr int XS = Q + 8;                  // LDS row stride (bf16) of x^T
-  constexpr int kItems = (Q / 2) * (kP / 8);    // (token pair, 8-channel group) items of x
-  static_assert(kItems % NT == 0 || kItems < NT, "the x items divide over the threads");
-  constexpr int XPER = (kItems + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) __bf16 Xs[2][kP * XS];
-  const int64_t h = blockIdx.x, b = blockIdx.y;
-  const int64_t nch = (p.L + Q - 1) / Q;
-  const int64_t L = p.L, H = p.H;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hi = lane >> 5;
-  const float a2 = p.A[h] * kLog2e;
-  const int64_t PN = (int64_t)kP * N;
-  const int64_t bg = b * p.G + h / (H / p.G);   // this head's (batch, group)
-  const bf16_t* Bt_all = static_cast<const bf16_t*>(p.ws_Bt) + bg * nch * (int64_t)(N * Q);
-
-  // state element (n, p) of value v of tile pt: n = 32 w + 8 (v / 4) + 4 hi + v % 4, p = 32 pt + l32
-  f32x16 acc[2];
-  const float* s_init = p.h0;
-#pragma unroll
-  for (int pt = 0; pt < 2; ++pt) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[pt][v] = 0.f;
-    if (s_init) {
-      const float* src = s_init + (b * H + h) * PN + (int64_t)(32 * pt + l32) * N + 32 * w + 4 * hi;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 v4 = *reinterpret_cast<const float4*>(src + 8 * k);
-        acc[pt][4 * k + 0] = v4.x; acc[pt][4 * k + 1] = v4.y; acc[pt][4 * k + 2] = v4.z; acc[pt][4 * k + 3] = v4.w;
-      }
-    }
-  }
-
-  // ---- x of a chunk: item = (token pair jp, channel group pg of 8), so the eight lanes of a row
-  // load its 128 bytes in one instruction; tokens past L read the last token (its weight is 0
-  // when padded)
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  struct ChunkX {
-    u32x4 x[XPER][2];      // [item][token]: 8 channels
-    f32x2 sp[XPER][2];     // (S, phi) of the two tokens
-    float s_last;
-  };
-  const bf16_t* xg = static_cast<const bf16_t*>(p.x);
-  auto load_x = [&](int64_t c, ChunkX& in) __attribute__((always_inline)) {
-    const float2* sp = p.ws_sphi + ((b * nch + c) * H + h) * Q;
-#pragma unroll
-    for (int k = 0; k < XPER; ++k) {
-      const int it = std::min(tid + k * NT, kItems - 1), jp = it / (kP / 8), pg = it % (kP / 8);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int64_t t = std::min<int64_t>(c * Q + 2 * jp + u, L - 1);
-        in.x[k][u] = *reinterpret_cast<const u32x4*>(xg + ((b * L + t) * H + h) * kP + 8 * pg);
-        in.sp[k][u] = reinterpret_cast<const f32x2*>(sp)[2 * jp + u];
-      }
-    }
-    in.s_last = sp[Q - 1].x;
-  };
-  // x^T scaled by w_j into buffer xsb (two tokens of one channel per 32-bit word, word column
-  // XORed by xt_swizzle_words); returns the chunk's decay exp(a S_last)
-  auto stage = [&](const ChunkX& in, __bf16* xsb) __attribute__((always_inline)) {
-    uint32_t* X32 = reinterpret_cast<uint32_t*>(xsb);
-#pragma unroll
-    for (int k = 0; k < XPER; ++k) {
-      const int it = tid + k * NT, jp = it / (kP / 8), pg = it % (kP / 8);
-      if (kItems < NT && it >= kItems) continue;
-      const float w0 = exp2_fast(a2 * (in.s_last - in.sp[k][0].x)) * in.sp[k][0].y;
-      const float w1 = exp2_fast(a2 * (in.s_last - in.sp[k][1].x)) * in.sp[k][1].y;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        // channels 2q (low halves) and 2q+1 (high halves) of the two tokens
-        const int ra = pg * 8 + 2 * q, rb = ra + 1;
-        X32[ra * (XS / 2) + (jp ^ xt_swizzle_words<Q>(ra))] = pack_bf16x2(bf16_lo(in.x[k][0][q]) * w0, bf16_lo(in.x[k][1][q]) * w1);
-        X32[rb * (XS / 2) + (jp ^ xt_swizzle_words<Q>(rb))] = pack_bf16x2(bf16_hi(in.x[k][0][q]) * w0, bf16_hi(in.x[k][1][q]) * w1);
-      }
-    }
-    return exp2_fast(a2 * in.s_last);
-  };
-  // B operand of step s: x^T rows p = 32 pt + l32, tokens 16 s + 8 hi .. + 7
-  auto frag_x = [&](const __bf16* xsb, int s, int pt) __attribute__((always_inline)) {
-    const int row = 32 * pt + l32;
-    const int col = 16 * s + 8 * hi;   // in bf16 elements; the XOR swizzle moves whole words
-    return *reinterpret_cast<const bf16x8*>(&xsb[row * XS + (col ^ (2 * xt_swizzle_words<Q>(row)))]);
-  };
-  // A operand of global step gs (chunk gs / KQ, step gs % KQ): the 1 KB fragment of B^T rows
-  // 32 w .. + 31, tokens 16 s .. + 15 (laid out in lane order by the prep kernel); past the last
-  // chunk it repeats the last step (never used)
-  const int64_t nsteps = nch * KQ;
-  auto load_bt = [&](int64_t gs) __attribute__((always_inline)) {
-    gs = gs < nsteps ? gs : nsteps - 1;
-    const int64_t c = gs / KQ, s = gs % KQ;
-    return load_frag(Bt_all + c * (int64_t)(N * Q) + ((int64_t)w * KQ + s) * 512 + lane * 8);
-  };
-
-  bf16_t* hin_all = static_cast<bf16_t*>(p.ws_hin);
-  auto store_carried = [&](int64_t c) __attribute__((always_inline)) {
-    bf16_t* hc = hin_all + ((b * nch + c) * H + h) * PN;
-#pragma unroll
-    for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        *reinterpret_cast<uint2*>(hc + (int64_t)(32 * pt + l32) * N + 32 * w + 8 * k + 4 * hi) =
-            make_uint2(pack_bf16x2(acc[pt][4 * k], acc[pt][4 * k + 1]), pack_bf16x2(acc[pt][4 * k + 2], acc[pt][4 * k + 3]));
-  };
-
-  // Two register sets of B^T fragments used by chunk parity (the loop is unrolled by two so they
-  // are named statically). Every load of a chunk step is issued at its start -- B^T of the next
-  // chunk and x of the one after -- before the carried-state stores are older than anything the
-  // step waits for: with loads and stores in flight together the compiler can only wait for all
-  // of them, so the one wait per chunk (at its start) finds loads issued a whole chunk earlier.
-  bf16x8 ringA[KQ], ringB[KQ];
-  auto load_ring = [&](int64_t c, bf16x8 (&r)[KQ]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s = 0; s < KQ; ++s) r[s] = load_bt(c * KQ + s);
-  };
-  ChunkX in;
-  float dec = 0.f;
-  if (nch > 0) {
-    load_x(0, in);
-    load_ring(0, ringA);
-    dec = stage(in, Xs[0]);
-    load_x(nch > 1 ? 1 : 0, in);
-  }
-  __syncthreads();
-  auto step = [&](int64_t c, const bf16x8 (&cur)[KQ], bf16x8 (&nxt)[KQ]) __attribute__((always_inline)) {
-    const __bf16* xsb = Xs[c & 1];
-    store_carried(c);
-#pragma unroll
-    for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[pt][v] *= dec;
-    // the next chunk's x^T into the other buffer (free since the last barrier); x of chunk c + 2
-    // and B^T of chunk c + 1 loaded (the last chunk repeated past the end: every load stays
-    // unconditional)
-    dec = stage(in, Xs[(c + 1) & 1]);
-    load_x(c + 2 < nch ? c + 2 : nch - 1, in);
-    load_ring(c + 1 < nch ? c + 1 : nch - 1, nxt);
-    // x fragments read one step ahead of their products (a read waited for right before its
-    // product would expose the LDS latency at every step)
-    bf16x8 xf[2][2];
-    xf[0][0] = frag_x(xsb, 0, 0);
-    xf[0][1] = frag_x(xsb, 0, 1);
-#pragma unroll
-    for (int s = 0; s < KQ; ++s) {
-      if (s + 1 < KQ) {
-        xf[(s + 1) & 1][0] = frag_x(xsb, s + 1, 0);
-        xf[(s + 1) & 1][1] = frag_x(xsb, s + 1, 1);
-      }
-#pragma unroll
-      for (int pt = 0; pt < 2; ++pt) acc[pt] = mfma32(cur[s], xf[s & 1][pt], acc[pt]);
-    }
-    __syncthreads();
-  };
-  int64_t c = 0;
-  for (; c + 1 < nch; c += 2) {
-    step(c, ringA, ringB);
-    step(c + 1, ringB, ringA);
-  }
-  if (c < nch) step(c, ringA, ringB);
-
-  if (p.h_last) {
-#pragma unroll
-    for (int pt = 0; pt < 2; ++pt) {
-      float* dst = p.h_last + (b * H + h) * PN + (int64_t)(32 * pt + l32) * N + 32 * w + 4 * hi;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        *reinterpret_cast<float4*>(dst + 8 * k) =
-            make_float4(acc[pt][4 * k], acc[pt][4 * k + 1], acc[pt][4 * k + 2], acc[pt][4 * k + 3]);
-    }
-  }
-}
-
 template <int Q, int N>
 hipError_t launch_qn(const SsdParams& p, hipStream_t stream) {
   const int64_t nch = (p.L + Q - 1) / Q;
@@ -533,7 +340,7 @@ hipError_t launch_qn(const SsdParams& p, hipStream_t stream) {
                      stream, p);
   hipLaunchKernelGGL((ssd_prep_kernel<Q, N>), dim3(4, (unsigned)nch, (unsigned)(p.B * p.G)), dim3(256), 0, stream,
                      p);
-  hipLaunchKernelGGL((ssd_state32_kernel<Q, N>), dim3((unsigned)p.H, (unsigned)p.B), dim3(64 * (N / 32)), 0, stream, p);
+  hipLaunchKernelGGL((ssd_chunk_state_kernel<Q, Q, N>), dim3((unsigned)p.H, (unsigned)p.B), dim3(64 * (N / 32)), 0, stream, p);
   // output workgroups: runs of hpw heads inside one group, wpg runs per group, aiming at one
   // workgroup per CU (256) before splitting a group's heads further
   const int64_t hpg = p.H / p.G;
@@ -564,7 +371,7 @@ void ssd_workspace_carve(SsdParams& p, void* ws) {
   base += ssd_align((size_t)(p.B * nch * p.H * p.P * p.N) * 2);
   p.ws_G = base;
   base += ssd_align((size_t)(p.B * p.G * nch * p.Q * p.Q) * 2);
-  p.ws_Bt = base;
+  p.ws_Btf = base;
   base += ssd_align((size_t)(p.B * p.G * nch * p.N * p.Q) * 2);
   p.ws_sphi = reinterpret_cast<float2*>(base);
 }

@@ -788,8 +788,12 @@ hipError_t launch_n(const SsdBwdParams& bp, hipStream_t stream) {
   hipLaunchKernelGGL((ssd_cumsum_kernel<Q>), chunks, dim3(256), 0, stream, p);
   hipLaunchKernelGGL((ssd_prep_kernel<Q, N, true>), dim3(4, (unsigned)nch, (unsigned)(p.B * p.G)), dim3(256), 0,
                      stream, p);
-  hipLaunchKernelGGL((ssd_state_kernel<Q, N, false>), dim3((unsigned)p.H, (unsigned)p.B), dim3(512), 0, stream, p);
-  hipLaunchKernelGGL((ssd_state_kernel<Q, N, true>), dim3((unsigned)p.H, (unsigned)p.B), dim3(512), 0, stream, p);
+  // the two state passes take the chunks four at a time (one 256-token step), storing the state
+  // at every chunk boundary
+  hipLaunchKernelGGL((ssd_chunk_state_kernel<4 * Q, Q, N, false>), dim3((unsigned)p.H, (unsigned)p.B),
+                     dim3(64 * (N / 32)), 0, stream, p);
+  hipLaunchKernelGGL((ssd_chunk_state_kernel<4 * Q, Q, N, true>), dim3((unsigned)p.H, (unsigned)p.B),
+                     dim3(64 * (N / 32)), 0, stream, p);
   const dim3 grid((unsigned)(p.H / bp.hb), (unsigned)nch, (unsigned)p.B);
   if (p.z)
     hipLaunchKernelGGL((ssd_bwd_main_kernel<N, true>), grid, dim3(512), 0, stream, bp);
@@ -815,7 +819,7 @@ size_t ssd_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64
   const size_t part = align256((size_t)(B * (H / hb) * L * N) * 4);
   const size_t ph = align256((size_t)(B * nch * H) * 4);
   const size_t pd = align256((size_t)(B * nch * H * P) * 4);
-  return 2 * st + gg + 2 * bt + sp + 2 * part + 2 * ph + pd;
+  return 2 * st + gg + 4 * bt + sp + 2 * part + 2 * ph + pd;
 }
 
 void ssd_bwd_workspace_carve(SsdBwdParams& bp, void* ws) {
@@ -833,6 +837,8 @@ void ssd_bwd_workspace_carve(SsdBwdParams& bp, void* ws) {
   p.ws_G = base; base += gg;
   p.ws_Bt = base; base += bt;
   p.ws_Ct = base; base += bt;
+  p.ws_Btf = base; base += bt;
+  p.ws_Ctf = base; base += bt;
   p.ws_sphi = reinterpret_cast<float2*>(base); base += sp;
   bp.ws_dBp = reinterpret_cast<float*>(base); base += part;
   bp.ws_dCp = reinterpret_cast<float*>(base); base += part;

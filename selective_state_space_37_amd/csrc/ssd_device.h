@@ -163,9 +163,9 @@ __global__ __launch_bounds__(256) void ssd_cumsum_kernel(SsdParams p) {
 // grid (4, chunks, B G): part `part` transposes states [part N/4, (part+1) N/4) of one group's B
 // and computes every fourth lower-triangular 16 x 16 tile of that group's G (row blocks ib,
 // column tiles jt <= ib). Token t's row of the group starts at element (t G + grp) N.
-// BWD: C is transposed as well (ws_Ct), and G is stored in float32 (ws_G, [Q][Q]) for the
-// backward's elementwise use. Only the tiles on and below the diagonal of G are written; the
-// forward packs them (bf16) in row-block order for the output kernel's LDS copy.
+// BWD: C is transposed as well, and G is stored in float32 (ws_G, [Q][Q]) for the backward's
+// elementwise use. Only the tiles on and below the diagonal of G are written; the forward packs
+// them (bf16) in row-block order for the output kernel's LDS copy.
 template <int Q, int N, bool BWD = false>
 __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
   const int part = blockIdx.x;
@@ -176,19 +176,19 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
   const int64_t rs = p.G * N;                      // token row stride of B and C
   const bf16_t* Bg = static_cast<const bf16_t*>(p.Bm) + b * p.L * rs + grp * N;
   const bf16_t* Cg = static_cast<const bf16_t*>(p.Cm) + b * p.L * rs + grp * N;
-  // transposed B, 8 tokens per 16-byte store. Backward: Bt[n][j]. Forward: in the order the
-  // forward's chunk-state kernel reads its MFMA operands (v_mfma_f32_32x32x16_bf16, A = B^T): the
-  // piece (n, j0 .. j0 + 7) of 32-row tile nt = n / 32 and 16-token step s = j0 / 16 is lane
+  // transposed B (and C in the backward), 8 tokens per 16-byte store, written in the order the
+  // chunk-state kernel reads its MFMA operands (v_mfma_f32_32x32x16_bf16, A = B^T): the piece
+  // (n, j0 .. j0 + 7) of 32-row tile nt = n / 32 and 16-token step s = j0 / 16 is lane
   // n % 32 + 32 ((j0 / 8) % 2) of the 1 KB fragment (nt, s), fragments in the order
-  // nt Q / 16 + s, so that one fragment load of a wave is 1 KB of consecutive memory.
-  bf16_t* Bt = static_cast<bf16_t*>(p.ws_Bt) + (bg * nch + c) * (int64_t)(N * Q);
+  // nt Q / 16 + s, so that one fragment load of a wave is 1 KB of consecutive memory. The
+  // backward's main kernel also gets plain [n][j] copies (ws_Bt, ws_Ct).
   constexpr int NQ = N / 4;
-  auto piece_off = [](int n, int j0) -> int64_t {
-    if constexpr (BWD) return (int64_t)n * Q + j0;
+  const int64_t cbase = (bg * nch + c) * (int64_t)(N * Q);
+  auto frag_off = [](int n, int j0) -> int64_t {
     const int frag = (n / 32) * (Q / 16) + j0 / 16, ln = n % 32 + 32 * ((j0 / 8) % 2);
     return (int64_t)frag * 512 + ln * 8;
   };
-  auto transpose = [&](const bf16_t* src, bf16_t* dst) {
+  auto transpose = [&](const bf16_t* src, void* plain, void* frag) {
     for (int it = tid; it < NQ * (Q / 8); it += 256) {
       const int n = part * NQ + it / (Q / 8);
       const int j0 = (it % (Q / 8)) * 8;
@@ -201,11 +201,13 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
         if (t0 + 1 < p.L) hi = src[(t0 + 1) * rs + n].bits;
         wv[q] = lo | (hi << 16);
       }
-      *reinterpret_cast<uint4*>(dst + piece_off(n, j0)) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      const uint4 v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      *reinterpret_cast<uint4*>(static_cast<bf16_t*>(frag) + cbase + frag_off(n, j0)) = v;
+      if constexpr (BWD) *reinterpret_cast<uint4*>(static_cast<bf16_t*>(plain) + cbase + (int64_t)n * Q + j0) = v;
     }
   };
-  transpose(Bg, Bt);
-  if constexpr (BWD) transpose(Cg, static_cast<bf16_t*>(p.ws_Ct) + (bg * nch + c) * (int64_t)(N * Q));
+  transpose(Bg, p.ws_Bt, p.ws_Btf);
+  if constexpr (BWD) transpose(Cg, p.ws_Ct, p.ws_Ctf);
   // G tiles
   // the wave index is the same for all lanes of a wave: readfirstlane lets the compiler keep it
   // (and the row blocks derived from it) in scalar registers, so branches on it are not divergent
@@ -239,255 +241,243 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
 }
 
 // ---------------------------------------------------------------------------- chunk states
-// grid (H, B), 512 threads: one head, sequential over the chunks. Wave w owns the state block
-// p in [16 pq, 16 pq + 16) x n in [NH w2, NH (w2 + 1)) with pq = w / 2, w2 = w % 2, NH = N / 2,
-// as NTW = N / 32 MFMA tiles computed transposed (states x channels), so that
-// acc[k][r] = h[p = 16 pq + lane % 16][n = (w2 NTW + k) 16 + 4 g + r]: four consecutive states
-// per lane, stored as one 8-byte (bf16) or 16-byte (float) piece. Per chunk the transposed B
-// (shared by the heads of a group) and the scaled, transposed x of the head are staged in LDS
-// once for all eight waves.
+// grid (H, B), N / 32 waves: one head, sequential over its chunks of QS tokens, with the P x N
+// state in MFMA accumulators. Wave w owns the states n in [32 w, 32 w + 32) for every channel p,
+// as two 32 x 32 tiles of D[n][p] (v_mfma_f32_32x32x16_bf16, computed transposed: states x
+// channels; output layout: lane l, value v holds column l % 32, row 8 (v / 4) + 4 (l / 32) + v % 4).
+// The chunks are taken Q / QS at a time (one step): per step the x^T of its Q tokens is staged
+// once, and every load of the step is issued at its start (x of the step after next, the B^T
+// fragments of the next step), so the one wait per step (at its start) finds loads issued a whole
+// step earlier. Per chunk of the step, in order:
+//   store h_{c-1} (bf16: the carried state of the output kernel), decay it by exp(a S_last),
+//   h_c += sum_j B_j^T (w_j x_j), w_j = exp(a (S_last - S_j)) phi_j (K = QS).
+// The B^T operand comes straight from global memory in the prep kernel's fragment order (1 KB of
+// consecutive memory per load, each wave reading only its own 32 rows).
 //
-// Inputs are loaded two chunks ahead into two register buffers used in turn (the loop is
-// unrolled by two; no buffer is copied). Every global load and store of the loop is issued
-// unconditionally -- rows past L are read from the last token, whose weight is 0 for padded
-// tokens, and the prefetch index is clamped -- so the compiler's count of outstanding
-// memory operations stays exact and the waits for a buffer do not also wait for the loads of
-// the other.
-//
-// ADJ: the same pass run backwards for the adjoint of the state (the backward's dL/dh). With
-// ybar = dy sigmoid-gated (dy z sigmoid(z), or dy without a gate) it walks the chunks from the
-// last, stores the adjoint of the state leaving chunk c (ws_gout), then
-//   g_{c-1} = exp(a S_last) g_c + sum_i exp(a S_i) ybar_i C_i^T
-// (C^T of the chunk from ws_Ct, tokens past L weighted 0), starting from dh_last and ending with
-// dh0.
-template <int Q, int N, bool ADJ = false>
-__global__ __launch_bounds__(512) void ssd_state_kernel(SsdParams p) {
-  constexpr int KQ = Q / 32;                 // K steps over a chunk
-  constexpr int NTW = N / 32;                // state tiles per wave
-  constexpr int XPAIRS = Q / 2 * 4;          // (token pair, 16-channel group) items of x
-  constexpr int BT16 = N * Q / 8;            // 16-byte pieces of B^T
-  static_assert(BT16 % 512 == 0, "B^T pieces divide over the threads");
-  static_assert(512 % XPAIRS == 0, "x items repeat evenly over the threads");
-  constexpr int BT_PER = BT16 / 512;
-  // two buffers of each where they fit beside each other in LDS (chunks of up to 128 tokens)
-  constexpr bool kDoubleLds = Q <= 128;
-  __shared__ __attribute__((aligned(16))) __bf16 Xs[kDoubleLds ? 2 : 1][kP * (Q + 8)];
-  __shared__ __attribute__((aligned(16))) __bf16 Bs[kDoubleLds ? 2 : 1][N * (Q + 8)];
+// ADJ: the same pass run backwards for the adjoint of the state (the backward's dL/dh): with
+// ybar = dy z sigmoid(z) (dy without a gate) it walks the chunks from the last, stores the
+// adjoint of the state leaving chunk c (ws_gout), then
+//   g_{c-1} = exp(a S_last) g_c + sum_i exp(a S_i) ybar_i C_i^T,
+// starting from dh_last and ending with dh0.
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int Q, int QS, int N, bool ADJ = false>
+__global__ __launch_bounds__(64 * (N / 32)) void ssd_chunk_state_kernel(SsdParams p) {
+  constexpr int NW = N / 32, NT = 64 * NW;
+  static_assert(Q % QS == 0 && QS % 16 == 0, "a step is whole chunks of whole 16-token steps");
+  constexpr int NSUB = Q / QS;               // chunks per step
+  constexpr int KQS = QS / 16;               // 16-token MFMA steps per chunk
+  constexpr int KQ = Q / 16;                 // ... per step
+  constexpr int XS = Q + 8;                  // LDS row stride (bf16) of x^T
+  constexpr int kItems = (Q / 2) * (kP / 8); // (token pair, 8-channel group) items of a step's x
+  static_assert(kItems % NT == 0 || kItems < NT, "the x items divide over the threads");
+  constexpr int XPER = (kItems + NT - 1) / NT;
+  __shared__ __attribute__((aligned(16))) __bf16 Xs[2][kP * XS];
   const int64_t h = blockIdx.x, b = blockIdx.y;
-  const int64_t nch = (p.L + Q - 1) / Q;
+  const int64_t L = p.L, H = p.H;
+  const int64_t nch = (L + QS - 1) / QS;       // chunks
+  const int64_t nst = (nch + NSUB - 1) / NSUB; // steps
   const int tid = threadIdx.x;
-  // the wave index is the same for all lanes of a wave: readfirstlane lets the compiler keep it
-  // (and the row blocks derived from it) in scalar registers, so branches on it are not divergent
-  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 4, r16 = lane & 15;
-  const int pq = w >> 1, w2 = w & 1;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
   const float a2 = p.A[h] * kLog2e;
   const int64_t PN = (int64_t)kP * N;
-  // first of the four consecutive states of tile k
-  auto st_idx = [&](int k) { return (int64_t)(16 * pq + r16) * N + (w2 * NTW + k) * 16 + 4 * g; };
+  const int64_t bg = b * p.G + h / (H / p.G);   // this head's (batch, group)
+  const bf16_t* Bt_all = static_cast<const bf16_t*>(ADJ ? p.ws_Ctf : p.ws_Btf) + bg * nch * (int64_t)(N * QS);
+  // chunk at position q of step k (past the ends: out of range, never processed)
+  auto chunk_at = [&](int64_t k, int q) -> int64_t { return ADJ ? nch - 1 - (k * NSUB + q) : k * NSUB + q; };
+  auto clamp_chunk = [&](int64_t c) -> int64_t { return c < 0 ? 0 : (c >= nch ? nch - 1 : c); };
 
+  // state element (n, p) of value v of tile pt: n = 32 w + 8 (v / 4) + 4 hi + v % 4, p = 32 pt + l32
+  f32x16 acc[2];
   const float* s_init = ADJ ? p.dh_last : p.h0;
-  f32x4 acc[NTW];
 #pragma unroll
-  for (int k = 0; k < NTW; ++k) {
-    acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int pt = 0; pt < 2; ++pt) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[pt][v] = 0.f;
     if (s_init) {
-      const float4 v = *reinterpret_cast<const float4*>(s_init + (b * p.H + h) * PN + st_idx(k));
-      acc[k] = f32x4{v.x, v.y, v.z, v.w};
+      const float* src = s_init + (b * H + h) * PN + (int64_t)(32 * pt + l32) * N + 32 * w + 4 * hi;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float4 v4 = *reinterpret_cast<const float4*>(src + 8 * k);
+        acc[pt][4 * k + 0] = v4.x; acc[pt][4 * k + 1] = v4.y; acc[pt][4 * k + 2] = v4.z; acc[pt][4 * k + 3] = v4.w;
+      }
     }
   }
-  // per-token input: x (forward) or dy (adjoint; z alongside for the gate)
-  const bf16_t* xg = static_cast<const bf16_t*>(ADJ ? p.dy : p.x);
-  const bf16_t* zg = ADJ ? static_cast<const bf16_t*>(p.z) : nullptr;
-  bf16_t* hin_all = static_cast<bf16_t*>(ADJ ? p.ws_gout : p.ws_hin);
-  const int64_t bg = b * p.G + h / (p.H / p.G);   // this head's (batch, group)
-  const bf16_t* Bt_all = static_cast<const bf16_t*>(ADJ ? p.ws_Ct : p.ws_Bt) + bg * nch * (int64_t)(N * Q);
 
-  // x item of this thread: tokens (2 jp, 2 jp + 1), channels [16 pg, 16 pg + 16). With fewer
-  // items than threads, threads tid and tid + XPAIRS take the same item and write the same
-  // values to the same LDS words.
-  const int item = tid % XPAIRS;
-  const int jp = item >> 2, pg = item & 3;
-  // native vector fields: plain register loads and stores (a struct-typed copy becomes a memcpy,
-  // which keeps the buffer out of registers)
+  // ---- the x (dy, with z) of a step: item = (token pair jp, channel group pg of 8), so the eight
+  // lanes of a row load its 128 bytes in one instruction. Column pair jp of the step belongs to
+  // position q = 2 jp / QS. Tokens past L (and chunks past the ends) read a valid stand-in
+  // and are weighted 0.
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
-  struct ChunkIn {
-    u32x4 x[2][2];      // two tokens x 16 channels
-    u32x4 z[ADJ ? 2 : 1][ADJ ? 2 : 1];   // the gate of the same elements (adjoint with z)
-    f32x2 sphi[2];      // (S_j, phi_j) of the two tokens
-    float s_last;
-    u32x4 bt[BT_PER];   // pieces of the chunk's B^T (C^T in the adjoint)
+  constexpr bool kGate = ADJ;
+  struct StepX {
+    u32x4 x[XPER][2];                          // [item][token]: 8 channels
+    u32x4 z[kGate ? XPER : 1][kGate ? 2 : 1];  // the gate of the same elements
+    f32x2 sp[XPER][2];                         // (S, phi) of the two tokens
+    float se[XPER];                            // S at the end of their chunk
   };
-  // (both lambdas are forced inline: the buffers they take by reference must stay in registers)
-  auto load_chunk = [&](int64_t c, ChunkIn& in) __attribute__((always_inline)) {
-    const float2* sp = p.ws_sphi + ((b * nch + c) * p.H + h) * Q;
+  const bf16_t* xg = static_cast<const bf16_t*>(ADJ ? p.dy : p.x);
+  const bf16_t* zg = ADJ ? static_cast<const bf16_t*>(p.z) : nullptr;
+  auto load_x = [&](int64_t k, StepX& in) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int j = 2 * jp + u;
-      const int64_t t = c * Q + j < p.L ? c * Q + j : p.L - 1;
-      const int64_t off = ((b * p.L + t) * p.H + h) * kP + 16 * pg;
-      const u32x4* src = reinterpret_cast<const u32x4*>(xg + off);
-      in.x[u][0] = src[0];
-      in.x[u][1] = src[1];
-      if constexpr (ADJ) {
-        if (zg) {
-          const u32x4* zs = reinterpret_cast<const u32x4*>(zg + off);
-          in.z[u][0] = zs[0];
-          in.z[u][1] = zs[1];
+    for (int e = 0; e < XPER; ++e) {
+      const int it = std::min(tid + e * NT, kItems - 1), jp = it / (kP / 8), pg = it % (kP / 8);
+      const int q = (2 * jp) / QS, j = (2 * jp) % QS;
+      const int64_t c = clamp_chunk(chunk_at(k, q));
+      const float2* sp = p.ws_sphi + ((b * nch + c) * H + h) * QS;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t t = std::min<int64_t>(c * QS + j + u, L - 1);
+        const int64_t off = ((b * L + t) * H + h) * kP + 8 * pg;
+        in.x[e][u] = *reinterpret_cast<const u32x4*>(xg + off);
+        if constexpr (kGate) {
+          if (zg) in.z[e][u] = *reinterpret_cast<const u32x4*>(zg + off);
         }
+        in.sp[e][u] = reinterpret_cast<const f32x2*>(sp)[j + u];
       }
-      in.sphi[u] = reinterpret_cast<const f32x2*>(sp)[j];
+      in.se[e] = sp[QS - 1].x;
     }
-    in.s_last = sp[Q - 1].x;
-    const u32x4* bt = reinterpret_cast<const u32x4*>(Bt_all + c * (int64_t)(N * Q));
-#pragma unroll
-    for (int k = 0; k < BT_PER; ++k) in.bt[k] = bt[tid + 512 * k];
   };
-
-  auto pick = [](const u32x4& v, int q) { return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w; };
-  // chunk of the k-th step: ascending in the forward, descending in the adjoint
-  auto chunk_of = [&](int64_t k) { return ADJ ? nch - 1 - k : k; };
-
-  // stage B^T (C^T) and the weighted, transposed x (ybar) of the chunk in `in` into the LDS
-  // buffers xsb, bsb; returns the chunk's decay exp(a S_last)
-  auto stage = [&](int64_t c, const ChunkIn& in, __bf16* xsb, __bf16* bsb) __attribute__((always_inline)) {
-#pragma unroll
-    for (int k2 = 0; k2 < BT_PER; ++k2) {
-      const int e = tid + 512 * k2;
-      const int n = e / (Q / 8), j8 = (e % (Q / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&bsb[n * (Q + 8) + j8]) = in.bt[k2];
-    }
-    float wj[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if constexpr (ADJ)
-        wj[u] = c * Q + 2 * jp + u < p.L ? exp2_fast(a2 * in.sphi[u].x) : 0.f;
-      else
-        wj[u] = exp2_fast(a2 * (in.s_last - in.sphi[u].x)) * in.sphi[u].y;
-    }
+  // x^T of the step weighted per token into buffer xsb (two tokens of one channel per 32-bit
+  // word, word column XORed by xt_swizzle_words)
+  auto stage = [&](int64_t k, const StepX& in, __bf16* xsb) __attribute__((always_inline)) {
     uint32_t* X32 = reinterpret_cast<uint32_t*>(xsb);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const uint32_t u0 = pick(in.x[0][q >> 3], (q & 7) >> 1);
-      const uint32_t u1 = pick(in.x[1][q >> 3], (q & 7) >> 1);
-      float f0 = (q & 1) ? bf16_hi(u0) : bf16_lo(u0);
-      float f1 = (q & 1) ? bf16_hi(u1) : bf16_lo(u1);
-      if constexpr (ADJ) {
-        if (zg) {
-          const uint32_t v0 = pick(in.z[0][q >> 3], (q & 7) >> 1);
-          const uint32_t v1 = pick(in.z[1][q >> 3], (q & 7) >> 1);
-          f0 *= silu((q & 1) ? bf16_hi(v0) : bf16_lo(v0));
-          f1 *= silu((q & 1) ? bf16_hi(v1) : bf16_lo(v1));
+    for (int e = 0; e < XPER; ++e) {
+      const int it = tid + e * NT, jp = it / (kP / 8), pg = it % (kP / 8);
+      if (kItems < NT && it >= kItems) continue;
+      const int q = (2 * jp) / QS, j = (2 * jp) % QS;
+      const int64_t c = chunk_at(k, q);
+      float wt[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bool live = c >= 0 && c < nch && c * QS + j + u < L;
+        const float wv = ADJ ? exp2_fast(a2 * in.sp[e][u].x) : exp2_fast(a2 * (in.se[e] - in.sp[e][u].x)) * in.sp[e][u].y;
+        wt[u] = live ? wv : 0.f;
+      }
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        // channels 2qq (low halves) and 2qq+1 (high halves) of the two tokens
+        float v[2][2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          v[u][0] = bf16_lo(in.x[e][u][qq]);
+          v[u][1] = bf16_hi(in.x[e][u][qq]);
+          if constexpr (kGate) {
+            if (zg) {
+              v[u][0] *= silu(bf16_lo(in.z[e][u][qq]));
+              v[u][1] *= silu(bf16_hi(in.z[e][u][qq]));
+            }
+          }
         }
+        const int ra = pg * 8 + 2 * qq, rb = ra + 1;
+        X32[ra * (XS / 2) + (jp ^ xt_swizzle_words<Q>(ra))] = pack_bf16x2(v[0][0] * wt[0], v[1][0] * wt[1]);
+        X32[rb * (XS / 2) + (jp ^ xt_swizzle_words<Q>(rb))] = pack_bf16x2(v[0][1] * wt[0], v[1][1] * wt[1]);
       }
-      // word column XORed with 16 pg (inside the row): the four channel groups of a wave
-      // write to four different 16-bank ranges
-      X32[(16 * pg + q) * ((Q + 8) / 2) + (jp ^ ((16 * pg) & (Q / 2 - 1)))] = pack_bf16x2(f0 * wj[0], f1 * wj[1]);
-    }
-    return exp2_fast(a2 * in.s_last);
-  };
-  // the state entering chunk c (the adjoint of the state leaving it), for the output kernel
-  // (the backward); then decay it over the chunk
-  auto store_and_decay = [&](int64_t c, float decay) __attribute__((always_inline)) {
-    bf16_t* hin = hin_all + ((b * nch + c) * p.H + h) * PN;
-#pragma unroll
-    for (int k2 = 0; k2 < NTW; ++k2) {
-      *reinterpret_cast<uint2*>(hin + st_idx(k2)) =
-          make_uint2(pack_bf16x2(acc[k2][0], acc[k2][1]), pack_bf16x2(acc[k2][2], acc[k2][3]));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[k2][r] *= decay;
     }
   };
-  // acc += (B^T of the chunk) (weighted x^T), operands read one K step ahead into a second
-  // register set; the scheduling barriers keep the reads of step kq + 1 ahead of the products
-  // of step kq (without them the compiler reuses one register set and waits for each read
-  // before its product)
-  auto products = [&](const __bf16* xsb, const __bf16* bsb) __attribute__((always_inline)) {
-    auto frag_x = [&](int kq) __attribute__((always_inline)) {
-      return *reinterpret_cast<const bf16x8*>(&xsb[(16 * pq + r16) * (Q + 8) + ((kq * 32 + 8 * g) ^ ((32 * pq) & (Q - 1)))]);
-    };
-    auto frag_b = [&](int kq, int k2) __attribute__((always_inline)) {
-      return *reinterpret_cast<const bf16x8*>(&bsb[((w2 * NTW + k2) * 16 + r16) * (Q + 8) + kq * 32 + 8 * g]);
-    };
-    bf16x8 xf[2], bfr[2][NTW];
-    xf[0] = frag_x(0);
+  // B operand of 16-token step s of the staged step: x^T rows p = 32 pt + l32, tokens
+  // 16 s + 8 hi .. + 7
+  auto frag_x = [&](const __bf16* xsb, int s, int pt) __attribute__((always_inline)) {
+    const int row = 32 * pt + l32;
+    const int col = 16 * s + 8 * hi;   // in bf16 elements; the XOR swizzle moves whole words
+    return *reinterpret_cast<const bf16x8*>(&xsb[row * XS + (col ^ (2 * xt_swizzle_words<Q>(row)))]);
+  };
+  // A operands of step k: the 1 KB fragments of B^T (C^T) rows 32 w .. + 31 for each chunk and
+  // 16-token step (chunks past the ends read a valid stand-in, never used)
+  auto load_ring = [&](int64_t k, bf16x8 (&r)[KQ]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k2 = 0; k2 < NTW; ++k2) bfr[0][k2] = frag_b(0, k2);
+    for (int q = 0; q < NSUB; ++q) {
+      const int64_t c = clamp_chunk(chunk_at(k, q));
 #pragma unroll
-    for (int kq = 0; kq < KQ; ++kq) {
-      const int cb = kq & 1;
-      if (kq + 1 < KQ) {
-        xf[cb ^ 1] = frag_x(kq + 1);
-#pragma unroll
-        for (int k2 = 0; k2 < NTW; ++k2) bfr[cb ^ 1][k2] = frag_b(kq + 1, k2);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int k2 = 0; k2 < NTW; ++k2) acc[k2] = mfma16(bfr[cb][k2], xf[cb], acc[k2]);   // (states x tokens) . (tokens x channels)
-      __builtin_amdgcn_sched_barrier(0);
+      for (int s = 0; s < KQS; ++s)
+        r[q * KQS + s] = load_frag(Bt_all + c * (int64_t)(N * QS) + ((int64_t)w * KQS + s) * 512 + lane * 8);
     }
+  };
+  bf16_t* hc_all = static_cast<bf16_t*>(ADJ ? p.ws_gout : p.ws_hin);
+  auto store_carried = [&](int64_t c) __attribute__((always_inline)) {
+    bf16_t* hc = hc_all + ((b * nch + c) * H + h) * PN;
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        *reinterpret_cast<uint2*>(hc + (int64_t)(32 * pt + l32) * N + 32 * w + 8 * k + 4 * hi) =
+            make_uint2(pack_bf16x2(acc[pt][4 * k], acc[pt][4 * k + 1]), pack_bf16x2(acc[pt][4 * k + 2], acc[pt][4 * k + 3]));
   };
 
-  ChunkIn buf0, buf1;   // even steps in buf0, odd steps in buf1
-  if (nch > 0) {
-    load_chunk(chunk_of(0), buf0);
-    load_chunk(chunk_of(nch > 1 ? 1 : 0), buf1);
+  // Two register sets of B^T fragments used by step parity (the loop is unrolled by two so they
+  // are named statically): the fragments of step k + 1 are loaded while step k runs.
+  bf16x8 ringA[KQ], ringB[KQ];
+  StepX in;
+  if (nst > 0) {
+    load_x(0, in);
+    load_ring(0, ringA);
+    stage(0, in, Xs[0]);
+    load_x(nst > 1 ? 1 : 0, in);
   }
-  // wait for the entering state here, once: its loads are conditional, and a first use inside
-  // the loop would put a wait for every outstanding load at the head of each step
+  __syncthreads();
+  auto step = [&](int64_t k, const bf16x8 (&cur)[KQ], bf16x8 (&nxt)[KQ]) __attribute__((always_inline)) {
+    const __bf16* xsb = Xs[k & 1];
+    // decays of the step's chunks (uniform loads)
+    float dec[NSUB];
 #pragma unroll
-  for (int k = 0; k < NTW; ++k) asm volatile("" : "+v"(acc[k]));
-  if constexpr (!kDoubleLds) {
-    // one LDS buffer: stage, barrier, products, barrier
-    auto process = [&](int64_t k, ChunkIn& cur) __attribute__((always_inline)) {
-      const int64_t c = chunk_of(k);
-      const float decay = stage(c, cur, Xs[0], Bs[0]);
-      load_chunk(chunk_of(k + 2 < nch ? k + 2 : nch - 1), cur);
-      store_and_decay(c, decay);
-      __syncthreads();
-      products(Xs[0], Bs[0]);
-      __syncthreads();
-    };
-    int64_t k = 0;
-    for (; k + 1 < nch; k += 2) {
-      process(k, buf0);
-      process(k + 1, buf1);
+    for (int q = 0; q < NSUB; ++q) {
+      const int64_t c = clamp_chunk(chunk_at(k, q));
+      dec[q] = exp2_fast(a2 * p.ws_sphi[((b * nch + c) * H + h) * QS + QS - 1].x);
     }
-    if (k < nch) process(k, buf0);
-  } else {
-    // two LDS buffers: chunk k + 1 is staged while the products of chunk k run; one barrier
-    // per chunk (after it, the next chunk's operands are complete and this chunk's buffer free)
-    float dec = 0.f;
-    if (nch > 0) {
-      dec = stage(chunk_of(0), buf0, Xs[0], Bs[0]);
-      load_chunk(chunk_of(nch > 2 ? 2 : nch - 1), buf0);
+    // the next step's x^T into the other buffer (free since the last barrier); x of step k + 2
+    // and the fragments of step k + 1 loaded (past the end: a repeated step, every load stays
+    // unconditional)
+    stage(k + 1, in, Xs[(k + 1) & 1]);
+    load_x(k + 2 < nst ? k + 2 : nst - 1, in);
+    load_ring(k + 1 < nst ? k + 1 : nst - 1, nxt);
+#pragma unroll
+    for (int q = 0; q < NSUB; ++q) {
+      const int64_t c = chunk_at(k, q);
+      if (c < 0 || c >= nch) break;   // uniform: the remaining positions are past the ends
+      store_carried(c);
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[pt][v] *= dec[q];
+      // x fragments read one step ahead of their products
+      bf16x8 xf[2][2];
+      xf[0][0] = frag_x(xsb, q * KQS, 0);
+      xf[0][1] = frag_x(xsb, q * KQS, 1);
+#pragma unroll
+      for (int s = 0; s < KQS; ++s) {
+        if (s + 1 < KQS) {
+          xf[(s + 1) & 1][0] = frag_x(xsb, q * KQS + s + 1, 0);
+          xf[(s + 1) & 1][1] = frag_x(xsb, q * KQS + s + 1, 1);
+        }
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) acc[pt] = mfma32(cur[q * KQS + s], xf[s & 1][pt], acc[pt]);
+      }
     }
     __syncthreads();
-    // step k: the register buffer `nxt` holds chunk k + 1 (k + 1 < nch), refilled with k + 3
-    auto step = [&](int64_t k, ChunkIn& nxt) __attribute__((always_inline)) {
-      const int64_t c = chunk_of(k);
-      store_and_decay(c, dec);
-      if (k + 1 < nch) dec = stage(chunk_of(k + 1), nxt, Xs[(k + 1) & 1], Bs[(k + 1) & 1]);
-      // (issued on the last step too, where it is not used: with every load of the loop
-      // unconditional the compiler's count of outstanding operations at the loop head is exact)
-      load_chunk(chunk_of(k + 3 < nch ? k + 3 : nch - 1), nxt);
-      products(Xs[k & 1], Bs[k & 1]);
-      __syncthreads();
-    };
-    int64_t k = 0;
-    for (; k + 1 < nch; k += 2) {
-      step(k, buf1);
-      step(k + 1, buf0);
-    }
-    if (k < nch) step(k, buf1);
+  };
+  int64_t k = 0;
+  for (; k + 1 < nst; k += 2) {
+    step(k, ringA, ringB);
+    step(k + 1, ringB, ringA);
   }
+  if (k < nst) step(k, ringA, ringB);
 
   float* s_out = ADJ ? p.dh0 : p.h_last;
   if (s_out) {
 #pragma unroll
-    for (int k2 = 0; k2 < NTW; ++k2)
-      *reinterpret_cast<float4*>(s_out + (b * p.H + h) * PN + st_idx(k2)) =
-          make_float4(acc[k2][0], acc[k2][1], acc[k2][2], acc[k2][3]);
+    for (int pt = 0; pt < 2; ++pt) {
+      float* dst = s_out + (b * H + h) * PN + (int64_t)(32 * pt + l32) * N + 32 * w + 4 * hi;
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2)
+        *reinterpret_cast<float4*>(dst + 8 * k2) =
+            make_float4(acc[pt][4 * k2], acc[pt][4 * k2 + 1], acc[pt][4 * k2 + 2], acc[pt][4 * k2 + 3]);
+    }
   }
 }
 

@@ -147,6 +147,12 @@ struct SsdParams {
   void* ws_Btf;            // bf16 [B, G, nchunks, N Q]: B^T of each chunk in MFMA fragment order
   void* ws_Ctf;            // backward: the same for C
   float2* ws_sphi;         // [B, nchunks, H, Q]: (inclusive cumulative Delta, ZOH input scale)
+  // forward with the state pass cut into L-segments (NULL otherwise)
+  float* ws_seg_h;         // [B, segments, H, P, N]: each segment's own end state
+  float* ws_seg_s;         // [B, segments, H]: each segment's sum of step sizes
+  void* ws_seg_in;         // bf16 [B, segments, H, P, N]: the state entering each segment
+  float* ws_dpre;          // [B, nchunks, H]: the step sizes of the segment's chunks before each chunk
+  int nseg;                // segments of the state pass (1: none)
   // backward only (NULL in the forward)
   const void* dy;          // bf16 [B, L, H, P]: dL/dy
   const float* dh_last;    // nullable [B, H, P, N]

@@ -100,6 +100,10 @@ __global__ __launch_bounds__(64 * SsdOutCfg<Q>::NW) void ssd_out_kernel(SsdParam
     ib = slot == 0 ? sm : slot == 1 ? 7 - sm : slot == 2 ? 8 + sm : 15 - sm;
   }
   const bool active = ib < NIB;   // uniform
+  // the L-segment of the state pass this chunk belongs to (segment s holds chunks
+  // [s nch / S, (s + 1) nch / S))
+  int cseg = 0;
+  while (cseg + 1 < p.nseg && (int64_t)(cseg + 1) * nch / p.nseg <= c) ++cseg;
   const int64_t L = p.L, H = p.H, rs = p.G * N;   // token row stride of B and C
   const bf16_t* xg = static_cast<const bf16_t*>(p.x);
   const bf16_t* zg = static_cast<const bf16_t*>(p.z);
@@ -115,6 +119,8 @@ __global__ __launch_bounds__(64 * SsdOutCfg<Q>::NW) void ssd_out_kernel(SsdParam
     f32x2 s0[XPER], s1[XPER];   // their (S, phi)
     float se[XPER];             // S at the end of their 16-token tile
     u32x4 hv[HPER];             // pieces of the carried-in state
+    u32x4 sv[HPER];             // pieces of the state entering the chunk's segment (segments >= 1)
+    float dpre;                 // step sizes of the segment's chunks before this one
   };
   // Addressing: per head a wave-uniform base (the chunk's first row of the head, its (S, phi)
   // table, its carried state) plus per-lane 32-bit byte offsets that are the same for every head
@@ -146,6 +152,12 @@ __global__ __launch_bounds__(64 * SsdOutCfg<Q>::NW) void ssd_out_kernel(SsdParam
     const bf16_t* hin = static_cast<const bf16_t*>(p.ws_hin) + ((b * nch + c) * H + hh) * (int64_t)(kP * N);
 #pragma unroll
     for (int k = 0; k < HPER; ++k) in.hv[k] = ld_at<u32x4>(hin, (uint32_t)(std::min(tid + k * NT, kHP - 1) * 16));
+    if (cseg > 0) {   // uniform
+      const bf16_t* sin = static_cast<const bf16_t*>(p.ws_seg_in) + ((b * p.nseg + cseg) * H + hh) * (int64_t)(kP * N);
+#pragma unroll
+      for (int k = 0; k < HPER; ++k) in.sv[k] = ld_at<u32x4>(sin, (uint32_t)(std::min(tid + k * NT, kHP - 1) * 16));
+      in.dpre = p.ws_dpre[(b * nch + c) * H + hh];
+    }
   };
   // x^T of the head scaled by cp_j = 2^max(a2 (S_e - S_j), -64) phi_j (two tokens of one channel
   // per 32-bit word, word column XORed by xt_swizzle_words) into buffer buf, S (written by the
@@ -171,11 +183,20 @@ __global__ __launch_bounds__(64 * SsdOutCfg<Q>::NW) void ssd_out_kernel(SsdParam
         X32[rb * (XS / 2) + (jp ^ xt_swizzle_words<Q>(rb))] = pack_bf16x2(bf16_hi(in.x0[k][q]) * cp0, bf16_hi(in.x1[k][q]) * cp1);
       }
     }
+    // (a chunk of a later L-segment: the state pass started the segment from zero, so the
+    // segment's entering state, decayed to the chunk, is added)
+    const float fdec = cseg > 0 ? exp2_fast(a2 * in.dpre) : 0.f;
 #pragma unroll
     for (int k = 0; k < HPER; ++k) {
       const int e = tid + k * NT, row = e / (N / 8), c8 = (e % (N / 8)) * 8;
       if (kHP < NT && e >= kHP) continue;
-      *reinterpret_cast<u32x4*>(&Hs[row * HSTR + c8]) = in.hv[k];
+      u32x4 hv = in.hv[k];
+      if (cseg > 0) {   // uniform
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          hv[q] = pack_bf16x2(fmaf(fdec, bf16_lo(in.sv[k][q]), bf16_lo(hv[q])), fmaf(fdec, bf16_hi(in.sv[k][q]), bf16_hi(hv[q])));
+      }
+      *reinterpret_cast<u32x4*>(&Hs[row * HSTR + c8]) = hv;
     }
   };
 
@@ -340,7 +361,14 @@ hipError_t launch_qn(const SsdParams& p, hipStream_t stream) {
                      stream, p);
   hipLaunchKernelGGL((ssd_prep_kernel<Q, N>), dim3(4, (unsigned)nch, (unsigned)(p.B * p.G)), dim3(256), 0, stream,
                      p);
-  hipLaunchKernelGGL((ssd_chunk_state_kernel<Q, Q, N>), dim3((unsigned)p.H, (unsigned)p.B), dim3(64 * (N / 32)), 0, stream, p);
+  // the state pass: 128-token steps (lighter on registers, so two workgroups share a CU), cut
+  // into L-segments when the heads alone leave CUs idle; the carry kernel composes the segments
+  constexpr int QST = Q < 128 ? Q : 128;
+  hipLaunchKernelGGL((ssd_chunk_state_kernel<QST, Q, N>), dim3((unsigned)p.H, (unsigned)p.B, (unsigned)p.nseg),
+                     dim3(64 * (N / 32)), 0, stream, p);
+  if (p.nseg > 1)
+    hipLaunchKernelGGL(ssd_seg_carry_kernel, dim3((unsigned)((kP * N / 4 + 255) / 256), (unsigned)p.H, (unsigned)p.B),
+                       dim3(256), 0, stream, p, p.nseg);
   // output workgroups: runs of hpw heads inside one group, wpg runs per group, aiming at one
   // workgroup per CU (256) before splitting a group's heads further
   const int64_t hpg = p.H / p.G;
@@ -358,10 +386,22 @@ hipError_t launch_qn(const SsdParams& p, hipStream_t stream) {
 // group (bf16), (S, phi) per chunk, head and token (float2), each 256-byte aligned.
 static size_t ssd_align(size_t n) { return (n + 255) & ~(size_t)255; }
 
+// L-segments of the state pass: enough (batch, head, segment) workgroups for about two per CU
+// of MI355X's 256, at most 8 and at most one per chunk.
+int64_t ssd_state_segments(int64_t B, int64_t H, int64_t nch) {
+  const int64_t chains = std::max<int64_t>(1, B * H);
+  return std::max<int64_t>(1, std::min<int64_t>({(512 + chains / 2) / chains, 8, nch}));
+}
+
 size_t ssd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q) {
   const int64_t nch = (L + Q - 1) / Q;
+  const int64_t nseg = ssd_state_segments(B, H, nch);
+  size_t seg = 0;
+  if (nseg > 1)
+    seg = ssd_align((size_t)(B * nseg * H * P * N) * 4) + ssd_align((size_t)(B * nseg * H) * 4) +
+          ssd_align((size_t)(B * nseg * H * P * N) * 2) + ssd_align((size_t)(B * nch * H) * 4);
   return ssd_align((size_t)(B * nch * H * P * N) * 2) + ssd_align((size_t)(B * G * nch * Q * Q) * 2) +
-         ssd_align((size_t)(B * G * nch * N * Q) * 2) + ssd_align((size_t)(B * nch * H * Q) * 8);
+         ssd_align((size_t)(B * G * nch * N * Q) * 2) + ssd_align((size_t)(B * nch * H * Q) * 8) + seg;
 }
 
 void ssd_workspace_carve(SsdParams& p, void* ws) {
@@ -374,6 +414,17 @@ void ssd_workspace_carve(SsdParams& p, void* ws) {
   p.ws_Btf = base;
   base += ssd_align((size_t)(p.B * p.G * nch * p.N * p.Q) * 2);
   p.ws_sphi = reinterpret_cast<float2*>(base);
+  base += ssd_align((size_t)(p.B * nch * p.H * p.Q) * 8);
+  p.nseg = (int)ssd_state_segments(p.B, p.H, nch);
+  if (p.nseg > 1) {
+    p.ws_seg_h = reinterpret_cast<float*>(base);
+    base += ssd_align((size_t)(p.B * p.nseg * p.H * p.P * p.N) * 4);
+    p.ws_seg_s = reinterpret_cast<float*>(base);
+    base += ssd_align((size_t)(p.B * p.nseg * p.H) * 4);
+    p.ws_seg_in = base;
+    base += ssd_align((size_t)(p.B * p.nseg * p.H * p.P * p.N) * 2);
+    p.ws_dpre = reinterpret_cast<float*>(base);
+  }
 }
 
 hipError_t launch_ssd(const SsdParams& p, hipStream_t stream) {

@@ -241,18 +241,25 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
 }
 
 // ---------------------------------------------------------------------------- chunk states
-// grid (H, B), N / 32 waves: one head, sequential over its chunks of QS tokens, with the P x N
-// state in MFMA accumulators. Wave w owns the states n in [32 w, 32 w + 32) for every channel p,
-// as two 32 x 32 tiles of D[n][p] (v_mfma_f32_32x32x16_bf16, computed transposed: states x
-// channels; output layout: lane l, value v holds column l % 32, row 8 (v / 4) + 4 (l / 32) + v % 4).
-// The chunks are taken Q / QS at a time (one step): per step the x^T of its Q tokens is staged
-// once, and every load of the step is issued at its start (x of the step after next, the B^T
-// fragments of the next step), so the one wait per step (at its start) finds loads issued a whole
-// step earlier. Per chunk of the step, in order:
+// grid (H, B, segments), N / 32 waves: one head, sequential over its chunks of QS tokens (those of
+// one L-segment), with the P x N state in MFMA accumulators. Wave w owns the states n in
+// [32 w, 32 w + 32) for every channel p, as two 32 x 32 tiles of D[n][p] (v_mfma_f32_32x32x16_bf16,
+// computed transposed: states x channels; output layout: lane l, value v holds column l % 32,
+// row 8 (v / 4) + 4 (l / 32) + v % 4).
+// The tokens are taken Q at a time (one step): per step the x^T of its Q tokens is staged once,
+// and the step's loads are issued at its start (the x of the step after, the B^T fragments of the
+// next step). A step is one or more whole chunks (Q >= QS) or a part of one (Q < QS); per chunk,
+// at its first part:
 //   store h_{c-1} (bf16: the carried state of the output kernel), decay it by exp(a S_last),
-//   h_c += sum_j B_j^T (w_j x_j), w_j = exp(a (S_last - S_j)) phi_j (K = QS).
+// and per part h_c += sum_j B_j^T (w_j x_j), w_j = exp(a (S_last - S_j)) phi_j.
 // The B^T operand comes straight from global memory in the prep kernel's fragment order (1 KB of
 // consecutive memory per load, each wave reading only its own 32 rows).
+//
+// Segments (forward only): with several, segment s runs chunks [s nch / S, (s + 1) nch / S), the
+// first from h0 and the others from zero; the carried states it stores are then those of the
+// segment alone. It leaves its end state (ws_seg_h) and its total sum of step sizes (ws_seg_s),
+// and per chunk the sum of the step sizes of the segment's earlier chunks (ws_dpre); the carry
+// kernel composes the segments and the output kernel adds the decayed entering state.
 //
 // ADJ: the same pass run backwards for the adjoint of the state (the backward's dL/dh): with
 // ybar = dy z sigmoid(z) (dy without a gate) it walks the chunks from the last, stores the
@@ -267,19 +274,23 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 template <int Q, int QS, int N, bool ADJ = false>
 __global__ __launch_bounds__(64 * (N / 32)) void ssd_chunk_state_kernel(SsdParams p) {
   constexpr int NW = N / 32, NT = 64 * NW;
-  static_assert(Q % QS == 0 && QS % 16 == 0, "a step is whole chunks of whole 16-token steps");
-  constexpr int NSUB = Q / QS;               // chunks per step
-  constexpr int KQS = QS / 16;               // 16-token MFMA steps per chunk
+  constexpr int UT = Q < QS ? Q : QS;        // tokens of one unit: a chunk, or a part of one
+  static_assert(Q % UT == 0 && QS % UT == 0 && UT % 16 == 0, "steps and chunks are whole units");
+  constexpr int NU = Q / UT;                 // units per step
+  constexpr int PPC = QS / UT;               // units (parts) per chunk
+  constexpr int KU = UT / 16;                // 16-token MFMA steps per unit
   constexpr int KQ = Q / 16;                 // ... per step
   constexpr int XS = Q + 8;                  // LDS row stride (bf16) of x^T
   constexpr int kItems = (Q / 2) * (kP / 8); // (token pair, 8-channel group) items of a step's x
   static_assert(kItems % NT == 0 || kItems < NT, "the x items divide over the threads");
   constexpr int XPER = (kItems + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) __bf16 Xs[2][kP * XS];
-  const int64_t h = blockIdx.x, b = blockIdx.y;
+  const int64_t h = blockIdx.x, b = blockIdx.y, seg = blockIdx.z, nseg = gridDim.z;
   const int64_t L = p.L, H = p.H;
   const int64_t nch = (L + QS - 1) / QS;       // chunks
-  const int64_t nst = (nch + NSUB - 1) / NSUB; // steps
+  const int64_t c_begin = seg * nch / nseg, c_end = (seg + 1) * nch / nseg;
+  const int64_t nun = (c_end - c_begin) * PPC; // units of the segment
+  const int64_t nst = (nun + NU - 1) / NU;     // steps
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
@@ -287,13 +298,22 @@ __global__ __launch_bounds__(64 * (N / 32)) void ssd_chunk_state_kernel(SsdParam
   const int64_t PN = (int64_t)kP * N;
   const int64_t bg = b * p.G + h / (H / p.G);   // this head's (batch, group)
   const bf16_t* Bt_all = static_cast<const bf16_t*>(ADJ ? p.ws_Ctf : p.ws_Btf) + bg * nch * (int64_t)(N * QS);
-  // chunk at position q of step k (past the ends: out of range, never processed)
-  auto chunk_at = [&](int64_t k, int q) -> int64_t { return ADJ ? nch - 1 - (k * NSUB + q) : k * NSUB + q; };
-  auto clamp_chunk = [&](int64_t c) -> int64_t { return c < 0 ? 0 : (c >= nch ? nch - 1 : c); };
+  // unit at position q of step k: its chunk and its first token inside the chunk (units past the
+  // segment's end map to a chunk out of [c_begin, c_end) and are never processed)
+  auto unit_at = [&](int64_t k, int q, int64_t& c, int& off) __attribute__((always_inline)) {
+    const int64_t u = k * NU + q;
+    const int64_t ur = ADJ ? nun - 1 - u : u;   // the adjoint takes the units in reverse
+    const int64_t cc = ur >= 0 ? ur / PPC : -1;
+    c = c_begin + cc;
+    off = (int)((ur >= 0 ? ur % PPC : 0) * UT);
+    if (u >= nun) c = c_end;                     // past the end
+  };
+  auto live_chunk = [&](int64_t c) { return c >= c_begin && c < c_end; };
+  auto clamp_chunk = [&](int64_t c) -> int64_t { return c < c_begin ? c_begin : (c >= c_end ? c_end - 1 : c); };
 
   // state element (n, p) of value v of tile pt: n = 32 w + 8 (v / 4) + 4 hi + v % 4, p = 32 pt + l32
   f32x16 acc[2];
-  const float* s_init = ADJ ? p.dh_last : p.h0;
+  const float* s_init = ADJ ? p.dh_last : (seg == 0 ? p.h0 : nullptr);
 #pragma unroll
   for (int pt = 0; pt < 2; ++pt) {
 #pragma unroll
@@ -310,8 +330,8 @@ __global__ __launch_bounds__(64 * (N / 32)) void ssd_chunk_state_kernel(SsdParam
 
   // ---- the x (dy, with z) of a step: item = (token pair jp, channel group pg of 8), so the eight
   // lanes of a row load its 128 bytes in one instruction. Column pair jp of the step belongs to
-  // position q = 2 jp / QS. Tokens past L (and chunks past the ends) read a valid stand-in
-  // and are weighted 0.
+  // unit q = 2 jp / UT. Tokens past L (and units past the segment) read a valid stand-in and are
+  // weighted 0.
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   constexpr bool kGate = ADJ;
@@ -327,18 +347,21 @@ __global__ __launch_bounds__(64 * (N / 32)) void ssd_chunk_state_kernel(SsdParam
 #pragma unroll
     for (int e = 0; e < XPER; ++e) {
       const int it = std::min(tid + e * NT, kItems - 1), jp = it / (kP / 8), pg = it % (kP / 8);
-      const int q = (2 * jp) / QS, j = (2 * jp) % QS;
-      const int64_t c = clamp_chunk(chunk_at(k, q));
+      const int q = (2 * jp) / UT, j = (2 * jp) % UT;
+      int64_t c;
+      int off;
+      unit_at(k, q, c, off);
+      c = clamp_chunk(c);
       const float2* sp = p.ws_sphi + ((b * nch + c) * H + h) * QS;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int64_t t = std::min<int64_t>(c * QS + j + u, L - 1);
-        const int64_t off = ((b * L + t) * H + h) * kP + 8 * pg;
-        in.x[e][u] = *reinterpret_cast<const u32x4*>(xg + off);
+        const int64_t t = std::min<int64_t>(c * QS + off + j + u, L - 1);
+        const int64_t o = ((b * L + t) * H + h) * kP + 8 * pg;
+        in.x[e][u] = *reinterpret_cast<const u32x4*>(xg + o);
         if constexpr (kGate) {
-          if (zg) in.z[e][u] = *reinterpret_cast<const u32x4*>(zg + off);
+          if (zg) in.z[e][u] = *reinterpret_cast<const u32x4*>(zg + o);
         }
-        in.sp[e][u] = reinterpret_cast<const f32x2*>(sp)[j + u];
+        in.sp[e][u] = reinterpret_cast<const f32x2*>(sp)[off + j + u];
       }
       in.se[e] = sp[QS - 1].x;
     }
@@ -351,12 +374,14 @@ __global__ __launch_bounds__(64 * (N / 32)) void ssd_chunk_state_kernel(SsdParam
     for (int e = 0; e < XPER; ++e) {
       const int it = tid + e * NT, jp = it / (kP / 8), pg = it % (kP / 8);
       if (kItems < NT && it >= kItems) continue;
-      const int q = (2 * jp) / QS, j = (2 * jp) % QS;
-      const int64_t c = chunk_at(k, q);
+      const int q = (2 * jp) / UT, j = (2 * jp) % UT;
+      int64_t c;
+      int off;
+      unit_at(k, q, c, off);
       float wt[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const bool live = c >= 0 && c < nch && c * QS + j + u < L;
+        const bool live = live_chunk(c) && c * QS + off + j + u < L;
         const float wv = ADJ ? exp2_fast(a2 * in.sp[e][u].x) : exp2_fast(a2 * (in.se[e] - in.sp[e][u].x)) * in.sp[e][u].y;
         wt[u] = live ? wv : 0.f;
       }
@@ -388,15 +413,18 @@ __global__ __launch_bounds__(64 * (N / 32)) void ssd_chunk_state_kernel(SsdParam
     const int col = 16 * s + 8 * hi;   // in bf16 elements; the XOR swizzle moves whole words
     return *reinterpret_cast<const bf16x8*>(&xsb[row * XS + (col ^ (2 * xt_swizzle_words<Q>(row)))]);
   };
-  // A operands of step k: the 1 KB fragments of B^T (C^T) rows 32 w .. + 31 for each chunk and
-  // 16-token step (chunks past the ends read a valid stand-in, never used)
+  // A operands of step k: the 1 KB fragments of B^T (C^T) rows 32 w .. + 31 for each unit and
+  // 16-token step (units past the segment read a valid stand-in, never used)
   auto load_ring = [&](int64_t k, bf16x8 (&r)[KQ]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < NSUB; ++q) {
-      const int64_t c = clamp_chunk(chunk_at(k, q));
+    for (int q = 0; q < NU; ++q) {
+      int64_t c;
+      int off;
+      unit_at(k, q, c, off);
+      c = clamp_chunk(c);
 #pragma unroll
-      for (int s = 0; s < KQS; ++s)
-        r[q * KQS + s] = load_frag(Bt_all + c * (int64_t)(N * QS) + ((int64_t)w * KQS + s) * 512 + lane * 8);
+      for (int s = 0; s < KU; ++s)
+        r[q * KU + s] = load_frag(Bt_all + c * (int64_t)(N * QS) + ((int64_t)w * (QS / 16) + off / 16 + s) * 512 + lane * 8);
     }
   };
   bf16_t* hc_all = static_cast<bf16_t*>(ADJ ? p.ws_gout : p.ws_hin);
@@ -409,6 +437,8 @@ __global__ __launch_bounds__(64 * (N / 32)) void ssd_chunk_state_kernel(SsdParam
         *reinterpret_cast<uint2*>(hc + (int64_t)(32 * pt + l32) * N + 32 * w + 8 * k + 4 * hi) =
             make_uint2(pack_bf16x2(acc[pt][4 * k], acc[pt][4 * k + 1]), pack_bf16x2(acc[pt][4 * k + 2], acc[pt][4 * k + 3]));
   };
+  // segments: the sum of the step sizes of the segment's chunks before the current one
+  float dsum = 0.f;
 
   // Two register sets of B^T fragments used by step parity (the loop is unrolled by two so they
   // are named statically): the fragments of step k + 1 are loaded while step k runs.
@@ -423,13 +453,34 @@ __global__ __launch_bounds__(64 * (N / 32)) void ssd_chunk_state_kernel(SsdParam
   __syncthreads();
   auto step = [&](int64_t k, const bf16x8 (&cur)[KQ], bf16x8 (&nxt)[KQ]) __attribute__((always_inline)) {
     const __bf16* xsb = Xs[k & 1];
-    // decays of the step's chunks (uniform loads)
-    float dec[NSUB];
+    // the step sizes summed over the chunks of the step's units (uniform loads)
+    float stot[NU];
 #pragma unroll
-    for (int q = 0; q < NSUB; ++q) {
-      const int64_t c = clamp_chunk(chunk_at(k, q));
-      dec[q] = exp2_fast(a2 * p.ws_sphi[((b * nch + c) * H + h) * QS + QS - 1].x);
+    for (int q = 0; q < NU; ++q) {
+      int64_t c;
+      int off;
+      unit_at(k, q, c, off);
+      stot[q] = p.ws_sphi[((b * nch + clamp_chunk(c)) * H + h) * QS + QS - 1].x;
     }
+    // a chunk's first unit in the walk: store the carried state, then decay it over the chunk
+    auto chunk_start = [&](int q, int64_t c) __attribute__((always_inline)) {
+      store_carried(c);
+      if (!ADJ && nseg > 1 && w == 0 && lane == 0) p.ws_dpre[(b * nch + c) * H + h] = dsum;
+      dsum += stot[q];
+      const float dec = exp2_fast(a2 * stot[q]);
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[pt][v] *= dec;
+    };
+    // The first unit's stores go out before the step's loads: with stores and loads in flight
+    // together the compiler can only wait for all of them, and the next wait (at the next step)
+    // then finds the stores older than the loads it needs.
+    int64_t c0;
+    int off0;
+    unit_at(k, 0, c0, off0);
+    const bool start0 = live_chunk(c0) && off0 == (ADJ ? QS - UT : 0);
+    if (start0) chunk_start(0, c0);   // uniform
     // the next step's x^T into the other buffer (free since the last barrier); x of step k + 2
     // and the fragments of step k + 1 loaded (past the end: a repeated step, every load stays
     // unconditional)
@@ -437,26 +488,24 @@ __global__ __launch_bounds__(64 * (N / 32)) void ssd_chunk_state_kernel(SsdParam
     load_x(k + 2 < nst ? k + 2 : nst - 1, in);
     load_ring(k + 1 < nst ? k + 1 : nst - 1, nxt);
 #pragma unroll
-    for (int q = 0; q < NSUB; ++q) {
-      const int64_t c = chunk_at(k, q);
-      if (c < 0 || c >= nch) break;   // uniform: the remaining positions are past the ends
-      store_carried(c);
-#pragma unroll
-      for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[pt][v] *= dec[q];
+    for (int q = 0; q < NU; ++q) {
+      int64_t c;
+      int off;
+      unit_at(k, q, c, off);
+      if (!live_chunk(c)) break;   // uniform: the remaining units are past the segment
+      if (q > 0 && off == (ADJ ? QS - UT : 0)) chunk_start(q, c);
       // x fragments read one step ahead of their products
       bf16x8 xf[2][2];
-      xf[0][0] = frag_x(xsb, q * KQS, 0);
-      xf[0][1] = frag_x(xsb, q * KQS, 1);
+      xf[0][0] = frag_x(xsb, q * KU, 0);
+      xf[0][1] = frag_x(xsb, q * KU, 1);
 #pragma unroll
-      for (int s = 0; s < KQS; ++s) {
-        if (s + 1 < KQS) {
-          xf[(s + 1) & 1][0] = frag_x(xsb, q * KQS + s + 1, 0);
-          xf[(s + 1) & 1][1] = frag_x(xsb, q * KQS + s + 1, 1);
+      for (int s = 0; s < KU; ++s) {
+        if (s + 1 < KU) {
+          xf[(s + 1) & 1][0] = frag_x(xsb, q * KU + s + 1, 0);
+          xf[(s + 1) & 1][1] = frag_x(xsb, q * KU + s + 1, 1);
         }
 #pragma unroll
-        for (int pt = 0; pt < 2; ++pt) acc[pt] = mfma32(cur[q * KQS + s], xf[s & 1][pt], acc[pt]);
+        for (int pt = 0; pt < 2; ++pt) acc[pt] = mfma32(cur[q * KU + s], xf[s & 1][pt], acc[pt]);
       }
     }
     __syncthreads();
@@ -468,17 +517,44 @@ __global__ __launch_bounds__(64 * (N / 32)) void ssd_chunk_state_kernel(SsdParam
   }
   if (k < nst) step(k, ringA, ringB);
 
-  float* s_out = ADJ ? p.dh0 : p.h_last;
+  // the end state: the final one (one segment), else the segment's own (for the carry kernel)
+  float* fin = ADJ ? p.dh0 : p.h_last;
+  float* s_out = nseg > 1 ? p.ws_seg_h + ((b * nseg + seg) * H + h) * PN : (fin ? fin + (b * H + h) * PN : nullptr);
   if (s_out) {
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
-      float* dst = s_out + (b * H + h) * PN + (int64_t)(32 * pt + l32) * N + 32 * w + 4 * hi;
+      float* dst = s_out + (int64_t)(32 * pt + l32) * N + 32 * w + 4 * hi;
 #pragma unroll
       for (int k2 = 0; k2 < 4; ++k2)
         *reinterpret_cast<float4*>(dst + 8 * k2) =
             make_float4(acc[pt][4 * k2], acc[pt][4 * k2 + 1], acc[pt][4 * k2 + 2], acc[pt][4 * k2 + 3]);
     }
   }
+  if (nseg > 1 && tid == 0) p.ws_seg_s[(b * nseg + seg) * H + h] = dsum;
+}
+
+// grid (ceil(P N / 4 / 256), H, B): composes the segments of the chunk-state pass. The state
+// entering segment s is h_in[s] = exp(a S[s-1]) h_in[s-1] + e[s-1] (h_in[0] = h0), with e the
+// segments' own end states and S their sums of step sizes; h_in[s] for s >= 1 goes to ws_seg_in
+// (bf16, for the output kernel) and the state after the last segment to h_last.
+__global__ __launch_bounds__(256) void ssd_seg_carry_kernel(SsdParams p, int nseg) {
+  const int64_t h = blockIdx.y, b = blockIdx.z;
+  const int64_t PN = p.P * p.N;
+  const int64_t e4 = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 4 consecutive states
+  if (e4 * 4 >= PN) return;
+  const float a2 = p.A[h] * kLog2e;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (p.h0) v = reinterpret_cast<const float4*>(p.h0 + (b * p.H + h) * PN)[e4];
+  for (int s = 0; s < nseg; ++s) {
+    if (s > 0) {
+      bf16_t* dst = static_cast<bf16_t*>(p.ws_seg_in) + ((b * nseg + s) * p.H + h) * PN + e4 * 4;
+      *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+    }
+    const float d = exp2_fast(a2 * p.ws_seg_s[(b * nseg + s) * p.H + h]);
+    const float4 e = reinterpret_cast<const float4*>(p.ws_seg_h + ((b * nseg + s) * p.H + h) * PN)[e4];
+    v = make_float4(fmaf(d, v.x, e.x), fmaf(d, v.y, e.y), fmaf(d, v.z, e.z), fmaf(d, v.w, e.w));
+  }
+  if (p.h_last) reinterpret_cast<float4*>(p.h_last + (b * p.H + h) * PN)[e4] = v;
 }
 
 }  // namespace

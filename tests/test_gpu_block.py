@@ -116,6 +116,13 @@ def test_block_step_conv_widths(Dm, W):
     assert max(max(e) for e in errs) <= gu.TOL["bf16"]
 
 
+@pytest.mark.parametrize("R", [128, 256])
+def test_block_step_wide_model(R):
+    """d_model 4096 (32 K chunks of the input projection), rank 128 and 256."""
+    errs = _block_run(Bsz=6, Dm=4096, Di=256, N=16, steps=2, seed=95 + R // 128, R=R)
+    assert max(max(e) for e in errs) <= gu.TOL["bf16"]
+
+
 def test_block_step_mamba_1_4b_layer():
     """Batch 128, d_model 2048, d_inner 4096, N 16, conv 4, rank 128: two tokens."""
     errs = _block_run(Bsz=128, Dm=2048, Di=4096, N=16, steps=2, seed=72)

@@ -188,15 +188,20 @@ constexpr int kGemmKC = 128;  // K chunk
 constexpr int kGemmXS = kGemmKC + 8;   // LDS row stride (bf16) of an X chunk
 constexpr int kGemmNW = 8;    // waves per workgroup: 16 output columns each
 
-template <int MT>
+template <int MT, bool XRES = false>
 __global__ __launch_bounds__(64 * kGemmNW) void gemm_xwt_kernel(GemmParams p) {
-  constexpr int kGemmPD = 2;   // W chunks in flight per wave (the loop is unrolled by this)
+  // W chunks in flight per wave (the loop is unrolled by this); with the X slice resident the
+  // loop has no barrier, so a deeper ring keeps more of the weight stream in flight
+  constexpr int kGemmPD = XRES ? 4 : 2;
   constexpr int NT = 64 * kGemmNW;
   constexpr int ROWS = MT * 16;
   constexpr int KS = kGemmKC / 32;                         // 32-wide steps per chunk
   constexpr int XPIECES = ROWS * (kGemmKC / 8);            // 16-byte pieces of an X chunk
   constexpr int XPER = (XPIECES + NT - 1) / NT;            // per thread
-  __shared__ __attribute__((aligned(16))) __bf16 xs[2][ROWS * kGemmXS];
+  __shared__ __attribute__((aligned(16))) __bf16 xs_st[XRES ? 1 : 2][XRES ? 8 : ROWS * kGemmXS];
+  // resident X: the row block's whole K slice, rows kslice + 8 elements apart (dynamic LDS)
+  extern __shared__ __attribute__((aligned(16))) __bf16 xs_dyn[];
+  __bf16* const xs0 = XRES ? xs_dyn : &xs_st[0][0];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t col0 = (int64_t)blockIdx.x * 16 * kGemmNW;
@@ -207,34 +212,47 @@ __global__ __launch_bounds__(64 * kGemmNW) void gemm_xwt_kernel(GemmParams p) {
   const bf16_t* W = static_cast<const bf16_t*>(p.w);
   const bf16_t* X = static_cast<const bf16_t*>(p.x);
 
-  // this wave's W rows (zero past Nout)
-  const int64_t nrow = col0 + w * 16 + r16;
-  const bool n_ok = nrow < p.Nout;
-  const bf16_t* wrow = W + (n_ok ? nrow : 0) * p.K + kbeg + 8 * g;
+  // this wave's W rows and the row block's X rows through buffer descriptors: a row past Nout (or
+  // past M) lies beyond the descriptor's size and reads as zero, so no load is conditional and the
+  // compiler's count of loads in flight stays exact (a branch around a load makes it wait for
+  // every load at the join). Sizes are counted from the slice start kbeg; a valid row's slice ends
+  // at or before K, so it stays inside.
+  const int64_t wrow0 = col0 + w * 16;
+  const int64_t wrows = std::max<int64_t>(0, std::min<int64_t>(16, p.Nout - wrow0));
+  const Rsrc wr_rs = make_rsrc(W + std::min<int64_t>(wrow0, p.Nout - 1) * p.K + kbeg,
+                               (int)(wrow0 < p.Nout ? wrows * p.K * 2 - kbeg * 2 : 0));
+  const uint32_t wlane = (uint32_t)((r16 * p.K + 8 * g) * 2);
+  // a chunk past the end loads from an offset past every descriptor's size: it reads zeros
+  // (unused) and moves no data
+  constexpr uint32_t kPastEnd = 0x80000000u;
   auto load_w = [&](int64_t c, bf16x8 out[KS]) __attribute__((always_inline)) {
-    const int64_t cc = c < nchunks ? c : nchunks - 1;   // past the end: a repeated, unused load
+    const uint32_t o = c < nchunks ? wlane + (uint32_t)(c * kGemmKC * 2) : kPastEnd;
 #pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2)
-      out[s2] = n_ok ? *reinterpret_cast<const bf16x8*>(wrow + cc * kGemmKC + s2 * 32) : zero8();
+    for (int s2 = 0; s2 < KS; ++s2) {
+      uint4 v;
+      buf_load(wr_rs, o + (uint32_t)(s2 * 64), v);
+      out[s2] = __builtin_bit_cast(bf16x8, v);
+    }
   };
   // this thread's pieces of an X chunk: row e / (KC / 8), 8-element column group e % (KC / 8)
+  // (threads past the pieces read past the size, and their values are never stored)
   constexpr int PPR = kGemmKC / 8;
+  const int64_t xrows = std::max<int64_t>(0, std::min<int64_t>(ROWS, p.M - m0));
+  const Rsrc x_rs = make_rsrc(X + std::min<int64_t>(m0, p.M - 1) * p.ldx + kbeg,
+                              (int)(m0 < p.M ? (xrows - 1) * p.ldx * 2 + (p.K - kbeg) * 2 : 0));
   auto load_x = [&](int64_t c, uint4 out[XPER]) __attribute__((always_inline)) {
-    const int64_t cc = c < nchunks ? c : nchunks - 1;
+    const uint32_t o = c < nchunks ? (uint32_t)(c * kGemmKC * 2) : kPastEnd;
 #pragma unroll
     for (int k = 0; k < XPER; ++k) {
       const int e = tid + NT * k;
-      const int64_t m = m0 + e / PPR;
-      out[k] = make_uint4(0, 0, 0, 0);
-      if (e < XPIECES && m < p.M)
-        out[k] = *reinterpret_cast<const uint4*>(X + m * p.ldx + kbeg + cc * kGemmKC + (e % PPR) * 8);
+      buf_load(x_rs, o + (uint32_t)(((e / PPR) * p.ldx + (e % PPR) * 8) * 2), out[k]);
     }
   };
   auto store_x = [&](int buf, const uint4 in[XPER]) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < XPER; ++k) {
       const int e = tid + NT * k;
-      if (e < XPIECES) *reinterpret_cast<uint4*>(&xs[buf][(e / PPR) * kGemmXS + (e % PPR) * 8]) = in[k];
+      if (e < XPIECES) *reinterpret_cast<uint4*>(&xs0[buf * (ROWS * kGemmXS) + (e / PPR) * kGemmXS + (e % PPR) * 8]) = in[k];
     }
   };
 
@@ -282,47 +300,93 @@ __global__ __launch_bounds__(64 * kGemmNW) void gemm_xwt_kernel(GemmParams p) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   bf16x8 wr[kGemmPD][KS];
-#pragma unroll
-  for (int k = 0; k < kGemmPD; ++k) load_w(k, wr[k]);
-  // X chunks two ahead in registers: xr[(c + 1) % 2] holds chunk c + 1 when chunk c is used
-  uint4 xr[2][XPER];
-  load_x(0, xr[0]);
-  store_x(0, xr[0]);
-  load_x(1, xr[1]);
-  load_x(2, xr[0]);
-  __syncthreads();
-
-  // chunk c: X from LDS buffer c % 2, W from ring slot c % PD (PD even, so slot parity = c parity)
-  auto step = [&](int64_t c, int slot) __attribute__((always_inline)) {
-    const int buf = (int)(c & 1);
-#pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 xf = *reinterpret_cast<const bf16x8*>(&xs[buf][(mt * 16 + r16) * kGemmXS + s2 * 32 + 8 * g]);
-        acc[mt] = mfma16(wr[slot][s2], xf, acc[mt]);
-      }
-    }
-    load_w(c + kGemmPD, wr[slot]);        // refill the slot just used
-    store_x(buf ^ 1, xr[(slot + 1) & 1]);  // chunk c + 1 (its buffer held chunk c - 1)
-    load_x(c + 3, xr[(slot + 1) & 1]);
-    __syncthreads();
-  };
   int64_t c = 0;
-  for (; c + kGemmPD <= nchunks; c += kGemmPD) {
+  if constexpr (XRES) {
+    // The row block's X slice goes straight to LDS once (each wave load moves 1 KB: 512 elements
+    // of one row, lane l's 16 bytes landing 16 l bytes after the load's base); rows past M read
+    // as zero. Then the weight ring is issued, and the wait for all but the ring's loads retires
+    // the X loads. No barrier interrupts the stream after that.
+    const int64_t XSTR = p.kslice + 8;
+    const int per_row = (int)(p.kslice / 512);
+    for (int q = w; q < ROWS * per_row; q += kGemmNW) {   // uniform per wave
+      const int r = q / per_row, part = q % per_row;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          x_rs, (__attribute__((address_space(3))) void*)(xs0 + r * XSTR + part * 512), 16,
+          (uint32_t)((r * p.ldx + part * 512 + lane * 8) * 2), 0, 0, 0);
+    }
 #pragma unroll
-    for (int k = 0; k < kGemmPD; ++k) step(c + k, k);
+    for (int k = 0; k < kGemmPD; ++k) load_w(k, wr[k]);
+    constexpr int kRing = kGemmPD * KS;   // loads of the ring, issued after the X loads
+    static_assert(kRing < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((kRing & 15) | ((kRing >> 4) << 14) | 0x0F70);
+    __syncthreads();
+    const __bf16* xrow[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) xrow[mt] = xs0 + (mt * 16 + r16) * XSTR + 8 * g;
+    // chunk c: X from the resident rows, W from ring slot c % PD
+    auto step = [&](int64_t cc, int slot) __attribute__((always_inline)) {
+      const int kc = (int)(cc * kGemmKC);
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const bf16x8 xf = *reinterpret_cast<const bf16x8*>(xrow[mt] + kc + s2 * 32);
+          acc[mt] = mfma16(wr[slot][s2], xf, acc[mt]);
+        }
+      }
+      load_w(cc + kGemmPD, wr[slot]);   // refill the slot just used
+    };
+    for (; c + kGemmPD <= nchunks; c += kGemmPD) {
+#pragma unroll
+      for (int k = 0; k < kGemmPD; ++k) step(c + k, k);
+    }
+#pragma unroll
+    for (int k = 0; k < kGemmPD; ++k)
+      if (c + k < nchunks) step(c + k, k);
+    // every wave is done with X before the epilogue parks its u tile over it
+    if (xp_on) __syncthreads();   // uniform
+  } else {
+#pragma unroll
+    for (int k = 0; k < kGemmPD; ++k) load_w(k, wr[k]);
+    // X chunks two ahead in registers: xr[(c + 1) % 2] holds chunk c + 1 when chunk c is used
+    uint4 xr[2][XPER];
+    load_x(0, xr[0]);
+    store_x(0, xr[0]);
+    load_x(1, xr[1]);
+    load_x(2, xr[0]);
+    __syncthreads();
+
+    // chunk c: X from LDS buffer c % 2, W from ring slot c % PD (PD even, so slot parity = c parity)
+    auto step = [&](int64_t cc, int slot) __attribute__((always_inline)) {
+      const int buf = (int)(cc & 1);
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const bf16x8 xf = *reinterpret_cast<const bf16x8*>(&xs0[buf * (ROWS * kGemmXS) + (mt * 16 + r16) * kGemmXS + s2 * 32 + 8 * g]);
+          acc[mt] = mfma16(wr[slot][s2], xf, acc[mt]);
+        }
+      }
+      load_w(cc + kGemmPD, wr[slot]);        // refill the slot just used
+      store_x(buf ^ 1, xr[(slot + 1) & 1]);  // chunk c + 1 (its buffer held chunk c - 1)
+      load_x(cc + 3, xr[(slot + 1) & 1]);
+      __syncthreads();
+    };
+    for (; c + kGemmPD <= nchunks; c += kGemmPD) {
+#pragma unroll
+      for (int k = 0; k < kGemmPD; ++k) step(c + k, k);
+    }
+#pragma unroll
+    for (int k = 0; k < kGemmPD; ++k)
+      if (c + k < nchunks) step(c + k, k);
   }
-#pragma unroll
-  for (int k = 0; k < kGemmPD; ++k)
-    if (c + k < nchunks) step(c + k, k);
 
   // epilogue: the lane holds n = col0 + w 16 + 4 g + r, m = m0 + mt 16 + r16. With the
   // x-projection epilogue the u values of this workgroup (all in the conv range, as conv_D is a
   // multiple of 128) are also parked in LDS as a [ROWS][kGemmXS] bf16 tile (the X buffers are free
   // after the last chunk's barrier); rows past M are left as they are and only feed rows that are
   // never stored.
-  __bf16* ut = &xs[0][0];
+  __bf16* ut = xs0;
   const int64_t n = col0 + w * 16 + 4 * g;
   if (n < p.Nout) {
 #pragma unroll
@@ -724,10 +788,33 @@ static void launch_reduce(const GemmParams& p, hipStream_t stream) {
   else hipLaunchKernelGGL(gemm_reduce_kernel<8>, grid, dim3(256), 0, stream, p);
 }
 
+// The chunked kernel with the row block's X slice resident in LDS (kind 2): its dynamic LDS limit
+// is raised once per process to what a workgroup may hold.
+constexpr size_t kXresMaxLds = 160 * 1024 - 1024;
+size_t gemm_xres_lds_bytes(int mt, int64_t kslice) { return (size_t)mt * 16 * (size_t)(kslice + 8) * 2; }
+bool gemm_xres_fits(int mt, int64_t kslice) {
+  return mt <= 2 && kslice % 512 == 0 && gemm_xres_lds_bytes(mt, kslice) <= kXresMaxLds;
+}
+template <int MT>
+static hipError_t launch_xres(const GemmParams& p, dim3 grid, dim3 block, hipStream_t stream) {
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_xwt_kernel<MT, true>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXresMaxLds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((gemm_xwt_kernel<MT, true>), grid, block, gemm_xres_lds_bytes(MT, p.kslice), stream, p);
+  return hipSuccess;
+}
+
 hipError_t launch_gemm_with(GemmParams p, const GemmChoice& c, hipStream_t stream) {
   p.S = c.S;
   p.kslice = p.K / p.S;
-  if (c.kind == 0) {
+  if (c.kind == 2) {
+    if (!gemm_xres_fits(c.mt, p.kslice)) return hipErrorInvalidValue;
+    const int64_t blocks = (p.M + c.mt * 16 - 1) / (c.mt * 16);
+    const dim3 grid((unsigned)((p.Nout + 16 * kGemmNW - 1) / (16 * kGemmNW)), (unsigned)blocks, (unsigned)p.S);
+    const dim3 block(64 * kGemmNW);
+    const hipError_t e = c.mt == 1 ? launch_xres<1>(p, grid, block, stream) : launch_xres<2>(p, grid, block, stream);
+    if (e != hipSuccess) return e;
+  } else if (c.kind == 0) {
     const int64_t blocks = (p.M + c.mt * 16 - 1) / (c.mt * 16);
     const dim3 grid((unsigned)((p.Nout + 16 * kGemmNW - 1) / (16 * kGemmNW)), (unsigned)blocks, (unsigned)p.S);
     const dim3 block(64 * kGemmNW);
@@ -804,7 +891,9 @@ hipError_t launch_block_step(const BlockParams& bp, void* ws, hipStream_t st) {
     g.conv_state = bp.conv_state; g.conv_w = bp.conv_w; g.conv_b = bp.conv_b; g.u = u;
     g.conv_D = Di; g.conv_W = bp.W;
     g.xp_w = bp.W_xp; g.xp_n = XP; g.xp_partial = partial;   // [Delta rank | B | C] per 128-channel slice
-    e = launch_gemm_with(g, GemmChoice{0, std::min(row_tiles(B), 2), 0, 1}, st);
+    // (the X slice resident in LDS where a 32-row block of it fits)
+    const int mt = std::min(row_tiles(B), 2);
+    e = launch_gemm_with(g, GemmChoice{gemm_xres_fits(mt, Dm) ? 2 : 0, mt, 0, 1}, st);
   }
   if (e == hipSuccess) {   // xp = the sum of the Di / 128 slice partials
     GemmParams r{};

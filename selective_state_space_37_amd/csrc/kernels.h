@@ -218,11 +218,14 @@ struct GemmParams {
 // How a product runs. kind 0: the activations stream through LDS in K chunks (gemm_xwt_kernel, MT
 // row tiles per row block, S splits of K). kind 1: the activation slice is resident in LDS
 // (gemm_res_kernel, all rows in MT tiles, configuration cfg of kResCfgs, S = K / its slice).
+// kind 2: as kind 0, but each row block's whole K slice is loaded into LDS once and the weight
+// stream runs with no barrier (MT <= 2, K slice a multiple of 512 that fits; gemm_xres_fits).
 struct GemmChoice {
   int kind, mt, cfg;
   int64_t S;
 };
 GemmChoice gemm_plan(int64_t M, int64_t K, int64_t Nout);
+bool gemm_xres_fits(int mt, int64_t kslice);
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t Nout);
 hipError_t launch_gemm(GemmParams p, hipStream_t stream);
 hipError_t launch_gemm_with(GemmParams p, const GemmChoice& c, hipStream_t stream);

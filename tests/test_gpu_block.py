@@ -123,6 +123,15 @@ def test_block_step_wide_model(R):
     assert max(max(e) for e in errs) <= gu.TOL["bf16"]
 
 
+@pytest.mark.parametrize("Bsz,Dm", [(40, 512), (100, 1024), (33, 2048)])
+def test_block_step_resident_activations_ragged_rows(Bsz, Dm):
+    """d_model a multiple of 512: the input projection keeps each 32-row block of the normalised
+    activations resident in LDS (loaded straight to LDS once), and the last row block is ragged
+    (8, 4 and 1 live rows: the rows past the batch read as zero)."""
+    errs = _block_run(Bsz=Bsz, Dm=Dm, Di=256, N=16, steps=2, seed=60 + Bsz)
+    assert max(max(e) for e in errs) <= gu.TOL["bf16"]
+
+
 def test_block_step_mamba_1_4b_layer():
     """Batch 128, d_model 2048, d_inner 4096, N 16, conv 4, rank 128: two tokens."""
     errs = _block_run(Bsz=128, Dm=2048, Di=4096, N=16, steps=2, seed=72)

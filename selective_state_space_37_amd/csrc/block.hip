@@ -135,7 +135,10 @@ __global__ __launch_bounds__(256) void layernorm_kernel(int64_t D, const bf16_t*
 // channel the register of the last W inputs (oldest first) is shifted, the new input (rounded to
 // bf16, the register's type) appended, and u = SiLU(sum_k w[k] reg[k] + bias), the newest input
 // multiplied by w[W - 1]. At width 4 the caller has loaded the 32 register bytes (r0, r1).
-__device__ __forceinline__ float4 conv_silu4(const GemmParams& p, int64_t m, int64_t n, float4 v, uint4 r0, uint4 r1) {
+// (cwq, cbq: the width-4 weights of the four channels and their biases when the caller loaded
+// them ahead, else NULL)
+__device__ __forceinline__ float4 conv_silu4(const GemmParams& p, int64_t m, int64_t n, float4 v, uint4 r0, uint4 r1,
+                                             const float4* cwq = nullptr, const float4* cbq = nullptr) {
   const int64_t W = p.conv_W;
   bf16_t* reg = static_cast<bf16_t*>(p.conv_state) + (m * p.conv_D + n) * W;
   const float xv[4] = {v.x, v.y, v.z, v.w};
@@ -150,12 +153,14 @@ __device__ __forceinline__ float4 conv_silu4(const GemmParams& p, int64_t m, int
       // taps oldest first: (lo, hi) of word 2j, then of word 2j + 1; shift by one and append x
       const float t1 = bf16_hi(wd[2 * j]), t2 = bf16_lo(wd[2 * j + 1]), t3 = bf16_hi(wd[2 * j + 1]);
       const float t4 = bf16_to_f32(xb);
-      const float* cw = p.conv_w + (n + j) * 4;
-      float acc = p.conv_b ? p.conv_b[n + j] : 0.f;
-      acc += cw[0] * t1;
-      acc += cw[1] * t2;
-      acc += cw[2] * t3;
-      acc += cw[3] * t4;
+      const float* cwg = p.conv_w + (n + j) * 4;
+      const float4 cw = cwq ? cwq[j] : make_float4(cwg[0], cwg[1], cwg[2], cwg[3]);
+      const float cbv[4] = {cbq ? cbq->x : 0.f, cbq ? cbq->y : 0.f, cbq ? cbq->z : 0.f, cbq ? cbq->w : 0.f};
+      float acc = cbq ? cbv[j] : (p.conv_b ? p.conv_b[n + j] : 0.f);
+      acc += cw.x * t1;
+      acc += cw.y * t2;
+      acc += cw.z * t3;
+      acc += cw.w * t4;
       uo[j] = silu(acc);
       out[2 * j] = (wd[2 * j] >> 16) | (wd[2 * j + 1] << 16);
       out[2 * j + 1] = (wd[2 * j + 1] >> 16) | (xb << 16);
@@ -271,10 +276,21 @@ __global__ __launch_bounds__(64 * kGemmNW) void gemm_xwt_kernel(GemmParams p) {
   uint4 rg[kRegEarly ? MT : 1][2];
 #pragma unroll
   for (int mt = 0; mt < (kRegEarly ? MT : 1); ++mt) rg[mt][0] = rg[mt][1] = make_uint4(0, 0, 0, 0);
+  // and the width-4 weights and biases of the lane's four channels (a workgroup past conv_D
+  // reads channel conv_D - 4 as a stand-in)
+  float4 cwq[kRegEarly ? 4 : 1], cbq = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int j = 0; j < (kRegEarly ? 4 : 1); ++j) cwq[j] = make_float4(0.f, 0.f, 0.f, 0.f);
   if constexpr (kRegEarly) {
     if (p.conv_state && p.conv_W == 4) {   // uniform
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) reg_words(mt, rg[mt][0], rg[mt][1]);
+      // (element loads: the block step does not require these tensors to be 16-byte aligned)
+      const int64_t nc = std::min<int64_t>(ne, p.conv_D - 4);
+      const float* cw = p.conv_w + nc * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cwq[j] = make_float4(cw[4 * j], cw[4 * j + 1], cw[4 * j + 2], cw[4 * j + 3]);
+      if (p.conv_b) cbq = make_float4(p.conv_b[nc], p.conv_b[nc + 1], p.conv_b[nc + 2], p.conv_b[nc + 3]);
     }
   }
   // x-projection epilogue: this wave's W_xp fragments (output fragments w + 8 i, i < kXpF, of the
@@ -399,7 +415,8 @@ __global__ __launch_bounds__(64 * kGemmNW) void gemm_xwt_kernel(GemmParams p) {
       } else if (p.conv_state && n < p.conv_D) {
         float4 uv;
         if constexpr (kRegEarly) {
-          uv = conv_silu4(p, m, n, sv, rg[mt][0], rg[mt][1]);
+          uv = p.conv_W == 4 ? conv_silu4(p, m, n, sv, rg[mt][0], rg[mt][1], cwq, &cbq)
+                             : conv_silu4(p, m, n, sv, rg[mt][0], rg[mt][1]);
         } else {
           if (p.conv_W == 4) reg_words(mt, rg[0][0], rg[0][1]);
           uv = conv_silu4(p, m, n, sv, rg[0][0], rg[0][1]);

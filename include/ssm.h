@@ -292,7 +292,12 @@ ssm_status ssm_state_update(int64_t B, int64_t D, int64_t N, int64_t conv_width,
  *   (C_i . B_j) exp(a (cumsum Delta_i - cumsum Delta_j)) expm1(a Delta_j)/a on the matrix
  *   cores (bf16 operands, float32 accumulation); between chunks the float32 state.
  *
- *   Requirements: io_dtype SSM_BF16; P == 64; N in {64, 128}; chunk in {64, 128, 256};
+ *   io_dtype SSM_BF16, or SSM_F32: then x, z, Bm and Cm are first rounded to bf16 copies in the
+ *   workspace (they are the matrix-core operands either way), delta is read as float32, and y
+ *   is written as float32 (widened from a bf16 result); the accuracy is that of bf16 operands.
+ *   The float32 workspace is larger by 3 B L H P + 2 B L N bf16 elements.
+ *
+ *   Requirements: P == 64; N in {64, 128}; chunk in {64, 128, 256};
  *   B, L >= 0 (0 is a no-op; with L == 0 h_last receives h0 or zeros); 1 <= H <= 65535,
  *   B <= 65535 and at most 65535 chunks (grid dimensions).
  */
@@ -318,7 +323,8 @@ ssm_status ssd_chunk_fwd(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, 
  *
  *   Requirements: those of ssd_chunk_fwd; G >= 1 and G divides H; B * G <= 65535, H <= 65535
  *   and at most 65535 chunks. The workspace grows with G (C B^T and B per chunk are kept per
- *   group); query it with ssd_chunk_fwd_grouped_workspace_bytes.
+ *   group, and with SSM_F32 the bf16 copies of Bm and Cm); query it with
+ *   ssd_chunk_fwd_grouped_workspace_bytes.
  */
 size_t ssd_chunk_fwd_grouped_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N,
                                              int64_t G, int64_t chunk, ssm_dtype io_dtype);

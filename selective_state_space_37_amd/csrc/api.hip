@@ -464,15 +464,15 @@ ssm_status ssm_state_update(int64_t B, int64_t D, int64_t N, int64_t W, ssm_dtyp
 }
 
 size_t ssd_chunk_fwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t chunk,
-                                     ssm_dtype) {
+                                     ssm_dtype io) {
   if (B <= 0 || L <= 0 || H <= 0 || P <= 0 || N <= 0 || chunk <= 0) return 0;
-  return ssm::ssd_workspace_bytes(B, L, H, P, N, 1, chunk);
+  return ssm::ssd_workspace_bytes(B, L, H, P, N, 1, chunk, enum_bits(io) == SSM_F32);
 }
 
 size_t ssd_chunk_fwd_grouped_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
-                                             int64_t chunk, ssm_dtype) {
+                                             int64_t chunk, ssm_dtype io) {
   if (B <= 0 || L <= 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || chunk <= 0) return 0;
-  return ssm::ssd_workspace_bytes(B, L, H, P, N, G, chunk);
+  return ssm::ssd_workspace_bytes(B, L, H, P, N, G, chunk, enum_bits(io) == SSM_F32);
 }
 
 size_t ssm_linear_workspace_bytes(int64_t M, int64_t K, int64_t Nout) {
@@ -592,11 +592,12 @@ ssm_status ssd_common(const char* fn, int64_t B, int64_t L, int64_t H, int64_t P
   if (G < 1 || H % G != 0)
     return fail(SSM_ERR_INVALID_ARGUMENT, "G=%lld must be >= 1 and divide H=%lld", (long long)G, (long long)H);
   if (!valid_dtype(io)) return fail(SSM_ERR_INVALID_ARGUMENT, "unknown io_dtype %d", (int)io);
-  if (io != SSM_BF16) return fail(SSM_ERR_UNSUPPORTED, "%s supports io_dtype SSM_BF16 only", fn);
   if (P != 64) return fail(SSM_ERR_UNSUPPORTED, "P=%lld: supported head dim is 64", (long long)P);
   if (N != 64 && N != 128) return fail(SSM_ERR_UNSUPPORTED, "N=%lld: supported 64, 128", (long long)N);
   if (chunk != 64 && chunk != 128 && chunk != 256)
     return fail(SSM_ERR_UNSUPPORTED, "chunk=%lld: supported 64, 128, 256", (long long)chunk);
+  const bool f32 = io == SSM_F32;
+  const size_t esz = f32 ? 4 : 2;
   // grid limits: chunks and batch rows x groups index grid dimensions y and z, heads x
   if ((L + chunk - 1) / chunk > 65535)
     return fail(SSM_ERR_UNSUPPORTED, "L=%lld: at most 65535 chunks of %lld tokens", (long long)L, (long long)chunk);
@@ -617,13 +618,13 @@ ssm_status ssd_common(const char* fn, int64_t B, int64_t L, int64_t H, int64_t P
   if (!aligned16(x) || !aligned16(y) || !aligned16(Bm) || !aligned16(Cm) || (z && !aligned16(z)) ||
       (Dskip && dskip_per_channel && !aligned16(Dskip)))
     return fail(SSM_ERR_INVALID_ARGUMENT, "per-token tensors and a per-channel Dskip must be 16-byte aligned");
-  const size_t tok = (size_t)(B * L * H * P) * 2;
-  const size_t bc = (size_t)(B * L * G * N) * 2;
+  const size_t tok = (size_t)(B * L * H * P) * esz;
+  const size_t bc = (size_t)(B * L * G * N) * esz;
   const void* ins[] = {x, delta, z, Bm, Cm, A, h0};
-  const size_t insz[] = {tok, (size_t)(B * L * H) * 2, tok, bc, bc, (size_t)H * 4, stb};
+  const size_t insz[] = {tok, (size_t)(B * L * H) * esz, tok, bc, bc, (size_t)H * 4, stb};
   for (int k = 0; k < 7; ++k)
     if (overlaps(y, tok, ins[k], insz[k])) return fail(SSM_ERR_INVALID_ARGUMENT, "y overlaps an input");
-  const size_t need = ssm::ssd_workspace_bytes(B, L, H, P, N, G, chunk);
+  const size_t need = ssm::ssd_workspace_bytes(B, L, H, P, N, G, chunk, f32);
   if (!ws) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace is NULL; %zu bytes needed", need);
   if (ws_bytes < need) return fail(SSM_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, need);
   if (!aligned16(ws)) return fail(SSM_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
@@ -634,6 +635,7 @@ ssm_status ssd_common(const char* fn, int64_t B, int64_t L, int64_t H, int64_t P
   p.delta_bias = delta_bias; p.A = A; p.Dskip = Dskip; p.h0 = h0;
   p.dskip_per_channel = Dskip && dskip_per_channel ? 1 : 0;
   p.y = y; p.h_last = h_last; p.delta_softplus = delta_softplus ? 1 : 0;
+  p.io_f32 = f32 ? 1 : 0;
   ssm::ssd_workspace_carve(p, ws);
   return from_hip(ssm::launch_ssd(p, st), fn);
 }

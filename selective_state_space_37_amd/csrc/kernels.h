@@ -129,7 +129,13 @@ struct SsdParams {
   int64_t B, L, H, P, N, Q;  // Q = chunk length
   int64_t G;               // groups of B and C: head h reads group h / (H / G)
   const void* x;           // bf16 [B, L, H, P]
-  const void* delta;       // bf16 [B, L, H]
+  const void* delta;       // bf16 [B, L, H], float32 with delta_f32
+  int delta_f32;
+  // float32 per-token tensors (launch_ssd): x, z, B and C are first rounded to the bf16 copies
+  // cvt_x, cvt_z, cvt_B, cvt_C in the workspace, the layer runs on them with delta read as
+  // float32, and y is widened from cvt_y
+  int io_f32;
+  void *cvt_x, *cvt_z, *cvt_B, *cvt_C, *cvt_y;
   const void* z;           // nullable
   const void* Bm;          // bf16 [B, L, G, N]
   const void* Cm;
@@ -162,7 +168,8 @@ struct SsdParams {
                            // (in the backward ws_G holds G in float32, [Q][Q])
 };
 
-size_t ssd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q);
+size_t ssd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q,
+                           bool io_f32 = false);
 // Point the workspace fields of p at their parts of ws (ssd_workspace_bytes() bytes).
 void ssd_workspace_carve(SsdParams& p, void* ws);
 hipError_t launch_ssd(const SsdParams& p, hipStream_t stream);

@@ -393,15 +393,17 @@ int64_t ssd_state_segments(int64_t B, int64_t H, int64_t nch) {
   return std::max<int64_t>(1, std::min<int64_t>({(512 + chains / 2) / chains, 8, nch}));
 }
 
-size_t ssd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q) {
+size_t ssd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q, bool io_f32) {
   const int64_t nch = (L + Q - 1) / Q;
   const int64_t nseg = ssd_state_segments(B, H, nch);
   size_t seg = 0;
   if (nseg > 1)
     seg = ssd_align((size_t)(B * nseg * H * P * N) * 4) + ssd_align((size_t)(B * nseg * H) * 4) +
           ssd_align((size_t)(B * nseg * H * P * N) * 2) + ssd_align((size_t)(B * nch * H) * 4);
+  // float32 I/O: bf16 copies of x, z, B, C and y
+  const size_t cvt = io_f32 ? 3 * ssd_align((size_t)(B * L * H * P) * 2) + 2 * ssd_align((size_t)(B * L * G * N) * 2) : 0;
   return ssd_align((size_t)(B * nch * H * P * N) * 2) + ssd_align((size_t)(B * G * nch * Q * Q) * 2) +
-         ssd_align((size_t)(B * G * nch * N * Q) * 2) + ssd_align((size_t)(B * nch * H * Q) * 8) + seg;
+         ssd_align((size_t)(B * G * nch * N * Q) * 2) + ssd_align((size_t)(B * nch * H * Q) * 8) + seg + cvt;
 }
 
 void ssd_workspace_carve(SsdParams& p, void* ws) {
@@ -424,10 +426,37 @@ void ssd_workspace_carve(SsdParams& p, void* ws) {
     p.ws_seg_in = base;
     base += ssd_align((size_t)(p.B * p.nseg * p.H * p.P * p.N) * 2);
     p.ws_dpre = reinterpret_cast<float*>(base);
+    base += ssd_align((size_t)(p.B * nch * p.H) * 4);
+  }
+  if (p.io_f32) {
+    const size_t tok = ssd_align((size_t)(p.B * p.L * p.H * p.P) * 2), bc = ssd_align((size_t)(p.B * p.L * p.G * p.N) * 2);
+    p.cvt_x = base;
+    p.cvt_z = base + tok;
+    p.cvt_y = base + 2 * tok;
+    p.cvt_B = base + 3 * tok;
+    p.cvt_C = base + 3 * tok + bc;
   }
 }
 
-hipError_t launch_ssd(const SsdParams& p, hipStream_t stream) {
+namespace {
+// float32 I/O: n4 groups of four elements rounded to bf16 (nearest even), and widened back
+__global__ __launch_bounds__(256) void ssd_f32_to_bf16_kernel(const float* __restrict__ src, bf16_t* __restrict__ dst,
+                                                             int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    const float4 v = reinterpret_cast<const float4*>(src)[i];
+    reinterpret_cast<uint2*>(dst)[i] = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+  }
+}
+__global__ __launch_bounds__(256) void ssd_bf16_to_f32_kernel(const bf16_t* __restrict__ src, float* __restrict__ dst,
+                                                             int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    const uint2 v = reinterpret_cast<const uint2*>(src)[i];
+    reinterpret_cast<float4*>(dst)[i] = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+  }
+}
+dim3 cvt_grid(int64_t n4) { return dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>((n4 + 255) / 256, 4096))); }
+
+hipError_t launch_ssd_bf16(const SsdParams& p, hipStream_t stream) {
   if (p.N == 128) {
     if (p.Q == 64) return launch_qn<64, 128>(p, stream);
     if (p.Q == 128) return launch_qn<128, 128>(p, stream);
@@ -438,6 +467,34 @@ hipError_t launch_ssd(const SsdParams& p, hipStream_t stream) {
     if (p.Q == 256) return launch_qn<256, 64>(p, stream);
   }
   return hipErrorInvalidValue;
+}
+}  // namespace
+
+hipError_t launch_ssd(const SsdParams& p, hipStream_t stream) {
+  if (!p.io_f32) return launch_ssd_bf16(p, stream);
+  // float32 I/O (the element counts are multiples of 4: P = 64, N in {64, 128})
+  const int64_t ntok4 = p.B * p.L * p.H * p.P / 4, nbc4 = p.B * p.L * p.G * p.N / 4;
+  auto to_bf16 = [&](const void* src, void* dst, int64_t n4) {
+    hipLaunchKernelGGL(ssd_f32_to_bf16_kernel, cvt_grid(n4), dim3(256), 0, stream, static_cast<const float*>(src),
+                       static_cast<bf16_t*>(dst), n4);
+  };
+  to_bf16(p.x, p.cvt_x, ntok4);
+  if (p.z) to_bf16(p.z, p.cvt_z, ntok4);
+  to_bf16(p.Bm, p.cvt_B, nbc4);
+  to_bf16(p.Cm, p.cvt_C, nbc4);
+  SsdParams q = p;
+  q.io_f32 = 0;
+  q.delta_f32 = 1;
+  q.x = p.cvt_x;
+  q.z = p.z ? p.cvt_z : nullptr;
+  q.Bm = p.cvt_B;
+  q.Cm = p.cvt_C;
+  q.y = p.cvt_y;
+  const hipError_t e = launch_ssd_bf16(q, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ssd_bf16_to_f32_kernel, cvt_grid(ntok4), dim3(256), 0, stream,
+                     static_cast<const bf16_t*>(p.cvt_y), static_cast<float*>(p.y), ntok4);
+  return hipGetLastError();
 }
 
 }  // namespace ssm

@@ -60,7 +60,8 @@ __device__ void chunk_prologue(const SsdParams& p, int64_t b, int64_t c, int64_t
   const int64_t t = c * Q + tid;
   float dt = 0.f;
   if (tid < Q && t < p.L) {
-    dt = bf16_to_f32(static_cast<const bf16_t*>(p.delta)[(b * p.L + t) * p.H + h].bits) +
+    const int64_t i = (b * p.L + t) * p.H + h;
+    dt = (p.delta_f32 ? static_cast<const float*>(p.delta)[i] : bf16_to_f32(static_cast<const bf16_t*>(p.delta)[i].bits)) +
          (p.delta_bias ? p.delta_bias[h] : 0.f);
     if (p.delta_softplus) dt = softplus_f32(dt);
   }
@@ -534,17 +535,17 @@ __global__ __launch_bounds__(64 * (N / 32)) void ssd_chunk_state_kernel(SsdParam
 }
 
 // grid (ceil(P N / 4 / 256), H, B): composes the segments of the chunk-state pass. The state
-// entering segment s is h_in[s] = exp(a S[s-1]) h_in[s-1] + e[s-1] (h_in[0] = h0), with e the
-// segments' own end states and S their sums of step sizes; h_in[s] for s >= 1 goes to ws_seg_in
-// (bf16, for the output kernel) and the state after the last segment to h_last.
+// entering segment s >= 1 is h_in[s] = exp(a S[s-1]) h_in[s-1] + e[s-1] with h_in[1] = e[0]:
+// segment 0 ran from h0, so its end state e[0] already holds h0's part, while every later e[s]
+// is the segment's own (from zero); S are the segments' sums of step sizes. h_in[s] for s >= 1
+// goes to ws_seg_in (bf16, for the output kernel) and the state after the last segment to h_last.
 __global__ __launch_bounds__(256) void ssd_seg_carry_kernel(SsdParams p, int nseg) {
   const int64_t h = blockIdx.y, b = blockIdx.z;
   const int64_t PN = p.P * p.N;
   const int64_t e4 = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 4 consecutive states
   if (e4 * 4 >= PN) return;
   const float a2 = p.A[h] * kLog2e;
-  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (p.h0) v = reinterpret_cast<const float4*>(p.h0 + (b * p.H + h) * PN)[e4];
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);   // (h0 is inside e[0])
   for (int s = 0; s < nseg; ++s) {
     if (s > 0) {
       bf16_t* dst = static_cast<bf16_t*>(p.ws_seg_in) + ((b * nseg + s) * p.H + h) * PN + e4 * 4;

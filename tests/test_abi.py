@@ -197,13 +197,31 @@ def ssd_call(lib, B=1, L=512, H=2, P=64, N=128, chunk=256, io=BF16, x=A_, y=6 * 
 
 
 @pytest.mark.parametrize("kw,expect", [
-    (dict(io=F32), UNSUPPORTED), (dict(P=32), UNSUPPORTED), (dict(N=96), UNSUPPORTED),
+    (dict(io=F32, P=32), UNSUPPORTED), (dict(P=32), UNSUPPORTED), (dict(N=96), UNSUPPORTED),
     (dict(chunk=100), UNSUPPORTED), (dict(H=0), INVALID), (dict(x=0), INVALID), (dict(A=0), INVALID),
+    (dict(io=F32, wsb=16), WS_SMALL), (dict(io=7), INVALID),
     (dict(ws=None, wsb=0), WS_SMALL), (dict(wsb=16), WS_SMALL), (dict(y=A_ + 32), INVALID),
     (dict(x=A_ + 2), INVALID),
 ])
 def test_ssd_rejects(lib, kw, expect):
     assert ssd_call(lib, **kw) == expect
+
+
+def test_ssd_f32_workspace_holds_bf16_copies(lib):
+    """float32 I/O: the workspace adds bf16 copies of x, z, y (B L H P each) and of B, C."""
+    B, L, H, P, N, Q = 2, 1000, 4, 64, 128, 256
+    w16 = lib.ssd_chunk_fwd_workspace_bytes(B, L, H, P, N, Q, BF16)
+    w32 = lib.ssd_chunk_fwd_workspace_bytes(B, L, H, P, N, Q, F32)
+    assert w32 >= w16 + 3 * B * L * H * P * 2 + 2 * B * L * N * 2
+    g16 = lib.ssd_chunk_fwd_grouped_workspace_bytes(B, L, H, P, N, 2, Q, BF16)
+    g32 = lib.ssd_chunk_fwd_grouped_workspace_bytes(B, L, H, P, N, 2, Q, F32)
+    assert g32 >= g16 + 3 * B * L * H * P * 2 + 2 * B * L * 2 * N * 2
+
+
+def test_ssd_f32_checks_float32_sizes(lib):
+    """With SSM_F32 the overlap checks use 4-byte elements: y placed 160 KB after x lies inside
+    x's float32 extent (B L H P * 4 = 256 KB), past its bf16 extent (128 KB)."""
+    assert ssd_call(lib, B=1, L=512, H=2, io=F32, x=A_, y=A_ + (160 << 10)) == INVALID
 
 
 def ssd_grouped_call(lib, B=1, L=512, H=4, P=64, N=128, G=2, chunk=256, io=BF16, Dskip=None, dpc=0, wsb=1 << 40):

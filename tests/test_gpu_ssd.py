@@ -1,6 +1,6 @@
 """GPU parity of ssd_chunk_fwd (Mamba-2, scalar A per head) against the fp64 oracle's plain
 recurrence: every chunk length (chunk-size invariance), both state sizes, ragged L, the optional
-arguments, the state carried in and out, and the full-size layer (sampled heads)."""
+arguments, the state carried in and out, float32 I/O, and the full-size layer."""
 import ctypes
 
 import numpy as np
@@ -36,6 +36,19 @@ def test_softplus_and_bias():
     assert gu.ssd_parity(inp, gu.ssd_on_gpu(inp, chunk=64)) <= gu.TOL["bf16"]
 
 
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_initial_state_with_segments(chunk):
+    """h0 with slow decays (A = -0.5 .. -4, small steps) and 64- or 128-token chunks: the state pass
+    runs in L-segments (4 heads of one row: 8 segments), the first from h0 and the others from
+    zero, so h0 must enter the composition once (through the first segment's end state). Counted
+    twice, it adds about exp(a S) h0 again to the outputs of the second segment's chunks."""
+    inp = inputs.ssd_layer(seed=79, Bsz=1, L=700, H=4, N=64, h0=True)
+    inp.A = np.array([-0.5, -1.0, -2.0, -4.0], dtype=np.float32)
+    err = gu.ssd_parity(inp, gu.ssd_on_gpu(inp, chunk=chunk))
+    print("chunk", chunk, "err", err)
+    assert err <= gu.TOL["bf16"]
+
+
 def test_short_sequences():
     for L in (1, 17, 64):
         inp = inputs.ssd_layer(seed=73, Bsz=1, L=L, H=2, h0=True)
@@ -48,6 +61,53 @@ def test_chunk_invariance_between_gpu_runs():
     for y, hl in outs[1:]:
         assert gu.rel_err(y, outs[0][0]) <= gu.TOL["bf16"]
         assert gu.rel_err(hl, outs[0][1]) <= gu.TOL["bf16"]
+
+
+@pytest.mark.parametrize("chunk", [64, 256])
+@pytest.mark.parametrize("grouped", [False, True])
+def test_float32_io(chunk, grouped):
+    """float32 per-token tensors: x, z, B and C become bf16 copies in the workspace (the
+    matrix-core operands), delta is read as float32 and y written as float32. The accuracy is
+    that of bf16 operands, so the bar is the bf16 one."""
+    inp = inputs.ssd_layer(seed=76, Bsz=2, L=700, H=4, N=128, dtype="f32", gate=True, dskip=not grouped, h0=True,
+                           groups=2 if grouped else None, dskip_per_channel=grouped)
+    y, hl = gu.ssd_on_gpu(inp, chunk=chunk)
+    assert np.isfinite(y).all()
+    err = gu.ssd_parity(inp, (y, hl))
+    print("f32 io chunk", chunk, "grouped", grouped, "err", err)
+    assert err <= gu.TOL["bf16"]
+
+
+@pytest.mark.parametrize("chunk", [64, 256])
+def test_float32_io_equals_bf16_io_on_bf16_values(chunk):
+    """Inputs whose values are bf16 numbers, given once as float32 and once as bf16: the kernels
+    see the same operands and step sizes, so y (float32: the widened bf16 result) and the final
+    state agree bit for bit."""
+    b16 = inputs.ssd_layer(seed=78, Bsz=2, L=700, H=4, N=128, gate=True, dskip=True, h0=True)
+    f32 = inputs.ssd_layer(seed=78, Bsz=2, L=700, H=4, N=128, gate=True, dskip=True, h0=True)
+    f32.dtype = "f32"
+    for k in ("x", "delta", "Bm", "Cm", "z"):
+        setattr(f32, k, inputs.widen(getattr(b16, k), "bf16").astype(np.float32))
+    ya, ha = gu.ssd_on_gpu(b16, chunk=chunk)
+    yb, hb = gu.ssd_on_gpu(f32, chunk=chunk)
+    print("chunk", chunk, "max |dy|", np.abs(ya - yb).max(), "max |dh|", np.abs(ha - hb).max())
+    assert np.array_equal(ya, yb) and np.array_equal(ha, hb)
+
+
+def test_float32_io_step_sizes_kept_in_float32():
+    """Large step sizes (softplus of N(0, 1) + 0.5, about 0.1 .. 3.5) with A = -16 on every other
+    head: rounding each step size to bf16 would move the decay between neighbouring tokens by
+    about |A| Delta 2^-9 (3 % at Delta = 1), past the bar; delta read in float32 stays within it."""
+    inp = inputs.ssd_layer(seed=77, Bsz=1, L=512, H=2, N=64, dtype="f32", gate=True, dskip=True, h0=True)
+    inp.delta = inputs.store(np.random.default_rng(7).standard_normal((1, 512, 2)), "f32")
+    inp.delta_bias = np.full((2,), 0.5, dtype=np.float32)
+    inp.delta_softplus = True
+    inp.A = np.array([-16.0, -1.0], dtype=np.float32)
+    y, hl = gu.ssd_on_gpu(inp, chunk=128)
+    assert np.isfinite(y).all()
+    err = gu.ssd_parity(inp, (y, hl))
+    print("f32 io large steps err", err)
+    assert err <= gu.TOL["bf16"]
 
 
 def test_final_state_in_place():

@@ -2,6 +2,8 @@
 sizes, storage type and optional arguments from a generator seeded by the case number, so that
 combinations no hand-written case names (a state from h0 with segments, slow decays with small
 chunks, float32 with groups, ...) are still compared with the oracle, output and final state."""
+import copy
+
 import numpy as np
 import pytest
 
@@ -68,3 +70,89 @@ def test_ssd_sweep(k):
           % (k, Bsz, L, H, N, inp.groups, chunk, inp.dtype, inp.h0 is not None, inp.z is not None,
              inp.delta_softplus, err))
     assert err <= gu.TOL["bf16"]
+
+
+def _scan_bwd_case(k):
+    r = np.random.default_rng(5000 + k)
+    Bsz, L = int(r.integers(1, 3)), int(r.integers(1, 400))
+    D, N = 4 * int(r.integers(1, 33)), int(r.choice([1, 2, 4, 8, 16]))
+    dtype = str(r.choice(["f32", "bf16"]))
+    inp = inputs.scan_small(seed=6000 + k, Bsz=Bsz, L=L, D=D, N=N, dtype=dtype, gate=bool(r.integers(2)),
+                            dskip=bool(r.integers(2)), h0=bool(r.integers(2)))
+    seg = int(r.integers(8, 200)) if r.integers(2) else None
+    return inp, seg, bool(r.integers(2))
+
+
+@pytest.mark.parametrize("k", range(8))
+def test_scan_bwd_sweep(k):
+    inp, seg, dhl_on = _scan_bwd_case(k)
+    Bsz, L, D, N = inp.shape
+    dy, dhl = inputs.scan_grads(7000 + k, Bsz, L, D, N, inp.dtype, dh_last=dhl_on)
+    gpu = gu.scan_bwd_on_gpu(inp, dy, dhl, segment_len=seg)
+    errs = gu.scan_bwd_errors(gpu, gu.scan_bwd_oracle(inp, dy, dhl))
+    print("case %d: %dx%dx%d N %d %s segment %s" % (k, Bsz, L, D, N, inp.dtype, seg),
+          {n: "%.1e" % v for n, v in errs.items()})
+    bad = {n: v for n, v in errs.items() if not v <= gu.TOL[inp.dtype]}
+    assert not bad, bad
+
+
+def _ssd_bwd_case(k):
+    r = np.random.default_rng(8000 + k)
+    G = int(r.choice([1, 2]))
+    H = G * int(r.integers(1, 3))
+    Bsz, L, N = int(r.integers(1, 3)), int(r.integers(1, 300)), int(r.choice([64, 128]))
+    per_channel = G > 1 and bool(r.integers(2))
+    inp = inputs.ssd_layer(seed=9000 + k, Bsz=Bsz, L=L, H=H, N=N, gate=bool(r.integers(2)),
+                           dskip=bool(r.integers(2)) and not per_channel, h0=bool(r.integers(2)),
+                           groups=G, dskip_per_channel=per_channel)
+    inp.A = -np.exp(r.uniform(np.log(0.1), np.log(16.0), H)).astype(np.float32)
+    if r.integers(2):
+        inp.delta = inputs.store(r.standard_normal((Bsz, L, H)) * 0.5 - 2.0, "bf16")
+        inp.delta_bias = r.uniform(-0.5, 0.5, H).astype(np.float32)
+        inp.delta_softplus = True
+    return inp, bool(r.integers(2))
+
+
+def _perturbed_deviation(inp, dy, dhl, ref, keys, trials=2):
+    """How far the oracle's values of `keys` move when x, B, C, z and dy are each multiplied by
+    (1 + u 2^-9), u ~ U(-1, 1): the spread that bf16 operands alone put into a quantity. A sum over
+    every token of a head (dA, the bias gradient) can cancel down to a value far below its terms,
+    and then that spread is several times the bf16 bar."""
+    rng = np.random.default_rng(11)
+    dev = {k: 0.0 for k in keys}
+    for _ in range(trials):
+        p = copy.deepcopy(inp)
+        p.dtype = "f32"
+        p.delta = inputs.widen(inp.delta, "bf16").astype(np.float32)
+        for name in ("x", "Bm", "Cm", "z"):
+            a = getattr(inp, name)
+            if a is not None:
+                w = inputs.widen(a, "bf16")
+                setattr(p, name, (w * (1 + 2.0 ** -9 * rng.uniform(-1, 1, w.shape))).astype(np.float32))
+        w = inputs.widen(dy, "bf16")
+        dyp = (w * (1 + 2.0 ** -9 * rng.uniform(-1, 1, w.shape))).astype(np.float32)
+        ref2 = gu.ssd_bwd_oracle(p, dyp, dhl)
+        for k in keys:
+            if ref.get(k) is not None:
+                dev[k] = max(dev[k], gu.rel_err(ref2[k], ref[k]))
+    return dev
+
+
+@pytest.mark.parametrize("k", range(8))
+def test_ssd_bwd_sweep(k):
+    """Every gradient within the bf16 bar, except that the per-head sums (dA, the bias and D
+    gradients) may instead stay within 4 times their spread under bf16-sized input noise (an
+    ill-conditioned sum: two sweep cases have dA or the bias gradient 10-60 times smaller than
+    their terms)."""
+    inp, dhl_on = _ssd_bwd_case(k)
+    Bsz, L, H, P, N = inp.shape
+    dy, dhl = inputs.ssd_grads(10000 + k, Bsz, L, H, P, N, dh_last=dhl_on)
+    gpu = gu.ssd_bwd_on_gpu(inp, dy, dhl)
+    ref = gu.ssd_bwd_oracle(inp, dy, dhl)
+    errs = gu.ssd_bwd_errors(gpu, ref)
+    sums = ("dA", "ddelta_bias", "dDskip")
+    dev = _perturbed_deviation(inp, dy, dhl, ref, [n for n in sums if errs.get(n, 0.0) > gu.TOL["bf16"]])
+    print("case %d: %dx%dx%d N %d G %d" % (k, Bsz, L, H, N, inp.groups), {n: "%.1e" % v for n, v in errs.items()},
+          "spread", {n: "%.1e" % v for n, v in dev.items()})
+    bad = {n: v for n, v in errs.items() if not (v <= gu.TOL["bf16"] or (n in dev and v <= 4 * dev[n]))}
+    assert not bad, bad

@@ -53,7 +53,9 @@ int main(void) {
   for (int64_t L = 0; L <= 65536; L = L ? L * 4 : 1)
     for (int64_t q = 64; q <= 256; q *= 2) {
       acc += ssd_chunk_fwd_workspace_bytes(2, L, 80, 64, 128, q, SSM_BF16);
+      acc += ssd_chunk_fwd_workspace_bytes(2, L, 80, 64, 128, q, SSM_F32);
       acc += ssd_chunk_fwd_grouped_workspace_bytes(2, L, 80, 64, 64, 8, q, SSM_BF16);
+      acc += ssd_chunk_fwd_grouped_workspace_bytes(2, L, 80, 64, 64, 8, q, SSM_F32);
       acc += ssd_chunk_bwd_workspace_bytes(2, L, 80, 64, 128, 1, SSM_BF16);
     }
   for (int64_t M = 1; M <= 128; M *= 2) {
@@ -114,7 +116,10 @@ int main(void) {
   EXPECT(ssd_chunk_fwd(2, 512, 8, 64, 128, 100, SSM_BF16, P(1), P(2), NULL, 1, F(3), P(4), P(5), NULL,
                        NULL, NULL, P(6), NULL, P(9), (size_t)ws_big, NULL), SSM_ERR_UNSUPPORTED);
   EXPECT(ssd_chunk_fwd(2, 512, 8, 64, 128, 256, SSM_F32, P(1), P(2), NULL, 1, F(3), P(4), P(5), NULL,
-                       NULL, NULL, P(6), NULL, P(9), (size_t)ws_big, NULL), SSM_ERR_UNSUPPORTED);
+                       NULL, NULL, P(6), NULL, P(9), 16, NULL), SSM_ERR_WORKSPACE_TOO_SMALL);
+  EXPECT(ssd_chunk_bwd(2, 512, 8, 64, 128, 1, SSM_F32, P(1), P(2), NULL, 1, F(3), P(4), P(5), NULL, 0,
+                       NULL, NULL, P(6), NULL, P(7), P(8), F(9), F(10), F(11), NULL, NULL, NULL, NULL, P(12),
+                       (size_t)ws_big, NULL), SSM_ERR_UNSUPPORTED);   /* backward: bf16 only */
   EXPECT(ssd_chunk_fwd(2, 512, 8, 64, 128, 256, SSM_BF16, P(1), P(2), NULL, 1, F(3), P(4), P(5), NULL,
                        NULL, NULL, P(6), NULL, P(9), 16, NULL), SSM_ERR_WORKSPACE_TOO_SMALL);
   EXPECT(ssd_chunk_fwd_grouped(2, 512, 8, 64, 128, 3, 256, SSM_BF16, P(1), P(2), NULL, 1, F(3), P(4), P(5),

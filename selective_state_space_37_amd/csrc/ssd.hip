@@ -357,9 +357,9 @@ __global__ __launch_bounds__(64 * SsdOutCfg<Q>::NW) void ssd_out_kernel(SsdParam
 template <int Q, int N>
 hipError_t launch_qn(const SsdParams& p, hipStream_t stream) {
   const int64_t nch = (p.L + Q - 1) / Q;
-  hipLaunchKernelGGL((ssd_cumsum_kernel<Q>), dim3((unsigned)p.H, (unsigned)nch, (unsigned)p.B), dim3(256), 0,
-                     stream, p);
-  hipLaunchKernelGGL((ssd_prep_kernel<Q, N>), dim3(4, (unsigned)nch, (unsigned)(p.B * p.G)), dim3(256), 0, stream,
+  hipLaunchKernelGGL((ssd_cumsum_kernel<Q>), dim3((unsigned)((p.H + kCumHeads - 1) / kCumHeads), (unsigned)nch, (unsigned)p.B),
+                     dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((ssd_prep_kernel<Q, N>), dim3(prep_parts<Q>(), (unsigned)nch, (unsigned)(p.B * p.G)), dim3(256), 0, stream,
                      p);
   // the state pass: 128-token steps (lighter on registers, so two workgroups share a CU), cut
   // into L-segments when the heads alone leave CUs idle; the carry kernel composes the segments

@@ -784,9 +784,9 @@ hipError_t launch_n(const SsdBwdParams& bp, hipStream_t stream) {
   constexpr int Q = kQb;
   const SsdParams& p = bp.f;
   const int64_t nch = (p.L + Q - 1) / Q;
-  const dim3 chunks((unsigned)p.H, (unsigned)nch, (unsigned)p.B);
-  hipLaunchKernelGGL((ssd_cumsum_kernel<Q>), chunks, dim3(256), 0, stream, p);
-  hipLaunchKernelGGL((ssd_prep_kernel<Q, N, true>), dim3(4, (unsigned)nch, (unsigned)(p.B * p.G)), dim3(256), 0,
+  hipLaunchKernelGGL((ssd_cumsum_kernel<Q>), dim3((unsigned)((p.H + kCumHeads - 1) / kCumHeads), (unsigned)nch, (unsigned)p.B),
+                     dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((ssd_prep_kernel<Q, N, true>), dim3(prep_parts<Q>(), (unsigned)nch, (unsigned)(p.B * p.G)), dim3(256), 0,
                      stream, p);
   // the two state passes take the chunks four at a time (one 256-token step), storing the state
   // at every chunk boundary

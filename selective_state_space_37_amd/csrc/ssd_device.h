@@ -50,38 +50,6 @@ __device__ __forceinline__ void st_at(E* base, uint32_t byte_off, const T& v) {
 
 constexpr int kP = 64;  // head dim supported
 
-// Step sizes, inclusive cumulative sums and ZOH input scales of one chunk (Q <= 256 tokens),
-// for 256 threads. Tokens past L get Delta = 0 (identity).
-template <int Q>
-__device__ void chunk_prologue(const SsdParams& p, int64_t b, int64_t c, int64_t h, float a,
-                               float* sS, float* sPhi, float* sTot) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t t = c * Q + tid;
-  float dt = 0.f;
-  if (tid < Q && t < p.L) {
-    const int64_t i = (b * p.L + t) * p.H + h;
-    dt = (p.delta_f32 ? static_cast<const float*>(p.delta)[i] : bf16_to_f32(static_cast<const bf16_t*>(p.delta)[i].bits)) +
-         (p.delta_bias ? p.delta_bias[h] : 0.f);
-    if (p.delta_softplus) dt = softplus_f32(dt);
-  }
-  float v = dt;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
-  if (lane == 63) sTot[w] = v;
-  __syncthreads();
-  float pre = 0.f;
-  for (int k = 0; k < w; ++k) pre += sTot[k];
-  if (tid < Q) {
-    sS[tid] = v + pre;
-    sPhi[tid] = expm1f(a * dt) / a;
-  }
-  __syncthreads();
-}
-
 // LDS layout of a transposed x tile (rows = channels p, columns = tokens j, row stride Q + 8
 // bf16): the 4-byte word column of row p is XORed with 8 ((p >> 4) & 3) (kept inside the row).
 // The staging writes (8 channel groups x 8 token pairs per wave) then fall on 64 different banks
@@ -148,27 +116,102 @@ __device__ void stage_x_transposed_scaled(const SsdParams& p, int64_t b, int64_t
 }
 
 // ---------------------------------------------------------------------------- step sizes
-// grid (H, chunks, B): per chunk and head, the inclusive cumulative sum S_j of the step sizes and
-// the ZOH input scale phi_j = expm1(a Delta_j) / a, for the state and output kernels.
+// grid (ceil(H / 4), chunks, B), 256 threads: per chunk and head the inclusive cumulative sum
+// S_j of the step sizes (bias and softplus applied) and the ZOH input scale
+// phi_j = expm1(a Delta_j) / a, for the state and output kernels. A workgroup takes 4 heads, so
+// the step sizes of a token row come in as one contiguous run (8 bytes in bf16) rather than one
+// element 2 H bytes from the next; they pass through LDS (rows padded to a word past the heads),
+// and each wave then scans one head. Lane l owns tokens l, l + 64, ...: each 64-token block is one wave
+// scan, the blocks are joined by their totals, and every store of the (S, phi) table is 512
+// contiguous bytes. Tokens past L get Delta = 0 (identity).
+constexpr int kCumHeads = 4;
 template <int Q>
 __global__ __launch_bounds__(256) void ssd_cumsum_kernel(SsdParams p) {
-  __shared__ float sS[Q], sPhi[Q], sTot[4];
-  const int64_t h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
-  const int64_t nch = gridDim.y;
-  chunk_prologue<Q>(p, b, c, h, p.A[h], sS, sPhi, sTot);
+  static_assert(Q % 64 == 0 && Q <= 256, "chunks of 64, 128 or 256 tokens");
+  constexpr int NB = Q / 64;                        // 64-token blocks
+  constexpr int E = Q * kCumHeads / 256;            // loaded elements per thread
+  constexpr int RS = kCumHeads + 1;                 // LDS row stride (words)
+  __shared__ float sDt[Q * RS];
+  const int64_t h0 = (int64_t)blockIdx.x * kCumHeads, c = blockIdx.y, b = blockIdx.z;
+  const int64_t nch = gridDim.y, H = p.H, L = p.L;
   const int tid = threadIdx.x;
-  if (tid < Q) p.ws_sphi[((b * nch + c) * p.H + h) * Q + tid] = make_float2(sS[tid], sPhi[tid]);
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // every load issued before any is used
+  float raw[E];
+#pragma unroll
+  for (int k = 0; k < E; ++k) {
+    const int idx = tid + k * 256, row = idx / kCumHeads, hh = idx % kCumHeads;
+    const int64_t t = c * Q + row, h = h0 + hh;
+    raw[k] = 0.f;
+    if (t < L && h < H) {
+      const int64_t i = (b * L + t) * H + h;
+      raw[k] = p.delta_f32 ? static_cast<const float*>(p.delta)[i] : bf16_to_f32(static_cast<const bf16_t*>(p.delta)[i].bits);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < E; ++k) {
+    const int idx = tid + k * 256, row = idx / kCumHeads, hh = idx % kCumHeads;
+    const int64_t t = c * Q + row, h = h0 + hh;
+    float dt = 0.f;
+    if (t < L && h < H) {
+      dt = raw[k] + (p.delta_bias ? p.delta_bias[h] : 0.f);
+      if (p.delta_softplus) dt = softplus_f32(dt);
+    }
+    sDt[row * RS + hh] = dt;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kCumHeads / 4; ++i) {
+    const int hh = w * (kCumHeads / 4) + i;
+    const int64_t h = h0 + hh;
+    if (h >= H) break;   // uniform
+    const float a = p.A[h];
+    float dt[NB], v[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) v[u] = dt[u] = sDt[(lane + 64 * u) * RS + hh];
+    // inclusive scans of the blocks over the wave, interleaved
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const float o = __shfl_up(v[u], off, 64);
+        if (lane >= off) v[u] += o;
+      }
+    }
+    float2* dst = p.ws_sphi + ((b * nch + c) * H + h) * Q + lane;
+    float carry = 0.f;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      dst[64 * u] = make_float2(carry + v[u], expm1f(a * dt[u]) / a);
+      carry += __shfl(v[u], 63, 64);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------- prep
-// grid (4, chunks, B G): part `part` transposes states [part N/4, (part+1) N/4) of one group's B
-// and computes every fourth lower-triangular 16 x 16 tile of that group's G (row blocks ib,
-// column tiles jt <= ib). Token t's row of the group starts at element (t G + grp) N.
-// BWD: C is transposed as well, and G is stored in float32 (ws_G, [Q][Q]) for the backward's
-// elementwise use. Only the tiles on and below the diagonal of G are written; the forward packs
-// them (bf16) in row-block order for the output kernel's LDS copy.
+// grid (prep_parts<Q>(), chunks, B G), 256 threads.
+// (1) B^T (and C^T in the backward) of one group's chunk, written in the order the chunk-state
+// kernel reads its MFMA operands (v_mfma_f32_32x32x16_bf16, A = B^T): the piece
+// (n, j0 .. j0 + 7) of 32-row tile nt = n / 32 and 16-token step s = j0 / 16 is lane
+// n % 32 + 32 ((j0 / 8) % 2) of the 1 KB fragment (nt, s), fragments in the order nt Q / 16 + s,
+// so that one fragment load of a wave is 1 KB of consecutive memory. The backward's main kernel
+// also gets plain [n][j] copies (ws_Bt, ws_Ct). Part k takes states [k N / parts, (k + 1) N / parts),
+// a thread 8 tokens of one state per item (one 16-byte store); spreading the items over every part
+// keeps each thread's work to one round trip (the items are few per chunk). Token t's row of the
+// group starts at element (t G + grp) N.
+// (2) The lower-triangular 16 x 16 tiles of G = C B^T (row blocks ib, column tiles jt <= ib),
+// spread over the kPrepParts x 4 waves of a chunk; a wave issues the row loads of all its tiles
+// before its first product. BWD: G is stored in float32 (ws_G, [Q][Q]) for the backward's
+// elementwise use; the forward packs the tiles (bf16) in row-block order for the output kernel's
+// LDS copy.
+// Parts per chunk: Q / 16 (measured: 16 parts at 256-token chunks take 19 us against 22 us for
+// 4; 64-token chunks take 13 us with 4 parts against 24 us with 16).
+template <int Q>
+constexpr int prep_parts() { return Q / 16; }
 template <int Q, int N, bool BWD = false>
 __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
+  constexpr int kPrepParts = prep_parts<Q>();
+  static_assert(N % kPrepParts == 0, "the states divide over the parts");
   const int part = blockIdx.x;
   const int64_t c = blockIdx.y, bg = blockIdx.z;   // bg = b G + grp
   const int64_t b = bg / p.G, grp = bg % p.G;
@@ -177,19 +220,17 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
   const int64_t rs = p.G * N;                      // token row stride of B and C
   const bf16_t* Bg = static_cast<const bf16_t*>(p.Bm) + b * p.L * rs + grp * N;
   const bf16_t* Cg = static_cast<const bf16_t*>(p.Cm) + b * p.L * rs + grp * N;
-  // transposed B (and C in the backward), 8 tokens per 16-byte store, written in the order the
-  // chunk-state kernel reads its MFMA operands (v_mfma_f32_32x32x16_bf16, A = B^T): the piece
-  // (n, j0 .. j0 + 7) of 32-row tile nt = n / 32 and 16-token step s = j0 / 16 is lane
-  // n % 32 + 32 ((j0 / 8) % 2) of the 1 KB fragment (nt, s), fragments in the order
-  // nt Q / 16 + s, so that one fragment load of a wave is 1 KB of consecutive memory. The
-  // backward's main kernel also gets plain [n][j] copies (ws_Bt, ws_Ct).
-  constexpr int NQ = N / 4;
   const int64_t cbase = (bg * nch + c) * (int64_t)(N * Q);
   auto frag_off = [](int n, int j0) -> int64_t {
     const int frag = (n / 32) * (Q / 16) + j0 / 16, ln = n % 32 + 32 * ((j0 / 8) % 2);
     return (int64_t)frag * 512 + ln * 8;
   };
+  // Workgroups go to the XCDs by linear id, and part is its lowest index: the tiles are dealt to
+  // the parts rotated by chunk, so that the parts holding the most tiles do not all fall on the
+  // same XCDs.
+  const int rpart = (int)((part + c + bg) % kPrepParts);
   auto transpose = [&](const bf16_t* src, void* plain, void* frag) {
+    constexpr int NQ = N / kPrepParts;
     for (int it = tid; it < NQ * (Q / 8); it += 256) {
       const int n = part * NQ + it / (Q / 8);
       const int j0 = (it % (Q / 8)) * 8;
@@ -214,19 +255,31 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
   // (and the row blocks derived from it) in scalar registers, so branches on it are not divergent
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 4, r16 = lane & 15;
   constexpr int NIB = Q / 16, KS = N / 32, NTILES = NIB * (NIB + 1) / 2;
-  bf16_t* G = static_cast<bf16_t*>(p.ws_G) + (bg * nch + c) * (int64_t)(Q * Q);
-  for (int k = part * 4 + w; k < NTILES; k += 16) {
-    int ib = 0, rem = k;
+  constexpr int kWaves = kPrepParts * 4, kPerWave = (NTILES + kWaves - 1) / kWaves;
+  bf16x8 ca[kPerWave][KS], bb[kPerWave][KS];
+  int tib[kPerWave], tjt[kPerWave];
+#pragma unroll
+  for (int q = 0; q < kPerWave; ++q) {
+    const int k = rpart * 4 + w + q * kWaves;
+    int ib = 0, rem = k < NTILES ? k : 0;
     while (rem > ib) { rem -= ib + 1; ++ib; }
-    const int jt = rem;
-    const int64_t ti = c * Q + ib * 16 + r16, tj = c * Q + jt * 16 + r16;   // tokens in the row
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    tib[q] = ib;
+    tjt[q] = rem;
+    const int64_t ti = c * Q + ib * 16 + r16, tj = c * Q + rem * 16 + r16;   // tokens in the row
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 ca = ti < p.L ? load_frag(Cg + ti * rs + ks * 32 + 8 * g) : zero_frag();
-      const bf16x8 bb = tj < p.L ? load_frag(Bg + tj * rs + ks * 32 + 8 * g) : zero_frag();
-      acc = mfma16(ca, bb, acc);  // D[i][j] = sum_n C_i[n] B_j[n]
+      ca[q][ks] = ti < p.L ? load_frag(Cg + ti * rs + ks * 32 + 8 * g) : zero_frag();
+      bb[q][ks] = tj < p.L ? load_frag(Bg + tj * rs + ks * 32 + 8 * g) : zero_frag();
     }
+  }
+  bf16_t* G = static_cast<bf16_t*>(p.ws_G) + (bg * nch + c) * (int64_t)(Q * Q);
+#pragma unroll
+  for (int q = 0; q < kPerWave; ++q) {
+    if (rpart * 4 + w + q * kWaves >= NTILES) break;   // uniform
+    const int ib = tib[q], jt = tjt[q];
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) acc = mfma16(ca[q][ks], bb[q][ks], acc);  // D[i][j] = sum_n C_i[n] B_j[n]
     if constexpr (BWD) {
       float* G32 = static_cast<float*>(p.ws_G) + (bg * nch + c) * (int64_t)(Q * Q);
 #pragma unroll

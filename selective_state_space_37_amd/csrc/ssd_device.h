@@ -50,6 +50,9 @@ __device__ __forceinline__ void st_at(E* base, uint32_t byte_off, const T& v) {
 
 constexpr int kP = 64;  // head dim supported
 
+// s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt left at their maxima)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // LDS layout of a transposed x tile (rows = channels p, columns = tokens j, row stride Q + 8
 // bf16): the 4-byte word column of row p is XORed with 8 ((p >> 4) & 3) (kept inside the row).
 // The staging writes (8 channel groups x 8 token pairs per wave) then fall on 64 different banks
@@ -381,6 +384,10 @@ __global__ __launch_bounds__(64 * (N / 32)) void ssd_chunk_state_kernel(SsdParam
       }
     }
   }
+  // The initial state's loads (taken only with a state given) complete here, once: left in flight
+  // into the loop, the compiler cannot tell at the loop head whether they are and waits for every
+  // outstanding load there on each iteration.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // ---- the x (dy, with z) of a step: item = (token pair jp, channel group pg of 8), so the eight
   // lanes of a row load its 128 bytes in one instruction. Column pair jp of the step belongs to
@@ -494,59 +501,102 @@ __global__ __launch_bounds__(64 * (N / 32)) void ssd_chunk_state_kernel(SsdParam
   // segments: the sum of the step sizes of the segment's chunks before the current one
   float dsum = 0.f;
 
-  // Two register sets of B^T fragments used by step parity (the loop is unrolled by two so they
-  // are named statically): the fragments of step k + 1 are loaded while step k runs.
-  bf16x8 ringA[KQ], ringB[KQ];
-  StepX in;
-  if (nst > 0) {
-    load_x(0, in);
-    load_ring(0, ringA);
-    stage(0, in, Xs[0]);
-    load_x(nst > 1 ? 1 : 0, in);
-  }
-  __syncthreads();
-  auto step = [&](int64_t k, const bf16x8 (&cur)[KQ], bf16x8 (&nxt)[KQ]) __attribute__((always_inline)) {
-    const __bf16* xsb = Xs[k & 1];
-    // the step sizes summed over the chunks of the step's units (uniform loads)
-    float stot[NU];
+  // The step sizes summed over the chunks of step k's units (uniform loads), loaded one step
+  // ahead of use.
+  auto load_stot = [&](int64_t k, float (&st)[NU]) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < NU; ++q) {
       int64_t c;
       int off;
       unit_at(k, q, c, off);
-      stot[q] = p.ws_sphi[((b * nch + clamp_chunk(c)) * H + h) * QS + QS - 1].x;
+      st[q] = p.ws_sphi[((b * nch + clamp_chunk(c)) * H + h) * QS + QS - 1].x;
+    }
+  };
+  // Loads in flight: the x of the next XA steps (XA register sets, by step parity), the B^T
+  // fragments of the next step and (XA = 2) its step-size totals (two sets, used by step parity). The loop is
+  // unrolled by two so every set is named statically, and within a step the loads are issued in
+  // the order they are needed (totals, fragments, then x XA steps ahead): the memory counter
+  // completes in order, so each wait then covers only what the step uses. Two steps of x ahead
+  // at 128-token steps (the second set fits the registers of two waves per SIMD); one at
+  // 256-token steps.
+  static_assert(PPC <= 2, "a step covers whole chunks or one half of a chunk");
+  constexpr int XA = Q <= 128 ? 2 : 1;
+  bf16x8 ringA[KQ], ringB[KQ];
+  float stA[NU], stB[NU];
+  StepX inA, inB;   // (with XA = 1 only inA is used)
+  if (nst > 0) {
+    if constexpr (XA == 2) load_stot(0, stA);
+    load_ring(0, ringA);
+    load_x(0, inA);
+    stage(0, inA, Xs[0]);
+    if constexpr (XA == 2) {
+      load_x(nst > 1 ? 1 : 0, inB);
+      load_x(nst > 2 ? 2 : nst - 1, inA);
+    } else {
+      load_x(nst > 1 ? 1 : 0, inA);
+    }
+  }
+  __syncthreads();
+  // step k: START whether its first unit starts a chunk (with two steps of x ahead known at
+  // compile time: always with whole chunks per step, on even steps with half chunks, since a
+  // segment's first step starts its first chunk). TAIL: a step whose units may run past the
+  // segment's end.
+  auto step = [&](int64_t k, auto start_tag, auto tail_tag, const bf16x8 (&cur)[KQ], bf16x8 (&nxt)[KQ],
+                  const float (&stp)[NU], float (&stn)[NU], StepX& xin) __attribute__((always_inline)) {
+    // START: 1 / 0 known at compile time, -1 tested here
+    constexpr int START = decltype(start_tag)::value;
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    const __bf16* xsb = Xs[k & 1];
+    // the totals of this step: prefetched with two steps of x in flight; else loaded here (the
+    // registers of the 256-token steps are spent on x)
+    float stc[NU];
+    if constexpr (XA == 2) {
+#pragma unroll
+      for (int q = 0; q < NU; ++q) stc[q] = stp[q];
+    } else {
+      load_stot(k, stc);
     }
     // a chunk's first unit in the walk: store the carried state, then decay it over the chunk
     auto chunk_start = [&](int q, int64_t c) __attribute__((always_inline)) {
       store_carried(c);
       if (!ADJ && nseg > 1 && w == 0 && lane == 0) p.ws_dpre[(b * nch + c) * H + h] = dsum;
-      dsum += stot[q];
-      const float dec = exp2_fast(a2 * stot[q]);
+      dsum += stc[q];
+      const float dec = exp2_fast(a2 * stc[q]);
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[pt][v] *= dec;
     };
-    // The first unit's stores go out before the step's loads: with stores and loads in flight
-    // together the compiler can only wait for all of them, and the next wait (at the next step)
-    // then finds the stores older than the loads it needs.
+    // The first unit's stores go out before the step's loads, so that the waits of the next step
+    // find them older than the loads it needs.
     int64_t c0;
     int off0;
     unit_at(k, 0, c0, off0);
-    const bool start0 = live_chunk(c0) && off0 == (ADJ ? QS - UT : 0);
-    if (start0) chunk_start(0, c0);   // uniform
-    // the next step's x^T into the other buffer (free since the last barrier); x of step k + 2
-    // and the fragments of step k + 1 loaded (past the end: a repeated step, every load stays
-    // unconditional)
-    stage(k + 1, in, Xs[(k + 1) & 1]);
-    load_x(k + 2 < nst ? k + 2 : nst - 1, in);
-    load_ring(k + 1 < nst ? k + 1 : nst - 1, nxt);
+    if constexpr (START == 1) {
+      chunk_start(0, c0);
+    } else if constexpr (START == -1) {
+      if (live_chunk(c0) && off0 == (ADJ ? QS - UT : 0)) chunk_start(0, c0);   // uniform
+    }
+    // the next step's x^T into the other buffer (free since the last barrier); then the totals and
+    // fragments of step k + 1 and the x of step k + 1 + XA (past the end: a repeated step, every
+    // load stays unconditional)
+    stage(k + 1, xin, Xs[(k + 1) & 1]);
+    if constexpr (XA == 2) {
+      load_stot(k + 1 < nst ? k + 1 : nst - 1, stn);
+      load_ring(k + 1 < nst ? k + 1 : nst - 1, nxt);
+      load_x(k + 3 < nst ? k + 3 : nst - 1, xin);
+    } else {
+      load_x(k + 2 < nst ? k + 2 : nst - 1, xin);
+      load_ring(k + 1 < nst ? k + 1 : nst - 1, nxt);
+    }
 #pragma unroll
     for (int q = 0; q < NU; ++q) {
       int64_t c;
       int off;
       unit_at(k, q, c, off);
-      if (!live_chunk(c)) break;   // uniform: the remaining units are past the segment
+      if constexpr (TAIL) {
+        if (!live_chunk(c)) break;   // uniform: the remaining units are past the segment
+      }
       if (q > 0 && off == (ADJ ? QS - UT : 0)) chunk_start(q, c);
       // x fragments read one step ahead of their products
       bf16x8 xf[2][2];
@@ -564,12 +614,30 @@ __global__ __launch_bounds__(64 * (N / 32)) void ssd_chunk_state_kernel(SsdParam
     }
     __syncthreads();
   };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  using S1 = std::integral_constant<int, 1>;
+  using SR = std::integral_constant<int, -1>;
   int64_t k = 0;
-  for (; k + 1 < nst; k += 2) {
-    step(k, ringA, ringB);
-    step(k + 1, ringB, ringA);
+  if constexpr (XA == 2) {
+    // even steps start a chunk (half chunks per step) or every step does (whole chunks); x of
+    // step k + 1 is in the set of k + 1's parity (inB for even k, inA for odd k)
+    using OddStart = std::integral_constant<int, PPC == 1 ? 1 : 0>;
+    for (; k + 3 < nst; k += 2) {
+      step(k, S1{}, F_{}, ringA, ringB, stA, stB, inB);
+      step(k + 1, OddStart{}, F_{}, ringB, ringA, stB, stA, inA);
+    }
+    if (k < nst) step(k, S1{}, T_{}, ringA, ringB, stA, stB, inB);
+    if (k + 1 < nst) step(k + 1, OddStart{}, T_{}, ringB, ringA, stB, stA, inA);
+    if (k + 2 < nst) step(k + 2, S1{}, T_{}, ringA, ringB, stA, stB, inB);
+  } else {
+    // (the 256-token steps keep the run-time tests: their registers are full)
+    for (; k + 1 < nst; k += 2) {
+      step(k, SR{}, T_{}, ringA, ringB, stA, stB, inA);
+      step(k + 1, SR{}, T_{}, ringB, ringA, stB, stA, inA);
+    }
+    if (k < nst) step(k, SR{}, T_{}, ringA, ringB, stA, stB, inA);
   }
-  if (k < nst) step(k, ringA, ringB);
 
   // the end state: the final one (one segment), else the segment's own (for the carry kernel)
   float* fin = ADJ ? p.dh0 : p.h_last;

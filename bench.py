@@ -118,6 +118,10 @@ def copy_ceiling_gbs(torch, nbytes=1 << 30, reps=10):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+# each secondary figure is timed after this much back-to-back work of its own (see settle)
+SECONDARY_SETTLE_S = 0.3
+
+
 def settle(fn, torch, seconds):
     """Launch fn back to back (batches of 64, synchronised) for the given time. The GPU raises its
     clocks only under sustained load: after several seconds idle (input generation) the first
@@ -355,6 +359,7 @@ def secondary(torch, np, inputs, ssm, dev, generation_figure=True):
     ws = ssm.workspace(nb, "cuda")
     fn = lambda i: ssm.scan_fwd(x, delta, A, Bm, Cm, delta_bias=bias, delta_softplus=True, Dskip=Dk, z=z,
                                 y=y, h_last=hl, ws=ws)
+    settle(fn, torch, SECONDARY_SETTLE_S)
     _, ms = timed(fn, 10, 3, torch)
     nbytes = scan_bytes(B, L, D, N, 4, bias=True)
     res["scan_long_1x1048576x256_f32"] = {"ms": round(ms, 4), "GB_s": round(nbytes / ms / 1e6, 1),
@@ -373,6 +378,7 @@ def secondary(torch, np, inputs, ssm, dev, generation_figure=True):
     nb = ssm.load().ssm_scan_bwd_workspace_bytes(B, L, D, N, ssm.SSM_BF16)
     ws = ssm.workspace(nb, "cuda")
     fn = lambda i: ssm.scan_bwd(x, delta, A, Bm, Cm, dy, Dskip=Dk, z=z, ws=ws)
+    settle(fn, torch, SECONDARY_SETTLE_S)
     _, ms = timed(fn, 10, 3, torch)
     # essential I/O: x, delta, z, dy, B, C in; dx, ddelta, dz (bf16), dB, dC (fp32) out
     nbytes = 7 * B * L * D * 2 + 2 * B * L * N * 2 + 2 * B * L * N * 4 + 2 * D * N * 4 + 2 * D * 4
@@ -398,6 +404,7 @@ def secondary(torch, np, inputs, ssm, dev, generation_figure=True):
     y = torch.empty_like(x)
     hl = torch.empty((B, D, N), device="cuda")
     fn = lambda i: ssm.scan_fwd_conv(x, delta, A, Bm, Cm, cw, conv_state=reg, Dskip=Dk, z=z, y=y, h_last=hl)
+    settle(fn, torch, SECONDARY_SETTLE_S)
     _, ms = timed(fn, 5, 3, torch)
     nbytes = scan_bytes(B, L, D, N, 2) + D * W * 4 + 2 * B * D * W * 2
     res["prefill_conv_128x2048x4096_n16_bf16"] = {
@@ -432,6 +439,7 @@ def secondary(torch, np, inputs, ssm, dev, generation_figure=True):
     with torch.cuda.graph(graph):
         for i in range(layers):
             dec(i)
+    settle(lambda i: graph.replay(), torch, SECONDARY_SETTLE_S)
     _, ms = timed(lambda i: graph.replay(), 20, 3, torch)
     per_step = ms / layers
     nbytes = B * D * (2 * N * 4 + 2 * W * 2 + 4 * 2) + D * N * 4 + D * W * 4 + D * 4 + 2 * B * N * 2
@@ -445,6 +453,7 @@ def secondary(torch, np, inputs, ssm, dev, generation_figure=True):
     with torch.cuda.graph(graph1):
         for i in range(layers):
             dec(0)
+    settle(lambda i: graph1.replay(), torch, SECONDARY_SETTLE_S)
     _, ms1 = timed(lambda i: graph1.replay(), 20, 3, torch)
     per1 = ms1 / layers
     res["decode_128x4096_n16_bf16_single_layer_cache_resident"] = {
@@ -462,6 +471,7 @@ def secondary(torch, np, inputs, ssm, dev, generation_figure=True):
     nb = ssm.load().ssd_chunk_fwd_workspace_bytes(B, L, H, P, N, Q, ssm.SSM_BF16)
     ws = ssm.workspace(nb, "cuda")
     fn = lambda i: ssm.ssd_chunk_fwd(x, delta, Ah, Bm, Cm, chunk=Q, y=y, ws=ws)
+    settle(fn, torch, SECONDARY_SETTLE_S)
     _, ms = timed(fn, 10, 3, torch)
     nbytes = 2 * B * L * H * P * 2 + B * L * H * 2 + 2 * B * L * N * 2 + H * 4 + B * H * P * N * 4
     nch = L // Q
@@ -476,6 +486,7 @@ def secondary(torch, np, inputs, ssm, dev, generation_figure=True):
     wsb = ssm.workspace(nbw, "cuda")
     Bg, Cg = Bm.unsqueeze(2), Cm.unsqueeze(2)
     fnb = lambda i: ssm.ssd_chunk_bwd(x, delta, Ah, Bg, Cg, dy, ws=wsb)
+    settle(fnb, torch, SECONDARY_SETTLE_S)
     _, msb = timed(fnb, 10, 3, torch)
     # essential I/O: x, dy, dx; delta, ddelta (bf16); B, C (bf16) and dB, dC (float32); dh0
     nbytes_b = 3 * B * L * H * P * 2 + 2 * B * L * H * 2 + 2 * B * L * N * 2 + 2 * B * L * N * 4 + B * H * P * N * 4
@@ -541,6 +552,7 @@ def generation(torch, ssm, g):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         one_step()
+    settle(lambda i: graph.replay(), torch, SECONDARY_SETTLE_S)
     _, ms = timed(lambda i: graph.replay(), 20, 3, torch)
     # HBM bytes per step: every weight once; the SSM state (float32) and the conv register (bf16)
     # of every layer read and written; activations are small and mostly cache-resident

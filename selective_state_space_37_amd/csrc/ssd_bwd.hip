@@ -219,7 +219,10 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
     if (tv < Q) psp = ld_at<float2>(sp, (uint32_t)tv * 8u);
     if (w == 0) {
       const bf16_t* dl0 = static_cast<const bf16_t*>(p.delta) + (b * L + tc0) * H + h;
-      pdl = tc0 + lane < L ? ld_at<uint16_t>(dl0, (uint32_t)(lane * H) * 2u) : 0u;
+      // (an unconditional load of a row inside the sequence, then a select: a load under a branch
+      // leaves the compiler unsure of the loads in flight, and it then waits for all of them)
+      const int lr = (int)std::min<int64_t>(lane, L - 1 - tc0);
+      pdl = ld_at<uint16_t>(dl0, (uint32_t)(lr * H) * 2u);   // rows past L: zeroed at use
     }
     if constexpr (kEarlyGcB) load_gcb(kh, tv);
   };
@@ -236,6 +239,10 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
     const bool has_hg = tv < NHG;
     const int64_t h = hblk * bp.hb + kh;
     const float a = p.A[h], a2 = a * kLog2e;
+    // the step-size bias of the head, loaded here with the head's other scalars (a stand-in
+    // address and a select when there is none: see the Delta bits in the prefetch)
+    const float dbias_v = *(p.delta_bias ? p.delta_bias + h : p.A + h);
+    const float dbias = p.delta_bias ? dbias_v : 0.f;
     // (first token of this wave's tile, head h, channel 0), and this lane's token and channel
     // group 4 g relative to it
     const int64_t trow = ((b * L + tc0 + tt * 16) * H + h) * kP;
@@ -665,27 +672,29 @@ __global__ __launch_bounds__(512) void ssd_bwd_main_kernel(SsdBwdParams bp) {
       const float vv = sVv[0][t] + sVv[1][t];
       const float ddt = a * u + vv;
       const int64_t tt2 = tc0 + t;
-      float pa = 0.f, pb = 0.f;
-      if (tt2 < L) {
-        const float raw = bf16_to_f32((uint16_t)dl) + (p.delta_bias ? p.delta_bias[h] : 0.f);
-        const float dt = p.delta_softplus ? softplus_f32(raw) : raw;
-        const float gu = p.delta_softplus ? ddt * sigmoid_fast(raw) : ddt;
-        st_at(static_cast<bf16_t*>(bp.ddelta) + (b * L + tc0) * H + h, (uint32_t)(t * H) * 2u, f32_to_bf16(gu));
-        // (Delta - phi) / a = (a Delta - expm1(a Delta)) / a^2
-        const float xa = a * dt;
-        pa = dt * u + (xa - expm1f(xa)) / (a * a) * vv;
-        pb = gu;
-      }
+      // (no branch on the token: rows past L compute from a zero step and are selected away, and
+      // their dDelta store falls outside the descriptor, so the stores in flight are the same on
+      // every path)
+      const float raw = (tt2 < L ? bf16_to_f32((uint16_t)dl) : 0.f) + dbias;
+      const float dt = p.delta_softplus ? softplus_f32(raw) : raw;
+      const float gu = p.delta_softplus ? ddt * sigmoid_fast(raw) : ddt;
+      const int64_t rows_in = std::min<int64_t>(64, L - tc0);
+      buf_store(make_rsrc(static_cast<bf16_t*>(bp.ddelta) + (b * L + tc0) * H + h, (int)(((rows_in - 1) * H + 1) * 2)),
+                (uint32_t)(t * H) * 2u, gu, (bf16_t*)nullptr);
+      // (Delta - phi) / a = (a Delta - expm1(a Delta)) / a^2
+      const float xa = a * dt;
+      float pa = dt * u + (xa - expm1f(xa)) / (a * a) * vv;
+      float pb = gu;
+      if (!(tt2 < L)) pa = pb = 0.f;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) {
         pa += __shfl_xor(pa, off, 64);
         pb += __shfl_xor(pb, off, 64);
       }
       const int64_t pidx = (b * nch + c) * H + h;
-      if (t == 0) {
-        bp.ws_pA[pidx] = pa;
-        bp.ws_pb[pidx] = pb;
-      }
+      // (every lane holds the sums: all store the same value, with no branch)
+      bp.ws_pA[pidx] = pa;
+      bp.ws_pb[pidx] = pb;
       bp.ws_pD[pidx * kP + t] = sDD[0][t] + sDD[1][t] + sDD[2][t] + sDD[3][t];
     }
     // (no barrier here: the next head's staging writes none of what wave 0 reads above, and the

@@ -342,7 +342,17 @@ __global__ __launch_bounds__(64 * (N / 32)) void ssd_chunk_state_kernel(SsdParam
   static_assert(kItems % NT == 0 || kItems < NT, "the x items divide over the threads");
   constexpr int XPER = (kItems + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) __bf16 Xs[2][kP * XS];
-  const int64_t h = blockIdx.x, b = blockIdx.y, seg = blockIdx.z, nseg = gridDim.z;
+  // Workgroups go to the 8 XCDs round-robin by linear id. In the segmented forward pass with H a
+  // multiple of 8, XCD x takes the heads [x H/8, (x+1) H/8) of each (batch, segment), so heads
+  // that sit side by side in every token row of x are read from one XCD at about the same time
+  // (89.9 -> 87.9 us at the 80-head layer; the backward's unsegmented passes ran 1.5% slower with
+  // it and keep the plain order).
+  int64_t h = blockIdx.x;
+  if (!ADJ && gridDim.z > 1 && gridDim.x % 8 == 0) {
+    const int64_t per = gridDim.x / 8;
+    h = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  }
+  const int64_t b = blockIdx.y, seg = blockIdx.z, nseg = gridDim.z;
   const int64_t L = p.L, H = p.H;
   const int64_t nch = (L + QS - 1) / QS;       // chunks
   const int64_t c_begin = seg * nch / nseg, c_end = (seg + 1) * nch / nseg;

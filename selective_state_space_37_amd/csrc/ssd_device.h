@@ -304,8 +304,9 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(SsdParams p) {
 // computed transposed: states x channels; output layout: lane l, value v holds column l % 32,
 // row 8 (v / 4) + 4 (l / 32) + v % 4).
 // The tokens are taken Q at a time (one step): per step the x^T of its Q tokens is staged once,
-// and the step's loads are issued at its start (the x of the step after, the B^T fragments of the
-// next step). A step is one or more whole chunks (Q >= QS) or a part of one (Q < QS); per chunk,
+// and the step's loads are issued at its start (the x of the step one or two ahead, the B^T
+// fragments of the next step; see the loop). A step is one or more whole chunks (Q >= QS) or a
+// part of one (Q < QS); per chunk,
 // at its first part:
 //   store h_{c-1} (bf16: the carried state of the output kernel), decay it by exp(a S_last),
 // and per part h_c += sum_j B_j^T (w_j x_j), w_j = exp(a (S_last - S_j)) phi_j.

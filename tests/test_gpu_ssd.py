@@ -49,6 +49,17 @@ def test_initial_state_with_segments(chunk):
     assert err <= gu.TOL["bf16"]
 
 
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_segments_with_head_runs_per_xcd(chunk):
+    """16 heads of one row with the state pass in L-segments (16 chains: 8 segments): with the head
+    count a multiple of 8 the segmented pass hands each XCD a run of adjacent heads (here 2 per run,
+    not the identity order), so a head mapped twice or not at all would show in its outputs."""
+    inp = inputs.ssd_layer(seed=81, Bsz=1, L=1024, H=16, N=64, gate=True, dskip=True, h0=True)
+    err = gu.ssd_parity(inp, gu.ssd_on_gpu(inp, chunk=chunk))
+    print("chunk", chunk, "err", err)
+    assert err <= gu.TOL["bf16"]
+
+
 def test_short_sequences():
     for L in (1, 17, 64):
         inp = inputs.ssd_layer(seed=73, Bsz=1, L=L, H=2, h0=True)
